@@ -1,0 +1,150 @@
+/*
+ * kivi.h -- C ABI of libkivi: a 2-bit KIVI KV cache and fused decode attention for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method (pages on KIVI, cited by title and section):
+ *  - "KIVI: A Tuning-Free Asymmetric 2bit Quantization for KV Cache" (arXiv 2402.02750v2
+ *    summary): title ("asymmetric 2bit"); "Key points"/"Summary": serving batches many
+ *    requests and the KV cache becomes the speed and memory bottleneck as batch and
+ *    context grow, so the cache is quantized.
+ *  - inference-research record kv-efficiency/kivi-2bit-llama2-13b-mha-4k, "KV bytes
+ *    basis", "Quant method" and "Methodology": keys quantized per-channel and values
+ *    per-token, group size 32, the most recent R = 128 tokens kept in 16-bit floats and
+ *    only the grouped history quantized.
+ *  - "Your KV cache doesn't have a bit problem, it has a geometry problem", paragraphs
+ *    1-4: why keys go per-channel (fixed outlier channels) and values per-token (errors
+ *    matter at the attention output), and the full-precision residual.
+ *
+ * Conventions for every call:
+ *  - Pointers are DEVICE pointers unless marked (host).  The caller allocates and frees
+ *    every buffer; the library allocates nothing, on any path, and keeps no mutable
+ *    global state.  fp16 data are IEEE binary16 bit patterns (uint16_t).
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue work on
+ *    it and never synchronise the device.
+ *  - Return value: KIVI_OK (0) or a negative KIVI_ERR_* code.  Arguments are validated
+ *    on the host before anything is enqueued; on any error nothing is enqueued and the
+ *    cache state fields are unchanged.  Nothing throws across this boundary.
+ *  - Inputs must be finite (NaN/Inf are outside the contract and are not scanned).
+ *  - This version implements head_dim == 128 and group == 32 (other valid shapes return
+ *    KIVI_ERR_UNSUPPORTED).
+ */
+#ifndef KIVI_H
+#define KIVI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    KIVI_OK = 0,
+    KIVI_ERR_NULL = -1,          /* a required pointer is NULL */
+    KIVI_ERR_SHAPE = -2,         /* sizes inconsistent (divisibility, empty context, ...) */
+    KIVI_ERR_UNSUPPORTED = -3,   /* valid but not implemented here (head_dim != 128, ...) */
+    KIVI_ERR_CAPACITY = -4,      /* the call would write past token_cap / residual_cap */
+    KIVI_ERR_WORKSPACE = -5,     /* workspace missing or too small */
+    KIVI_ERR_HIP = -6,           /* a HIP runtime error while enqueueing */
+    KIVI_ERR_STATE = -7          /* the cache state fields are inconsistent */
+};
+
+/*
+ * The cache descriptor (host struct; the caller owns it and every buffer it points to).
+ * row = b * kv_heads + h.  D = head_dim, G = group, R = residual_cap.
+ *
+ * Packed layout (four 2-bit codes per byte, least significant bits first):
+ *   k_codes, v_codes : uint8  [row][token_cap][D/4]; code of (token t, channel j) at
+ *                      byte t*(D/4) + j/4, bits 2*(j%4) .. 2*(j%4)+1.
+ *   k_sz             : fp16   [row][token_cap/G][D][2]  (scale, zero) of key token group
+ *                      g, channel j  -- keys are quantized per-channel over G tokens.
+ *   v_sz             : fp16   [row][token_cap][D/G][2]  (scale, zero) of value token t,
+ *                      channel group k -- values are quantized per-token over G channels.
+ *   k_res, v_res     : fp16   [row][R][D] residual ring; the n_res newest tokens, oldest
+ *                      first, sit in slots (res_head + i) % R, i < n_res.
+ * Dequantized value: zero + code * scale.  Quantizer: zero = group min, scale =
+ * fp16(fp32(fp32(max - min) / 3)), code = clamp(round_half_even(fp32(fp32(x - min) /
+ * scale)), 0, 3) (scale 0 -> code 0), a -0 minimum stored as +0.
+ *
+ * State: the first n_quant tokens of the context (a multiple of G) are in the quantized
+ * history; the next n_res (0..R) are in the ring.  res_head is a multiple of G.
+ */
+typedef struct kivi_cache {
+    int32_t batch, kv_heads, head_dim;
+    int32_t group;           /* G */
+    int32_t residual_cap;    /* R, a multiple of G */
+    int32_t token_cap;       /* capacity of the quantized history in tokens, multiple of G */
+    int32_t n_quant, n_res, res_head;
+    int32_t reserved;        /* must be 0 */
+    uint8_t* k_codes;
+    uint8_t* v_codes;
+    uint16_t* k_sz;
+    uint16_t* v_sz;
+    uint16_t* k_res;
+    uint16_t* v_res;
+} kivi_cache;
+
+/* Keys per-channel (record "Quant method"; article paragraph 2).
+ * k: fp16, element (row, t, j) at k[row*src_row_stride + t*D + j], t < tokens.
+ * Quantizes token groups [0, tokens) into history tokens [dst_token_off, +tokens).
+ * tokens and dst_token_off are multiples of G; src_row_stride >= tokens*D.
+ * Does not read or change the state fields. */
+int kivi_quantize_k_per_channel(const uint16_t* k, int32_t tokens, int64_t src_row_stride,
+                                kivi_cache* cache, int32_t dst_token_off, void* stream);
+
+/* Values per-token (record "Quant method"; article paragraph 3): every token's D
+ * channels in D/G groups of G.  Same source convention; any tokens >= 0 and any
+ * dst_token_off >= 0 with dst_token_off + tokens <= token_cap. */
+int kivi_quantize_v_per_token(const uint16_t* v, int32_t tokens, int64_t src_row_stride,
+                              kivi_cache* cache, int32_t dst_token_off, void* stream);
+
+/* Prefill from a context of `tokens` fp16 keys and values (same source convention):
+ * quantizes the first n_quant (multiple of G, <= token_cap) tokens of both, copies the
+ * remaining tokens - n_quant (<= R) into ring slots 0.. and sets n_quant, n_res and
+ * res_head = 0 in *cache (host side, immediately). */
+int kivi_prefill(const uint16_t* k, const uint16_t* v, int32_t tokens, int64_t src_row_stride,
+                 int32_t n_quant, kivi_cache* cache, void* stream);
+
+/* One decode-time token per row (k_new, v_new: fp16 [row][D], contiguous).
+ * The record keeps the newest R tokens in 16-bit floats and quantizes only grouped
+ * history ("KV bytes basis").  If the ring already holds R tokens, the oldest G of them
+ * become key token group n_quant/G and value tokens n_quant..n_quant+G-1 (flush), then
+ * the new token enters the ring.  Updates n_quant, n_res and res_head on the host
+ * immediately (no device round trip).  *flushed (host, nullable) receives 1 if a group
+ * was flushed, else 0.  KIVI_ERR_CAPACITY if a flush would pass token_cap. */
+int kivi_append_flush(kivi_cache* cache, const uint16_t* k_new, const uint16_t* v_new,
+                      int32_t* flushed, void* stream);
+
+/* Fused decode attention over the whole cache (dequantized history followed by the
+ * residual), one query per head: out = softmax(sm_scale * q.K^T) . V.
+ * q: fp16 [batch][q_heads][D]; q_heads a multiple of kv_heads, query head hq reads kv
+ * head hq / (q_heads / kv_heads).  out: fp16 [batch][q_heads][D].  lse (nullable): fp32
+ * [batch][q_heads], natural log of the softmax denominator including sm_scale.
+ * The context is split into num_splits parts per row (0 = automatic) and the partial
+ * softmax states are merged with a log-sum-exp merge.  workspace: device scratch of at
+ * least kivi_decode_attn_workspace(cache, q_heads, num_splits) bytes, 256-byte aligned.
+ * KIVI_ERR_SHAPE if the context is empty. */
+int kivi_decode_attn(const kivi_cache* cache, const uint16_t* q, int32_t q_heads,
+                     float sm_scale, uint16_t* out, float* lse, void* workspace,
+                     size_t workspace_bytes, int32_t num_splits, void* stream);
+
+/* Host-only helpers (no device access; safe without a GPU). */
+
+/* Split count that kivi_decode_attn uses for num_splits == 0 (depends on shapes only).
+ * Returns a value >= 1, or a negative KIVI_ERR_* code. */
+int32_t kivi_decode_attn_splits(const kivi_cache* cache, int32_t q_heads);
+
+/* Workspace bytes kivi_decode_attn needs for this shape and split count (0 = auto). */
+size_t kivi_decode_attn_workspace(const kivi_cache* cache, int32_t q_heads, int32_t num_splits);
+
+/* Buffer sizes (bytes) for a cache of this shape (pointer fields are ignored):
+ * codes = k_codes + v_codes, pairs = k_sz + v_sz, residual = k_res + v_res. */
+int kivi_cache_bytes(const kivi_cache* shape, size_t* codes, size_t* pairs, size_t* residual);
+
+/* Static description of an error code. */
+const char* kivi_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KIVI_H */

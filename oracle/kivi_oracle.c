@@ -90,8 +90,9 @@ static float rne_float(float t) {
  * binary32 with one rounding each (true division, no reciprocal); the scale is
  * stored as fp16 (RNE, subnormals kept) and the codes are computed against that
  * stored scale, so a code is the nearest level of the stored (scale, zero);
- * rounding ties go to the even code; a zero scale gives all codes 0; a -0 minimum
- * is stored as +0. */
+ * rounding ties go to the even code; a zero scale gives all codes 0; signed zeros
+ * are read as +0 for the minimum and maximum, so the zero point and a zero scale are
+ * stored as +0 whatever the order of -0 and +0 in the group. */
 void kivi_ref_quant_group(const uint16_t* x, ptrdiff_t stride, int32_t n,
                           uint16_t* scale, uint16_t* zero, uint8_t* codes) {
     float mn = INFINITY, mx = -INFINITY;
@@ -101,6 +102,7 @@ void kivi_ref_quant_group(const uint16_t* x, ptrdiff_t stride, int32_t n,
         if (v > mx) mx = v;
     }
     if (mn == 0.0f) mn = 0.0f;             /* canonical +0 zero point */
+    if (mx == 0.0f) mx = 0.0f;             /* so a zero range, hence a zero scale, is +0 */
     float range = mx - mn;
     float s32 = range / 3.0f;
     uint16_t s16 = kivi_ref_f32_to_f16(s32);

@@ -24,6 +24,7 @@ MUTATIONS = [
     ("no_clamp", "if (r > 3.0f) r = 3.0f;", "", False),
     ("zero_is_max", "*zero = kivi_ref_f32_to_f16(mn);", "*zero = kivi_ref_f32_to_f16(mx);", False),
     ("keep_negative_zero", "if (mn == 0.0f) mn = 0.0f;", "", False),
+    ("keep_negative_zero_max", "if (mx == 0.0f) mx = 0.0f;", "", False),
     ("msb_first_packing", "int sh = 2 * (j % 4);", "int sh = 6 - 2 * (j % 4);", False),
     ("key_pair_per_token", "const uint16_t* kp = k_pair(c, row, t / G, j);",
      "const uint16_t* kp = k_pair(c, row, t % (c->token_cap / G), j);", False),

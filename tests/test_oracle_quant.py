@@ -172,6 +172,15 @@ def test_codes_do_not_depend_on_element_order():
     assert np.array_equal(c1[:, perm], c2)
 
 
+def test_signed_zeros_do_not_depend_on_order():
+    rng = np.random.default_rng(6)
+    x = rng.choice(np.array([0x8000, 0x0000, 0x3C00, 0xBC00], np.uint16), (20000, G), p=[.45, .45, .05, .05])
+    s1, z1, c1 = _quantize_as_values(x)
+    s2, z2, c2 = _quantize_as_values(np.ascontiguousarray(x[:, ::-1]))
+    assert np.array_equal(s1, s2) and np.array_equal(z1, z2) and np.array_equal(c1[:, ::-1], c2)
+    assert not (s1 == 0x8000).any() and not (z1 == 0x8000).any()
+
+
 def test_keys_per_channel_values_per_token_axes():
     """Keys group along tokens for each channel, values along channels for each token."""
     rng = np.random.default_rng(9)
