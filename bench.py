@@ -1,0 +1,216 @@
+"""Decode benchmark of the 2-bit KIVI cache on one MI355X.
+
+One step = one decode step of the whole hot path: kivi_append_flush (the new token enters
+the fp16 residual; whenever the residual is already full, the oldest 32 residual tokens
+are first quantized into a new key/value group) followed by kivi_decode_attn (fused attention
+of one query per head over the packed history plus the residual, split-K with the
+log-sum-exp merge in the same launch).  Inputs are seeded synthetic tensors already
+resident in HBM when the timed region starts.
+
+Prints ONE JSON line.  Metric: achieved HBM GB/s (algorithmic bytes / time) and tokens/s.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-attn over 2-bit KV: achieved HBM GB/s (% of peak) and tokens/s at 1 GPU"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+D, G = 128, 32
+QUANT_TOKEN_BYTES = 96         # per kv head: 32 B key codes + 16 B key pairs + 32 B value codes + 16 B value pairs
+RES_TOKEN_BYTES = 512          # per kv head: fp16 key + value
+KERNEL = "attn_split_kernel"
+KERNEL_SOURCES = ["kv_cache_bit_quantize_amd/csrc/kivi_attn.hip", "kv_cache_bit_quantize_amd/csrc/kivi_device.h"]
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_attn_long-128k_counters.json")
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def attn_bytes(w, n_quant, n_res):
+    """Algorithmic HBM bytes of one decode-attention call: the packed history and the
+    residual read once per kv head, q read and out written once per query head."""
+    rows = w.batch * w.kv_heads
+    return rows * (n_quant * QUANT_TOKEN_BYTES + n_res * RES_TOKEN_BYTES) + 2 * w.batch * w.q_heads * D * 2
+
+
+def append_bytes(w, flushed):
+    """One append: read k_new, v_new and write them into the ring; a flush also reads 32
+    ring tokens of keys and values and writes one group of codes and pairs."""
+    rows = w.batch * w.kv_heads
+    b = rows * 4 * D * 2
+    if flushed:
+        b += rows * (G * RES_TOKEN_BYTES + G * QUANT_TOKEN_BYTES)
+    return b
+
+
+def cpu_baseline(w, k, v, n_heads, steps_tokens):
+    """Time the CPU oracle (as it stands, one thread) on a bounded sample: the first
+    n_heads kv heads of batch row 0, one decode step (append + attention)."""
+    from oracle import ref
+    from kv_cache_bit_quantize_amd import synth
+
+    def host_bits(t):
+        return t.contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+    rc = ref.RefCache(1, n_heads, D, G, w.residual_cap, token_cap=w.token_cap)
+    t0 = time.perf_counter()
+    rc.prefill(host_bits(k[0, :n_heads]), host_bits(v[0, :n_heads]), w.n_quant)
+    prefill_s = time.perf_counter() - t0
+    kn, vn = steps_tokens
+    q = host_bits(synth.query(w, step=1)[:1, :n_heads])
+    t0 = time.perf_counter()
+    flushed = rc.append(host_bits(kn[0, :n_heads]), host_bits(vn[0, :n_heads]))
+    rc.decode_attn(q, synth.SM_SCALE_D128)
+    step_s = time.perf_counter() - t0
+    nbytes = n_heads * (rc.n_quant * QUANT_TOKEN_BYTES + rc.n_res * RES_TOKEN_BYTES) + 2 * n_heads * D * 2 \
+        + n_heads * 4 * D * 2 + (n_heads * G * (RES_TOKEN_BYTES + QUANT_TOKEN_BYTES) if flushed else 0)
+    return {
+        "value": nbytes / step_s / 1e9,
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"one decode step (append + fp64 attention over the dequantized cache) of {n_heads} of the "
+                  f"{w.batch * w.kv_heads} kv heads of the {w.name} workload, single thread; "
+                  f"{step_s:.2f} s timed (oracle prefill of the sample {prefill_s:.1f} s, untimed)",
+        "tokens_per_s": (n_heads / (w.batch * w.kv_heads)) * w.batch / step_s,
+        "seconds": step_s,
+    }
+
+
+def read_traffic(attn_b):
+    """HBM bytes per launch from committed rocprofv3 counters, if they were taken on the
+    current kernel source; else None."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    with open(COUNTERS_FILE) as f:
+        c = json.load(f)
+    if c.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return c.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="long-128k")
+    ap.add_argument("--cpu-heads", type=int, default=12, help="kv heads in the CPU oracle sample (0: skip)")
+    ap.add_argument("--splits", type=int, default=0, help="split count override (0: library's choice)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the decode hot path shards "
+              "by batch or kv head with no communication, see DESIGN.md.", file=sys.stderr)
+        sys.exit(2)
+
+    from kv_cache_bit_quantize_amd import kivi, synth
+    w = synth.WORKLOADS[args.workload]
+    if w.layers != 1:
+        raise SystemExit("bench.py times single-layer workloads")
+    dev = torch.device("cuda:0")
+    total_steps = args.warmup + args.steps
+    if total_steps > w.token_cap - w.context:
+        import dataclasses
+        w = dataclasses.replace(w, decode_steps=total_steps)
+
+    k, v = synth.prefill_kv(w, device=dev)
+    cache = kivi.Cache(w.batch, w.kv_heads, w.token_cap, device=dev)
+    kivi.kivi_prefill(k, v, w.n_quant, cache)
+    steps_kv = [synth.step_kv(w, s, device=dev) for s in range(total_steps)]
+    queries = [synth.query(w, step=s + 1, device=dev) for s in range(total_steps)]
+    out = torch.empty_like(queries[0])
+    ws = cache.workspace(w.q_heads, args.splits)
+    torch.cuda.synchronize()
+
+    def step(s, ev=None):
+        if ev is not None:
+            ev[0].record()
+        f = kivi.kivi_append_flush(cache, *steps_kv[s])
+        if ev is not None:
+            ev[1].record()
+        state = cache.state
+        kivi.kivi_decode_attn(cache, queries[s], synth.SM_SCALE_D128, out=out, num_splits=args.splits,
+                              workspace=ws)
+        if ev is not None:
+            ev[2].record()
+        return f, state
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    flags, states = [], []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        f, st = step(args.warmup + i, evs[i])
+        flags.append(f)
+        states.append(st)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    attn_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    app_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    step_bytes = [attn_bytes(w, nq, nr) + append_bytes(w, f) for f, (nq, nr, _) in zip(flags, states)]
+    attn_b = [attn_bytes(w, nq, nr) for nq, nr, _ in states]
+    value = sum(step_bytes) / elapsed / 1e9
+    achieved = float(np.mean(attn_b)) / (attn_ms.mean() / 1e3) / 1e9
+    splits = kivi.kivi_decode_attn_splits(cache, w.q_heads) if args.splits == 0 else args.splits
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "batch": w.batch, "q_heads": w.q_heads, "kv_heads": w.kv_heads,
+            "head_dim": D, "group": G, "residual": w.residual_cap, "context_start": w.context,
+            "n_quant_start": w.n_quant, "splits": splits,
+        },
+        "pct_of_peak_hbm": round(100 * value / PEAK_HBM_GBS, 2),
+        "tokens_per_s": round(w.batch * args.steps / elapsed, 1),
+        "decode_attn_us": round(float(attn_ms.mean()) * 1e3, 2),
+        "append_flush_us": round(float(app_ms.mean()) * 1e3, 2),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": KERNEL,
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": read_traffic(float(np.mean(attn_b))),
+            "algorithmic_bytes_per_launch": int(np.mean(attn_b)),
+        },
+        "cpu_baseline": None,
+    }
+    if args.cpu_heads > 0:
+        kn, vn = steps_kv[0]
+        res["cpu_baseline"] = cpu_baseline(w, k, v, min(args.cpu_heads, w.kv_heads), (kn, vn))
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

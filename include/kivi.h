@@ -121,9 +121,13 @@ int kivi_append_flush(kivi_cache* cache, const uint16_t* k_new, const uint16_t* 
  * head hq / (q_heads / kv_heads).  out: fp16 [batch][q_heads][D].  lse (nullable): fp32
  * [batch][q_heads], natural log of the softmax denominator including sm_scale.
  * The context is split into num_splits parts per row (0 = automatic) and the partial
- * softmax states are merged with a log-sum-exp merge.  workspace: device scratch of at
- * least kivi_decode_attn_workspace(cache, q_heads, num_splits) bytes, 256-byte aligned.
- * KIVI_ERR_SHAPE if the context is empty. */
+ * softmax states are merged with a log-sum-exp merge inside the same kernel launch.
+ * workspace: device scratch of at least kivi_decode_attn_workspace(cache, q_heads,
+ * num_splits) bytes, 256-byte aligned, owned by the caller.  Its first
+ * round_up(batch*q_heads*4, 256) bytes are per-row arrival counters that must be zero
+ * before the first call that uses the workspace (clear it once after allocating it);
+ * every completed call leaves them zero again.  Calls that share a workspace must not
+ * run concurrently.  KIVI_ERR_SHAPE if the context is empty. */
 int kivi_decode_attn(const kivi_cache* cache, const uint16_t* q, int32_t q_heads,
                      float sm_scale, uint16_t* out, float* lse, void* workspace,
                      size_t workspace_bytes, int32_t num_splits, void* stream);

@@ -1,0 +1,296 @@
+// kivi_api.hip -- the extern "C" entry points of libkivi (declared in include/kivi.h).
+//
+// Every entry point validates its arguments on the host before it touches the HIP
+// runtime, so the error paths run without a GPU.  Kernels are only enqueued on the
+// caller's stream; nothing here allocates or synchronises.
+#include "kivi.h"
+#include "kivi_device.h"
+#include "kivi_internal.h"
+
+#include <cmath>
+
+using namespace kivi;
+
+namespace {
+
+constexpr int kMaxSplits = 1024;
+constexpr int64_t kTargetBlocks = 1024;     // ~4 workgroups of 4 waves per CU on 256 CUs
+constexpr int kMinGroupsPerSplit = 8;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_shape(const kivi_cache* c) {
+    if (c == nullptr) return KIVI_ERR_NULL;
+    if (c->batch <= 0 || c->kv_heads <= 0 || c->head_dim <= 0 || c->group <= 0 ||
+        c->residual_cap <= 0 || c->token_cap < 0 || c->reserved != 0)
+        return KIVI_ERR_SHAPE;
+    if (c->head_dim % 4 != 0 || c->head_dim % c->group != 0 || c->residual_cap % c->group != 0 ||
+        c->token_cap % c->group != 0)
+        return KIVI_ERR_SHAPE;
+    if (c->head_dim != kD || c->group != kG) return KIVI_ERR_UNSUPPORTED;
+    return KIVI_OK;
+}
+
+int check_state(const kivi_cache* c) {
+    const int G = c->group, R = c->residual_cap;
+    if (c->n_quant < 0 || c->n_quant % G != 0 || c->n_quant > c->token_cap) return KIVI_ERR_STATE;
+    if (c->n_res < 0 || c->n_res > R) return KIVI_ERR_STATE;
+    if (c->res_head < 0 || c->res_head >= R || c->res_head % G != 0) return KIVI_ERR_STATE;
+    return KIVI_OK;
+}
+
+int check_quant_bufs(const kivi_cache* c, bool keys, bool values) {
+    if (keys && (c->k_codes == nullptr || c->k_sz == nullptr)) return KIVI_ERR_NULL;
+    if (values && (c->v_codes == nullptr || c->v_sz == nullptr)) return KIVI_ERR_NULL;
+    if (keys && (!aligned16(c->k_codes) || !aligned16(c->k_sz))) return KIVI_ERR_SHAPE;
+    if (values && (!aligned16(c->v_codes) || !aligned16(c->v_sz))) return KIVI_ERR_SHAPE;
+    return KIVI_OK;
+}
+
+int check_res_bufs(const kivi_cache* c) {
+    if (c->k_res == nullptr || c->v_res == nullptr) return KIVI_ERR_NULL;
+    if (!aligned16(c->k_res) || !aligned16(c->v_res)) return KIVI_ERR_SHAPE;
+    return KIVI_OK;
+}
+
+int64_t rows_of(const kivi_cache* c) { return (int64_t)c->batch * c->kv_heads; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? KIVI_OK : KIVI_ERR_HIP; }
+
+int32_t auto_splits(const kivi_cache* c, int32_t q_heads) {
+    const int64_t rows = (int64_t)c->batch * q_heads;
+    const int64_t groups = c->n_quant / c->group;
+    int64_t s = (kTargetBlocks + rows - 1) / rows;
+    const int64_t cap = groups / kMinGroupsPerSplit;
+    if (s > cap) s = cap;
+    if (s < 1) s = 1;
+    if (s > kMaxSplits) s = kMaxSplits;
+    return (int32_t)s;
+}
+
+// leading area of the attention workspace: one arrival counter per query row
+size_t counter_bytes(const kivi_cache* c, int32_t q_heads) {
+    return ((size_t)c->batch * (size_t)q_heads * sizeof(uint32_t) + 255) & ~(size_t)255;
+}
+
+QuantArgs quant_args(const kivi_cache* c, const uint16_t* src, int32_t tokens, int64_t stride,
+                     int32_t dst) {
+    QuantArgs a;
+    a.src = src;
+    a.src_row_stride = stride;
+    a.rows = rows_of(c);
+    a.tokens = tokens;
+    a.dst_token_off = dst;
+    a.token_cap = c->token_cap;
+    a.k_codes = c->k_codes;
+    a.v_codes = c->v_codes;
+    a.k_sz = c->k_sz;
+    a.v_sz = c->v_sz;
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kivi_status_str(int status) {
+    switch (status) {
+        case KIVI_OK: return "ok";
+        case KIVI_ERR_NULL: return "a required pointer is NULL";
+        case KIVI_ERR_SHAPE: return "inconsistent sizes, strides or alignment";
+        case KIVI_ERR_UNSUPPORTED: return "shape not implemented (head_dim must be 128, group 32)";
+        case KIVI_ERR_CAPACITY: return "the call would write past token_cap";
+        case KIVI_ERR_WORKSPACE: return "workspace missing or too small";
+        case KIVI_ERR_HIP: return "HIP runtime error while enqueueing";
+        case KIVI_ERR_STATE: return "inconsistent cache state (n_quant, n_res, res_head)";
+        default: return "unknown status";
+    }
+}
+
+int kivi_cache_bytes(const kivi_cache* shape, size_t* codes, size_t* pairs, size_t* residual) {
+    int st = check_shape(shape);
+    if (st != KIVI_OK) return st;
+    if (codes == nullptr || pairs == nullptr || residual == nullptr) return KIVI_ERR_NULL;
+    const int64_t rows = rows_of(shape), D = shape->head_dim, G = shape->group;
+    const int64_t T = shape->token_cap, R = shape->residual_cap;
+    *codes = (size_t)(2 * rows * T * (D / 4));
+    *pairs = (size_t)(rows * (T / G) * D * 4 + rows * T * (D / G) * 4);
+    *residual = (size_t)(2 * rows * R * D * 2);
+    return KIVI_OK;
+}
+
+int kivi_quantize_k_per_channel(const uint16_t* k, int32_t tokens, int64_t src_row_stride,
+                                kivi_cache* c, int32_t dst_token_off, void* stream) {
+    int st = check_shape(c);
+    if (st != KIVI_OK) return st;
+    if ((st = check_quant_bufs(c, true, false)) != KIVI_OK) return st;
+    if (tokens < 0 || dst_token_off < 0 || tokens % c->group != 0 || dst_token_off % c->group != 0)
+        return KIVI_ERR_SHAPE;
+    if ((int64_t)dst_token_off + tokens > c->token_cap) return KIVI_ERR_CAPACITY;
+    if (tokens == 0) return KIVI_OK;
+    if (k == nullptr) return KIVI_ERR_NULL;
+    if (src_row_stride < (int64_t)tokens * c->head_dim || src_row_stride % 8 != 0 || !aligned16(k))
+        return KIVI_ERR_SHAPE;
+    return hip_status(launch_quantize_k(quant_args(c, k, tokens, src_row_stride, dst_token_off),
+                                        (hipStream_t)stream));
+}
+
+int kivi_quantize_v_per_token(const uint16_t* v, int32_t tokens, int64_t src_row_stride,
+                              kivi_cache* c, int32_t dst_token_off, void* stream) {
+    int st = check_shape(c);
+    if (st != KIVI_OK) return st;
+    if ((st = check_quant_bufs(c, false, true)) != KIVI_OK) return st;
+    if (tokens < 0 || dst_token_off < 0) return KIVI_ERR_SHAPE;
+    if ((int64_t)dst_token_off + tokens > c->token_cap) return KIVI_ERR_CAPACITY;
+    if (tokens == 0) return KIVI_OK;
+    if (v == nullptr) return KIVI_ERR_NULL;
+    if (src_row_stride < (int64_t)tokens * c->head_dim || src_row_stride % 8 != 0 || !aligned16(v))
+        return KIVI_ERR_SHAPE;
+    return hip_status(launch_quantize_v(quant_args(c, v, tokens, src_row_stride, dst_token_off),
+                                        (hipStream_t)stream));
+}
+
+int kivi_prefill(const uint16_t* k, const uint16_t* v, int32_t tokens, int64_t src_row_stride,
+                 int32_t n_quant, kivi_cache* c, void* stream) {
+    int st = check_shape(c);
+    if (st != KIVI_OK) return st;
+    if ((st = check_quant_bufs(c, true, true)) != KIVI_OK) return st;
+    if ((st = check_res_bufs(c)) != KIVI_OK) return st;
+    if (tokens < 0 || n_quant < 0 || n_quant > tokens || n_quant % c->group != 0) return KIVI_ERR_SHAPE;
+    if (n_quant > c->token_cap || tokens - n_quant > c->residual_cap) return KIVI_ERR_CAPACITY;
+    if (tokens > 0) {
+        if (k == nullptr || v == nullptr) return KIVI_ERR_NULL;
+        if (src_row_stride < (int64_t)tokens * c->head_dim || src_row_stride % 8 != 0 || !aligned16(k) ||
+            !aligned16(v))
+            return KIVI_ERR_SHAPE;
+    }
+    hipStream_t s = (hipStream_t)stream;
+    if (n_quant > 0) {
+        if ((st = hip_status(launch_quantize_k(quant_args(c, k, n_quant, src_row_stride, 0), s))) != KIVI_OK)
+            return st;
+        if ((st = hip_status(launch_quantize_v(quant_args(c, v, n_quant, src_row_stride, 0), s))) != KIVI_OK)
+            return st;
+    }
+    if (tokens > n_quant) {
+        ResidualArgs r;
+        r.k = k;
+        r.v = v;
+        r.src_row_stride = src_row_stride;
+        r.rows = rows_of(c);
+        r.first = n_quant;
+        r.n = tokens - n_quant;
+        r.residual_cap = c->residual_cap;
+        r.k_res = c->k_res;
+        r.v_res = c->v_res;
+        if ((st = hip_status(launch_residual_load(r, s))) != KIVI_OK) return st;
+    }
+    c->n_quant = n_quant;
+    c->n_res = tokens - n_quant;
+    c->res_head = 0;
+    return KIVI_OK;
+}
+
+int kivi_append_flush(kivi_cache* c, const uint16_t* k_new, const uint16_t* v_new, int32_t* flushed,
+                      void* stream) {
+    int st = check_shape(c);
+    if (st != KIVI_OK) return st;
+    if ((st = check_state(c)) != KIVI_OK) return st;
+    if ((st = check_quant_bufs(c, true, true)) != KIVI_OK) return st;
+    if ((st = check_res_bufs(c)) != KIVI_OK) return st;
+    if (k_new == nullptr || v_new == nullptr) return KIVI_ERR_NULL;
+    if (!aligned16(k_new) || !aligned16(v_new)) return KIVI_ERR_SHAPE;
+    const int G = c->group, R = c->residual_cap;
+    const bool flush = c->n_res == R;
+    if (flush && c->n_quant + G > c->token_cap) return KIVI_ERR_CAPACITY;
+    int n_quant = c->n_quant, n_res = c->n_res, head = c->res_head;
+    AppendArgs a;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.rows = rows_of(c);
+    a.do_flush = flush ? 1 : 0;
+    a.flush_slot = head;
+    a.flush_group = n_quant / G;
+    if (flush) {
+        n_quant += G;
+        head = (head + G) % R;
+        n_res -= G;
+    }
+    a.new_slot = (head + n_res) % R;
+    a.token_cap = c->token_cap;
+    a.residual_cap = R;
+    a.k_codes = c->k_codes;
+    a.v_codes = c->v_codes;
+    a.k_sz = c->k_sz;
+    a.v_sz = c->v_sz;
+    a.k_res = c->k_res;
+    a.v_res = c->v_res;
+    if ((st = hip_status(launch_append_flush(a, (hipStream_t)stream))) != KIVI_OK) return st;
+    c->n_quant = n_quant;
+    c->n_res = n_res + 1;
+    c->res_head = head;
+    if (flushed != nullptr) *flushed = flush ? 1 : 0;
+    return KIVI_OK;
+}
+
+int32_t kivi_decode_attn_splits(const kivi_cache* c, int32_t q_heads) {
+    int st = check_shape(c);
+    if (st != KIVI_OK) return st;
+    if ((st = check_state(c)) != KIVI_OK) return st;
+    if (q_heads <= 0 || q_heads % c->kv_heads != 0) return KIVI_ERR_SHAPE;
+    return auto_splits(c, q_heads);
+}
+
+size_t kivi_decode_attn_workspace(const kivi_cache* c, int32_t q_heads, int32_t num_splits) {
+    if (check_shape(c) != KIVI_OK || q_heads <= 0) return 0;
+    const int32_t s = num_splits > 0 ? num_splits : auto_splits(c, q_heads);
+    const size_t bytes = (size_t)s * (size_t)c->batch * (size_t)q_heads * (size_t)(c->head_dim + 2) * sizeof(float);
+    return counter_bytes(c, q_heads) + ((bytes + 255) & ~(size_t)255);
+}
+
+int kivi_decode_attn(const kivi_cache* c, const uint16_t* q, int32_t q_heads, float sm_scale, uint16_t* out,
+                     float* lse, void* workspace, size_t workspace_bytes, int32_t num_splits, void* stream) {
+    int st = check_shape(c);
+    if (st != KIVI_OK) return st;
+    if ((st = check_state(c)) != KIVI_OK) return st;
+    if ((st = check_quant_bufs(c, true, true)) != KIVI_OK) return st;
+    if ((st = check_res_bufs(c)) != KIVI_OK) return st;
+    if (q == nullptr || out == nullptr) return KIVI_ERR_NULL;
+    if (!aligned16(q) || (reinterpret_cast<uintptr_t>(out) & 1u) || (reinterpret_cast<uintptr_t>(lse) & 3u))
+        return KIVI_ERR_SHAPE;
+    if (q_heads <= 0 || q_heads % c->kv_heads != 0) return KIVI_ERR_SHAPE;
+    if (c->n_quant + c->n_res == 0) return KIVI_ERR_SHAPE;
+    if (num_splits < 0 || num_splits > kMaxSplits) return KIVI_ERR_SHAPE;
+    if (!std::isfinite(sm_scale)) return KIVI_ERR_SHAPE;
+    const int32_t splits = num_splits > 0 ? num_splits : auto_splits(c, q_heads);
+    const size_t need = kivi_decode_attn_workspace(c, q_heads, splits);
+    if (workspace == nullptr || workspace_bytes < need) return KIVI_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return KIVI_ERR_WORKSPACE;
+    const int32_t groups = c->n_quant / c->group;
+    AttnArgs a;
+    a.q = q;
+    a.k_codes = c->k_codes;
+    a.v_codes = c->v_codes;
+    a.k_sz = c->k_sz;
+    a.v_sz = c->v_sz;
+    a.k_res = c->k_res;
+    a.v_res = c->v_res;
+    a.counters = static_cast<uint32_t*>(workspace);
+    a.ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + counter_bytes(c, q_heads));
+    a.out = out;
+    a.lse = lse;
+    a.sm_log2 = (float)((double)sm_scale * 1.4426950408889634);
+    a.q_heads = q_heads;
+    a.kv_heads = c->kv_heads;
+    a.ratio = q_heads / c->kv_heads;
+    a.token_cap = c->token_cap;
+    a.residual_cap = c->residual_cap;
+    a.n_quant = c->n_quant;
+    a.n_res = c->n_res;
+    a.res_head = c->res_head;
+    a.splits = splits;
+    a.groups_per_split = (groups + splits - 1) / splits;
+    a.q_rows = (int64_t)c->batch * q_heads;
+    return hip_status(launch_decode_attn(a, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,72 @@
+// kivi_internal.h -- kernel argument blocks and launchers inside libkivi.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kivi {
+
+struct QuantArgs {          // kivi_quantize_{k,v}
+    const uint16_t* src;
+    int64_t src_row_stride;
+    int64_t rows;
+    int32_t tokens;
+    int32_t dst_token_off;
+    int32_t token_cap;
+    uint8_t* k_codes;
+    uint8_t* v_codes;
+    uint16_t* k_sz;
+    uint16_t* v_sz;
+};
+
+struct ResidualArgs {       // prefill: tokens [first, first+n) -> ring slots [0, n)
+    const uint16_t* k;
+    const uint16_t* v;
+    int64_t src_row_stride;
+    int64_t rows;
+    int32_t first, n, residual_cap;
+    uint16_t* k_res;
+    uint16_t* v_res;
+};
+
+struct AppendArgs {
+    const uint16_t* k_new;
+    const uint16_t* v_new;
+    int64_t rows;
+    int32_t do_flush, flush_slot, flush_group, new_slot;
+    int32_t token_cap, residual_cap;
+    uint8_t* k_codes;
+    uint8_t* v_codes;
+    uint16_t* k_sz;
+    uint16_t* v_sz;
+    uint16_t* k_res;
+    uint16_t* v_res;
+};
+
+struct AttnArgs {
+    const uint16_t* q;          // [B][Hq][D]
+    const uint8_t* k_codes;
+    const uint8_t* v_codes;
+    const uint16_t* k_sz;
+    const uint16_t* v_sz;
+    const uint16_t* k_res;
+    const uint16_t* v_res;
+    float* ws;                  // [splits][B*Hq][D+2] partial (o, m, l), log2 domain
+    uint32_t* counters;         // [B*Hq] arrival counters, zero between calls
+    uint16_t* out;              // [B][Hq][D]
+    float* lse;                 // [B][Hq] or null
+    float sm_log2;              // sm_scale * log2(e)
+    int32_t q_heads, kv_heads, ratio;
+    int32_t token_cap, residual_cap;
+    int32_t n_quant, n_res, res_head;
+    int32_t splits, groups_per_split;
+    int64_t q_rows;             // B * Hq
+};
+
+hipError_t launch_quantize_k(const QuantArgs& a, hipStream_t s);
+hipError_t launch_quantize_v(const QuantArgs& a, hipStream_t s);
+hipError_t launch_residual_load(const ResidualArgs& a, hipStream_t s);
+hipError_t launch_append_flush(const AppendArgs& a, hipStream_t s);
+hipError_t launch_decode_attn(const AttnArgs& a, hipStream_t s);
+
+}  // namespace kivi

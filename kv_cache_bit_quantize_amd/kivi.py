@@ -1,0 +1,188 @@
+"""Python binding of libkivi (include/kivi.h): argument marshalling only.
+
+PyTorch supplies device memory and streams; every step of the quantize / append /
+attention path runs in libkivi's HIP kernels.  There is no fallback: if libkivi.so is
+missing, importing this module fails.
+"""
+import ctypes as C
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkivi.so")
+
+KIVI_OK = 0
+_STATUS_NAMES = {0: "KIVI_OK", -1: "KIVI_ERR_NULL", -2: "KIVI_ERR_SHAPE", -3: "KIVI_ERR_UNSUPPORTED",
+                 -4: "KIVI_ERR_CAPACITY", -5: "KIVI_ERR_WORKSPACE", -6: "KIVI_ERR_HIP", -7: "KIVI_ERR_STATE"}
+
+EXPORTS = ["kivi_quantize_k_per_channel", "kivi_quantize_v_per_token", "kivi_prefill", "kivi_append_flush",
+           "kivi_decode_attn", "kivi_decode_attn_splits", "kivi_decode_attn_workspace", "kivi_cache_bytes",
+           "kivi_status_str"]
+
+
+class KiviError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {_STATUS_NAMES.get(status, status)} ({status_str(status)})")
+
+
+class kivi_cache(C.Structure):
+    _fields_ = [
+        ("batch", C.c_int32), ("kv_heads", C.c_int32), ("head_dim", C.c_int32), ("group", C.c_int32),
+        ("residual_cap", C.c_int32), ("token_cap", C.c_int32),
+        ("n_quant", C.c_int32), ("n_res", C.c_int32), ("res_head", C.c_int32), ("reserved", C.c_int32),
+        ("k_codes", C.c_void_p), ("v_codes", C.c_void_p), ("k_sz", C.c_void_p), ("v_sz", C.c_void_p),
+        ("k_res", C.c_void_p), ("v_res", C.c_void_p),
+    ]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libkivi.so is not built ({LIB_PATH}); run __graft_entry__.build()")
+    L = C.CDLL(LIB_PATH)
+    p, i32, i64, cp = C.c_void_p, C.c_int32, C.c_int64, C.POINTER(kivi_cache)
+    L.kivi_quantize_k_per_channel.argtypes = [p, i32, i64, cp, i32, p]
+    L.kivi_quantize_v_per_token.argtypes = [p, i32, i64, cp, i32, p]
+    L.kivi_prefill.argtypes = [p, p, i32, i64, i32, cp, p]
+    L.kivi_append_flush.argtypes = [cp, p, p, C.POINTER(i32), p]
+    L.kivi_decode_attn.argtypes = [cp, p, i32, C.c_float, p, p, p, C.c_size_t, i32, p]
+    L.kivi_decode_attn_splits.argtypes = [cp, i32]
+    L.kivi_decode_attn_splits.restype = i32
+    L.kivi_decode_attn_workspace.argtypes = [cp, i32, i32]
+    L.kivi_decode_attn_workspace.restype = C.c_size_t
+    L.kivi_cache_bytes.argtypes = [cp, C.POINTER(C.c_size_t), C.POINTER(C.c_size_t), C.POINTER(C.c_size_t)]
+    L.kivi_status_str.argtypes = [C.c_int]
+    L.kivi_status_str.restype = C.c_char_p
+    for name in EXPORTS:
+        L[name].restype = L[name].restype if name in ("kivi_decode_attn_splits", "kivi_decode_attn_workspace",
+                                                      "kivi_status_str") else C.c_int
+    return L
+
+
+lib = _load()
+
+
+def status_str(status):
+    return lib.kivi_status_str(int(status)).decode()
+
+
+def _check(status, where):
+    if status != KIVI_OK:
+        raise KiviError(status, where)
+
+
+def _stream(t):
+    return C.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return C.c_void_p(t.data_ptr()) if t is not None else None
+
+
+class Cache:
+    """Device buffers of one KIVI cache (layout of include/kivi.h) and its descriptor."""
+
+    def __init__(self, batch, kv_heads, token_cap, head_dim=128, group=32, residual_cap=128, device="cuda"):
+        rows = batch * kv_heads
+        u8, f16 = torch.uint8, torch.int16
+        self.k_codes = torch.zeros((rows, token_cap, head_dim // 4), dtype=u8, device=device)
+        self.v_codes = torch.zeros((rows, token_cap, head_dim // 4), dtype=u8, device=device)
+        self.k_sz = torch.zeros((rows, token_cap // group, head_dim, 2), dtype=f16, device=device)
+        self.v_sz = torch.zeros((rows, token_cap, head_dim // group, 2), dtype=f16, device=device)
+        self.k_res = torch.zeros((rows, residual_cap, head_dim), dtype=f16, device=device)
+        self.v_res = torch.zeros((rows, residual_cap, head_dim), dtype=f16, device=device)
+        self.c = kivi_cache(batch, kv_heads, head_dim, group, residual_cap, token_cap, 0, 0, 0, 0,
+                            self.k_codes.data_ptr(), self.v_codes.data_ptr(), self.k_sz.data_ptr(),
+                            self.v_sz.data_ptr(), self.k_res.data_ptr(), self.v_res.data_ptr())
+        self.device = torch.device(device)
+        self._ws = None
+
+    @property
+    def state(self):
+        return self.c.n_quant, self.c.n_res, self.c.res_head
+
+    def set_state(self, n_quant, n_res, res_head):
+        self.c.n_quant, self.c.n_res, self.c.res_head = n_quant, n_res, res_head
+
+    def workspace(self, q_heads, num_splits=0):
+        need = lib.kivi_decode_attn_workspace(C.byref(self.c), q_heads, num_splits)
+        if self._ws is None or self._ws.numel() < need:
+            # zero-filled: the leading per-row arrival counters must start at zero
+            self._ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=self.device)
+        return self._ws
+
+
+def _src(t):
+    """fp16 [B, H, T, D] (T*D contiguous per row) -> (pointer, tokens, row stride)."""
+    if t.dtype != torch.float16:
+        raise TypeError("expected float16")
+    if t.dim() != 4 or not (t.stride(3) == 1 and t.stride(2) == t.shape[3] and t.stride(0) == t.stride(1) * t.shape[1]):
+        raise ValueError("expected [B, H, T, D] with each (b, h) row's T*D contiguous and a common row stride")
+    return _ptr(t), t.shape[2], t.stride(1)
+
+
+def kivi_quantize_k_per_channel(k, cache, dst_token_off=0):
+    p, T, stride = _src(k)
+    _check(lib.kivi_quantize_k_per_channel(p, T, stride, C.byref(cache.c), dst_token_off, _stream(k)),
+           "kivi_quantize_k_per_channel")
+
+
+def kivi_quantize_v_per_token(v, cache, dst_token_off=0):
+    p, T, stride = _src(v)
+    _check(lib.kivi_quantize_v_per_token(p, T, stride, C.byref(cache.c), dst_token_off, _stream(v)),
+           "kivi_quantize_v_per_token")
+
+
+def kivi_prefill(k, v, n_quant, cache):
+    pk, T, stride = _src(k)
+    pv, Tv, stride_v = _src(v)
+    if (T, stride) != (Tv, stride_v):
+        raise ValueError("k and v must have the same shape and strides")
+    _check(lib.kivi_prefill(pk, pv, T, stride, n_quant, C.byref(cache.c), _stream(k)), "kivi_prefill")
+
+
+def kivi_append_flush(cache, k_new, v_new):
+    """k_new, v_new: fp16 [B, Hkv, D] contiguous. Returns True if a group was flushed."""
+    if not (k_new.is_contiguous() and v_new.is_contiguous()) or k_new.dtype != torch.float16:
+        raise ValueError("expected contiguous float16 [B, Hkv, D]")
+    flushed = C.c_int32(0)
+    _check(lib.kivi_append_flush(C.byref(cache.c), _ptr(k_new), _ptr(v_new), C.byref(flushed), _stream(k_new)),
+           "kivi_append_flush")
+    return bool(flushed.value)
+
+
+def kivi_decode_attn(cache, q, sm_scale, out=None, lse=None, num_splits=0, workspace=None):
+    """q: fp16 [B, Hq, D] contiguous. Returns out fp16 [B, Hq, D] (and lse fp32 [B, Hq] if
+    `lse` is True or a tensor)."""
+    if not q.is_contiguous() or q.dtype != torch.float16:
+        raise ValueError("expected contiguous float16 q [B, Hq, D]")
+    B, Hq, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    want_lse = lse is not None and lse is not False
+    if lse is True:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    ws = workspace if workspace is not None else cache.workspace(Hq, num_splits)
+    _check(lib.kivi_decode_attn(C.byref(cache.c), _ptr(q), Hq, float(sm_scale), _ptr(out),
+                                _ptr(lse) if want_lse else None, _ptr(ws), ws.numel() * ws.element_size(),
+                                num_splits, _stream(q)), "kivi_decode_attn")
+    return (out, lse) if want_lse else out
+
+
+def kivi_decode_attn_splits(cache, q_heads):
+    s = lib.kivi_decode_attn_splits(C.byref(cache.c), q_heads)
+    if s < 0:
+        raise KiviError(s, "kivi_decode_attn_splits")
+    return s
+
+
+def kivi_decode_attn_workspace(cache, q_heads, num_splits=0):
+    return lib.kivi_decode_attn_workspace(C.byref(cache.c), q_heads, num_splits)
+
+
+def kivi_cache_bytes(cache_or_struct):
+    c = cache_or_struct.c if isinstance(cache_or_struct, Cache) else cache_or_struct
+    a, b, d = C.c_size_t(), C.c_size_t(), C.c_size_t()
+    _check(lib.kivi_cache_bytes(C.byref(c), C.byref(a), C.byref(b), C.byref(d)), "kivi_cache_bytes")
+    return a.value, b.value, d.value

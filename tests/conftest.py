@@ -17,3 +17,17 @@ def pytest_configure(config):
 def oracle_lib():
     from oracle import ref
     return ref.lib()
+
+
+def pytest_sessionfinish(session, exitstatus):
+    """Write the worst attention errors seen by the GPU parity tests (if any ran)."""
+    try:
+        from kivi_testlib import REPORT
+    except Exception:
+        return
+    if REPORT:
+        import json
+        out = os.path.join(ROOT, "gpurun_out")
+        os.makedirs(out, exist_ok=True)
+        with open(os.path.join(out, "parity_report.json"), "w") as f:
+            json.dump(dict(sorted(REPORT.items())), f, indent=1)

@@ -1,0 +1,156 @@
+"""CPU tests of the C ABI: the library loads, exports every declared entry point, and
+rejects bad arguments on the host, before any HIP call, leaving the cache state as it
+was.  No kernel is launched here (no GPU in this environment)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from kv_cache_bit_quantize_amd import kivi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+L = kivi.lib
+FAKE = 0x7F0000000000          # aligned, never dereferenced (validation fails first)
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "kivi.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:int|int32_t|size_t|const char\*)\s+(kivi_\w+)\s*\(", text, re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert len(names) == 9
+    out = os.popen(f"nm -D --defined-only {kivi.LIB_PATH}").read()
+    exported = set(re.findall(r" T (kivi_\w+)$", out, re.M))
+    assert set(names) <= exported, set(names) - exported
+    for n in names:
+        assert hasattr(L, n)
+
+
+def _cache(**kw):
+    f = dict(batch=2, kv_heads=2, head_dim=128, group=32, residual_cap=128, token_cap=256,
+             n_quant=64, n_res=10, res_head=0, reserved=0)
+    f.update({k: v for k, v in kw.items() if k in f})
+    c = kivi.kivi_cache(*[f[k] for k in ("batch", "kv_heads", "head_dim", "group", "residual_cap",
+                                         "token_cap", "n_quant", "n_res", "res_head", "reserved")])
+    for name in ("k_codes", "v_codes", "k_sz", "v_sz", "k_res", "v_res"):
+        setattr(c, name, kw.get(name, FAKE))
+    return c
+
+
+def _state(c):
+    return c.n_quant, c.n_res, c.res_head
+
+
+def test_status_strings():
+    for s in range(0, -8, -1):
+        assert kivi.status_str(s) and kivi.status_str(s) != "unknown status"
+    assert kivi.status_str(-99) == "unknown status"
+
+
+def test_cache_bytes_matches_layout():
+    c = _cache(batch=3, kv_heads=4, token_cap=4096)
+    codes, pairs, res = kivi.kivi_cache_bytes(c)
+    rows = 12
+    assert codes == 2 * rows * 4096 * 32
+    assert pairs == rows * 128 * 128 * 4 + rows * 4096 * 4 * 4
+    assert res == 2 * rows * 128 * 128 * 2
+    # 96 bytes per quantized token per head: 64 code bytes + 32 pair bytes
+    assert (codes + pairs) // (rows * 4096) == 96
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=64), -3),
+    (dict(group=16), -3),
+    (dict(head_dim=100), -2),
+    (dict(token_cap=100), -2),
+    (dict(residual_cap=100), -2),
+    (dict(batch=0), -2),
+    (dict(reserved=1), -2),
+])
+def test_shape_validation(kw, code):
+    c = _cache(**kw)
+    assert L.kivi_decode_attn_splits(C.byref(c), 2) == code
+    assert L.kivi_quantize_k_per_channel(C.c_void_p(FAKE), 32, 32 * 128, C.byref(c), 0, None) == code
+
+
+def test_quantize_argument_errors():
+    c = _cache()
+    st = _state(c)
+    q = lambda *a: L.kivi_quantize_k_per_channel(*a)
+    assert q(C.c_void_p(FAKE), 33, 33 * 128, C.byref(c), 0, None) == -2          # tokens % G
+    assert q(C.c_void_p(FAKE), 32, 32 * 128, C.byref(c), 16, None) == -2         # dst % G
+    assert q(C.c_void_p(FAKE), 64, 64 * 128, C.byref(c), 224, None) == -4        # past token_cap
+    assert q(None, 32, 32 * 128, C.byref(c), 0, None) == -1
+    assert q(C.c_void_p(FAKE), 32, 31 * 128, C.byref(c), 0, None) == -2          # stride too small
+    assert q(C.c_void_p(FAKE + 2), 32, 32 * 128, C.byref(c), 0, None) == -2      # misaligned
+    assert q(C.c_void_p(FAKE), 0, 0, C.byref(c), 0, None) == 0                   # empty is a no-op
+    assert q(C.c_void_p(FAKE), 32, 32 * 128, None, 0, None) == -1
+    v = lambda *a: L.kivi_quantize_v_per_token(*a)
+    assert v(C.c_void_p(FAKE), 250, 250 * 128, C.byref(c), 10, None) == -4
+    assert v(C.c_void_p(FAKE), -1, 0, C.byref(c), 0, None) == -2
+    c2 = _cache(v_codes=0)
+    assert v(C.c_void_p(FAKE), 1, 128, C.byref(c2), 0, None) == -1
+    assert _state(c) == st
+
+
+def test_prefill_argument_errors_leave_state():
+    c = _cache()
+    st = _state(c)
+    p = lambda *a: L.kivi_prefill(*a)
+    assert p(C.c_void_p(FAKE), C.c_void_p(FAKE), 300, 300 * 128, 100, C.byref(c), None) == -2  # n_quant % G
+    assert p(C.c_void_p(FAKE), C.c_void_p(FAKE), 300, 300 * 128, 128, C.byref(c), None) == -4  # residual > R
+    assert p(C.c_void_p(FAKE), C.c_void_p(FAKE), 600, 600 * 128, 512, C.byref(c), None) == -4  # > token_cap
+    assert p(C.c_void_p(FAKE), None, 64, 64 * 128, 32, C.byref(c), None) == -1
+    assert p(C.c_void_p(FAKE), C.c_void_p(FAKE), 64, 64 * 128, 96, C.byref(c), None) == -2     # n_quant > tokens
+    assert _state(c) == st
+
+
+def test_append_flush_errors_leave_state():
+    flushed = C.c_int32(7)
+    full = _cache(n_quant=256, n_res=128, res_head=32)       # flush needed, no room
+    st = _state(full)
+    assert L.kivi_append_flush(C.byref(full), C.c_void_p(FAKE), C.c_void_p(FAKE), C.byref(flushed), None) == -4
+    assert _state(full) == st and flushed.value == 7
+    for bad in (dict(n_quant=33), dict(n_res=129), dict(res_head=16), dict(res_head=128), dict(n_quant=288)):
+        c = _cache(**bad)
+        st = _state(c)
+        assert L.kivi_append_flush(C.byref(c), C.c_void_p(FAKE), C.c_void_p(FAKE), None, None) == -7
+        assert _state(c) == st
+    c = _cache()
+    assert L.kivi_append_flush(C.byref(c), None, C.c_void_p(FAKE), None, None) == -1
+    assert L.kivi_append_flush(C.byref(c), C.c_void_p(FAKE + 8), C.c_void_p(FAKE), None, None) == -2
+    c = _cache(k_res=0)
+    assert L.kivi_append_flush(C.byref(c), C.c_void_p(FAKE), C.c_void_p(FAKE), None, None) == -1
+
+
+def test_decode_attn_argument_errors():
+    c = _cache()
+    ws_need = L.kivi_decode_attn_workspace(C.byref(c), 4, 0)
+    a = lambda cache, q_heads=4, ws=FAKE, wsb=1 << 30, splits=0, q=FAKE, out=FAKE, sm=0.088: L.kivi_decode_attn(
+        C.byref(cache), C.c_void_p(q), q_heads, sm, C.c_void_p(out), None, C.c_void_p(ws), wsb, splits, None)
+    assert a(c, q_heads=3) == -2                        # not a multiple of kv_heads
+    assert a(c, q=0) == -1
+    assert a(c, out=0) == -1
+    assert a(c, ws=0) == -5
+    assert a(c, wsb=ws_need - 1) == -5
+    assert a(c, ws=FAKE + 64) == -5                     # workspace alignment
+    assert a(c, splits=-1) == -2
+    assert a(c, splits=5000) == -2
+    assert a(c, sm=float("inf")) == -2
+    assert a(_cache(n_quant=0, n_res=0)) == -2          # empty context
+    assert a(_cache(n_res=200)) == -7
+
+
+def test_split_selection_and_workspace():
+    # one 131,072-token sequence, 32 heads: plenty of splits
+    c = _cache(batch=1, kv_heads=32, token_cap=131104, n_quant=131040, n_res=32)
+    s = L.kivi_decode_attn_splits(C.byref(c), 32)
+    assert 8 <= s <= 1024
+    assert L.kivi_decode_attn_workspace(C.byref(c), 32, 0) == 256 + ((s * 32 * 130 * 4 + 255) // 256) * 256
+    # very short history: one split
+    c = _cache(n_quant=32, n_res=0)
+    assert L.kivi_decode_attn_splits(C.byref(c), 2) == 1
+    assert L.kivi_decode_attn_workspace(C.byref(c), 2, 7) == 256 + ((7 * 2 * 2 * 130 * 4 + 255) // 256) * 256
