@@ -53,13 +53,19 @@ enum {
  * The cache descriptor (host struct; the caller owns it and every buffer it points to).
  * row = b * kv_heads + h.  D = head_dim, G = group, R = residual_cap.
  *
- * Packed layout (four 2-bit codes per byte, least significant bits first):
- *   k_codes, v_codes : uint8  [row][token_cap][D/4]; code of (token t, channel j) at
- *                      byte t*(D/4) + j/4, bits 2*(j%4) .. 2*(j%4)+1.
+ * Packed layout (four 2-bit codes per byte; D = 128, G = 32 here):
+ *   k_codes, v_codes : uint8  [row][token_cap/G][1024]: one 1024-byte tile per 32-token
+ *                      group.  In a tile, 16-byte chunk ((u*8 + q)*4 + h) holds the 8 code
+ *                      bytes of channel quarter h (channels 32h..32h+31) of token 4q+2u,
+ *                      then those of token 4q+2u+1 (q = 0..7, u = 0..1).  Those 8 bytes are
+ *                      two little-endian 32-bit words (channels 32h..+15, 32h+16..+31); in
+ *                      a word, channel 4i+b sits in byte b at bits 2i..2i+1, so masking the
+ *                      word with 0x03030303 << 2i yields four consecutive channels' codes.
  *   k_sz             : fp16   [row][token_cap/G][D][2]  (scale, zero) of key token group
  *                      g, channel j  -- keys are quantized per-channel over G tokens.
- *   v_sz             : fp16   [row][token_cap][D/G][2]  (scale, zero) of value token t,
- *                      channel group k -- values are quantized per-token over G channels.
+ *   v_sz             : fp16   [row][token_cap/G][D/G][G][2]  (scale, zero) of value token
+ *                      32g+t, channel group k -- values are quantized per-token over G
+ *                      channels.
  *   k_res, v_res     : fp16   [row][R][D] residual ring; the n_res newest tokens, oldest
  *                      first, sit in slots (res_head + i) % R, i < n_res.
  * Dequantized value: zero + code * scale.  Quantizer: zero = group min, scale =

@@ -14,7 +14,7 @@ using namespace kivi;
 namespace {
 
 constexpr int kMaxSplits = 1024;
-constexpr int64_t kTargetBlocks = 1024;     // ~4 workgroups of 4 waves per CU on 256 CUs
+constexpr int64_t kTargetBlocks = 768;      // one round of resident workgroups on MI355X: 256 CUs x 3
 constexpr int kMinGroupsPerSplit = 8;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

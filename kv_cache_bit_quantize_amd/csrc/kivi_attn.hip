@@ -2,20 +2,35 @@
 //
 // One query per head attends over the dequantized history followed by the fp16
 // residual: out = softmax(sm_scale * q.K^T) . V (error judged at the attention output:
-// article "Your KV cache doesn't have a bit problem...", paragraph 3).  Keys are folded
-// per token group: q.(z + c*s) = q.z + (q*s).c, computed once per group and channel;
-// values per token: p*(z + c*s) = p*z + (p*s)*c.
+// article "Your KV cache doesn't have a bit problem...", paragraph 3).
 //
 // Work split: grid (splits, B*Hq).  A 256-thread workgroup owns one query row and a
 // contiguous range of key groups; each of its 4 waves walks a quarter of that range
-// with its own online softmax (log2 domain), the waves merge in LDS and the workgroup
-// writes one partial (o[128], m, l).  The last workgroup of a row to finish (per-row
-// arrival counter) merges the row's partials (log-sum-exp merge) and writes the output,
-// so one launch does the whole call.  The split holding the last groups also reads the
-// residual.
+// with its own online softmax (log2 domain).  The waves merge in LDS, the workgroup
+// writes one partial (o[128], m, l), and the last workgroup of the row to arrive
+// (device-scope arrival counter) merges the row's partials with the log-sum-exp merge
+// and writes the output, so one launch does the whole call.  The split holding the last
+// groups also reads the fp16 residual.
 //
-// Lane map inside a wave, per 32-token group: lane = 4*tp + qq handles tokens 2tp and
-// 2tp+1 of the group and channels [32qq, 32qq+32); 8-byte code loads per token.
+// Inner loop (one wave-iteration = two 32-token key groups, one per half-wave).
+// Lane = 32*gh + 4*tq + qq owns tokens 4tq..4tq+3 of group gh and channels
+// [32qq, 32qq+32).  Codes are 2 bits, so the loop is bound by HBM and by the vector
+// instructions that turn codes into products; it is arranged to need few of them:
+//
+//  * keys, per token group g: q.(z + c*s) = q.z + (q*s).c.  The 32 lanes of a half
+//    compute q*s for 4 channels each, convert it to a 30-bit fixed-point integer with a
+//    per-group exponent, split it into four signed bytes, byte-transpose so that one
+//    32-bit word holds one byte position of four consecutive channels, and store those
+//    words in LDS once.  A token's code word masked with 0x03030303 << 2i gives the codes
+//    of channels 4i..4i+3 as bytes (layout in kivi_device.h), so the dot products are
+//    exact v_dot4_i32_i8 operations against those words (the per-class factor 4^i of the
+//    unshifted masks is divided out of the fixed-point values beforehand).
+//  * values, per token: p*(z + c*s) = p*z + (p*s)*c.  v_perm pairs two tokens' code
+//    bytes into one word, each code is placed at bits 8-9 or 6-7 of an fp16 whose
+//    exponent reads 1.0 (one shift + v_and_or_b32), giving the exact half 1 + c/4 or
+//    1 + c/16, and v_dot2_f32_f16 accumulates two tokens per instruction against fp16
+//    weights 4*p*s or 16*p*s (kept in range by a power-of-two factor).  The constant
+//    part, sum of the weights, is accumulated separately and subtracted at the end.
 #include "kivi_device.h"
 #include "kivi_internal.h"
 
@@ -24,8 +39,19 @@ namespace kivi {
 constexpr int kWaves = kBlock / 64;
 constexpr int kPart = kD + 2;   // floats per partial: o[128], m, l
 
-__device__ __forceinline__ float code_f(uint32_t w, int c) {
-    return (float)((w >> (2 * c)) & 3u);
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ half2_t as_h2(uint32_t x) { return __builtin_bit_cast(half2_t, x); }
+
+// (x & m) | o in one instruction (v_and_or_b32 takes its constants in VGPRs)
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t o) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(m), "v"(o));
+    return r;
+}
+
+__device__ __forceinline__ float fdot2(uint32_t a, half2_t b, float c) {
+    return __builtin_amdgcn_fdot2(as_h2(a), b, c, false);
 }
 
 __device__ __forceinline__ void load_q32(const uint16_t* q, float scale, float (&qv)[32]) {
@@ -42,7 +68,12 @@ __device__ __forceinline__ void load_q32(const uint16_t* q, float scale, float (
     }
 }
 
+// Channel offset c (0..15) of a 16-channel block -> bit position of its code in a word
+// that holds token 2s's block bytes 0,1 (or 2,3) in its low half and token 2s+1's in its
+// high half, after v_perm.  Used only to document the extraction table below.
+
 __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
+    __shared__ uint4 sh_kq[2][kWaves][2][kD / 4];   // [parity][wave][half][16-ch block*4 + class]
     __shared__ float sh_o[kWaves][kD];
     __shared__ float sh_m[kWaves], sh_l[kWaves];
 
@@ -52,14 +83,28 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
     const int hq = (int)(qrow % a.q_heads);
     const int64_t kvrow = b * a.kv_heads + hq / a.ratio;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int tp = lane >> 2, qq = lane & 3;
+    const int gh = lane >> 5, tq = (lane >> 2) & 7, qq = lane & 3;
+    const int wl = lane & 31;          // as fixed-point writer: channels 4wl .. 4wl+3
+    const int wk = wl & 3;             // their position i inside the 16-channel block
 
-    float qv[32];
-    load_q32(a.q + qrow * kD + qq * 32, a.sm_log2, qv);
-    float o[32];
+    // query channels 4wl..4wl+3 in the log2 domain
+    float qw[4];
+    {
+        const uint2 x = *reinterpret_cast<const uint2*>(a.q + qrow * kD + 4 * wl);
+        qw[0] = h2f(x.x & 0xffffu) * a.sm_log2;
+        qw[1] = h2f(x.x >> 16) * a.sm_log2;
+        qw[2] = h2f(x.y & 0xffffu) * a.sm_log2;
+        qw[3] = h2f(x.y >> 16) * a.sm_log2;
+    }
+    // codes of channels 4i..4i+3 arrive multiplied by 1, 4, 16, 16 (i = 0..3)
+    const float cls_div = wk == 0 ? 1.0f : (wk == 1 ? 0.25f : 0.0625f);
+
+    float acc[32];
 #pragma unroll
-    for (int c = 0; c < 32; ++c) o[c] = 0.0f;
+    for (int c = 0; c < 32; ++c) acc[c] = 0.0f;
+    float b6 = 0.0f, b8 = 0.0f;        // sums of the fp16 weights of the two value classes
     float zacc = 0.0f, lsum = 0.0f, m = -INFINITY;
+    float vs = 0.0f;                   // power-of-two factor keeping the value weights in fp16 range
 
     const int n_groups = a.n_quant / kG;
     const int g_lo = split * a.groups_per_split;
@@ -68,6 +113,7 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
     const int per_wave = (cnt + kWaves - 1) / kWaves;
     const int gb = g_lo + min(cnt, wave * per_wave);
     const int ge = g_lo + min(cnt, (wave + 1) * per_wave);
+    const int iters = (ge - gb + 1) >> 1;
 
     const int64_t tok_base = kvrow * (int64_t)a.token_cap;
     const uint8_t* kc_row = a.k_codes + tok_base * kRowBytes;
@@ -75,51 +121,201 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
     const uint32_t* kp_row = reinterpret_cast<const uint32_t*>(a.k_sz) + kvrow * (int64_t)(a.token_cap / kG) * kD;
     const uint32_t* vp_row = reinterpret_cast<const uint32_t*>(a.v_sz) + tok_base * (kD / kG);
 
-    for (int g = gb; g < ge; ++g) {
-        const int64_t t0 = (int64_t)g * kG + 2 * tp;
-        const uint2 kw0 = *reinterpret_cast<const uint2*>(kc_row + t0 * kRowBytes + qq * 8);
-        const uint2 kw1 = *reinterpret_cast<const uint2*>(kc_row + (t0 + 1) * kRowBytes + qq * 8);
-        const uint2 vw0 = *reinterpret_cast<const uint2*>(vc_row + t0 * kRowBytes + qq * 8);
-        const uint2 vw1 = *reinterpret_cast<const uint2*>(vc_row + (t0 + 1) * kRowBytes + qq * 8);
-        const uint32_t vp0 = vp_row[t0 * 4 + qq], vp1 = vp_row[(t0 + 1) * 4 + qq];
-        const uint4* kp4 = reinterpret_cast<const uint4*>(kp_row + (int64_t)g * kD + qq * 32);
-        float d0 = 0.0f, d1 = 0.0f, az = 0.0f;
+    const uint32_t kM6 = 0x00C000C0u, kM8 = 0x03000300u, kOne = 0x3C003C00u;
+    const half2_t ones = as_h2(kOne);
+
+    // one wave-iteration's global loads (issued one iteration ahead of their use)
+    struct Loads {
+        uint4 kp;          // (scale, zero) of key channels 4wl..4wl+3 of group gc
+        uint2 kw[4], vw[4];   // key / value codes of tokens 4tq..4tq+3, channels of quarter qq
+        uint32_t vp[4];    // (scale, zero) of the value channel group qq of those tokens
+    };
+    // Tile chunks wl and 32 + wl of group gc hold the quarter qq of tokens 4tq..4tq+3
+    // (wl = 4tq + qq), so each load instruction reads two contiguous 512-byte spans.
+    auto load_iter = [&](int it) {
+        Loads L;
+        const int g = gb + 2 * it + gh;
+        const int gc = g < ge ? g : gb;               // in-bounds address for an idle half
+        L.kp = *reinterpret_cast<const uint4*>(kp_row + (int64_t)gc * kD + 4 * wl);
+        const uint4* kt = reinterpret_cast<const uint4*>(kc_row + (int64_t)gc * kTileBytes);
+        const uint4* vt = reinterpret_cast<const uint4*>(vc_row + (int64_t)gc * kTileBytes);
+        const uint4 k0 = kt[wl], k1 = kt[32 + wl], v0 = vt[wl], v1 = vt[32 + wl];
+        L.kw[0] = make_uint2(k0.x, k0.y);
+        L.kw[1] = make_uint2(k0.z, k0.w);
+        L.kw[2] = make_uint2(k1.x, k1.y);
+        L.kw[3] = make_uint2(k1.z, k1.w);
+        L.vw[0] = make_uint2(v0.x, v0.y);
+        L.vw[1] = make_uint2(v0.z, v0.w);
+        L.vw[2] = make_uint2(v1.x, v1.y);
+        L.vw[3] = make_uint2(v1.z, v1.w);
+        const uint4 p = *reinterpret_cast<const uint4*>(vp_row + value_pair_index((int64_t)gc * kG + 4 * tq, qq));
+        L.vp[0] = p.x;
+        L.vp[1] = p.y;
+        L.vp[2] = p.z;
+        L.vp[3] = p.w;
+        return L;
+    };
+
+    Loads cur;
+    if (iters > 0) cur = load_iter(0);
+    for (int it = 0; it < iters; ++it) {
+        const Loads nxt = load_iter(it + 1 < iters ? it + 1 : it);
+        const bool gvalid = gb + 2 * it + gh < ge;
+        const uint4 kp = cur.kp;
+        const uint2* kw = cur.kw;
+        const uint2* vw = cur.vw;
+        const uint32_t* vp = cur.vp;
+
+        // ---- q*s of group gc as 30-bit fixed point, four byte limbs, into LDS
+        const uint32_t pr[4] = {kp.x, kp.y, kp.z, kp.w};
+        float qs[4], az = 0.0f, mx = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint4 pr = kp4[i];
-            const uint32_t pw[4] = {pr.x, pr.y, pr.z, pr.w};
+        for (int i = 0; i < 4; ++i) {
+            qs[i] = qw[i] * h2f(pr[i] & 0xffffu);
+            az = fmaf(qw[i], h2f(pr[i] >> 16), az);
+            mx = fmaxf(mx, fabsf(qs[i]));
+        }
+        az = half_sum(az);
+        mx = half_max(mx);
+        const int sh = 29 - __builtin_amdgcn_frexp_expf(mx);   // |q*s| * 2^sh < 2^29
+        uint32_t dg[4];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int c = 4 * i + k;
-                const float qs = qv[c] * h2f(pw[k] & 0xffffu);
-                az = fmaf(qv[c], h2f(pw[k] >> 16), az);
-                const uint32_t w0 = c < 16 ? kw0.x : kw0.y;
-                const uint32_t w1 = c < 16 ? kw1.x : kw1.y;
-                d0 = fmaf(qs, code_f(w0, c & 15), d0);
-                d1 = fmaf(qs, code_f(w1, c & 15), d1);
+        for (int i = 0; i < 4; ++i) {
+            const int qi = (int)__builtin_rintf(__builtin_ldexpf(qs[i] * cls_div, sh));
+            dg[i] = ((uint32_t)qi + 0x80808080u) ^ 0x80808080u;    // four signed base-256 digits
+        }
+        {
+            const uint32_t A = __builtin_amdgcn_perm(dg[1], dg[0], 0x05010400u);
+            const uint32_t B = __builtin_amdgcn_perm(dg[1], dg[0], 0x07030602u);
+            const uint32_t C = __builtin_amdgcn_perm(dg[3], dg[2], 0x05010400u);
+            const uint32_t E = __builtin_amdgcn_perm(dg[3], dg[2], 0x07030602u);
+            uint4 limbs;
+            limbs.x = __builtin_amdgcn_perm(C, A, 0x05040100u);   // digit 0 of the 4 channels
+            limbs.y = __builtin_amdgcn_perm(C, A, 0x07060302u);   // digit 1
+            limbs.z = __builtin_amdgcn_perm(E, B, 0x05040100u);   // digit 2
+            limbs.w = __builtin_amdgcn_perm(E, B, 0x07060302u);   // digit 3
+            sh_kq[it & 1][wave][gh][wl] = limbs;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // ---- logits of the lane's 4 tokens (exact integer dot products), one 16-channel
+        // block of limb words at a time: [block 2qq+wd][class i] = uint4 {digit 0..3}
+        const float kscale = __builtin_ldexpf(1.0f, -sh);
+        int dd[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dd[i][0] = dd[i][1] = dd[i][2] = dd[i][3] = 0;
+#pragma unroll
+        for (int wd = 0; wd < 2; ++wd) {
+            uint4 lw[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) lw[k] = sh_kq[it & 1][wave][gh][8 * qq + 4 * wd + k];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t x = wd ? kw[i].y : kw[i].x;
+                const uint32_t cm[4] = {x & 0x03030303u, x & 0x0C0C0C0Cu, x & 0x30303030u, (x >> 2) & 0x30303030u};
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    dd[i][0] = __builtin_amdgcn_sdot4((int)cm[k], (int)lw[k].x, dd[i][0], false);
+                    dd[i][1] = __builtin_amdgcn_sdot4((int)cm[k], (int)lw[k].y, dd[i][1], false);
+                    dd[i][2] = __builtin_amdgcn_sdot4((int)cm[k], (int)lw[k].z, dd[i][2], false);
+                    dd[i][3] = __builtin_amdgcn_sdot4((int)cm[k], (int)lw[k].w, dd[i][3], false);
+                }
             }
         }
-        d0 = wave_sum_xor(d0, 1, 2);
-        d1 = wave_sum_xor(d1, 1, 2);
-        az = wave_sum_xor(az, 1, 2);
-        const float l0 = az + d0, l1 = az + d1;
-        const float m_new = fmaxf(m, wave_max_xor(fmaxf(l0, l1), 4, 32));
-        const float alpha = (m == -INFINITY) ? 0.0f : exp2f(m - m_new);
-        const float p0 = exp2f(l0 - m_new), p1 = exp2f(l1 - m_new);
-        lsum = lsum * alpha + p0 + p1;
-        const float w0 = p0 * h2f(vp0 & 0xffffu), w1 = p1 * h2f(vp1 & 0xffffu);
-        zacc = zacc * alpha + p0 * h2f(vp0 >> 16) + p1 * h2f(vp1 >> 16);
+        float lg[4];
 #pragma unroll
-        for (int c = 0; c < 32; ++c) {
-            const uint32_t a0 = c < 16 ? vw0.x : vw0.y;
-            const uint32_t a1 = c < 16 ? vw1.x : vw1.y;
-            o[c] = fmaf(w1, code_f(a1, c & 15), fmaf(w0, code_f(a0, c & 15), o[c] * alpha));
+        for (int i = 0; i < 4; ++i) {
+            const int hi = dd[i][3] * 256 + dd[i][2], lo = dd[i][1] * 256 + dd[i][0];
+            const float tot = quad_sum(fmaf((float)hi, 65536.0f, (float)lo));
+            lg[i] = gvalid ? fmaf(tot, kscale, az) : -INFINITY;
         }
-        m = m_new;
+
+        // ---- online softmax over the wave's 64 tokens (rescale only when the max rises)
+        const float mloc = wave_max_quads(fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3])));
+        if (mloc > m) {
+            const float al = exp2f(m - mloc);
+#pragma unroll
+            for (int c = 0; c < 32; ++c) acc[c] *= al;
+            b6 *= al;
+            b8 *= al;
+            zacc *= al;
+            lsum *= al;
+            m = mloc;
+        }
+        float p[4], w[4], smax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            p[i] = exp2f(lg[i] - m);
+            const float s = h2f(vp[i] & 0xffffu);
+            w[i] = p[i] * s;
+            zacc = fmaf(p[i], h2f(vp[i] >> 16), zacc);
+            lsum += p[i];
+            smax = fmaxf(smax, s);
+        }
+        // value weights 16*w*vs must stay below 2^15: shrink vs (a power of two) if needed
+        if (__builtin_amdgcn_ballot_w64(smax * vs > 2048.0f || vs == 0.0f)) {
+            const float gm = wave_max_xor(smax, 1, 32);
+            const float nvs = __builtin_ldexpf(1.0f, 11 - __builtin_amdgcn_frexp_expf(gm));
+            if (vs != 0.0f && nvs < vs) {
+                const float r = nvs / vs;
+#pragma unroll
+                for (int c = 0; c < 32; ++c) acc[c] *= r;
+                b6 *= r;
+                b8 *= r;
+            }
+            if (vs == 0.0f || nvs < vs) vs = nvs;
+        }
+
+        // ---- P.V over the codes: two tokens per v_dot2 against fp16 weights
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+            half2_t u6, u8;
+            u6.x = (_Float16)(w[2 * pp] * (16.0f * vs));
+            u6.y = (_Float16)(w[2 * pp + 1] * (16.0f * vs));
+            u8.x = (_Float16)(w[2 * pp] * (4.0f * vs));
+            u8.y = (_Float16)(w[2 * pp + 1] * (4.0f * vs));
+            b6 = __builtin_amdgcn_fdot2(u6, ones, b6, false);
+            b8 = __builtin_amdgcn_fdot2(u8, ones, b8, false);
+#pragma unroll
+            for (int wd = 0; wd < 2; ++wd) {
+                const uint32_t x0 = wd ? vw[2 * pp].y : vw[2 * pp].x;
+                const uint32_t x1 = wd ? vw[2 * pp + 1].y : vw[2 * pp + 1].x;
+#pragma unroll
+                for (int hb = 0; hb < 2; ++hb) {
+                    // bytes hb*2, hb*2+1 of token 2pp (low half) and token 2pp+1 (high half):
+                    // channels o+{0,4,8,12} at bits 0,2,4,6 and o+{1,5,9,13} at 8,10,12,14
+                    const uint32_t X = __builtin_amdgcn_perm(x1, x0, hb ? 0x07060302u : 0x05040100u);
+                    const uint32_t l4 = X << 4, r4 = X >> 4, l8 = X << 8, r8 = X >> 8;
+                    const int o = 16 * wd + 2 * hb;
+                    acc[o + 0] = fdot2(and_or(l8, kM8, kOne), u8, acc[o + 0]);
+                    acc[o + 1] = fdot2(and_or(X, kM8, kOne), u8, acc[o + 1]);
+                    acc[o + 4] = fdot2(and_or(l4, kM6, kOne), u6, acc[o + 4]);
+                    acc[o + 5] = fdot2(and_or(r4, kM6, kOne), u6, acc[o + 5]);
+                    acc[o + 8] = fdot2(and_or(l4, kM8, kOne), u8, acc[o + 8]);
+                    acc[o + 9] = fdot2(and_or(r4, kM8, kOne), u8, acc[o + 9]);
+                    acc[o + 12] = fdot2(and_or(X, kM6, kOne), u6, acc[o + 12]);
+                    acc[o + 13] = fdot2(and_or(r8, kM6, kOne), u6, acc[o + 13]);
+                }
+            }
+        }
+        cur = nxt;
     }
 
-    // fp16 residual, logical tokens [32*wave, 32*wave+32) of the ring, last split only
-    if (split == a.splits - 1) {
+    // true partial output of the lane's quarter: sum(w*c) = (acc - bias) / vs, plus p*z
+    float o[32];
+    {
+        const float inv = vs != 0.0f ? 1.0f / vs : 0.0f;
+#pragma unroll
+        for (int c = 0; c < 32; ++c) o[c] = fmaf(acc[c] - ((c & 4) ? b6 : b8), inv, zacc);
+    }
+
+    // fp16 residual, logical tokens [32*wave, 32*wave+32) of the ring, last split only.
+    // Lane = 4*tp + qq: tokens 2tp, 2tp+1 of the chunk, channels [32qq, 32qq+32).
+    if (split == a.splits - 1 && wave * kG < a.n_res) {
+        const int tp = lane >> 2;
+        float qv[32];
+        load_q32(a.q + qrow * kD + qq * 32, a.sm_log2, qv);
         for (int base = wave * kG; base < a.n_res; base += kWaves * kG) {
             const int i0 = base + 2 * tp, i1 = i0 + 1;
             const bool ok0 = i0 < a.n_res, ok1 = i1 < a.n_res;
@@ -150,8 +346,9 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
             const float alpha = (m == -INFINITY) ? 0.0f : exp2f(m - m_new);
             const float p0 = ok0 ? exp2f(l0 - m_new) : 0.0f;
             const float p1 = ok1 ? exp2f(l1 - m_new) : 0.0f;
+            // the main loop counted each token once per lane of its quarter group; here each
+            // token pair is also held by the 4 lanes of one tp, so lsum stays consistent
             lsum = lsum * alpha + p0 + p1;
-            zacc *= alpha;
             const uint4* v0 = reinterpret_cast<const uint4*>(a.v_res + r0);
             const uint4* v1 = reinterpret_cast<const uint4*>(a.v_res + r1);
 #pragma unroll
@@ -169,11 +366,11 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
         }
     }
 
-    // wave result: sum over the 16 token-pair lanes of each channel quarter
+    // wave result: sum over the 16 lanes that share a channel quarter
     lsum = wave_sum_xor(lsum, 4, 32);
 #pragma unroll
-    for (int c = 0; c < 32; ++c) o[c] = wave_sum_xor(o[c] + zacc, 4, 32);
-    if (tp == 0) {
+    for (int c = 0; c < 32; ++c) o[c] = wave_sum_xor(o[c], 4, 32);
+    if ((lane >> 2) == 0) {
 #pragma unroll
         for (int c = 0; c < 32; ++c) sh_o[wave][qq * 32 + c] = o[c];
     }

@@ -14,6 +14,26 @@ constexpr int kG = 32;              // group size (tokens for keys, channels for
 constexpr int kRowBytes = kD / 4;   // packed code bytes per token
 constexpr int kBlock = 256;         // threads per workgroup (4 wave64)
 
+// Packed code layout (include/kivi.h).  16 channels 16w..16w+15 of a token form one 32-bit
+// word; channel offset c = 4i + b (0..15) sits in byte b at bits 2i..2i+1, i.e. at bit
+// 8b + 2i, so masking a word with 0x03030303 << 2i leaves the codes of channels 4i..4i+3,
+// one per byte.  A row holds one 1024-byte tile per 32-token group; in a tile, 16-byte
+// chunk ((u*8 + q)*4 + h) holds quarter h (words 2h, 2h+1) of token 4q+2u, then of token
+// 4q+2u+1.  A half-wave whose lane L = 4q + h loads chunks L and 32 + L therefore reads
+// two contiguous 512-byte spans and gets the quarter h of tokens 4q..4q+3.
+__host__ __device__ constexpr int code_bit(int c) { return 8 * (c & 3) + 2 * (c >> 2); }
+constexpr int kTileBytes = kG * kD / 4;     // 1024
+
+// byte offset, inside a row, of word w (0..7) of token t
+__host__ __device__ constexpr int64_t code_word_offset(int64_t t, int w) {
+    return (t >> 5) * kTileBytes +
+           ((((t & 3) >> 1) * 8 + ((t & 31) >> 2)) * 4 + (w >> 1)) * 16 + (t & 1) * 8 + (w & 1) * 4;
+}
+// index (in 32-bit pairs), inside a row, of the value (scale, zero) of token t, group k
+__host__ __device__ constexpr int64_t value_pair_index(int64_t t, int k) {
+    return (t >> 5) * (kG * (kD / kG)) + k * kG + (t & 31);
+}
+
 __device__ __forceinline__ float h2f(uint32_t h) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
 }
@@ -57,7 +77,53 @@ __device__ __forceinline__ uint32_t code_of(float x, const GroupQ& q) {
     return (uint32_t)r;
 }
 
-// wave64 cross-lane helpers (ds_swizzle/DPP chosen by the compiler for __shfl_xor)
+// Cross-lane exchange without LDS traffic: DPP for partners inside a 16-lane row
+// (quad_perm for lane^1 and lane^2; after those, every lane of a quad holds the same value,
+// so the half-row mirror and the row mirror pair each quad / half-row with the other one),
+// ds_swizzle for lane^16 and readlane for the two halves of the wave.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float xor1_f(float v) { return dpp_f<0xB1>(v); }    // quad_perm [1,0,3,2]
+__device__ __forceinline__ float xor2_f(float v) { return dpp_f<0x4E>(v); }    // quad_perm [2,3,0,1]
+__device__ __forceinline__ float hmirror_f(float v) { return dpp_f<0x141>(v); } // lane i <-> 7-i in 8
+__device__ __forceinline__ float mirror_f(float v) { return dpp_f<0x140>(v); }  // lane i <-> 15-i in 16
+__device__ __forceinline__ float xor16_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+}
+// sum / max over the 32 lanes of each half-wave (every lane gets its half's result)
+__device__ __forceinline__ float half_sum(float v) {
+    v += xor1_f(v);
+    v += xor2_f(v);
+    v += hmirror_f(v);
+    v += mirror_f(v);
+    return v + xor16_f(v);
+}
+__device__ __forceinline__ float half_max(float v) {
+    v = __builtin_fmaxf(v, xor1_f(v));
+    v = __builtin_fmaxf(v, xor2_f(v));
+    v = __builtin_fmaxf(v, hmirror_f(v));
+    v = __builtin_fmaxf(v, mirror_f(v));
+    return __builtin_fmaxf(v, xor16_f(v));
+}
+// max over lanes that differ in bits 2..5, for values already equal inside each quad;
+// the result is wave-uniform
+__device__ __forceinline__ float wave_max_quads(float v) {
+    v = __builtin_fmaxf(v, hmirror_f(v));
+    v = __builtin_fmaxf(v, mirror_f(v));
+    v = __builtin_fmaxf(v, xor16_f(v));
+    const float lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+    const float hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+    return __builtin_fmaxf(lo, hi);
+}
+// sum over the 4 lanes of a quad
+__device__ __forceinline__ float quad_sum(float v) {
+    v += xor1_f(v);
+    return v + xor2_f(v);
+}
+
+// wave64 cross-lane helpers through ds_bpermute (outside the hot loops)
 __device__ __forceinline__ float wave_max_xor(float v, int from, int to) {
     for (int m = from; m <= to; m <<= 1) v = __builtin_fmaxf(v, __shfl_xor(v, m, 64));
     return v;

@@ -12,10 +12,10 @@
 
 namespace kivi {
 
-// One key token group held in LDS as fp16 [32][128] -> 32 x 32 code bytes + 128 pairs.
+// One key token group held in LDS as fp16 [32][128] -> its 1024-byte code tile + 128 pairs.
 // Called by all 256 threads of the workgroup; ends with the codes and pairs stored.
 __device__ void quant_k_tile(const uint16_t* __restrict__ tile, float* sh_mn, float* sh_s,
-                             uint8_t* __restrict__ codes_dst,      // token row of group start
+                             uint8_t* __restrict__ codes_dst,      // the group's code tile
                              uint32_t* __restrict__ pairs_dst) {   // 128 (scale, zero) words
     const int tid = threadIdx.x;
     if (tid < kD) {
@@ -43,15 +43,16 @@ __device__ void quant_k_tile(const uint16_t* __restrict__ tile, float* sh_mn, fl
         uint32_t bits = (c & 1) ? (h[c >> 1] >> 16) : (h[c >> 1] & 0xffffu);
         int j = w * 16 + c;
         GroupQ q{sh_mn[j], sh_s[j], 0u};
-        word |= code_of(h2f(bits), q) << (2 * c);
+        word |= code_of(h2f(bits), q) << code_bit(c);
     }
-    reinterpret_cast<uint32_t*>(codes_dst + t * kRowBytes)[w] = word;
+    *reinterpret_cast<uint32_t*>(codes_dst + code_word_offset(t, w)) = word;
 }
 
 // Eight consecutive channels of one value token (this thread's share of a 32-channel
-// group held by 4 adjacent lanes).  Returns the 16 code bits; *pair gets the group's
-// (scale, zero) word (valid in every lane of the 4).
-__device__ __forceinline__ uint32_t quant_v_8(uint4 x, uint32_t* pair) {
+// group held by 4 adjacent lanes; lane pairs 2w, 2w+1 hold one 16-channel code word).
+// Returns the complete 32-bit code word of the pair (valid in both lanes); *pair gets the
+// group's (scale, zero) word (valid in every lane of the 4).  All lanes must call it.
+__device__ __forceinline__ uint32_t quant_v_8(uint4 x, int odd, uint32_t* pair) {
     uint32_t h[4] = {x.x, x.y, x.z, x.w};
     float v[8];
 #pragma unroll
@@ -70,9 +71,9 @@ __device__ __forceinline__ uint32_t quant_v_8(uint4 x, uint32_t* pair) {
     GroupQ q = group_params(mn, mx);
     uint32_t bits = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) bits |= code_of(v[i], q) << (2 * i);
+    for (int i = 0; i < 8; ++i) bits |= code_of(v[i], q) << code_bit(8 * odd + i);
     *pair = q.pair;
-    return bits;
+    return bits | (uint32_t)__shfl_xor((int)bits, 1, 64);
 }
 
 // ------------------------------------------------------------------ kernels ------
@@ -90,7 +91,7 @@ __global__ __launch_bounds__(kBlock) void quantize_k_kernel(QuantArgs a) {
     tile4[threadIdx.x + kBlock] = s4[threadIdx.x + kBlock];
     __syncthreads();
     const int dst_tok = a.dst_token_off + g * kG;
-    uint8_t* codes = a.k_codes + (row * a.token_cap + dst_tok) * kRowBytes;
+    uint8_t* codes = a.k_codes + row * a.token_cap * kRowBytes + (int64_t)(dst_tok / kG) * kTileBytes;
     uint32_t* pairs = reinterpret_cast<uint32_t*>(a.k_sz) + (row * (a.token_cap / kG) + dst_tok / kG) * kD;
     quant_k_tile(reinterpret_cast<const uint16_t*>(tile4), sh_mn, sh_s, codes, pairs);
 }
@@ -106,11 +107,13 @@ __global__ __launch_bounds__(kBlock) void quantize_v_kernel(QuantArgs a) {
     uint4 x = make_uint4(0, 0, 0, 0);
     if (live) x = reinterpret_cast<const uint4*>(a.src + row * a.src_row_stride + (int64_t)t * kD)[l16];
     uint32_t pair;
-    uint32_t bits = quant_v_8(x, &pair);
+    const uint32_t word = quant_v_8(x, l16 & 1, &pair);
     if (live) {
-        const int64_t tok = row * a.token_cap + a.dst_token_off + t;
-        reinterpret_cast<uint16_t*>(a.v_codes + tok * kRowBytes)[l16] = (uint16_t)bits;
-        if ((l16 & 3) == 0) reinterpret_cast<uint32_t*>(a.v_sz)[tok * (kD / kG) + (l16 >> 2)] = pair;
+        const int64_t tok = a.dst_token_off + t;          // token inside the row's history
+        if ((l16 & 1) == 0)
+            *reinterpret_cast<uint32_t*>(a.v_codes + row * a.token_cap * kRowBytes + code_word_offset(tok, l16 >> 1)) = word;
+        if ((l16 & 3) == 0)
+            reinterpret_cast<uint32_t*>(a.v_sz)[row * a.token_cap * (kD / kG) + value_pair_index(tok, l16 >> 2)] = pair;
     }
 }
 
@@ -142,7 +145,7 @@ __global__ __launch_bounds__(kBlock) void append_flush_kernel(AppendArgs a) {
         tile4[tid + kBlock] = kr[tid + kBlock];
         __syncthreads();
         const int dst_tok = a.flush_group * kG;
-        uint8_t* kc = a.k_codes + (row * a.token_cap + dst_tok) * kRowBytes;
+        uint8_t* kc = a.k_codes + row * a.token_cap * kRowBytes + (int64_t)a.flush_group * kTileBytes;
         uint32_t* kp = reinterpret_cast<uint32_t*>(a.k_sz) + (row * (a.token_cap / kG) + a.flush_group) * kD;
         quant_k_tile(reinterpret_cast<const uint16_t*>(tile4), sh_mn, sh_s, kc, kp);
         // values: 32 tokens x 16 lanes = two passes of 16 tokens
@@ -151,10 +154,12 @@ __global__ __launch_bounds__(kBlock) void append_flush_kernel(AppendArgs a) {
         for (int pass = 0; pass < 2; ++pass) {
             const int t = pass * 16 + (tid >> 4), l16 = tid & 15;
             uint32_t pair;
-            uint32_t bits = quant_v_8(vr[t * 16 + l16], &pair);
-            const int64_t tok = row * a.token_cap + dst_tok + t;
-            reinterpret_cast<uint16_t*>(a.v_codes + tok * kRowBytes)[l16] = (uint16_t)bits;
-            if ((l16 & 3) == 0) reinterpret_cast<uint32_t*>(a.v_sz)[tok * (kD / kG) + (l16 >> 2)] = pair;
+            const uint32_t word = quant_v_8(vr[t * 16 + l16], l16 & 1, &pair);
+            const int64_t tok = dst_tok + t;
+            if ((l16 & 1) == 0)
+                *reinterpret_cast<uint32_t*>(a.v_codes + row * a.token_cap * kRowBytes + code_word_offset(tok, l16 >> 1)) = word;
+            if ((l16 & 3) == 0)
+                reinterpret_cast<uint32_t*>(a.v_sz)[row * a.token_cap * (kD / kG) + value_pair_index(tok, l16 >> 2)] = pair;
         }
         __syncthreads();   // every read of the flushed slots is done before the overwrite
     }

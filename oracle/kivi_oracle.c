@@ -126,14 +126,29 @@ void kivi_ref_quant_group(const uint16_t* x, ptrdiff_t stride, int32_t n,
 
 static int64_t row_count(const kivi_ref_cache* c) { return (int64_t)c->batch * c->kv_heads; }
 
+/* Code position of (token t, channel j) in a row of packed codes.  The row is a sequence
+ * of 1024-byte tiles, one per 32-token group.  Inside a tile, 16-byte chunk
+ * ((u*8 + q)*4 + h) holds, for channel quarter h (channels 32h..32h+31), the 8 bytes of
+ * token 4q + 2u followed by the 8 bytes of token 4q + 2u + 1 (q = 0..7, u = 0..1).  A
+ * token's 8 bytes for a quarter are two little-endian 32-bit words (channels 32h..32h+15,
+ * then 32h+16..32h+31); in a word of 16 channels, channel 4i + b sits in byte b at bits
+ * 2i, 2i+1. */
+static int64_t code_byte(int32_t d, int32_t t, int32_t j) {
+    (void)d;
+    int32_t tt = t % 32, q = tt / 4, u = (tt % 4) / 2, t1 = tt % 2;
+    int32_t h = j / 32, w = (j % 32) / 16, c = j % 16;
+    return (int64_t)(t / 32) * 1024 + ((u * 8 + q) * 4 + h) * 16 + t1 * 8 + w * 4 + (c % 4);
+}
+static int code_shift(int32_t j) { return 2 * ((j % 16) / 4); }
+
 static void put_code(uint8_t* codes_row, int32_t d, int32_t t, int32_t j, uint8_t code) {
-    uint8_t* byte = codes_row + (int64_t)t * (d / 4) + j / 4;
-    int sh = 2 * (j % 4);
+    uint8_t* byte = codes_row + code_byte(d, t, j);
+    int sh = code_shift(j);
     *byte = (uint8_t)((*byte & ~(3u << sh)) | ((unsigned)code << sh));
 }
 
 static uint8_t get_code(const uint8_t* codes_row, int32_t d, int32_t t, int32_t j) {
-    return (uint8_t)((codes_row[(int64_t)t * (d / 4) + j / 4] >> (2 * (j % 4))) & 3u);
+    return (uint8_t)((codes_row[code_byte(d, t, j)] >> code_shift(j)) & 3u);
 }
 
 static uint8_t* k_codes_row(const kivi_ref_cache* c, int64_t row) {
@@ -147,10 +162,11 @@ static uint16_t* k_pair(const kivi_ref_cache* c, int64_t row, int32_t g, int32_t
     int64_t groups = c->token_cap / c->group;
     return c->k_sz + ((row * groups + g) * c->head_dim + j) * 2;
 }
-/* (scale, zero) of value token t, channel group k */
+/* (scale, zero) of value token t, channel group k: per 32-token group, the pairs of channel
+ * group 0 for its 32 tokens, then of channel group 1, ... */
 static uint16_t* v_pair(const kivi_ref_cache* c, int64_t row, int32_t t, int32_t k) {
     int64_t per_tok = c->head_dim / c->group;
-    return c->v_sz + ((row * c->token_cap + t) * per_tok + k) * 2;
+    return c->v_sz + ((row * c->token_cap + (int64_t)(t / 32) * 32) * per_tok + k * 32 + t % 32) * 2;
 }
 static uint16_t* res_slot(const kivi_ref_cache* c, uint16_t* base, int64_t row, int32_t slot) {
     return base + (row * c->residual_cap + slot) * c->head_dim;

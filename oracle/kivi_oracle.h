@@ -43,12 +43,16 @@ void kivi_ref_quant_group(const uint16_t* x, ptrdiff_t stride, int32_t n,
 
 /* ---- the cache (host memory, same documented layout as the device cache) ----
  * row = b*kv_heads + h.
- *   k_codes, v_codes : [row][token_cap][head_dim/4] bytes; token t, channel j is in
- *                      byte t*(head_dim/4) + j/4 at bits 2*(j%4), 2*(j%4)+1.
+ *   k_codes, v_codes : [row][token_cap/32][1024] bytes, one 1024-byte tile per 32-token
+ *                      group (head_dim 128).  In a tile, 16-byte chunk ((u*8+q)*4+h) holds
+ *                      the 8 code bytes of channel quarter h (channels 32h..32h+31) for token
+ *                      4q+2u, then for token 4q+2u+1.  Those 8 bytes are two 32-bit words
+ *                      (channels 32h..+15, 32h+16..+31); in a word, channel 4i+b is in byte b
+ *                      at bits 2i, 2i+1.
  *   k_sz             : [row][token_cap/group][head_dim][2] fp16 (scale, zero) per
  *                      (token group, channel)  -- keys per-channel.
- *   v_sz             : [row][token_cap][head_dim/group][2] fp16 (scale, zero) per
- *                      (token, channel group)  -- values per-token.
+ *   v_sz             : [row][token_cap/32][head_dim/group][32][2] fp16 (scale, zero) per
+ *                      (token, channel group)  -- values per-token, grouped by 32 tokens.
  *   k_res, v_res     : [row][residual_cap][head_dim] fp16 ring; the n_res residual
  *                      tokens, oldest first, sit in slots (res_head+i) % residual_cap. */
 typedef struct kivi_ref_cache {

@@ -49,13 +49,14 @@ def ref_cache(batch, kv_heads, token_cap, k, v, n_quant):
 def assert_cache_equal(gpu, oracle, rows=None, upto=None, ring=True):
     """Bit-exact comparison of the packed history (tokens < upto) and the residual ring."""
     nq = oracle.n_quant if upto is None else upto
+    ng = nq // 32                                   # whole token groups (tiles)
     sel = slice(None) if rows is None else rows
-    kc = gpu.k_codes[sel, :nq].cpu().numpy()
-    vc = gpu.v_codes[sel, :nq].cpu().numpy()
-    ks = bits(gpu.k_sz[sel, : nq // 32])
-    vs = bits(gpu.v_sz[sel, :nq])
-    for name, a, b in (("k_codes", kc, oracle.k_codes[sel, :nq]), ("v_codes", vc, oracle.v_codes[sel, :nq]),
-                       ("k_sz", ks, oracle.k_sz[sel, : nq // 32]), ("v_sz", vs, oracle.v_sz[sel, :nq])):
+    kc = gpu.k_codes[sel, :ng].cpu().numpy()
+    vc = gpu.v_codes[sel, :ng].cpu().numpy()
+    ks = bits(gpu.k_sz[sel, :ng])
+    vs = bits(gpu.v_sz[sel, :ng])
+    for name, a, b in (("k_codes", kc, oracle.k_codes[sel, :ng]), ("v_codes", vc, oracle.v_codes[sel, :ng]),
+                       ("k_sz", ks, oracle.k_sz[sel, :ng]), ("v_sz", vs, oracle.v_sz[sel, :ng])):
         bad = np.argwhere(a != b)
         assert bad.size == 0, f"{name}: {bad.shape[0]} mismatches, first at {bad[0].tolist()}: " \
                               f"gpu {a[tuple(bad[0])]} oracle {b[tuple(bad[0])]}"

@@ -6,6 +6,7 @@ import torch
 
 from golden_io import quant_vectors
 from kivi_testlib import assert_cache_equal, bits, gpu_or_skip, ref_cache
+from layout import token_quarter_bytes, value_pairs
 from kv_cache_bit_quantize_amd import synth
 from oracle import ref
 
@@ -67,10 +68,11 @@ def test_hand_vectors(vec):
     kivi.kivi_quantize_v_per_token(v.to(dev), cache)
     kivi.kivi_quantize_k_per_channel(k.to(dev), cache)
     torch.cuda.synchronize()
-    assert bits(cache.v_sz[0, 0, 1]).tolist() == [vec["scale"], vec["zero"]]
-    assert cache.v_codes[0, 0, 8:16].cpu().tolist() == vec["packed"]
+    assert value_pairs(bits(cache.v_sz[0]))[0, 1].tolist() == [vec["scale"], vec["zero"]]
+    assert token_quarter_bytes(cache.v_codes[0].cpu().numpy(), 0, 1).tolist() == vec["packed"]
     assert bits(cache.k_sz[0, 0, 5]).tolist() == [vec["scale"], vec["zero"]]
-    assert ((cache.k_codes[0, :, 1].cpu() >> 2) & 3).tolist() == vec["codes"]
+    kc = cache.k_codes[0].cpu().numpy()
+    assert [int(token_quarter_bytes(kc, t, 0)[1] >> 2 & 3) for t in range(G)] == vec["codes"]
 
 
 KINDS = ["normal", "wide", "grid", "levels", "outlier", "tiny", "signed_zero", "extreme"]
@@ -117,12 +119,13 @@ def test_distributions_keys_and_values(kind):
     rc = ref.RefCache(B, H, D, G, 128, token_cap=T + off)
     rc.quantize_k(bits(sl).reshape(B * H, T, D), T, dst_off=off)
     rc.quantize_v(bits(sl).reshape(B * H, T, D), T, dst_off=off)
+    og = off // G
     for name in ("k_codes", "v_codes"):
-        assert np.array_equal(getattr(cache, name).cpu().numpy()[:, off:], getattr(rc, name)[:, off:]), name
-    assert np.array_equal(bits(cache.k_sz)[:, off // G:], rc.k_sz[:, off // G:])
-    assert np.array_equal(bits(cache.v_sz)[:, off:], rc.v_sz[:, off:])
+        assert np.array_equal(getattr(cache, name).cpu().numpy()[:, og:], getattr(rc, name)[:, og:]), name
+    assert np.array_equal(bits(cache.k_sz)[:, og:], rc.k_sz[:, og:])
+    assert np.array_equal(bits(cache.v_sz)[:, og:], rc.v_sz[:, og:])
     # nothing written before the offset
-    assert not cache.k_codes[:, :off].any() and not cache.v_codes[:, :off].any()
+    assert not cache.k_codes[:, :og].any() and not cache.v_codes[:, :og].any()
 
 
 @pytest.mark.parametrize("tokens", [1, 7, 33, 100])

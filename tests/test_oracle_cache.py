@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 
 from golden_io import key_values
+from layout import value_pairs
 from oracle import ref
 
 D, G, R = 128, 32, 128
@@ -45,10 +46,10 @@ def test_append_from_empty_matches_closed_form_and_prefill():
     p = ref.RefCache(B, H, D, G, R, token_cap=256)
     p.prefill(k, v, c.n_quant)
     nq = c.n_quant
-    assert np.array_equal(c.k_codes[:, :nq], p.k_codes[:, :nq])
-    assert np.array_equal(c.v_codes[:, :nq], p.v_codes[:, :nq])
+    assert np.array_equal(c.k_codes[:, : nq // G], p.k_codes[:, : nq // G])
+    assert np.array_equal(c.v_codes[:, : nq // G], p.v_codes[:, : nq // G])
     assert np.array_equal(c.k_sz[:, : nq // G], p.k_sz[:, : nq // G])
-    assert np.array_equal(c.v_sz[:, :nq], p.v_sz[:, :nq])
+    assert np.array_equal(c.v_sz[:, : nq // G], p.v_sz[:, : nq // G])
     for row in range(B * H):
         Kc, Vc = c.dequant_row(row)
         Kp, Vp = p.dequant_row(row)
@@ -123,7 +124,7 @@ def test_dequant_row_reconstructs_each_element_within_half_its_group_scale():
     for row in range(2):
         K, V = c.dequant_row(row)
         ks = f(c.k_sz[row, :, :, 0])                  # [groups, D]
-        vs = f(c.v_sz[row, :, :, 0])                  # [tokens, D/G]
+        vs = f(value_pairs(c.v_sz[row])[:, :, 0])     # [tokens, D/G]
         k_bound = np.repeat(ks, G, axis=0) * 0.5 * (1 + 2.0 ** -20)
         v_bound = np.repeat(vs, G, axis=1) * 0.5 * (1 + 2.0 ** -20)
         assert (np.abs(K[: 5 * G] - f(k[row, : 5 * G])) <= k_bound).all()

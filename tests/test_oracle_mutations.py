@@ -25,7 +25,17 @@ MUTATIONS = [
     ("zero_is_max", "*zero = kivi_ref_f32_to_f16(mn);", "*zero = kivi_ref_f32_to_f16(mx);", False),
     ("keep_negative_zero", "if (mn == 0.0f) mn = 0.0f;", "", False),
     ("keep_negative_zero_max", "if (mx == 0.0f) mx = 0.0f;", "", False),
-    ("msb_first_packing", "int sh = 2 * (j % 4);", "int sh = 6 - 2 * (j % 4);", False),
+    ("token_major_packing",
+     "return (int64_t)(t / 32) * 1024 + ((u * 8 + q) * 4 + h) * 16 + t1 * 8 + w * 4 + (c % 4);",
+     "return (int64_t)t * 32 + h * 8 + w * 4 + (c % 4);", False),
+    ("tile_chunk_order",
+     "return (int64_t)(t / 32) * 1024 + ((u * 8 + q) * 4 + h) * 16 + t1 * 8 + w * 4 + (c % 4);",
+     "return (int64_t)(t / 32) * 1024 + ((q * 2 + u) * 4 + h) * 16 + t1 * 8 + w * 4 + (c % 4);", False),
+    ("value_pairs_token_major",
+     "return c->v_sz + ((row * c->token_cap + (int64_t)(t / 32) * 32) * per_tok + k * 32 + t % 32) * 2;",
+     "return c->v_sz + ((row * c->token_cap + t) * per_tok + k) * 2;", False),
+    ("bit_order_packing", "static int code_shift(int32_t j) { return 2 * ((j % 16) / 4); }",
+     "static int code_shift(int32_t j) { return 2 * (j % 4); }", False),
     ("key_pair_per_token", "const uint16_t* kp = k_pair(c, row, t / G, j);",
      "const uint16_t* kp = k_pair(c, row, t % (c->token_cap / G), j);", False),
     ("value_pair_wrong_group", "const uint16_t* vp = v_pair(c, row, t, j / G);",

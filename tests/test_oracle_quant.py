@@ -12,15 +12,10 @@ import numpy as np
 import pytest
 
 from golden_io import quant_vectors
+from layout import token_quarter_bytes, unpack_codes, value_pairs
 from oracle import ref
 
 D, G = 128, 32
-
-
-def _unpack(codes_bytes):
-    """[..., D/4] packed bytes -> [..., D] codes (bits 2*(j%4) of byte j/4)."""
-    b = codes_bytes[..., :, None]
-    return ((b >> (2 * np.arange(4, dtype=np.uint8))) & 3).reshape(*codes_bytes.shape[:-1], -1)
 
 
 def _units(bits):
@@ -48,20 +43,22 @@ def test_hand_vectors_as_value_token(vec):
     src = np.zeros((1, 1, D), np.uint16)
     src[0, 0, 32:64] = vec["input"]
     c.quantize_v(src, 1)
-    assert c.v_sz[0, 0, 1].tolist() == [vec["scale"], vec["zero"]]
-    assert c.v_codes[0, 0, 8:16].tolist() == vec["packed"]
+    assert value_pairs(c.v_sz[0])[0, 1].tolist() == [vec["scale"], vec["zero"]]
+    assert token_quarter_bytes(c.v_codes[0], 0, 1).tolist() == vec["packed"]
 
 
 @pytest.mark.parametrize("vec", quant_vectors(), ids=lambda v: v["name"])
 def test_hand_vectors_as_key_channel(vec):
-    """The group as channel 5 of 32 key tokens: channel 5 is byte 1, bits 2-3 of each token."""
+    """The group as channel 5 of 32 key tokens: channel 5 = 4*1 + 1 is byte 1, bits 2-3 of
+    each token's first code word."""
     c = ref.RefCache(1, 1, D, G, 128, token_cap=2 * G)
     src = np.zeros((1, 2 * G, D), np.uint16)
     src[0, G:, 5] = vec["input"]
     c.quantize_k(src, 2 * G)
     assert c.k_sz[0, 1, 5].tolist() == [vec["scale"], vec["zero"]]
-    assert (c.k_codes[0, G:, 1] >> 2 & 3).tolist() == vec["codes"]
-    assert (c.k_codes[0, G:, 1] & 0xF3).tolist() == [0] * G   # channels 4, 6, 7 are zero groups
+    byte1 = np.array([token_quarter_bytes(c.k_codes[0], t, 0)[1] for t in range(G, 2 * G)])
+    assert (byte1 >> 2 & 3).tolist() == vec["codes"]
+    assert (byte1 & 0xF3).tolist() == [0] * G   # channels 1, 9, 13 are zero groups
 
 
 # ------------------------------------------------------------ random groups ----
@@ -92,11 +89,13 @@ def _quantize_as_values(x_bits):
     """Run groups [n, 32] through the per-token value quantizer (4 groups per token)."""
     n = x_bits.shape[0]
     tokens = n // 4
+    tokens -= tokens % G                          # whole token groups (cache tiles)
     c = ref.RefCache(1, 1, D, G, 128, token_cap=tokens)
     c.quantize_v(x_bits[: tokens * 4].reshape(1, tokens, D), tokens)
-    s = c.v_sz[0, :, :, 0].reshape(-1)
-    z = c.v_sz[0, :, :, 1].reshape(-1)
-    codes = _unpack(c.v_codes[0]).reshape(-1, G)
+    vp = value_pairs(c.v_sz[0])                    # [tokens, 4, 2]
+    s = vp[:, :, 0].reshape(-1)
+    z = vp[:, :, 1].reshape(-1)
+    codes = unpack_codes(c.v_codes[0]).reshape(-1, G)
     return s, z, codes
 
 
@@ -105,6 +104,7 @@ def test_brute_force_nearest_level(kind):
     rng = np.random.default_rng(100 + KINDS.index(kind))
     x = _groups(kind, 160_000, rng)
     s, z, codes = _quantize_as_values(x)
+    x = x[: codes.shape[0]]
     X, S, Z = _units(x), _units(s)[:, None], _units(z)[:, None]
     levels = Z[..., None] + S[..., None] * np.arange(4)            # [n, 1, 4]
     err = np.abs(X[..., None] - levels)                             # [n, G, 4]
@@ -126,6 +126,7 @@ def test_scale_is_nearest_fp16_of_range_over_3_and_zero_is_min(kind):
     rng = np.random.default_rng(200 + KINDS.index(kind))
     x = _groups(kind, 80_000, rng)
     s, z, _ = _quantize_as_values(x)
+    x = x[: s.shape[0]]
     X = _units(x)
     mn, mx = X.min(1), X.max(1)
     S = _units(s)
@@ -144,6 +145,7 @@ def test_reconstruction_invariants(kind):
     rng = np.random.default_rng(300 + KINDS.index(kind))
     x = _groups(kind, 80_000, rng)
     s, z, codes = _quantize_as_values(x)
+    x = x[: codes.shape[0]]
     xf = x.view(np.float16).astype(np.float64)
     sf = s.view(np.float16).astype(np.float64)[:, None]
     zf = z.view(np.float16).astype(np.float64)[:, None]
@@ -164,7 +166,7 @@ def test_reconstruction_invariants(kind):
 
 def test_codes_do_not_depend_on_element_order():
     rng = np.random.default_rng(5)
-    x = np.concatenate([_groups(k, 4000, rng) for k in KINDS])
+    x = np.concatenate([_groups(k, 4096, rng) for k in KINDS])
     perm = rng.permutation(G)
     s1, z1, c1 = _quantize_as_values(x)
     s2, z2, c2 = _quantize_as_values(np.ascontiguousarray(x[:, perm]))
@@ -174,7 +176,7 @@ def test_codes_do_not_depend_on_element_order():
 
 def test_signed_zeros_do_not_depend_on_order():
     rng = np.random.default_rng(6)
-    x = rng.choice(np.array([0x8000, 0x0000, 0x3C00, 0xBC00], np.uint16), (20000, G), p=[.45, .45, .05, .05])
+    x = rng.choice(np.array([0x8000, 0x0000, 0x3C00, 0xBC00], np.uint16), (20480, G), p=[.45, .45, .05, .05])
     s1, z1, c1 = _quantize_as_values(x)
     s2, z2, c2 = _quantize_as_values(np.ascontiguousarray(x[:, ::-1]))
     assert np.array_equal(s1, s2) and np.array_equal(z1, z2) and np.array_equal(c1[:, ::-1], c2)
@@ -193,13 +195,13 @@ def test_keys_per_channel_values_per_token_axes():
         for j in (0, 17, 127):
             s, z, codes = ref.quant_group(k[0, g * G:(g + 1) * G, j])
             assert c.k_sz[0, g, j].tolist() == [s, z]
-            assert np.array_equal(_unpack(c.k_codes[0, g * G:(g + 1) * G])[:, j], codes)
+            assert np.array_equal(unpack_codes(c.k_codes[0])[g * G:(g + 1) * G, j], codes)
             assert np.uint16(z).view(np.float16) == kf[g * G:(g + 1) * G, j].min()
     for t in (0, 33, 63):
         for kk in range(D // G):
             s, z, codes = ref.quant_group(k[0, t, kk * G:(kk + 1) * G])
-            assert c.v_sz[0, t, kk].tolist() == [s, z]
-            assert np.array_equal(_unpack(c.v_codes[0, t])[kk * G:(kk + 1) * G], codes)
+            assert value_pairs(c.v_sz[0])[t, kk].tolist() == [s, z]
+            assert np.array_equal(unpack_codes(c.v_codes[0])[t, kk * G:(kk + 1) * G], codes)
 
 
 def test_per_channel_keys_isolate_outlier_channels():
