@@ -13,7 +13,6 @@ using namespace kivi;
 
 namespace {
 
-constexpr int kMaxSplits = 1024;
 constexpr int64_t kTargetBlocks = 768;      // one round of resident workgroups on MI355X: 256 CUs x 3
 constexpr int kMinGroupsPerSplit = 8;
 

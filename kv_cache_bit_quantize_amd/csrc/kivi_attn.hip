@@ -68,9 +68,71 @@ __device__ __forceinline__ void load_q32(const uint16_t* q, float scale, float (
     }
 }
 
-// Channel offset c (0..15) of a 16-channel block -> bit position of its code in a word
-// that holds token 2s's block bytes 0,1 (or 2,3) in its low half and token 2s+1's in its
-// high half, after v_perm.  Used only to document the extraction table below.
+// Split partials cross workgroups, which may sit on different XCDs with separate L2 caches.
+// They are written and read with agent-scope atomic accesses (global_store / global_load with
+// the sc1 coherence bit), each coherent by itself.  Device-scope fences are avoided on
+// purpose: on this chip each one writes back and invalidates the whole L2 of the XCD, which
+// stalls every other workgroup streaming through it.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(float* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// s_waitcnt with vmcnt(0) and the other counters left free (expcnt 7, lgkmcnt 15)
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+// Log-sum-exp merge of one query row's split partials by the whole workgroup: the m and l of
+// every split are read once (spread over the threads), then each output channel sums its
+// splits' o with several loads in flight.  out = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M),
+// lse = (M + log2 L) ln 2.  Re-arms the row counter.
+__device__ __forceinline__ void merge_row(const AttnArgs& a, int64_t qrow) {
+    __shared__ float sh_sc[kMaxSplits];
+    __shared__ float sh_red[kWaves];
+    __shared__ float sh_half[2][kD];
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    float* rowp = a.ws + qrow * kPart;
+    const int64_t stride = a.q_rows * kPart;
+    float mloc = -INFINITY;
+    for (int s = t; s < a.splits; s += kBlock) {
+        const float ms = load_coherent(rowp + s * stride + kD);
+        sh_sc[s] = ms;
+        mloc = fmaxf(mloc, ms);
+    }
+    mloc = wave_max_xor(mloc, 1, 32);
+    if (lane == 0) sh_red[wave] = mloc;
+    __syncthreads();
+    float M = sh_red[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sh_red[w]);
+    __syncthreads();
+    float lloc = 0.0f;
+    for (int s = t; s < a.splits; s += kBlock) {
+        const float ms = sh_sc[s];
+        const float sc = ms == -INFINITY ? 0.0f : exp2f(ms - M);
+        sh_sc[s] = sc;
+        lloc = fmaf(load_coherent(rowp + s * stride + kD + 1), sc, lloc);
+    }
+    lloc = wave_sum_xor(lloc, 1, 32);
+    if (lane == 0) sh_red[wave] = lloc;
+    __syncthreads();
+    float L = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) L += sh_red[w];
+    const int j = t & (kD - 1), h = t >> 7;
+    float O = 0.0f;
+#pragma unroll 8
+    for (int s = h; s < a.splits; s += 2) O = fmaf(load_coherent(rowp + s * stride + j), sh_sc[s], O);
+    sh_half[h][j] = O;
+    __syncthreads();
+    if (t < kD) {
+        a.out[qrow * kD + t] = (uint16_t)f2h((sh_half[0][t] + sh_half[1][t]) / L);
+        if (t == 0) {
+            if (a.lse != nullptr) a.lse[qrow] = (M + log2f(L)) * 0.69314718055994531f;
+            a.counters[qrow] = 0u;
+        }
+    }
+}
 
 __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
     __shared__ uint4 sh_kq[2][kWaves][2][kD / 4];   // [parity][wave][half][16-ch block*4 + class]
@@ -392,41 +454,24 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
             L = fmaf(sh_l[w], sc, L);
             O = fmaf(sh_o[w][j], sc, O);
         }
-        part[j] = O;
+        store_coherent(&part[j], O);
         if (j == 0) {
-            part[kD] = M;
-            part[kD + 1] = L;
+            store_coherent(&part[kD], M);
+            store_coherent(&part[kD + 1], L);
         }
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // those stores have completed
     }
-    // The last workgroup of this row to finish merges every split's partial
-    // (log-sum-exp merge) and writes the output; it then re-arms the row counter.
-    __threadfence();
+    // The last workgroup of this row to arrive merges every split's partial and writes the
+    // output.  The counter add comes after every partial store of this workgroup completed
+    // (the wait above, then the barrier), and the merging workgroup issues its coherent loads
+    // only after its own add returned the final count, so it reads every partial.
     __syncthreads();
     __shared__ bool sh_last;
-    if (threadIdx.x == 0) sh_last = atomicAdd(&a.counters[qrow], 1u) == (unsigned)(a.splits - 1);
+    if (threadIdx.x == 0)
+        sh_last = __hip_atomic_fetch_add(&a.counters[qrow], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                  (unsigned)(a.splits - 1);
     __syncthreads();
-    if (!sh_last) return;
-    __threadfence();
-    if (threadIdx.x < kD) {
-        const int j = threadIdx.x;
-        const float* rowp = a.ws + qrow * kPart;
-        const int64_t stride = a.q_rows * kPart;
-        float M = -INFINITY;
-        for (int s = 0; s < a.splits; ++s) M = fmaxf(M, rowp[s * stride + kD]);
-        float L = 0.0f, O = 0.0f;
-        for (int s = 0; s < a.splits; ++s) {
-            const float ms = rowp[s * stride + kD];
-            if (ms == -INFINITY) continue;
-            const float sc = exp2f(ms - M);
-            L = fmaf(rowp[s * stride + kD + 1], sc, L);
-            O = fmaf(rowp[s * stride + j], sc, O);
-        }
-        a.out[qrow * kD + j] = (uint16_t)f2h(O / L);
-        if (j == 0) {
-            if (a.lse != nullptr) a.lse[qrow] = (M + log2f(L)) * 0.69314718055994531f;
-            a.counters[qrow] = 0u;
-        }
-    }
+    if (sh_last) merge_row(a, qrow);
 }
 
 hipError_t launch_decode_attn(const AttnArgs& a, hipStream_t s) {

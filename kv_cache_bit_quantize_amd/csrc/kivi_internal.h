@@ -6,6 +6,8 @@
 
 namespace kivi {
 
+constexpr int kMaxSplits = 1024;   // upper bound on split-K partitions of one decode call
+
 struct QuantArgs {          // kivi_quantize_{k,v}
     const uint16_t* src;
     int64_t src_row_stride;
