@@ -55,12 +55,16 @@ enum {
  *
  * Packed layout (four 2-bit codes per byte; D = 128, G = 32 here):
  *   k_codes, v_codes : uint8  [row][token_cap/G][1024]: one 1024-byte tile per 32-token
- *                      group.  In a tile, 16-byte chunk ((u*8 + q)*4 + h) holds the 8 code
- *                      bytes of channel quarter h (channels 32h..32h+31) of token 4q+2u,
- *                      then those of token 4q+2u+1 (q = 0..7, u = 0..1).  Those 8 bytes are
- *                      two little-endian 32-bit words (channels 32h..+15, 32h+16..+31); in
- *                      a word, channel 4i+b sits in byte b at bits 2i..2i+1, so masking the
- *                      word with 0x03030303 << 2i yields four consecutive channels' codes.
+ *                      group.  Codes are packed in little-endian 32-bit words; word w of a
+ *                      token holds channels 16w..16w+15, channel 16w + 4i + b in byte b at
+ *                      bits 2i..2i+1, so masking a word with 0x03030303 << 2i yields the
+ *                      codes of four consecutive channels, one per byte.  The two caches
+ *                      order the words inside a tile differently:
+ *                      v_codes: 16-byte chunk ((u*8 + q)*4 + h) holds words 2h and 2h+1
+ *                        (channels 32h..32h+31) of token 4q+2u, then those of token
+ *                        4q+2u+1 (q = 0..7, u = 0..1);
+ *                      k_codes: 16-byte chunk (16k + n) holds words k and 4+k of token n,
+ *                        then words k and 4+k of token 16+n (k = 0..3, n = 0..15).
  *   k_sz             : fp16   [row][token_cap/G][D][2]  (scale, zero) of key token group
  *                      g, channel j  -- keys are quantized per-channel over G tokens.
  *   v_sz             : fp16   [row][token_cap/G][D/G][G][2]  (scale, zero) of value token

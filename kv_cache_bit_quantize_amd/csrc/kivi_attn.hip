@@ -38,6 +38,16 @@ namespace kivi {
 
 constexpr int kWaves = kBlock / 64;
 constexpr int kPart = kD + 2;   // floats per partial: o[128], m, l
+// LDS table of one (parity, wave): two groups' digit planes, then a zero plane
+constexpr int kGroupTbl = 4 * kD;             // 4 digit planes of 128 channel bytes
+constexpr int kZeroPlane = 2 * kGroupTbl;
+constexpr int kTblBytes = kZeroPlane + kD;
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// value of lane 4*(lane/4) + i, for CTRL = quad_perm [i, i, i, i]
+template <int CTRL>
+__device__ __forceinline__ float quad_bcast(float v) { return dpp_f<CTRL>(v); }
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
@@ -135,7 +145,9 @@ __device__ __forceinline__ void merge_row(const AttnArgs& a, int64_t qrow) {
 }
 
 __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
-    __shared__ uint4 sh_kq[2][kWaves][2][kD / 4];   // [parity][wave][half][16-ch block*4 + class]
+    // Per (parity, wave): the fixed-point digits of q*s for the wave's two groups, as
+    // [group][digit plane d][128 channels] bytes, then one all-zero plane.
+    __shared__ __align__(16) uint8_t sh_tbl[2][kWaves][kTblBytes];
     __shared__ float sh_o[kWaves][kD];
     __shared__ float sh_m[kWaves], sh_l[kWaves];
 
@@ -145,9 +157,11 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
     const int hq = (int)(qrow % a.q_heads);
     const int64_t kvrow = b * a.kv_heads + hq / a.ratio;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int gh = lane >> 5, tq = (lane >> 2) & 7, qq = lane & 3;
-    const int wl = lane & 31;          // as fixed-point writer: channels 4wl .. 4wl+3
+    const int gh = lane >> 5;          // group of the wave-iteration this lane serves
+    const int tq = (lane >> 2) & 7, qq = lane & 3;   // value role: tokens 4tq.., channel group qq
+    const int wl = lane & 31;          // fixed-point writer role: channels 4wl .. 4wl+3
     const int wk = wl & 3;             // their position i inside the 16-channel block
+    const int mrow = lane & 15, kgrp = lane >> 4;     // matrix-operand role
 
     // query channels 4wl..4wl+3 in the log2 domain
     float qw[4];
@@ -160,6 +174,15 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
     }
     // codes of channels 4i..4i+3 arrive multiplied by 1, 4, 16, 16 (i = 0..3)
     const float cls_div = wk == 0 ? 1.0f : (wk == 1 ? 0.25f : 0.0625f);
+
+    // A operand of tile t (rows 4t..4t+3 = digits 0..3 of its group, all other rows zero):
+    // this lane's 16 bytes come from its own digit plane or from the zero plane.
+    int a_off[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+        a_off[t] = ((mrow >> 2) == t) ? (t >> 1) * kGroupTbl + (mrow & 3) * kD + 16 * kgrp : kZeroPlane + 16 * kgrp;
+    // the zero planes of both parities, written once
+    reinterpret_cast<uint32_t*>(&sh_tbl[lane >> 5][wave][kZeroPlane])[lane & 31] = 0u;
 
     float acc[32];
 #pragma unroll
@@ -188,24 +211,22 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
 
     // one wave-iteration's global loads (issued one iteration ahead of their use)
     struct Loads {
-        uint4 kp;          // (scale, zero) of key channels 4wl..4wl+3 of group gc
-        uint2 kw[4], vw[4];   // key / value codes of tokens 4tq..4tq+3, channels of quarter qq
+        uint4 kp;          // (scale, zero) of key channels 4wl..4wl+3 of group gh
+        uint4 kc[2];       // key tile chunk `lane` of both groups (matrix operand B)
+        uint2 vw[4];       // value codes of tokens 4tq..4tq+3, channel quarter qq, group gh
         uint32_t vp[4];    // (scale, zero) of the value channel group qq of those tokens
     };
-    // Tile chunks wl and 32 + wl of group gc hold the quarter qq of tokens 4tq..4tq+3
-    // (wl = 4tq + qq), so each load instruction reads two contiguous 512-byte spans.
     auto load_iter = [&](int it) {
         Loads L;
-        const int g = gb + 2 * it + gh;
-        const int gc = g < ge ? g : gb;               // in-bounds address for an idle half
+        const int g0 = gb + 2 * it;
+        const int g1 = g0 + 1 < ge ? g0 + 1 : gb;     // in-bounds address for an idle half
+        const int gc = gh ? g1 : g0;
         L.kp = *reinterpret_cast<const uint4*>(kp_row + (int64_t)gc * kD + 4 * wl);
-        const uint4* kt = reinterpret_cast<const uint4*>(kc_row + (int64_t)gc * kTileBytes);
+        L.kc[0] = reinterpret_cast<const uint4*>(kc_row + (int64_t)g0 * kTileBytes)[lane];
+        L.kc[1] = reinterpret_cast<const uint4*>(kc_row + (int64_t)g1 * kTileBytes)[lane];
+        // value tile chunks wl and 32 + wl of group gc hold quarter qq of tokens 4tq..4tq+3
         const uint4* vt = reinterpret_cast<const uint4*>(vc_row + (int64_t)gc * kTileBytes);
-        const uint4 k0 = kt[wl], k1 = kt[32 + wl], v0 = vt[wl], v1 = vt[32 + wl];
-        L.kw[0] = make_uint2(k0.x, k0.y);
-        L.kw[1] = make_uint2(k0.z, k0.w);
-        L.kw[2] = make_uint2(k1.x, k1.y);
-        L.kw[3] = make_uint2(k1.z, k1.w);
+        const uint4 v0 = vt[wl], v1 = vt[32 + wl];
         L.vw[0] = make_uint2(v0.x, v0.y);
         L.vw[1] = make_uint2(v0.z, v0.w);
         L.vw[2] = make_uint2(v1.x, v1.y);
@@ -223,13 +244,11 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
     for (int it = 0; it < iters; ++it) {
         const Loads nxt = load_iter(it + 1 < iters ? it + 1 : it);
         const bool gvalid = gb + 2 * it + gh < ge;
-        const uint4 kp = cur.kp;
-        const uint2* kw = cur.kw;
-        const uint2* vw = cur.vw;
-        const uint32_t* vp = cur.vp;
+        uint8_t* tbl = &sh_tbl[it & 1][wave][0];
 
-        // ---- q*s of group gc as 30-bit fixed point, four byte limbs, into LDS
-        const uint32_t pr[4] = {kp.x, kp.y, kp.z, kp.w};
+        // ---- q*s of this half's group as 30-bit fixed point, four signed byte digits,
+        // stored as digit planes
+        const uint32_t pr[4] = {cur.kp.x, cur.kp.y, cur.kp.z, cur.kp.w};
         float qs[4], az = 0.0f, mx = 0.0f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -251,50 +270,43 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
             const uint32_t B = __builtin_amdgcn_perm(dg[1], dg[0], 0x07030602u);
             const uint32_t C = __builtin_amdgcn_perm(dg[3], dg[2], 0x05010400u);
             const uint32_t E = __builtin_amdgcn_perm(dg[3], dg[2], 0x07030602u);
-            uint4 limbs;
-            limbs.x = __builtin_amdgcn_perm(C, A, 0x05040100u);   // digit 0 of the 4 channels
-            limbs.y = __builtin_amdgcn_perm(C, A, 0x07060302u);   // digit 1
-            limbs.z = __builtin_amdgcn_perm(E, B, 0x05040100u);   // digit 2
-            limbs.w = __builtin_amdgcn_perm(E, B, 0x07060302u);   // digit 3
-            sh_kq[it & 1][wave][gh][wl] = limbs;
+            uint32_t* plane = reinterpret_cast<uint32_t*>(tbl + gh * kGroupTbl) + wl;
+            plane[0 * kD / 4] = __builtin_amdgcn_perm(C, A, 0x05040100u);   // digit 0 of the 4 channels
+            plane[1 * kD / 4] = __builtin_amdgcn_perm(C, A, 0x07060302u);   // digit 1
+            plane[2 * kD / 4] = __builtin_amdgcn_perm(E, B, 0x05040100u);   // digit 2
+            plane[3 * kD / 4] = __builtin_amdgcn_perm(E, B, 0x07060302u);   // digit 3
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // ---- logits of the lane's 4 tokens (exact integer dot products), one 16-channel
-        // block of limb words at a time: [block 2qq+wd][class i] = uint4 {digit 0..3}
-        const float kscale = __builtin_ldexpf(1.0f, -sh);
-        int dd[4][4];
+
+        // ---- key logits on the matrix cores: tile t = 2*group + token half, K = 64
+        // channels per instruction.  Row 4t + d of the accumulator collects digit d's dot
+        // product for tile t's 16 tokens, so lane L ends with the four digit sums of token L.
+        v4i cacc = {0, 0, 0, 0};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dd[i][0] = dd[i][1] = dd[i][2] = dd[i][3] = 0;
+        for (int t = 0; t < 4; ++t) {
+            const uint4 kc = cur.kc[t >> 1];
 #pragma unroll
-        for (int wd = 0; wd < 2; ++wd) {
-            uint4 lw[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) lw[k] = sh_kq[it & 1][wave][gh][8 * qq + 4 * wd + k];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t x = wd ? kw[i].y : kw[i].x;
-                const uint32_t cm[4] = {x & 0x03030303u, x & 0x0C0C0C0Cu, x & 0x30303030u, (x >> 2) & 0x30303030u};
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    dd[i][0] = __builtin_amdgcn_sdot4((int)cm[k], (int)lw[k].x, dd[i][0], false);
-                    dd[i][1] = __builtin_amdgcn_sdot4((int)cm[k], (int)lw[k].y, dd[i][1], false);
-                    dd[i][2] = __builtin_amdgcn_sdot4((int)cm[k], (int)lw[k].z, dd[i][2], false);
-                    dd[i][3] = __builtin_amdgcn_sdot4((int)cm[k], (int)lw[k].w, dd[i][3], false);
-                }
+            for (int kh = 0; kh < 2; ++kh) {
+                const uint32_t x = (t & 1) ? (kh ? kc.w : kc.z) : (kh ? kc.y : kc.x);
+                const v4i bop = {(int)(x & 0x03030303u), (int)(x & 0x0C0C0C0Cu), (int)(x & 0x30303030u),
+                                 (int)((x >> 2) & 0x30303030u)};
+                const v4i aop = *reinterpret_cast<const v4i*>(tbl + a_off[t] + 64 * kh);
+                cacc = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop, bop, cacc, 0, 0, 0);
             }
         }
-        float lg[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int hi = dd[i][3] * 256 + dd[i][2], lo = dd[i][1] * 256 + dd[i][0];
-            const float tot = quad_sum(fmaf((float)hi, 65536.0f, (float)lo));
-            lg[i] = gvalid ? fmaf(tot, kscale, az) : -INFINITY;
+        float lg;
+        {
+            const int hi = cacc[3] * 256 + cacc[2], lo = cacc[1] * 256 + cacc[0];
+            const float tot = fmaf((float)hi, 65536.0f, (float)lo);
+            lg = gvalid ? fmaf(tot, __builtin_ldexpf(1.0f, -sh), az) : -INFINITY;
         }
 
         // ---- online softmax over the wave's 64 tokens (rescale only when the max rises)
-        const float mloc = wave_max_quads(fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3])));
+        float mloc = half_max(lg);
+        mloc = fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mloc), 0)),
+                     __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mloc), 32)));
         if (mloc > m) {
             const float al = exp2f(m - mloc);
 #pragma unroll
@@ -305,16 +317,19 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
             lsum *= al;
             m = mloc;
         }
-        float p[4], w[4], smax = 0.0f;
+        const float pt = exp2f(lg - m);      // this lane's token
+        lsum += pt;
+        // value role: the weights of tokens 4tq..4tq+3 sit in this lane's quad
+        const float p[4] = {quad_bcast<0x00>(pt), quad_bcast<0x55>(pt), quad_bcast<0xAA>(pt), quad_bcast<0xFF>(pt)};
+        float w[4], smax = 0.0f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            p[i] = exp2f(lg[i] - m);
-            const float s = h2f(vp[i] & 0xffffu);
+            const float s = h2f(cur.vp[i] & 0xffffu);
             w[i] = p[i] * s;
-            zacc = fmaf(p[i], h2f(vp[i] >> 16), zacc);
-            lsum += p[i];
+            zacc = fmaf(p[i], h2f(cur.vp[i] >> 16), zacc);
             smax = fmaxf(smax, s);
         }
+        const uint2* vw = cur.vw;
         // value weights 16*w*vs must stay below 2^15: shrink vs (a power of two) if needed
         if (__builtin_amdgcn_ballot_w64(smax * vs > 2048.0f || vs == 0.0f)) {
             const float gm = wave_max_xor(smax, 1, 32);
@@ -408,9 +423,9 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
             const float alpha = (m == -INFINITY) ? 0.0f : exp2f(m - m_new);
             const float p0 = ok0 ? exp2f(l0 - m_new) : 0.0f;
             const float p1 = ok1 ? exp2f(l1 - m_new) : 0.0f;
-            // the main loop counted each token once per lane of its quarter group; here each
-            // token pair is also held by the 4 lanes of one tp, so lsum stays consistent
-            lsum = lsum * alpha + p0 + p1;
+            // lsum holds one share per token: the quantized tokens' in the lane that owned
+            // them, a residual pair's in the qq = 0 lane of its quad
+            lsum = lsum * alpha + (qq == 0 ? p0 + p1 : 0.0f);
             const uint4* v0 = reinterpret_cast<const uint4*>(a.v_res + r0);
             const uint4* v1 = reinterpret_cast<const uint4*>(a.v_res + r1);
 #pragma unroll
@@ -429,7 +444,7 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
     }
 
     // wave result: sum over the 16 lanes that share a channel quarter
-    lsum = wave_sum_xor(lsum, 4, 32);
+    lsum = wave_sum_xor(lsum, 1, 32);
 #pragma unroll
     for (int c = 0; c < 32; ++c) o[c] = wave_sum_xor(o[c], 4, 32);
     if ((lane >> 2) == 0) {

@@ -17,17 +17,25 @@ constexpr int kBlock = 256;         // threads per workgroup (4 wave64)
 // Packed code layout (include/kivi.h).  16 channels 16w..16w+15 of a token form one 32-bit
 // word; channel offset c = 4i + b (0..15) sits in byte b at bits 2i..2i+1, i.e. at bit
 // 8b + 2i, so masking a word with 0x03030303 << 2i leaves the codes of channels 4i..4i+3,
-// one per byte.  A row holds one 1024-byte tile per 32-token group; in a tile, 16-byte
-// chunk ((u*8 + q)*4 + h) holds quarter h (words 2h, 2h+1) of token 4q+2u, then of token
-// 4q+2u+1.  A half-wave whose lane L = 4q + h loads chunks L and 32 + L therefore reads
-// two contiguous 512-byte spans and gets the quarter h of tokens 4q..4q+3.
+// one per byte.  A row holds one 1024-byte tile per 32-token group.
+//  * Value tiles: 16-byte chunk ((u*8 + q)*4 + h) holds words 2h, 2h+1 of token 4q+2u, then
+//    of token 4q+2u+1.  A half-wave whose lane L = 4q + h loads chunks L and 32 + L reads
+//    two contiguous 512-byte spans and gets quarter h of tokens 4q..4q+3.
+//  * Key tiles: 16-byte chunk (16k + n) holds words k, 4+k of token n, then of token 16+n.
+//    Lane 16k + n of a wave loading chunk (lane) reads the whole tile in one contiguous
+//    access and gets exactly the codes the integer matrix instruction wants from it as the
+//    K x N operand (channels 16k..16k+15 and 64+16k.. of tokens n and 16+n).
 __host__ __device__ constexpr int code_bit(int c) { return 8 * (c & 3) + 2 * (c >> 2); }
 constexpr int kTileBytes = kG * kD / 4;     // 1024
 
-// byte offset, inside a row, of word w (0..7) of token t
-__host__ __device__ constexpr int64_t code_word_offset(int64_t t, int w) {
+// byte offset, inside a row, of word w (0..7) of value token t
+__host__ __device__ constexpr int64_t value_word_offset(int64_t t, int w) {
     return (t >> 5) * kTileBytes +
            ((((t & 3) >> 1) * 8 + ((t & 31) >> 2)) * 4 + (w >> 1)) * 16 + (t & 1) * 8 + (w & 1) * 4;
+}
+// byte offset, inside a row, of word w (0..7) of key token t
+__host__ __device__ constexpr int64_t key_word_offset(int64_t t, int w) {
+    return (t >> 5) * kTileBytes + ((w & 3) * 16 + (t & 15)) * 16 + ((t >> 4) & 1) * 8 + (w >> 2) * 4;
 }
 // index (in 32-bit pairs), inside a row, of the value (scale, zero) of token t, group k
 __host__ __device__ constexpr int64_t value_pair_index(int64_t t, int k) {

@@ -45,7 +45,7 @@ __device__ void quant_k_tile(const uint16_t* __restrict__ tile, float* sh_mn, fl
         GroupQ q{sh_mn[j], sh_s[j], 0u};
         word |= code_of(h2f(bits), q) << code_bit(c);
     }
-    *reinterpret_cast<uint32_t*>(codes_dst + code_word_offset(t, w)) = word;
+    *reinterpret_cast<uint32_t*>(codes_dst + key_word_offset(t, w)) = word;
 }
 
 // Eight consecutive channels of one value token (this thread's share of a 32-channel
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(kBlock) void quantize_v_kernel(QuantArgs a) {
     if (live) {
         const int64_t tok = a.dst_token_off + t;          // token inside the row's history
         if ((l16 & 1) == 0)
-            *reinterpret_cast<uint32_t*>(a.v_codes + row * a.token_cap * kRowBytes + code_word_offset(tok, l16 >> 1)) = word;
+            *reinterpret_cast<uint32_t*>(a.v_codes + row * a.token_cap * kRowBytes + value_word_offset(tok, l16 >> 1)) = word;
         if ((l16 & 3) == 0)
             reinterpret_cast<uint32_t*>(a.v_sz)[row * a.token_cap * (kD / kG) + value_pair_index(tok, l16 >> 2)] = pair;
     }
@@ -157,7 +157,7 @@ __global__ __launch_bounds__(kBlock) void append_flush_kernel(AppendArgs a) {
             const uint32_t word = quant_v_8(vr[t * 16 + l16], l16 & 1, &pair);
             const int64_t tok = dst_tok + t;
             if ((l16 & 1) == 0)
-                *reinterpret_cast<uint32_t*>(a.v_codes + row * a.token_cap * kRowBytes + code_word_offset(tok, l16 >> 1)) = word;
+                *reinterpret_cast<uint32_t*>(a.v_codes + row * a.token_cap * kRowBytes + value_word_offset(tok, l16 >> 1)) = word;
             if ((l16 & 3) == 0)
                 reinterpret_cast<uint32_t*>(a.v_sz)[row * a.token_cap * (kD / kG) + value_pair_index(tok, l16 >> 2)] = pair;
         }

@@ -126,29 +126,39 @@ void kivi_ref_quant_group(const uint16_t* x, ptrdiff_t stride, int32_t n,
 
 static int64_t row_count(const kivi_ref_cache* c) { return (int64_t)c->batch * c->kv_heads; }
 
-/* Code position of (token t, channel j) in a row of packed codes.  The row is a sequence
- * of 1024-byte tiles, one per 32-token group.  Inside a tile, 16-byte chunk
- * ((u*8 + q)*4 + h) holds, for channel quarter h (channels 32h..32h+31), the 8 bytes of
- * token 4q + 2u followed by the 8 bytes of token 4q + 2u + 1 (q = 0..7, u = 0..1).  A
- * token's 8 bytes for a quarter are two little-endian 32-bit words (channels 32h..32h+15,
- * then 32h+16..32h+31); in a word of 16 channels, channel 4i + b sits in byte b at bits
- * 2i, 2i+1. */
-static int64_t code_byte(int32_t d, int32_t t, int32_t j) {
-    (void)d;
+/* Code positions.  Codes are packed four to a byte: a little-endian 32-bit word holds the
+ * 16 channels 16w..16w+15 of one token, channel 16w + 4i + b in byte b at bits 2i, 2i+1.
+ * A row is a sequence of 1024-byte tiles, one per 32-token group; the key and value caches
+ * order the words inside a tile differently.
+ *
+ * Value tiles: 16-byte chunk ((u*8 + q)*4 + h) holds, for channel quarter h (channels
+ * 32h..32h+31), the 8 bytes of token 4q + 2u followed by the 8 bytes of token 4q + 2u + 1
+ * (q = 0..7, u = 0..1); a token's 8 bytes for a quarter are its words 2h and 2h + 1.
+ *
+ * Key tiles: 16-byte chunk (16k + n) (k = 0..3, n = 0..15) holds words k and 4 + k of
+ * token n, then words k and 4 + k of token 16 + n. */
+static int64_t value_code_byte(int32_t t, int32_t j) {
     int32_t tt = t % 32, q = tt / 4, u = (tt % 4) / 2, t1 = tt % 2;
     int32_t h = j / 32, w = (j % 32) / 16, c = j % 16;
     return (int64_t)(t / 32) * 1024 + ((u * 8 + q) * 4 + h) * 16 + t1 * 8 + w * 4 + (c % 4);
 }
+static int64_t key_code_byte(int32_t t, int32_t j) {
+    int32_t tt = t % 32, w = j / 16, c = j % 16;
+    return (int64_t)(t / 32) * 1024 + ((w % 4) * 16 + tt % 16) * 16 + (tt / 16) * 8 + (w / 4) * 4 + (c % 4);
+}
+static int64_t code_byte(int key, int32_t t, int32_t j) {
+    return key ? key_code_byte(t, j) : value_code_byte(t, j);
+}
 static int code_shift(int32_t j) { return 2 * ((j % 16) / 4); }
 
-static void put_code(uint8_t* codes_row, int32_t d, int32_t t, int32_t j, uint8_t code) {
-    uint8_t* byte = codes_row + code_byte(d, t, j);
+static void put_code(uint8_t* codes_row, int key, int32_t t, int32_t j, uint8_t code) {
+    uint8_t* byte = codes_row + code_byte(key, t, j);
     int sh = code_shift(j);
     *byte = (uint8_t)((*byte & ~(3u << sh)) | ((unsigned)code << sh));
 }
 
-static uint8_t get_code(const uint8_t* codes_row, int32_t d, int32_t t, int32_t j) {
-    return (uint8_t)((codes_row[code_byte(d, t, j)] >> code_shift(j)) & 3u);
+static uint8_t get_code(const uint8_t* codes_row, int key, int32_t t, int32_t j) {
+    return (uint8_t)((codes_row[code_byte(key, t, j)] >> code_shift(j)) & 3u);
 }
 
 static uint8_t* k_codes_row(const kivi_ref_cache* c, int64_t row) {
@@ -191,7 +201,7 @@ void kivi_ref_quantize_k(kivi_ref_cache* c, const uint16_t* src, int32_t tokens,
                 uint16_t* pr = k_pair(c, row, cg, j);
                 kivi_ref_quant_group(s_row + (int64_t)t0 * d + j, d, G, &pr[0], &pr[1], codes);
                 for (int32_t i = 0; i < G; ++i)
-                    put_code(k_codes_row(c, row), d, dst_off + t0 + i, j, codes[i]);
+                    put_code(k_codes_row(c, row), 1, dst_off + t0 + i, j, codes[i]);
             }
         }
     }
@@ -210,7 +220,7 @@ void kivi_ref_quantize_v(kivi_ref_cache* c, const uint16_t* src, int32_t tokens,
                 uint16_t* pr = v_pair(c, row, dst_off + t, k);
                 kivi_ref_quant_group(s_row + (int64_t)t * d + k * G, 1, G, &pr[0], &pr[1], codes);
                 for (int32_t i = 0; i < G; ++i)
-                    put_code(v_codes_row(c, row), d, dst_off + t, k * G + i, codes[i]);
+                    put_code(v_codes_row(c, row), 0, dst_off + t, k * G + i, codes[i]);
             }
         }
     }
@@ -291,8 +301,8 @@ void kivi_ref_dequant_row(const kivi_ref_cache* c, int32_t row, double* K, doubl
         for (int32_t j = 0; j < d; ++j) {
             const uint16_t* kp = k_pair(c, row, t / G, j);
             const uint16_t* vp = v_pair(c, row, t, j / G);
-            double kc = get_code(k_codes_row(c, row), d, t, j);
-            double vc = get_code(v_codes_row(c, row), d, t, j);
+            double kc = get_code(k_codes_row(c, row), 1, t, j);
+            double vc = get_code(v_codes_row(c, row), 0, t, j);
             K[(int64_t)t * d + j] = (double)kivi_ref_f16_to_f32(kp[1]) + kc * (double)kivi_ref_f16_to_f32(kp[0]);
             V[(int64_t)t * d + j] = (double)kivi_ref_f16_to_f32(vp[1]) + vc * (double)kivi_ref_f16_to_f32(vp[0]);
         }

@@ -44,11 +44,11 @@ void kivi_ref_quant_group(const uint16_t* x, ptrdiff_t stride, int32_t n,
 /* ---- the cache (host memory, same documented layout as the device cache) ----
  * row = b*kv_heads + h.
  *   k_codes, v_codes : [row][token_cap/32][1024] bytes, one 1024-byte tile per 32-token
- *                      group (head_dim 128).  In a tile, 16-byte chunk ((u*8+q)*4+h) holds
- *                      the 8 code bytes of channel quarter h (channels 32h..32h+31) for token
- *                      4q+2u, then for token 4q+2u+1.  Those 8 bytes are two 32-bit words
- *                      (channels 32h..+15, 32h+16..+31); in a word, channel 4i+b is in byte b
- *                      at bits 2i, 2i+1.
+ *                      group (head_dim 128).  A little-endian 32-bit word holds channels
+ *                      16w..16w+15 of one token, channel 16w+4i+b in byte b at bits 2i, 2i+1.
+ *                      v_codes tiles: 16-byte chunk ((u*8+q)*4+h) holds words 2h, 2h+1 of
+ *                      token 4q+2u, then of token 4q+2u+1.  k_codes tiles: 16-byte chunk
+ *                      (16k+n) holds words k, 4+k of token n, then of token 16+n.
  *   k_sz             : [row][token_cap/group][head_dim][2] fp16 (scale, zero) per
  *                      (token group, channel)  -- keys per-channel.
  *   v_sz             : [row][token_cap/32][head_dim/group][32][2] fp16 (scale, zero) per

@@ -1,9 +1,10 @@
 """Readers of the packed cache layout documented in include/kivi.h, for tests.
 
-Codes: one 1024-byte tile per 32-token group.  In a tile, 16-byte chunk ((u*8+q)*4+h)
-holds the 8 code bytes of channel quarter h (channels 32h..32h+31) of token 4q+2u, then
-of token 4q+2u+1; those 8 bytes are two 32-bit words (channels 32h..+15 and 32h+16..+31)
-and in a word channel 4i+b sits in byte b at bits 2i, 2i+1.
+Codes: one 1024-byte tile per 32-token group.  A little-endian 32-bit word holds the 16
+channels 16w..16w+15 of one token, channel 16w + 4i + b in byte b at bits 2i, 2i+1.
+Value tiles: 16-byte chunk ((u*8+q)*4+h) holds words 2h and 2h+1 of token 4q+2u, then of
+token 4q+2u+1.  Key tiles: 16-byte chunk (16k+n) holds words k and 4+k of token n, then of
+token 16+n.
 Value pairs: per 32-token group, [channel group][token in group][scale, zero].
 """
 import numpy as np
@@ -11,8 +12,8 @@ import numpy as np
 D, G = 128, 32
 
 
-def code_pos(t, j):
-    """(byte offset within the row, bit shift) of token t, channel j."""
+def value_code_pos(t, j):
+    """(byte offset within the row, bit shift) of value token t, channel j."""
     t, j = np.asarray(t), np.asarray(j)
     tt = t % 32
     q, u, t1 = tt // 4, (tt % 4) // 2, tt % 2
@@ -21,16 +22,35 @@ def code_pos(t, j):
     return byte, 2 * (c // 4)
 
 
-def unpack_codes(tiles):
-    """[..., n_tiles, 1024] uint8 -> [..., n_tiles*32, 128] codes (token-major)."""
+def key_code_pos(t, j):
+    """(byte offset within the row, bit shift) of key token t, channel j."""
+    t, j = np.asarray(t), np.asarray(j)
+    tt = t % 32
+    w, c = j // 16, j % 16
+    chunk = (w % 4) * 16 + tt % 16
+    byte = (t // 32) * 1024 + chunk * 16 + (tt // 16) * 8 + (w // 4) * 4 + (c % 4)
+    return byte, 2 * (c // 4)
+
+
+def _unpack(tiles, pos):
     tiles = np.asarray(tiles)
     lead = tiles.shape[:-2]
     flat = tiles.reshape(*lead, -1)
     T = tiles.shape[-2] * 32
     t = np.arange(T)[:, None]
     j = np.arange(D)[None, :]
-    byte, shift = code_pos(t, j)
+    byte, shift = pos(t, j)
     return (flat[..., byte] >> shift.astype(np.uint8)) & 3
+
+
+def unpack_value_codes(tiles):
+    """[..., n_tiles, 1024] uint8 -> [..., n_tiles*32, 128] codes (token-major)."""
+    return _unpack(tiles, value_code_pos)
+
+
+def unpack_key_codes(tiles):
+    """[..., n_tiles, 1024] uint8 -> [..., n_tiles*32, 128] codes (token-major)."""
+    return _unpack(tiles, key_code_pos)
 
 
 def value_pairs(v_sz):
@@ -41,7 +61,14 @@ def value_pairs(v_sz):
 
 
 def token_quarter_bytes(tiles_row, t, h):
-    """The 8 code bytes of token t, channel quarter h, from one row's tiles [n, 1024]."""
+    """The 8 value-code bytes of token t, channel quarter h, from one row's tiles [n, 1024]."""
     flat = np.asarray(tiles_row).reshape(-1)
-    start, _ = code_pos(t, 32 * h)
+    start, _ = value_code_pos(t, 32 * h)
     return flat[start:start + 8]
+
+
+def key_word_bytes(tiles_row, t, w):
+    """The 4 key-code bytes of word w (channels 16w..16w+15) of token t, from one row's tiles."""
+    flat = np.asarray(tiles_row).reshape(-1)
+    start, _ = key_code_pos(t, 16 * w)
+    return flat[start:start + 4]

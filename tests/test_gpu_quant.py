@@ -6,7 +6,7 @@ import torch
 
 from golden_io import quant_vectors
 from kivi_testlib import assert_cache_equal, bits, gpu_or_skip, ref_cache
-from layout import token_quarter_bytes, value_pairs
+from layout import key_word_bytes, token_quarter_bytes, value_pairs
 from kv_cache_bit_quantize_amd import synth
 from oracle import ref
 
@@ -72,7 +72,7 @@ def test_hand_vectors(vec):
     assert token_quarter_bytes(cache.v_codes[0].cpu().numpy(), 0, 1).tolist() == vec["packed"]
     assert bits(cache.k_sz[0, 0, 5]).tolist() == [vec["scale"], vec["zero"]]
     kc = cache.k_codes[0].cpu().numpy()
-    assert [int(token_quarter_bytes(kc, t, 0)[1] >> 2 & 3) for t in range(G)] == vec["codes"]
+    assert [int(key_word_bytes(kc, t, 0)[1] >> 2 & 3) for t in range(G)] == vec["codes"]
 
 
 KINDS = ["normal", "wide", "grid", "levels", "outlier", "tiny", "signed_zero", "extreme"]

@@ -34,6 +34,14 @@ MUTATIONS = [
     ("value_pairs_token_major",
      "return c->v_sz + ((row * c->token_cap + (int64_t)(t / 32) * 32) * per_tok + k * 32 + t % 32) * 2;",
      "return c->v_sz + ((row * c->token_cap + t) * per_tok + k) * 2;", False),
+    ("key_token_major_packing",
+     "return (int64_t)(t / 32) * 1024 + ((w % 4) * 16 + tt % 16) * 16 + (tt / 16) * 8 + (w / 4) * 4 + (c % 4);",
+     "return (int64_t)t * 32 + w * 4 + (c % 4);", False),
+    ("key_chunk_order",
+     "return (int64_t)(t / 32) * 1024 + ((w % 4) * 16 + tt % 16) * 16 + (tt / 16) * 8 + (w / 4) * 4 + (c % 4);",
+     "return (int64_t)(t / 32) * 1024 + ((tt % 16) * 4 + w % 4) * 16 + (tt / 16) * 8 + (w / 4) * 4 + (c % 4);", False),
+    ("keys_in_value_order", "return key ? key_code_byte(t, j) : value_code_byte(t, j);",
+     "return value_code_byte(t, j);", False),
     ("bit_order_packing", "static int code_shift(int32_t j) { return 2 * ((j % 16) / 4); }",
      "static int code_shift(int32_t j) { return 2 * (j % 4); }", False),
     ("key_pair_per_token", "const uint16_t* kp = k_pair(c, row, t / G, j);",

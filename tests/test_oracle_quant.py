@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 from golden_io import quant_vectors
-from layout import token_quarter_bytes, unpack_codes, value_pairs
+from layout import key_word_bytes, token_quarter_bytes, unpack_key_codes, unpack_value_codes, value_pairs
 from oracle import ref
 
 D, G = 128, 32
@@ -56,7 +56,7 @@ def test_hand_vectors_as_key_channel(vec):
     src[0, G:, 5] = vec["input"]
     c.quantize_k(src, 2 * G)
     assert c.k_sz[0, 1, 5].tolist() == [vec["scale"], vec["zero"]]
-    byte1 = np.array([token_quarter_bytes(c.k_codes[0], t, 0)[1] for t in range(G, 2 * G)])
+    byte1 = np.array([key_word_bytes(c.k_codes[0], t, 0)[1] for t in range(G, 2 * G)])
     assert (byte1 >> 2 & 3).tolist() == vec["codes"]
     assert (byte1 & 0xF3).tolist() == [0] * G   # channels 1, 9, 13 are zero groups
 
@@ -95,7 +95,7 @@ def _quantize_as_values(x_bits):
     vp = value_pairs(c.v_sz[0])                    # [tokens, 4, 2]
     s = vp[:, :, 0].reshape(-1)
     z = vp[:, :, 1].reshape(-1)
-    codes = unpack_codes(c.v_codes[0]).reshape(-1, G)
+    codes = unpack_value_codes(c.v_codes[0]).reshape(-1, G)
     return s, z, codes
 
 
@@ -195,13 +195,13 @@ def test_keys_per_channel_values_per_token_axes():
         for j in (0, 17, 127):
             s, z, codes = ref.quant_group(k[0, g * G:(g + 1) * G, j])
             assert c.k_sz[0, g, j].tolist() == [s, z]
-            assert np.array_equal(unpack_codes(c.k_codes[0])[g * G:(g + 1) * G, j], codes)
+            assert np.array_equal(unpack_key_codes(c.k_codes[0])[g * G:(g + 1) * G, j], codes)
             assert np.uint16(z).view(np.float16) == kf[g * G:(g + 1) * G, j].min()
     for t in (0, 33, 63):
         for kk in range(D // G):
             s, z, codes = ref.quant_group(k[0, t, kk * G:(kk + 1) * G])
             assert value_pairs(c.v_sz[0])[t, kk].tolist() == [s, z]
-            assert np.array_equal(unpack_codes(c.v_codes[0])[t, kk * G:(kk + 1) * G], codes)
+            assert np.array_equal(unpack_value_codes(c.v_codes[0])[t, kk * G:(kk + 1) * G], codes)
 
 
 def test_per_channel_keys_isolate_outlier_channels():
