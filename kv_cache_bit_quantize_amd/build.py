@@ -17,6 +17,9 @@ FLAGS = [
     "-fhip-fp32-correctly-rounded-divide-sqrt",
     # no packed fp32 instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-instruction accumulators in ordinary VGPRs: the decode loop rescales them with
+    # vector instructions, and accumulation registers would be copied back and forth
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wall", "-Wno-unused-command-line-argument",
 ]
 

@@ -6,52 +6,53 @@
 //
 // Work split: grid (splits, B*Hq).  A 256-thread workgroup owns one query row and a
 // contiguous range of key groups; each of its 4 waves walks a quarter of that range
-// with its own online softmax (log2 domain).  The waves merge in LDS, the workgroup
-// writes one partial (o[128], m, l), and the last workgroup of the row to arrive
-// (device-scope arrival counter) merges the row's partials with the log-sum-exp merge
-// and writes the output, so one launch does the whole call.  The split holding the last
-// groups also reads the fp16 residual.
+// with its own online softmax (log2 domain).  The split holding the last groups also
+// reads the fp16 residual, as separate softmax states.  The workgroup merges its states
+// in LDS and writes one partial (o[128], m, l); the last workgroup of the row to arrive
+// merges the row's partials with the log-sum-exp merge and writes the output, so one
+// launch does the whole call.
 //
-// Inner loop (one wave-iteration = two 32-token key groups, one per half-wave).
-// Lane = 32*gh + 4*tq + qq owns tokens 4tq..4tq+3 of group gh and channels
-// [32qq, 32qq+32).  Codes are 2 bits, so the loop is bound by HBM and by the vector
-// instructions that turn codes into products; it is arranged to need few of them:
+// Inner loop: one wave-iteration = two 32-token groups (64 tokens).  The 2-bit codes make
+// the loop bound by HBM and by the instructions that turn codes into products, so both
+// contractions run on the matrix cores and the vector units only prepare operands:
 //
-//  * keys, per token group g: q.(z + c*s) = q.z + (q*s).c.  The 32 lanes of a half
-//    compute q*s for 4 channels each, convert it to a 30-bit fixed-point integer with a
-//    per-group exponent, split it into four signed bytes, byte-transpose so that one
-//    32-bit word holds one byte position of four consecutive channels, and store those
-//    words in LDS once.  A token's code word masked with 0x03030303 << 2i gives the codes
-//    of channels 4i..4i+3 as bytes (layout in kivi_device.h), so the dot products are
-//    exact v_dot4_i32_i8 operations against those words (the per-class factor 4^i of the
-//    unshifted masks is divided out of the fixed-point values beforehand).
-//  * values, per token: p*(z + c*s) = p*z + (p*s)*c.  v_perm pairs two tokens' code
-//    bytes into one word, each code is placed at bits 8-9 or 6-7 of an fp16 whose
-//    exponent reads 1.0 (one shift + v_and_or_b32), giving the exact half 1 + c/4 or
-//    1 + c/16, and v_dot2_f32_f16 accumulates two tokens per instruction against fp16
-//    weights 4*p*s or 16*p*s (kept in range by a power-of-two factor).  The constant
-//    part, sum of the weights, is accumulated separately and subtracted at the end.
+//  * keys, per token group g: q.(z + c*s) = q.z + (q*s).c.  The 32 lanes of a half-wave
+//    compute q*s for 4 channels each, turn it into a 30-bit fixed-point integer with a
+//    per-group exponent and split it into four signed byte digits, stored in LDS as four
+//    128-byte digit planes.  v_mfma_i32_16x16x64_i8 then multiplies those digits (A,
+//    rows = digits) with the codes (B, one token per column; a code word masked with
+//    0x03030303 << 2i gives channels 4i..4i+3 as bytes, the factor 4^i divided out of
+//    the fixed-point values beforehand).  The products are exact integers.  Tile t (16
+//    tokens) puts its digits in rows 4t..4t+3 and zeros elsewhere, so one accumulator
+//    leaves lane L with the four digit sums of token L.
+//  * values, per token: p*(z + c*s) = p*z + (p*s)*c.  Each lane's token weight p*s is
+//    rounded to fp16 and stored in LDS in the A-operand order of v_mfma_f32_16x16x32_f16
+//    (row 0; the other rows read zeros).  The codes become B operands with one shift and
+//    one v_and_or_b32 per two tokens, placing a code at bits 8-9 or 6-7 of an fp16 whose
+//    exponent reads 1.0 (the exact halves 1 + c/4, 1 + c/16); the weights carry the
+//    matching factor 4 or 16 and a power of two keeping them in fp16 range.  The constant
+//    part, the sum of the weights, is accumulated on the side and subtracted at the end.
 #include "kivi_device.h"
 #include "kivi_internal.h"
 
 namespace kivi {
 
 constexpr int kWaves = kBlock / 64;
-constexpr int kPart = kD + 2;   // floats per partial: o[128], m, l
-// LDS table of one (parity, wave): two groups' digit planes, then a zero plane
-constexpr int kGroupTbl = 4 * kD;             // 4 digit planes of 128 channel bytes
-constexpr int kZeroPlane = 2 * kGroupTbl;
-constexpr int kTblBytes = kZeroPlane + kD;
+constexpr int kSlots = 2 * kWaves;   // softmax states per workgroup: quantized, residual
+constexpr int kPart = kD + 2;        // floats per partial: o[128], m, l
+// LDS area of one (parity, wave)
+constexpr int kGroupTbl = 4 * kD;                 // key digit planes of one group: 4 x 128 B
+constexpr int kWtOff = 2 * kGroupTbl;             // value weights [group][chgroup][kg][8] fp16
+constexpr int kZeroOff = kWtOff + 2 * 4 * 4 * 16;  // 512 zero bytes
+constexpr int kAreaBytes = kZeroOff + 512;
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
 // value of lane 4*(lane/4) + i, for CTRL = quad_perm [i, i, i, i]
 template <int CTRL>
 __device__ __forceinline__ float quad_bcast(float v) { return dpp_f<CTRL>(v); }
-
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ half2_t as_h2(uint32_t x) { return __builtin_bit_cast(half2_t, x); }
 
 // (x & m) | o in one instruction (v_and_or_b32 takes its constants in VGPRs)
 __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t o) {
@@ -60,8 +61,11 @@ __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t o) {
     return r;
 }
 
-__device__ __forceinline__ float fdot2(uint32_t a, half2_t b, float c) {
-    return __builtin_amdgcn_fdot2(as_h2(a), b, c, false);
+// sum over all 64 lanes (every lane gets it)
+__device__ __forceinline__ float wave_sum(float v) {
+    v = half_sum(v);
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0)) +
+           __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
 }
 
 __device__ __forceinline__ void load_q32(const uint16_t* q, float scale, float (&qv)[32]) {
@@ -145,11 +149,9 @@ __device__ __forceinline__ void merge_row(const AttnArgs& a, int64_t qrow) {
 }
 
 __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
-    // Per (parity, wave): the fixed-point digits of q*s for the wave's two groups, as
-    // [group][digit plane d][128 channels] bytes, then one all-zero plane.
-    __shared__ __align__(16) uint8_t sh_tbl[2][kWaves][kTblBytes];
-    __shared__ float sh_o[kWaves][kD];
-    __shared__ float sh_m[kWaves], sh_l[kWaves];
+    __shared__ __align__(16) uint8_t sh_area[2][kWaves][kAreaBytes];
+    __shared__ float sh_o[kSlots][kD];
+    __shared__ float sh_m[kSlots], sh_l[kSlots];
 
     const int split = blockIdx.x;
     const int64_t qrow = blockIdx.y;
@@ -158,7 +160,7 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
     const int64_t kvrow = b * a.kv_heads + hq / a.ratio;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int gh = lane >> 5;          // group of the wave-iteration this lane serves
-    const int tq = (lane >> 2) & 7, qq = lane & 3;   // value role: tokens 4tq.., channel group qq
+    const int tt = lane & 31;          // token role: token tt of group gh
     const int wl = lane & 31;          // fixed-point writer role: channels 4wl .. 4wl+3
     const int wk = wl & 3;             // their position i inside the 16-channel block
     const int mrow = lane & 15, kgrp = lane >> 4;     // matrix-operand role
@@ -175,20 +177,28 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
     // codes of channels 4i..4i+3 arrive multiplied by 1, 4, 16, 16 (i = 0..3)
     const float cls_div = wk == 0 ? 1.0f : (wk == 1 ? 0.25f : 0.0625f);
 
-    // A operand of tile t (rows 4t..4t+3 = digits 0..3 of its group, all other rows zero):
-    // this lane's 16 bytes come from its own digit plane or from the zero plane.
-    int a_off[4];
+    // Key A operand of tile t: rows 4t..4t+3 hold digits 0..3 of the tile's group, all
+    // other rows are zero; this lane's 16 bytes come from its digit plane or the zeros.
+    int ka_off[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
-        a_off[t] = ((mrow >> 2) == t) ? (t >> 1) * kGroupTbl + (mrow & 3) * kD + 16 * kgrp : kZeroPlane + 16 * kgrp;
-    // the zero planes of both parities, written once
-    reinterpret_cast<uint32_t*>(&sh_tbl[lane >> 5][wave][kZeroPlane])[lane & 31] = 0u;
+        ka_off[t] = ((mrow >> 2) == t) ? (t >> 1) * kGroupTbl + (mrow & 3) * kD + 16 * kgrp : kZeroOff + 16 * kgrp;
+    // Value A operand of (group, channel group): row 0 holds the weights, other rows zero.
+    const int va_off = (mrow == 0 ? kWtOff : kZeroOff) + 16 * kgrp;
+    // this lane's slot in the weight table: tokens 8kg..8kg+7 of a group are ordered
+    // 0,4,1,5,2,6,3,7 (the order the code operand produces them in)
+    const int w_off = kWtOff + gh * 4 * 64 + (tt >> 3) * 16 + (((tt & 3) << 1) | ((tt >> 2) & 1)) * 2;
+    // even tokens meet codes read as 1 + c/16, odd ones 1 + c/4
+    const float cls_w = (tt & 1) ? 4.0f : 16.0f;
+    // the zero areas of both parities, written once
+    reinterpret_cast<uint4*>(&sh_area[lane >> 5][wave][kZeroOff])[lane & 31] = make_uint4(0, 0, 0, 0);
 
-    float acc[32];
+    v4f cv[8];                         // P.V accumulators, one per 16-channel block (row 0)
 #pragma unroll
-    for (int c = 0; c < 32; ++c) acc[c] = 0.0f;
-    float b6 = 0.0f, b8 = 0.0f;        // sums of the fp16 weights of the two value classes
-    float zacc = 0.0f, lsum = 0.0f, m = -INFINITY;
+    for (int v = 0; v < 8; ++v) cv[v] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+    float bk[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // this lane's share of the fp16 weight sums
+    float zk[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // ... and of sum p*zero, per channel group
+    float lsum = 0.0f, m = -INFINITY;
     float vs = 0.0f;                   // power-of-two factor keeping the value weights in fp16 range
 
     const int n_groups = a.n_quant / kG;
@@ -207,14 +217,14 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
     const uint32_t* vp_row = reinterpret_cast<const uint32_t*>(a.v_sz) + tok_base * (kD / kG);
 
     const uint32_t kM6 = 0x00C000C0u, kM8 = 0x03000300u, kOne = 0x3C003C00u;
-    const half2_t ones = as_h2(kOne);
 
-    // one wave-iteration's global loads (issued one iteration ahead of their use)
+    // one wave-iteration's global loads (issued one iteration ahead of their use); every
+    // load instruction reads a contiguous span
     struct Loads {
         uint4 kp;          // (scale, zero) of key channels 4wl..4wl+3 of group gh
         uint4 kc[2];       // key tile chunk `lane` of both groups (matrix operand B)
-        uint2 vw[4];       // value codes of tokens 4tq..4tq+3, channel quarter qq, group gh
-        uint32_t vp[4];    // (scale, zero) of the value channel group qq of those tokens
+        uint4 vc[2];       // value tile chunk `lane` of both groups (matrix operand B)
+        uint4 vp;          // (scale, zero) of the 4 channel groups of token tt of group gh
     };
     auto load_iter = [&](int it) {
         Loads L;
@@ -224,18 +234,9 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
         L.kp = *reinterpret_cast<const uint4*>(kp_row + (int64_t)gc * kD + 4 * wl);
         L.kc[0] = reinterpret_cast<const uint4*>(kc_row + (int64_t)g0 * kTileBytes)[lane];
         L.kc[1] = reinterpret_cast<const uint4*>(kc_row + (int64_t)g1 * kTileBytes)[lane];
-        // value tile chunks wl and 32 + wl of group gc hold quarter qq of tokens 4tq..4tq+3
-        const uint4* vt = reinterpret_cast<const uint4*>(vc_row + (int64_t)gc * kTileBytes);
-        const uint4 v0 = vt[wl], v1 = vt[32 + wl];
-        L.vw[0] = make_uint2(v0.x, v0.y);
-        L.vw[1] = make_uint2(v0.z, v0.w);
-        L.vw[2] = make_uint2(v1.x, v1.y);
-        L.vw[3] = make_uint2(v1.z, v1.w);
-        const uint4 p = *reinterpret_cast<const uint4*>(vp_row + value_pair_index((int64_t)gc * kG + 4 * tq, qq));
-        L.vp[0] = p.x;
-        L.vp[1] = p.y;
-        L.vp[2] = p.z;
-        L.vp[3] = p.w;
+        L.vc[0] = reinterpret_cast<const uint4*>(vc_row + (int64_t)g0 * kTileBytes)[lane];
+        L.vc[1] = reinterpret_cast<const uint4*>(vc_row + (int64_t)g1 * kTileBytes)[lane];
+        L.vp = *reinterpret_cast<const uint4*>(vp_row + value_pair_index((int64_t)gc * kG + tt, 0));
         return L;
     };
 
@@ -244,7 +245,7 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
     for (int it = 0; it < iters; ++it) {
         const Loads nxt = load_iter(it + 1 < iters ? it + 1 : it);
         const bool gvalid = gb + 2 * it + gh < ge;
-        uint8_t* tbl = &sh_tbl[it & 1][wave][0];
+        uint8_t* area = &sh_area[it & 1][wave][0];
 
         // ---- q*s of this half's group as 30-bit fixed point, four signed byte digits,
         // stored as digit planes
@@ -270,7 +271,7 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
             const uint32_t B = __builtin_amdgcn_perm(dg[1], dg[0], 0x07030602u);
             const uint32_t C = __builtin_amdgcn_perm(dg[3], dg[2], 0x05010400u);
             const uint32_t E = __builtin_amdgcn_perm(dg[3], dg[2], 0x07030602u);
-            uint32_t* plane = reinterpret_cast<uint32_t*>(tbl + gh * kGroupTbl) + wl;
+            uint32_t* plane = reinterpret_cast<uint32_t*>(area + gh * kGroupTbl) + wl;
             plane[0 * kD / 4] = __builtin_amdgcn_perm(C, A, 0x05040100u);   // digit 0 of the 4 channels
             plane[1 * kD / 4] = __builtin_amdgcn_perm(C, A, 0x07060302u);   // digit 1
             plane[2 * kD / 4] = __builtin_amdgcn_perm(E, B, 0x05040100u);   // digit 2
@@ -281,8 +282,7 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
         // ---- key logits on the matrix cores: tile t = 2*group + token half, K = 64
-        // channels per instruction.  Row 4t + d of the accumulator collects digit d's dot
-        // product for tile t's 16 tokens, so lane L ends with the four digit sums of token L.
+        // channels per instruction
         v4i cacc = {0, 0, 0, 0};
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -292,7 +292,7 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
                 const uint32_t x = (t & 1) ? (kh ? kc.w : kc.z) : (kh ? kc.y : kc.x);
                 const v4i bop = {(int)(x & 0x03030303u), (int)(x & 0x0C0C0C0Cu), (int)(x & 0x30303030u),
                                  (int)((x >> 2) & 0x30303030u)};
-                const v4i aop = *reinterpret_cast<const v4i*>(tbl + a_off[t] + 64 * kh);
+                const v4i aop = *reinterpret_cast<const v4i*>(area + ka_off[t] + 64 * kh);
                 cacc = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop, bop, cacc, 0, 0, 0);
             }
         }
@@ -310,89 +310,98 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
         if (mloc > m) {
             const float al = exp2f(m - mloc);
 #pragma unroll
-            for (int c = 0; c < 32; ++c) acc[c] *= al;
-            b6 *= al;
-            b8 *= al;
-            zacc *= al;
+            for (int v = 0; v < 8; ++v) cv[v] *= al;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                bk[k] *= al;
+                zk[k] *= al;
+            }
             lsum *= al;
             m = mloc;
         }
-        const float pt = exp2f(lg - m);      // this lane's token
-        lsum += pt;
-        // value role: the weights of tokens 4tq..4tq+3 sit in this lane's quad
-        const float p[4] = {quad_bcast<0x00>(pt), quad_bcast<0x55>(pt), quad_bcast<0xAA>(pt), quad_bcast<0xFF>(pt)};
-        float w[4], smax = 0.0f;
+        const float p = exp2f(lg - m);       // this lane's token
+        lsum += p;
+        const uint32_t vpr[4] = {cur.vp.x, cur.vp.y, cur.vp.z, cur.vp.w};
+        float sv[4], smax = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float s = h2f(cur.vp[i] & 0xffffu);
-            w[i] = p[i] * s;
-            zacc = fmaf(p[i], h2f(cur.vp[i] >> 16), zacc);
-            smax = fmaxf(smax, s);
+        for (int k = 0; k < 4; ++k) {
+            sv[k] = h2f(vpr[k] & 0xffffu);
+            zk[k] = fmaf(p, h2f(vpr[k] >> 16), zk[k]);
+            smax = fmaxf(smax, sv[k]);
         }
-        const uint2* vw = cur.vw;
-        // value weights 16*w*vs must stay below 2^15: shrink vs (a power of two) if needed
+        // value weights 16*p*s*vs must stay below 2^15: shrink vs (a power of two) if needed
         if (__builtin_amdgcn_ballot_w64(smax * vs > 2048.0f || vs == 0.0f)) {
             const float gm = wave_max_xor(smax, 1, 32);
             const float nvs = __builtin_ldexpf(1.0f, 11 - __builtin_amdgcn_frexp_expf(gm));
             if (vs != 0.0f && nvs < vs) {
                 const float r = nvs / vs;
 #pragma unroll
-                for (int c = 0; c < 32; ++c) acc[c] *= r;
-                b6 *= r;
-                b8 *= r;
+                for (int v = 0; v < 8; ++v) cv[v] *= r;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) bk[k] *= r;
             }
             if (vs == 0.0f || nvs < vs) vs = nvs;
         }
+        {
+            const float f = p * (cls_w * vs);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const _Float16 h = (_Float16)(f * sv[k]);
+                bk[k] += (float)h;
+                *reinterpret_cast<_Float16*>(area + w_off + k * 64) = h;
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-        // ---- P.V over the codes: two tokens per v_dot2 against fp16 weights
+        // ---- P.V on the matrix cores: K = the 32 tokens of a group, N = 16 channels
 #pragma unroll
-        for (int pp = 0; pp < 2; ++pp) {
-            half2_t u6, u8;
-            u6.x = (_Float16)(w[2 * pp] * (16.0f * vs));
-            u6.y = (_Float16)(w[2 * pp + 1] * (16.0f * vs));
-            u8.x = (_Float16)(w[2 * pp] * (4.0f * vs));
-            u8.y = (_Float16)(w[2 * pp + 1] * (4.0f * vs));
-            b6 = __builtin_amdgcn_fdot2(u6, ones, b6, false);
-            b8 = __builtin_amdgcn_fdot2(u8, ones, b8, false);
+        for (int g = 0; g < 2; ++g) {
+            const uint4 vc = cur.vc[g];
+            const uint32_t words[4] = {vc.x, vc.y, vc.z, vc.w};
 #pragma unroll
-            for (int wd = 0; wd < 2; ++wd) {
-                const uint32_t x0 = wd ? vw[2 * pp].y : vw[2 * pp].x;
-                const uint32_t x1 = wd ? vw[2 * pp + 1].y : vw[2 * pp + 1].x;
-#pragma unroll
-                for (int hb = 0; hb < 2; ++hb) {
-                    // bytes hb*2, hb*2+1 of token 2pp (low half) and token 2pp+1 (high half):
-                    // channels o+{0,4,8,12} at bits 0,2,4,6 and o+{1,5,9,13} at 8,10,12,14
-                    const uint32_t X = __builtin_amdgcn_perm(x1, x0, hb ? 0x07060302u : 0x05040100u);
-                    const uint32_t l4 = X << 4, r4 = X >> 4, l8 = X << 8, r8 = X >> 8;
-                    const int o = 16 * wd + 2 * hb;
-                    acc[o + 0] = fdot2(and_or(l8, kM8, kOne), u8, acc[o + 0]);
-                    acc[o + 1] = fdot2(and_or(X, kM8, kOne), u8, acc[o + 1]);
-                    acc[o + 4] = fdot2(and_or(l4, kM6, kOne), u6, acc[o + 4]);
-                    acc[o + 5] = fdot2(and_or(r4, kM6, kOne), u6, acc[o + 5]);
-                    acc[o + 8] = fdot2(and_or(l4, kM8, kOne), u8, acc[o + 8]);
-                    acc[o + 9] = fdot2(and_or(r4, kM8, kOne), u8, acc[o + 9]);
-                    acc[o + 12] = fdot2(and_or(X, kM6, kOne), u6, acc[o + 12]);
-                    acc[o + 13] = fdot2(and_or(r8, kM6, kOne), u6, acc[o + 13]);
-                }
+            for (int v = 0; v < 8; ++v) {
+                // word v/2 holds blocks v (even) and v+1 in alternate bytes
+                const uint32_t x = words[v >> 1];
+                const uint32_t s1 = (v & 1) ? x >> 2 : x << 6, s2 = (v & 1) ? x >> 6 : x << 2;
+                const uint32_t bw[4] = {and_or(s1, kM6, kOne), and_or(s1, kM8, kOne), and_or(s2, kM6, kOne),
+                                        and_or(s2, kM8, kOne)};
+                const v8h bop = __builtin_bit_cast(v8h, make_uint4(bw[0], bw[1], bw[2], bw[3]));
+                const v8h aop = *reinterpret_cast<const v8h*>(area + va_off + (g * 4 + (v >> 1)) * 64);
+                cv[v] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop, cv[v], 0, 0, 0);
             }
         }
         cur = nxt;
     }
 
-    // true partial output of the lane's quarter: sum(w*c) = (acc - bias) / vs, plus p*z
-    float o[32];
-    {
+    // ---- the wave's quantized-part state: o = (P.V - weight sums) / vs + sum p*zero
+    lsum = wave_sum(lsum);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        bk[k] = wave_sum(bk[k]);
+        zk[k] = wave_sum(zk[k]);
+    }
+    if (lane < 16) {   // row 0 of the accumulators: channel 16v + lane
         const float inv = vs != 0.0f ? 1.0f / vs : 0.0f;
 #pragma unroll
-        for (int c = 0; c < 32; ++c) o[c] = fmaf(acc[c] - ((c & 4) ? b6 : b8), inv, zacc);
+        for (int v = 0; v < 8; ++v) sh_o[wave][16 * v + lane] = fmaf(cv[v][0] - bk[v >> 1], inv, zk[v >> 1]);
+    }
+    if (lane == 0) {
+        sh_m[wave] = m;
+        sh_l[wave] = lsum;
     }
 
-    // fp16 residual, logical tokens [32*wave, 32*wave+32) of the ring, last split only.
-    // Lane = 4*tp + qq: tokens 2tp, 2tp+1 of the chunk, channels [32qq, 32qq+32).
+    // ---- fp16 residual, logical tokens [32*wave, 32*wave+32) of the ring, last split only,
+    // as a separate state.  Lane = 4*tp + qq: tokens 2tp, 2tp+1 of the chunk, channels
+    // [32qq, 32qq+32).
+    float mr = -INFINITY, lr = 0.0f;
     if (split == a.splits - 1 && wave * kG < a.n_res) {
-        const int tp = lane >> 2;
-        float qv[32];
+        const int tp = lane >> 2, qq = lane & 3;
+        float qv[32], o[32];
         load_q32(a.q + qrow * kD + qq * 32, a.sm_log2, qv);
+#pragma unroll
+        for (int c = 0; c < 32; ++c) o[c] = 0.0f;
         for (int base = wave * kG; base < a.n_res; base += kWaves * kG) {
             const int i0 = base + 2 * tp, i1 = i0 + 1;
             const bool ok0 = i0 < a.n_res, ok1 = i1 < a.n_res;
@@ -419,13 +428,11 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
             d0 = wave_sum_xor(d0, 1, 2);
             d1 = wave_sum_xor(d1, 1, 2);
             const float l0 = ok0 ? d0 : -INFINITY, l1 = ok1 ? d1 : -INFINITY;
-            const float m_new = fmaxf(m, wave_max_xor(fmaxf(l0, l1), 4, 32));
-            const float alpha = (m == -INFINITY) ? 0.0f : exp2f(m - m_new);
+            const float m_new = fmaxf(mr, wave_max_xor(fmaxf(l0, l1), 4, 32));
+            const float alpha = (mr == -INFINITY) ? 0.0f : exp2f(mr - m_new);
             const float p0 = ok0 ? exp2f(l0 - m_new) : 0.0f;
             const float p1 = ok1 ? exp2f(l1 - m_new) : 0.0f;
-            // lsum holds one share per token: the quantized tokens' in the lane that owned
-            // them, a residual pair's in the qq = 0 lane of its quad
-            lsum = lsum * alpha + (qq == 0 ? p0 + p1 : 0.0f);
+            lr = lr * alpha + (qq == 0 ? p0 + p1 : 0.0f);   // one share per token pair
             const uint4* v0 = reinterpret_cast<const uint4*>(a.v_res + r0);
             const uint4* v1 = reinterpret_cast<const uint4*>(a.v_res + r1);
 #pragma unroll
@@ -439,33 +446,34 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
                     o[c + 1] = fmaf(p1, h2f(w1[k] >> 16), fmaf(p0, h2f(w0[k] >> 16), o[c + 1] * alpha));
                 }
             }
-            m = m_new;
+            mr = m_new;
+        }
+        lr = wave_sum(lr);
+#pragma unroll
+        for (int c = 0; c < 32; ++c) o[c] = wave_sum_xor(o[c], 4, 32);
+        if (tp == 0) {
+#pragma unroll
+            for (int c = 0; c < 32; ++c) sh_o[kWaves + wave][qq * 32 + c] = o[c];
         }
     }
-
-    // wave result: sum over the 16 lanes that share a channel quarter
-    lsum = wave_sum_xor(lsum, 1, 32);
-#pragma unroll
-    for (int c = 0; c < 32; ++c) o[c] = wave_sum_xor(o[c], 4, 32);
-    if ((lane >> 2) == 0) {
-#pragma unroll
-        for (int c = 0; c < 32; ++c) sh_o[wave][qq * 32 + c] = o[c];
-    }
     if (lane == 0) {
-        sh_m[wave] = m;
-        sh_l[wave] = lsum;
+        sh_m[kWaves + wave] = mr;
+        sh_l[kWaves + wave] = lr;
     }
     __syncthreads();
+
+    // ---- the workgroup's partial: log-sum-exp merge of its states (empty states skipped)
     float* part = a.ws + ((int64_t)split * a.q_rows + qrow) * kPart;
     if (threadIdx.x < kD) {
         const int j = threadIdx.x;
-        float M = sh_m[0];
+        float M = -INFINITY;
 #pragma unroll
-        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sh_m[w]);
+        for (int w = 0; w < kSlots; ++w) M = fmaxf(M, sh_m[w]);
         float L = 0.0f, O = 0.0f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            const float sc = (sh_m[w] == -INFINITY) ? 0.0f : exp2f(sh_m[w] - M);
+        for (int w = 0; w < kSlots; ++w) {
+            if (sh_m[w] == -INFINITY) continue;
+            const float sc = exp2f(sh_m[w] - M);
             L = fmaf(sh_l[w], sc, L);
             O = fmaf(sh_o[w][j], sc, O);
         }

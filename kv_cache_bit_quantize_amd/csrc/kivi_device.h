@@ -14,33 +14,29 @@ constexpr int kG = 32;              // group size (tokens for keys, channels for
 constexpr int kRowBytes = kD / 4;   // packed code bytes per token
 constexpr int kBlock = 256;         // threads per workgroup (4 wave64)
 
-// Packed code layout (include/kivi.h).  16 channels 16w..16w+15 of a token form one 32-bit
-// word; channel offset c = 4i + b (0..15) sits in byte b at bits 2i..2i+1, i.e. at bit
-// 8b + 2i, so masking a word with 0x03030303 << 2i leaves the codes of channels 4i..4i+3,
-// one per byte.  A row holds one 1024-byte tile per 32-token group.
-//  * Value tiles: 16-byte chunk ((u*8 + q)*4 + h) holds words 2h, 2h+1 of token 4q+2u, then
-//    of token 4q+2u+1.  A half-wave whose lane L = 4q + h loads chunks L and 32 + L reads
-//    two contiguous 512-byte spans and gets quarter h of tokens 4q..4q+3.
-//  * Key tiles: 16-byte chunk (16k + n) holds words k, 4+k of token n, then of token 16+n.
-//    Lane 16k + n of a wave loading chunk (lane) reads the whole tile in one contiguous
-//    access and gets exactly the codes the integer matrix instruction wants from it as the
-//    K x N operand (channels 16k..16k+15 and 64+16k.. of tokens n and 16+n).
+// Packed code layout (include/kivi.h).  A row holds one 1024-byte tile per 32-token group.
+//  * Key tiles: the 16 channels 16w..16w+15 of a token form one 32-bit word, channel offset
+//    c = 4i + b (0..15) in byte b at bits 2i..2i+1, i.e. at bit 8b + 2i, so masking a word
+//    with 0x03030303 << 2i leaves the codes of channels 4i..4i+3, one per byte.  16-byte
+//    chunk (16k + n) holds words k, 4+k of token n, then of token 16+n: lane 16k + n of a
+//    wave loading chunk (lane) reads the whole tile in one contiguous access and gets
+//    exactly its part of the integer matrix instruction's K x N operand (channels
+//    16k..16k+15 and 64+16k.. of tokens n and 16+n).
+//  * Value tiles: a byte holds one channel's codes for four consecutive tokens (token 4a+i
+//    at bits 2i..2i+1).  16-byte chunk (16k + n) covers tokens 8k..8k+7 and the channels
+//    n + 16v; its 32-bit word p holds, byte by byte, channel n+32p for tokens 8k..8k+3,
+//    channel n+32p+16 for the same tokens, then both channels for tokens 8k+4..8k+7.  Lane
+//    16k + n loading chunk (lane) gets its part of the fp16 matrix instruction's K x N
+//    operand (tokens 8k..8k+7 of channels n + 16v) for all eight 16-channel blocks v.
 __host__ __device__ constexpr int code_bit(int c) { return 8 * (c & 3) + 2 * (c >> 2); }
 constexpr int kTileBytes = kG * kD / 4;     // 1024
 
-// byte offset, inside a row, of word w (0..7) of value token t
-__host__ __device__ constexpr int64_t value_word_offset(int64_t t, int w) {
-    return (t >> 5) * kTileBytes +
-           ((((t & 3) >> 1) * 8 + ((t & 31) >> 2)) * 4 + (w >> 1)) * 16 + (t & 1) * 8 + (w & 1) * 4;
-}
 // byte offset, inside a row, of word w (0..7) of key token t
 __host__ __device__ constexpr int64_t key_word_offset(int64_t t, int w) {
     return (t >> 5) * kTileBytes + ((w & 3) * 16 + (t & 15)) * 16 + ((t >> 4) & 1) * 8 + (w >> 2) * 4;
 }
 // index (in 32-bit pairs), inside a row, of the value (scale, zero) of token t, group k
-__host__ __device__ constexpr int64_t value_pair_index(int64_t t, int k) {
-    return (t >> 5) * (kG * (kD / kG)) + k * kG + (t & 31);
-}
+__host__ __device__ constexpr int64_t value_pair_index(int64_t t, int k) { return t * (kD / kG) + k; }
 
 __device__ __forceinline__ float h2f(uint32_t h) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)h);

@@ -48,32 +48,71 @@ __device__ void quant_k_tile(const uint16_t* __restrict__ tile, float* sh_mn, fl
     *reinterpret_cast<uint32_t*>(codes_dst + key_word_offset(t, w)) = word;
 }
 
-// Eight consecutive channels of one value token (this thread's share of a 32-channel
-// group held by 4 adjacent lanes; lane pairs 2w, 2w+1 hold one 16-channel code word).
-// Returns the complete 32-bit code word of the pair (valid in both lanes); *pair gets the
-// group's (scale, zero) word (valid in every lane of the 4).  All lanes must call it.
-__device__ __forceinline__ uint32_t quant_v_8(uint4 x, int odd, uint32_t* pair) {
-    uint32_t h[4] = {x.x, x.y, x.z, x.w};
-    float v[8];
+// One 32-token value tile by the whole workgroup.  Tokens lo..hi-1 (tile-local) are
+// quantized from src_lo (token t at src_lo + (t - lo)*src_tok_stride, 128 fp16 channels);
+// their codes and (scale, zero) words are stored and the codes of the tile's other tokens
+// are kept.
+// sh_codes: LDS scratch [32][128] bytes.  All 256 threads must call it.
+__device__ void quant_v_tile(const uint16_t* __restrict__ src_lo, int64_t src_tok_stride, int lo, int hi,
+                             uint8_t (*sh_codes)[kD], uint8_t* __restrict__ tile_dst,
+                             uint32_t* __restrict__ pairs_dst) {   // pair word of tile token 0, group 0
+    const int tid = threadIdx.x;
+    // thread -> (token t, 16-channel block cb); the two blocks of a 32-channel group are
+    // adjacent lanes
+    const int t = tid >> 3, cb = tid & 7;
+    const bool live = t >= lo && t < hi;
+    uint4 x0 = make_uint4(0, 0, 0, 0), x1 = x0;
+    if (live) {
+        const uint4* p = reinterpret_cast<const uint4*>(src_lo + (t - lo) * src_tok_stride + cb * 16);
+        x0 = p[0];
+        x1 = p[1];
+    }
+    const uint32_t h[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    float v[16];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 8; ++i) {
         v[2 * i] = h2f(h[i] & 0xffffu);
         v[2 * i + 1] = h2f(h[i] >> 16);
     }
     float mn = v[0], mx = v[0];
 #pragma unroll
-    for (int i = 1; i < 8; ++i) {
+    for (int i = 1; i < 16; ++i) {
         mn = __builtin_fminf(mn, v[i]);
         mx = __builtin_fmaxf(mx, v[i]);
     }
-    mn = wave_min_xor(mn, 1, 2);
-    mx = wave_max_xor(mx, 1, 2);
-    GroupQ q = group_params(mn, mx);
-    uint32_t bits = 0;
+    mn = __builtin_fminf(mn, __shfl_xor(mn, 1, 64));
+    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 1, 64));
+    const GroupQ q = group_params(mn, mx);
+    uint32_t packed[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) bits |= code_of(v[i], q) << code_bit(8 * odd + i);
-    *pair = q.pair;
-    return bits | (uint32_t)__shfl_xor((int)bits, 1, 64);
+    for (int w = 0; w < 4; ++w) {
+        packed[w] = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) packed[w] |= code_of(v[4 * w + b], q) << (8 * b);
+    }
+    *reinterpret_cast<uint4*>(&sh_codes[t][cb * 16]) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    if (live && (cb & 1) == 0) pairs_dst[value_pair_index(t, cb >> 1)] = q.pair;
+    __syncthreads();
+    // thread -> 32-bit word tid of the tile: chunk L = tid/4 (tokens 8kg.., channel n + 16v),
+    // word p = tid%4; its byte 2hh + e holds channel n + 32p + 16e for tokens 8kg + 4hh + i
+    const int L = tid >> 2, p = tid & 3, kg = L >> 4, n = L & 15;
+    uint32_t word = 0, mask = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const int ch = n + 32 * p + 16 * (b & 1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int tt = 8 * kg + 4 * (b >> 1) + i;
+            if (tt >= lo && tt < hi) {
+                word |= (uint32_t)sh_codes[tt][ch] << (8 * b + 2 * i);
+                mask |= 3u << (8 * b + 2 * i);
+            }
+        }
+    }
+    uint32_t* dst = reinterpret_cast<uint32_t*>(tile_dst) + tid;
+    if (mask == 0xffffffffu) *dst = word;
+    else if (mask != 0u) *dst = (*dst & ~mask) | word;
+    __syncthreads();   // sh_codes may be reused by the caller
 }
 
 // ------------------------------------------------------------------ kernels ------
@@ -96,25 +135,20 @@ __global__ __launch_bounds__(kBlock) void quantize_k_kernel(QuantArgs a) {
     quant_k_tile(reinterpret_cast<const uint16_t*>(tile4), sh_mn, sh_s, codes, pairs);
 }
 
-// grid.x = ceil(rows * tokens / 16); 16 value tokens per workgroup, 16 lanes per token.
+// grid.x = rows * (32-token tiles touched by [dst_token_off, dst_token_off + tokens)).
 __global__ __launch_bounds__(kBlock) void quantize_v_kernel(QuantArgs a) {
-    const int64_t total = a.rows * (int64_t)a.tokens;
-    const int64_t gt = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-    const int l16 = threadIdx.x & 15;
-    const bool live = gt < total;
-    const int64_t row = live ? gt / a.tokens : 0;
-    const int t = live ? (int)(gt % a.tokens) : 0;
-    uint4 x = make_uint4(0, 0, 0, 0);
-    if (live) x = reinterpret_cast<const uint4*>(a.src + row * a.src_row_stride + (int64_t)t * kD)[l16];
-    uint32_t pair;
-    const uint32_t word = quant_v_8(x, l16 & 1, &pair);
-    if (live) {
-        const int64_t tok = a.dst_token_off + t;          // token inside the row's history
-        if ((l16 & 1) == 0)
-            *reinterpret_cast<uint32_t*>(a.v_codes + row * a.token_cap * kRowBytes + value_word_offset(tok, l16 >> 1)) = word;
-        if ((l16 & 3) == 0)
-            reinterpret_cast<uint32_t*>(a.v_sz)[row * a.token_cap * (kD / kG) + value_pair_index(tok, l16 >> 2)] = pair;
-    }
+    __shared__ __align__(16) uint8_t sh_codes[kG][kD];
+    const int first = a.dst_token_off / kG;
+    const int n_tiles = (a.dst_token_off + a.tokens - 1) / kG - first + 1;
+    const int64_t row = blockIdx.x / n_tiles;
+    const int tile = first + (int)(blockIdx.x % n_tiles);
+    const int t0 = tile * kG;                                   // first token of the tile
+    const int lo = max(a.dst_token_off, t0) - t0;
+    const int hi = min(a.dst_token_off + a.tokens, t0 + kG) - t0;
+    // source token of tile token lo: t0 + lo - dst_token_off
+    const uint16_t* src = a.src + row * a.src_row_stride + (int64_t)(t0 + lo - a.dst_token_off) * kD;
+    quant_v_tile(src, kD, lo, hi, sh_codes, a.v_codes + (row * a.token_cap + t0) * kRowBytes,
+                 reinterpret_cast<uint32_t*>(a.v_sz) + value_pair_index(row * a.token_cap + t0, 0));
 }
 
 // grid.x = ceil(rows * n * 16 / 256): copy tokens [first, first+n) of each row into ring
@@ -148,19 +182,11 @@ __global__ __launch_bounds__(kBlock) void append_flush_kernel(AppendArgs a) {
         uint8_t* kc = a.k_codes + row * a.token_cap * kRowBytes + (int64_t)a.flush_group * kTileBytes;
         uint32_t* kp = reinterpret_cast<uint32_t*>(a.k_sz) + (row * (a.token_cap / kG) + a.flush_group) * kD;
         quant_k_tile(reinterpret_cast<const uint16_t*>(tile4), sh_mn, sh_s, kc, kp);
-        // values: 32 tokens x 16 lanes = two passes of 16 tokens
-        const uint4* vr = reinterpret_cast<const uint4*>(a.v_res + (row * a.residual_cap + a.flush_slot) * kD);
-#pragma unroll
-        for (int pass = 0; pass < 2; ++pass) {
-            const int t = pass * 16 + (tid >> 4), l16 = tid & 15;
-            uint32_t pair;
-            const uint32_t word = quant_v_8(vr[t * 16 + l16], l16 & 1, &pair);
-            const int64_t tok = dst_tok + t;
-            if ((l16 & 1) == 0)
-                *reinterpret_cast<uint32_t*>(a.v_codes + row * a.token_cap * kRowBytes + value_word_offset(tok, l16 >> 1)) = word;
-            if ((l16 & 3) == 0)
-                reinterpret_cast<uint32_t*>(a.v_sz)[row * a.token_cap * (kD / kG) + value_pair_index(tok, l16 >> 2)] = pair;
-        }
+        // values: the same 32 ring tokens as one value tile
+        __shared__ __align__(16) uint8_t sh_codes[kG][kD];
+        quant_v_tile(a.v_res + (row * a.residual_cap + a.flush_slot) * kD, kD, 0, kG, sh_codes,
+                     a.v_codes + (row * a.token_cap + dst_tok) * kRowBytes,
+                     reinterpret_cast<uint32_t*>(a.v_sz) + value_pair_index(row * a.token_cap + dst_tok, 0));
         __syncthreads();   // every read of the flushed slots is done before the overwrite
     }
     if (tid < 32) {
@@ -181,7 +207,9 @@ hipError_t launch_quantize_k(const QuantArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_quantize_v(const QuantArgs& a, hipStream_t s) {
-    const int64_t blocks = (a.rows * (int64_t)a.tokens + 15) / 16;
+    if (a.tokens <= 0) return hipSuccess;
+    const int64_t n_tiles = (a.dst_token_off + a.tokens - 1) / kG - a.dst_token_off / kG + 1;
+    const int64_t blocks = a.rows * n_tiles;
     if (blocks == 0) return hipSuccess;
     hipLaunchKernelGGL(quantize_v_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, s, a);
     return hipGetLastError();

@@ -90,7 +90,7 @@ class Cache:
         self.k_codes = torch.zeros((rows, tiles, group * head_dim // 4), dtype=u8, device=device)
         self.v_codes = torch.zeros((rows, tiles, group * head_dim // 4), dtype=u8, device=device)
         self.k_sz = torch.zeros((rows, tiles, head_dim, 2), dtype=f16, device=device)
-        self.v_sz = torch.zeros((rows, tiles, head_dim // group, group, 2), dtype=f16, device=device)
+        self.v_sz = torch.zeros((rows, token_cap, head_dim // group, 2), dtype=f16, device=device)
         self.k_res = torch.zeros((rows, residual_cap, head_dim), dtype=f16, device=device)
         self.v_res = torch.zeros((rows, residual_cap, head_dim), dtype=f16, device=device)
         self.c = kivi_cache(batch, kv_heads, head_dim, group, residual_cap, token_cap, 0, 0, 0, 0,

@@ -126,39 +126,43 @@ void kivi_ref_quant_group(const uint16_t* x, ptrdiff_t stride, int32_t n,
 
 static int64_t row_count(const kivi_ref_cache* c) { return (int64_t)c->batch * c->kv_heads; }
 
-/* Code positions.  Codes are packed four to a byte: a little-endian 32-bit word holds the
- * 16 channels 16w..16w+15 of one token, channel 16w + 4i + b in byte b at bits 2i, 2i+1.
- * A row is a sequence of 1024-byte tiles, one per 32-token group; the key and value caches
- * order the words inside a tile differently.
+/* Code positions.  Codes are packed four to a byte, and a row is a sequence of 1024-byte
+ * tiles, one per 32-token group.
  *
- * Value tiles: 16-byte chunk ((u*8 + q)*4 + h) holds, for channel quarter h (channels
- * 32h..32h+31), the 8 bytes of token 4q + 2u followed by the 8 bytes of token 4q + 2u + 1
- * (q = 0..7, u = 0..1); a token's 8 bytes for a quarter are its words 2h and 2h + 1.
+ * Key tiles: a little-endian 32-bit word holds the 16 channels 16w..16w+15 of one token,
+ * channel 16w + 4i + b in byte b at bits 2i, 2i+1.  16-byte chunk (16k + n) (k = 0..3,
+ * n = 0..15) holds words k and 4 + k of token n, then words k and 4 + k of token 16 + n.
  *
- * Key tiles: 16-byte chunk (16k + n) (k = 0..3, n = 0..15) holds words k and 4 + k of
- * token n, then words k and 4 + k of token 16 + n. */
-static int64_t value_code_byte(int32_t t, int32_t j) {
-    int32_t tt = t % 32, q = tt / 4, u = (tt % 4) / 2, t1 = tt % 2;
-    int32_t h = j / 32, w = (j % 32) / 16, c = j % 16;
-    return (int64_t)(t / 32) * 1024 + ((u * 8 + q) * 4 + h) * 16 + t1 * 8 + w * 4 + (c % 4);
-}
+ * Value tiles: a byte holds one channel's codes for four consecutive tokens, token 4a + i
+ * at bits 2i, 2i+1.  16-byte chunk (16k + n) holds, for the 8 tokens 8k..8k+7, the codes
+ * of the 8 channels n + 16v (v = 0..7): its byte 4p + 2h + e holds channel n + 16(2p + e)
+ * for tokens 8k + 4h .. 8k + 4h + 3 (p = 0..3, h = 0..1, e = 0..1). */
 static int64_t key_code_byte(int32_t t, int32_t j) {
     int32_t tt = t % 32, w = j / 16, c = j % 16;
     return (int64_t)(t / 32) * 1024 + ((w % 4) * 16 + tt % 16) * 16 + (tt / 16) * 8 + (w / 4) * 4 + (c % 4);
 }
+static int key_code_shift(int32_t j) { return 2 * ((j % 16) / 4); }
+static int64_t value_code_byte(int32_t t, int32_t j) {
+    int32_t tt = t % 32, v = j / 16, n = j % 16;
+    return (int64_t)(t / 32) * 1024 + ((tt / 8) * 16 + n) * 16 + (v / 2) * 4 + ((tt % 8) / 4) * 2 + v % 2;
+}
+static int value_code_shift(int32_t t) { return 2 * (t % 4); }
+
 static int64_t code_byte(int key, int32_t t, int32_t j) {
     return key ? key_code_byte(t, j) : value_code_byte(t, j);
 }
-static int code_shift(int32_t j) { return 2 * ((j % 16) / 4); }
+static int code_shift(int key, int32_t t, int32_t j) {
+    return key ? key_code_shift(j) : value_code_shift(t);
+}
 
 static void put_code(uint8_t* codes_row, int key, int32_t t, int32_t j, uint8_t code) {
     uint8_t* byte = codes_row + code_byte(key, t, j);
-    int sh = code_shift(j);
+    int sh = code_shift(key, t, j);
     *byte = (uint8_t)((*byte & ~(3u << sh)) | ((unsigned)code << sh));
 }
 
 static uint8_t get_code(const uint8_t* codes_row, int key, int32_t t, int32_t j) {
-    return (uint8_t)((codes_row[code_byte(key, t, j)] >> code_shift(j)) & 3u);
+    return (uint8_t)((codes_row[code_byte(key, t, j)] >> code_shift(key, t, j)) & 3u);
 }
 
 static uint8_t* k_codes_row(const kivi_ref_cache* c, int64_t row) {
@@ -172,11 +176,10 @@ static uint16_t* k_pair(const kivi_ref_cache* c, int64_t row, int32_t g, int32_t
     int64_t groups = c->token_cap / c->group;
     return c->k_sz + ((row * groups + g) * c->head_dim + j) * 2;
 }
-/* (scale, zero) of value token t, channel group k: per 32-token group, the pairs of channel
- * group 0 for its 32 tokens, then of channel group 1, ... */
+/* (scale, zero) of value token t, channel group k */
 static uint16_t* v_pair(const kivi_ref_cache* c, int64_t row, int32_t t, int32_t k) {
     int64_t per_tok = c->head_dim / c->group;
-    return c->v_sz + ((row * c->token_cap + (int64_t)(t / 32) * 32) * per_tok + k * 32 + t % 32) * 2;
+    return c->v_sz + ((row * c->token_cap + t) * per_tok + k) * 2;
 }
 static uint16_t* res_slot(const kivi_ref_cache* c, uint16_t* base, int64_t row, int32_t slot) {
     return base + (row * c->residual_cap + slot) * c->head_dim;

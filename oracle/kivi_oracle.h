@@ -44,15 +44,18 @@ void kivi_ref_quant_group(const uint16_t* x, ptrdiff_t stride, int32_t n,
 /* ---- the cache (host memory, same documented layout as the device cache) ----
  * row = b*kv_heads + h.
  *   k_codes, v_codes : [row][token_cap/32][1024] bytes, one 1024-byte tile per 32-token
- *                      group (head_dim 128).  A little-endian 32-bit word holds channels
- *                      16w..16w+15 of one token, channel 16w+4i+b in byte b at bits 2i, 2i+1.
- *                      v_codes tiles: 16-byte chunk ((u*8+q)*4+h) holds words 2h, 2h+1 of
- *                      token 4q+2u, then of token 4q+2u+1.  k_codes tiles: 16-byte chunk
+ *                      group (head_dim 128).
+ *                      k_codes: a little-endian 32-bit word holds channels 16w..16w+15 of
+ *                      one token, channel 16w+4i+b in byte b at bits 2i, 2i+1; 16-byte chunk
  *                      (16k+n) holds words k, 4+k of token n, then of token 16+n.
+ *                      v_codes: a byte holds one channel's codes for four consecutive tokens
+ *                      (token 4a+i at bits 2i, 2i+1); 16-byte chunk (16k+n) covers tokens
+ *                      8k..8k+7 and channels n+16v, its byte 4p+2h+e holding channel
+ *                      n+16(2p+e) for tokens 8k+4h..8k+4h+3.
  *   k_sz             : [row][token_cap/group][head_dim][2] fp16 (scale, zero) per
  *                      (token group, channel)  -- keys per-channel.
- *   v_sz             : [row][token_cap/32][head_dim/group][32][2] fp16 (scale, zero) per
- *                      (token, channel group)  -- values per-token, grouped by 32 tokens.
+ *   v_sz             : [row][token_cap][head_dim/group][2] fp16 (scale, zero) per
+ *                      (token, channel group)  -- values per-token.
  *   k_res, v_res     : [row][residual_cap][head_dim] fp16 ring; the n_res residual
  *                      tokens, oldest first, sit in slots (res_head+i) % residual_cap. */
 typedef struct kivi_ref_cache {

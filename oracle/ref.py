@@ -99,7 +99,7 @@ class RefCache:
         self.k_codes = np.zeros((rows, tiles, group * head_dim // 4), np.uint8)
         self.v_codes = np.zeros((rows, tiles, group * head_dim // 4), np.uint8)
         self.k_sz = np.zeros((rows, tiles, head_dim, 2), np.uint16)
-        self.v_sz = np.zeros((rows, tiles, head_dim // group, group, 2), np.uint16)
+        self.v_sz = np.zeros((rows, tiles * group, head_dim // group, 2), np.uint16)
         self.k_res = np.zeros((rows, residual_cap, head_dim), np.uint16)
         self.v_res = np.zeros((rows, residual_cap, head_dim), np.uint16)
         self.s = _CacheStruct(batch, kv_heads, head_dim, group, residual_cap, token_cap, 0, 0, 0,

@@ -38,7 +38,6 @@ def quant_vectors():
             "scale": int(b["scale"], 16),
             "zero": int(b["zero"], 16),
             "codes": _expand(b["codes"].split(), int),
-            "packed": [int(x, 16) for x in b["packed"].split()],
         })
     return vecs
 

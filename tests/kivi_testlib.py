@@ -54,9 +54,9 @@ def assert_cache_equal(gpu, oracle, rows=None, upto=None, ring=True):
     kc = gpu.k_codes[sel, :ng].cpu().numpy()
     vc = gpu.v_codes[sel, :ng].cpu().numpy()
     ks = bits(gpu.k_sz[sel, :ng])
-    vs = bits(gpu.v_sz[sel, :ng])
+    vs = bits(gpu.v_sz[sel, :nq])                   # value pairs are per token
     for name, a, b in (("k_codes", kc, oracle.k_codes[sel, :ng]), ("v_codes", vc, oracle.v_codes[sel, :ng]),
-                       ("k_sz", ks, oracle.k_sz[sel, :ng]), ("v_sz", vs, oracle.v_sz[sel, :ng])):
+                       ("k_sz", ks, oracle.k_sz[sel, :ng]), ("v_sz", vs, oracle.v_sz[sel, :nq])):
         bad = np.argwhere(a != b)
         assert bad.size == 0, f"{name}: {bad.shape[0]} mismatches, first at {bad[0].tolist()}: " \
                               f"gpu {a[tuple(bad[0])]} oracle {b[tuple(bad[0])]}"

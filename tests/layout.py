@@ -1,11 +1,13 @@
 """Readers of the packed cache layout documented in include/kivi.h, for tests.
 
-Codes: one 1024-byte tile per 32-token group.  A little-endian 32-bit word holds the 16
-channels 16w..16w+15 of one token, channel 16w + 4i + b in byte b at bits 2i, 2i+1.
-Value tiles: 16-byte chunk ((u*8+q)*4+h) holds words 2h and 2h+1 of token 4q+2u, then of
-token 4q+2u+1.  Key tiles: 16-byte chunk (16k+n) holds words k and 4+k of token n, then of
-token 16+n.
-Value pairs: per 32-token group, [channel group][token in group][scale, zero].
+Codes: one 1024-byte tile per 32-token group.
+Key tiles: a little-endian 32-bit word holds the 16 channels 16w..16w+15 of one token,
+channel 16w + 4i + b in byte b at bits 2i, 2i+1; 16-byte chunk (16k+n) holds words k and
+4+k of token n, then of token 16+n.
+Value tiles: a byte holds one channel's codes for four consecutive tokens, token 4a+i at
+bits 2i, 2i+1; 16-byte chunk (16k+n) covers tokens 8k..8k+7 and its byte 4p+2h+e holds
+channel n+16(2p+e) for tokens 8k+4h..8k+4h+3.
+Value pairs: [token][channel group][scale, zero].
 """
 import numpy as np
 
@@ -16,10 +18,10 @@ def value_code_pos(t, j):
     """(byte offset within the row, bit shift) of value token t, channel j."""
     t, j = np.asarray(t), np.asarray(j)
     tt = t % 32
-    q, u, t1 = tt // 4, (tt % 4) // 2, tt % 2
-    h, w, c = j // 32, (j % 32) // 16, j % 16
-    byte = (t // 32) * 1024 + ((u * 8 + q) * 4 + h) * 16 + t1 * 8 + w * 4 + (c % 4)
-    return byte, 2 * (c // 4)
+    v, n = j // 16, j % 16
+    chunk = (tt // 8) * 16 + n
+    byte = (t // 32) * 1024 + chunk * 16 + (v // 2) * 4 + ((tt % 8) // 4) * 2 + v % 2
+    return byte, 2 * (tt % 4)
 
 
 def key_code_pos(t, j):
@@ -54,17 +56,8 @@ def unpack_key_codes(tiles):
 
 
 def value_pairs(v_sz):
-    """[..., n_tiles, 4, 32, 2] -> [..., n_tiles*32, 4, 2] (token-major)."""
-    v = np.asarray(v_sz)
-    v = np.swapaxes(v, -3, -2)                      # [..., tiles, 32, 4, 2]
-    return v.reshape(*v.shape[:-4], -1, v.shape[-2], 2)
-
-
-def token_quarter_bytes(tiles_row, t, h):
-    """The 8 value-code bytes of token t, channel quarter h, from one row's tiles [n, 1024]."""
-    flat = np.asarray(tiles_row).reshape(-1)
-    start, _ = value_code_pos(t, 32 * h)
-    return flat[start:start + 8]
+    """[..., tokens, 4, 2] value pairs (stored token-major already)."""
+    return np.asarray(v_sz)
 
 
 def key_word_bytes(tiles_row, t, w):

@@ -6,7 +6,7 @@ import torch
 
 from golden_io import quant_vectors
 from kivi_testlib import assert_cache_equal, bits, gpu_or_skip, ref_cache
-from layout import key_word_bytes, token_quarter_bytes, value_pairs
+from layout import key_word_bytes, unpack_value_codes, value_pairs
 from kv_cache_bit_quantize_amd import synth
 from oracle import ref
 
@@ -69,7 +69,7 @@ def test_hand_vectors(vec):
     kivi.kivi_quantize_k_per_channel(k.to(dev), cache)
     torch.cuda.synchronize()
     assert value_pairs(bits(cache.v_sz[0]))[0, 1].tolist() == [vec["scale"], vec["zero"]]
-    assert token_quarter_bytes(cache.v_codes[0].cpu().numpy(), 0, 1).tolist() == vec["packed"]
+    assert unpack_value_codes(cache.v_codes[0].cpu().numpy())[0, 32:64].tolist() == vec["codes"]
     assert bits(cache.k_sz[0, 0, 5]).tolist() == [vec["scale"], vec["zero"]]
     kc = cache.k_codes[0].cpu().numpy()
     assert [int(key_word_bytes(kc, t, 0)[1] >> 2 & 3) for t in range(G)] == vec["codes"]
@@ -123,7 +123,7 @@ def test_distributions_keys_and_values(kind):
     for name in ("k_codes", "v_codes"):
         assert np.array_equal(getattr(cache, name).cpu().numpy()[:, og:], getattr(rc, name)[:, og:]), name
     assert np.array_equal(bits(cache.k_sz)[:, og:], rc.k_sz[:, og:])
-    assert np.array_equal(bits(cache.v_sz)[:, og:], rc.v_sz[:, og:])
+    assert np.array_equal(bits(cache.v_sz)[:, off:], rc.v_sz[:, off:])
     # nothing written before the offset
     assert not cache.k_codes[:, :og].any() and not cache.v_codes[:, :og].any()
 

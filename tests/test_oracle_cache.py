@@ -49,7 +49,7 @@ def test_append_from_empty_matches_closed_form_and_prefill():
     assert np.array_equal(c.k_codes[:, : nq // G], p.k_codes[:, : nq // G])
     assert np.array_equal(c.v_codes[:, : nq // G], p.v_codes[:, : nq // G])
     assert np.array_equal(c.k_sz[:, : nq // G], p.k_sz[:, : nq // G])
-    assert np.array_equal(c.v_sz[:, : nq // G], p.v_sz[:, : nq // G])
+    assert np.array_equal(c.v_sz[:, :nq], p.v_sz[:, :nq])
     for row in range(B * H):
         Kc, Vc = c.dequant_row(row)
         Kp, Vp = p.dequant_row(row)

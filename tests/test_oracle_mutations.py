@@ -25,15 +25,20 @@ MUTATIONS = [
     ("zero_is_max", "*zero = kivi_ref_f32_to_f16(mn);", "*zero = kivi_ref_f32_to_f16(mx);", False),
     ("keep_negative_zero", "if (mn == 0.0f) mn = 0.0f;", "", False),
     ("keep_negative_zero_max", "if (mx == 0.0f) mx = 0.0f;", "", False),
-    ("token_major_packing",
-     "return (int64_t)(t / 32) * 1024 + ((u * 8 + q) * 4 + h) * 16 + t1 * 8 + w * 4 + (c % 4);",
-     "return (int64_t)t * 32 + h * 8 + w * 4 + (c % 4);", False),
-    ("tile_chunk_order",
-     "return (int64_t)(t / 32) * 1024 + ((u * 8 + q) * 4 + h) * 16 + t1 * 8 + w * 4 + (c % 4);",
-     "return (int64_t)(t / 32) * 1024 + ((q * 2 + u) * 4 + h) * 16 + t1 * 8 + w * 4 + (c % 4);", False),
-    ("value_pairs_token_major",
-     "return c->v_sz + ((row * c->token_cap + (int64_t)(t / 32) * 32) * per_tok + k * 32 + t % 32) * 2;",
-     "return c->v_sz + ((row * c->token_cap + t) * per_tok + k) * 2;", False),
+    ("value_token_major_packing",
+     "return (int64_t)(t / 32) * 1024 + ((tt / 8) * 16 + n) * 16 + (v / 2) * 4 + ((tt % 8) / 4) * 2 + v % 2;",
+     "return (int64_t)t * 32 + v * 4 + n / 4;", False),
+    ("value_chunk_order",
+     "return (int64_t)(t / 32) * 1024 + ((tt / 8) * 16 + n) * 16 + (v / 2) * 4 + ((tt % 8) / 4) * 2 + v % 2;",
+     "return (int64_t)(t / 32) * 1024 + (n * 4 + tt / 8) * 16 + (v / 2) * 4 + ((tt % 8) / 4) * 2 + v % 2;", False),
+    ("value_byte_pairing",
+     "return (int64_t)(t / 32) * 1024 + ((tt / 8) * 16 + n) * 16 + (v / 2) * 4 + ((tt % 8) / 4) * 2 + v % 2;",
+     "return (int64_t)(t / 32) * 1024 + ((tt / 8) * 16 + n) * 16 + (v / 2) * 4 + (v % 2) * 2 + (tt % 8) / 4;", False),
+    ("value_token_bits_reversed", "static int value_code_shift(int32_t t) { return 2 * (t % 4); }",
+     "static int value_code_shift(int32_t t) { return 6 - 2 * (t % 4); }", False),
+    ("value_pairs_group_major",
+     "return c->v_sz + ((row * c->token_cap + t) * per_tok + k) * 2;",
+     "return c->v_sz + ((row * c->token_cap + (int64_t)(t / 32) * 32) * per_tok + k * 32 + t % 32) * 2;", False),
     ("key_token_major_packing",
      "return (int64_t)(t / 32) * 1024 + ((w % 4) * 16 + tt % 16) * 16 + (tt / 16) * 8 + (w / 4) * 4 + (c % 4);",
      "return (int64_t)t * 32 + w * 4 + (c % 4);", False),
@@ -42,8 +47,8 @@ MUTATIONS = [
      "return (int64_t)(t / 32) * 1024 + ((tt % 16) * 4 + w % 4) * 16 + (tt / 16) * 8 + (w / 4) * 4 + (c % 4);", False),
     ("keys_in_value_order", "return key ? key_code_byte(t, j) : value_code_byte(t, j);",
      "return value_code_byte(t, j);", False),
-    ("bit_order_packing", "static int code_shift(int32_t j) { return 2 * ((j % 16) / 4); }",
-     "static int code_shift(int32_t j) { return 2 * (j % 4); }", False),
+    ("key_bit_order_packing", "static int key_code_shift(int32_t j) { return 2 * ((j % 16) / 4); }",
+     "static int key_code_shift(int32_t j) { return 2 * (j % 4); }", False),
     ("key_pair_per_token", "const uint16_t* kp = k_pair(c, row, t / G, j);",
      "const uint16_t* kp = k_pair(c, row, t % (c->token_cap / G), j);", False),
     ("value_pair_wrong_group", "const uint16_t* vp = v_pair(c, row, t, j / G);",

@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 from golden_io import quant_vectors
-from layout import key_word_bytes, token_quarter_bytes, unpack_key_codes, unpack_value_codes, value_pairs
+from layout import key_word_bytes, unpack_key_codes, unpack_value_codes, value_pairs
 from oracle import ref
 
 D, G = 128, 32
@@ -38,13 +38,13 @@ def test_hand_vectors_group(vec):
 
 @pytest.mark.parametrize("vec", quant_vectors(), ids=lambda v: v["name"])
 def test_hand_vectors_as_value_token(vec):
-    """The group as channels 32..63 of one value token: pair and packed bytes."""
+    """The group as channels 32..63 of one value token: pair and codes at their documented places."""
     c = ref.RefCache(1, 1, D, G, 128, token_cap=G)
     src = np.zeros((1, 1, D), np.uint16)
     src[0, 0, 32:64] = vec["input"]
     c.quantize_v(src, 1)
     assert value_pairs(c.v_sz[0])[0, 1].tolist() == [vec["scale"], vec["zero"]]
-    assert token_quarter_bytes(c.v_codes[0], 0, 1).tolist() == vec["packed"]
+    assert unpack_value_codes(c.v_codes[0])[0, 32:64].tolist() == vec["codes"]
 
 
 @pytest.mark.parametrize("vec", quant_vectors(), ids=lambda v: v["name"])
