@@ -56,8 +56,24 @@ int64_t rows_of(const kivi_cache* c) { return (int64_t)c->batch * c->kv_heads; }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? KIVI_OK : KIVI_ERR_HIP; }
 
+// Query heads one workgroup takes: a KV head's query group (or an equal share of it) goes
+// to one workgroup, which streams the KV head's cache once for all of them.
+int32_t queries_per_block(int32_t ratio) {
+    if (ratio % 4 == 0) return 4;
+    if (ratio % 3 == 0) return 3;
+    if (ratio % 2 == 0) return 2;
+    return 1;
+}
+
+// workgroup rows of the attention grid
+int64_t block_rows(const kivi_cache* c, int32_t q_heads) {
+    const int32_t ratio = q_heads / c->kv_heads;
+    const int32_t nq = queries_per_block(ratio);
+    return nq > 1 ? (int64_t)c->batch * c->kv_heads * (ratio / nq) : (int64_t)c->batch * q_heads;
+}
+
 int32_t auto_splits(const kivi_cache* c, int32_t q_heads) {
-    const int64_t rows = (int64_t)c->batch * q_heads;
+    const int64_t rows = block_rows(c, q_heads);
     const int64_t groups = c->n_quant / c->group;
     int64_t s = (kTargetBlocks + rows - 1) / rows;
     const int64_t cap = groups / kMinGroupsPerSplit;
@@ -287,8 +303,13 @@ int kivi_decode_attn(const kivi_cache* c, const uint16_t* q, int32_t q_heads, fl
     a.n_res = c->n_res;
     a.res_head = c->res_head;
     a.splits = splits;
-    a.groups_per_split = (groups + splits - 1) / splits;
+    // The last split also reads the fp16 residual (512 bytes per token against 96 for a
+    // quantized token): count it as that many groups so the last split gets fewer.
+    const int32_t res_groups = (c->n_res * 512 + 96 * c->group - 1) / (96 * c->group);
+    a.groups_per_split = (groups + res_groups + splits - 1) / splits;
     a.q_rows = (int64_t)c->batch * q_heads;
+    a.nq = queries_per_block(a.ratio);
+    a.block_rows = block_rows(c, q_heads);
     return hip_status(launch_decode_attn(a, (hipStream_t)stream));
 }
 

@@ -32,126 +32,20 @@
 //    exponent reads 1.0 (the exact halves 1 + c/4, 1 + c/16); the weights carry the
 //    matching factor 4 or 16 and a power of two keeping them in fp16 range.  The constant
 //    part, the sum of the weights, is accumulated on the side and subtracted at the end.
-#include "kivi_device.h"
-#include "kivi_internal.h"
+#include "kivi_attn_common.h"
 
 namespace kivi {
 
-constexpr int kWaves = kBlock / 64;
-constexpr int kSlots = 2 * kWaves;   // softmax states per workgroup: quantized, residual
-constexpr int kPart = kD + 2;        // floats per partial: o[128], m, l
 // LDS area of one (parity, wave)
 constexpr int kGroupTbl = 4 * kD;                 // key digit planes of one group: 4 x 128 B
 constexpr int kWtOff = 2 * kGroupTbl;             // value weights [group][chgroup][kg][8] fp16
 constexpr int kZeroOff = kWtOff + 2 * 4 * 4 * 16;  // 512 zero bytes
 constexpr int kAreaBytes = kZeroOff + 512;
 
-typedef int v4i __attribute__((ext_vector_type(4)));
-typedef float v4f __attribute__((ext_vector_type(4)));
-typedef _Float16 v8h __attribute__((ext_vector_type(8)));
-
-// value of lane 4*(lane/4) + i, for CTRL = quad_perm [i, i, i, i]
-template <int CTRL>
-__device__ __forceinline__ float quad_bcast(float v) { return dpp_f<CTRL>(v); }
-
-// (x & m) | o in one instruction (v_and_or_b32 takes its constants in VGPRs)
-__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t o) {
-    uint32_t r;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(m), "v"(o));
-    return r;
-}
-
-// sum over all 64 lanes (every lane gets it)
-__device__ __forceinline__ float wave_sum(float v) {
-    v = half_sum(v);
-    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0)) +
-           __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
-}
-
-__device__ __forceinline__ void load_q32(const uint16_t* q, float scale, float (&qv)[32]) {
-    const uint4* qp = reinterpret_cast<const uint4*>(q);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        uint4 x = qp[i];
-        uint32_t w[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            qv[8 * i + 2 * k] = h2f(w[k] & 0xffffu) * scale;
-            qv[8 * i + 2 * k + 1] = h2f(w[k] >> 16) * scale;
-        }
-    }
-}
-
-// Split partials cross workgroups, which may sit on different XCDs with separate L2 caches.
-// They are written and read with agent-scope atomic accesses (global_store / global_load with
-// the sc1 coherence bit), each coherent by itself.  Device-scope fences are avoided on
-// purpose: on this chip each one writes back and invalidates the whole L2 of the XCD, which
-// stalls every other workgroup streaming through it.
-__device__ __forceinline__ void store_coherent(float* p, float v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_coherent(float* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// s_waitcnt with vmcnt(0) and the other counters left free (expcnt 7, lgkmcnt 15)
-constexpr int kWaitVmcnt0 = 0x0F70;
-
-// Log-sum-exp merge of one query row's split partials by the whole workgroup: the m and l of
-// every split are read once (spread over the threads), then each output channel sums its
-// splits' o with several loads in flight.  out = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M),
-// lse = (M + log2 L) ln 2.  Re-arms the row counter.
-__device__ __forceinline__ void merge_row(const AttnArgs& a, int64_t qrow) {
-    __shared__ float sh_sc[kMaxSplits];
-    __shared__ float sh_red[kWaves];
-    __shared__ float sh_half[2][kD];
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    float* rowp = a.ws + qrow * kPart;
-    const int64_t stride = a.q_rows * kPart;
-    float mloc = -INFINITY;
-    for (int s = t; s < a.splits; s += kBlock) {
-        const float ms = load_coherent(rowp + s * stride + kD);
-        sh_sc[s] = ms;
-        mloc = fmaxf(mloc, ms);
-    }
-    mloc = wave_max_xor(mloc, 1, 32);
-    if (lane == 0) sh_red[wave] = mloc;
-    __syncthreads();
-    float M = sh_red[0];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sh_red[w]);
-    __syncthreads();
-    float lloc = 0.0f;
-    for (int s = t; s < a.splits; s += kBlock) {
-        const float ms = sh_sc[s];
-        const float sc = ms == -INFINITY ? 0.0f : exp2f(ms - M);
-        sh_sc[s] = sc;
-        lloc = fmaf(load_coherent(rowp + s * stride + kD + 1), sc, lloc);
-    }
-    lloc = wave_sum_xor(lloc, 1, 32);
-    if (lane == 0) sh_red[wave] = lloc;
-    __syncthreads();
-    float L = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) L += sh_red[w];
-    const int j = t & (kD - 1), h = t >> 7;
-    float O = 0.0f;
-#pragma unroll 8
-    for (int s = h; s < a.splits; s += 2) O = fmaf(load_coherent(rowp + s * stride + j), sh_sc[s], O);
-    sh_half[h][j] = O;
-    __syncthreads();
-    if (t < kD) {
-        a.out[qrow * kD + t] = (uint16_t)f2h((sh_half[0][t] + sh_half[1][t]) / L);
-        if (t == 0) {
-            if (a.lse != nullptr) a.lse[qrow] = (M + log2f(L)) * 0.69314718055994531f;
-            a.counters[qrow] = 0u;
-        }
-    }
-}
-
 __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
     __shared__ __align__(16) uint8_t sh_area[2][kWaves][kAreaBytes];
-    __shared__ float sh_o[kSlots][kD];
-    __shared__ float sh_m[kSlots], sh_l[kSlots];
+    __shared__ float sh_o[1][kSlots][kD];
+    __shared__ float sh_m[1][kSlots], sh_l[1][kSlots];
 
     const int split = blockIdx.x;
     const int64_t qrow = blockIdx.y;
@@ -216,7 +110,7 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
     const uint32_t* kp_row = reinterpret_cast<const uint32_t*>(a.k_sz) + kvrow * (int64_t)(a.token_cap / kG) * kD;
     const uint32_t* vp_row = reinterpret_cast<const uint32_t*>(a.v_sz) + tok_base * (kD / kG);
 
-    const uint32_t kM6 = 0x00C000C0u, kM8 = 0x03000300u, kOne = 0x3C003C00u;
+    const uint32_t kM6 = in_vgpr(0x00C000C0u), kM8 = in_vgpr(0x03000300u), kOne = in_vgpr(0x3C003C00u);
 
     // one wave-iteration's global loads (issued one iteration ahead of their use); every
     // load instruction reads a contiguous span
@@ -385,119 +279,31 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
     if (lane < 16) {   // row 0 of the accumulators: channel 16v + lane
         const float inv = vs != 0.0f ? 1.0f / vs : 0.0f;
 #pragma unroll
-        for (int v = 0; v < 8; ++v) sh_o[wave][16 * v + lane] = fmaf(cv[v][0] - bk[v >> 1], inv, zk[v >> 1]);
+        for (int v = 0; v < 8; ++v) sh_o[0][wave][16 * v + lane] = fmaf(cv[v][0] - bk[v >> 1], inv, zk[v >> 1]);
     }
     if (lane == 0) {
-        sh_m[wave] = m;
-        sh_l[wave] = lsum;
+        sh_m[0][wave] = m;
+        sh_l[0][wave] = lsum;
     }
 
-    // ---- fp16 residual, logical tokens [32*wave, 32*wave+32) of the ring, last split only,
-    // as a separate state.  Lane = 4*tp + qq: tokens 2tp, 2tp+1 of the chunk, channels
-    // [32qq, 32qq+32).
-    float mr = -INFINITY, lr = 0.0f;
-    if (split == a.splits - 1 && wave * kG < a.n_res) {
-        const int tp = lane >> 2, qq = lane & 3;
-        float qv[32], o[32];
-        load_q32(a.q + qrow * kD + qq * 32, a.sm_log2, qv);
-#pragma unroll
-        for (int c = 0; c < 32; ++c) o[c] = 0.0f;
-        for (int base = wave * kG; base < a.n_res; base += kWaves * kG) {
-            const int i0 = base + 2 * tp, i1 = i0 + 1;
-            const bool ok0 = i0 < a.n_res, ok1 = i1 < a.n_res;
-            const int s0 = (a.res_head + (ok0 ? i0 : 0)) % a.residual_cap;
-            const int s1 = (a.res_head + (ok1 ? i1 : 0)) % a.residual_cap;
-            const int64_t r0 = (kvrow * a.residual_cap + s0) * kD + qq * 32;
-            const int64_t r1 = (kvrow * a.residual_cap + s1) * kD + qq * 32;
-            const uint4* k0 = reinterpret_cast<const uint4*>(a.k_res + r0);
-            const uint4* k1 = reinterpret_cast<const uint4*>(a.k_res + r1);
-            float d0 = 0.0f, d1 = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint4 x0 = k0[i], x1 = k1[i];
-                const uint32_t w0[4] = {x0.x, x0.y, x0.z, x0.w}, w1[4] = {x1.x, x1.y, x1.z, x1.w};
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const int c = 8 * i + 2 * k;
-                    d0 = fmaf(qv[c], h2f(w0[k] & 0xffffu), d0);
-                    d0 = fmaf(qv[c + 1], h2f(w0[k] >> 16), d0);
-                    d1 = fmaf(qv[c], h2f(w1[k] & 0xffffu), d1);
-                    d1 = fmaf(qv[c + 1], h2f(w1[k] >> 16), d1);
-                }
-            }
-            d0 = wave_sum_xor(d0, 1, 2);
-            d1 = wave_sum_xor(d1, 1, 2);
-            const float l0 = ok0 ? d0 : -INFINITY, l1 = ok1 ? d1 : -INFINITY;
-            const float m_new = fmaxf(mr, wave_max_xor(fmaxf(l0, l1), 4, 32));
-            const float alpha = (mr == -INFINITY) ? 0.0f : exp2f(mr - m_new);
-            const float p0 = ok0 ? exp2f(l0 - m_new) : 0.0f;
-            const float p1 = ok1 ? exp2f(l1 - m_new) : 0.0f;
-            lr = lr * alpha + (qq == 0 ? p0 + p1 : 0.0f);   // one share per token pair
-            const uint4* v0 = reinterpret_cast<const uint4*>(a.v_res + r0);
-            const uint4* v1 = reinterpret_cast<const uint4*>(a.v_res + r1);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint4 x0 = v0[i], x1 = v1[i];
-                const uint32_t w0[4] = {x0.x, x0.y, x0.z, x0.w}, w1[4] = {x1.x, x1.y, x1.z, x1.w};
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const int c = 8 * i + 2 * k;
-                    o[c] = fmaf(p1, h2f(w1[k] & 0xffffu), fmaf(p0, h2f(w0[k] & 0xffffu), o[c] * alpha));
-                    o[c + 1] = fmaf(p1, h2f(w1[k] >> 16), fmaf(p0, h2f(w0[k] >> 16), o[c + 1] * alpha));
-                }
-            }
-            mr = m_new;
-        }
-        lr = wave_sum(lr);
-#pragma unroll
-        for (int c = 0; c < 32; ++c) o[c] = wave_sum_xor(o[c], 4, 32);
-        if (tp == 0) {
-#pragma unroll
-            for (int c = 0; c < 32; ++c) sh_o[kWaves + wave][qq * 32 + c] = o[c];
-        }
+    // ---- fp16 residual (last split only), as separate states
+    float mr[1], lr[1];
+    if (split == a.splits - 1) {
+        residual_states<1>(a, qrow, kvrow, wave, &sh_o[0][kWaves + wave][0], kSlots * kD, mr, lr);
+    } else {
+        mr[0] = -INFINITY;
+        lr[0] = 0.0f;
     }
     if (lane == 0) {
-        sh_m[kWaves + wave] = mr;
-        sh_l[kWaves + wave] = lr;
+        sh_m[0][kWaves + wave] = mr[0];
+        sh_l[0][kWaves + wave] = lr[0];
     }
     __syncthreads();
-
-    // ---- the workgroup's partial: log-sum-exp merge of its states (empty states skipped)
-    float* part = a.ws + ((int64_t)split * a.q_rows + qrow) * kPart;
-    if (threadIdx.x < kD) {
-        const int j = threadIdx.x;
-        float M = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < kSlots; ++w) M = fmaxf(M, sh_m[w]);
-        float L = 0.0f, O = 0.0f;
-#pragma unroll
-        for (int w = 0; w < kSlots; ++w) {
-            if (sh_m[w] == -INFINITY) continue;
-            const float sc = exp2f(sh_m[w] - M);
-            L = fmaf(sh_l[w], sc, L);
-            O = fmaf(sh_o[w][j], sc, O);
-        }
-        store_coherent(&part[j], O);
-        if (j == 0) {
-            store_coherent(&part[kD], M);
-            store_coherent(&part[kD + 1], L);
-        }
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // those stores have completed
-    }
-    // The last workgroup of this row to arrive merges every split's partial and writes the
-    // output.  The counter add comes after every partial store of this workgroup completed
-    // (the wait above, then the barrier), and the merging workgroup issues its coherent loads
-    // only after its own add returned the final count, so it reads every partial.
-    __syncthreads();
-    __shared__ bool sh_last;
-    if (threadIdx.x == 0)
-        sh_last = __hip_atomic_fetch_add(&a.counters[qrow], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                  (unsigned)(a.splits - 1);
-    __syncthreads();
-    if (sh_last) merge_row(a, qrow);
+    finish_block<1>(a, split, qrow, qrow, sh_o, sh_m, sh_l);
 }
 
 hipError_t launch_decode_attn(const AttnArgs& a, hipStream_t s) {
+    if (a.nq > 1) return launch_decode_attn_gqa(a, s);
     hipLaunchKernelGGL(attn_split_kernel, dim3((unsigned)a.splits, (unsigned)a.q_rows), dim3(kBlock), 0, s, a);
     return hipGetLastError();
 }

@@ -1,0 +1,283 @@
+// kivi_attn_common.h -- pieces shared by the decode-attention kernels (gfx950).
+//
+// Every kernel keeps, per workgroup and query row, kSlots softmax states in the log2 domain
+// (m, l, o[128] with o relative to 2^m): one per wave for the quantized history and one per
+// wave for the fp16 residual.  finish_block() merges them (log-sum-exp), then either writes
+// the output (one split) or a split partial; the last workgroup of a row to arrive merges
+// the partials and writes the output, so one launch does the whole call.
+#pragma once
+
+#include "kivi_device.h"
+#include "kivi_internal.h"
+
+namespace kivi {
+
+constexpr int kWaves = kBlock / 64;
+constexpr int kSlots = 2 * kWaves;   // softmax states per workgroup and row: quantized, residual
+constexpr int kPart = kD + 2;        // floats per split partial: o[128], m, l
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+
+// value of lane 4*(lane/4) + i, for CTRL = quad_perm [i, i, i, i]
+template <int CTRL>
+__device__ __forceinline__ float quad_bcast(float v) { return dpp_f<CTRL>(v); }
+
+// (x & m) | o, one v_and_or_b32 when m and o sit in VGPRs (see in_vgpr).  Written in C, not
+// inline asm, so that the compiler sees the instruction: its results feed matrix
+// instructions, and the compiler must insert the wait states between a matrix instruction
+// reading a register and a vector write to it.
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t o) { return (x & m) | o; }
+// A constant the compiler may not fold into literals: an empty asm statement (no instruction)
+// pins it to a VGPR, so (x & m) | o selects one three-operand v_and_or_b32 instead of a
+// v_and_b32 and a v_or_b32 with literal operands.
+__device__ __forceinline__ uint32_t in_vgpr(uint32_t c) {
+    asm volatile("" : "+v"(c));
+    return c;
+}
+
+__device__ __forceinline__ float readlane_f(float v, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+
+// sum over all 64 lanes (every lane gets it)
+__device__ __forceinline__ float wave_sum(float v) {
+    v = half_sum(v);
+    return readlane_f(v, 0) + readlane_f(v, 32);
+}
+// sum / max over the 16 lanes of each DPP row (every lane gets its row's result)
+__device__ __forceinline__ float row_sum(float v) {
+    v += xor1_f(v);
+    v += xor2_f(v);
+    v += hmirror_f(v);
+    return v + mirror_f(v);
+}
+__device__ __forceinline__ float row_max(float v) {
+    v = __builtin_fmaxf(v, xor1_f(v));
+    v = __builtin_fmaxf(v, xor2_f(v));
+    v = __builtin_fmaxf(v, hmirror_f(v));
+    return __builtin_fmaxf(v, mirror_f(v));
+}
+
+__device__ __forceinline__ void load_q32(const uint16_t* q, float scale, float (&qv)[32]) {
+    const uint4* qp = reinterpret_cast<const uint4*>(q);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint4 x = qp[i];
+        uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            qv[8 * i + 2 * k] = h2f(w[k] & 0xffffu) * scale;
+            qv[8 * i + 2 * k + 1] = h2f(w[k] >> 16) * scale;
+        }
+    }
+}
+
+// Split partials cross workgroups, which may sit on different XCDs with separate L2 caches.
+// They are written and read with agent-scope atomic accesses (global_store / global_load with
+// the sc1 coherence bit), each coherent by itself.  Device-scope fences are avoided on
+// purpose: on this chip each one writes back and invalidates the whole L2 of the XCD, which
+// stalls every other workgroup streaming through it.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(float* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// s_waitcnt with vmcnt(0) and the other counters left free (expcnt 7, lgkmcnt 15)
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+// Softmax states of query rows qrow0..qrow0+NQ-1 over the fp16 residual ring.  Called by one
+// whole wave; wave w takes the ring's logical tokens [32w + 128i, 32w + 128i + 32).  Lane
+// 4*tp + qq holds tokens 2tp, 2tp+1 of such a chunk and channels [32qq, 32qq+32); a chunk's
+// keys and values are loaded once, in one round, for all NQ rows, which then take turns,
+// 8 channels at a time, to keep few registers live.  Row r's o accumulates in o_dst[r*o_stride
+// + c]; m[r] = -inf and l[r] = 0 when the wave has no residual token.
+template <int NQ>
+__device__ void residual_states(const AttnArgs& a, int64_t qrow0, int64_t kvrow, int wave, float* o_dst,
+                                int o_stride, float (&mr)[NQ], float (&lr)[NQ]) {
+    const int lane = threadIdx.x & 63, tp = lane >> 2, qq = lane & 3;
+#pragma unroll
+    for (int r = 0; r < NQ; ++r) {
+        mr[r] = -INFINITY;
+        lr[r] = 0.0f;
+    }
+    for (int base = wave * kG; base < a.n_res; base += kWaves * kG) {
+        const int i0 = base + 2 * tp, i1 = i0 + 1;
+        const bool ok0 = i0 < a.n_res, ok1 = i1 < a.n_res;
+        const int s0 = (a.res_head + (ok0 ? i0 : 0)) % a.residual_cap;
+        const int s1 = (a.res_head + (ok1 ? i1 : 0)) % a.residual_cap;
+        const int64_t r0 = (kvrow * a.residual_cap + s0) * kD + qq * 32;
+        const int64_t r1 = (kvrow * a.residual_cap + s1) * kD + qq * 32;
+        const uint4* k0 = reinterpret_cast<const uint4*>(a.k_res + r0);
+        const uint4* k1 = reinterpret_cast<const uint4*>(a.k_res + r1);
+        const uint4* v0 = reinterpret_cast<const uint4*>(a.v_res + r0);
+        const uint4* v1 = reinterpret_cast<const uint4*>(a.v_res + r1);
+        uint4 kx0[4], kx1[4], vx0[4], vx1[4];   // keys and values in one round of loads
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            kx0[i] = k0[i];
+            kx1[i] = k1[i];
+            vx0[i] = v0[i];
+            vx1[i] = v1[i];
+        }
+        const bool first = base == wave * kG;
+        for (int r = 0; r < NQ; ++r) {
+            const uint4* qp = reinterpret_cast<const uint4*>(a.q + (qrow0 + r) * kD + qq * 32);
+            float d0 = 0.0f, d1 = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint4 qx = qp[i];
+                const uint32_t qh[4] = {qx.x, qx.y, qx.z, qx.w};
+                const uint32_t w0[4] = {kx0[i].x, kx0[i].y, kx0[i].z, kx0[i].w};
+                const uint32_t w1[4] = {kx1[i].x, kx1[i].y, kx1[i].z, kx1[i].w};
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const float qa = h2f(qh[k] & 0xffffu) * a.sm_log2, qb = h2f(qh[k] >> 16) * a.sm_log2;
+                    d0 = fmaf(qa, h2f(w0[k] & 0xffffu), d0);
+                    d0 = fmaf(qb, h2f(w0[k] >> 16), d0);
+                    d1 = fmaf(qa, h2f(w1[k] & 0xffffu), d1);
+                    d1 = fmaf(qb, h2f(w1[k] >> 16), d1);
+                }
+            }
+            d0 = wave_sum_xor(d0, 1, 2);
+            d1 = wave_sum_xor(d1, 1, 2);
+            const float l0 = ok0 ? d0 : -INFINITY, l1 = ok1 ? d1 : -INFINITY;
+            const float m_new = fmaxf(mr[r], wave_max_xor(fmaxf(l0, l1), 4, 32));
+            const float alpha = (mr[r] == -INFINITY) ? 0.0f : exp2f(mr[r] - m_new);
+            const float p0 = ok0 ? exp2f(l0 - m_new) : 0.0f;
+            const float p1 = ok1 ? exp2f(l1 - m_new) : 0.0f;
+            lr[r] = lr[r] * alpha + wave_sum(qq == 0 ? p0 + p1 : 0.0f);   // one share per token pair
+            mr[r] = m_new;
+            float* od = o_dst + r * o_stride + qq * 32;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t w0[4] = {vx0[i].x, vx0[i].y, vx0[i].z, vx0[i].w};
+                const uint32_t w1[4] = {vx1[i].x, vx1[i].y, vx1[i].z, vx1[i].w};
+                float oc[8];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    oc[2 * k] = fmaf(p1, h2f(w1[k] & 0xffffu), p0 * h2f(w0[k] & 0xffffu));
+                    oc[2 * k + 1] = fmaf(p1, h2f(w1[k] >> 16), p0 * h2f(w0[k] >> 16));
+                }
+#pragma unroll
+                for (int c = 0; c < 8; ++c) oc[c] = wave_sum_xor(oc[c], 4, 32);   // over the token pairs
+                if (tp == 0) {
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) od[8 * i + c] = first ? oc[c] : fmaf(od[8 * i + c], alpha, oc[c]);
+                }
+            }
+        }
+    }
+}
+
+// Log-sum-exp merge of the split partials of query rows qrow0..qrow0+NQ-1, by the whole
+// workgroup, with each thread's coherent loads issued together: a thread merges, for one
+// (row, channel), every lpp-th split online (lpp = 2 for one row, else 1), and thread
+// pairs combine in LDS.  out = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M),
+// lse = (M + log2 L) ln 2.  Re-arms the arrival counter.
+constexpr int kMergeBatch = 16;
+template <int NQ>
+__device__ __forceinline__ void merge_rows(const AttnArgs& a, int64_t qrow0, int64_t counter) {
+    constexpr int kLpp = NQ == 1 ? 2 : 1;
+    __shared__ float sh_mo[kD + 2];
+    const int t = threadIdx.x, sub = kLpp == 2 ? (t >> 7) : 0;
+    const int64_t stride = a.q_rows * kPart;
+    for (int idx = kLpp == 2 ? (t & (kD - 1)) : t; idx < NQ * kD; idx += kBlock / kLpp) {
+        const int r = idx / kD, j = idx % kD;
+        float* rowp = a.ws + (qrow0 + r) * kPart;
+        float M = -INFINITY, L = 0.0f, O = 0.0f;
+        for (int s0 = sub; s0 < a.splits; s0 += kLpp * kMergeBatch) {
+            float ms[kMergeBatch], ls[kMergeBatch], os[kMergeBatch];
+#pragma unroll
+            for (int u = 0; u < kMergeBatch; ++u) {
+                const int s = s0 + kLpp * u;
+                ms[u] = -INFINITY;
+                ls[u] = os[u] = 0.0f;
+                if (s < a.splits) {
+                    float* ps = rowp + s * stride;
+                    ms[u] = load_coherent(ps + kD);
+                    ls[u] = load_coherent(ps + kD + 1);
+                    os[u] = load_coherent(ps + j);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kMergeBatch; ++u) {
+                if (ms[u] == -INFINITY) continue;
+                const float mn = fmaxf(M, ms[u]);
+                const float al = exp2f(M - mn), be = exp2f(ms[u] - mn);   // M = -inf gives al = 0
+                L = fmaf(L, al, ls[u] * be);
+                O = fmaf(O, al, os[u] * be);
+                M = mn;
+            }
+        }
+        if (kLpp == 2) {
+            if (sub == 1) {
+                sh_mo[j] = O;
+                if (j == 0) {
+                    sh_mo[kD] = M;
+                    sh_mo[kD + 1] = L;
+                }
+            }
+            __syncthreads();
+            if (sub == 1) return;
+            const float m1 = sh_mo[kD], l1 = sh_mo[kD + 1], o1 = sh_mo[j];
+            const float mn = fmaxf(M, m1);
+            const float al = M == -INFINITY ? 0.0f : exp2f(M - mn), be = m1 == -INFINITY ? 0.0f : exp2f(m1 - mn);
+            L = fmaf(L, al, l1 * be);
+            O = fmaf(O, al, o1 * be);
+            M = mn;
+        }
+        a.out[(qrow0 + r) * kD + j] = (uint16_t)f2h(O / L);
+        if (j == 0 && a.lse != nullptr) a.lse[qrow0 + r] = (M + log2f(L)) * 0.69314718055994531f;
+    }
+    if (t == 0) a.counters[counter] = 0u;
+}
+
+// End of a workgroup: merge its kSlots states per row (empty states skipped), then write the
+// output directly (one split) or the split partial, and let the last workgroup of the row
+// group to arrive merge the partials.  The counter add comes after every partial store of
+// this workgroup completed (the wait, then the barrier), and the merging workgroup issues its
+// coherent loads only after its own add returned the final count, so it reads every partial.
+template <int NQ>
+__device__ __forceinline__ void finish_block(const AttnArgs& a, int split, int64_t qrow0, int64_t counter,
+                                             const float (*sh_o)[kSlots][kD], const float (*sh_m)[kSlots],
+                                             const float (*sh_l)[kSlots]) {
+    for (int idx = threadIdx.x; idx < NQ * kD; idx += kBlock) {
+        const int r = idx / kD, j = idx % kD;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kSlots; ++w) M = fmaxf(M, sh_m[r][w]);
+        float L = 0.0f, O = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kSlots; ++w) {
+            if (sh_m[r][w] == -INFINITY) continue;
+            const float sc = exp2f(sh_m[r][w] - M);
+            L = fmaf(sh_l[r][w], sc, L);
+            O = fmaf(sh_o[r][w][j], sc, O);
+        }
+        if (a.splits == 1) {
+            a.out[(qrow0 + r) * kD + j] = (uint16_t)f2h(O / L);
+            if (j == 0 && a.lse != nullptr) a.lse[qrow0 + r] = (M + log2f(L)) * 0.69314718055994531f;
+        } else {
+            float* part = a.ws + ((int64_t)split * a.q_rows + qrow0 + r) * kPart;
+            store_coherent(&part[j], O);
+            if (j == 0) {
+                store_coherent(&part[kD], M);
+                store_coherent(&part[kD + 1], L);
+            }
+        }
+    }
+    if (a.splits == 1) return;
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // the partial stores have completed
+    __syncthreads();
+    __shared__ bool sh_last;
+    if (threadIdx.x == 0)
+        sh_last = __hip_atomic_fetch_add(&a.counters[counter], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                  (unsigned)(a.splits - 1);
+    __syncthreads();
+    if (sh_last) merge_rows<NQ>(a, qrow0, counter);
+}
+
+}  // namespace kivi

@@ -1,0 +1,367 @@
+// kivi_attn_gqa.hip -- decode attention for grouped-query heads (gfx950).
+//
+// With grouped-query attention several query heads share one KV head (the query group of a
+// KV head; the Mistral-7B shape has 4).  Running them one head at a time would stream the
+// same 2-bit cache once per query.  Here one workgroup takes NQ query heads of a KV head and
+// streams that KV head's cache once, and the query group is the M dimension of both matrix
+// contractions:
+//
+//  * keys: the A operand of v_mfma_i32_16x16x64_i8 holds, in row 4h + d, digit d of the
+//    fixed-point q_h*s (the 30-bit integer scheme of the single-query kernel), so one
+//    instruction gives the four digit sums of NQ queries for 16 tokens.  Tile t (tokens
+//    16t..16t+15 of the wave-iteration's 64) has its own accumulator; lane 16h + n ends
+//    with query h's digit sums for token 16t + n.
+//  * values: the A operand of v_mfma_f32_16x16x32_f16 holds query h's fp16 token weights
+//    p*s in row h, against the same code operands as the single-query kernel, so the
+//    accumulator rows are the NQ queries' outputs.
+//
+// Split-K, the residual, the per-query online softmax (log2 domain) and the merge follow
+// the single-query kernel (kivi_attn.hip, kivi_attn_common.h).
+#include "kivi_attn_common.h"
+
+namespace kivi {
+
+template <int NQ>
+struct GqaLds {
+    static constexpr int kKeyGroup = NQ * 4 * kD;      // digit planes of one group: [query][digit][128 B]
+    static constexpr int kWtOff = 2 * kKeyGroup;        // weights [group][chgroup][query][kg][8] fp16
+    static constexpr int kWtGroup = 4 * NQ * 64;
+    static constexpr int kPairOff = kWtOff + 2 * kWtGroup;   // value pairs of the 64 tokens, [64][16 B]
+    static constexpr int kBytes = kPairOff + 64 * 16;
+    static constexpr int kZeroBytes = kKeyGroup + 256;  // covers every offset a zero row reads at
+};
+
+template <int NQ>
+__global__ __launch_bounds__(kBlock) void attn_gqa_kernel(AttnArgs a) {
+    using Lds = GqaLds<NQ>;
+    __shared__ __align__(16) uint8_t sh_area[kWaves][Lds::kBytes];
+    __shared__ __align__(16) uint8_t sh_zero[Lds::kZeroBytes];
+    __shared__ float sh_o[NQ][kSlots][kD];
+    __shared__ float sh_m[NQ][kSlots], sh_l[NQ][kSlots];
+
+    const int split = blockIdx.x;
+    const int64_t grow = blockIdx.y;                 // (batch, kv head, query chunk)
+    const int chunks = a.ratio / NQ;
+    const int64_t kvrow = grow / chunks;
+    const int chunk = (int)(grow % chunks);
+    const int64_t qrow0 = (kvrow / a.kv_heads) * a.q_heads + (kvrow % a.kv_heads) * a.ratio + chunk * NQ;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int gh = lane >> 5, tt = lane & 31;        // token role (loads): token tt of group gh
+    const int wl = lane & 31, wk = wl & 3;           // fixed-point writer role: channels 4wl..4wl+3
+    const int mrow = lane & 15, kgrp = lane >> 4;    // matrix-operand role
+    const int qh = lane >> 4, n = lane & 15;         // logit / weight role: query qh, token n of each tile
+    const bool qlive = qh < NQ;
+    uint8_t* area = &sh_area[wave][0];
+
+    for (int i = threadIdx.x; i < Lds::kZeroBytes / 16; i += kBlock)
+        reinterpret_cast<uint4*>(sh_zero)[i] = make_uint4(0, 0, 0, 0);
+
+    // query channels 4wl..4wl+3 of the NQ queries, log2 domain
+    float qw[NQ][4];
+#pragma unroll
+    for (int r = 0; r < NQ; ++r) {
+        const uint2 x = *reinterpret_cast<const uint2*>(a.q + (qrow0 + r) * kD + 4 * wl);
+        qw[r][0] = h2f(x.x & 0xffffu) * a.sm_log2;
+        qw[r][1] = h2f(x.x >> 16) * a.sm_log2;
+        qw[r][2] = h2f(x.y & 0xffffu) * a.sm_log2;
+        qw[r][3] = h2f(x.y >> 16) * a.sm_log2;
+    }
+    // codes of channels 4i..4i+3 arrive multiplied by 1, 4, 16, 16 (i = 0..3)
+    const float cls_div = wk == 0 ? 1.0f : (wk == 1 ? 0.25f : 0.0625f);
+
+    // key A operand of group g, channel half kh: row 4h + d = digit plane (h, d) of the group
+    // (rows of absent queries read zeros) at kbase + g*kKeyGroup + 64*kh
+    const uint8_t* kbase = ((mrow >> 2) < NQ) ? area + ((mrow >> 2) * 4 + (mrow & 3)) * kD + 16 * kgrp
+                                              : sh_zero + 16 * kgrp;
+    // value A operand of (group g, channel group k): row h = query h's weights, at
+    // vbase + (g*4 + k)*NQ*64
+    const uint8_t* vbase = (mrow < NQ) ? area + Lds::kWtOff + mrow * 64 + 16 * kgrp : sh_zero + 16 * kgrp;
+    // this lane's weight slots: token 16t + n of the wave-iteration is token 16(t&1) + n of
+    // group t>>1; tokens 8kg..8kg+7 of a group are ordered 0,4,1,5,2,6,3,7 in their slots
+    uint8_t* wbase = area + Lds::kWtOff + qh * 64 + (n >> 3) * 16 + (((n & 3) << 1) | ((n >> 2) & 1)) * 2;
+    // even tokens meet codes read as 1 + c/16, odd ones 1 + c/4
+    const float cls_w = (n & 1) ? 4.0f : 16.0f;
+
+    v4f cv[8];                          // P.V accumulators, row h = query h
+#pragma unroll
+    for (int v = 0; v < 8; ++v) cv[v] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+    float bk[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // this lane's share (query qh) of the fp16 weight sums
+    float zk[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // ... and of sum p*zero, per channel group
+    float lsum = 0.0f, m = -INFINITY;          // query qh's running sum and max
+    float vs = 0.0f;                    // power-of-two factor keeping the value weights in fp16 range
+
+    const int n_groups = a.n_quant / kG;
+    const int g_lo = split * a.groups_per_split;
+    const int g_hi = min(n_groups, g_lo + a.groups_per_split);
+    const int cnt = max(0, g_hi - g_lo);
+    const int per_wave = (cnt + kWaves - 1) / kWaves;
+    const int gb = g_lo + min(cnt, wave * per_wave);
+    const int ge = g_lo + min(cnt, (wave + 1) * per_wave);
+    const int iters = (ge - gb + 1) >> 1;
+
+    const int64_t tok_base = kvrow * (int64_t)a.token_cap;
+    const uint8_t* kc_row = a.k_codes + tok_base * kRowBytes;
+    const uint8_t* vc_row = a.v_codes + tok_base * kRowBytes;
+    const uint32_t* kp_row = reinterpret_cast<const uint32_t*>(a.k_sz) + kvrow * (int64_t)(a.token_cap / kG) * kD;
+    const uint32_t* vp_row = reinterpret_cast<const uint32_t*>(a.v_sz) + tok_base * (kD / kG);
+
+    const uint32_t kM6 = in_vgpr(0x00C000C0u), kM8 = in_vgpr(0x03000300u), kOne = in_vgpr(0x3C003C00u);
+
+    struct Loads {
+        uint4 kp;          // (scale, zero) of key channels 4wl..4wl+3 of group gh
+        uint4 kc[2];       // key tile chunk `lane` of both groups (matrix operand B)
+        uint4 vc[2];       // value tile chunk `lane` of both groups (matrix operand B)
+        uint4 vp;          // (scale, zero) of the 4 channel groups of token tt of group gh
+    };
+    auto load_iter = [&](int it) {
+        Loads L;
+        const int g0 = gb + 2 * it;
+        const int g1 = g0 + 1 < ge ? g0 + 1 : gb;     // in-bounds address for an idle half
+        const int gc = gh ? g1 : g0;
+        L.kp = *reinterpret_cast<const uint4*>(kp_row + (int64_t)gc * kD + 4 * wl);
+        L.kc[0] = reinterpret_cast<const uint4*>(kc_row + (int64_t)g0 * kTileBytes)[lane];
+        L.kc[1] = reinterpret_cast<const uint4*>(kc_row + (int64_t)g1 * kTileBytes)[lane];
+        L.vc[0] = reinterpret_cast<const uint4*>(vc_row + (int64_t)g0 * kTileBytes)[lane];
+        L.vc[1] = reinterpret_cast<const uint4*>(vc_row + (int64_t)g1 * kTileBytes)[lane];
+        L.vp = *reinterpret_cast<const uint4*>(vp_row + value_pair_index((int64_t)gc * kG + tt, 0));
+        return L;
+    };
+
+    __syncthreads();   // the zero area is written
+    Loads cur;
+    if (iters > 0) cur = load_iter(0);
+    for (int it = 0; it < iters; ++it) {
+        const Loads nxt = load_iter(it + 1 < iters ? it + 1 : it);
+        const bool gv0 = gb + 2 * it < ge, gv1 = gb + 2 * it + 1 < ge;
+
+        // ---- q_r*s of this half's group as 30-bit fixed point (one exponent for the NQ
+        // queries), four signed byte digits per channel, stored as digit planes
+        float az[NQ], mx = 0.0f;
+        int sh;
+        {
+            const uint32_t pr[4] = {cur.kp.x, cur.kp.y, cur.kp.z, cur.kp.w};
+            float s4[4], z4[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                s4[i] = h2f(pr[i] & 0xffffu);
+                z4[i] = h2f(pr[i] >> 16);
+            }
+            float qs[NQ][4];
+#pragma unroll
+            for (int r = 0; r < NQ; ++r) {
+                az[r] = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    qs[r][i] = qw[r][i] * s4[i];
+                    az[r] = fmaf(qw[r][i], z4[i], az[r]);
+                    mx = fmaxf(mx, fabsf(qs[r][i]));
+                }
+                az[r] = half_sum(az[r]);
+            }
+            mx = half_max(mx);
+            sh = 29 - __builtin_amdgcn_frexp_expf(mx);   // |q*s| * 2^sh < 2^29
+#pragma unroll
+            for (int r = 0; r < NQ; ++r) {
+                uint32_t dg[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int qi = (int)__builtin_rintf(__builtin_ldexpf(qs[r][i] * cls_div, sh));
+                    dg[i] = ((uint32_t)qi + 0x80808080u) ^ 0x80808080u;    // four signed base-256 digits
+                }
+                const uint32_t A = __builtin_amdgcn_perm(dg[1], dg[0], 0x05010400u);
+                const uint32_t B = __builtin_amdgcn_perm(dg[1], dg[0], 0x07030602u);
+                const uint32_t C = __builtin_amdgcn_perm(dg[3], dg[2], 0x05010400u);
+                const uint32_t E = __builtin_amdgcn_perm(dg[3], dg[2], 0x07030602u);
+                uint32_t* plane = reinterpret_cast<uint32_t*>(area + gh * Lds::kKeyGroup + r * 4 * kD) + wl;
+                plane[0 * kD / 4] = __builtin_amdgcn_perm(C, A, 0x05040100u);   // digit 0 of the 4 channels
+                plane[1 * kD / 4] = __builtin_amdgcn_perm(C, A, 0x07060302u);   // digit 1
+                plane[2 * kD / 4] = __builtin_amdgcn_perm(E, B, 0x05040100u);   // digit 2
+                plane[3 * kD / 4] = __builtin_amdgcn_perm(E, B, 0x07060302u);   // digit 3
+            }
+        }
+        // value pairs of the 64 tokens, for the lanes that need another lane's token
+        *reinterpret_cast<uint4*>(area + Lds::kPairOff + lane * 16) = cur.vp;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+        // ---- key logits: tile t = 2*group + token half, K = 64 channels per instruction
+        v4i ct[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            ct[t] = (v4i){0, 0, 0, 0};
+            const uint4 kc = cur.kc[t >> 1];
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh) {
+                const uint32_t x = (t & 1) ? (kh ? kc.w : kc.z) : (kh ? kc.y : kc.x);
+                const v4i bop = {(int)(x & 0x03030303u), (int)(x & 0x0C0C0C0Cu), (int)(x & 0x30303030u),
+                                 (int)((x >> 2) & 0x30303030u)};
+                const v4i aop = *reinterpret_cast<const v4i*>(kbase + (t >> 1) * Lds::kKeyGroup + 64 * kh);
+                ct[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop, bop, ct[t], 0, 0, 0);
+            }
+        }
+        // per group: exponent and q.z of this lane's query, from the writer half of the group
+        float kscale[2], azq[2];
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            kscale[g] = __builtin_ldexpf(1.0f, -__builtin_amdgcn_readlane(sh, 32 * g));
+            float z = readlane_f(az[0], 32 * g);
+#pragma unroll
+            for (int r = 1; r < NQ; ++r) z = qh == r ? readlane_f(az[r], 32 * g) : z;
+            azq[g] = z;
+        }
+        float lg[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int hi = ct[t][3] * 256 + ct[t][2], lo = ct[t][1] * 256 + ct[t][0];
+            const float tot = fmaf((float)hi, 65536.0f, (float)lo);
+            const bool ok = qlive && ((t >> 1) ? gv1 : gv0);
+            lg[t] = ok ? fmaf(tot, kscale[t >> 1], azq[t >> 1]) : -INFINITY;
+        }
+
+        // ---- online softmax per query over the 64 tokens (rescale only when a max rises)
+        const float mnew = fmaxf(m, row_max(fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3]))));
+        const float al = mnew == m ? 1.0f : exp2f(m - mnew);
+        if (__builtin_amdgcn_ballot_w64(al < 1.0f)) {
+#pragma unroll
+            for (int r = 0; r < NQ; ++r) {
+                const float ar = readlane_f(al, 16 * r);
+#pragma unroll
+                for (int v = 0; v < 8; ++v) cv[v][r] *= ar;
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                bk[k] *= al;
+                zk[k] *= al;
+            }
+            lsum *= al;
+        }
+        m = mnew;
+        float p[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            p[t] = lg[t] == -INFINITY ? 0.0f : exp2f(lg[t] - m);
+            lsum += p[t];
+        }
+        // value pairs of this lane's 4 tokens 16t + n
+        float sv[4][4], smax = 0.0f;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const uint4 pq = *reinterpret_cast<const uint4*>(area + Lds::kPairOff + (16 * t + n) * 16);
+            const uint32_t pw[4] = {pq.x, pq.y, pq.z, pq.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                sv[t][k] = h2f(pw[k] & 0xffffu);
+                zk[k] = fmaf(p[t], h2f(pw[k] >> 16), zk[k]);
+                smax = fmaxf(smax, sv[t][k]);
+            }
+        }
+        // value weights 16*p*s*vs must stay below 2^15: shrink vs (a power of two) if needed
+        if (__builtin_amdgcn_ballot_w64(smax * vs > 2048.0f || vs == 0.0f)) {
+            const float gm = wave_max_xor(smax, 1, 32);
+            const float nvs = __builtin_ldexpf(1.0f, 11 - __builtin_amdgcn_frexp_expf(gm));
+            if (vs != 0.0f && nvs < vs) {
+                const float rs = nvs / vs;
+#pragma unroll
+                for (int v = 0; v < 8; ++v) cv[v] *= rs;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) bk[k] *= rs;
+            }
+            if (vs == 0.0f || nvs < vs) vs = nvs;
+        }
+        if (qlive) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const float f = p[t] * (cls_w * vs);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const _Float16 h = (_Float16)(f * sv[t][k]);
+                    bk[k] += (float)h;
+                    *reinterpret_cast<_Float16*>(wbase + (t >> 1) * Lds::kWtGroup + (t & 1) * 32 + k * NQ * 64) = h;
+                }
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+        // ---- P.V: K = the 32 tokens of a group, N = 16 channels, M = the NQ queries
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            const uint4 vc = cur.vc[g];
+            const uint32_t words[4] = {vc.x, vc.y, vc.z, vc.w};
+#pragma unroll
+            for (int v = 0; v < 8; ++v) {
+                const uint32_t x = words[v >> 1];
+                const uint32_t s1 = (v & 1) ? x >> 2 : x << 6, s2 = (v & 1) ? x >> 6 : x << 2;
+                const uint32_t bw[4] = {and_or(s1, kM6, kOne), and_or(s1, kM8, kOne), and_or(s2, kM6, kOne),
+                                        and_or(s2, kM8, kOne)};
+                const v8h bop = __builtin_bit_cast(v8h, make_uint4(bw[0], bw[1], bw[2], bw[3]));
+                const v8h aop = *reinterpret_cast<const v8h*>(vbase + (g * 4 + (v >> 1)) * NQ * 64);
+                cv[v] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop, cv[v], 0, 0, 0);
+            }
+        }
+        cur = nxt;
+    }
+
+    // ---- each query's quantized-part state: o = (P.V - weight sums) / vs + sum p*zero
+    lsum = row_sum(lsum);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        bk[k] = row_sum(bk[k]);
+        zk[k] = row_sum(zk[k]);
+    }
+    const float inv = vs != 0.0f ? 1.0f / vs : 0.0f;
+#pragma unroll
+    for (int r = 0; r < NQ; ++r) {
+        float br[4], zr[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            br[k] = readlane_f(bk[k], 16 * r);
+            zr[k] = readlane_f(zk[k], 16 * r);
+        }
+        if (lane < 16) {   // accumulator row r: channel 16v + lane
+#pragma unroll
+            for (int v = 0; v < 8; ++v) sh_o[r][wave][16 * v + lane] = fmaf(cv[v][r] - br[v >> 1], inv, zr[v >> 1]);
+        }
+        const float mq = readlane_f(m, 16 * r), lq = readlane_f(lsum, 16 * r);
+        if (lane == 0) {
+            sh_m[r][wave] = mq;
+            sh_l[r][wave] = lq;
+        }
+    }
+
+    // ---- fp16 residual (last split only), as separate states
+    float mr[NQ], lr[NQ];
+    if (split == a.splits - 1) {
+        residual_states<NQ>(a, qrow0, kvrow, wave, &sh_o[0][kWaves + wave][0], kSlots * kD, mr, lr);
+    } else {
+#pragma unroll
+        for (int r = 0; r < NQ; ++r) {
+            mr[r] = -INFINITY;
+            lr[r] = 0.0f;
+        }
+    }
+    if (lane == 0) {
+#pragma unroll
+        for (int r = 0; r < NQ; ++r) {
+            sh_m[r][kWaves + wave] = mr[r];
+            sh_l[r][kWaves + wave] = lr[r];
+        }
+    }
+    __syncthreads();
+    finish_block<NQ>(a, split, qrow0, grow, sh_o, sh_m, sh_l);
+}
+
+hipError_t launch_decode_attn_gqa(const AttnArgs& a, hipStream_t s) {
+    const dim3 grid((unsigned)a.splits, (unsigned)a.block_rows);
+    switch (a.nq) {
+        case 2: hipLaunchKernelGGL(attn_gqa_kernel<2>, grid, dim3(kBlock), 0, s, a); break;
+        case 3: hipLaunchKernelGGL(attn_gqa_kernel<3>, grid, dim3(kBlock), 0, s, a); break;
+        case 4: hipLaunchKernelGGL(attn_gqa_kernel<4>, grid, dim3(kBlock), 0, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace kivi

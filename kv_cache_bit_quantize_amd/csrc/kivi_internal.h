@@ -63,6 +63,8 @@ struct AttnArgs {
     int32_t n_quant, n_res, res_head;
     int32_t splits, groups_per_split;
     int64_t q_rows;             // B * Hq
+    int32_t nq;                 // query heads per workgroup: 1, or 2..4 of one KV head's group
+    int64_t block_rows;         // workgroup rows of the grid: B*Hq, or B*Hkv*(ratio/nq)
 };
 
 hipError_t launch_quantize_k(const QuantArgs& a, hipStream_t s);
@@ -70,5 +72,6 @@ hipError_t launch_quantize_v(const QuantArgs& a, hipStream_t s);
 hipError_t launch_residual_load(const ResidualArgs& a, hipStream_t s);
 hipError_t launch_append_flush(const AppendArgs& a, hipStream_t s);
 hipError_t launch_decode_attn(const AttnArgs& a, hipStream_t s);
+hipError_t launch_decode_attn_gqa(const AttnArgs& a, hipStream_t s);
 
 }  // namespace kivi

@@ -103,6 +103,26 @@ def test_gqa_ratio_four():
     _check(cache, rc, q, what="gqa")
 
 
+@pytest.mark.parametrize("q_heads,kv_heads,n_quant,n_res,splits", [
+    (4, 2, 1024, 37, 0),     # ratio 2: two queries per workgroup
+    (6, 2, 640, 128, 0),     # ratio 3
+    (16, 2, 512, 5, 3),      # ratio 8: two workgroups of 4 queries per kv head, 3 splits
+    (10, 2, 320, 64, 0),     # ratio 5: one query per workgroup
+    (12, 4, 96, 0, 1),       # ratio 3, one split (output written without the merge)
+    (8, 1, 2048, 128, 5),    # ratio 8, one kv head, full residual ring
+    (8, 2, 0, 77, 0),        # residual only
+    (4, 1, 32, 1, 2),        # one group, one residual token, more splits than needed
+])
+def test_gqa_query_groups(q_heads, kv_heads, n_quant, n_res, splits):
+    """Every query head of a group gets its own attention over the shared kv head, for the
+    query-group sizes the kernels take together and the ones they split or run alone."""
+    dev = gpu_or_skip()
+    w = synth.small(seed=q_heads * 100 + n_quant + n_res, batch=2, q_heads=q_heads, kv_heads=kv_heads,
+                    context=n_quant + n_res, n_quant=n_quant)
+    cache, rc, q = _setup(w, dev)
+    _check(cache, rc, q, splits=splits, what=f"gqa {q_heads}/{kv_heads}")
+
+
 def test_split_count_does_not_change_the_result():
     dev = gpu_or_skip()
     w = synth.small(seed=7, batch=1, q_heads=4, kv_heads=4, context=4096 + 50, n_quant=4096, outliers=0)
