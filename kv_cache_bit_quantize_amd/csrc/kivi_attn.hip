@@ -120,24 +120,36 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
         uint4 vc[2];       // value tile chunk `lane` of both groups (matrix operand B)
         uint4 vp;          // (scale, zero) of the 4 channel groups of token tt of group gh
     };
-    auto load_iter = [&](int it) {
-        Loads L;
+    // Each stream has one register set and reloads the next iteration's data right after its
+    // last use in this one, so every load still has most of an iteration to arrive.
+    auto group_of = [&](int it, int half) {
         const int g0 = gb + 2 * it;
-        const int g1 = g0 + 1 < ge ? g0 + 1 : gb;     // in-bounds address for an idle half
-        const int gc = gh ? g1 : g0;
-        L.kp = *reinterpret_cast<const uint4*>(kp_row + (int64_t)gc * kD + 4 * wl);
-        L.kc[0] = reinterpret_cast<const uint4*>(kc_row + (int64_t)g0 * kTileBytes)[lane];
-        L.kc[1] = reinterpret_cast<const uint4*>(kc_row + (int64_t)g1 * kTileBytes)[lane];
-        L.vc[0] = reinterpret_cast<const uint4*>(vc_row + (int64_t)g0 * kTileBytes)[lane];
-        L.vc[1] = reinterpret_cast<const uint4*>(vc_row + (int64_t)g1 * kTileBytes)[lane];
-        L.vp = *reinterpret_cast<const uint4*>(vp_row + value_pair_index((int64_t)gc * kG + tt, 0));
-        return L;
+        return half == 0 ? g0 : (g0 + 1 < ge ? g0 + 1 : gb);   // in-bounds address for an idle half
+    };
+    auto load_kp = [&](Loads& L, int it) {
+        L.kp = *reinterpret_cast<const uint4*>(kp_row + (int64_t)group_of(it, gh) * kD + 4 * wl);
+    };
+    auto load_kc = [&](Loads& L, int it) {
+        L.kc[0] = reinterpret_cast<const uint4*>(kc_row + (int64_t)group_of(it, 0) * kTileBytes)[lane];
+        L.kc[1] = reinterpret_cast<const uint4*>(kc_row + (int64_t)group_of(it, 1) * kTileBytes)[lane];
+    };
+    auto load_vc = [&](Loads& L, int it) {
+        L.vc[0] = reinterpret_cast<const uint4*>(vc_row + (int64_t)group_of(it, 0) * kTileBytes)[lane];
+        L.vc[1] = reinterpret_cast<const uint4*>(vc_row + (int64_t)group_of(it, 1) * kTileBytes)[lane];
+    };
+    auto load_vp = [&](Loads& L, int it) {
+        L.vp = *reinterpret_cast<const uint4*>(vp_row + value_pair_index((int64_t)group_of(it, gh) * kG + tt, 0));
     };
 
     Loads cur;
-    if (iters > 0) cur = load_iter(0);
+    if (iters > 0) {
+        load_kp(cur, 0);
+        load_kc(cur, 0);
+        load_vp(cur, 0);
+        load_vc(cur, 0);
+    }
     for (int it = 0; it < iters; ++it) {
-        const Loads nxt = load_iter(it + 1 < iters ? it + 1 : it);
+        const bool more = it + 1 < iters;
         const bool gvalid = gb + 2 * it + gh < ge;
         uint8_t* area = &sh_area[it & 1][wave][0];
 
@@ -171,6 +183,7 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
             plane[2 * kD / 4] = __builtin_amdgcn_perm(E, B, 0x05040100u);   // digit 2
             plane[3 * kD / 4] = __builtin_amdgcn_perm(E, B, 0x07060302u);   // digit 3
         }
+        if (more) load_kp(cur, it + 1);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -190,6 +203,7 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
                 cacc = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop, bop, cacc, 0, 0, 0);
             }
         }
+        if (more) load_kc(cur, it + 1);
         float lg;
         {
             const int hi = cacc[3] * 256 + cacc[2], lo = cacc[1] * 256 + cacc[0];
@@ -245,6 +259,7 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
                 *reinterpret_cast<_Float16*>(area + w_off + k * 64) = h;
             }
         }
+        if (more) load_vp(cur, it + 1);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -266,7 +281,7 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
                 cv[v] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop, cv[v], 0, 0, 0);
             }
         }
-        cur = nxt;
+        if (more) load_vc(cur, it + 1);
     }
 
     // ---- the wave's quantized-part state: o = (P.V - weight sums) / vs + sum p*zero

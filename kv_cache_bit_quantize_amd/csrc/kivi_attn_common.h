@@ -19,6 +19,7 @@ constexpr int kPart = kD + 2;        // floats per split partial: o[128], m, l
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
 
 // value of lane 4*(lane/4) + i, for CTRL = quad_perm [i, i, i, i]
 template <int CTRL>
@@ -124,6 +125,7 @@ __device__ void residual_states(const AttnArgs& a, int64_t qrow0, int64_t kvrow,
         }
         const bool first = base == wave * kG;
         for (int r = 0; r < NQ; ++r) {
+            // q.k on packed halves: each fp16 product is exact in fp32, summed in fp32
             const uint4* qp = reinterpret_cast<const uint4*>(a.q + (qrow0 + r) * kD + qq * 32);
             float d0 = 0.0f, d1 = 0.0f;
 #pragma unroll
@@ -134,13 +136,12 @@ __device__ void residual_states(const AttnArgs& a, int64_t qrow0, int64_t kvrow,
                 const uint32_t w1[4] = {kx1[i].x, kx1[i].y, kx1[i].z, kx1[i].w};
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
-                    const float qa = h2f(qh[k] & 0xffffu) * a.sm_log2, qb = h2f(qh[k] >> 16) * a.sm_log2;
-                    d0 = fmaf(qa, h2f(w0[k] & 0xffffu), d0);
-                    d0 = fmaf(qb, h2f(w0[k] >> 16), d0);
-                    d1 = fmaf(qa, h2f(w1[k] & 0xffffu), d1);
-                    d1 = fmaf(qb, h2f(w1[k] >> 16), d1);
+                    d0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2v, qh[k]), __builtin_bit_cast(h2v, w0[k]), d0, false);
+                    d1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2v, qh[k]), __builtin_bit_cast(h2v, w1[k]), d1, false);
                 }
             }
+            d0 *= a.sm_log2;
+            d1 *= a.sm_log2;
             d0 = wave_sum_xor(d0, 1, 2);
             d1 = wave_sum_xor(d1, 1, 2);
             const float l0 = ok0 ? d0 : -INFINITY, l1 = ok1 ? d1 : -INFINITY;

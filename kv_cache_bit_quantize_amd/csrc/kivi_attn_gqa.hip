@@ -113,25 +113,37 @@ __global__ __launch_bounds__(kBlock) void attn_gqa_kernel(AttnArgs a) {
         uint4 vc[2];       // value tile chunk `lane` of both groups (matrix operand B)
         uint4 vp;          // (scale, zero) of the 4 channel groups of token tt of group gh
     };
-    auto load_iter = [&](int it) {
-        Loads L;
+    // Each stream has one register set and reloads the next iteration's data right after its
+    // last use in this one, so every load still has most of an iteration to arrive.
+    auto group_of = [&](int it, int half) {
         const int g0 = gb + 2 * it;
-        const int g1 = g0 + 1 < ge ? g0 + 1 : gb;     // in-bounds address for an idle half
-        const int gc = gh ? g1 : g0;
-        L.kp = *reinterpret_cast<const uint4*>(kp_row + (int64_t)gc * kD + 4 * wl);
-        L.kc[0] = reinterpret_cast<const uint4*>(kc_row + (int64_t)g0 * kTileBytes)[lane];
-        L.kc[1] = reinterpret_cast<const uint4*>(kc_row + (int64_t)g1 * kTileBytes)[lane];
-        L.vc[0] = reinterpret_cast<const uint4*>(vc_row + (int64_t)g0 * kTileBytes)[lane];
-        L.vc[1] = reinterpret_cast<const uint4*>(vc_row + (int64_t)g1 * kTileBytes)[lane];
-        L.vp = *reinterpret_cast<const uint4*>(vp_row + value_pair_index((int64_t)gc * kG + tt, 0));
-        return L;
+        return half == 0 ? g0 : (g0 + 1 < ge ? g0 + 1 : gb);   // in-bounds address for an idle half
+    };
+    auto load_kp = [&](Loads& L, int it) {
+        L.kp = *reinterpret_cast<const uint4*>(kp_row + (int64_t)group_of(it, gh) * kD + 4 * wl);
+    };
+    auto load_kc = [&](Loads& L, int it) {
+        L.kc[0] = reinterpret_cast<const uint4*>(kc_row + (int64_t)group_of(it, 0) * kTileBytes)[lane];
+        L.kc[1] = reinterpret_cast<const uint4*>(kc_row + (int64_t)group_of(it, 1) * kTileBytes)[lane];
+    };
+    auto load_vc = [&](Loads& L, int it) {
+        L.vc[0] = reinterpret_cast<const uint4*>(vc_row + (int64_t)group_of(it, 0) * kTileBytes)[lane];
+        L.vc[1] = reinterpret_cast<const uint4*>(vc_row + (int64_t)group_of(it, 1) * kTileBytes)[lane];
+    };
+    auto load_vp = [&](Loads& L, int it) {
+        L.vp = *reinterpret_cast<const uint4*>(vp_row + value_pair_index((int64_t)group_of(it, gh) * kG + tt, 0));
     };
 
     __syncthreads();   // the zero area is written
     Loads cur;
-    if (iters > 0) cur = load_iter(0);
+    if (iters > 0) {
+        load_kp(cur, 0);
+        load_kc(cur, 0);
+        load_vp(cur, 0);
+        load_vc(cur, 0);
+    }
     for (int it = 0; it < iters; ++it) {
-        const Loads nxt = load_iter(it + 1 < iters ? it + 1 : it);
+        const bool more = it + 1 < iters;
         const bool gv0 = gb + 2 * it < ge, gv1 = gb + 2 * it + 1 < ge;
 
         // ---- q_r*s of this half's group as 30-bit fixed point (one exponent for the NQ
@@ -181,27 +193,15 @@ __global__ __launch_bounds__(kBlock) void attn_gqa_kernel(AttnArgs a) {
         }
         // value pairs of the 64 tokens, for the lanes that need another lane's token
         *reinterpret_cast<uint4*>(area + Lds::kPairOff + lane * 16) = cur.vp;
+        if (more) load_vp(cur, it + 1);
+        if (more) load_kp(cur, it + 1);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-        // ---- key logits: tile t = 2*group + token half, K = 64 channels per instruction
-        v4i ct[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            ct[t] = (v4i){0, 0, 0, 0};
-            const uint4 kc = cur.kc[t >> 1];
-#pragma unroll
-            for (int kh = 0; kh < 2; ++kh) {
-                const uint32_t x = (t & 1) ? (kh ? kc.w : kc.z) : (kh ? kc.y : kc.x);
-                const v4i bop = {(int)(x & 0x03030303u), (int)(x & 0x0C0C0C0Cu), (int)(x & 0x30303030u),
-                                 (int)((x >> 2) & 0x30303030u)};
-                const v4i aop = *reinterpret_cast<const v4i*>(kbase + (t >> 1) * Lds::kKeyGroup + 64 * kh);
-                ct[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop, bop, ct[t], 0, 0, 0);
-            }
-        }
-        // per group: exponent and q.z of this lane's query, from the writer half of the group
-        float kscale[2], azq[2];
+        // ---- key logits: tile t = 2*group + token half, K = 64 channels per instruction;
+        // each tile's digit sums are combined as soon as its two instructions are done
+        float kscale[2], azq[2];   // per group: exponent and q.z of this lane's query
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
             kscale[g] = __builtin_ldexpf(1.0f, -__builtin_amdgcn_readlane(sh, 32 * g));
@@ -213,11 +213,22 @@ __global__ __launch_bounds__(kBlock) void attn_gqa_kernel(AttnArgs a) {
         float lg[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const int hi = ct[t][3] * 256 + ct[t][2], lo = ct[t][1] * 256 + ct[t][0];
+            v4i ct = {0, 0, 0, 0};
+            const uint4 kc = cur.kc[t >> 1];
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh) {
+                const uint32_t x = (t & 1) ? (kh ? kc.w : kc.z) : (kh ? kc.y : kc.x);
+                const v4i bop = {(int)(x & 0x03030303u), (int)(x & 0x0C0C0C0Cu), (int)(x & 0x30303030u),
+                                 (int)((x >> 2) & 0x30303030u)};
+                const v4i aop = *reinterpret_cast<const v4i*>(kbase + (t >> 1) * Lds::kKeyGroup + 64 * kh);
+                ct = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop, bop, ct, 0, 0, 0);
+            }
+            const int hi = ct[3] * 256 + ct[2], lo = ct[1] * 256 + ct[0];
             const float tot = fmaf((float)hi, 65536.0f, (float)lo);
             const bool ok = qlive && ((t >> 1) ? gv1 : gv0);
             lg[t] = ok ? fmaf(tot, kscale[t >> 1], azq[t >> 1]) : -INFINITY;
         }
+        if (more) load_kc(cur, it + 1);
 
         // ---- online softmax per query over the 64 tokens (rescale only when a max rises)
         const float mnew = fmaxf(m, row_max(fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3]))));
@@ -243,17 +254,16 @@ __global__ __launch_bounds__(kBlock) void attn_gqa_kernel(AttnArgs a) {
             p[t] = lg[t] == -INFINITY ? 0.0f : exp2f(lg[t] - m);
             lsum += p[t];
         }
-        // value pairs of this lane's 4 tokens 16t + n
-        float sv[4][4], smax = 0.0f;
+        // value pairs of this lane's 4 tokens 16t + n: zero-point sums and the largest scale
+        float smax = 0.0f;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const uint4 pq = *reinterpret_cast<const uint4*>(area + Lds::kPairOff + (16 * t + n) * 16);
             const uint32_t pw[4] = {pq.x, pq.y, pq.z, pq.w};
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                sv[t][k] = h2f(pw[k] & 0xffffu);
                 zk[k] = fmaf(p[t], h2f(pw[k] >> 16), zk[k]);
-                smax = fmaxf(smax, sv[t][k]);
+                smax = fmaxf(smax, h2f(pw[k] & 0xffffu));
             }
         }
         // value weights 16*p*s*vs must stay below 2^15: shrink vs (a power of two) if needed
@@ -269,13 +279,15 @@ __global__ __launch_bounds__(kBlock) void attn_gqa_kernel(AttnArgs a) {
             }
             if (vs == 0.0f || nvs < vs) vs = nvs;
         }
-        if (qlive) {
+        if (qlive) {   // the weights, from the pairs read again
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
+                const uint4 pq = *reinterpret_cast<const uint4*>(area + Lds::kPairOff + (16 * t + n) * 16);
+                const uint32_t pw[4] = {pq.x, pq.y, pq.z, pq.w};
                 const float f = p[t] * (cls_w * vs);
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
-                    const _Float16 h = (_Float16)(f * sv[t][k]);
+                    const _Float16 h = (_Float16)(f * h2f(pw[k] & 0xffffu));
                     bk[k] += (float)h;
                     *reinterpret_cast<_Float16*>(wbase + (t >> 1) * Lds::kWtGroup + (t & 1) * 32 + k * NQ * 64) = h;
                 }
@@ -301,7 +313,7 @@ __global__ __launch_bounds__(kBlock) void attn_gqa_kernel(AttnArgs a) {
                 cv[v] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop, cv[v], 0, 0, 0);
             }
         }
-        cur = nxt;
+        if (more) load_vc(cur, it + 1);
     }
 
     // ---- each query's quantized-part state: o = (P.V - weight sums) / vs + sum p*zero
@@ -331,7 +343,9 @@ __global__ __launch_bounds__(kBlock) void attn_gqa_kernel(AttnArgs a) {
         }
     }
 
-    // ---- fp16 residual (last split only), as separate states
+    // ---- fp16 residual (last split only), as separate states.  The scheduling barrier keeps
+    // its loads from being hoisted above this point, where the accumulators are still live.
+    __builtin_amdgcn_sched_barrier(0);
     float mr[NQ], lr[NQ];
     if (split == a.splits - 1) {
         residual_states<NQ>(a, qrow0, kvrow, wave, &sh_o[0][kWaves + wave][0], kSlots * kD, mr, lr);
