@@ -10,7 +10,6 @@ resident in HBM when the timed region starts.
 Prints ONE JSON line.  Metric: achieved HBM GB/s (algorithmic bytes / time) and tokens/s.
 """
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -27,17 +26,8 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 D, G = 128, 32
 QUANT_TOKEN_BYTES = 96         # per kv head: 32 B key codes + 16 B key pairs + 32 B value codes + 16 B value pairs
 RES_TOKEN_BYTES = 512          # per kv head: fp16 key + value
-KERNEL = "attn_split_kernel"
-KERNEL_SOURCES = ["kv_cache_bit_quantize_amd/csrc/kivi_attn.hip", "kv_cache_bit_quantize_amd/csrc/kivi_device.h"]
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_attn_long-128k_counters.json")
-
-
-def kernel_source_hash():
-    h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+def counters_file(workload):
+    return os.path.join(ROOT, "profiles", f"decode_attn_{workload}_counters.json")
 
 
 def attn_bytes(w, n_quant, n_res):
@@ -57,48 +47,64 @@ def append_bytes(w, flushed):
     return b
 
 
-def cpu_baseline(w, k, v, n_heads, steps_tokens):
-    """Time the CPU oracle (as it stands, one thread) on a bounded sample: the first
-    n_heads kv heads of batch row 0, one decode step (append + attention)."""
+def cpu_baseline(w, k, v, n_heads, steps_tokens, threads):
+    """Time the CPU oracle (as it stands) on a bounded sample: the first n_heads kv heads of
+    batch row 0, one decode step (append + attention), the heads split over `threads` host
+    threads that each drive their own oracle cache (the oracle's C code releases the GIL)."""
+    import concurrent.futures
     from oracle import ref
     from kv_cache_bit_quantize_amd import synth
 
     def host_bits(t):
         return t.contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
 
-    rc = ref.RefCache(1, n_heads, D, G, w.residual_cap, token_cap=w.token_cap)
-    t0 = time.perf_counter()
-    rc.prefill(host_bits(k[0, :n_heads]), host_bits(v[0, :n_heads]), w.n_quant)
-    prefill_s = time.perf_counter() - t0
+    threads = max(1, min(threads, n_heads))
+    bounds = [(i * n_heads // threads, (i + 1) * n_heads // threads) for i in range(threads)]
+    kh, vh = host_bits(k[0, :n_heads]), host_bits(v[0, :n_heads])
     kn, vn = steps_tokens
-    q = host_bits(synth.query(w, step=1)[:1, :n_heads])
-    t0 = time.perf_counter()
-    flushed = rc.append(host_bits(kn[0, :n_heads]), host_bits(vn[0, :n_heads]))
-    rc.decode_attn(q, synth.SM_SCALE_D128)
-    step_s = time.perf_counter() - t0
-    nbytes = n_heads * (rc.n_quant * QUANT_TOKEN_BYTES + rc.n_res * RES_TOKEN_BYTES) + 2 * n_heads * D * 2 \
+    knh, vnh = host_bits(kn[0, :n_heads]), host_bits(vn[0, :n_heads])
+    qh = host_bits(synth.query(w, step=1)[:1, :n_heads])
+    caches = [ref.RefCache(1, b1 - b0, D, G, w.residual_cap, token_cap=w.token_cap) for b0, b1 in bounds]
+    with concurrent.futures.ThreadPoolExecutor(threads) as ex:
+        t0 = time.perf_counter()
+        list(ex.map(lambda i: caches[i].prefill(kh[bounds[i][0]:bounds[i][1]], vh[bounds[i][0]:bounds[i][1]],
+                                                w.n_quant), range(threads)))
+        prefill_s = time.perf_counter() - t0
+
+        def step(i):
+            b0, b1 = bounds[i]
+            f = caches[i].append(knh[b0:b1], vnh[b0:b1])
+            caches[i].decode_attn(qh[:, b0:b1], synth.SM_SCALE_D128)
+            return f
+        t0 = time.perf_counter()
+        flushed = list(ex.map(step, range(threads)))[0]
+        step_s = time.perf_counter() - t0
+    nq, nr = caches[0].n_quant, caches[0].n_res
+    nbytes = n_heads * (nq * QUANT_TOKEN_BYTES + nr * RES_TOKEN_BYTES) + 2 * n_heads * D * 2 \
         + n_heads * 4 * D * 2 + (n_heads * G * (RES_TOKEN_BYTES + QUANT_TOKEN_BYTES) if flushed else 0)
     return {
         "value": nbytes / step_s / 1e9,
         "unit": "GB/s",
-        "cores": 1,
+        "cores": threads,
         "kind": "oracle",
         "sample": f"one decode step (append + fp64 attention over the dequantized cache) of {n_heads} of the "
-                  f"{w.batch * w.kv_heads} kv heads of the {w.name} workload, single thread; "
+                  f"{w.batch * w.kv_heads} kv heads of the {w.name} workload on {threads} host threads; "
                   f"{step_s:.2f} s timed (oracle prefill of the sample {prefill_s:.1f} s, untimed)",
         "tokens_per_s": (n_heads / (w.batch * w.kv_heads)) * w.batch / step_s,
         "seconds": step_s,
     }
 
 
-def read_traffic(attn_b):
+def read_traffic(workload):
     """HBM bytes per launch from committed rocprofv3 counters, if they were taken on the
-    current kernel source; else None."""
-    if not os.path.exists(COUNTERS_FILE):
+    current kernel sources; else None."""
+    from kv_cache_bit_quantize_amd import traffic
+    path = counters_file(workload)
+    if not os.path.exists(path):
         return None
-    with open(COUNTERS_FILE) as f:
+    with open(path) as f:
         c = json.load(f)
-    if c.get("kernel_source_hash") != kernel_source_hash():
+    if c.get("kernel_source_hash") != traffic.kernel_source_hash():
         return None
     return c.get("hbm_bytes_per_launch")
 
@@ -109,7 +115,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="long-128k")
-    ap.add_argument("--cpu-heads", type=int, default=12, help="kv heads in the CPU oracle sample (0: skip)")
+    ap.add_argument("--cpu-heads", type=int, default=32, help="kv heads in the CPU oracle sample (0: skip)")
+    ap.add_argument("--cpu-threads", type=int, default=16, help="host threads for the CPU oracle sample")
     ap.add_argument("--splits", type=int, default=0, help="split count override (0: library's choice)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -196,19 +203,20 @@ def main():
         "append_flush_us": round(float(app_ms.mean()) * 1e3, 2),
         "roofline": {
             "bound": "hbm",
-            "kernel": KERNEL,
+            "kernel": "attn_split_kernel" if w.q_heads == w.kv_heads else "attn_gqa_kernel",
             "achieved": round(achieved, 1),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": read_traffic(float(np.mean(attn_b))),
+            "traffic": read_traffic(w.name),
             "algorithmic_bytes_per_launch": int(np.mean(attn_b)),
         },
         "cpu_baseline": None,
     }
     if args.cpu_heads > 0:
         kn, vn = steps_kv[0]
-        res["cpu_baseline"] = cpu_baseline(w, k, v, min(args.cpu_heads, w.kv_heads), (kn, vn))
+        res["cpu_baseline"] = cpu_baseline(w, k, v, min(args.cpu_heads, w.kv_heads), (kn, vn),
+                                           min(args.cpu_threads, os.cpu_count() or 1))
     print(json.dumps(res), flush=True)
 
 
