@@ -1,11 +1,12 @@
 """Decode benchmark of the 2-bit KIVI cache on one MI355X.
 
-One step = one decode step of the whole hot path: kivi_append_flush (the new token enters
-the fp16 residual; whenever the residual is already full, the oldest 32 residual tokens
-are first quantized into a new key/value group) followed by kivi_decode_attn (fused attention
-of one query per head over the packed history plus the residual, split-K with the
-log-sum-exp merge in the same launch).  Inputs are seeded synthetic tensors already
-resident in HBM when the timed region starts.
+One step = one decode step of the whole hot path, kivi_decode_step: the new token enters
+the fp16 residual (whenever the residual is already full, the oldest 32 residual tokens
+are first quantized into a new key/value group) and fused attention of one query per head
+runs over the packed history plus the residual, split-K with the log-sum-exp merge in the
+same launch.  A step is one kernel launch, or two when a group is flushed; --separate
+times the two separate calls kivi_append_flush + kivi_decode_attn instead.  Inputs are
+seeded synthetic tensors already resident in HBM when the timed region starts.
 
 Prints ONE JSON line.  Metric: achieved HBM GB/s (algorithmic bytes / time) and tokens/s.
 """
@@ -26,6 +27,7 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 D, G = 128, 32
 QUANT_TOKEN_BYTES = 96         # per kv head: 32 B key codes + 16 B key pairs + 32 B value codes + 16 B value pairs
 RES_TOKEN_BYTES = 512          # per kv head: fp16 key + value
+EVENT_EVERY = 3                # steps bracketed by HIP events: 0, 3, 6, ...
 def counters_file(workload):
     return os.path.join(ROOT, "profiles", f"decode_attn_{workload}_counters.json")
 
@@ -118,6 +120,7 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=32, help="kv heads in the CPU oracle sample (0: skip)")
     ap.add_argument("--cpu-threads", type=int, default=16, help="host threads for the CPU oracle sample")
     ap.add_argument("--splits", type=int, default=0, help="split count override (0: library's choice)")
+    ap.add_argument("--separate", action="store_true", help="time kivi_append_flush + kivi_decode_attn")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the decode hot path shards "
@@ -146,38 +149,49 @@ def main():
     def step(s, ev=None):
         if ev is not None:
             ev[0].record()
-        f = kivi.kivi_append_flush(cache, *steps_kv[s])
-        if ev is not None:
-            ev[1].record()
-        state = cache.state
-        kivi.kivi_decode_attn(cache, queries[s], synth.SM_SCALE_D128, out=out, num_splits=args.splits,
-                              workspace=ws)
+        if args.separate:
+            f = kivi.kivi_append_flush(cache, *steps_kv[s])
+            if ev is not None:
+                ev[1].record()
+            kivi.kivi_decode_attn(cache, queries[s], synth.SM_SCALE_D128, out=out, num_splits=args.splits,
+                                  workspace=ws)
+        else:
+            if ev is not None:
+                ev[1].record()
+            _, f = kivi.kivi_decode_step(cache, *steps_kv[s], queries[s], synth.SM_SCALE_D128, out=out,
+                                         num_splits=args.splits, workspace=ws)
         if ev is not None:
             ev[2].record()
-        return f, state
+        return f, cache.state
 
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # Every EVENT_EVERY-th step is bracketed by HIP events on the launch stream (each marker
+    # costs the stream a few microseconds, so the other steps carry none); the attention
+    # launch duration is [ev1, ev2] of those steps: the attention call, or with the fused
+    # step on a step without flush its one launch.
+    timed = set(range(0, args.steps, EVENT_EVERY))
+    evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for i in timed}
     flags, states = [], []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        f, st = step(args.warmup + i, evs[i])
+        f, st = step(args.warmup + i, evs.get(i))
         flags.append(f)
         states.append(st)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    attn_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
-    app_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    one_launch = [i for i in sorted(timed) if args.separate or not flags[i]]
+    attn_ms = np.array([evs[i][1].elapsed_time(evs[i][2]) for i in one_launch])
     step_bytes = [attn_bytes(w, nq, nr) + append_bytes(w, f) for f, (nq, nr, _) in zip(flags, states)]
-    attn_b = [attn_bytes(w, nq, nr) for nq, nr, _ in states]
     value = sum(step_bytes) / elapsed / 1e9
-    achieved = float(np.mean(attn_b)) / (attn_ms.mean() / 1e3) / 1e9
+    launch_b = [attn_bytes(w, *states[i][:2]) + (0 if args.separate else append_bytes(w, False)) for i in one_launch]
+    achieved = float(np.mean(launch_b)) / (attn_ms.mean() / 1e3) / 1e9
     splits = kivi.kivi_decode_attn_splits(cache, w.q_heads) if args.splits == 0 else args.splits
+    kernel = "attn_split_kernel" if w.q_heads == w.kv_heads else "attn_gqa_kernel"
 
     res = {
         "metric": METRIC,
@@ -199,17 +213,19 @@ def main():
         },
         "pct_of_peak_hbm": round(100 * value / PEAK_HBM_GBS, 2),
         "tokens_per_s": round(w.batch * args.steps / elapsed, 1),
+        "step_path": "separate append_flush + decode_attn" if args.separate else "fused decode_step",
         "decode_attn_us": round(float(attn_ms.mean()) * 1e3, 2),
-        "append_flush_us": round(float(app_ms.mean()) * 1e3, 2),
+        "event_timed_launches": len(one_launch),
+        "flush_steps": int(sum(bool(f) for f in flags)),
         "roofline": {
             "bound": "hbm",
-            "kernel": "attn_split_kernel" if w.q_heads == w.kv_heads else "attn_gqa_kernel",
+            "kernel": kernel if args.separate else kernel + " (append fused)",
             "achieved": round(achieved, 1),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": read_traffic(w.name),
-            "algorithmic_bytes_per_launch": int(np.mean(attn_b)),
+            "algorithmic_bytes_per_launch": int(np.mean(launch_b)),
         },
         "cpu_baseline": None,
     }

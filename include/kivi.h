@@ -142,6 +142,19 @@ int kivi_decode_attn(const kivi_cache* cache, const uint16_t* q, int32_t q_heads
                      float sm_scale, uint16_t* out, float* lse, void* workspace,
                      size_t workspace_bytes, int32_t num_splits, void* stream);
 
+/* One whole decode step: kivi_append_flush(cache, k_new, v_new, flushed, stream) followed by
+ * kivi_decode_attn(cache, q, ...) on the updated cache, with the same arguments, results,
+ * state update and errors as those two calls (record "KV bytes basis": the newest R tokens
+ * in 16-bit floats; decoding attends over the history and the residual, the new token
+ * included).  When the ring has room it is one kernel launch: attention reads the new
+ * token straight from k_new / v_new while one workgroup per KV head writes it into its
+ * ring slot; when a group must be flushed first it is the two launches of the separate
+ * calls.  Validation happens before anything is enqueued, so on error nothing changes. */
+int kivi_decode_step(kivi_cache* cache, const uint16_t* k_new, const uint16_t* v_new,
+                     const uint16_t* q, int32_t q_heads, float sm_scale, uint16_t* out, float* lse,
+                     void* workspace, size_t workspace_bytes, int32_t num_splits, int32_t* flushed,
+                     void* stream);
+
 /* Host-only helpers (no device access; safe without a GPU). */
 
 /* Split count that kivi_decode_attn uses for num_splits == 0 (depends on shapes only).

@@ -104,6 +104,109 @@ QuantArgs quant_args(const kivi_cache* c, const uint16_t* src, int32_t tokens, i
     return a;
 }
 
+// Validates an append and fills its arguments; *next receives the state after it.
+int prepare_append(const kivi_cache* c, const uint16_t* k_new, const uint16_t* v_new, AppendArgs* a,
+                   kivi_cache* next) {
+    int st = check_shape(c);
+    if (st != KIVI_OK) return st;
+    if ((st = check_state(c)) != KIVI_OK) return st;
+    if ((st = check_quant_bufs(c, true, true)) != KIVI_OK) return st;
+    if ((st = check_res_bufs(c)) != KIVI_OK) return st;
+    if (k_new == nullptr || v_new == nullptr) return KIVI_ERR_NULL;
+    if (!aligned16(k_new) || !aligned16(v_new)) return KIVI_ERR_SHAPE;
+    const int G = c->group, R = c->residual_cap;
+    const bool flush = c->n_res == R;
+    if (flush && c->n_quant + G > c->token_cap) return KIVI_ERR_CAPACITY;
+    int n_quant = c->n_quant, n_res = c->n_res, head = c->res_head;
+    a->k_new = k_new;
+    a->v_new = v_new;
+    a->rows = rows_of(c);
+    a->do_flush = flush ? 1 : 0;
+    a->flush_slot = head;
+    a->flush_group = n_quant / G;
+    if (flush) {
+        n_quant += G;
+        head = (head + G) % R;
+        n_res -= G;
+    }
+    a->new_slot = (head + n_res) % R;
+    a->token_cap = c->token_cap;
+    a->residual_cap = R;
+    a->k_codes = c->k_codes;
+    a->v_codes = c->v_codes;
+    a->k_sz = c->k_sz;
+    a->v_sz = c->v_sz;
+    a->k_res = c->k_res;
+    a->v_res = c->v_res;
+    *next = *c;
+    next->n_quant = n_quant;
+    next->n_res = n_res + 1;
+    next->res_head = head;
+    return KIVI_OK;
+}
+
+void commit_state(kivi_cache* c, const kivi_cache& next) {
+    c->n_quant = next.n_quant;
+    c->n_res = next.n_res;
+    c->res_head = next.res_head;
+}
+
+// Validates a decode-attention call on cache state *c and fills its arguments.
+int prepare_attn(const kivi_cache* c, const uint16_t* q, int32_t q_heads, float sm_scale, uint16_t* out,
+                 float* lse, void* workspace, size_t workspace_bytes, int32_t num_splits, AttnArgs* pa) {
+    int st = check_shape(c);
+    if (st != KIVI_OK) return st;
+    if ((st = check_state(c)) != KIVI_OK) return st;
+    if ((st = check_quant_bufs(c, true, true)) != KIVI_OK) return st;
+    if ((st = check_res_bufs(c)) != KIVI_OK) return st;
+    if (q == nullptr || out == nullptr) return KIVI_ERR_NULL;
+    if (!aligned16(q) || (reinterpret_cast<uintptr_t>(out) & 1u) || (reinterpret_cast<uintptr_t>(lse) & 3u))
+        return KIVI_ERR_SHAPE;
+    if (q_heads <= 0 || q_heads % c->kv_heads != 0) return KIVI_ERR_SHAPE;
+    if (c->n_quant + c->n_res == 0) return KIVI_ERR_SHAPE;
+    if (num_splits < 0 || num_splits > kMaxSplits) return KIVI_ERR_SHAPE;
+    if (!std::isfinite(sm_scale)) return KIVI_ERR_SHAPE;
+    const int32_t splits = num_splits > 0 ? num_splits : auto_splits(c, q_heads);
+    const size_t need = kivi_decode_attn_workspace(c, q_heads, splits);
+    if (workspace == nullptr || workspace_bytes < need) return KIVI_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return KIVI_ERR_WORKSPACE;
+    const int32_t groups = c->n_quant / c->group;
+    AttnArgs a{};
+    a.q = q;
+    a.k_codes = c->k_codes;
+    a.v_codes = c->v_codes;
+    a.k_sz = c->k_sz;
+    a.v_sz = c->v_sz;
+    a.k_res = c->k_res;
+    a.v_res = c->v_res;
+    a.counters = static_cast<uint32_t*>(workspace);
+    a.ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + counter_bytes(c, q_heads));
+    a.out = out;
+    a.lse = lse;
+    a.sm_log2 = (float)((double)sm_scale * 1.4426950408889634);
+    a.q_heads = q_heads;
+    a.kv_heads = c->kv_heads;
+    a.ratio = q_heads / c->kv_heads;
+    a.token_cap = c->token_cap;
+    a.residual_cap = c->residual_cap;
+    a.n_quant = c->n_quant;
+    a.n_res = c->n_res;
+    a.res_head = c->res_head;
+    a.splits = splits;
+    // The last split also reads the fp16 residual (512 bytes per token against 96 for a
+    // quantized token): count it as that many groups so the last split gets fewer.
+    const int32_t res_groups = (c->n_res * 512 + 96 * c->group - 1) / (96 * c->group);
+    a.groups_per_split = (groups + res_groups + splits - 1) / splits;
+    a.q_rows = (int64_t)c->batch * q_heads;
+    a.nq = queries_per_block(a.ratio);
+    a.block_rows = block_rows(c, q_heads);
+    a.k_new = a.v_new = nullptr;
+    a.k_ring = a.v_ring = nullptr;
+    a.new_slot = 0;
+    *pa = a;
+    return KIVI_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -207,43 +310,13 @@ int kivi_prefill(const uint16_t* k, const uint16_t* v, int32_t tokens, int64_t s
 
 int kivi_append_flush(kivi_cache* c, const uint16_t* k_new, const uint16_t* v_new, int32_t* flushed,
                       void* stream) {
-    int st = check_shape(c);
-    if (st != KIVI_OK) return st;
-    if ((st = check_state(c)) != KIVI_OK) return st;
-    if ((st = check_quant_bufs(c, true, true)) != KIVI_OK) return st;
-    if ((st = check_res_bufs(c)) != KIVI_OK) return st;
-    if (k_new == nullptr || v_new == nullptr) return KIVI_ERR_NULL;
-    if (!aligned16(k_new) || !aligned16(v_new)) return KIVI_ERR_SHAPE;
-    const int G = c->group, R = c->residual_cap;
-    const bool flush = c->n_res == R;
-    if (flush && c->n_quant + G > c->token_cap) return KIVI_ERR_CAPACITY;
-    int n_quant = c->n_quant, n_res = c->n_res, head = c->res_head;
     AppendArgs a;
-    a.k_new = k_new;
-    a.v_new = v_new;
-    a.rows = rows_of(c);
-    a.do_flush = flush ? 1 : 0;
-    a.flush_slot = head;
-    a.flush_group = n_quant / G;
-    if (flush) {
-        n_quant += G;
-        head = (head + G) % R;
-        n_res -= G;
-    }
-    a.new_slot = (head + n_res) % R;
-    a.token_cap = c->token_cap;
-    a.residual_cap = R;
-    a.k_codes = c->k_codes;
-    a.v_codes = c->v_codes;
-    a.k_sz = c->k_sz;
-    a.v_sz = c->v_sz;
-    a.k_res = c->k_res;
-    a.v_res = c->v_res;
+    kivi_cache next;
+    int st = prepare_append(c, k_new, v_new, &a, &next);
+    if (st != KIVI_OK) return st;
     if ((st = hip_status(launch_append_flush(a, (hipStream_t)stream))) != KIVI_OK) return st;
-    c->n_quant = n_quant;
-    c->n_res = n_res + 1;
-    c->res_head = head;
-    if (flushed != nullptr) *flushed = flush ? 1 : 0;
+    commit_state(c, next);
+    if (flushed != nullptr) *flushed = a.do_flush;
     return KIVI_OK;
 }
 
@@ -264,53 +337,37 @@ size_t kivi_decode_attn_workspace(const kivi_cache* c, int32_t q_heads, int32_t 
 
 int kivi_decode_attn(const kivi_cache* c, const uint16_t* q, int32_t q_heads, float sm_scale, uint16_t* out,
                      float* lse, void* workspace, size_t workspace_bytes, int32_t num_splits, void* stream) {
-    int st = check_shape(c);
-    if (st != KIVI_OK) return st;
-    if ((st = check_state(c)) != KIVI_OK) return st;
-    if ((st = check_quant_bufs(c, true, true)) != KIVI_OK) return st;
-    if ((st = check_res_bufs(c)) != KIVI_OK) return st;
-    if (q == nullptr || out == nullptr) return KIVI_ERR_NULL;
-    if (!aligned16(q) || (reinterpret_cast<uintptr_t>(out) & 1u) || (reinterpret_cast<uintptr_t>(lse) & 3u))
-        return KIVI_ERR_SHAPE;
-    if (q_heads <= 0 || q_heads % c->kv_heads != 0) return KIVI_ERR_SHAPE;
-    if (c->n_quant + c->n_res == 0) return KIVI_ERR_SHAPE;
-    if (num_splits < 0 || num_splits > kMaxSplits) return KIVI_ERR_SHAPE;
-    if (!std::isfinite(sm_scale)) return KIVI_ERR_SHAPE;
-    const int32_t splits = num_splits > 0 ? num_splits : auto_splits(c, q_heads);
-    const size_t need = kivi_decode_attn_workspace(c, q_heads, splits);
-    if (workspace == nullptr || workspace_bytes < need) return KIVI_ERR_WORKSPACE;
-    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return KIVI_ERR_WORKSPACE;
-    const int32_t groups = c->n_quant / c->group;
     AttnArgs a;
-    a.q = q;
-    a.k_codes = c->k_codes;
-    a.v_codes = c->v_codes;
-    a.k_sz = c->k_sz;
-    a.v_sz = c->v_sz;
-    a.k_res = c->k_res;
-    a.v_res = c->v_res;
-    a.counters = static_cast<uint32_t*>(workspace);
-    a.ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + counter_bytes(c, q_heads));
-    a.out = out;
-    a.lse = lse;
-    a.sm_log2 = (float)((double)sm_scale * 1.4426950408889634);
-    a.q_heads = q_heads;
-    a.kv_heads = c->kv_heads;
-    a.ratio = q_heads / c->kv_heads;
-    a.token_cap = c->token_cap;
-    a.residual_cap = c->residual_cap;
-    a.n_quant = c->n_quant;
-    a.n_res = c->n_res;
-    a.res_head = c->res_head;
-    a.splits = splits;
-    // The last split also reads the fp16 residual (512 bytes per token against 96 for a
-    // quantized token): count it as that many groups so the last split gets fewer.
-    const int32_t res_groups = (c->n_res * 512 + 96 * c->group - 1) / (96 * c->group);
-    a.groups_per_split = (groups + res_groups + splits - 1) / splits;
-    a.q_rows = (int64_t)c->batch * q_heads;
-    a.nq = queries_per_block(a.ratio);
-    a.block_rows = block_rows(c, q_heads);
+    const int st = prepare_attn(c, q, q_heads, sm_scale, out, lse, workspace, workspace_bytes, num_splits, &a);
+    if (st != KIVI_OK) return st;
     return hip_status(launch_decode_attn(a, (hipStream_t)stream));
+}
+
+int kivi_decode_step(kivi_cache* c, const uint16_t* k_new, const uint16_t* v_new, const uint16_t* q,
+                     int32_t q_heads, float sm_scale, uint16_t* out, float* lse, void* workspace,
+                     size_t workspace_bytes, int32_t num_splits, int32_t* flushed, void* stream) {
+    AppendArgs ap;
+    kivi_cache next;
+    int st = prepare_append(c, k_new, v_new, &ap, &next);
+    if (st != KIVI_OK) return st;
+    AttnArgs at;   // attention on the state after the append
+    st = prepare_attn(&next, q, q_heads, sm_scale, out, lse, workspace, workspace_bytes, num_splits, &at);
+    if (st != KIVI_OK) return st;
+    if (ap.do_flush) {
+        if ((st = hip_status(launch_append_flush(ap, (hipStream_t)stream))) != KIVI_OK) return st;
+    } else {
+        // the new token is residual token next.n_res - 1: attention reads it from k_new /
+        // v_new and one workgroup per KV row stores it into its ring slot
+        at.k_new = k_new;
+        at.v_new = v_new;
+        at.k_ring = c->k_res;
+        at.v_ring = c->v_res;
+        at.new_slot = ap.new_slot;
+    }
+    if ((st = hip_status(launch_decode_attn(at, (hipStream_t)stream))) != KIVI_OK) return st;
+    commit_state(c, next);
+    if (flushed != nullptr) *flushed = ap.do_flush;
+    return KIVI_OK;
 }
 
 }  // extern "C"

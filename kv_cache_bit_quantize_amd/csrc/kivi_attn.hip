@@ -52,6 +52,7 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
     const int64_t b = qrow / a.q_heads;
     const int hq = (int)(qrow % a.q_heads);
     const int64_t kvrow = b * a.kv_heads + hq / a.ratio;
+    if (a.k_new != nullptr && split == 0 && hq % a.ratio == 0) store_new_token(a, kvrow);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int gh = lane >> 5;          // group of the wave-iteration this lane serves
     const int tt = lane & 31;          // token role: token tt of group gh

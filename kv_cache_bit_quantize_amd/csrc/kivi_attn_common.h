@@ -111,10 +111,14 @@ __device__ void residual_states(const AttnArgs& a, int64_t qrow0, int64_t kvrow,
         const int s1 = (a.res_head + (ok1 ? i1 : 0)) % a.residual_cap;
         const int64_t r0 = (kvrow * a.residual_cap + s0) * kD + qq * 32;
         const int64_t r1 = (kvrow * a.residual_cap + s1) * kD + qq * 32;
-        const uint4* k0 = reinterpret_cast<const uint4*>(a.k_res + r0);
-        const uint4* k1 = reinterpret_cast<const uint4*>(a.k_res + r1);
-        const uint4* v0 = reinterpret_cast<const uint4*>(a.v_res + r0);
-        const uint4* v1 = reinterpret_cast<const uint4*>(a.v_res + r1);
+        // in a fused decode step the last residual token is the new one, still in k_new / v_new
+        const bool new0 = a.k_new != nullptr && (ok0 ? i0 : 0) == a.n_res - 1;
+        const bool new1 = a.k_new != nullptr && (ok1 ? i1 : 0) == a.n_res - 1;
+        const int64_t rn = kvrow * kD + qq * 32;
+        const uint4* k0 = reinterpret_cast<const uint4*>(new0 ? a.k_new + rn : a.k_res + r0);
+        const uint4* k1 = reinterpret_cast<const uint4*>(new1 ? a.k_new + rn : a.k_res + r1);
+        const uint4* v0 = reinterpret_cast<const uint4*>(new0 ? a.v_new + rn : a.v_res + r0);
+        const uint4* v1 = reinterpret_cast<const uint4*>(new1 ? a.v_new + rn : a.v_res + r1);
         uint4 kx0[4], kx1[4], vx0[4], vx1[4];   // keys and values in one round of loads
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -170,6 +174,18 @@ __device__ void residual_states(const AttnArgs& a, int64_t qrow0, int64_t kvrow,
                 }
             }
         }
+    }
+}
+
+// Fused decode step: threads 0..31 of the calling workgroup store the new token (k_new /
+// v_new of KV row kvrow) into its ring slot.  Exactly one workgroup per KV row calls it;
+// no workgroup of the launch reads that slot (attention takes the token from k_new / v_new).
+__device__ __forceinline__ void store_new_token(const AttnArgs& a, int64_t kvrow) {
+    if (threadIdx.x < 32) {
+        const int c = threadIdx.x & 15;
+        const uint16_t* src = (threadIdx.x < 16 ? a.k_new : a.v_new) + kvrow * kD;
+        uint16_t* dst = (threadIdx.x < 16 ? a.k_ring : a.v_ring) + (kvrow * a.residual_cap + a.new_slot) * kD;
+        reinterpret_cast<uint4*>(dst)[c] = reinterpret_cast<const uint4*>(src)[c];
     }
 }
 

@@ -45,6 +45,7 @@ __global__ __launch_bounds__(kBlock) void attn_gqa_kernel(AttnArgs a) {
     const int64_t kvrow = grow / chunks;
     const int chunk = (int)(grow % chunks);
     const int64_t qrow0 = (kvrow / a.kv_heads) * a.q_heads + (kvrow % a.kv_heads) * a.ratio + chunk * NQ;
+    if (a.k_new != nullptr && split == 0 && chunk == 0) store_new_token(a, kvrow);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int gh = lane >> 5, tt = lane & 31;        // token role (loads): token tt of group gh
     const int wl = lane & 31, wk = wl & 3;           // fixed-point writer role: channels 4wl..4wl+3

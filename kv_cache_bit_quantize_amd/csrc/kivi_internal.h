@@ -65,6 +65,14 @@ struct AttnArgs {
     int64_t q_rows;             // B * Hq
     int32_t nq;                 // query heads per workgroup: 1, or 2..4 of one KV head's group
     int64_t block_rows;         // workgroup rows of the grid: B*Hq, or B*Hkv*(ratio/nq)
+    // fused append (decode step): when k_new is set, residual token n_res - 1 is the new
+    // token, read from k_new / v_new ([row][D]); one workgroup per KV row also writes it into
+    // ring slot new_slot
+    const uint16_t* k_new;
+    const uint16_t* v_new;
+    uint16_t* k_ring;           // k_res / v_res, written (the attention reads them as const)
+    uint16_t* v_ring;
+    int32_t new_slot;
 };
 
 hipError_t launch_quantize_k(const QuantArgs& a, hipStream_t s);

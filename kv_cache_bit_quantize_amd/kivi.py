@@ -17,7 +17,7 @@ _STATUS_NAMES = {0: "KIVI_OK", -1: "KIVI_ERR_NULL", -2: "KIVI_ERR_SHAPE", -3: "K
                  -4: "KIVI_ERR_CAPACITY", -5: "KIVI_ERR_WORKSPACE", -6: "KIVI_ERR_HIP", -7: "KIVI_ERR_STATE"}
 
 EXPORTS = ["kivi_quantize_k_per_channel", "kivi_quantize_v_per_token", "kivi_prefill", "kivi_append_flush",
-           "kivi_decode_attn", "kivi_decode_attn_splits", "kivi_decode_attn_workspace", "kivi_cache_bytes",
+           "kivi_decode_attn", "kivi_decode_step", "kivi_decode_attn_splits", "kivi_decode_attn_workspace", "kivi_cache_bytes",
            "kivi_status_str"]
 
 
@@ -47,6 +47,7 @@ def _load():
     L.kivi_prefill.argtypes = [p, p, i32, i64, i32, cp, p]
     L.kivi_append_flush.argtypes = [cp, p, p, C.POINTER(i32), p]
     L.kivi_decode_attn.argtypes = [cp, p, i32, C.c_float, p, p, p, C.c_size_t, i32, p]
+    L.kivi_decode_step.argtypes = [cp, p, p, p, i32, C.c_float, p, p, p, C.c_size_t, i32, C.POINTER(i32), p]
     L.kivi_decode_attn_splits.argtypes = [cp, i32]
     L.kivi_decode_attn_splits.restype = i32
     L.kivi_decode_attn_workspace.argtypes = [cp, i32, i32]
@@ -169,6 +170,28 @@ def kivi_decode_attn(cache, q, sm_scale, out=None, lse=None, num_splits=0, works
                                 _ptr(lse) if want_lse else None, _ptr(ws), ws.numel() * ws.element_size(),
                                 num_splits, _stream(q)), "kivi_decode_attn")
     return (out, lse) if want_lse else out
+
+
+def kivi_decode_step(cache, k_new, v_new, q, sm_scale, out=None, lse=None, num_splits=0, workspace=None):
+    """kivi_append_flush(cache, k_new, v_new) then kivi_decode_attn(cache, q, ...), one launch
+    when no group is flushed.  Returns (out, flushed) or (out, lse, flushed) if `lse`."""
+    for t in (k_new, v_new):
+        if not t.is_contiguous() or t.dtype != torch.float16:
+            raise ValueError("expected contiguous float16 [B, Hkv, D]")
+    if not q.is_contiguous() or q.dtype != torch.float16:
+        raise ValueError("expected contiguous float16 q [B, Hq, D]")
+    B, Hq, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    want_lse = lse is not None and lse is not False
+    if lse is True:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    ws = workspace if workspace is not None else cache.workspace(Hq, num_splits)
+    flushed = C.c_int32(0)
+    _check(lib.kivi_decode_step(C.byref(cache.c), _ptr(k_new), _ptr(v_new), _ptr(q), Hq, float(sm_scale),
+                                _ptr(out), _ptr(lse) if want_lse else None, _ptr(ws), ws.numel() * ws.element_size(),
+                                num_splits, C.byref(flushed), _stream(q)), "kivi_decode_step")
+    return (out, lse, bool(flushed.value)) if want_lse else (out, bool(flushed.value))
 
 
 def kivi_decode_attn_splits(cache, q_heads):

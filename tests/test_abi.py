@@ -21,7 +21,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 9
+    assert len(names) == 10
     out = os.popen(f"nm -D --defined-only {kivi.LIB_PATH}").read()
     exported = set(re.findall(r" T (kivi_\w+)$", out, re.M))
     assert set(names) <= exported, set(names) - exported
@@ -142,6 +142,30 @@ def test_decode_attn_argument_errors():
     assert a(c, sm=float("inf")) == -2
     assert a(_cache(n_quant=0, n_res=0)) == -2          # empty context
     assert a(_cache(n_res=200)) == -7
+
+
+def test_decode_step_errors_leave_state():
+    """The step validates the append and the attention on the post-append state before it
+    enqueues anything: every error leaves the cache state as it was."""
+    flushed = C.c_int32(7)
+
+    def step(cache, k=FAKE, v=FAKE, q=FAKE, q_heads=4, ws=FAKE, wsb=1 << 30, splits=0):
+        return L.kivi_decode_step(C.byref(cache), C.c_void_p(k), C.c_void_p(v), C.c_void_p(q), q_heads, 0.088,
+                                  C.c_void_p(FAKE), None, C.c_void_p(ws), wsb, splits, C.byref(flushed), None)
+    cases = [(_cache(n_quant=256, n_res=128, res_head=32), {}, -4),     # flush needed, no room
+             (_cache(), dict(k=0), -1), (_cache(), dict(v=FAKE + 8), -2),
+             (_cache(), dict(q=0), -1), (_cache(), dict(q_heads=3), -2), (_cache(), dict(ws=0), -5),
+             (_cache(), dict(splits=-1), -2), (_cache(n_res=129), {}, -7), (_cache(res_head=16), {}, -7)]
+    for c, kw, code in cases:
+        st = _state(c)
+        assert step(c, **kw) == code, (kw, code)
+        assert _state(c) == st and flushed.value == 7
+    # the workspace check uses the post-append state: a flush adds a group, so the
+    # requirement is computed on the cache after the append
+    c = _cache(n_quant=64, n_res=128, res_head=0)
+    after = _cache(n_quant=96, n_res=97, res_head=32)
+    need = L.kivi_decode_attn_workspace(C.byref(after), 4, 0)
+    assert step(c, wsb=need - 1) == -5 and _state(c) == (64, 128, 0)
 
 
 def test_split_selection_and_workspace():

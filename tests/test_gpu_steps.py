@@ -16,7 +16,7 @@ def _kivi():
     return kivi
 
 
-def _steps(w, dev, steps, check_cache_every, attn_rows_every, bsel=None):
+def _steps(w, dev, steps, check_cache_every, attn_rows_every, bsel=None, fused=False):
     kivi = _kivi()
     k, v = synth.prefill_kv(w, device=dev)
     cache = kivi.Cache(w.batch, w.kv_heads, w.token_cap, device=dev)
@@ -29,12 +29,15 @@ def _steps(w, dev, steps, check_cache_every, attn_rows_every, bsel=None):
     for s in range(steps):
         kn, vn = synth.step_kv(w, s, device=dev)
         q = synth.query(w, step=s + 1, device=dev)
-        f_gpu = kivi.kivi_append_flush(cache, kn, vn)
+        if fused:
+            out, lse, f_gpu = kivi.kivi_decode_step(cache, kn, vn, q, SM, lse=True)
+        else:
+            f_gpu = kivi.kivi_append_flush(cache, kn, vn)
+            out, lse = kivi.kivi_decode_attn(cache, q, SM, lse=True)
         f_ref = rc.append(bits(kn[bsel]).reshape(-1, 128), bits(vn[bsel]).reshape(-1, 128))
         assert f_gpu == f_ref, s
         if f_gpu:
             flushes.append(s)
-        out, lse = kivi.kivi_decode_attn(cache, q, SM, lse=True)
         torch.cuda.synchronize()
         if f_gpu or (check_cache_every and s % check_cache_every == 0) or s == steps - 1:
             class View:
@@ -78,3 +81,35 @@ def test_gqa_mistral_128_steps_sampled():
     w = synth.WORKLOADS["gqa-mistral-7b"]
     flushes = _steps(w, dev, 128, check_cache_every=0, attn_rows_every=8, bsel=[5])
     assert flushes == [0, 32, 64, 96]
+
+
+# ---- the fused decode step (kivi_decode_step): same state machine and results, one launch
+# when no group is flushed
+
+@pytest.mark.parametrize("q_heads,kv_heads", [(4, 2), (3, 3), (8, 2)])
+def test_fused_step_small_loop_every_step(q_heads, kv_heads):
+    dev = gpu_or_skip()
+    w = synth.small(seed=20 + q_heads, batch=2, q_heads=q_heads, kv_heads=kv_heads, context=96 + 100, n_quant=96,
+                    decode_steps=70)
+    flushes = _steps(w, dev, 70, check_cache_every=1, attn_rows_every=1, fused=True)
+    assert flushes == [28, 60]
+
+
+def test_fused_step_empty_start():
+    dev = gpu_or_skip()
+    w = synth.small(seed=21, batch=1, q_heads=2, kv_heads=1, context=1, n_quant=0, decode_steps=170)
+    flushes = _steps(w, dev, 170, check_cache_every=7, attn_rows_every=3, fused=True)
+    assert flushes == [127, 159]
+
+
+def test_fused_step_gqa_mistral_sampled():
+    dev = gpu_or_skip()
+    w = synth.WORKLOADS["gqa-mistral-7b"]
+    flushes = _steps(w, dev, 40, check_cache_every=0, attn_rows_every=5, bsel=[9], fused=True)
+    assert flushes == [0, 32]
+
+
+def test_fused_step_long_context_sampled():
+    dev = gpu_or_skip()
+    w = synth.WORKLOADS["long-128k"]
+    _steps(w, dev, 3, check_cache_every=1, attn_rows_every=1, fused=True)
