@@ -13,7 +13,10 @@ using namespace kivi;
 
 namespace {
 
-constexpr int64_t kTargetBlocks = 768;      // one round of resident workgroups on MI355X: 256 CUs x 3
+// One round of resident workgroups on MI355X's 256 CUs: three per CU for the single-query
+// kernel, two for the query-group kernel (their register use sets three and two waves per SIMD).
+constexpr int64_t kTargetBlocks = 768;
+constexpr int64_t kTargetBlocksGroup = 512;
 constexpr int kMinGroupsPerSplit = 8;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -75,7 +78,8 @@ int64_t block_rows(const kivi_cache* c, int32_t q_heads) {
 int32_t auto_splits(const kivi_cache* c, int32_t q_heads) {
     const int64_t rows = block_rows(c, q_heads);
     const int64_t groups = c->n_quant / c->group;
-    int64_t s = (kTargetBlocks + rows - 1) / rows;
+    const int64_t target = queries_per_block(q_heads / c->kv_heads) > 1 ? kTargetBlocksGroup : kTargetBlocks;
+    int64_t s = (target + rows - 1) / rows;
     const int64_t cap = groups / kMinGroupsPerSplit;
     if (s > cap) s = cap;
     if (s < 1) s = 1;

@@ -44,7 +44,7 @@ constexpr int kAreaBytes = kZeroOff + 512;
 
 __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
     __shared__ __align__(16) uint8_t sh_area[2][kWaves][kAreaBytes];
-    __shared__ float sh_o[1][kSlots][kD];
+    __shared__ __align__(16) float sh_o[1][kSlots][kD];
     __shared__ float sh_m[1][kSlots], sh_l[1][kSlots];
 
     const int split = blockIdx.x;

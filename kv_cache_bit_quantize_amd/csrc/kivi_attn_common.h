@@ -90,44 +90,48 @@ __device__ __forceinline__ float load_coherent(float* p) {
 constexpr int kWaitVmcnt0 = 0x0F70;
 
 // Softmax states of query rows qrow0..qrow0+NQ-1 over the fp16 residual ring.  Called by one
-// whole wave; wave w takes the ring's logical tokens [32w + 128i, 32w + 128i + 32).  Lane
-// 4*tp + qq holds tokens 2tp, 2tp+1 of such a chunk and channels [32qq, 32qq+32); a chunk's
-// keys and values are loaded once, in one round, for all NQ rows, which then take turns,
-// 8 channels at a time, to keep few registers live.  Row r's o accumulates in o_dst[r*o_stride
-// + c]; m[r] = -inf and l[r] = 0 when the wave has no residual token.
+// whole wave; wave w takes the ring's logical tokens [32w + 128i, 32w + 128i + 32).  Per such
+// chunk, two phases:
+//  * logits: lane 4*tp + qq holds tokens 2tp, 2tp+1 and channels [32qq, 32qq+32) and forms
+//    q.k with v_dot2_f32_f16 on packed halves for every row; the chunk's probabilities go to
+//    LDS (o_dst, channels 0..31 of each row, as scratch);
+//  * P.V, channel-parallel: lane l accumulates channels 2l, 2l+1 of every row over the
+//    chunk's tokens (token rows loaded 256 bytes per instruction, probabilities read from LDS
+//    as broadcasts), so no cross-lane sums are needed.
+// Row r's o (relative to 2^m[r]) ends in o_dst[r*o_stride + c]; m[r] = -inf and l[r] = 0 when
+// the wave has no residual token.  In a fused decode step the last residual token is the new
+// one, read from k_new / v_new.
 template <int NQ>
 __device__ void residual_states(const AttnArgs& a, int64_t qrow0, int64_t kvrow, int wave, float* o_dst,
                                 int o_stride, float (&mr)[NQ], float (&lr)[NQ]) {
     const int lane = threadIdx.x & 63, tp = lane >> 2, qq = lane & 3;
+    float o[NQ][2];
 #pragma unroll
     for (int r = 0; r < NQ; ++r) {
         mr[r] = -INFINITY;
         lr[r] = 0.0f;
+        o[r][0] = o[r][1] = 0.0f;
     }
+    auto token_slot = [&](int i) { return (a.res_head + i) % a.residual_cap; };
+    auto is_new = [&](int i) { return a.k_new != nullptr && i == a.n_res - 1; };
     for (int base = wave * kG; base < a.n_res; base += kWaves * kG) {
+        // ---- logits of tokens 2tp, 2tp+1 for every row
         const int i0 = base + 2 * tp, i1 = i0 + 1;
         const bool ok0 = i0 < a.n_res, ok1 = i1 < a.n_res;
-        const int s0 = (a.res_head + (ok0 ? i0 : 0)) % a.residual_cap;
-        const int s1 = (a.res_head + (ok1 ? i1 : 0)) % a.residual_cap;
-        const int64_t r0 = (kvrow * a.residual_cap + s0) * kD + qq * 32;
-        const int64_t r1 = (kvrow * a.residual_cap + s1) * kD + qq * 32;
-        // in a fused decode step the last residual token is the new one, still in k_new / v_new
-        const bool new0 = a.k_new != nullptr && (ok0 ? i0 : 0) == a.n_res - 1;
-        const bool new1 = a.k_new != nullptr && (ok1 ? i1 : 0) == a.n_res - 1;
+        const int j0 = ok0 ? i0 : 0, j1 = ok1 ? i1 : 0;
         const int64_t rn = kvrow * kD + qq * 32;
-        const uint4* k0 = reinterpret_cast<const uint4*>(new0 ? a.k_new + rn : a.k_res + r0);
-        const uint4* k1 = reinterpret_cast<const uint4*>(new1 ? a.k_new + rn : a.k_res + r1);
-        const uint4* v0 = reinterpret_cast<const uint4*>(new0 ? a.v_new + rn : a.v_res + r0);
-        const uint4* v1 = reinterpret_cast<const uint4*>(new1 ? a.v_new + rn : a.v_res + r1);
-        uint4 kx0[4], kx1[4], vx0[4], vx1[4];   // keys and values in one round of loads
+        const uint4* k0 = reinterpret_cast<const uint4*>(
+            is_new(j0) ? a.k_new + rn : a.k_res + (kvrow * a.residual_cap + token_slot(j0)) * kD + qq * 32);
+        const uint4* k1 = reinterpret_cast<const uint4*>(
+            is_new(j1) ? a.k_new + rn : a.k_res + (kvrow * a.residual_cap + token_slot(j1)) * kD + qq * 32);
+        uint4 kx0[4], kx1[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             kx0[i] = k0[i];
             kx1[i] = k1[i];
-            vx0[i] = v0[i];
-            vx1[i] = v1[i];
         }
-        const bool first = base == wave * kG;
+        float al[NQ];
+#pragma unroll
         for (int r = 0; r < NQ; ++r) {
             // q.k on packed halves: each fp16 product is exact in fp32, summed in fp32
             const uint4* qp = reinterpret_cast<const uint4*>(a.q + (qrow0 + r) * kD + qq * 32);
@@ -144,35 +148,60 @@ __device__ void residual_states(const AttnArgs& a, int64_t qrow0, int64_t kvrow,
                     d1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2v, qh[k]), __builtin_bit_cast(h2v, w1[k]), d1, false);
                 }
             }
-            d0 *= a.sm_log2;
-            d1 *= a.sm_log2;
-            d0 = wave_sum_xor(d0, 1, 2);
-            d1 = wave_sum_xor(d1, 1, 2);
+            d0 = quad_sum(d0) * a.sm_log2;   // over the 4 channel quarters
+            d1 = quad_sum(d1) * a.sm_log2;
             const float l0 = ok0 ? d0 : -INFINITY, l1 = ok1 ? d1 : -INFINITY;
-            const float m_new = fmaxf(mr[r], wave_max_xor(fmaxf(l0, l1), 4, 32));
-            const float alpha = (mr[r] == -INFINITY) ? 0.0f : exp2f(mr[r] - m_new);
+            const float m_new = fmaxf(mr[r], wave_max_quads(fmaxf(l0, l1)));
+            al[r] = (mr[r] == -INFINITY) ? 0.0f : exp2f(mr[r] - m_new);
             const float p0 = ok0 ? exp2f(l0 - m_new) : 0.0f;
             const float p1 = ok1 ? exp2f(l1 - m_new) : 0.0f;
-            lr[r] = lr[r] * alpha + wave_sum(qq == 0 ? p0 + p1 : 0.0f);   // one share per token pair
+            lr[r] = lr[r] * al[r] + wave_sum(qq == 0 ? p0 + p1 : 0.0f);   // one share per token pair
             mr[r] = m_new;
-            float* od = o_dst + r * o_stride + qq * 32;
+            if (qq == 0) {
+                o_dst[r * o_stride + 2 * tp] = p0;
+                o_dst[r * o_stride + 2 * tp + 1] = p1;
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // ---- P.V: lane l takes channels 2l, 2l+1 of the chunk's 32 token rows
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t w0[4] = {vx0[i].x, vx0[i].y, vx0[i].z, vx0[i].w};
-                const uint32_t w1[4] = {vx1[i].x, vx1[i].y, vx1[i].z, vx1[i].w};
-                float oc[8];
+        for (int r = 0; r < NQ; ++r) {
+            o[r][0] *= al[r];
+            o[r][1] *= al[r];
+        }
+        const int nt = min(kG, a.n_res - base);
+        for (int t0 = 0; t0 < nt; t0 += 8) {
+            uint32_t vv[8];
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    oc[2 * k] = fmaf(p1, h2f(w1[k] & 0xffffu), p0 * h2f(w0[k] & 0xffffu));
-                    oc[2 * k + 1] = fmaf(p1, h2f(w1[k] >> 16), p0 * h2f(w0[k] >> 16));
-                }
+            for (int u = 0; u < 8; ++u) {
+                const int i = base + min(t0 + u, nt - 1);
+                const uint16_t* row = is_new(i) ? a.v_new + kvrow * kD : a.v_res + (kvrow * a.residual_cap + token_slot(i)) * kD;
+                vv[u] = reinterpret_cast<const uint32_t*>(row)[lane];
+            }
 #pragma unroll
-                for (int c = 0; c < 8; ++c) oc[c] = wave_sum_xor(oc[c], 4, 32);   // over the token pairs
-                if (tp == 0) {
+            for (int r = 0; r < NQ; ++r) {
+                const float4 pa = *reinterpret_cast<const float4*>(o_dst + r * o_stride + t0);
+                const float4 pb = *reinterpret_cast<const float4*>(o_dst + r * o_stride + t0 + 4);
+                const float pt[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
 #pragma unroll
-                    for (int c = 0; c < 8; ++c) od[8 * i + c] = first ? oc[c] : fmaf(od[8 * i + c], alpha, oc[c]);
+                for (int u = 0; u < 8; ++u) {
+                    const float pu = t0 + u < nt ? pt[u] : 0.0f;
+                    o[r][0] = fmaf(pu, h2f(vv[u] & 0xffffu), o[r][0]);
+                    o[r][1] = fmaf(pu, h2f(vv[u] >> 16), o[r][1]);
                 }
             }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    if (wave * kG < a.n_res) {
+#pragma unroll
+        for (int r = 0; r < NQ; ++r) {
+            o_dst[r * o_stride + 2 * lane] = o[r][0];
+            o_dst[r * o_stride + 2 * lane + 1] = o[r][1];
         }
     }
 }

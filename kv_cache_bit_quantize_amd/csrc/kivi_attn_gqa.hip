@@ -36,7 +36,7 @@ __global__ __launch_bounds__(kBlock) void attn_gqa_kernel(AttnArgs a) {
     using Lds = GqaLds<NQ>;
     __shared__ __align__(16) uint8_t sh_area[kWaves][Lds::kBytes];
     __shared__ __align__(16) uint8_t sh_zero[Lds::kZeroBytes];
-    __shared__ float sh_o[NQ][kSlots][kD];
+    __shared__ __align__(16) float sh_o[NQ][kSlots][kD];
     __shared__ float sh_m[NQ][kSlots], sh_l[NQ][kSlots];
 
     const int split = blockIdx.x;
@@ -136,15 +136,19 @@ __global__ __launch_bounds__(kBlock) void attn_gqa_kernel(AttnArgs a) {
     };
 
     __syncthreads();   // the zero area is written
-    Loads cur;
-    if (iters > 0) {
-        load_kp(cur, 0);
-        load_kc(cur, 0);
-        load_vp(cur, 0);
-        load_vc(cur, 0);
-    }
-    for (int it = 0; it < iters; ++it) {
-        const bool more = it + 1 < iters;
+    // Two register sets of loads, used by alternate iterations: each stream reloads its set
+    // for two iterations ahead right after its last use, so every load has more than an
+    // iteration to arrive (a kv head's query group keeps the grid at two waves per SIMD,
+    // so the registers are there).
+    constexpr int kPrefetch = 2;
+    auto load_all = [&](Loads& L, int it) {
+        load_kp(L, it);
+        load_kc(L, it);
+        load_vp(L, it);
+        load_vc(L, it);
+    };
+    auto iteration = [&](Loads& cur, int it) {
+        const bool more = it + kPrefetch < iters;
         const bool gv0 = gb + 2 * it < ge, gv1 = gb + 2 * it + 1 < ge;
 
         // ---- q_r*s of this half's group as 30-bit fixed point (one exponent for the NQ
@@ -194,8 +198,8 @@ __global__ __launch_bounds__(kBlock) void attn_gqa_kernel(AttnArgs a) {
         }
         // value pairs of the 64 tokens, for the lanes that need another lane's token
         *reinterpret_cast<uint4*>(area + Lds::kPairOff + lane * 16) = cur.vp;
-        if (more) load_vp(cur, it + 1);
-        if (more) load_kp(cur, it + 1);
+        if (more) load_vp(cur, it + kPrefetch);
+        if (more) load_kp(cur, it + kPrefetch);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -229,7 +233,7 @@ __global__ __launch_bounds__(kBlock) void attn_gqa_kernel(AttnArgs a) {
             const bool ok = qlive && ((t >> 1) ? gv1 : gv0);
             lg[t] = ok ? fmaf(tot, kscale[t >> 1], azq[t >> 1]) : -INFINITY;
         }
-        if (more) load_kc(cur, it + 1);
+        if (more) load_kc(cur, it + kPrefetch);
 
         // ---- online softmax per query over the 64 tokens (rescale only when a max rises)
         const float mnew = fmaxf(m, row_max(fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3]))));
@@ -314,7 +318,14 @@ __global__ __launch_bounds__(kBlock) void attn_gqa_kernel(AttnArgs a) {
                 cv[v] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop, cv[v], 0, 0, 0);
             }
         }
-        if (more) load_vc(cur, it + 1);
+        if (more) load_vc(cur, it + kPrefetch);
+    };
+    Loads set0, set1;
+    if (iters > 0) load_all(set0, 0);
+    if (iters > 1) load_all(set1, 1);
+    for (int it = 0; it < iters; it += 2) {
+        iteration(set0, it);
+        if (it + 1 < iters) iteration(set1, it + 1);
     }
 
     // ---- each query's quantized-part state: o = (P.V - weight sums) / vs + sum p*zero
