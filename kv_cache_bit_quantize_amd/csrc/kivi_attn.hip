@@ -53,7 +53,8 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
     const int hq = (int)(qrow % a.q_heads);
     const int64_t kvrow = b * a.kv_heads + hq / a.ratio;
     if (a.k_new != nullptr && split == 0 && hq % a.ratio == 0) store_new_token(a, kvrow);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform, as the compiler sees it
     const int gh = lane >> 5;          // group of the wave-iteration this lane serves
     const int tt = lane & 31;          // token role: token tt of group gh
     const int wl = lane & 31;          // fixed-point writer role: channels 4wl .. 4wl+3
@@ -142,147 +143,150 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
         L.vp = *reinterpret_cast<const uint4*>(vp_row + value_pair_index((int64_t)group_of(it, gh) * kG + tt, 0));
     };
 
+    // Every load is issued unconditionally (past the end it reads the last iteration's data
+    // again, from the L2), so the compiler knows how many loads are in flight at each use and
+    // waits for exactly the one it needs.
     Loads cur;
     if (iters > 0) {
         load_kp(cur, 0);
         load_kc(cur, 0);
         load_vp(cur, 0);
         load_vc(cur, 0);
-    }
-    for (int it = 0; it < iters; ++it) {
-        const bool more = it + 1 < iters;
-        const bool gvalid = gb + 2 * it + gh < ge;
-        uint8_t* area = &sh_area[it & 1][wave][0];
+        for (int it = 0; it < iters; ++it) {
+            const int nxt = min(it + 1, iters - 1);
+            const bool gvalid = gb + 2 * it + gh < ge;
+            uint8_t* area = &sh_area[it & 1][wave][0];
 
-        // ---- q*s of this half's group as 30-bit fixed point, four signed byte digits,
-        // stored as digit planes
-        const uint32_t pr[4] = {cur.kp.x, cur.kp.y, cur.kp.z, cur.kp.w};
-        float qs[4], az = 0.0f, mx = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            qs[i] = qw[i] * h2f(pr[i] & 0xffffu);
-            az = fmaf(qw[i], h2f(pr[i] >> 16), az);
-            mx = fmaxf(mx, fabsf(qs[i]));
-        }
-        az = half_sum(az);
-        mx = half_max(mx);
-        const int sh = 29 - __builtin_amdgcn_frexp_expf(mx);   // |q*s| * 2^sh < 2^29
-        uint32_t dg[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int qi = (int)__builtin_rintf(__builtin_ldexpf(qs[i] * cls_div, sh));
-            dg[i] = ((uint32_t)qi + 0x80808080u) ^ 0x80808080u;    // four signed base-256 digits
-        }
-        {
-            const uint32_t A = __builtin_amdgcn_perm(dg[1], dg[0], 0x05010400u);
-            const uint32_t B = __builtin_amdgcn_perm(dg[1], dg[0], 0x07030602u);
-            const uint32_t C = __builtin_amdgcn_perm(dg[3], dg[2], 0x05010400u);
-            const uint32_t E = __builtin_amdgcn_perm(dg[3], dg[2], 0x07030602u);
-            uint32_t* plane = reinterpret_cast<uint32_t*>(area + gh * kGroupTbl) + wl;
-            plane[0 * kD / 4] = __builtin_amdgcn_perm(C, A, 0x05040100u);   // digit 0 of the 4 channels
-            plane[1 * kD / 4] = __builtin_amdgcn_perm(C, A, 0x07060302u);   // digit 1
-            plane[2 * kD / 4] = __builtin_amdgcn_perm(E, B, 0x05040100u);   // digit 2
-            plane[3 * kD / 4] = __builtin_amdgcn_perm(E, B, 0x07060302u);   // digit 3
-        }
-        if (more) load_kp(cur, it + 1);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-        // ---- key logits on the matrix cores: tile t = 2*group + token half, K = 64
-        // channels per instruction
-        v4i cacc = {0, 0, 0, 0};
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const uint4 kc = cur.kc[t >> 1];
-#pragma unroll
-            for (int kh = 0; kh < 2; ++kh) {
-                const uint32_t x = (t & 1) ? (kh ? kc.w : kc.z) : (kh ? kc.y : kc.x);
-                const v4i bop = {(int)(x & 0x03030303u), (int)(x & 0x0C0C0C0Cu), (int)(x & 0x30303030u),
-                                 (int)((x >> 2) & 0x30303030u)};
-                const v4i aop = *reinterpret_cast<const v4i*>(area + ka_off[t] + 64 * kh);
-                cacc = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop, bop, cacc, 0, 0, 0);
+            // ---- q*s of this half's group as 30-bit fixed point, four signed byte digits,
+            // stored as digit planes
+            const uint32_t pr[4] = {cur.kp.x, cur.kp.y, cur.kp.z, cur.kp.w};
+            float qs[4], az = 0.0f, mx = 0.0f;
+    #pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                qs[i] = qw[i] * h2f(pr[i] & 0xffffu);
+                az = fmaf(qw[i], h2f(pr[i] >> 16), az);
+                mx = fmaxf(mx, fabsf(qs[i]));
             }
-        }
-        if (more) load_kc(cur, it + 1);
-        float lg;
-        {
-            const int hi = cacc[3] * 256 + cacc[2], lo = cacc[1] * 256 + cacc[0];
-            const float tot = fmaf((float)hi, 65536.0f, (float)lo);
-            lg = gvalid ? fmaf(tot, __builtin_ldexpf(1.0f, -sh), az) : -INFINITY;
-        }
+            az = half_sum(az);
+            mx = half_max(mx);
+            const int sh = 29 - __builtin_amdgcn_frexp_expf(mx);   // |q*s| * 2^sh < 2^29
+            uint32_t dg[4];
+    #pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int qi = (int)__builtin_rintf(__builtin_ldexpf(qs[i] * cls_div, sh));
+                dg[i] = ((uint32_t)qi + 0x80808080u) ^ 0x80808080u;    // four signed base-256 digits
+            }
+            {
+                const uint32_t A = __builtin_amdgcn_perm(dg[1], dg[0], 0x05010400u);
+                const uint32_t B = __builtin_amdgcn_perm(dg[1], dg[0], 0x07030602u);
+                const uint32_t C = __builtin_amdgcn_perm(dg[3], dg[2], 0x05010400u);
+                const uint32_t E = __builtin_amdgcn_perm(dg[3], dg[2], 0x07030602u);
+                uint32_t* plane = reinterpret_cast<uint32_t*>(area + gh * kGroupTbl) + wl;
+                plane[0 * kD / 4] = __builtin_amdgcn_perm(C, A, 0x05040100u);   // digit 0 of the 4 channels
+                plane[1 * kD / 4] = __builtin_amdgcn_perm(C, A, 0x07060302u);   // digit 1
+                plane[2 * kD / 4] = __builtin_amdgcn_perm(E, B, 0x05040100u);   // digit 2
+                plane[3 * kD / 4] = __builtin_amdgcn_perm(E, B, 0x07060302u);   // digit 3
+            }
+            load_kp(cur, nxt);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-        // ---- online softmax over the wave's 64 tokens (rescale only when the max rises)
-        float mloc = half_max(lg);
-        mloc = fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mloc), 0)),
-                     __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mloc), 32)));
-        if (mloc > m) {
-            const float al = exp2f(m - mloc);
-#pragma unroll
-            for (int v = 0; v < 8; ++v) cv[v] *= al;
-#pragma unroll
+            // ---- key logits on the matrix cores: tile t = 2*group + token half, K = 64
+            // channels per instruction
+            v4i cacc = {0, 0, 0, 0};
+    #pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const uint4 kc = cur.kc[t >> 1];
+    #pragma unroll
+                for (int kh = 0; kh < 2; ++kh) {
+                    const uint32_t x = (t & 1) ? (kh ? kc.w : kc.z) : (kh ? kc.y : kc.x);
+                    const v4i bop = {(int)(x & 0x03030303u), (int)(x & 0x0C0C0C0Cu), (int)(x & 0x30303030u),
+                                     (int)((x >> 2) & 0x30303030u)};
+                    const v4i aop = *reinterpret_cast<const v4i*>(area + ka_off[t] + 64 * kh);
+                    cacc = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop, bop, cacc, 0, 0, 0);
+                }
+            }
+            load_kc(cur, nxt);
+            float lg;
+            {
+                const int hi = cacc[3] * 256 + cacc[2], lo = cacc[1] * 256 + cacc[0];
+                const float tot = fmaf((float)hi, 65536.0f, (float)lo);
+                lg = gvalid ? fmaf(tot, __builtin_ldexpf(1.0f, -sh), az) : -INFINITY;
+            }
+
+            // ---- online softmax over the wave's 64 tokens (rescale only when the max rises)
+            float mloc = half_max(lg);
+            mloc = fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mloc), 0)),
+                         __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mloc), 32)));
+            if (mloc > m) {
+                const float al = exp2f(m - mloc);
+    #pragma unroll
+                for (int v = 0; v < 8; ++v) cv[v] *= al;
+    #pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    bk[k] *= al;
+                    zk[k] *= al;
+                }
+                lsum *= al;
+                m = mloc;
+            }
+            const float p = exp2f(lg - m);       // this lane's token
+            lsum += p;
+            const uint32_t vpr[4] = {cur.vp.x, cur.vp.y, cur.vp.z, cur.vp.w};
+            float sv[4], smax = 0.0f;
+    #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                bk[k] *= al;
-                zk[k] *= al;
+                sv[k] = h2f(vpr[k] & 0xffffu);
+                zk[k] = fmaf(p, h2f(vpr[k] >> 16), zk[k]);
+                smax = fmaxf(smax, sv[k]);
             }
-            lsum *= al;
-            m = mloc;
-        }
-        const float p = exp2f(lg - m);       // this lane's token
-        lsum += p;
-        const uint32_t vpr[4] = {cur.vp.x, cur.vp.y, cur.vp.z, cur.vp.w};
-        float sv[4], smax = 0.0f;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            sv[k] = h2f(vpr[k] & 0xffffu);
-            zk[k] = fmaf(p, h2f(vpr[k] >> 16), zk[k]);
-            smax = fmaxf(smax, sv[k]);
-        }
-        // value weights 16*p*s*vs must stay below 2^15: shrink vs (a power of two) if needed
-        if (__builtin_amdgcn_ballot_w64(smax * vs > 2048.0f || vs == 0.0f)) {
-            const float gm = wave_max_xor(smax, 1, 32);
-            const float nvs = __builtin_ldexpf(1.0f, 11 - __builtin_amdgcn_frexp_expf(gm));
-            if (vs != 0.0f && nvs < vs) {
-                const float r = nvs / vs;
-#pragma unroll
-                for (int v = 0; v < 8; ++v) cv[v] *= r;
-#pragma unroll
-                for (int k = 0; k < 4; ++k) bk[k] *= r;
+            // value weights 16*p*s*vs must stay below 2^15: shrink vs (a power of two) if needed
+            if (__builtin_amdgcn_ballot_w64(smax * vs > 2048.0f || vs == 0.0f)) {
+                const float gm = wave_max_xor(smax, 1, 32);
+                const float nvs = __builtin_ldexpf(1.0f, 11 - __builtin_amdgcn_frexp_expf(gm));
+                if (vs != 0.0f && nvs < vs) {
+                    const float r = nvs / vs;
+    #pragma unroll
+                    for (int v = 0; v < 8; ++v) cv[v] *= r;
+    #pragma unroll
+                    for (int k = 0; k < 4; ++k) bk[k] *= r;
+                }
+                if (vs == 0.0f || nvs < vs) vs = nvs;
             }
-            if (vs == 0.0f || nvs < vs) vs = nvs;
-        }
-        {
-            const float f = p * (cls_w * vs);
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const _Float16 h = (_Float16)(f * sv[k]);
-                bk[k] += (float)h;
-                *reinterpret_cast<_Float16*>(area + w_off + k * 64) = h;
+            {
+                const float f = p * (cls_w * vs);
+    #pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const _Float16 h = (_Float16)(f * sv[k]);
+                    bk[k] += (float)h;
+                    *reinterpret_cast<_Float16*>(area + w_off + k * 64) = h;
+                }
             }
-        }
-        if (more) load_vp(cur, it + 1);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            load_vp(cur, nxt);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-        // ---- P.V on the matrix cores: K = the 32 tokens of a group, N = 16 channels
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-            const uint4 vc = cur.vc[g];
-            const uint32_t words[4] = {vc.x, vc.y, vc.z, vc.w};
-#pragma unroll
-            for (int v = 0; v < 8; ++v) {
-                // word v/2 holds blocks v (even) and v+1 in alternate bytes
-                const uint32_t x = words[v >> 1];
-                const uint32_t s1 = (v & 1) ? x >> 2 : x << 6, s2 = (v & 1) ? x >> 6 : x << 2;
-                const uint32_t bw[4] = {and_or(s1, kM6, kOne), and_or(s1, kM8, kOne), and_or(s2, kM6, kOne),
-                                        and_or(s2, kM8, kOne)};
-                const v8h bop = __builtin_bit_cast(v8h, make_uint4(bw[0], bw[1], bw[2], bw[3]));
-                const v8h aop = *reinterpret_cast<const v8h*>(area + va_off + (g * 4 + (v >> 1)) * 64);
-                cv[v] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop, cv[v], 0, 0, 0);
+            // ---- P.V on the matrix cores: K = the 32 tokens of a group, N = 16 channels
+    #pragma unroll
+            for (int g = 0; g < 2; ++g) {
+                const uint4 vc = cur.vc[g];
+                const uint32_t words[4] = {vc.x, vc.y, vc.z, vc.w};
+    #pragma unroll
+                for (int v = 0; v < 8; ++v) {
+                    // word v/2 holds blocks v (even) and v+1 in alternate bytes
+                    const uint32_t x = words[v >> 1];
+                    const uint32_t s1 = (v & 1) ? x >> 2 : x << 6, s2 = (v & 1) ? x >> 6 : x << 2;
+                    const uint32_t bw[4] = {and_or(s1, kM6, kOne), and_or(s1, kM8, kOne), and_or(s2, kM6, kOne),
+                                            and_or(s2, kM8, kOne)};
+                    const v8h bop = __builtin_bit_cast(v8h, make_uint4(bw[0], bw[1], bw[2], bw[3]));
+                    const v8h aop = *reinterpret_cast<const v8h*>(area + va_off + (g * 4 + (v >> 1)) * 64);
+                    cv[v] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop, cv[v], 0, 0, 0);
+                }
             }
+            load_vc(cur, nxt);
         }
-        if (more) load_vc(cur, it + 1);
     }
 
     // ---- the wave's quantized-part state: o = (P.V - weight sums) / vs + sum p*zero

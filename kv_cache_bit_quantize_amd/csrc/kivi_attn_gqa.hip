@@ -46,7 +46,8 @@ __global__ __launch_bounds__(kBlock) void attn_gqa_kernel(AttnArgs a) {
     const int chunk = (int)(grow % chunks);
     const int64_t qrow0 = (kvrow / a.kv_heads) * a.q_heads + (kvrow % a.kv_heads) * a.ratio + chunk * NQ;
     if (a.k_new != nullptr && split == 0 && chunk == 0) store_new_token(a, kvrow);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform, as the compiler sees it
     const int gh = lane >> 5, tt = lane & 31;        // token role (loads): token tt of group gh
     const int wl = lane & 31, wk = wl & 3;           // fixed-point writer role: channels 4wl..4wl+3
     const int mrow = lane & 15, kgrp = lane >> 4;    // matrix-operand role
@@ -148,7 +149,7 @@ __global__ __launch_bounds__(kBlock) void attn_gqa_kernel(AttnArgs a) {
         load_vc(L, it);
     };
     auto iteration = [&](Loads& cur, int it) {
-        const bool more = it + kPrefetch < iters;
+        const int nxt = min(it + kPrefetch, iters - 1);
         const bool gv0 = gb + 2 * it < ge, gv1 = gb + 2 * it + 1 < ge;
 
         // ---- q_r*s of this half's group as 30-bit fixed point (one exponent for the NQ
@@ -198,8 +199,8 @@ __global__ __launch_bounds__(kBlock) void attn_gqa_kernel(AttnArgs a) {
         }
         // value pairs of the 64 tokens, for the lanes that need another lane's token
         *reinterpret_cast<uint4*>(area + Lds::kPairOff + lane * 16) = cur.vp;
-        if (more) load_vp(cur, it + kPrefetch);
-        if (more) load_kp(cur, it + kPrefetch);
+        load_vp(cur, nxt);
+        load_kp(cur, nxt);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -233,7 +234,7 @@ __global__ __launch_bounds__(kBlock) void attn_gqa_kernel(AttnArgs a) {
             const bool ok = qlive && ((t >> 1) ? gv1 : gv0);
             lg[t] = ok ? fmaf(tot, kscale[t >> 1], azq[t >> 1]) : -INFINITY;
         }
-        if (more) load_kc(cur, it + kPrefetch);
+        load_kc(cur, nxt);
 
         // ---- online softmax per query over the 64 tokens (rescale only when a max rises)
         const float mnew = fmaxf(m, row_max(fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3]))));
@@ -318,14 +319,22 @@ __global__ __launch_bounds__(kBlock) void attn_gqa_kernel(AttnArgs a) {
                 cv[v] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop, cv[v], 0, 0, 0);
             }
         }
-        if (more) load_vc(cur, it + kPrefetch);
+        load_vc(cur, nxt);
     };
+    // Every load is issued unconditionally (past the end it reads the last iteration's data
+    // again, from the L2) and the loop has one exit, at its head, so both paths into the head
+    // have issued the same loads: the compiler then knows how many loads are in flight at
+    // each use and waits for exactly the one it needs.  With an odd iteration count the last
+    // pair's second half is idle: its groups are out of range, so its logits are -inf and its
+    // weights zero.
     Loads set0, set1;
-    if (iters > 0) load_all(set0, 0);
-    if (iters > 1) load_all(set1, 1);
-    for (int it = 0; it < iters; it += 2) {
-        iteration(set0, it);
-        if (it + 1 < iters) iteration(set1, it + 1);
+    if (iters > 0) {
+        load_all(set0, 0);
+        load_all(set1, min(1, iters - 1));
+        for (int it = 0; it < iters; it += 2) {
+            iteration(set0, it);
+            iteration(set1, it + 1);
+        }
     }
 
     // ---- each query's quantized-part state: o = (P.V - weight sums) / vs + sum p*zero
