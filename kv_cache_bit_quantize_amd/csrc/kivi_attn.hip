@@ -84,15 +84,15 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
     // this lane's slot in the weight table: tokens 8kg..8kg+7 of a group are ordered
     // 0,4,1,5,2,6,3,7 (the order the code operand produces them in)
     const int w_off = kWtOff + gh * 4 * 64 + (tt >> 3) * 16 + (((tt & 3) << 1) | ((tt >> 2) & 1)) * 2;
-    // even tokens meet codes read as 1 + c/16, odd ones 1 + c/4
-    const float cls_w = (tt & 1) ? 4.0f : 16.0f;
+    // token 4a + i meets its code as the fp16 subnormal c * 4^i * 2^-24; its weight carries
+    // 16 * 4^-i, so every product is 2^-20 * (weight without the factor) * c
+    const float cls_w = __builtin_ldexpf(16.0f, -2 * (tt & 3));
     // the zero areas of both parities, written once
     reinterpret_cast<uint4*>(&sh_area[lane >> 5][wave][kZeroOff])[lane & 31] = make_uint4(0, 0, 0, 0);
 
     v4f cv[8];                         // P.V accumulators, one per 16-channel block (row 0)
 #pragma unroll
     for (int v = 0; v < 8; ++v) cv[v] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
-    float bk[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // this lane's share of the fp16 weight sums
     float zk[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // ... and of sum p*zero, per channel group
     float lsum = 0.0f, m = -INFINITY;
     float vs = 0.0f;                   // power-of-two factor keeping the value weights in fp16 range
@@ -112,7 +112,7 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
     const uint32_t* kp_row = reinterpret_cast<const uint32_t*>(a.k_sz) + kvrow * (int64_t)(a.token_cap / kG) * kD;
     const uint32_t* vp_row = reinterpret_cast<const uint32_t*>(a.v_sz) + tok_base * (kD / kG);
 
-    const uint32_t kM6 = in_vgpr(0x00C000C0u), kM8 = in_vgpr(0x03000300u), kOne = in_vgpr(0x3C003C00u);
+    constexpr uint32_t kF0 = 0x00030003u, kF1 = 0x000C000Cu, kF2 = 0x00300030u, kF3 = 0x00C000C0u;
 
     // one wave-iteration's global loads (issued one iteration ahead of their use); every
     // load instruction reads a contiguous span
@@ -169,11 +169,12 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
             }
             az = half_sum(az);
             mx = half_max(mx);
-            const int sh = 29 - __builtin_amdgcn_frexp_expf(mx);   // |q*s| * 2^sh < 2^29
+            const int sh = min(29 - __builtin_amdgcn_frexp_expf(mx), 100);   // |q*s| * 2^sh < 2^29
+            const float fs = __builtin_ldexpf(cls_div, sh);
             uint32_t dg[4];
     #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int qi = (int)__builtin_rintf(__builtin_ldexpf(qs[i] * cls_div, sh));
+                const int qi = (int)(qs[i] * fs);   // truncated: off by less than 2^-29 of the largest
                 dg[i] = ((uint32_t)qi + 0x80808080u) ^ 0x80808080u;    // four signed base-256 digits
             }
             {
@@ -224,23 +225,17 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
     #pragma unroll
                 for (int v = 0; v < 8; ++v) cv[v] *= al;
     #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    bk[k] *= al;
-                    zk[k] *= al;
-                }
+                for (int k = 0; k < 4; ++k) zk[k] *= al;
                 lsum *= al;
                 m = mloc;
             }
             const float p = exp2f(lg - m);       // this lane's token
             lsum += p;
             const uint32_t vpr[4] = {cur.vp.x, cur.vp.y, cur.vp.z, cur.vp.w};
-            float sv[4], smax = 0.0f;
     #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                sv[k] = h2f(vpr[k] & 0xffffu);
-                zk[k] = fmaf(p, h2f(vpr[k] >> 16), zk[k]);
-                smax = fmaxf(smax, sv[k]);
-            }
+            for (int k = 0; k < 4; ++k) zk[k] = fmaf(p, h2f(vpr[k] >> 16), zk[k]);
+            // the largest scale, on the fp16 bit patterns (scales are never negative)
+            const float smax = h2f(max_u16x2(max_u16x2(vpr[0], vpr[1]), max_u16x2(vpr[2], vpr[3])) & 0xffffu);
             // value weights 16*p*s*vs must stay below 2^15: shrink vs (a power of two) if needed
             if (__builtin_amdgcn_ballot_w64(smax * vs > 2048.0f || vs == 0.0f)) {
                 const float gm = wave_max_xor(smax, 1, 32);
@@ -249,19 +244,14 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
                     const float r = nvs / vs;
     #pragma unroll
                     for (int v = 0; v < 8; ++v) cv[v] *= r;
-    #pragma unroll
-                    for (int k = 0; k < 4; ++k) bk[k] *= r;
                 }
                 if (vs == 0.0f || nvs < vs) vs = nvs;
             }
             {
                 const float f = p * (cls_w * vs);
     #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const _Float16 h = (_Float16)(f * sv[k]);
-                    bk[k] += (float)h;
-                    *reinterpret_cast<_Float16*>(area + w_off + k * 64) = h;
-                }
+                for (int k = 0; k < 4; ++k)
+                    *reinterpret_cast<_Float16*>(area + w_off + k * 64) = (_Float16)(f * h2f(vpr[k] & 0xffffu));
             }
             load_vp(cur, nxt);
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -275,12 +265,10 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
                 const uint32_t words[4] = {vc.x, vc.y, vc.z, vc.w};
     #pragma unroll
                 for (int v = 0; v < 8; ++v) {
-                    // word v/2 holds blocks v (even) and v+1 in alternate bytes
-                    const uint32_t x = words[v >> 1];
-                    const uint32_t s1 = (v & 1) ? x >> 2 : x << 6, s2 = (v & 1) ? x >> 6 : x << 2;
-                    const uint32_t bw[4] = {and_or(s1, kM6, kOne), and_or(s1, kM8, kOne), and_or(s2, kM6, kOne),
-                                            and_or(s2, kM8, kOne)};
-                    const v8h bop = __builtin_bit_cast(v8h, make_uint4(bw[0], bw[1], bw[2], bw[3]));
+                    // word v/2 holds blocks v (even) and v+1 in alternate bytes; token field i
+                    // of each byte, masked in place, is the fp16 subnormal c * 4^i * 2^-24
+                    const uint32_t x = (v & 1) ? words[v >> 1] >> 8 : words[v >> 1];
+                    const v8h bop = __builtin_bit_cast(v8h, make_uint4(x & kF0, x & kF1, x & kF2, x & kF3));
                     const v8h aop = *reinterpret_cast<const v8h*>(area + va_off + (g * 4 + (v >> 1)) * 64);
                     cv[v] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop, cv[v], 0, 0, 0);
                 }
@@ -289,17 +277,14 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
         }
     }
 
-    // ---- the wave's quantized-part state: o = (P.V - weight sums) / vs + sum p*zero
+    // ---- the wave's quantized-part state: o = P.V * 2^20 / vs + sum p*zero
     lsum = wave_sum(lsum);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        bk[k] = wave_sum(bk[k]);
-        zk[k] = wave_sum(zk[k]);
-    }
+    for (int k = 0; k < 4; ++k) zk[k] = wave_sum(zk[k]);
     if (lane < 16) {   // row 0 of the accumulators: channel 16v + lane
-        const float inv = vs != 0.0f ? 1.0f / vs : 0.0f;
+        const float inv = vs != 0.0f ? 1048576.0f / vs : 0.0f;
 #pragma unroll
-        for (int v = 0; v < 8; ++v) sh_o[0][wave][16 * v + lane] = fmaf(cv[v][0] - bk[v >> 1], inv, zk[v >> 1]);
+        for (int v = 0; v < 8; ++v) sh_o[0][wave][16 * v + lane] = fmaf(cv[v][0], inv, zk[v >> 1]);
     }
     if (lane == 0) {
         sh_m[0][wave] = m;

@@ -38,6 +38,13 @@ __device__ __forceinline__ uint32_t in_vgpr(uint32_t c) {
     return c;
 }
 
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+// per-half unsigned maximum of two packed 16-bit pairs (one v_pk_max_u16)
+__device__ __forceinline__ uint32_t max_u16x2(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t,
+                              __builtin_elementwise_max(__builtin_bit_cast(u16x2, a), __builtin_bit_cast(u16x2, b)));
+}
+
 __device__ __forceinline__ float readlane_f(float v, int l) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
 }

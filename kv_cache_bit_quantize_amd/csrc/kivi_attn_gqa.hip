@@ -68,6 +68,14 @@ __global__ __launch_bounds__(kBlock) void attn_gqa_kernel(AttnArgs a) {
         qw[r][2] = h2f(x.y & 0xffffu) * a.sm_log2;
         qw[r][3] = h2f(x.y >> 16) * a.sm_log2;
     }
+    // the largest |q| of the NQ queries, per channel: bounds |q_r*s| without the products
+    float qa[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        qa[i] = fabsf(qw[0][i]);
+#pragma unroll
+        for (int r = 1; r < NQ; ++r) qa[i] = fmaxf(qa[i], fabsf(qw[r][i]));
+    }
     // codes of channels 4i..4i+3 arrive multiplied by 1, 4, 16, 16 (i = 0..3)
     const float cls_div = wk == 0 ? 1.0f : (wk == 1 ? 0.25f : 0.0625f);
 
@@ -81,14 +89,14 @@ __global__ __launch_bounds__(kBlock) void attn_gqa_kernel(AttnArgs a) {
     // this lane's weight slots: token 16t + n of the wave-iteration is token 16(t&1) + n of
     // group t>>1; tokens 8kg..8kg+7 of a group are ordered 0,4,1,5,2,6,3,7 in their slots
     uint8_t* wbase = area + Lds::kWtOff + qh * 64 + (n >> 3) * 16 + (((n & 3) << 1) | ((n >> 2) & 1)) * 2;
-    // even tokens meet codes read as 1 + c/16, odd ones 1 + c/4
-    const float cls_w = (n & 1) ? 4.0f : 16.0f;
+    // token 4a + i meets its code as the fp16 subnormal c * 4^i * 2^-24; its weight carries
+    // 16 * 4^-i, so every product is 2^-20 * (weight without the factor) * c
+    const float cls_w = __builtin_ldexpf(16.0f, -2 * (n & 3));
 
     v4f cv[8];                          // P.V accumulators, row h = query h
 #pragma unroll
     for (int v = 0; v < 8; ++v) cv[v] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
-    float bk[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // this lane's share (query qh) of the fp16 weight sums
-    float zk[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // ... and of sum p*zero, per channel group
+    float zk[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // this lane's share (query qh) of sum p*zero, per channel group
     float lsum = 0.0f, m = -INFINITY;          // query qh's running sum and max
     float vs = 0.0f;                    // power-of-two factor keeping the value weights in fp16 range
 
@@ -107,7 +115,7 @@ __global__ __launch_bounds__(kBlock) void attn_gqa_kernel(AttnArgs a) {
     const uint32_t* kp_row = reinterpret_cast<const uint32_t*>(a.k_sz) + kvrow * (int64_t)(a.token_cap / kG) * kD;
     const uint32_t* vp_row = reinterpret_cast<const uint32_t*>(a.v_sz) + tok_base * (kD / kG);
 
-    const uint32_t kM6 = in_vgpr(0x00C000C0u), kM8 = in_vgpr(0x03000300u), kOne = in_vgpr(0x3C003C00u);
+    constexpr uint32_t kF0 = 0x00030003u, kF1 = 0x000C000Cu, kF2 = 0x00300030u, kF3 = 0x00C000C0u;
 
     struct Loads {
         uint4 kp;          // (scale, zero) of key channels 4wl..4wl+3 of group gh
@@ -164,26 +172,24 @@ __global__ __launch_bounds__(kBlock) void attn_gqa_kernel(AttnArgs a) {
                 s4[i] = h2f(pr[i] & 0xffffu);
                 z4[i] = h2f(pr[i] >> 16);
             }
-            float qs[NQ][4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, qa[i] * s4[i]);
 #pragma unroll
             for (int r = 0; r < NQ; ++r) {
                 az[r] = 0.0f;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    qs[r][i] = qw[r][i] * s4[i];
-                    az[r] = fmaf(qw[r][i], z4[i], az[r]);
-                    mx = fmaxf(mx, fabsf(qs[r][i]));
-                }
+                for (int i = 0; i < 4; ++i) az[r] = fmaf(qw[r][i], z4[i], az[r]);
                 az[r] = half_sum(az[r]);
             }
             mx = half_max(mx);
-            sh = 29 - __builtin_amdgcn_frexp_expf(mx);   // |q*s| * 2^sh < 2^29
+            sh = min(29 - __builtin_amdgcn_frexp_expf(mx), 100);   // |q*s| * 2^sh < 2^29
+            const float fs = __builtin_ldexpf(cls_div, sh);
 #pragma unroll
             for (int r = 0; r < NQ; ++r) {
                 uint32_t dg[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int qi = (int)__builtin_rintf(__builtin_ldexpf(qs[r][i] * cls_div, sh));
+                    const int qi = (int)(qw[r][i] * s4[i] * fs);   // truncated: off by less than 2^-29 of the largest
                     dg[i] = ((uint32_t)qi + 0x80808080u) ^ 0x80808080u;    // four signed base-256 digits
                 }
                 const uint32_t A = __builtin_amdgcn_perm(dg[1], dg[0], 0x05010400u);
@@ -247,10 +253,7 @@ __global__ __launch_bounds__(kBlock) void attn_gqa_kernel(AttnArgs a) {
                 for (int v = 0; v < 8; ++v) cv[v][r] *= ar;
             }
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                bk[k] *= al;
-                zk[k] *= al;
-            }
+            for (int k = 0; k < 4; ++k) zk[k] *= al;
             lsum *= al;
         }
         m = mnew;
@@ -261,17 +264,17 @@ __global__ __launch_bounds__(kBlock) void attn_gqa_kernel(AttnArgs a) {
             lsum += p[t];
         }
         // value pairs of this lane's 4 tokens 16t + n: zero-point sums and the largest scale
-        float smax = 0.0f;
+        // (taken on the fp16 bit patterns: scales are never negative)
+        uint32_t smw = 0;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const uint4 pq = *reinterpret_cast<const uint4*>(area + Lds::kPairOff + (16 * t + n) * 16);
             const uint32_t pw[4] = {pq.x, pq.y, pq.z, pq.w};
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                zk[k] = fmaf(p[t], h2f(pw[k] >> 16), zk[k]);
-                smax = fmaxf(smax, h2f(pw[k] & 0xffffu));
-            }
+            for (int k = 0; k < 4; ++k) zk[k] = fmaf(p[t], h2f(pw[k] >> 16), zk[k]);
+            smw = max_u16x2(smw, max_u16x2(max_u16x2(pw[0], pw[1]), max_u16x2(pw[2], pw[3])));
         }
+        const float smax = h2f(smw & 0xffffu);
         // value weights 16*p*s*vs must stay below 2^15: shrink vs (a power of two) if needed
         if (__builtin_amdgcn_ballot_w64(smax * vs > 2048.0f || vs == 0.0f)) {
             const float gm = wave_max_xor(smax, 1, 32);
@@ -280,8 +283,6 @@ __global__ __launch_bounds__(kBlock) void attn_gqa_kernel(AttnArgs a) {
                 const float rs = nvs / vs;
 #pragma unroll
                 for (int v = 0; v < 8; ++v) cv[v] *= rs;
-#pragma unroll
-                for (int k = 0; k < 4; ++k) bk[k] *= rs;
             }
             if (vs == 0.0f || nvs < vs) vs = nvs;
         }
@@ -292,11 +293,9 @@ __global__ __launch_bounds__(kBlock) void attn_gqa_kernel(AttnArgs a) {
                 const uint32_t pw[4] = {pq.x, pq.y, pq.z, pq.w};
                 const float f = p[t] * (cls_w * vs);
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const _Float16 h = (_Float16)(f * h2f(pw[k] & 0xffffu));
-                    bk[k] += (float)h;
-                    *reinterpret_cast<_Float16*>(wbase + (t >> 1) * Lds::kWtGroup + (t & 1) * 32 + k * NQ * 64) = h;
-                }
+                for (int k = 0; k < 4; ++k)
+                    *reinterpret_cast<_Float16*>(wbase + (t >> 1) * Lds::kWtGroup + (t & 1) * 32 + k * NQ * 64) =
+                        (_Float16)(f * h2f(pw[k] & 0xffffu));
             }
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -310,11 +309,9 @@ __global__ __launch_bounds__(kBlock) void attn_gqa_kernel(AttnArgs a) {
             const uint32_t words[4] = {vc.x, vc.y, vc.z, vc.w};
 #pragma unroll
             for (int v = 0; v < 8; ++v) {
-                const uint32_t x = words[v >> 1];
-                const uint32_t s1 = (v & 1) ? x >> 2 : x << 6, s2 = (v & 1) ? x >> 6 : x << 2;
-                const uint32_t bw[4] = {and_or(s1, kM6, kOne), and_or(s1, kM8, kOne), and_or(s2, kM6, kOne),
-                                        and_or(s2, kM8, kOne)};
-                const v8h bop = __builtin_bit_cast(v8h, make_uint4(bw[0], bw[1], bw[2], bw[3]));
+                // token field i of each byte, masked in place: the fp16 subnormal c * 4^i * 2^-24
+                const uint32_t x = (v & 1) ? words[v >> 1] >> 8 : words[v >> 1];
+                const v8h bop = __builtin_bit_cast(v8h, make_uint4(x & kF0, x & kF1, x & kF2, x & kF3));
                 const v8h aop = *reinterpret_cast<const v8h*>(vbase + (g * 4 + (v >> 1)) * NQ * 64);
                 cv[v] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop, cv[v], 0, 0, 0);
             }
@@ -337,25 +334,19 @@ __global__ __launch_bounds__(kBlock) void attn_gqa_kernel(AttnArgs a) {
         }
     }
 
-    // ---- each query's quantized-part state: o = (P.V - weight sums) / vs + sum p*zero
+    // ---- each query's quantized-part state: o = P.V * 2^20 / vs + sum p*zero
     lsum = row_sum(lsum);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        bk[k] = row_sum(bk[k]);
-        zk[k] = row_sum(zk[k]);
-    }
-    const float inv = vs != 0.0f ? 1.0f / vs : 0.0f;
+    for (int k = 0; k < 4; ++k) zk[k] = row_sum(zk[k]);
+    const float inv = vs != 0.0f ? 1048576.0f / vs : 0.0f;
 #pragma unroll
     for (int r = 0; r < NQ; ++r) {
-        float br[4], zr[4];
+        float zr[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            br[k] = readlane_f(bk[k], 16 * r);
-            zr[k] = readlane_f(zk[k], 16 * r);
-        }
+        for (int k = 0; k < 4; ++k) zr[k] = readlane_f(zk[k], 16 * r);
         if (lane < 16) {   // accumulator row r: channel 16v + lane
 #pragma unroll
-            for (int v = 0; v < 8; ++v) sh_o[r][wave][16 * v + lane] = fmaf(cv[v][r] - br[v >> 1], inv, zr[v >> 1]);
+            for (int v = 0; v < 8; ++v) sh_o[r][wave][16 * v + lane] = fmaf(cv[v][r], inv, zr[v >> 1]);
         }
         const float mq = readlane_f(m, 16 * r), lq = readlane_f(lsum, 16 * r);
         if (lane == 0) {
