@@ -32,7 +32,7 @@ struct GqaLds {
 };
 
 template <int NQ>
-__global__ __launch_bounds__(kBlock) void attn_gqa_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) void attn_gqa_kernel(AttnArgs a) {
     using Lds = GqaLds<NQ>;
     __shared__ __align__(16) uint8_t sh_area[kWaves][Lds::kBytes];
     __shared__ __align__(16) uint8_t sh_zero[Lds::kZeroBytes];
@@ -58,26 +58,33 @@ __global__ __launch_bounds__(kBlock) void attn_gqa_kernel(AttnArgs a) {
     for (int i = threadIdx.x; i < Lds::kZeroBytes / 16; i += kBlock)
         reinterpret_cast<uint4*>(sh_zero)[i] = make_uint4(0, 0, 0, 0);
 
-    // query channels 4wl..4wl+3 of the NQ queries, log2 domain
-    float qw[NQ][4];
+    // query channels 4wl..4wl+3 of the NQ queries as packed fp16 pairs (4wl, 4wl+1 and
+    // 4wl+2, 4wl+3)
+    uint32_t qp[NQ][2];
 #pragma unroll
     for (int r = 0; r < NQ; ++r) {
         const uint2 x = *reinterpret_cast<const uint2*>(a.q + (qrow0 + r) * kD + 4 * wl);
-        qw[r][0] = h2f(x.x & 0xffffu) * a.sm_log2;
-        qw[r][1] = h2f(x.x >> 16) * a.sm_log2;
-        qw[r][2] = h2f(x.y & 0xffffu) * a.sm_log2;
-        qw[r][3] = h2f(x.y >> 16) * a.sm_log2;
+        qp[r][0] = x.x;
+        qp[r][1] = x.y;
     }
-    // the largest |q| of the NQ queries, per channel: bounds |q_r*s| without the products
+    // the largest |q| of the NQ queries per channel, times |sm_scale * log2 e|: bounds
+    // |q_r * s| in the log2 domain without the products
     float qa[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        qa[i] = fabsf(qw[0][i]);
+        qa[i] = 0.0f;
 #pragma unroll
-        for (int r = 1; r < NQ; ++r) qa[i] = fmaxf(qa[i], fabsf(qw[r][i]));
+        for (int r = 0; r < NQ; ++r) qa[i] = fmaxf(qa[i], fabsf(h2f(qp[r][i >> 1] >> (16 * (i & 1)))));
+        qa[i] *= fabsf(a.sm_log2);
     }
     // codes of channels 4i..4i+3 arrive multiplied by 1, 4, 16, 16 (i = 0..3)
     const float cls_div = wk == 0 ? 1.0f : (wk == 1 ? 0.25f : 0.0625f);
+    const float csl = cls_div * a.sm_log2;
+    // a zero the compiler cannot see: fma(h, f, kZero) stays one mixed-precision fma (a
+    // literal zero would turn it into a multiply with a separate conversion)
+    const float kZero = __builtin_bit_cast(float, in_vgpr(0u));
+    // after half_sum4, the lane of a half-wave that holds query r's sum
+    auto q_lane = [](int r) { return (r >> 1) | ((r & 1) << 1); };
 
     // key A operand of group g, channel half kh: row 4h + d = digit plane (h, d) of the group
     // (rows of absent queries read zeros) at kbase + g*kKeyGroup + 64*kh
@@ -161,35 +168,47 @@ __global__ __launch_bounds__(kBlock) void attn_gqa_kernel(AttnArgs a) {
         const bool gv0 = gb + 2 * it < ge, gv1 = gb + 2 * it + 1 < ge;
 
         // ---- q_r*s of this half's group as 30-bit fixed point (one exponent for the NQ
-        // queries), four signed byte digits per channel, stored as digit planes
-        float az[NQ], mx = 0.0f;
+        // queries), four signed byte digits per channel, stored as digit planes; q_r.z as
+        // packed dot products
+        float az;    // after the reduction: q_r.z of the half's group, r as q_lane gives
         int sh;
         {
             const uint32_t pr[4] = {cur.kp.x, cur.kp.y, cur.kp.z, cur.kp.w};
-            float s4[4], z4[4];
+            float s4[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                s4[i] = h2f(pr[i] & 0xffffu);
-                z4[i] = h2f(pr[i] >> 16);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, qa[i] * s4[i]);
+            for (int i = 0; i < 4; ++i) s4[i] = h2f(pr[i] & 0xffffu);
+            // the packed queries stay packed: converting them once, outside the loop, would
+            // hold 4*NQ more registers for a saving of no instruction (the conversions fold
+            // into the mixed-precision products)
 #pragma unroll
             for (int r = 0; r < NQ; ++r) {
-                az[r] = 0.0f;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) az[r] = fmaf(qw[r][i], z4[i], az[r]);
-                az[r] = half_sum(az[r]);
+                asm volatile("" : "+v"(qp[r][0]));
+                asm volatile("" : "+v"(qp[r][1]));
             }
+            float mx = fmaxf(fmaxf(qa[0] * s4[0], qa[1] * s4[1]), fmaxf(qa[2] * s4[2], qa[3] * s4[3]));
+            const uint32_t z01 = __builtin_amdgcn_perm(pr[1], pr[0], 0x07060302u);   // zeros of 4wl, 4wl+1
+            const uint32_t z23 = __builtin_amdgcn_perm(pr[3], pr[2], 0x07060302u);
+            float az4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int r = 0; r < NQ; ++r)
+                az4[r] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2v, qp[r][0]), __builtin_bit_cast(h2v, z01),
+                                                __builtin_amdgcn_fdot2(__builtin_bit_cast(h2v, qp[r][1]),
+                                                                       __builtin_bit_cast(h2v, z23), 0.0f, false),
+                                                false);
+            az = half_sum4(az4);
             mx = half_max(mx);
             sh = min(29 - __builtin_amdgcn_frexp_expf(mx), 100);   // |q*s| * 2^sh < 2^29
-            const float fs = __builtin_ldexpf(cls_div, sh);
+            const float ff = __builtin_ldexpf(csl, sh);
+            float sf[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sf[i] = s4[i] * ff;
 #pragma unroll
             for (int r = 0; r < NQ; ++r) {
                 uint32_t dg[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int qi = (int)(qw[r][i] * s4[i] * fs);   // truncated: off by less than 2^-29 of the largest
+                    // truncated: off by less than 2^-29 of the largest
+                    const int qi = (int)__builtin_fmaf(h2f(qp[r][i >> 1] >> (16 * (i & 1))), sf[i], kZero);
                     dg[i] = ((uint32_t)qi + 0x80808080u) ^ 0x80808080u;    // four signed base-256 digits
                 }
                 const uint32_t A = __builtin_amdgcn_perm(dg[1], dg[0], 0x05010400u);
@@ -203,6 +222,9 @@ __global__ __launch_bounds__(kBlock) void attn_gqa_kernel(AttnArgs a) {
                 plane[3 * kD / 4] = __builtin_amdgcn_perm(E, B, 0x07060302u);   // digit 3
             }
         }
+        // the largest value scale among this lane's loaded token (fp16 bit patterns: scales
+        // are never negative); every token's pairs are loaded by exactly one lane
+        const float smax = h2f(max_u16x2(max_u16x2(cur.vp.x, cur.vp.y), max_u16x2(cur.vp.z, cur.vp.w)) & 0xffffu);
         // value pairs of the 64 tokens, for the lanes that need another lane's token
         *reinterpret_cast<uint4*>(area + Lds::kPairOff + lane * 16) = cur.vp;
         load_vp(cur, nxt);
@@ -217,10 +239,13 @@ __global__ __launch_bounds__(kBlock) void attn_gqa_kernel(AttnArgs a) {
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
             kscale[g] = __builtin_ldexpf(1.0f, -__builtin_amdgcn_readlane(sh, 32 * g));
-            float z = readlane_f(az[0], 32 * g);
+            float zs[NQ];
 #pragma unroll
-            for (int r = 1; r < NQ; ++r) z = qh == r ? readlane_f(az[r], 32 * g) : z;
-            azq[g] = z;
+            for (int r = 0; r < NQ; ++r) zs[r] = readlane_f(az, 32 * g + q_lane(r));
+            float z = zs[0];
+#pragma unroll
+            for (int r = 1; r < NQ; ++r) z = qh == r ? zs[r] : z;
+            azq[g] = z * a.sm_log2;
         }
         float lg[4];
 #pragma unroll
@@ -263,18 +288,14 @@ __global__ __launch_bounds__(kBlock) void attn_gqa_kernel(AttnArgs a) {
             p[t] = lg[t] == -INFINITY ? 0.0f : exp2f(lg[t] - m);
             lsum += p[t];
         }
-        // value pairs of this lane's 4 tokens 16t + n: zero-point sums and the largest scale
-        // (taken on the fp16 bit patterns: scales are never negative)
-        uint32_t smw = 0;
+        // value pairs of this lane's 4 tokens 16t + n: zero-point sums
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const uint4 pq = *reinterpret_cast<const uint4*>(area + Lds::kPairOff + (16 * t + n) * 16);
             const uint32_t pw[4] = {pq.x, pq.y, pq.z, pq.w};
 #pragma unroll
             for (int k = 0; k < 4; ++k) zk[k] = fmaf(p[t], h2f(pw[k] >> 16), zk[k]);
-            smw = max_u16x2(smw, max_u16x2(max_u16x2(pw[0], pw[1]), max_u16x2(pw[2], pw[3])));
         }
-        const float smax = h2f(smw & 0xffffu);
         // value weights 16*p*s*vs must stay below 2^15: shrink vs (a power of two) if needed
         if (__builtin_amdgcn_ballot_w64(smax * vs > 2048.0f || vs == 0.0f)) {
             const float gm = wave_max_xor(smax, 1, 32);

@@ -96,6 +96,24 @@ __device__ __forceinline__ float mirror_f(float v) { return dpp_f<0x140>(v); }  
 __device__ __forceinline__ float xor16_f(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
 }
+__device__ __forceinline__ float ror4_f(float v) { return dpp_f<0x124>(v); }   // lane (i+4)%16 of the row
+__device__ __forceinline__ float ror8_f(float v) { return dpp_f<0x128>(v); }   // lane (i+8)%16 of the row
+// Sums over the 32 lanes of each half-wave of four values at once: afterwards the lane with
+// bits (b0, b1) = (lane & 1, (lane >> 1) & 1) holds the sum of v[2*b0 + b1].  Lanes first
+// exchange halves of their sets (lane^1, then lane^2), then sum the rest over lanes that
+// agree in their two low bits (row rotations by 4 and 8, then lane^16).
+__device__ __forceinline__ float half_sum4(const float (&v)[4]) {
+    const int lane = threadIdx.x & 63;
+    const bool b0 = lane & 1, b1 = lane & 2;
+    const float k0 = b0 ? v[2] : v[0], k1 = b0 ? v[3] : v[1];
+    const float s0 = b0 ? v[0] : v[2], s1 = b0 ? v[1] : v[3];
+    const float u0 = k0 + xor1_f(s0), u1 = k1 + xor1_f(s1);
+    const float kk = b1 ? u1 : u0, ss = b1 ? u0 : u1;
+    float x = kk + xor2_f(ss);
+    x += ror4_f(x);
+    x += ror8_f(x);
+    return x + xor16_f(x);
+}
 // sum / max over the 32 lanes of each half-wave (every lane gets its half's result)
 __device__ __forceinline__ float half_sum(float v) {
     v += xor1_f(v);
