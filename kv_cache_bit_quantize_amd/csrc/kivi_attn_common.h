@@ -1,8 +1,8 @@
 // kivi_attn_common.h -- pieces shared by the decode-attention kernels (gfx950).
 //
-// Every kernel keeps, per workgroup and query row, kSlots softmax states in the log2 domain
-// (m, l, o[128] with o relative to 2^m): one per wave for the quantized history and one per
-// wave for the fp16 residual.  finish_block() merges them (log-sum-exp), then either writes
+// Every kernel keeps, per workgroup and query row, 2 * (its waves) softmax states in the log2
+// domain (m, l, o[128] with o relative to 2^m): one per wave for the quantized history and
+// one per wave for the fp16 residual.  finish_block() merges them (log-sum-exp), then either writes
 // the output (one split) or a split partial; the last workgroup of a row to arrive merges
 // the partials and writes the output, so one launch does the whole call.
 #pragma once
@@ -12,8 +12,8 @@
 
 namespace kivi {
 
-constexpr int kWaves = kBlock / 64;
-constexpr int kSlots = 2 * kWaves;   // softmax states per workgroup and row: quantized, residual
+constexpr int kWaves = kBlock / 64;  // waves of the single-query kernel's workgroup
+constexpr int kSlots = 2 * kWaves;   // its softmax states per workgroup and row: quantized, residual
 constexpr int kPart = kD + 2;        // floats per split partial: o[128], m, l
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -97,7 +97,8 @@ __device__ __forceinline__ float load_coherent(float* p) {
 constexpr int kWaitVmcnt0 = 0x0F70;
 
 // Softmax states of query rows qrow0..qrow0+NQ-1 over the fp16 residual ring.  Called by one
-// whole wave; wave w takes the ring's logical tokens [32w + 128i, 32w + 128i + 32).  Per such
+// whole wave of a WAVES-wave workgroup; wave w takes the ring's logical tokens
+// [32w + 32*WAVES*i, 32w + 32*WAVES*i + 32).  Per such
 // chunk, two phases:
 //  * logits: lane 4*tp + qq holds tokens 2tp, 2tp+1 and channels [32qq, 32qq+32) and forms
 //    q.k with v_dot2_f32_f16 on packed halves for every row; the chunk's probabilities go to
@@ -108,7 +109,7 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 // Row r's o (relative to 2^m[r]) ends in o_dst[r*o_stride + c]; m[r] = -inf and l[r] = 0 when
 // the wave has no residual token.  In a fused decode step the last residual token is the new
 // one, read from k_new / v_new.
-template <int NQ>
+template <int NQ, int WAVES = kWaves>
 __device__ void residual_states(const AttnArgs& a, int64_t qrow0, int64_t kvrow, int wave, float* o_dst,
                                 int o_stride, float (&mr)[NQ], float (&lr)[NQ]) {
     const int lane = threadIdx.x & 63, tp = lane >> 2, qq = lane & 3;
@@ -121,7 +122,7 @@ __device__ void residual_states(const AttnArgs& a, int64_t qrow0, int64_t kvrow,
     }
     auto token_slot = [&](int i) { return (a.res_head + i) % a.residual_cap; };
     auto is_new = [&](int i) { return a.k_new != nullptr && i == a.n_res - 1; };
-    for (int base = wave * kG; base < a.n_res; base += kWaves * kG) {
+    for (int base = wave * kG; base < a.n_res; base += WAVES * kG) {
         // ---- logits of tokens 2tp, 2tp+1 for every row
         const int i0 = base + 2 * tp, i1 = i0 + 1;
         const bool ok0 = i0 < a.n_res, ok1 = i1 < a.n_res;
@@ -231,13 +232,14 @@ __device__ __forceinline__ void store_new_token(const AttnArgs& a, int64_t kvrow
 // pairs combine in LDS.  out = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M),
 // lse = (M + log2 L) ln 2.  Re-arms the arrival counter.
 constexpr int kMergeBatch = 16;
-template <int NQ>
+template <int NQ, int THREADS = kBlock>
 __device__ __forceinline__ void merge_rows(const AttnArgs& a, int64_t qrow0, int64_t counter) {
     constexpr int kLpp = NQ == 1 ? 2 : 1;
+    static_assert(kLpp == 1 || THREADS == 2 * kD, "two threads per channel need 256 threads");
     __shared__ float sh_mo[kD + 2];
     const int t = threadIdx.x, sub = kLpp == 2 ? (t >> 7) : 0;
     const int64_t stride = a.q_rows * kPart;
-    for (int idx = kLpp == 2 ? (t & (kD - 1)) : t; idx < NQ * kD; idx += kBlock / kLpp) {
+    for (int idx = kLpp == 2 ? (t & (kD - 1)) : t; idx < NQ * kD; idx += THREADS / kLpp) {
         const int r = idx / kD, j = idx % kD;
         float* rowp = a.ws + (qrow0 + r) * kPart;
         float M = -INFINITY, L = 0.0f, O = 0.0f;
@@ -288,23 +290,24 @@ __device__ __forceinline__ void merge_rows(const AttnArgs& a, int64_t qrow0, int
     if (t == 0) a.counters[counter] = 0u;
 }
 
-// End of a workgroup: merge its kSlots states per row (empty states skipped), then write the
+// End of a WAVES-wave workgroup: merge its 2*WAVES states per row (empty states skipped), then write the
 // output directly (one split) or the split partial, and let the last workgroup of the row
 // group to arrive merge the partials.  The counter add comes after every partial store of
 // this workgroup completed (the wait, then the barrier), and the merging workgroup issues its
 // coherent loads only after its own add returned the final count, so it reads every partial.
-template <int NQ>
+template <int NQ, int WAVES = kWaves>
 __device__ __forceinline__ void finish_block(const AttnArgs& a, int split, int64_t qrow0, int64_t counter,
-                                             const float (*sh_o)[kSlots][kD], const float (*sh_m)[kSlots],
-                                             const float (*sh_l)[kSlots]) {
-    for (int idx = threadIdx.x; idx < NQ * kD; idx += kBlock) {
+                                             const float (*sh_o)[2 * WAVES][kD], const float (*sh_m)[2 * WAVES],
+                                             const float (*sh_l)[2 * WAVES]) {
+    constexpr int kS = 2 * WAVES;
+    for (int idx = threadIdx.x; idx < NQ * kD; idx += 64 * WAVES) {
         const int r = idx / kD, j = idx % kD;
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < kSlots; ++w) M = fmaxf(M, sh_m[r][w]);
+        for (int w = 0; w < kS; ++w) M = fmaxf(M, sh_m[r][w]);
         float L = 0.0f, O = 0.0f;
 #pragma unroll
-        for (int w = 0; w < kSlots; ++w) {
+        for (int w = 0; w < kS; ++w) {
             if (sh_m[r][w] == -INFINITY) continue;
             const float sc = exp2f(sh_m[r][w] - M);
             L = fmaf(sh_l[r][w], sc, L);
@@ -330,7 +333,7 @@ __device__ __forceinline__ void finish_block(const AttnArgs& a, int split, int64
         sh_last = __hip_atomic_fetch_add(&a.counters[counter], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
                   (unsigned)(a.splits - 1);
     __syncthreads();
-    if (sh_last) merge_rows<NQ>(a, qrow0, counter);
+    if (sh_last) merge_rows<NQ, 64 * WAVES>(a, qrow0, counter);
 }
 
 }  // namespace kivi

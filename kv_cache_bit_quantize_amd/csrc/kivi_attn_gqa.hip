@@ -31,13 +31,19 @@ struct GqaLds {
     static constexpr int kZeroBytes = kKeyGroup + 256;  // covers every offset a zero row reads at
 };
 
+// Four waves per workgroup (six, at two workgroups per compute unit, measured slower).  The
+// kernel is built for three waves per SIMD.
+constexpr int kGqaWaves = 4;
+constexpr int kGqaBlock = 64 * kGqaWaves;
+
 template <int NQ>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) void attn_gqa_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kGqaBlock) __attribute__((amdgpu_waves_per_eu(3))) void attn_gqa_kernel(AttnArgs a) {
     using Lds = GqaLds<NQ>;
-    __shared__ __align__(16) uint8_t sh_area[kWaves][Lds::kBytes];
+    constexpr int W = kGqaWaves, S = 2 * kGqaWaves;
+    __shared__ __align__(16) uint8_t sh_area[W][Lds::kBytes];
     __shared__ __align__(16) uint8_t sh_zero[Lds::kZeroBytes];
-    __shared__ __align__(16) float sh_o[NQ][kSlots][kD];
-    __shared__ float sh_m[NQ][kSlots], sh_l[NQ][kSlots];
+    __shared__ __align__(16) float sh_o[NQ][S][kD];
+    __shared__ float sh_m[NQ][S], sh_l[NQ][S];
 
     const int split = blockIdx.x;
     const int64_t grow = blockIdx.y;                 // (batch, kv head, query chunk)
@@ -55,7 +61,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     const bool qlive = qh < NQ;
     uint8_t* area = &sh_area[wave][0];
 
-    for (int i = threadIdx.x; i < Lds::kZeroBytes / 16; i += kBlock)
+    for (int i = threadIdx.x; i < Lds::kZeroBytes / 16; i += kGqaBlock)
         reinterpret_cast<uint4*>(sh_zero)[i] = make_uint4(0, 0, 0, 0);
 
     // query channels 4wl..4wl+3 of the NQ queries as packed fp16 pairs (4wl, 4wl+1 and
@@ -111,7 +117,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     const int g_lo = split * a.groups_per_split;
     const int g_hi = min(n_groups, g_lo + a.groups_per_split);
     const int cnt = max(0, g_hi - g_lo);
-    const int per_wave = (cnt + kWaves - 1) / kWaves;
+    const int per_wave = (cnt + W - 1) / W;
     const int gb = g_lo + min(cnt, wave * per_wave);
     const int ge = g_lo + min(cnt, (wave + 1) * per_wave);
     const int iters = (ge - gb + 1) >> 1;
@@ -154,8 +160,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     __syncthreads();   // the zero area is written
     // Two register sets of loads, used by alternate iterations: each stream reloads its set
     // for two iterations ahead right after its last use, so every load has more than an
-    // iteration to arrive (a kv head's query group keeps the grid at two waves per SIMD,
-    // so the registers are there).
+    // iteration to arrive (one workgroup per KV head leaves a 512-head batch at about two
+    // waves per SIMD, so the deeper prefetch is what hides the memory latency).
     constexpr int kPrefetch = 2;
     auto load_all = [&](Loads& L, int it) {
         load_kp(L, it);
@@ -381,7 +387,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     __builtin_amdgcn_sched_barrier(0);
     float mr[NQ], lr[NQ];
     if (split == a.splits - 1) {
-        residual_states<NQ>(a, qrow0, kvrow, wave, &sh_o[0][kWaves + wave][0], kSlots * kD, mr, lr);
+        residual_states<NQ, W>(a, qrow0, kvrow, wave, &sh_o[0][W + wave][0], S * kD, mr, lr);
     } else {
 #pragma unroll
         for (int r = 0; r < NQ; ++r) {
@@ -392,20 +398,20 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     if (lane == 0) {
 #pragma unroll
         for (int r = 0; r < NQ; ++r) {
-            sh_m[r][kWaves + wave] = mr[r];
-            sh_l[r][kWaves + wave] = lr[r];
+            sh_m[r][W + wave] = mr[r];
+            sh_l[r][W + wave] = lr[r];
         }
     }
     __syncthreads();
-    finish_block<NQ>(a, split, qrow0, grow, sh_o, sh_m, sh_l);
+    finish_block<NQ, W>(a, split, qrow0, grow, sh_o, sh_m, sh_l);
 }
 
 hipError_t launch_decode_attn_gqa(const AttnArgs& a, hipStream_t s) {
     const dim3 grid((unsigned)a.splits, (unsigned)a.block_rows);
     switch (a.nq) {
-        case 2: hipLaunchKernelGGL(attn_gqa_kernel<2>, grid, dim3(kBlock), 0, s, a); break;
-        case 3: hipLaunchKernelGGL(attn_gqa_kernel<3>, grid, dim3(kBlock), 0, s, a); break;
-        case 4: hipLaunchKernelGGL(attn_gqa_kernel<4>, grid, dim3(kBlock), 0, s, a); break;
+        case 2: hipLaunchKernelGGL(attn_gqa_kernel<2>, grid, dim3(kGqaBlock), 0, s, a); break;
+        case 3: hipLaunchKernelGGL(attn_gqa_kernel<3>, grid, dim3(kGqaBlock), 0, s, a); break;
+        case 4: hipLaunchKernelGGL(attn_gqa_kernel<4>, grid, dim3(kGqaBlock), 0, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
