@@ -27,7 +27,6 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 D, G = 128, 32
 QUANT_TOKEN_BYTES = 96         # per kv head: 32 B key codes + 16 B key pairs + 32 B value codes + 16 B value pairs
 RES_TOKEN_BYTES = 512          # per kv head: fp16 key + value
-EVENT_EVERY = 3                # steps bracketed by HIP events: 0, 3, 6, ...
 def counters_file(workload):
     return os.path.join(ROOT, "profiles", f"decode_attn_{workload}_counters.json")
 
@@ -147,45 +146,45 @@ def main():
     torch.cuda.synchronize()
 
     def step(s, ev=None):
-        if ev is not None:
-            ev[0].record()
         if args.separate:
             f = kivi.kivi_append_flush(cache, *steps_kv[s])
             if ev is not None:
-                ev[1].record()
+                kivi.kivi_time_next_attention(*ev)
             kivi.kivi_decode_attn(cache, queries[s], synth.SM_SCALE_D128, out=out, num_splits=args.splits,
                                   workspace=ws)
         else:
             if ev is not None:
-                ev[1].record()
+                kivi.kivi_time_next_attention(*ev)
             _, f = kivi.kivi_decode_step(cache, *steps_kv[s], queries[s], synth.SM_SCALE_D128, out=out,
                                          num_splits=args.splits, workspace=ws)
-        if ev is not None:
-            ev[2].record()
         return f, cache.state
 
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
 
-    # Every EVENT_EVERY-th step is bracketed by HIP events on the launch stream (each marker
-    # costs the stream a few microseconds, so the other steps carry none); the attention
-    # launch duration is [ev1, ev2] of those steps: the attention call, or with the fused
-    # step on a step without flush its one launch.
-    timed = set(range(0, args.steps, EVENT_EVERY))
-    evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for i in timed}
+    # Every timed step's attention kernel records its own start and end in a pair of HIP
+    # events, taken by the kernel's dispatch on the launch stream (kivi_time_next_attention:
+    # no marker command enters the stream).  The events are created by one record each,
+    # before the timed region.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for pair in evs:
+        for e in pair:
+            e.record()
     flags, states = [], []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        f, st = step(args.warmup + i, evs.get(i))
+        f, st = step(args.warmup + i, evs[i])
         flags.append(f)
         states.append(st)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    one_launch = [i for i in sorted(timed) if args.separate or not flags[i]]
-    attn_ms = np.array([evs[i][1].elapsed_time(evs[i][2]) for i in one_launch])
+    # the fused kernel (attention with the append) on steps without a flush; every attention
+    # launch with --separate
+    one_launch = [i for i in range(args.steps) if args.separate or not flags[i]]
+    attn_ms = np.array([evs[i][0].elapsed_time(evs[i][1]) for i in one_launch])
     step_bytes = [attn_bytes(w, nq, nr) + append_bytes(w, f) for f, (nq, nr, _) in zip(flags, states)]
     value = sum(step_bytes) / elapsed / 1e9
     launch_b = [attn_bytes(w, *states[i][:2]) + (0 if args.separate else append_bytes(w, False)) for i in one_launch]
@@ -216,6 +215,7 @@ def main():
         "step_path": "separate append_flush + decode_attn" if args.separate else "fused decode_step",
         "decode_attn_us": round(float(attn_ms.mean()) * 1e3, 2),
         "event_timed_launches": len(one_launch),
+        "attn_timing": "kernel start and end recorded by the dispatch (hipExtLaunchKernel events)",
         "flush_steps": int(sum(bool(f) for f in flags)),
         "roofline": {
             "bound": "hbm",

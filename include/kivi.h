@@ -155,6 +155,16 @@ int kivi_decode_step(kivi_cache* cache, const uint16_t* k_new, const uint16_t* v
                      void* workspace, size_t workspace_bytes, int32_t num_splits, int32_t* flushed,
                      void* stream);
 
+/* Measurement hook, for callers that time the attention kernel itself (not a step of the
+ * method).  The next decode-attention kernel that kivi_decode_attn or kivi_decode_step
+ * launches from the calling thread records its own start in start_event and its end in
+ * stop_event (hipEvent_t handles, created by the caller with timing enabled), taken by the
+ * dispatch itself with no marker command in the stream, so hipEventElapsedTime(start, stop)
+ * is that kernel's duration.  The setting is consumed by that one launch (a flush kernel
+ * launched before it by kivi_decode_step is not timed); both NULL clears it.
+ * KIVI_ERR_NULL if exactly one of the two is NULL.  No device access. */
+int kivi_time_next_attention(void* start_event, void* stop_event);
+
 /* Host-only helpers (no device access; safe without a GPU). */
 
 /* Split count that kivi_decode_attn uses for num_splits == 0 (depends on shapes only).

@@ -211,6 +211,14 @@ int prepare_attn(const kivi_cache* c, const uint16_t* q, int32_t q_heads, float 
     return KIVI_OK;
 }
 
+// Events for the next attention launch of this thread (kivi_time_next_attention).
+thread_local hipEvent_t t_timing[2] = {nullptr, nullptr};
+void take_timing(hipEvent_t* t0, hipEvent_t* t1) {
+    *t0 = t_timing[0];
+    *t1 = t_timing[1];
+    t_timing[0] = t_timing[1] = nullptr;
+}
+
 }  // namespace
 
 extern "C" {
@@ -339,12 +347,21 @@ size_t kivi_decode_attn_workspace(const kivi_cache* c, int32_t q_heads, int32_t 
     return counter_bytes(c, q_heads) + ((bytes + 255) & ~(size_t)255);
 }
 
+int kivi_time_next_attention(void* start_event, void* stop_event) {
+    if ((start_event == nullptr) != (stop_event == nullptr)) return KIVI_ERR_NULL;
+    t_timing[0] = static_cast<hipEvent_t>(start_event);
+    t_timing[1] = static_cast<hipEvent_t>(stop_event);
+    return KIVI_OK;
+}
+
 int kivi_decode_attn(const kivi_cache* c, const uint16_t* q, int32_t q_heads, float sm_scale, uint16_t* out,
                      float* lse, void* workspace, size_t workspace_bytes, int32_t num_splits, void* stream) {
     AttnArgs a;
     const int st = prepare_attn(c, q, q_heads, sm_scale, out, lse, workspace, workspace_bytes, num_splits, &a);
     if (st != KIVI_OK) return st;
-    return hip_status(launch_decode_attn(a, (hipStream_t)stream));
+    hipEvent_t t0, t1;
+    take_timing(&t0, &t1);
+    return hip_status(launch_decode_attn(a, (hipStream_t)stream, t0, t1));
 }
 
 int kivi_decode_step(kivi_cache* c, const uint16_t* k_new, const uint16_t* v_new, const uint16_t* q,
@@ -368,7 +385,9 @@ int kivi_decode_step(kivi_cache* c, const uint16_t* k_new, const uint16_t* v_new
         at.v_ring = c->v_res;
         at.new_slot = ap.new_slot;
     }
-    if ((st = hip_status(launch_decode_attn(at, (hipStream_t)stream))) != KIVI_OK) return st;
+    hipEvent_t t0, t1;
+    take_timing(&t0, &t1);
+    if ((st = hip_status(launch_decode_attn(at, (hipStream_t)stream, t0, t1))) != KIVI_OK) return st;
     commit_state(c, next);
     if (flushed != nullptr) *flushed = ap.do_flush;
     return KIVI_OK;

@@ -32,6 +32,8 @@
 //    exponent reads 1.0 (the exact halves 1 + c/4, 1 + c/16); the weights carry the
 //    matching factor 4 or 16 and a power of two keeping them in fp16 range.  The constant
 //    part, the sum of the weights, is accumulated on the side and subtracted at the end.
+#include <hip/hip_ext.h>
+
 #include "kivi_attn_common.h"
 
 namespace kivi {
@@ -307,9 +309,10 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
     finish_block<1>(a, split, qrow, qrow, sh_o, sh_m, sh_l);
 }
 
-hipError_t launch_decode_attn(const AttnArgs& a, hipStream_t s) {
-    if (a.nq > 1) return launch_decode_attn_gqa(a, s);
-    hipLaunchKernelGGL(attn_split_kernel, dim3((unsigned)a.splits, (unsigned)a.q_rows), dim3(kBlock), 0, s, a);
+hipError_t launch_decode_attn(const AttnArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+    if (a.nq > 1) return launch_decode_attn_gqa(a, s, t0, t1);
+    hipExtLaunchKernelGGL(attn_split_kernel, dim3((unsigned)a.splits, (unsigned)a.q_rows), dim3(kBlock), 0, s, t0, t1,
+                          0, a);
     return hipGetLastError();
 }
 

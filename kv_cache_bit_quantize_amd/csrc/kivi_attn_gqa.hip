@@ -17,6 +17,8 @@
 //
 // Split-K, the residual, the per-query online softmax (log2 domain) and the merge follow
 // the single-query kernel (kivi_attn.hip, kivi_attn_common.h).
+#include <hip/hip_ext.h>
+
 #include "kivi_attn_common.h"
 
 namespace kivi {
@@ -406,12 +408,12 @@ __global__ __launch_bounds__(kGqaBlock) __attribute__((amdgpu_waves_per_eu(3))) 
     finish_block<NQ, W>(a, split, qrow0, grow, sh_o, sh_m, sh_l);
 }
 
-hipError_t launch_decode_attn_gqa(const AttnArgs& a, hipStream_t s) {
+hipError_t launch_decode_attn_gqa(const AttnArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
     const dim3 grid((unsigned)a.splits, (unsigned)a.block_rows);
     switch (a.nq) {
-        case 2: hipLaunchKernelGGL(attn_gqa_kernel<2>, grid, dim3(kGqaBlock), 0, s, a); break;
-        case 3: hipLaunchKernelGGL(attn_gqa_kernel<3>, grid, dim3(kGqaBlock), 0, s, a); break;
-        case 4: hipLaunchKernelGGL(attn_gqa_kernel<4>, grid, dim3(kGqaBlock), 0, s, a); break;
+        case 2: hipExtLaunchKernelGGL(attn_gqa_kernel<2>, grid, dim3(kGqaBlock), 0, s, t0, t1, 0, a); break;
+        case 3: hipExtLaunchKernelGGL(attn_gqa_kernel<3>, grid, dim3(kGqaBlock), 0, s, t0, t1, 0, a); break;
+        case 4: hipExtLaunchKernelGGL(attn_gqa_kernel<4>, grid, dim3(kGqaBlock), 0, s, t0, t1, 0, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

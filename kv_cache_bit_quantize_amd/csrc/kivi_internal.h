@@ -79,7 +79,9 @@ hipError_t launch_quantize_k(const QuantArgs& a, hipStream_t s);
 hipError_t launch_quantize_v(const QuantArgs& a, hipStream_t s);
 hipError_t launch_residual_load(const ResidualArgs& a, hipStream_t s);
 hipError_t launch_append_flush(const AppendArgs& a, hipStream_t s);
-hipError_t launch_decode_attn(const AttnArgs& a, hipStream_t s);
-hipError_t launch_decode_attn_gqa(const AttnArgs& a, hipStream_t s);
+// t0 / t1 (nullable): events that record the kernel's own start and end (hipExtLaunchKernel)
+hipError_t launch_decode_attn(const AttnArgs& a, hipStream_t s, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
+hipError_t launch_decode_attn_gqa(const AttnArgs& a, hipStream_t s, hipEvent_t t0 = nullptr,
+                                  hipEvent_t t1 = nullptr);
 
 }  // namespace kivi

@@ -18,7 +18,7 @@ _STATUS_NAMES = {0: "KIVI_OK", -1: "KIVI_ERR_NULL", -2: "KIVI_ERR_SHAPE", -3: "K
 
 EXPORTS = ["kivi_quantize_k_per_channel", "kivi_quantize_v_per_token", "kivi_prefill", "kivi_append_flush",
            "kivi_decode_attn", "kivi_decode_step", "kivi_decode_attn_splits", "kivi_decode_attn_workspace", "kivi_cache_bytes",
-           "kivi_status_str"]
+           "kivi_status_str", "kivi_time_next_attention"]
 
 
 class KiviError(RuntimeError):
@@ -54,6 +54,7 @@ def _load():
     L.kivi_decode_attn_workspace.restype = C.c_size_t
     L.kivi_cache_bytes.argtypes = [cp, C.POINTER(C.c_size_t), C.POINTER(C.c_size_t), C.POINTER(C.c_size_t)]
     L.kivi_status_str.argtypes = [C.c_int]
+    L.kivi_time_next_attention.argtypes = [p, p]
     L.kivi_status_str.restype = C.c_char_p
     for name in EXPORTS:
         L[name].restype = L[name].restype if name in ("kivi_decode_attn_splits", "kivi_decode_attn_workspace",
@@ -199,6 +200,22 @@ def kivi_decode_attn_splits(cache, q_heads):
     if s < 0:
         raise KiviError(s, "kivi_decode_attn_splits")
     return s
+
+
+def kivi_time_next_attention(start=None, stop=None):
+    """The next attention kernel launched from this thread by kivi_decode_attn or
+    kivi_decode_step records its own start and end in two torch.cuda.Event(enable_timing=True)
+    objects; start.elapsed_time(stop) is then that kernel's duration in ms.  The events must
+    already exist on the device (record each once before); None, None clears the setting."""
+    handles = []
+    for ev in (start, stop):
+        if ev is None:
+            handles.append(None)
+            continue
+        if not ev.cuda_event:
+            raise ValueError("record the event once before passing it (it is created on first record)")
+        handles.append(C.c_void_p(ev.cuda_event))
+    _check(lib.kivi_time_next_attention(*handles), "kivi_time_next_attention")
 
 
 def kivi_decode_attn_workspace(cache, q_heads, num_splits=0):

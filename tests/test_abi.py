@@ -21,7 +21,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 10
+    assert len(names) == 11
     out = os.popen(f"nm -D --defined-only {kivi.LIB_PATH}").read()
     exported = set(re.findall(r" T (kivi_\w+)$", out, re.M))
     assert set(names) <= exported, set(names) - exported
@@ -42,6 +42,13 @@ def _cache(**kw):
 
 def _state(c):
     return c.n_quant, c.n_res, c.res_head
+
+
+def test_time_next_attention_arguments():
+    # no device access: the call only stores the two handles for the next attention launch
+    assert L.kivi_time_next_attention(None, C.c_void_p(FAKE)) == -1      # KIVI_ERR_NULL
+    assert L.kivi_time_next_attention(C.c_void_p(FAKE), None) == -1
+    assert L.kivi_time_next_attention(None, None) == kivi.KIVI_OK
 
 
 def test_status_strings():

@@ -123,6 +123,32 @@ def test_gqa_query_groups(q_heads, kv_heads, n_quant, n_res, splits):
     _check(cache, rc, q, splits=splits, what=f"gqa {q_heads}/{kv_heads}")
 
 
+@pytest.mark.parametrize("q_heads,kv_heads", [(4, 4), (8, 2)])
+def test_timed_launch_matches_untimed(q_heads, kv_heads):
+    """kivi_time_next_attention: the timed launch (hipExtLaunchKernel with the caller's events)
+    gives the same bytes as an untimed one and a positive kernel duration; the setting is
+    used by one launch only."""
+    dev = gpu_or_skip()
+    kivi = _kivi()
+    w = synth.small(seed=11, batch=2, q_heads=q_heads, kv_heads=kv_heads, context=1024 + 40, n_quant=1024)
+    cache, rc, q = _setup(w, dev)
+    plain, _ = _run(cache, q, lse=False)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for e in ev:
+        e.record()
+    torch.cuda.synchronize()
+    kivi.kivi_time_next_attention(*ev)
+    timed, _ = _run(cache, q, lse=False)
+    ms = ev[0].elapsed_time(ev[1])
+    assert torch.equal(timed, plain)
+    assert 0.0 < ms < 1000.0, ms
+    again, _ = _run(cache, q, lse=False)   # not timed: the events keep the first launch's times
+    assert torch.equal(again, plain)
+    assert ev[0].elapsed_time(ev[1]) == ms
+    with pytest.raises(ValueError):
+        kivi.kivi_time_next_attention(torch.cuda.Event(enable_timing=True), ev[1])
+
+
 def test_split_count_does_not_change_the_result():
     dev = gpu_or_skip()
     w = synth.small(seed=7, batch=1, q_heads=4, kv_heads=4, context=4096 + 50, n_quant=4096, outliers=0)
