@@ -9,6 +9,9 @@ times the two separate calls kivi_append_flush + kivi_decode_attn instead.  Inpu
 seeded synthetic tensors already resident in HBM when the timed region starts.
 
 Prints ONE JSON line.  Metric: achieved HBM GB/s (algorithmic bytes / time) and tokens/s.
+After the timed steps, the fp16 comparator (kivi_decode_attn_fp16: the same attention over
+an uncompressed fp16 cache of the starting context) is timed the same way and reported
+beside it ("fp16_comparator"; --no-fp16 skips it).
 """
 import argparse
 import json
@@ -120,6 +123,7 @@ def main():
     ap.add_argument("--cpu-threads", type=int, default=16, help="host threads for the CPU oracle sample")
     ap.add_argument("--splits", type=int, default=0, help="split count override (0: library's choice)")
     ap.add_argument("--separate", action="store_true", help="time kivi_append_flush + kivi_decode_attn")
+    ap.add_argument("--no-fp16", action="store_true", help="skip the fp16 comparator")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the decode hot path shards "
@@ -190,6 +194,33 @@ def main():
     launch_b = [attn_bytes(w, *states[i][:2]) + (0 if args.separate else append_bytes(w, False)) for i in one_launch]
     achieved = float(np.mean(launch_b)) / (attn_ms.mean() / 1e3) / 1e9
     splits = kivi.kivi_decode_attn_splits(cache, w.q_heads) if args.splits == 0 else args.splits
+
+    # fp16 comparator: kivi_decode_attn_fp16 over the prefill's own fp16 keys and values (the
+    # context the timed steps start from), the same queries, every launch timed the same way
+    fp16 = None
+    if not args.no_fp16:
+        ws16 = torch.zeros(max(kivi.kivi_decode_attn_fp16_workspace(w.batch, w.kv_heads, w.context, w.q_heads), 256),
+                           dtype=torch.uint8, device=dev)
+        for s in range(args.warmup):
+            kivi.kivi_decode_attn_fp16(k, v, queries[s], synth.SM_SCALE_D128, out=out, workspace=ws16)
+        ev16 = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for pair in ev16:
+            for e in pair:
+                e.record()
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            kivi.kivi_time_next_attention(*ev16[i])
+            kivi.kivi_decode_attn_fp16(k, v, queries[args.warmup + i], synth.SM_SCALE_D128, out=out, workspace=ws16)
+        torch.cuda.synchronize()
+        us16 = float(np.mean([a.elapsed_time(b) for a, b in ev16])) * 1e3
+        b16 = w.batch * w.kv_heads * w.context * RES_TOKEN_BYTES + 2 * w.batch * w.q_heads * D * 2
+        fp16 = {
+            "kernel": "attn_fp16_kernel", "tokens": w.context,
+            "splits": kivi.kivi_decode_attn_fp16_splits(w.batch, w.kv_heads, w.context, w.q_heads),
+            "decode_attn_us": round(us16, 2), "bytes_per_launch": b16,
+            "achieved": round(b16 / us16 / 1e3, 1), "unit": "GB/s", "frac": round(b16 / us16 / 1e3 / PEAK_HBM_GBS, 4),
+            "speedup_of_2bit": round(us16 / float(attn_ms.mean() * 1e3), 2),
+        }
     kernel = "attn_split_kernel" if w.q_heads == w.kv_heads else "attn_gqa_kernel"
 
     res = {
@@ -228,6 +259,7 @@ def main():
             "algorithmic_bytes_per_launch": int(np.mean(launch_b)),
         },
         "cpu_baseline": None,
+        "fp16_comparator": fp16,
     }
     if args.cpu_heads > 0:
         kn, vn = steps_kv[0]

@@ -155,6 +155,22 @@ int kivi_decode_step(kivi_cache* cache, const uint16_t* k_new, const uint16_t* v
                      void* workspace, size_t workspace_bytes, int32_t num_splits, int32_t* flushed,
                      void* stream);
 
+/* fp16 comparator (a measurement baseline, not the method): decode attention of one query
+ * per head over a plain fp16 KV cache, the uncompressed cache the pages set the 2-bit
+ * cache against (record "KV bytes basis": the 16-bit cache's bytes per token; "Methodology":
+ * the throughput claim against the 16-bit baseline), on the same harness: same query
+ * grouping, split-K and merge as kivi_decode_attn.
+ * k, v: fp16 [batch][kv_heads][token_stride][128], tokens [0, tokens) of each row used,
+ * 16-byte aligned, owned by the caller.  q, out, lse, workspace (at least
+ * kivi_decode_attn_fp16_workspace(...) bytes, 256-byte aligned, leading arrival counters
+ * zero before first use and left zero), num_splits (0 = automatic) and stream as in
+ * kivi_decode_attn.  KIVI_ERR_SHAPE if tokens < 1, tokens > token_stride, q_heads is not a
+ * multiple of kv_heads or a pointer is misaligned. */
+int kivi_decode_attn_fp16(const uint16_t* k, const uint16_t* v, int32_t batch, int32_t kv_heads,
+                          int32_t tokens, int32_t token_stride, const uint16_t* q, int32_t q_heads,
+                          float sm_scale, uint16_t* out, float* lse, void* workspace,
+                          size_t workspace_bytes, int32_t num_splits, void* stream);
+
 /* Measurement hook, for callers that time the attention kernel itself (not a step of the
  * method).  The next decode-attention kernel that kivi_decode_attn or kivi_decode_step
  * launches from the calling thread records its own start in start_event and its end in
@@ -173,6 +189,12 @@ int32_t kivi_decode_attn_splits(const kivi_cache* cache, int32_t q_heads);
 
 /* Workspace bytes kivi_decode_attn needs for this shape and split count (0 = auto). */
 size_t kivi_decode_attn_workspace(const kivi_cache* cache, int32_t q_heads, int32_t num_splits);
+
+/* Split count and workspace bytes of kivi_decode_attn_fp16 for this shape (0 = auto
+ * splits); a negative KIVI_ERR_* code / 0 for an invalid shape. */
+int32_t kivi_decode_attn_fp16_splits(int32_t batch, int32_t kv_heads, int32_t tokens, int32_t q_heads);
+size_t kivi_decode_attn_fp16_workspace(int32_t batch, int32_t kv_heads, int32_t tokens, int32_t q_heads,
+                                       int32_t num_splits);
 
 /* Buffer sizes (bytes) for a cache of this shape (pointer fields are ignored):
  * codes = k_codes + v_codes, pairs = k_sz + v_sz, residual = k_res + v_res. */

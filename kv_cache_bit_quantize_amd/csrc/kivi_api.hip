@@ -211,6 +211,36 @@ int prepare_attn(const kivi_cache* c, const uint16_t* q, int32_t q_heads, float 
     return KIVI_OK;
 }
 
+// ---- fp16 comparator
+constexpr int kMinTokensPerSplit = 256;
+
+int64_t fp16_block_rows(int32_t batch, int32_t kv_heads, int32_t q_heads) {
+    const int32_t ratio = q_heads / kv_heads;
+    const int32_t nq = queries_per_block(ratio);
+    return nq > 1 ? (int64_t)batch * kv_heads * (ratio / nq) : (int64_t)batch * q_heads;
+}
+
+int fp16_check(int32_t batch, int32_t kv_heads, int32_t tokens, int32_t q_heads) {
+    if (batch <= 0 || kv_heads <= 0 || q_heads <= 0 || q_heads % kv_heads != 0) return KIVI_ERR_SHAPE;
+    if (tokens <= 0) return KIVI_ERR_SHAPE;
+    return KIVI_OK;
+}
+
+int32_t fp16_auto_splits(int32_t batch, int32_t kv_heads, int32_t tokens, int32_t q_heads) {
+    const int64_t rows = fp16_block_rows(batch, kv_heads, q_heads);
+    const int64_t target = queries_per_block(q_heads / kv_heads) > 1 ? kTargetBlocksGroup : kTargetBlocks;
+    int64_t s = (target + rows - 1) / rows;
+    const int64_t cap = tokens / kMinTokensPerSplit;
+    if (s > cap) s = cap;
+    if (s < 1) s = 1;
+    if (s > kMaxSplits) s = kMaxSplits;
+    return (int32_t)s;
+}
+
+size_t fp16_counter_bytes(int32_t batch, int32_t q_heads) {
+    return ((size_t)batch * (size_t)q_heads * sizeof(uint32_t) + 255) & ~(size_t)255;
+}
+
 // Events for the next attention launch of this thread (kivi_time_next_attention).
 thread_local hipEvent_t t_timing[2] = {nullptr, nullptr};
 void take_timing(hipEvent_t* t0, hipEvent_t* t1) {
@@ -345,6 +375,60 @@ size_t kivi_decode_attn_workspace(const kivi_cache* c, int32_t q_heads, int32_t 
     const int32_t s = num_splits > 0 ? num_splits : auto_splits(c, q_heads);
     const size_t bytes = (size_t)s * (size_t)c->batch * (size_t)q_heads * (size_t)(c->head_dim + 2) * sizeof(float);
     return counter_bytes(c, q_heads) + ((bytes + 255) & ~(size_t)255);
+}
+
+int32_t kivi_decode_attn_fp16_splits(int32_t batch, int32_t kv_heads, int32_t tokens, int32_t q_heads) {
+    const int st = fp16_check(batch, kv_heads, tokens, q_heads);
+    if (st != KIVI_OK) return st;
+    return fp16_auto_splits(batch, kv_heads, tokens, q_heads);
+}
+
+size_t kivi_decode_attn_fp16_workspace(int32_t batch, int32_t kv_heads, int32_t tokens, int32_t q_heads,
+                                       int32_t num_splits) {
+    if (fp16_check(batch, kv_heads, tokens, q_heads) != KIVI_OK || num_splits < 0) return 0;
+    const int32_t s = num_splits > 0 ? num_splits : fp16_auto_splits(batch, kv_heads, tokens, q_heads);
+    const size_t bytes = (size_t)s * (size_t)batch * (size_t)q_heads * (size_t)(kD + 2) * sizeof(float);
+    return fp16_counter_bytes(batch, q_heads) + ((bytes + 255) & ~(size_t)255);
+}
+
+int kivi_decode_attn_fp16(const uint16_t* k, const uint16_t* v, int32_t batch, int32_t kv_heads, int32_t tokens,
+                          int32_t token_stride, const uint16_t* q, int32_t q_heads, float sm_scale, uint16_t* out,
+                          float* lse, void* workspace, size_t workspace_bytes, int32_t num_splits, void* stream) {
+    if (k == nullptr || v == nullptr || q == nullptr || out == nullptr) return KIVI_ERR_NULL;
+    int st = fp16_check(batch, kv_heads, tokens, q_heads);
+    if (st != KIVI_OK) return st;
+    if (token_stride < tokens) return KIVI_ERR_SHAPE;
+    if (!aligned16(k) || !aligned16(v) || !aligned16(q) || (reinterpret_cast<uintptr_t>(out) & 1u) ||
+        (reinterpret_cast<uintptr_t>(lse) & 3u))
+        return KIVI_ERR_SHAPE;
+    if (num_splits < 0 || num_splits > kMaxSplits) return KIVI_ERR_SHAPE;
+    if (!std::isfinite(sm_scale)) return KIVI_ERR_SHAPE;
+    const int32_t splits = num_splits > 0 ? num_splits : fp16_auto_splits(batch, kv_heads, tokens, q_heads);
+    const size_t need = kivi_decode_attn_fp16_workspace(batch, kv_heads, tokens, q_heads, splits);
+    if (workspace == nullptr || workspace_bytes < need) return KIVI_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return KIVI_ERR_WORKSPACE;
+    AttnArgs a{};
+    a.q = q;
+    a.counters = static_cast<uint32_t*>(workspace);
+    a.ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + fp16_counter_bytes(batch, q_heads));
+    a.out = out;
+    a.lse = lse;
+    a.sm_log2 = (float)((double)sm_scale * 1.4426950408889634);
+    a.q_heads = q_heads;
+    a.kv_heads = kv_heads;
+    a.ratio = q_heads / kv_heads;
+    a.splits = splits;
+    a.q_rows = (int64_t)batch * q_heads;
+    a.nq = queries_per_block(a.ratio);
+    a.block_rows = fp16_block_rows(batch, kv_heads, q_heads);
+    a.kf = k;
+    a.vf = v;
+    a.kv_stride = token_stride;
+    a.n_tokens = tokens;
+    a.tokens_per_split = (tokens + splits - 1) / splits;
+    hipEvent_t t0, t1;
+    take_timing(&t0, &t1);
+    return hip_status(launch_decode_attn_fp16(a, (hipStream_t)stream, t0, t1));
 }
 
 int kivi_time_next_attention(void* start_event, void* stop_event) {

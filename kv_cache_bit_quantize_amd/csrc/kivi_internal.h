@@ -73,6 +73,12 @@ struct AttnArgs {
     uint16_t* k_ring;           // k_res / v_res, written (the attention reads them as const)
     uint16_t* v_ring;
     int32_t new_slot;
+    // fp16 comparator (kivi_decode_attn_fp16): keys and values [row][kv_stride][D] in fp16,
+    // tokens [0, n_tokens) of each row valid, tokens_per_split of them per split
+    const uint16_t* kf;
+    const uint16_t* vf;
+    int64_t kv_stride;
+    int32_t n_tokens, tokens_per_split;
 };
 
 hipError_t launch_quantize_k(const QuantArgs& a, hipStream_t s);
@@ -83,5 +89,7 @@ hipError_t launch_append_flush(const AppendArgs& a, hipStream_t s);
 hipError_t launch_decode_attn(const AttnArgs& a, hipStream_t s, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 hipError_t launch_decode_attn_gqa(const AttnArgs& a, hipStream_t s, hipEvent_t t0 = nullptr,
                                   hipEvent_t t1 = nullptr);
+hipError_t launch_decode_attn_fp16(const AttnArgs& a, hipStream_t s, hipEvent_t t0 = nullptr,
+                                   hipEvent_t t1 = nullptr);
 
 }  // namespace kivi

@@ -18,7 +18,8 @@ _STATUS_NAMES = {0: "KIVI_OK", -1: "KIVI_ERR_NULL", -2: "KIVI_ERR_SHAPE", -3: "K
 
 EXPORTS = ["kivi_quantize_k_per_channel", "kivi_quantize_v_per_token", "kivi_prefill", "kivi_append_flush",
            "kivi_decode_attn", "kivi_decode_step", "kivi_decode_attn_splits", "kivi_decode_attn_workspace", "kivi_cache_bytes",
-           "kivi_status_str", "kivi_time_next_attention"]
+           "kivi_status_str", "kivi_time_next_attention", "kivi_decode_attn_fp16", "kivi_decode_attn_fp16_splits",
+           "kivi_decode_attn_fp16_workspace"]
 
 
 class KiviError(RuntimeError):
@@ -55,10 +56,16 @@ def _load():
     L.kivi_cache_bytes.argtypes = [cp, C.POINTER(C.c_size_t), C.POINTER(C.c_size_t), C.POINTER(C.c_size_t)]
     L.kivi_status_str.argtypes = [C.c_int]
     L.kivi_time_next_attention.argtypes = [p, p]
+    L.kivi_decode_attn_fp16.argtypes = [p, p, i32, i32, i32, i32, p, i32, C.c_float, p, p, p, C.c_size_t, i32, p]
+    L.kivi_decode_attn_fp16_splits.argtypes = [i32, i32, i32, i32]
+    L.kivi_decode_attn_fp16_splits.restype = i32
+    L.kivi_decode_attn_fp16_workspace.argtypes = [i32, i32, i32, i32, i32]
+    L.kivi_decode_attn_fp16_workspace.restype = C.c_size_t
     L.kivi_status_str.restype = C.c_char_p
     for name in EXPORTS:
         L[name].restype = L[name].restype if name in ("kivi_decode_attn_splits", "kivi_decode_attn_workspace",
-                                                      "kivi_status_str") else C.c_int
+                                                      "kivi_status_str", "kivi_decode_attn_fp16_splits",
+                                                      "kivi_decode_attn_fp16_workspace") else C.c_int
     return L
 
 
@@ -193,6 +200,44 @@ def kivi_decode_step(cache, k_new, v_new, q, sm_scale, out=None, lse=None, num_s
                                 _ptr(out), _ptr(lse) if want_lse else None, _ptr(ws), ws.numel() * ws.element_size(),
                                 num_splits, C.byref(flushed), _stream(q)), "kivi_decode_step")
     return (out, lse, bool(flushed.value)) if want_lse else (out, bool(flushed.value))
+
+
+def kivi_decode_attn_fp16(k, v, q, sm_scale, tokens=None, out=None, lse=None, num_splits=0, workspace=None):
+    """fp16 comparator: decode attention of q (fp16 [B, Hq, D]) over a plain fp16 cache
+    k, v (fp16 [B, Hkv, T_cap, D], contiguous), tokens [0, tokens) of each row (default
+    T_cap).  Returns out (and lse if `lse`), like kivi_decode_attn."""
+    for t in (k, v):
+        if not t.is_contiguous() or t.dtype != torch.float16 or t.dim() != 4:
+            raise ValueError("expected contiguous float16 k, v [B, Hkv, T, D]")
+    if not q.is_contiguous() or q.dtype != torch.float16:
+        raise ValueError("expected contiguous float16 q [B, Hq, D]")
+    B, Hkv, T_cap, D = k.shape
+    tokens = T_cap if tokens is None else tokens
+    Hq = q.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    want_lse = lse is not None and lse is not False
+    if lse is True:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        need = lib.kivi_decode_attn_fp16_workspace(B, Hkv, tokens, Hq, num_splits)
+        workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=q.device)
+    _check(lib.kivi_decode_attn_fp16(_ptr(k), _ptr(v), B, Hkv, tokens, T_cap, _ptr(q), Hq, float(sm_scale), _ptr(out),
+                                     _ptr(lse) if want_lse else None, _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(), num_splits, _stream(q)),
+           "kivi_decode_attn_fp16")
+    return (out, lse) if want_lse else out
+
+
+def kivi_decode_attn_fp16_splits(batch, kv_heads, tokens, q_heads):
+    s = lib.kivi_decode_attn_fp16_splits(batch, kv_heads, tokens, q_heads)
+    if s < 0:
+        raise KiviError(s, "kivi_decode_attn_fp16_splits")
+    return s
+
+
+def kivi_decode_attn_fp16_workspace(batch, kv_heads, tokens, q_heads, num_splits=0):
+    return lib.kivi_decode_attn_fp16_workspace(batch, kv_heads, tokens, q_heads, num_splits)
 
 
 def kivi_decode_attn_splits(cache, q_heads):

@@ -21,7 +21,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 11
+    assert len(names) == 14
     out = os.popen(f"nm -D --defined-only {kivi.LIB_PATH}").read()
     exported = set(re.findall(r" T (kivi_\w+)$", out, re.M))
     assert set(names) <= exported, set(names) - exported
@@ -49,6 +49,35 @@ def test_time_next_attention_arguments():
     assert L.kivi_time_next_attention(None, C.c_void_p(FAKE)) == -1      # KIVI_ERR_NULL
     assert L.kivi_time_next_attention(C.c_void_p(FAKE), None) == -1
     assert L.kivi_time_next_attention(None, None) == kivi.KIVI_OK
+
+
+def test_fp16_comparator_arguments():
+    """kivi_decode_attn_fp16 rejects bad arguments on the host (no kernel is launched)."""
+    f = L.kivi_decode_attn_fp16
+    P = C.c_void_p(FAKE)
+    ws = C.c_void_p(FAKE)
+    big = 1 << 30
+
+    def call(k=P, v=P, B=2, Hkv=2, T=100, stride=128, q=P, Hq=4, out=P, lse=None, w=ws, wb=big, splits=0):
+        return f(k, v, B, Hkv, T, stride, q, Hq, 0.1, out, lse, w, wb, splits, None)
+
+    assert call(k=None) == -1 and call(q=None) == -1 and call(out=None) == -1
+    assert call(T=0) == -2                          # empty context
+    assert call(T=200) == -2                        # more tokens than the row stride
+    assert call(Hq=3) == -2                         # q_heads not a multiple of kv_heads
+    assert call(k=C.c_void_p(FAKE + 8)) == -2       # misaligned
+    assert call(splits=-1) == -2
+    assert call(w=None) == -5 and call(wb=16) == -5 and call(w=C.c_void_p(FAKE + 16)) == -5
+    assert f(P, P, 2, 2, 100, 128, P, 4, float("nan"), P, None, ws, big, 0, None) == -2
+    # host-only helpers
+    s = L.kivi_decode_attn_fp16_splits(1, 32, 131072, 32)
+    assert s == 24                                  # 768 workgroups for 32 single-query rows
+    assert L.kivi_decode_attn_fp16_splits(64, 8, 8192, 32) == 1   # 512 query-group rows
+    assert L.kivi_decode_attn_fp16_splits(1, 1, 100, 1) == 1      # short context: one split
+    assert L.kivi_decode_attn_fp16_splits(1, 1, 0, 1) == -2
+    need = L.kivi_decode_attn_fp16_workspace(1, 32, 131072, 32, 0)
+    assert need == 256 + ((24 * 32 * 130 * 4 + 255) // 256) * 256
+    assert L.kivi_decode_attn_fp16_workspace(1, 1, 0, 1, 0) == 0
 
 
 def test_status_strings():
