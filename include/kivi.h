@@ -155,6 +155,39 @@ int kivi_decode_step(kivi_cache* cache, const uint16_t* k_new, const uint16_t* v
                      void* workspace, size_t workspace_bytes, int32_t num_splits, int32_t* flushed,
                      void* stream);
 
+/* ---- Ragged batches: sequences of one batch at different lengths.
+ * The per-sequence cache state lives in device memory, seq_state: int32 [batch][4] =
+ * {n_quant, n_res, res_head, flags}, 16-byte aligned, owned by the caller; the first three
+ * mean for sequence b (rows b*kv_heads .. b*kv_heads + kv_heads - 1) what the kivi_cache
+ * fields of the same names mean for a whole batch, and the descriptor's own n_quant, n_res
+ * and res_head are ignored by these calls.  A sequence's rows are contiguous in every
+ * buffer, so each sequence can be filled by the single-batch calls (kivi_prefill, ...) on
+ * a descriptor with batch = 1 whose pointers start at its first row.  The kernels check
+ * each state: one out of range (n_quant not a multiple of 32 or above token_cap, n_res
+ * above residual_cap, res_head not a multiple of 32 below residual_cap) is not used, the
+ * sequence attends over nothing and its flags get KIVI_SEQ_BAD_STATE.  flags bits are only
+ * ever set (OR) by the library, never cleared. */
+#define KIVI_SEQ_CAPACITY 1    /* an append was skipped: its flush would pass token_cap */
+#define KIVI_SEQ_BAD_STATE 2   /* the sequence's state was out of range and was not used */
+
+/* kivi_append_flush for every sequence of a ragged batch: one new token per sequence
+ * (k_new, v_new: fp16 [batch][kv_heads][128]), a sequence whose ring is full first
+ * flushing its oldest 32 ring tokens into a new group, then each sequence's state moved on
+ * on the device (two kernel launches in stream order).  A sequence whose flush would pass
+ * token_cap is left as it was and gets KIVI_SEQ_CAPACITY. */
+int kivi_append_flush_ragged(const kivi_cache* cache, int32_t* seq_state, const uint16_t* k_new,
+                             const uint16_t* v_new, void* stream);
+
+/* kivi_decode_attn for a ragged batch: each sequence's query heads attend over that
+ * sequence's history and residual.  The grid is sized for the longest context the cache can
+ * hold (num_splits == 0: kivi_decode_attn_ragged_splits; the workspace is
+ * kivi_decode_attn_workspace(cache, q_heads, that split count)); each workgroup finds its
+ * sequence's share on the device.  A sequence with an empty context gets out = 0 and
+ * lse = -inf. */
+int kivi_decode_attn_ragged(const kivi_cache* cache, int32_t* seq_state, const uint16_t* q,
+                            int32_t q_heads, float sm_scale, uint16_t* out, float* lse,
+                            void* workspace, size_t workspace_bytes, int32_t num_splits, void* stream);
+
 /* fp16 comparator (a measurement baseline, not the method): decode attention of one query
  * per head over a plain fp16 KV cache, the uncompressed cache the pages set the 2-bit
  * cache against (record "KV bytes basis": the 16-bit cache's bytes per token; "Methodology":
@@ -189,6 +222,9 @@ int32_t kivi_decode_attn_splits(const kivi_cache* cache, int32_t q_heads);
 
 /* Workspace bytes kivi_decode_attn needs for this shape and split count (0 = auto). */
 size_t kivi_decode_attn_workspace(const kivi_cache* cache, int32_t q_heads, int32_t num_splits);
+
+/* Split count kivi_decode_attn_ragged uses for num_splits == 0 (shape only). */
+int32_t kivi_decode_attn_ragged_splits(const kivi_cache* cache, int32_t q_heads);
 
 /* Split count and workspace bytes of kivi_decode_attn_fp16 for this shape (0 = auto
  * splits); a negative KIVI_ERR_* code / 0 for an invalid shape. */

@@ -75,9 +75,9 @@ int64_t block_rows(const kivi_cache* c, int32_t q_heads) {
     return nq > 1 ? (int64_t)c->batch * c->kv_heads * (ratio / nq) : (int64_t)c->batch * q_heads;
 }
 
-int32_t auto_splits(const kivi_cache* c, int32_t q_heads) {
+// Split count for a context of `groups` key groups.
+int32_t auto_splits_for(const kivi_cache* c, int32_t q_heads, int64_t groups) {
     const int64_t rows = block_rows(c, q_heads);
-    const int64_t groups = c->n_quant / c->group;
     const int64_t target = queries_per_block(q_heads / c->kv_heads) > 1 ? kTargetBlocksGroup : kTargetBlocks;
     int64_t s = (target + rows - 1) / rows;
     const int64_t cap = groups / kMinGroupsPerSplit;
@@ -85,6 +85,11 @@ int32_t auto_splits(const kivi_cache* c, int32_t q_heads) {
     if (s < 1) s = 1;
     if (s > kMaxSplits) s = kMaxSplits;
     return (int32_t)s;
+}
+int32_t auto_splits(const kivi_cache* c, int32_t q_heads) { return auto_splits_for(c, q_heads, c->n_quant / c->group); }
+// ragged batch: sized for the longest context the cache can hold
+int32_t ragged_auto_splits(const kivi_cache* c, int32_t q_heads) {
+    return auto_splits_for(c, q_heads, c->token_cap / c->group);
 }
 
 // leading area of the attention workspace: one arrival counter per query row
@@ -142,6 +147,8 @@ int prepare_append(const kivi_cache* c, const uint16_t* k_new, const uint16_t* v
     a->v_sz = c->v_sz;
     a->k_res = c->k_res;
     a->v_res = c->v_res;
+    a->seq_state = nullptr;   // one state for the whole batch (the fields above)
+    a->kv_heads = c->kv_heads;
     *next = *c;
     next->n_quant = n_quant;
     next->n_res = n_res + 1;
@@ -155,22 +162,27 @@ void commit_state(kivi_cache* c, const kivi_cache& next) {
     c->res_head = next.res_head;
 }
 
-// Validates a decode-attention call on cache state *c and fills its arguments.
+// Validates a decode-attention call on cache state *c (or, with seq_state, on the
+// per-sequence device states of a ragged batch, which the kernels check) and fills its
+// arguments.
 int prepare_attn(const kivi_cache* c, const uint16_t* q, int32_t q_heads, float sm_scale, uint16_t* out,
-                 float* lse, void* workspace, size_t workspace_bytes, int32_t num_splits, AttnArgs* pa) {
+                 float* lse, void* workspace, size_t workspace_bytes, int32_t num_splits, AttnArgs* pa,
+                 int32_t* seq_state = nullptr) {
     int st = check_shape(c);
     if (st != KIVI_OK) return st;
-    if ((st = check_state(c)) != KIVI_OK) return st;
+    if (seq_state == nullptr && (st = check_state(c)) != KIVI_OK) return st;
+    if (seq_state != nullptr && !aligned16(seq_state)) return KIVI_ERR_SHAPE;
     if ((st = check_quant_bufs(c, true, true)) != KIVI_OK) return st;
     if ((st = check_res_bufs(c)) != KIVI_OK) return st;
     if (q == nullptr || out == nullptr) return KIVI_ERR_NULL;
     if (!aligned16(q) || (reinterpret_cast<uintptr_t>(out) & 1u) || (reinterpret_cast<uintptr_t>(lse) & 3u))
         return KIVI_ERR_SHAPE;
     if (q_heads <= 0 || q_heads % c->kv_heads != 0) return KIVI_ERR_SHAPE;
-    if (c->n_quant + c->n_res == 0) return KIVI_ERR_SHAPE;
+    if (seq_state == nullptr && c->n_quant + c->n_res == 0) return KIVI_ERR_SHAPE;
     if (num_splits < 0 || num_splits > kMaxSplits) return KIVI_ERR_SHAPE;
     if (!std::isfinite(sm_scale)) return KIVI_ERR_SHAPE;
-    const int32_t splits = num_splits > 0 ? num_splits : auto_splits(c, q_heads);
+    const int32_t splits =
+        num_splits > 0 ? num_splits : (seq_state != nullptr ? ragged_auto_splits(c, q_heads) : auto_splits(c, q_heads));
     const size_t need = kivi_decode_attn_workspace(c, q_heads, splits);
     if (workspace == nullptr || workspace_bytes < need) return KIVI_ERR_WORKSPACE;
     if (reinterpret_cast<uintptr_t>(workspace) & 255u) return KIVI_ERR_WORKSPACE;
@@ -207,6 +219,7 @@ int prepare_attn(const kivi_cache* c, const uint16_t* q, int32_t q_heads, float 
     a.k_new = a.v_new = nullptr;
     a.k_ring = a.v_ring = nullptr;
     a.new_slot = 0;
+    a.seq_state = seq_state;
     *pa = a;
     return KIVI_OK;
 }
@@ -360,6 +373,51 @@ int kivi_append_flush(kivi_cache* c, const uint16_t* k_new, const uint16_t* v_ne
     commit_state(c, next);
     if (flushed != nullptr) *flushed = a.do_flush;
     return KIVI_OK;
+}
+
+int kivi_append_flush_ragged(const kivi_cache* c, int32_t* seq_state, const uint16_t* k_new, const uint16_t* v_new,
+                             void* stream) {
+    int st = check_shape(c);
+    if (st != KIVI_OK) return st;
+    if ((st = check_quant_bufs(c, true, true)) != KIVI_OK) return st;
+    if ((st = check_res_bufs(c)) != KIVI_OK) return st;
+    if (seq_state == nullptr || k_new == nullptr || v_new == nullptr) return KIVI_ERR_NULL;
+    if (!aligned16(seq_state) || !aligned16(k_new) || !aligned16(v_new)) return KIVI_ERR_SHAPE;
+    AppendArgs a{};
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.rows = rows_of(c);
+    a.token_cap = c->token_cap;
+    a.residual_cap = c->residual_cap;
+    a.k_codes = c->k_codes;
+    a.v_codes = c->v_codes;
+    a.k_sz = c->k_sz;
+    a.v_sz = c->v_sz;
+    a.k_res = c->k_res;
+    a.v_res = c->v_res;
+    a.seq_state = seq_state;
+    a.kv_heads = c->kv_heads;
+    return hip_status(launch_append_flush_ragged(a, c->batch, (hipStream_t)stream));
+}
+
+int kivi_decode_attn_ragged(const kivi_cache* c, int32_t* seq_state, const uint16_t* q, int32_t q_heads,
+                            float sm_scale, uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
+                            int32_t num_splits, void* stream) {
+    if (seq_state == nullptr) return KIVI_ERR_NULL;
+    AttnArgs a;
+    const int st =
+        prepare_attn(c, q, q_heads, sm_scale, out, lse, workspace, workspace_bytes, num_splits, &a, seq_state);
+    if (st != KIVI_OK) return st;
+    hipEvent_t t0, t1;
+    take_timing(&t0, &t1);
+    return hip_status(launch_decode_attn(a, (hipStream_t)stream, t0, t1));
+}
+
+int32_t kivi_decode_attn_ragged_splits(const kivi_cache* c, int32_t q_heads) {
+    const int st = check_shape(c);
+    if (st != KIVI_OK) return st;
+    if (q_heads <= 0 || q_heads % c->kv_heads != 0) return KIVI_ERR_SHAPE;
+    return ragged_auto_splits(c, q_heads);
 }
 
 int32_t kivi_decode_attn_splits(const kivi_cache* c, int32_t q_heads) {

@@ -99,9 +99,10 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
     float lsum = 0.0f, m = -INFINITY;
     float vs = 0.0f;                   // power-of-two factor keeping the value weights in fp16 range
 
-    const int n_groups = a.n_quant / kG;
-    const int g_lo = split * a.groups_per_split;
-    const int g_hi = min(n_groups, g_lo + a.groups_per_split);
+    const RowState rs = row_state(a, kvrow, split);
+    const int n_groups = rs.n_quant / kG;
+    const int g_lo = split * rs.groups_per_split;
+    const int g_hi = min(n_groups, g_lo + rs.groups_per_split);
     const int cnt = max(0, g_hi - g_lo);
     const int per_wave = (cnt + kWaves - 1) / kWaves;
     const int gb = g_lo + min(cnt, wave * per_wave);
@@ -296,7 +297,7 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
     // ---- fp16 residual (last split only), as separate states
     float mr[1], lr[1];
     if (split == a.splits - 1) {
-        residual_states<1>(a, qrow, kvrow, wave, &sh_o[0][kWaves + wave][0], kSlots * kD, mr, lr);
+        residual_states<1>(a, rs, qrow, kvrow, wave, &sh_o[0][kWaves + wave][0], kSlots * kD, mr, lr);
     } else {
         mr[0] = -INFINITY;
         lr[0] = 0.0f;

@@ -96,6 +96,26 @@ __device__ __forceinline__ float load_coherent(float* p) {
 // s_waitcnt with vmcnt(0) and the other counters left free (expcnt 7, lgkmcnt 15)
 constexpr int kWaitVmcnt0 = 0x0F70;
 
+// The cache state one workgroup attends over: the call's, or (ragged batch) its sequence's,
+// with that sequence's share of key groups per split.  A sequence state out of range gives
+// an empty context (nothing is read) and sets the sequence's kSeqBadState flag.
+struct RowState {
+    int32_t n_quant, n_res, res_head, groups_per_split;
+};
+__device__ __forceinline__ RowState row_state(const AttnArgs& a, int64_t kvrow, int split) {
+    if (a.seq_state == nullptr) return {a.n_quant, a.n_res, a.res_head, a.groups_per_split};
+    int32_t* s = a.seq_state + 4 * (kvrow / a.kv_heads);
+    int32_t nq = s[0], nr = s[1], rh = s[2];
+    if (!state_in_range(nq, nr, rh, a.token_cap, a.residual_cap)) {
+        if (split == 0 && threadIdx.x == 0)
+            __hip_atomic_fetch_or(&s[3], kSeqBadState, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        nq = nr = rh = 0;
+    }
+    // the split that also reads the residual counts it as that many quantized groups
+    const int32_t res_groups = (nr * 512 + 96 * kG - 1) / (96 * kG);
+    return {nq, nr, rh, (nq / kG + res_groups + a.splits - 1) / a.splits};
+}
+
 // Softmax states of query rows qrow0..qrow0+NQ-1 over the fp16 residual ring.  Called by one
 // whole wave of a WAVES-wave workgroup; wave w takes the ring's logical tokens
 // [32w + 32*WAVES*i, 32w + 32*WAVES*i + 32).  Per such
@@ -110,8 +130,8 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 // the wave has no residual token.  In a fused decode step the last residual token is the new
 // one, read from k_new / v_new.
 template <int NQ, int WAVES = kWaves>
-__device__ void residual_states(const AttnArgs& a, int64_t qrow0, int64_t kvrow, int wave, float* o_dst,
-                                int o_stride, float (&mr)[NQ], float (&lr)[NQ]) {
+__device__ void residual_states(const AttnArgs& a, const RowState& rs, int64_t qrow0, int64_t kvrow, int wave,
+                                float* o_dst, int o_stride, float (&mr)[NQ], float (&lr)[NQ]) {
     const int lane = threadIdx.x & 63, tp = lane >> 2, qq = lane & 3;
     float o[NQ][2];
 #pragma unroll
@@ -120,12 +140,12 @@ __device__ void residual_states(const AttnArgs& a, int64_t qrow0, int64_t kvrow,
         lr[r] = 0.0f;
         o[r][0] = o[r][1] = 0.0f;
     }
-    auto token_slot = [&](int i) { return (a.res_head + i) % a.residual_cap; };
-    auto is_new = [&](int i) { return a.k_new != nullptr && i == a.n_res - 1; };
-    for (int base = wave * kG; base < a.n_res; base += WAVES * kG) {
+    auto token_slot = [&](int i) { return (rs.res_head + i) % a.residual_cap; };
+    auto is_new = [&](int i) { return a.k_new != nullptr && i == rs.n_res - 1; };
+    for (int base = wave * kG; base < rs.n_res; base += WAVES * kG) {
         // ---- logits of tokens 2tp, 2tp+1 for every row
         const int i0 = base + 2 * tp, i1 = i0 + 1;
-        const bool ok0 = i0 < a.n_res, ok1 = i1 < a.n_res;
+        const bool ok0 = i0 < rs.n_res, ok1 = i1 < rs.n_res;
         const int j0 = ok0 ? i0 : 0, j1 = ok1 ? i1 : 0;
         const int64_t rn = kvrow * kD + qq * 32;
         const uint4* k0 = reinterpret_cast<const uint4*>(
@@ -179,7 +199,7 @@ __device__ void residual_states(const AttnArgs& a, int64_t qrow0, int64_t kvrow,
             o[r][0] *= al[r];
             o[r][1] *= al[r];
         }
-        const int nt = min(kG, a.n_res - base);
+        const int nt = min(kG, rs.n_res - base);
         for (int t0 = 0; t0 < nt; t0 += 8) {
             uint32_t vv[8];
 #pragma unroll
@@ -205,7 +225,7 @@ __device__ void residual_states(const AttnArgs& a, int64_t qrow0, int64_t kvrow,
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
-    if (wave * kG < a.n_res) {
+    if (wave * kG < rs.n_res) {
 #pragma unroll
         for (int r = 0; r < NQ; ++r) {
             o_dst[r * o_stride + 2 * lane] = o[r][0];
@@ -284,7 +304,7 @@ __device__ __forceinline__ void merge_rows(const AttnArgs& a, int64_t qrow0, int
             O = fmaf(O, al, o1 * be);
             M = mn;
         }
-        a.out[(qrow0 + r) * kD + j] = (uint16_t)f2h(O / L);
+        a.out[(qrow0 + r) * kD + j] = (uint16_t)f2h(L > 0.0f ? O / L : 0.0f);
         if (j == 0 && a.lse != nullptr) a.lse[qrow0 + r] = (M + log2f(L)) * 0.69314718055994531f;
     }
     if (t == 0) a.counters[counter] = 0u;
@@ -314,7 +334,8 @@ __device__ __forceinline__ void finish_block(const AttnArgs& a, int split, int64
             O = fmaf(sh_o[r][w][j], sc, O);
         }
         if (a.splits == 1) {
-            a.out[(qrow0 + r) * kD + j] = (uint16_t)f2h(O / L);
+            // an empty context (a ragged batch's empty sequence) gives out = 0, lse = -inf
+            a.out[(qrow0 + r) * kD + j] = (uint16_t)f2h(L > 0.0f ? O / L : 0.0f);
             if (j == 0 && a.lse != nullptr) a.lse[qrow0 + r] = (M + log2f(L)) * 0.69314718055994531f;
         } else {
             float* part = a.ws + ((int64_t)split * a.q_rows + qrow0 + r) * kPart;

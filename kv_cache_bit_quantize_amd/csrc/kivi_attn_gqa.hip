@@ -115,9 +115,10 @@ __global__ __launch_bounds__(kGqaBlock) __attribute__((amdgpu_waves_per_eu(3))) 
     float lsum = 0.0f, m = -INFINITY;          // query qh's running sum and max
     float vs = 0.0f;                    // power-of-two factor keeping the value weights in fp16 range
 
-    const int n_groups = a.n_quant / kG;
-    const int g_lo = split * a.groups_per_split;
-    const int g_hi = min(n_groups, g_lo + a.groups_per_split);
+    const RowState rs = row_state(a, kvrow, split);
+    const int n_groups = rs.n_quant / kG;
+    const int g_lo = split * rs.groups_per_split;
+    const int g_hi = min(n_groups, g_lo + rs.groups_per_split);
     const int cnt = max(0, g_hi - g_lo);
     const int per_wave = (cnt + W - 1) / W;
     const int gb = g_lo + min(cnt, wave * per_wave);
@@ -389,7 +390,7 @@ __global__ __launch_bounds__(kGqaBlock) __attribute__((amdgpu_waves_per_eu(3))) 
     __builtin_amdgcn_sched_barrier(0);
     float mr[NQ], lr[NQ];
     if (split == a.splits - 1) {
-        residual_states<NQ, W>(a, qrow0, kvrow, wave, &sh_o[0][W + wave][0], S * kD, mr, lr);
+        residual_states<NQ, W>(a, rs, qrow0, kvrow, wave, &sh_o[0][W + wave][0], S * kD, mr, lr);
     } else {
 #pragma unroll
         for (int r = 0; r < NQ; ++r) {

@@ -38,6 +38,14 @@ __host__ __device__ constexpr int64_t key_word_offset(int64_t t, int w) {
 // index (in 32-bit pairs), inside a row, of the value (scale, zero) of token t, group k
 __host__ __device__ constexpr int64_t value_pair_index(int64_t t, int k) { return t * (kD / kG) + k; }
 
+// A cache state the kernels can use without reading outside the buffers: whole groups in the
+// history, within capacity, and a ring head on a group boundary.
+__host__ __device__ inline bool state_in_range(int32_t n_quant, int32_t n_res, int32_t res_head, int32_t token_cap,
+                                               int32_t residual_cap) {
+    return n_quant >= 0 && n_quant <= token_cap && n_quant % kG == 0 && n_res >= 0 && n_res <= residual_cap &&
+           res_head >= 0 && res_head < residual_cap && res_head % kG == 0;
+}
+
 __device__ __forceinline__ float h2f(uint32_t h) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
 }

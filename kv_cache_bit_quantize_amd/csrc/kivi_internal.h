@@ -43,6 +43,11 @@ struct AppendArgs {
     uint16_t* v_sz;
     uint16_t* k_res;
     uint16_t* v_res;
+    // ragged batch: per-sequence state [batch][4] (n_quant, n_res, res_head, flags) in device
+    // memory; when set, every row takes its flush decision and slots from its sequence's
+    // state instead of the fields above
+    int32_t* seq_state;
+    int32_t kv_heads;
 };
 
 struct AttnArgs {
@@ -79,12 +84,22 @@ struct AttnArgs {
     const uint16_t* vf;
     int64_t kv_stride;
     int32_t n_tokens, tokens_per_split;
+    // ragged batch: per-sequence state [batch][4] (n_quant, n_res, res_head, flags) in device
+    // memory; when set it replaces n_quant, n_res, res_head and groups_per_split per row
+    int32_t* seq_state;
 };
+
+// bits of a sequence's flags word (ragged calls; only ever set, by the kernels)
+constexpr int32_t kSeqCapacity = 1;   // a flush would pass token_cap: the append was skipped
+constexpr int32_t kSeqBadState = 2;   // the state was out of range: the sequence was skipped
+
 
 hipError_t launch_quantize_k(const QuantArgs& a, hipStream_t s);
 hipError_t launch_quantize_v(const QuantArgs& a, hipStream_t s);
 hipError_t launch_residual_load(const ResidualArgs& a, hipStream_t s);
 hipError_t launch_append_flush(const AppendArgs& a, hipStream_t s);
+// ragged append: the per-row appends, then the per-sequence state update
+hipError_t launch_append_flush_ragged(const AppendArgs& a, int32_t batch, hipStream_t s);
 // t0 / t1 (nullable): events that record the kernel's own start and end (hipExtLaunchKernel)
 hipError_t launch_decode_attn(const AttnArgs& a, hipStream_t s, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 hipError_t launch_decode_attn_gqa(const AttnArgs& a, hipStream_t s, hipEvent_t t0 = nullptr,

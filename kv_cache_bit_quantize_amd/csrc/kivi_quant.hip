@@ -167,24 +167,45 @@ __global__ __launch_bounds__(kBlock) void residual_load_kernel(ResidualArgs a) {
 }
 
 // grid.x = rows.  Optional flush of ring slots [flush_slot, flush_slot+32) into key group
-// flush_group / value tokens flush_group*32.., then the new token into new_slot.
+// flush_group / value tokens flush_group*32.., then the new token into new_slot.  In a
+// ragged batch each row takes these from its sequence's state (flush when its ring is full);
+// a sequence whose state is out of range, or whose flush would pass token_cap, is skipped
+// and flagged.
 __global__ __launch_bounds__(kBlock) void append_flush_kernel(AppendArgs a) {
     __shared__ uint4 tile4[kG * kD / 8];
     __shared__ float sh_mn[kD], sh_s[kD];
     const int64_t row = blockIdx.x;
     const int tid = threadIdx.x;
-    if (a.do_flush) {
-        const uint4* kr = reinterpret_cast<const uint4*>(a.k_res + (row * a.residual_cap + a.flush_slot) * kD);
+    int do_flush = a.do_flush, flush_slot = a.flush_slot, flush_group = a.flush_group, new_slot = a.new_slot;
+    if (a.seq_state != nullptr) {
+        int32_t* s = a.seq_state + 4 * (row / a.kv_heads);
+        const int32_t nq = s[0], nr = s[1], rh = s[2];
+        const bool ok = state_in_range(nq, nr, rh, a.token_cap, a.residual_cap);
+        const bool flush = nr == a.residual_cap;
+        if (!ok || (flush && nq + kG > a.token_cap)) {   // the whole workgroup leaves together
+            if (row % a.kv_heads == 0 && tid == 0)
+                __hip_atomic_fetch_or(&s[3], ok ? kSeqCapacity : kSeqBadState, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+            return;
+        }
+        do_flush = flush;
+        flush_slot = rh;
+        flush_group = nq / kG;
+        const int head = flush ? (rh + kG) % a.residual_cap : rh;
+        new_slot = (head + (flush ? nr - kG : nr)) % a.residual_cap;
+    }
+    if (do_flush) {
+        const uint4* kr = reinterpret_cast<const uint4*>(a.k_res + (row * a.residual_cap + flush_slot) * kD);
         tile4[tid] = kr[tid];
         tile4[tid + kBlock] = kr[tid + kBlock];
         __syncthreads();
-        const int dst_tok = a.flush_group * kG;
-        uint8_t* kc = a.k_codes + row * a.token_cap * kRowBytes + (int64_t)a.flush_group * kTileBytes;
-        uint32_t* kp = reinterpret_cast<uint32_t*>(a.k_sz) + (row * (a.token_cap / kG) + a.flush_group) * kD;
+        const int dst_tok = flush_group * kG;
+        uint8_t* kc = a.k_codes + row * a.token_cap * kRowBytes + (int64_t)flush_group * kTileBytes;
+        uint32_t* kp = reinterpret_cast<uint32_t*>(a.k_sz) + (row * (a.token_cap / kG) + flush_group) * kD;
         quant_k_tile(reinterpret_cast<const uint16_t*>(tile4), sh_mn, sh_s, kc, kp);
         // values: the same 32 ring tokens as one value tile
         __shared__ __align__(16) uint8_t sh_codes[kG][kD];
-        quant_v_tile(a.v_res + (row * a.residual_cap + a.flush_slot) * kD, kD, 0, kG, sh_codes,
+        quant_v_tile(a.v_res + (row * a.residual_cap + flush_slot) * kD, kD, 0, kG, sh_codes,
                      a.v_codes + (row * a.token_cap + dst_tok) * kRowBytes,
                      reinterpret_cast<uint32_t*>(a.v_sz) + value_pair_index(row * a.token_cap + dst_tok, 0));
         __syncthreads();   // every read of the flushed slots is done before the overwrite
@@ -192,9 +213,24 @@ __global__ __launch_bounds__(kBlock) void append_flush_kernel(AppendArgs a) {
     if (tid < 32) {
         const int c = tid & 15;
         const uint16_t* src = (tid < 16 ? a.k_new : a.v_new) + row * kD;
-        uint16_t* dst = (tid < 16 ? a.k_res : a.v_res) + (row * a.residual_cap + a.new_slot) * kD;
+        uint16_t* dst = (tid < 16 ? a.k_res : a.v_res) + (row * a.residual_cap + new_slot) * kD;
         reinterpret_cast<uint4*>(dst)[c] = reinterpret_cast<const uint4*>(src)[c];
     }
+}
+
+// Ragged batch, after the appends: one thread per sequence moves its state on by one token
+// (and by one flushed group when its ring was full), with the decisions the appends took.
+__global__ __launch_bounds__(64) void seq_state_update_kernel(AppendArgs a, int32_t batch) {
+    const int64_t b = (int64_t)blockIdx.x * 64 + threadIdx.x;
+    if (b >= batch) return;
+    int32_t* s = a.seq_state + 4 * b;
+    const int32_t nq = s[0], nr = s[1], rh = s[2];
+    if (!state_in_range(nq, nr, rh, a.token_cap, a.residual_cap)) return;
+    const bool flush = nr == a.residual_cap;
+    if (flush && nq + kG > a.token_cap) return;
+    s[0] = flush ? nq + kG : nq;
+    s[1] = (flush ? nr - kG : nr) + 1;
+    s[2] = flush ? (rh + kG) % a.residual_cap : rh;
 }
 
 // ------------------------------------------------------------------ launchers ----
@@ -224,6 +260,14 @@ hipError_t launch_residual_load(const ResidualArgs& a, hipStream_t s) {
 
 hipError_t launch_append_flush(const AppendArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(append_flush_kernel, dim3((unsigned)a.rows), dim3(kBlock), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_append_flush_ragged(const AppendArgs& a, int32_t batch, hipStream_t s) {
+    hipLaunchKernelGGL(append_flush_kernel, dim3((unsigned)a.rows), dim3(kBlock), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(seq_state_update_kernel, dim3((unsigned)((batch + 63) / 64)), dim3(64), 0, s, a, batch);
     return hipGetLastError();
 }
 

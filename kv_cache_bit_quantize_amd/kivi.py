@@ -19,7 +19,11 @@ _STATUS_NAMES = {0: "KIVI_OK", -1: "KIVI_ERR_NULL", -2: "KIVI_ERR_SHAPE", -3: "K
 EXPORTS = ["kivi_quantize_k_per_channel", "kivi_quantize_v_per_token", "kivi_prefill", "kivi_append_flush",
            "kivi_decode_attn", "kivi_decode_step", "kivi_decode_attn_splits", "kivi_decode_attn_workspace", "kivi_cache_bytes",
            "kivi_status_str", "kivi_time_next_attention", "kivi_decode_attn_fp16", "kivi_decode_attn_fp16_splits",
-           "kivi_decode_attn_fp16_workspace"]
+           "kivi_decode_attn_fp16_workspace", "kivi_append_flush_ragged", "kivi_decode_attn_ragged",
+           "kivi_decode_attn_ragged_splits"]
+
+KIVI_SEQ_CAPACITY = 1     # seq_state flags: an append was skipped (its flush would pass token_cap)
+KIVI_SEQ_BAD_STATE = 2    # seq_state flags: the sequence's state was out of range and not used
 
 
 class KiviError(RuntimeError):
@@ -57,6 +61,10 @@ def _load():
     L.kivi_status_str.argtypes = [C.c_int]
     L.kivi_time_next_attention.argtypes = [p, p]
     L.kivi_decode_attn_fp16.argtypes = [p, p, i32, i32, i32, i32, p, i32, C.c_float, p, p, p, C.c_size_t, i32, p]
+    L.kivi_append_flush_ragged.argtypes = [cp, p, p, p, p]
+    L.kivi_decode_attn_ragged.argtypes = [cp, p, p, i32, C.c_float, p, p, p, C.c_size_t, i32, p]
+    L.kivi_decode_attn_ragged_splits.argtypes = [cp, i32]
+    L.kivi_decode_attn_ragged_splits.restype = i32
     L.kivi_decode_attn_fp16_splits.argtypes = [i32, i32, i32, i32]
     L.kivi_decode_attn_fp16_splits.restype = i32
     L.kivi_decode_attn_fp16_workspace.argtypes = [i32, i32, i32, i32, i32]
@@ -65,7 +73,8 @@ def _load():
     for name in EXPORTS:
         L[name].restype = L[name].restype if name in ("kivi_decode_attn_splits", "kivi_decode_attn_workspace",
                                                       "kivi_status_str", "kivi_decode_attn_fp16_splits",
-                                                      "kivi_decode_attn_fp16_workspace") else C.c_int
+                                                      "kivi_decode_attn_fp16_workspace",
+                                                      "kivi_decode_attn_ragged_splits") else C.c_int
     return L
 
 
@@ -114,6 +123,20 @@ class Cache:
 
     def set_state(self, n_quant, n_res, res_head):
         self.c.n_quant, self.c.n_res, self.c.res_head = n_quant, n_res, res_head
+
+    def sequence(self, b):
+        """Batch-1 view of sequence b (its kv_heads rows; the buffers are shared, nothing is
+        allocated), for the single-batch calls such as kivi_prefill.  Its state is its own."""
+        H = self.c.kv_heads
+        v = object.__new__(Cache)
+        for name in ("k_codes", "v_codes", "k_sz", "v_sz", "k_res", "v_res"):
+            setattr(v, name, getattr(self, name)[b * H:(b + 1) * H])
+        v.c = kivi_cache(1, H, self.c.head_dim, self.c.group, self.c.residual_cap, self.c.token_cap, 0, 0, 0, 0,
+                         v.k_codes.data_ptr(), v.v_codes.data_ptr(), v.k_sz.data_ptr(), v.v_sz.data_ptr(),
+                         v.k_res.data_ptr(), v.v_res.data_ptr())
+        v.device = self.device
+        v._ws = None
+        return v
 
     def workspace(self, q_heads, num_splits=0):
         need = lib.kivi_decode_attn_workspace(C.byref(self.c), q_heads, num_splits)
@@ -200,6 +223,51 @@ def kivi_decode_step(cache, k_new, v_new, q, sm_scale, out=None, lse=None, num_s
                                 _ptr(out), _ptr(lse) if want_lse else None, _ptr(ws), ws.numel() * ws.element_size(),
                                 num_splits, C.byref(flushed), _stream(q)), "kivi_decode_step")
     return (out, lse, bool(flushed.value)) if want_lse else (out, bool(flushed.value))
+
+
+def seq_state(states, device="cuda"):
+    """Ragged-batch state tensor: int32 [batch, 4] = (n_quant, n_res, res_head, flags) on the
+    device, from a list of (n_quant, n_res, res_head) per sequence."""
+    return torch.tensor([[int(a), int(b), int(c), 0] for a, b, c in states], dtype=torch.int32, device=device)
+
+
+def kivi_append_flush_ragged(cache, state, k_new, v_new):
+    """One new token per sequence (k_new, v_new fp16 [B, Hkv, D]); per-sequence flush and state
+    update on the device (state: int32 [B, 4] from seq_state)."""
+    for t in (k_new, v_new):
+        if not t.is_contiguous() or t.dtype != torch.float16:
+            raise ValueError("expected contiguous float16 [B, Hkv, D]")
+    if state.dtype != torch.int32 or not state.is_contiguous():
+        raise ValueError("expected contiguous int32 state [B, 4]")
+    _check(lib.kivi_append_flush_ragged(C.byref(cache.c), _ptr(state), _ptr(k_new), _ptr(v_new), _stream(k_new)),
+           "kivi_append_flush_ragged")
+
+
+def kivi_decode_attn_ragged(cache, state, q, sm_scale, out=None, lse=None, num_splits=0, workspace=None):
+    """kivi_decode_attn with per-sequence states (state: int32 [B, 4] from seq_state)."""
+    if not q.is_contiguous() or q.dtype != torch.float16:
+        raise ValueError("expected contiguous float16 q [B, Hq, D]")
+    if state.dtype != torch.int32 or not state.is_contiguous():
+        raise ValueError("expected contiguous int32 state [B, 4]")
+    B, Hq, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    want_lse = lse is not None and lse is not False
+    if lse is True:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    splits = num_splits if num_splits > 0 else kivi_decode_attn_ragged_splits(cache, Hq)
+    ws = workspace if workspace is not None else cache.workspace(Hq, splits)
+    _check(lib.kivi_decode_attn_ragged(C.byref(cache.c), _ptr(state), _ptr(q), Hq, float(sm_scale), _ptr(out),
+                                       _ptr(lse) if want_lse else None, _ptr(ws), ws.numel() * ws.element_size(),
+                                       num_splits, _stream(q)), "kivi_decode_attn_ragged")
+    return (out, lse) if want_lse else out
+
+
+def kivi_decode_attn_ragged_splits(cache, q_heads):
+    s = lib.kivi_decode_attn_ragged_splits(C.byref(cache.c), q_heads)
+    if s < 0:
+        raise KiviError(s, "kivi_decode_attn_ragged_splits")
+    return s
 
 
 def kivi_decode_attn_fp16(k, v, q, sm_scale, tokens=None, out=None, lse=None, num_splits=0, workspace=None):

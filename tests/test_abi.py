@@ -21,7 +21,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 14
+    assert len(names) == 17
     out = os.popen(f"nm -D --defined-only {kivi.LIB_PATH}").read()
     exported = set(re.findall(r" T (kivi_\w+)$", out, re.M))
     assert set(names) <= exported, set(names) - exported
@@ -78,6 +78,31 @@ def test_fp16_comparator_arguments():
     need = L.kivi_decode_attn_fp16_workspace(1, 32, 131072, 32, 0)
     assert need == 256 + ((24 * 32 * 130 * 4 + 255) // 256) * 256
     assert L.kivi_decode_attn_fp16_workspace(1, 1, 0, 1, 0) == 0
+
+
+def test_ragged_arguments():
+    """The ragged calls check the descriptor and pointers on the host; the per-sequence
+    states live on the device and are checked by the kernels (GPU tests)."""
+    c = _cache(n_quant=0, n_res=0)             # the descriptor's own state is not used
+    st = C.c_void_p(FAKE)
+    P = C.c_void_p(FAKE)
+    fa = L.kivi_append_flush_ragged
+    assert fa(C.byref(c), None, P, P, None) == -1
+    assert fa(C.byref(c), st, None, P, None) == -1
+    assert fa(C.byref(c), C.c_void_p(FAKE + 4), P, P, None) == -2       # state not 16-byte aligned
+    assert fa(C.byref(_cache(head_dim=64)), st, P, P, None) == -3
+    assert fa(C.byref(_cache(k_res=0)), st, P, P, None) == -1
+    fd = L.kivi_decode_attn_ragged
+    ws = C.c_void_p(FAKE)
+    assert fd(C.byref(c), None, P, 4, 0.1, P, None, ws, 1 << 30, 0, None) == -1
+    assert fd(C.byref(c), C.c_void_p(FAKE + 8), P, 4, 0.1, P, None, ws, 1 << 30, 0, None) == -2
+    assert fd(C.byref(c), st, P, 3, 0.1, P, None, ws, 1 << 30, 0, None) == -2   # q_heads % kv_heads
+    assert fd(C.byref(c), st, P, 4, 0.1, P, None, ws, 16, 0, None) == -5        # workspace too small
+    # split count for the longest context the cache holds: 256 tokens = 8 groups -> 1 split
+    assert L.kivi_decode_attn_ragged_splits(C.byref(c), 4) == 1
+    big = _cache(batch=1, kv_heads=32, token_cap=131072, n_quant=0, n_res=0)
+    assert L.kivi_decode_attn_ragged_splits(C.byref(big), 32) == 24
+    assert L.kivi_decode_attn_ragged_splits(C.byref(big), 31) == -2
 
 
 def test_status_strings():
