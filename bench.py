@@ -11,7 +11,8 @@ seeded synthetic tensors already resident in HBM when the timed region starts.
 Prints ONE JSON line.  Metric: achieved HBM GB/s (algorithmic bytes / time) and tokens/s.
 After the timed steps, the fp16 comparator (kivi_decode_attn_fp16: the same attention over
 an uncompressed fp16 cache of the starting context) is timed the same way and reported
-beside it ("fp16_comparator"; --no-fp16 skips it).
+beside it ("fp16_comparator"; --no-fp16 skips it), and so is the ragged-batch path on a
+serving batch of 64 sequences at different lengths ("ragged_batch"; --no-ragged skips it).
 """
 import argparse
 import json
@@ -99,6 +100,52 @@ def cpu_baseline(w, k, v, n_heads, steps_tokens, threads):
     }
 
 
+def ragged_measure(kivi, synth, dev, steps, warmup, seed=2402):
+    """Ragged batch (sequences at different lengths, per-sequence state on the device): the
+    query-group serving shape (batch 64, 32 query heads over 8 kv heads) with context lengths
+    drawn uniformly from [512, 8192] tokens; each sequence keeps 64..95 of them in the fp16
+    residual.  Times kivi_decode_attn_ragged (kernel-recorded events) against the algorithmic
+    bytes of the real lengths."""
+    B, Hq, Hkv, lo, hi = 64, 32, 8, 512, 8192
+    rng = np.random.default_rng(seed)
+    lengths = rng.integers(lo, hi + 1, size=B)
+    cache = kivi.Cache(B, Hkv, hi, device=dev)
+    states, byts = [], 2 * B * Hq * D * 2
+    for b, L in enumerate(lengths):
+        nq = int((L - 64) // G * G)
+        w = synth.small(seed=seed + b, batch=1, q_heads=Hq, kv_heads=Hkv, context=int(L), n_quant=nq)
+        k, v = synth.prefill_kv(w, device=dev)
+        view = cache.sequence(b)
+        kivi.kivi_prefill(k, v, nq, view)
+        states.append(view.state)
+        byts += Hkv * (nq * QUANT_TOKEN_BYTES + (int(L) - nq) * RES_TOKEN_BYTES)
+    state = kivi.seq_state(states, device=dev)
+    qw = synth.small(seed=seed + 999, batch=B, q_heads=Hq, kv_heads=Hkv, context=1, n_quant=0)
+    queries = [synth.query(qw, step=s, device=dev) for s in range(steps + warmup)]
+    out = torch.empty_like(queries[0])
+    splits = kivi.kivi_decode_attn_ragged_splits(cache, Hq)
+    ws = cache.workspace(Hq, splits)
+    for s in range(warmup):
+        kivi.kivi_decode_attn_ragged(cache, state, queries[s], synth.SM_SCALE_D128, out=out, workspace=ws)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for pair in ev:
+        for e in pair:
+            e.record()
+    torch.cuda.synchronize()
+    for i in range(steps):
+        kivi.kivi_time_next_attention(*ev[i])
+        kivi.kivi_decode_attn_ragged(cache, state, queries[warmup + i], synth.SM_SCALE_D128, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+    return {
+        "workload": "batch 64, 32 q / 8 kv heads, context lengths uniform in [512, 8192] (seeded)",
+        "tokens": int(lengths.sum()), "mean_context": round(float(lengths.mean()), 1), "splits": splits,
+        "decode_attn_us": round(us, 2), "bytes_per_launch": int(byts), "achieved": round(byts / us / 1e3, 1),
+        "unit": "GB/s", "frac": round(byts / us / 1e3 / PEAK_HBM_GBS, 4),
+        "tokens_per_s": round(B * 1e6 / us, 1),
+    }
+
+
 def read_traffic(workload):
     """HBM bytes per launch from committed rocprofv3 counters, if they were taken on the
     current kernel sources; else None."""
@@ -124,6 +171,7 @@ def main():
     ap.add_argument("--splits", type=int, default=0, help="split count override (0: library's choice)")
     ap.add_argument("--separate", action="store_true", help="time kivi_append_flush + kivi_decode_attn")
     ap.add_argument("--no-fp16", action="store_true", help="skip the fp16 comparator")
+    ap.add_argument("--no-ragged", action="store_true", help="skip the ragged-batch measurement")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the decode hot path shards "
@@ -260,7 +308,11 @@ def main():
         },
         "cpu_baseline": None,
         "fp16_comparator": fp16,
+        "ragged_batch": None,
     }
+    if not args.no_ragged:
+        del cache, ws
+        res["ragged_batch"] = ragged_measure(kivi, synth, dev, args.steps, args.warmup)
     if args.cpu_heads > 0:
         kn, vn = steps_kv[0]
         res["cpu_baseline"] = cpu_baseline(w, k, v, min(args.cpu_heads, w.kv_heads), (kn, vn),

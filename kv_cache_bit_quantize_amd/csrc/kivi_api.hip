@@ -87,9 +87,16 @@ int32_t auto_splits_for(const kivi_cache* c, int32_t q_heads, int64_t groups) {
     return (int32_t)s;
 }
 int32_t auto_splits(const kivi_cache* c, int32_t q_heads) { return auto_splits_for(c, q_heads, c->n_quant / c->group); }
-// ragged batch: sized for the longest context the cache can hold
+// ragged batch: room for four times the splits of the longest context the cache can hold;
+// the kernels plan from the real lengths how many of them each sequence uses
 int32_t ragged_auto_splits(const kivi_cache* c, int32_t q_heads) {
-    return auto_splits_for(c, q_heads, c->token_cap / c->group);
+    const int64_t groups = c->token_cap / c->group;
+    int64_t s = 4 * (int64_t)auto_splits_for(c, q_heads, groups);
+    const int64_t cap = groups / kMinGroupsPerSplit;
+    if (s > cap) s = cap;
+    if (s < 1) s = 1;
+    if (s > kMaxSplits) s = kMaxSplits;
+    return (int32_t)s;
 }
 
 // leading area of the attention workspace: one arrival counter per query row
@@ -220,6 +227,7 @@ int prepare_attn(const kivi_cache* c, const uint16_t* q, int32_t q_heads, float 
     a.k_ring = a.v_ring = nullptr;
     a.new_slot = 0;
     a.seq_state = seq_state;
+    a.slot_budget = (int32_t)kTargetBlocks;   // three resident workgroups per CU
     *pa = a;
     return KIVI_OK;
 }

@@ -49,8 +49,8 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
     __shared__ __align__(16) float sh_o[1][kSlots][kD];
     __shared__ float sh_m[1][kSlots], sh_l[1][kSlots];
 
-    const int split = blockIdx.x;
-    const int64_t qrow = blockIdx.y;
+    const int split = grid_split(a);
+    const int64_t qrow = grid_row(a);
     const int64_t b = qrow / a.q_heads;
     const int hq = (int)(qrow % a.q_heads);
     const int64_t kvrow = b * a.kv_heads + hq / a.ratio;
@@ -100,6 +100,7 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
     float vs = 0.0f;                   // power-of-two factor keeping the value weights in fp16 range
 
     const RowState rs = row_state(a, kvrow, split);
+    if (split >= rs.splits) return;   // (ragged batch) this row uses fewer splits: the whole workgroup leaves
     const int n_groups = rs.n_quant / kG;
     const int g_lo = split * rs.groups_per_split;
     const int g_hi = min(n_groups, g_lo + rs.groups_per_split);
@@ -296,7 +297,7 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
 
     // ---- fp16 residual (last split only), as separate states
     float mr[1], lr[1];
-    if (split == a.splits - 1) {
+    if (split == rs.res_split) {
         residual_states<1>(a, rs, qrow, kvrow, wave, &sh_o[0][kWaves + wave][0], kSlots * kD, mr, lr);
     } else {
         mr[0] = -INFINITY;
@@ -307,13 +308,12 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
         sh_l[0][kWaves + wave] = lr[0];
     }
     __syncthreads();
-    finish_block<1>(a, split, qrow, qrow, sh_o, sh_m, sh_l);
+    finish_block<1>(a, rs.splits, split, qrow, qrow, sh_o, sh_m, sh_l);
 }
 
 hipError_t launch_decode_attn(const AttnArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
     if (a.nq > 1) return launch_decode_attn_gqa(a, s, t0, t1);
-    hipExtLaunchKernelGGL(attn_split_kernel, dim3((unsigned)a.splits, (unsigned)a.q_rows), dim3(kBlock), 0, s, t0, t1,
-                          0, a);
+    hipExtLaunchKernelGGL(attn_split_kernel, attn_grid(a, a.q_rows), dim3(kBlock), 0, s, t0, t1, 0, a);
     return hipGetLastError();
 }
 

@@ -96,14 +96,52 @@ __device__ __forceinline__ float load_coherent(float* p) {
 // s_waitcnt with vmcnt(0) and the other counters left free (expcnt 7, lgkmcnt 15)
 constexpr int kWaitVmcnt0 = 0x0F70;
 
+// Grid of a decode-attention launch.  Workgroups go to the XCDs round-robin by linear id.
+// Normally x = split: a row's splits spread over the XCDs.  In a ragged batch the
+// sequences use different numbers of splits, so x = row instead (a sequence's kv heads are
+// consecutive rows, so every XCD gets a share of every sequence whatever its length).
+// The layout is chosen in launch code and kernels alike from a.seq_state.
+inline dim3 attn_grid(const AttnArgs& a, int64_t rows) {
+    return a.seq_state != nullptr ? dim3((unsigned)rows, (unsigned)a.splits) : dim3((unsigned)a.splits, (unsigned)rows);
+}
+__device__ __forceinline__ int grid_split(const AttnArgs& a) {
+    return a.seq_state != nullptr ? (int)blockIdx.y : (int)blockIdx.x;
+}
+__device__ __forceinline__ int64_t grid_row(const AttnArgs& a) {
+    return a.seq_state != nullptr ? (int64_t)blockIdx.x : (int64_t)blockIdx.y;
+}
+
 // The cache state one workgroup attends over: the call's, or (ragged batch) its sequence's,
-// with that sequence's share of key groups per split.  A sequence state out of range gives
-// an empty context (nothing is read) and sets the sequence's kSeqBadState flag.
+// with the number of splits its row uses, its key groups per split and the split that also
+// reads the residual.  A sequence state out of range gives an empty context (nothing is
+// read) and sets the sequence's kSeqBadState flag.
+//
+// Ragged batch plan, the same in every workgroup: the batch's work W (key groups, with the
+// residual counted as groups by its bytes) is read from all sequence states; a workgroup
+// should take about W * rows_per_sequence / slot_budget of it, so that the whole batch fits
+// one round of resident workgroups with even shares; a sequence uses floor(its work / that
+// share) splits (at least one, at most the grid's).  Workgroups past their row's count do
+// nothing.
 struct RowState {
-    int32_t n_quant, n_res, res_head, groups_per_split;
+    int32_t n_quant, n_res, res_head, groups_per_split, res_split, splits;
 };
+// key groups the residual counts as (512 bytes per fp16 token against 96 per 2-bit token)
+__device__ __forceinline__ int32_t residual_units(int32_t n_res) { return (n_res * 512 + 96 * kG - 1) / (96 * kG); }
+// The batch's total work, by each wave: lane i reads sequence i's state (one coalesced
+// 16-byte load per lane and 64 sequences), then a wave sum.
+__device__ __forceinline__ int32_t batch_units(const AttnArgs& a, int64_t batch) {
+    const int lane = threadIdx.x & 63;
+    int32_t u = 0;
+    for (int64_t b = lane; b < batch; b += 64) {
+        const int4 st = *reinterpret_cast<const int4*>(a.seq_state + 4 * b);
+        if (state_in_range(st.x, st.y, st.z, a.token_cap, a.residual_cap)) u += st.x / kG + residual_units(st.y);
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) u += __shfl_xor(u, m, 64);
+    return __builtin_amdgcn_readfirstlane(u);
+}
 __device__ __forceinline__ RowState row_state(const AttnArgs& a, int64_t kvrow, int split) {
-    if (a.seq_state == nullptr) return {a.n_quant, a.n_res, a.res_head, a.groups_per_split};
+    if (a.seq_state == nullptr) return {a.n_quant, a.n_res, a.res_head, a.groups_per_split, a.splits - 1, a.splits};
     int32_t* s = a.seq_state + 4 * (kvrow / a.kv_heads);
     int32_t nq = s[0], nr = s[1], rh = s[2];
     if (!state_in_range(nq, nr, rh, a.token_cap, a.residual_cap)) {
@@ -111,9 +149,13 @@ __device__ __forceinline__ RowState row_state(const AttnArgs& a, int64_t kvrow, 
             __hip_atomic_fetch_or(&s[3], kSeqBadState, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         nq = nr = rh = 0;
     }
-    // the split that also reads the residual counts it as that many quantized groups
-    const int32_t res_groups = (nr * 512 + 96 * kG - 1) / (96 * kG);
-    return {nq, nr, rh, (nq / kG + res_groups + a.splits - 1) / a.splits};
+    const int32_t units = nq / kG + residual_units(nr);
+    const int64_t batch = a.q_rows / a.q_heads;
+    const int64_t total = batch_units(a, batch);
+    const int64_t rows_per_seq = a.block_rows / batch;
+    const int64_t share = max((int64_t)1, (total * rows_per_seq + a.slot_budget - 1) / a.slot_budget);
+    const int32_t active = (int32_t)max((int64_t)1, min((int64_t)a.splits, (int64_t)units / share));
+    return {nq, nr, rh, (units + active - 1) / active, active - 1, active};
 }
 
 // Softmax states of query rows qrow0..qrow0+NQ-1 over the fp16 residual ring.  Called by one
@@ -253,7 +295,7 @@ __device__ __forceinline__ void store_new_token(const AttnArgs& a, int64_t kvrow
 // lse = (M + log2 L) ln 2.  Re-arms the arrival counter.
 constexpr int kMergeBatch = 16;
 template <int NQ, int THREADS = kBlock>
-__device__ __forceinline__ void merge_rows(const AttnArgs& a, int64_t qrow0, int64_t counter) {
+__device__ __forceinline__ void merge_rows(const AttnArgs& a, int splits, int64_t qrow0, int64_t counter) {
     constexpr int kLpp = NQ == 1 ? 2 : 1;
     static_assert(kLpp == 1 || THREADS == 2 * kD, "two threads per channel need 256 threads");
     __shared__ float sh_mo[kD + 2];
@@ -263,14 +305,14 @@ __device__ __forceinline__ void merge_rows(const AttnArgs& a, int64_t qrow0, int
         const int r = idx / kD, j = idx % kD;
         float* rowp = a.ws + (qrow0 + r) * kPart;
         float M = -INFINITY, L = 0.0f, O = 0.0f;
-        for (int s0 = sub; s0 < a.splits; s0 += kLpp * kMergeBatch) {
+        for (int s0 = sub; s0 < splits; s0 += kLpp * kMergeBatch) {
             float ms[kMergeBatch], ls[kMergeBatch], os[kMergeBatch];
 #pragma unroll
             for (int u = 0; u < kMergeBatch; ++u) {
                 const int s = s0 + kLpp * u;
                 ms[u] = -INFINITY;
                 ls[u] = os[u] = 0.0f;
-                if (s < a.splits) {
+                if (s < splits) {
                     float* ps = rowp + s * stride;
                     ms[u] = load_coherent(ps + kD);
                     ls[u] = load_coherent(ps + kD + 1);
@@ -316,7 +358,7 @@ __device__ __forceinline__ void merge_rows(const AttnArgs& a, int64_t qrow0, int
 // this workgroup completed (the wait, then the barrier), and the merging workgroup issues its
 // coherent loads only after its own add returned the final count, so it reads every partial.
 template <int NQ, int WAVES = kWaves>
-__device__ __forceinline__ void finish_block(const AttnArgs& a, int split, int64_t qrow0, int64_t counter,
+__device__ __forceinline__ void finish_block(const AttnArgs& a, int splits, int split, int64_t qrow0, int64_t counter,
                                              const float (*sh_o)[2 * WAVES][kD], const float (*sh_m)[2 * WAVES],
                                              const float (*sh_l)[2 * WAVES]) {
     constexpr int kS = 2 * WAVES;
@@ -333,7 +375,7 @@ __device__ __forceinline__ void finish_block(const AttnArgs& a, int split, int64
             L = fmaf(sh_l[r][w], sc, L);
             O = fmaf(sh_o[r][w][j], sc, O);
         }
-        if (a.splits == 1) {
+        if (splits == 1) {
             // an empty context (a ragged batch's empty sequence) gives out = 0, lse = -inf
             a.out[(qrow0 + r) * kD + j] = (uint16_t)f2h(L > 0.0f ? O / L : 0.0f);
             if (j == 0 && a.lse != nullptr) a.lse[qrow0 + r] = (M + log2f(L)) * 0.69314718055994531f;
@@ -346,15 +388,15 @@ __device__ __forceinline__ void finish_block(const AttnArgs& a, int split, int64
             }
         }
     }
-    if (a.splits == 1) return;
+    if (splits == 1) return;
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // the partial stores have completed
     __syncthreads();
     __shared__ bool sh_last;
     if (threadIdx.x == 0)
         sh_last = __hip_atomic_fetch_add(&a.counters[counter], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                  (unsigned)(a.splits - 1);
+                  (unsigned)(splits - 1);
     __syncthreads();
-    if (sh_last) merge_rows<NQ, 64 * WAVES>(a, qrow0, counter);
+    if (sh_last) merge_rows<NQ, 64 * WAVES>(a, splits, qrow0, counter);
 }
 
 }  // namespace kivi

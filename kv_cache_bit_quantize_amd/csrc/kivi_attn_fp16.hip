@@ -187,7 +187,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
         }
     }
     __syncthreads();
-    finish_block<NQ>(a, split, qrow0, grow, sh_o, sh_m, sh_l);
+    finish_block<NQ>(a, a.splits, split, qrow0, grow, sh_o, sh_m, sh_l);
 }
 
 hipError_t launch_decode_attn_fp16(const AttnArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {

@@ -47,8 +47,8 @@ __global__ __launch_bounds__(kGqaBlock) __attribute__((amdgpu_waves_per_eu(3))) 
     __shared__ __align__(16) float sh_o[NQ][S][kD];
     __shared__ float sh_m[NQ][S], sh_l[NQ][S];
 
-    const int split = blockIdx.x;
-    const int64_t grow = blockIdx.y;                 // (batch, kv head, query chunk)
+    const int split = grid_split(a);
+    const int64_t grow = grid_row(a);                 // (batch, kv head, query chunk)
     const int chunks = a.ratio / NQ;
     const int64_t kvrow = grow / chunks;
     const int chunk = (int)(grow % chunks);
@@ -116,6 +116,7 @@ __global__ __launch_bounds__(kGqaBlock) __attribute__((amdgpu_waves_per_eu(3))) 
     float vs = 0.0f;                    // power-of-two factor keeping the value weights in fp16 range
 
     const RowState rs = row_state(a, kvrow, split);
+    if (split >= rs.splits) return;   // (ragged batch) this row uses fewer splits: the whole workgroup leaves
     const int n_groups = rs.n_quant / kG;
     const int g_lo = split * rs.groups_per_split;
     const int g_hi = min(n_groups, g_lo + rs.groups_per_split);
@@ -389,7 +390,7 @@ __global__ __launch_bounds__(kGqaBlock) __attribute__((amdgpu_waves_per_eu(3))) 
     // its loads from being hoisted above this point, where the accumulators are still live.
     __builtin_amdgcn_sched_barrier(0);
     float mr[NQ], lr[NQ];
-    if (split == a.splits - 1) {
+    if (split == rs.res_split) {
         residual_states<NQ, W>(a, rs, qrow0, kvrow, wave, &sh_o[0][W + wave][0], S * kD, mr, lr);
     } else {
 #pragma unroll
@@ -406,11 +407,11 @@ __global__ __launch_bounds__(kGqaBlock) __attribute__((amdgpu_waves_per_eu(3))) 
         }
     }
     __syncthreads();
-    finish_block<NQ, W>(a, split, qrow0, grow, sh_o, sh_m, sh_l);
+    finish_block<NQ, W>(a, rs.splits, split, qrow0, grow, sh_o, sh_m, sh_l);
 }
 
 hipError_t launch_decode_attn_gqa(const AttnArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
-    const dim3 grid((unsigned)a.splits, (unsigned)a.block_rows);
+    const dim3 grid = attn_grid(a, a.block_rows);
     switch (a.nq) {
         case 2: hipExtLaunchKernelGGL(attn_gqa_kernel<2>, grid, dim3(kGqaBlock), 0, s, t0, t1, 0, a); break;
         case 3: hipExtLaunchKernelGGL(attn_gqa_kernel<3>, grid, dim3(kGqaBlock), 0, s, t0, t1, 0, a); break;

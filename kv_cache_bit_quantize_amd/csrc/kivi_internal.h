@@ -87,6 +87,7 @@ struct AttnArgs {
     // ragged batch: per-sequence state [batch][4] (n_quant, n_res, res_head, flags) in device
     // memory; when set it replaces n_quant, n_res, res_head and groups_per_split per row
     int32_t* seq_state;
+    int32_t slot_budget;        // ragged batch: workgroups resident in one round (the plan's target)
 };
 
 // bits of a sequence's flags word (ragged calls; only ever set, by the kernels)

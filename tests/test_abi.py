@@ -101,7 +101,7 @@ def test_ragged_arguments():
     # split count for the longest context the cache holds: 256 tokens = 8 groups -> 1 split
     assert L.kivi_decode_attn_ragged_splits(C.byref(c), 4) == 1
     big = _cache(batch=1, kv_heads=32, token_cap=131072, n_quant=0, n_res=0)
-    assert L.kivi_decode_attn_ragged_splits(C.byref(big), 32) == 24
+    assert L.kivi_decode_attn_ragged_splits(C.byref(big), 32) == 96   # four times the uniform count
     assert L.kivi_decode_attn_ragged_splits(C.byref(big), 31) == -2
 
 
