@@ -149,7 +149,9 @@ int kivi_decode_attn(const kivi_cache* cache, const uint16_t* q, int32_t q_heads
  * included).  When the ring has room it is one kernel launch: attention reads the new
  * token straight from k_new / v_new while one workgroup per KV head writes it into its
  * ring slot; when a group must be flushed first it is the two launches of the separate
- * calls.  Validation happens before anything is enqueued, so on error nothing changes. */
+ * calls.  The workspace must fit the attention on the state after the append: when the
+ * ring is full that is kivi_decode_attn_workspace of the cache with n_quant + group.
+ * Validation happens before anything is enqueued, so on error nothing changes. */
 int kivi_decode_step(kivi_cache* cache, const uint16_t* k_new, const uint16_t* v_new,
                      const uint16_t* q, int32_t q_heads, float sm_scale, uint16_t* out, float* lse,
                      void* workspace, size_t workspace_bytes, int32_t num_splits, int32_t* flushed,

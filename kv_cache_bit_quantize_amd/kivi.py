@@ -139,7 +139,14 @@ class Cache:
         return v
 
     def workspace(self, q_heads, num_splits=0):
+        """Attention workspace for this cache, also large enough for the state after the
+        next append (a decode step attends after its append, and a flush lengthens the history,
+        which can raise the automatic split count)."""
         need = lib.kivi_decode_attn_workspace(C.byref(self.c), q_heads, num_splits)
+        if self.c.n_res == self.c.residual_cap and self.c.n_quant + self.c.group <= self.c.token_cap:
+            nxt = kivi_cache.from_buffer_copy(self.c)
+            nxt.n_quant += nxt.group
+            need = max(need, lib.kivi_decode_attn_workspace(C.byref(nxt), q_heads, num_splits))
         if self._ws is None or self._ws.numel() < need:
             # zero-filled: the leading per-row arrival counters must start at zero
             self._ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=self.device)

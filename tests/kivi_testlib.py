@@ -38,10 +38,10 @@ def bits(t):
     return t.numpy().view(np.uint16)
 
 
-def ref_cache(batch, kv_heads, token_cap, k, v, n_quant):
+def ref_cache(batch, kv_heads, token_cap, k, v, n_quant, residual_cap=128):
     """Oracle cache prefilled from fp16 tensors k, v [B, H, T, D]."""
     B, H, T, D = k.shape
-    c = ref.RefCache(batch, kv_heads, D, 32, 128, token_cap=token_cap)
+    c = ref.RefCache(batch, kv_heads, D, 32, residual_cap, token_cap=token_cap)
     c.prefill(bits(k).reshape(B * H, T, D), bits(v).reshape(B * H, T, D), n_quant)
     return c
 
