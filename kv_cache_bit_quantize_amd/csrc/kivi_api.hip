@@ -29,7 +29,7 @@ int check_shape(const kivi_cache* c) {
     if (c->head_dim % 4 != 0 || c->head_dim % c->group != 0 || c->residual_cap % c->group != 0 ||
         c->token_cap % c->group != 0)
         return KIVI_ERR_SHAPE;
-    if (c->head_dim != kD || c->group != kG) return KIVI_ERR_UNSUPPORTED;
+    if (c->head_dim != kD || !group_supported(c->group)) return KIVI_ERR_UNSUPPORTED;
     return KIVI_OK;
 }
 
@@ -86,11 +86,12 @@ int32_t auto_splits_for(const kivi_cache* c, int32_t q_heads, int64_t groups) {
     if (s > kMaxSplits) s = kMaxSplits;
     return (int32_t)s;
 }
-int32_t auto_splits(const kivi_cache* c, int32_t q_heads) { return auto_splits_for(c, q_heads, c->n_quant / c->group); }
+// (contexts are counted in 32-token code tiles, the attention kernels' unit of work)
+int32_t auto_splits(const kivi_cache* c, int32_t q_heads) { return auto_splits_for(c, q_heads, c->n_quant / kG); }
 // ragged batch: room for four times the splits of the longest context the cache can hold;
 // the kernels plan from the real lengths how many of them each sequence uses
 int32_t ragged_auto_splits(const kivi_cache* c, int32_t q_heads) {
-    const int64_t groups = c->token_cap / c->group;
+    const int64_t groups = c->token_cap / kG;
     int64_t s = 4 * (int64_t)auto_splits_for(c, q_heads, groups);
     const int64_t cap = groups / kMinGroupsPerSplit;
     if (s > cap) s = cap;
@@ -117,6 +118,7 @@ QuantArgs quant_args(const kivi_cache* c, const uint16_t* src, int32_t tokens, i
     a.v_codes = c->v_codes;
     a.k_sz = c->k_sz;
     a.v_sz = c->v_sz;
+    a.group = c->group;
     return a;
 }
 
@@ -156,6 +158,7 @@ int prepare_append(const kivi_cache* c, const uint16_t* k_new, const uint16_t* v
     a->v_res = c->v_res;
     a->seq_state = nullptr;   // one state for the whole batch (the fields above)
     a->kv_heads = c->kv_heads;
+    a->group = G;
     *next = *c;
     next->n_quant = n_quant;
     next->n_res = n_res + 1;
@@ -193,7 +196,7 @@ int prepare_attn(const kivi_cache* c, const uint16_t* q, int32_t q_heads, float 
     const size_t need = kivi_decode_attn_workspace(c, q_heads, splits);
     if (workspace == nullptr || workspace_bytes < need) return KIVI_ERR_WORKSPACE;
     if (reinterpret_cast<uintptr_t>(workspace) & 255u) return KIVI_ERR_WORKSPACE;
-    const int32_t groups = c->n_quant / c->group;
+    const int32_t groups = c->n_quant / kG;   // 32-token code tiles
     AttnArgs a{};
     a.q = q;
     a.k_codes = c->k_codes;
@@ -218,7 +221,7 @@ int prepare_attn(const kivi_cache* c, const uint16_t* q, int32_t q_heads, float 
     a.splits = splits;
     // The last split also reads the fp16 residual (512 bytes per token against 96 for a
     // quantized token): count it as that many groups so the last split gets fewer.
-    const int32_t res_groups = (c->n_res * 512 + 96 * c->group - 1) / (96 * c->group);
+    const int32_t res_groups = (c->n_res * 512 + 96 * kG - 1) / (96 * kG);
     a.groups_per_split = (groups + res_groups + splits - 1) / splits;
     a.q_rows = (int64_t)c->batch * q_heads;
     a.nq = queries_per_block(a.ratio);
@@ -228,6 +231,7 @@ int prepare_attn(const kivi_cache* c, const uint16_t* q, int32_t q_heads, float 
     a.new_slot = 0;
     a.seq_state = seq_state;
     a.slot_budget = (int32_t)kTargetBlocks;   // three resident workgroups per CU
+    a.group = c->group;
     *pa = a;
     return KIVI_OK;
 }
@@ -279,7 +283,7 @@ const char* kivi_status_str(int status) {
         case KIVI_OK: return "ok";
         case KIVI_ERR_NULL: return "a required pointer is NULL";
         case KIVI_ERR_SHAPE: return "inconsistent sizes, strides or alignment";
-        case KIVI_ERR_UNSUPPORTED: return "shape not implemented (head_dim must be 128, group 32)";
+        case KIVI_ERR_UNSUPPORTED: return "shape not implemented (head_dim must be 128, group 32, 64 or 128)";
         case KIVI_ERR_CAPACITY: return "the call would write past token_cap";
         case KIVI_ERR_WORKSPACE: return "workspace missing or too small";
         case KIVI_ERR_HIP: return "HIP runtime error while enqueueing";
@@ -405,6 +409,7 @@ int kivi_append_flush_ragged(const kivi_cache* c, int32_t* seq_state, const uint
     a.v_res = c->v_res;
     a.seq_state = seq_state;
     a.kv_heads = c->kv_heads;
+    a.group = c->group;
     return hip_status(launch_append_flush_ragged(a, c->batch, (hipStream_t)stream));
 }
 

@@ -44,6 +44,7 @@ constexpr int kWtOff = 2 * kGroupTbl;             // value weights [group][chgro
 constexpr int kZeroOff = kWtOff + 2 * 4 * 4 * 16;  // 512 zero bytes
 constexpr int kAreaBytes = kZeroOff + 512;
 
+template <int GS>
 __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
     __shared__ __align__(16) uint8_t sh_area[2][kWaves][kAreaBytes];
     __shared__ __align__(16) float sh_o[1][kSlots][kD];
@@ -113,8 +114,8 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
     const int64_t tok_base = kvrow * (int64_t)a.token_cap;
     const uint8_t* kc_row = a.k_codes + tok_base * kRowBytes;
     const uint8_t* vc_row = a.v_codes + tok_base * kRowBytes;
-    const uint32_t* kp_row = reinterpret_cast<const uint32_t*>(a.k_sz) + kvrow * (int64_t)(a.token_cap / kG) * kD;
-    const uint32_t* vp_row = reinterpret_cast<const uint32_t*>(a.v_sz) + tok_base * (kD / kG);
+    const uint32_t* kp_row = reinterpret_cast<const uint32_t*>(a.k_sz) + kvrow * (int64_t)(a.token_cap / GS) * kD;
+    const uint32_t* vp_row = reinterpret_cast<const uint32_t*>(a.v_sz) + tok_base * (kD / GS);
 
     constexpr uint32_t kF0 = 0x00030003u, kF1 = 0x000C000Cu, kF2 = 0x00300030u, kF3 = 0x00C000C0u;
 
@@ -133,7 +134,7 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
         return half == 0 ? g0 : (g0 + 1 < ge ? g0 + 1 : gb);   // in-bounds address for an idle half
     };
     auto load_kp = [&](Loads& L, int it) {
-        L.kp = *reinterpret_cast<const uint4*>(kp_row + (int64_t)group_of(it, gh) * kD + 4 * wl);
+        L.kp = *reinterpret_cast<const uint4*>(kp_row + (int64_t)(group_of(it, gh) / (GS / kG)) * kD + 4 * wl);
     };
     auto load_kc = [&](Loads& L, int it) {
         L.kc[0] = reinterpret_cast<const uint4*>(kc_row + (int64_t)group_of(it, 0) * kTileBytes)[lane];
@@ -144,7 +145,7 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
         L.vc[1] = reinterpret_cast<const uint4*>(vc_row + (int64_t)group_of(it, 1) * kTileBytes)[lane];
     };
     auto load_vp = [&](Loads& L, int it) {
-        L.vp = *reinterpret_cast<const uint4*>(vp_row + value_pair_index((int64_t)group_of(it, gh) * kG + tt, 0));
+        L.vp = load_value_pairs<GS>(vp_row + value_pair_index<GS>((int64_t)group_of(it, gh) * kG + tt, 0));
     };
 
     // Every load is issued unconditionally (past the end it reads the last iteration's data
@@ -313,7 +314,8 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
 
 hipError_t launch_decode_attn(const AttnArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
     if (a.nq > 1) return launch_decode_attn_gqa(a, s, t0, t1);
-    hipExtLaunchKernelGGL(attn_split_kernel, attn_grid(a, a.q_rows), dim3(kBlock), 0, s, t0, t1, 0, a);
+    KIVI_BY_GROUP(a.group, hipExtLaunchKernelGGL(attn_split_kernel<GS>, attn_grid(a, a.q_rows), dim3(kBlock), 0, s, t0,
+                                                 t1, 0, a))
     return hipGetLastError();
 }
 

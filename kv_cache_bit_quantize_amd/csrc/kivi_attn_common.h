@@ -96,6 +96,22 @@ __device__ __forceinline__ float load_coherent(float* p) {
 // s_waitcnt with vmcnt(0) and the other counters left free (expcnt 7, lgkmcnt 15)
 constexpr int kWaitVmcnt0 = 0x0F70;
 
+// The (scale, zero) pairs of one value token, kD / GS of them, loaded at their own width (a
+// wider load would read past the last token of the last row) and returned as one word per
+// 32-channel block: word k is the pair of the group that holds channels 32k..32k+31.
+template <int GS>
+__device__ __forceinline__ uint4 load_value_pairs(const uint32_t* p) {
+    if constexpr (GS == 32) {
+        return *reinterpret_cast<const uint4*>(p);
+    } else if constexpr (GS == 64) {
+        const uint2 x = *reinterpret_cast<const uint2*>(p);
+        return make_uint4(x.x, x.x, x.y, x.y);
+    } else {
+        const uint32_t x = *p;
+        return make_uint4(x, x, x, x);
+    }
+}
+
 // Grid of a decode-attention launch.  Workgroups go to the XCDs round-robin by linear id.
 // Normally x = split: a row's splits spread over the XCDs.  In a ragged batch the
 // sequences use different numbers of splits, so x = row instead (a sequence's kv heads are
@@ -134,7 +150,7 @@ __device__ __forceinline__ int32_t batch_units(const AttnArgs& a, int64_t batch)
     int32_t u = 0;
     for (int64_t b = lane; b < batch; b += 64) {
         const int4 st = *reinterpret_cast<const int4*>(a.seq_state + 4 * b);
-        if (state_in_range(st.x, st.y, st.z, a.token_cap, a.residual_cap)) u += st.x / kG + residual_units(st.y);
+        if (state_in_range(st.x, st.y, st.z, a.token_cap, a.residual_cap, a.group)) u += st.x / kG + residual_units(st.y);
     }
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) u += __shfl_xor(u, m, 64);
@@ -144,7 +160,7 @@ __device__ __forceinline__ RowState row_state(const AttnArgs& a, int64_t kvrow, 
     if (a.seq_state == nullptr) return {a.n_quant, a.n_res, a.res_head, a.groups_per_split, a.splits - 1, a.splits};
     int32_t* s = a.seq_state + 4 * (kvrow / a.kv_heads);
     int32_t nq = s[0], nr = s[1], rh = s[2];
-    if (!state_in_range(nq, nr, rh, a.token_cap, a.residual_cap)) {
+    if (!state_in_range(nq, nr, rh, a.token_cap, a.residual_cap, a.group)) {
         if (split == 0 && threadIdx.x == 0)
             __hip_atomic_fetch_or(&s[3], kSeqBadState, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         nq = nr = rh = 0;

@@ -38,7 +38,7 @@ struct GqaLds {
 constexpr int kGqaWaves = 4;
 constexpr int kGqaBlock = 64 * kGqaWaves;
 
-template <int NQ>
+template <int NQ, int GS>
 __global__ __launch_bounds__(kGqaBlock) __attribute__((amdgpu_waves_per_eu(3))) void attn_gqa_kernel(AttnArgs a) {
     using Lds = GqaLds<NQ>;
     constexpr int W = kGqaWaves, S = 2 * kGqaWaves;
@@ -129,8 +129,8 @@ __global__ __launch_bounds__(kGqaBlock) __attribute__((amdgpu_waves_per_eu(3))) 
     const int64_t tok_base = kvrow * (int64_t)a.token_cap;
     const uint8_t* kc_row = a.k_codes + tok_base * kRowBytes;
     const uint8_t* vc_row = a.v_codes + tok_base * kRowBytes;
-    const uint32_t* kp_row = reinterpret_cast<const uint32_t*>(a.k_sz) + kvrow * (int64_t)(a.token_cap / kG) * kD;
-    const uint32_t* vp_row = reinterpret_cast<const uint32_t*>(a.v_sz) + tok_base * (kD / kG);
+    const uint32_t* kp_row = reinterpret_cast<const uint32_t*>(a.k_sz) + kvrow * (int64_t)(a.token_cap / GS) * kD;
+    const uint32_t* vp_row = reinterpret_cast<const uint32_t*>(a.v_sz) + tok_base * (kD / GS);
 
     constexpr uint32_t kF0 = 0x00030003u, kF1 = 0x000C000Cu, kF2 = 0x00300030u, kF3 = 0x00C000C0u;
 
@@ -147,7 +147,7 @@ __global__ __launch_bounds__(kGqaBlock) __attribute__((amdgpu_waves_per_eu(3))) 
         return half == 0 ? g0 : (g0 + 1 < ge ? g0 + 1 : gb);   // in-bounds address for an idle half
     };
     auto load_kp = [&](Loads& L, int it) {
-        L.kp = *reinterpret_cast<const uint4*>(kp_row + (int64_t)group_of(it, gh) * kD + 4 * wl);
+        L.kp = *reinterpret_cast<const uint4*>(kp_row + (int64_t)(group_of(it, gh) / (GS / kG)) * kD + 4 * wl);
     };
     auto load_kc = [&](Loads& L, int it) {
         L.kc[0] = reinterpret_cast<const uint4*>(kc_row + (int64_t)group_of(it, 0) * kTileBytes)[lane];
@@ -158,7 +158,7 @@ __global__ __launch_bounds__(kGqaBlock) __attribute__((amdgpu_waves_per_eu(3))) 
         L.vc[1] = reinterpret_cast<const uint4*>(vc_row + (int64_t)group_of(it, 1) * kTileBytes)[lane];
     };
     auto load_vp = [&](Loads& L, int it) {
-        L.vp = *reinterpret_cast<const uint4*>(vp_row + value_pair_index((int64_t)group_of(it, gh) * kG + tt, 0));
+        L.vp = load_value_pairs<GS>(vp_row + value_pair_index<GS>((int64_t)group_of(it, gh) * kG + tt, 0));
     };
 
     __syncthreads();   // the zero area is written
@@ -413,9 +413,15 @@ __global__ __launch_bounds__(kGqaBlock) __attribute__((amdgpu_waves_per_eu(3))) 
 hipError_t launch_decode_attn_gqa(const AttnArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
     const dim3 grid = attn_grid(a, a.block_rows);
     switch (a.nq) {
-        case 2: hipExtLaunchKernelGGL(attn_gqa_kernel<2>, grid, dim3(kGqaBlock), 0, s, t0, t1, 0, a); break;
-        case 3: hipExtLaunchKernelGGL(attn_gqa_kernel<3>, grid, dim3(kGqaBlock), 0, s, t0, t1, 0, a); break;
-        case 4: hipExtLaunchKernelGGL(attn_gqa_kernel<4>, grid, dim3(kGqaBlock), 0, s, t0, t1, 0, a); break;
+        case 2:
+            KIVI_BY_GROUP(a.group, hipExtLaunchKernelGGL(attn_gqa_kernel<2, GS>, grid, dim3(kGqaBlock), 0, s, t0, t1, 0, a))
+            break;
+        case 3:
+            KIVI_BY_GROUP(a.group, hipExtLaunchKernelGGL(attn_gqa_kernel<3, GS>, grid, dim3(kGqaBlock), 0, s, t0, t1, 0, a))
+            break;
+        case 4:
+            KIVI_BY_GROUP(a.group, hipExtLaunchKernelGGL(attn_gqa_kernel<4, GS>, grid, dim3(kGqaBlock), 0, s, t0, t1, 0, a))
+            break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -10,7 +10,18 @@
 namespace kivi {
 
 constexpr int kD = 128;             // head_dim implemented here
-constexpr int kG = 32;              // group size (tokens for keys, channels for values)
+constexpr int kG = 32;              // tokens per packed code tile, and the smallest group size
+// Group sizes (tokens per key group, channels per value group) the kernels are built for.
+__host__ __device__ constexpr bool group_supported(int g) { return g == 32 || g == 64 || g == 128; }
+// Launch code: one template instance per supported group size (GS inside CALL).
+#define KIVI_BY_GROUP(G, CALL)                  \
+    switch (G) {                                \
+        case 32: { constexpr int GS = 32; CALL; break; }   \
+        case 64: { constexpr int GS = 64; CALL; break; }   \
+        case 128: { constexpr int GS = 128; CALL; break; } \
+        default: return hipErrorInvalidValue;   \
+    }
+
 constexpr int kRowBytes = kD / 4;   // packed code bytes per token
 constexpr int kBlock = 256;         // threads per workgroup (4 wave64)
 
@@ -36,14 +47,16 @@ __host__ __device__ constexpr int64_t key_word_offset(int64_t t, int w) {
     return (t >> 5) * kTileBytes + ((w & 3) * 16 + (t & 15)) * 16 + ((t >> 4) & 1) * 8 + (w >> 2) * 4;
 }
 // index (in 32-bit pairs), inside a row, of the value (scale, zero) of token t, group k
-__host__ __device__ constexpr int64_t value_pair_index(int64_t t, int k) { return t * (kD / kG) + k; }
+// (groups of GS channels: kD / GS pairs per token)
+template <int GS = kG>
+__host__ __device__ constexpr int64_t value_pair_index(int64_t t, int k) { return t * (kD / GS) + k; }
 
 // A cache state the kernels can use without reading outside the buffers: whole groups in the
-// history, within capacity, and a ring head on a group boundary.
+// history, within capacity, and a ring head on a group boundary (group: tokens per key group).
 __host__ __device__ inline bool state_in_range(int32_t n_quant, int32_t n_res, int32_t res_head, int32_t token_cap,
-                                               int32_t residual_cap) {
-    return n_quant >= 0 && n_quant <= token_cap && n_quant % kG == 0 && n_res >= 0 && n_res <= residual_cap &&
-           res_head >= 0 && res_head < residual_cap && res_head % kG == 0;
+                                               int32_t residual_cap, int32_t group) {
+    return n_quant >= 0 && n_quant <= token_cap && n_quant % group == 0 && n_res >= 0 && n_res <= residual_cap &&
+           res_head >= 0 && res_head < residual_cap && res_head % group == 0;
 }
 
 __device__ __forceinline__ float h2f(uint32_t h) {

@@ -9,6 +9,7 @@ namespace kivi {
 constexpr int kMaxSplits = 1024;   // upper bound on split-K partitions of one decode call
 
 struct QuantArgs {          // kivi_quantize_{k,v}
+    int32_t group;              // tokens per key group / channels per value group
     const uint16_t* src;
     int64_t src_row_stride;
     int64_t rows;
@@ -48,6 +49,7 @@ struct AppendArgs {
     // state instead of the fields above
     int32_t* seq_state;
     int32_t kv_heads;
+    int32_t group;              // tokens per key group (= channels per value group): 32, 64 or 128
 };
 
 struct AttnArgs {
@@ -87,7 +89,8 @@ struct AttnArgs {
     // ragged batch: per-sequence state [batch][4] (n_quant, n_res, res_head, flags) in device
     // memory; when set it replaces n_quant, n_res, res_head and groups_per_split per row
     int32_t* seq_state;
-    int32_t slot_budget;        // ragged batch: workgroups resident in one round (the plan's target)
+    int32_t slot_budget;        // ragged batch: workgroups resident at once (the plan's target)
+    int32_t group;              // tokens per key group (= channels per value group): 32, 64 or 128
 };
 
 // bits of a sequence's flags word (ragged calls; only ever set, by the kernels)

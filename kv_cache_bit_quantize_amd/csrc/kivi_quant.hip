@@ -1,8 +1,11 @@
 // kivi_quant.hip -- quantize, prefill, append and group-flush kernels (gfx950).
 //
-// Keys are quantized per-channel over groups of 32 tokens, values per-token over
-// groups of 32 channels (record kv-efficiency/kivi-2bit-llama2-13b-mha-4k, "Quant
-// method"; article "Your KV cache doesn't have a bit problem...", paragraphs 2-3).
+// Keys are quantized per-channel over groups of G tokens, values per-token over groups
+// of G channels, G = 32 by default and 64 or 128 as the pages' ablation parameter (record
+// kv-efficiency/kivi-2bit-llama2-13b-mha-4k, "Quant method"; article "Your KV cache
+// doesn't have a bit problem...", paragraphs 2-3; KIVI summary, "Key points": group size
+// G and residual length R as hyperparameters).  Codes are stored in 32-token tiles
+// whatever G is.
 // The newest R tokens stay in fp16 and whole groups of the oldest residual tokens are
 // moved into the quantized history (record, "KV bytes basis").
 //
@@ -12,16 +15,18 @@
 
 namespace kivi {
 
-// One key token group held in LDS as fp16 [32][128] -> its 1024-byte code tile + 128 pairs.
-// Called by all 256 threads of the workgroup; ends with the codes and pairs stored.
-__device__ void quant_k_tile(const uint16_t* __restrict__ tile, float* sh_mn, float* sh_s,
-                             uint8_t* __restrict__ codes_dst,      // the group's code tile
-                             uint32_t* __restrict__ pairs_dst) {   // 128 (scale, zero) words
+// One key token group of GS tokens held in LDS as fp16 [GS][128] -> its GS/32 code tiles +
+// 128 pairs.  Called by all 256 threads of the workgroup; ends with the codes and pairs
+// stored.
+template <int GS>
+__device__ void quant_k_group(const uint16_t* __restrict__ tile, float* sh_mn, float* sh_s,
+                              uint8_t* __restrict__ codes_dst,      // the group's first code tile
+                              uint32_t* __restrict__ pairs_dst) {   // 128 (scale, zero) words
     const int tid = threadIdx.x;
     if (tid < kD) {
         float mn = h2f(tile[tid]), mx = mn;
 #pragma unroll 8
-        for (int t = 1; t < kG; ++t) {
+        for (int t = 1; t < GS; ++t) {
             float v = h2f(tile[t * kD + tid]);
             mn = __builtin_fminf(mn, v);
             mx = __builtin_fmaxf(mx, v);
@@ -32,33 +37,38 @@ __device__ void quant_k_tile(const uint16_t* __restrict__ tile, float* sh_mn, fl
         sh_s[tid] = q.s;
     }
     __syncthreads();
-    // thread -> (token t, 16-channel word w): 32 tokens x 8 words
+    // thread -> (token t, 16-channel word w) of each 32-token tile: 32 tokens x 8 words
     const int t = tid >> 3, w = tid & 7;
-    const uint4* src = reinterpret_cast<const uint4*>(tile + t * kD + w * 16);
-    uint4 a = src[0], b = src[1];
-    uint32_t h[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    uint32_t word = 0;
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
-        uint32_t bits = (c & 1) ? (h[c >> 1] >> 16) : (h[c >> 1] & 0xffffu);
-        int j = w * 16 + c;
-        GroupQ q{sh_mn[j], sh_s[j], 0u};
-        word |= code_of(h2f(bits), q) << code_bit(c);
+    for (int tl = 0; tl < GS / kG; ++tl) {
+        const uint4* src = reinterpret_cast<const uint4*>(tile + (tl * kG + t) * kD + w * 16);
+        uint4 a = src[0], b = src[1];
+        uint32_t h[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        uint32_t word = 0;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            uint32_t bits = (c & 1) ? (h[c >> 1] >> 16) : (h[c >> 1] & 0xffffu);
+            int j = w * 16 + c;
+            GroupQ q{sh_mn[j], sh_s[j], 0u};
+            word |= code_of(h2f(bits), q) << code_bit(c);
+        }
+        *reinterpret_cast<uint32_t*>(codes_dst + tl * kTileBytes + key_word_offset(t, w)) = word;
     }
-    *reinterpret_cast<uint32_t*>(codes_dst + key_word_offset(t, w)) = word;
 }
 
 // One 32-token value tile by the whole workgroup.  Tokens lo..hi-1 (tile-local) are
 // quantized from src_lo (token t at src_lo + (t - lo)*src_tok_stride, 128 fp16 channels);
 // their codes and (scale, zero) words are stored and the codes of the tile's other tokens
 // are kept.
-// sh_codes: LDS scratch [32][128] bytes.  All 256 threads must call it.
+// sh_codes: LDS scratch [32][128] bytes.  All 256 threads must call it.  Groups of GS
+// channels: the GS/16 lanes of a group reduce its min and max.
+template <int GS>
 __device__ void quant_v_tile(const uint16_t* __restrict__ src_lo, int64_t src_tok_stride, int lo, int hi,
                              uint8_t (*sh_codes)[kD], uint8_t* __restrict__ tile_dst,
                              uint32_t* __restrict__ pairs_dst) {   // pair word of tile token 0, group 0
     const int tid = threadIdx.x;
-    // thread -> (token t, 16-channel block cb); the two blocks of a 32-channel group are
-    // adjacent lanes
+    // thread -> (token t, 16-channel block cb); the blocks of a channel group are adjacent
+    // lanes
     const int t = tid >> 3, cb = tid & 7;
     const bool live = t >= lo && t < hi;
     uint4 x0 = make_uint4(0, 0, 0, 0), x1 = x0;
@@ -80,8 +90,11 @@ __device__ void quant_v_tile(const uint16_t* __restrict__ src_lo, int64_t src_to
         mn = __builtin_fminf(mn, v[i]);
         mx = __builtin_fmaxf(mx, v[i]);
     }
-    mn = __builtin_fminf(mn, __shfl_xor(mn, 1, 64));
-    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 1, 64));
+#pragma unroll
+    for (int m = 1; m < GS / 16; m <<= 1) {
+        mn = __builtin_fminf(mn, __shfl_xor(mn, m, 64));
+        mx = __builtin_fmaxf(mx, __shfl_xor(mx, m, 64));
+    }
     const GroupQ q = group_params(mn, mx);
     uint32_t packed[4];
 #pragma unroll
@@ -91,7 +104,7 @@ __device__ void quant_v_tile(const uint16_t* __restrict__ src_lo, int64_t src_to
         for (int b = 0; b < 4; ++b) packed[w] |= code_of(v[4 * w + b], q) << (8 * b);
     }
     *reinterpret_cast<uint4*>(&sh_codes[t][cb * 16]) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-    if (live && (cb & 1) == 0) pairs_dst[value_pair_index(t, cb >> 1)] = q.pair;
+    if (live && cb % (GS / 16) == 0) pairs_dst[value_pair_index<GS>(t, cb / (GS / 16))] = q.pair;
     __syncthreads();
     // thread -> 32-bit word tid of the tile: chunk L = tid/4 (tokens 8kg.., channel n + 16v),
     // word p = tid%4; its byte 2hh + e holds channel n + 32p + 16e for tokens 8kg + 4hh + i
@@ -117,25 +130,27 @@ __device__ void quant_v_tile(const uint16_t* __restrict__ src_lo, int64_t src_to
 
 // ------------------------------------------------------------------ kernels ------
 
-// grid.x = rows * (tokens / 32); one key token group per workgroup.
+// grid.x = rows * (tokens / GS); one key token group per workgroup.
+template <int GS>
 __global__ __launch_bounds__(kBlock) void quantize_k_kernel(QuantArgs a) {
-    __shared__ uint4 tile4[kG * kD / 8];
+    __shared__ uint4 tile4[GS * kD / 8];
     __shared__ float sh_mn[kD], sh_s[kD];
-    const int groups = a.tokens / kG;
+    const int groups = a.tokens / GS;
     const int64_t row = blockIdx.x / groups;
     const int g = blockIdx.x % groups;
-    const uint16_t* src = a.src + row * a.src_row_stride + (int64_t)g * kG * kD;
+    const uint16_t* src = a.src + row * a.src_row_stride + (int64_t)g * GS * kD;
     const uint4* s4 = reinterpret_cast<const uint4*>(src);
-    tile4[threadIdx.x] = s4[threadIdx.x];
-    tile4[threadIdx.x + kBlock] = s4[threadIdx.x + kBlock];
+#pragma unroll
+    for (int i = threadIdx.x; i < GS * kD / 8; i += kBlock) tile4[i] = s4[i];
     __syncthreads();
-    const int dst_tok = a.dst_token_off + g * kG;
+    const int dst_tok = a.dst_token_off + g * GS;
     uint8_t* codes = a.k_codes + row * a.token_cap * kRowBytes + (int64_t)(dst_tok / kG) * kTileBytes;
-    uint32_t* pairs = reinterpret_cast<uint32_t*>(a.k_sz) + (row * (a.token_cap / kG) + dst_tok / kG) * kD;
-    quant_k_tile(reinterpret_cast<const uint16_t*>(tile4), sh_mn, sh_s, codes, pairs);
+    uint32_t* pairs = reinterpret_cast<uint32_t*>(a.k_sz) + (row * (a.token_cap / GS) + dst_tok / GS) * kD;
+    quant_k_group<GS>(reinterpret_cast<const uint16_t*>(tile4), sh_mn, sh_s, codes, pairs);
 }
 
 // grid.x = rows * (32-token tiles touched by [dst_token_off, dst_token_off + tokens)).
+template <int GS>
 __global__ __launch_bounds__(kBlock) void quantize_v_kernel(QuantArgs a) {
     __shared__ __align__(16) uint8_t sh_codes[kG][kD];
     const int first = a.dst_token_off / kG;
@@ -147,8 +162,8 @@ __global__ __launch_bounds__(kBlock) void quantize_v_kernel(QuantArgs a) {
     const int hi = min(a.dst_token_off + a.tokens, t0 + kG) - t0;
     // source token of tile token lo: t0 + lo - dst_token_off
     const uint16_t* src = a.src + row * a.src_row_stride + (int64_t)(t0 + lo - a.dst_token_off) * kD;
-    quant_v_tile(src, kD, lo, hi, sh_codes, a.v_codes + (row * a.token_cap + t0) * kRowBytes,
-                 reinterpret_cast<uint32_t*>(a.v_sz) + value_pair_index(row * a.token_cap + t0, 0));
+    quant_v_tile<GS>(src, kD, lo, hi, sh_codes, a.v_codes + (row * a.token_cap + t0) * kRowBytes,
+                     reinterpret_cast<uint32_t*>(a.v_sz) + value_pair_index<GS>(row * a.token_cap + t0, 0));
 }
 
 // grid.x = ceil(rows * n * 16 / 256): copy tokens [first, first+n) of each row into ring
@@ -166,13 +181,14 @@ __global__ __launch_bounds__(kBlock) void residual_load_kernel(ResidualArgs a) {
     reinterpret_cast<uint4*>(a.v_res + d)[c] = reinterpret_cast<const uint4*>(a.v + so)[c];
 }
 
-// grid.x = rows.  Optional flush of ring slots [flush_slot, flush_slot+32) into key group
-// flush_group / value tokens flush_group*32.., then the new token into new_slot.  In a
+// grid.x = rows.  Optional flush of ring slots [flush_slot, flush_slot+GS) into key group
+// flush_group / value tokens flush_group*GS.., then the new token into new_slot.  In a
 // ragged batch each row takes these from its sequence's state (flush when its ring is full);
 // a sequence whose state is out of range, or whose flush would pass token_cap, is skipped
 // and flagged.
+template <int GS>
 __global__ __launch_bounds__(kBlock) void append_flush_kernel(AppendArgs a) {
-    __shared__ uint4 tile4[kG * kD / 8];
+    __shared__ uint4 tile4[GS * kD / 8];
     __shared__ float sh_mn[kD], sh_s[kD];
     const int64_t row = blockIdx.x;
     const int tid = threadIdx.x;
@@ -180,9 +196,9 @@ __global__ __launch_bounds__(kBlock) void append_flush_kernel(AppendArgs a) {
     if (a.seq_state != nullptr) {
         int32_t* s = a.seq_state + 4 * (row / a.kv_heads);
         const int32_t nq = s[0], nr = s[1], rh = s[2];
-        const bool ok = state_in_range(nq, nr, rh, a.token_cap, a.residual_cap);
+        const bool ok = state_in_range(nq, nr, rh, a.token_cap, a.residual_cap, GS);
         const bool flush = nr == a.residual_cap;
-        if (!ok || (flush && nq + kG > a.token_cap)) {   // the whole workgroup leaves together
+        if (!ok || (flush && nq + GS > a.token_cap)) {   // the whole workgroup leaves together
             if (row % a.kv_heads == 0 && tid == 0)
                 __hip_atomic_fetch_or(&s[3], ok ? kSeqCapacity : kSeqBadState, __ATOMIC_RELAXED,
                                       __HIP_MEMORY_SCOPE_AGENT);
@@ -190,24 +206,28 @@ __global__ __launch_bounds__(kBlock) void append_flush_kernel(AppendArgs a) {
         }
         do_flush = flush;
         flush_slot = rh;
-        flush_group = nq / kG;
-        const int head = flush ? (rh + kG) % a.residual_cap : rh;
-        new_slot = (head + (flush ? nr - kG : nr)) % a.residual_cap;
+        flush_group = nq / GS;
+        const int head = flush ? (rh + GS) % a.residual_cap : rh;
+        new_slot = (head + (flush ? nr - GS : nr)) % a.residual_cap;
     }
     if (do_flush) {
+        // the GS oldest ring tokens, contiguous: the ring length and its head are multiples of GS
         const uint4* kr = reinterpret_cast<const uint4*>(a.k_res + (row * a.residual_cap + flush_slot) * kD);
-        tile4[tid] = kr[tid];
-        tile4[tid + kBlock] = kr[tid + kBlock];
+#pragma unroll
+        for (int i = tid; i < GS * kD / 8; i += kBlock) tile4[i] = kr[i];
         __syncthreads();
-        const int dst_tok = flush_group * kG;
-        uint8_t* kc = a.k_codes + row * a.token_cap * kRowBytes + (int64_t)flush_group * kTileBytes;
-        uint32_t* kp = reinterpret_cast<uint32_t*>(a.k_sz) + (row * (a.token_cap / kG) + flush_group) * kD;
-        quant_k_tile(reinterpret_cast<const uint16_t*>(tile4), sh_mn, sh_s, kc, kp);
-        // values: the same 32 ring tokens as one value tile
+        const int dst_tok = flush_group * GS;
+        uint8_t* kc = a.k_codes + row * a.token_cap * kRowBytes + (int64_t)(dst_tok / kG) * kTileBytes;
+        uint32_t* kp = reinterpret_cast<uint32_t*>(a.k_sz) + (row * (a.token_cap / GS) + flush_group) * kD;
+        quant_k_group<GS>(reinterpret_cast<const uint16_t*>(tile4), sh_mn, sh_s, kc, kp);
+        // values: the same GS ring tokens as GS/32 value tiles
         __shared__ __align__(16) uint8_t sh_codes[kG][kD];
-        quant_v_tile(a.v_res + (row * a.residual_cap + flush_slot) * kD, kD, 0, kG, sh_codes,
-                     a.v_codes + (row * a.token_cap + dst_tok) * kRowBytes,
-                     reinterpret_cast<uint32_t*>(a.v_sz) + value_pair_index(row * a.token_cap + dst_tok, 0));
+#pragma unroll 1
+        for (int tl = 0; tl < GS / kG; ++tl)
+            quant_v_tile<GS>(a.v_res + (row * a.residual_cap + flush_slot + tl * kG) * kD, kD, 0, kG, sh_codes,
+                             a.v_codes + (row * a.token_cap + dst_tok + tl * kG) * kRowBytes,
+                             reinterpret_cast<uint32_t*>(a.v_sz) +
+                                 value_pair_index<GS>(row * a.token_cap + dst_tok + tl * kG, 0));
         __syncthreads();   // every read of the flushed slots is done before the overwrite
     }
     if (tid < 32) {
@@ -224,21 +244,21 @@ __global__ __launch_bounds__(64) void seq_state_update_kernel(AppendArgs a, int3
     const int64_t b = (int64_t)blockIdx.x * 64 + threadIdx.x;
     if (b >= batch) return;
     int32_t* s = a.seq_state + 4 * b;
-    const int32_t nq = s[0], nr = s[1], rh = s[2];
-    if (!state_in_range(nq, nr, rh, a.token_cap, a.residual_cap)) return;
+    const int32_t nq = s[0], nr = s[1], rh = s[2], G = a.group;
+    if (!state_in_range(nq, nr, rh, a.token_cap, a.residual_cap, G)) return;
     const bool flush = nr == a.residual_cap;
-    if (flush && nq + kG > a.token_cap) return;
-    s[0] = flush ? nq + kG : nq;
-    s[1] = (flush ? nr - kG : nr) + 1;
-    s[2] = flush ? (rh + kG) % a.residual_cap : rh;
+    if (flush && nq + G > a.token_cap) return;
+    s[0] = flush ? nq + G : nq;
+    s[1] = (flush ? nr - G : nr) + 1;
+    s[2] = flush ? (rh + G) % a.residual_cap : rh;
 }
 
 // ------------------------------------------------------------------ launchers ----
 
 hipError_t launch_quantize_k(const QuantArgs& a, hipStream_t s) {
-    const int64_t blocks = a.rows * (int64_t)(a.tokens / kG);
+    const int64_t blocks = a.rows * (int64_t)(a.tokens / a.group);
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL(quantize_k_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, s, a);
+    KIVI_BY_GROUP(a.group, hipLaunchKernelGGL(quantize_k_kernel<GS>, dim3((unsigned)blocks), dim3(kBlock), 0, s, a))
     return hipGetLastError();
 }
 
@@ -247,7 +267,7 @@ hipError_t launch_quantize_v(const QuantArgs& a, hipStream_t s) {
     const int64_t n_tiles = (a.dst_token_off + a.tokens - 1) / kG - a.dst_token_off / kG + 1;
     const int64_t blocks = a.rows * n_tiles;
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL(quantize_v_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, s, a);
+    KIVI_BY_GROUP(a.group, hipLaunchKernelGGL(quantize_v_kernel<GS>, dim3((unsigned)blocks), dim3(kBlock), 0, s, a))
     return hipGetLastError();
 }
 
@@ -259,12 +279,12 @@ hipError_t launch_residual_load(const ResidualArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_append_flush(const AppendArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL(append_flush_kernel, dim3((unsigned)a.rows), dim3(kBlock), 0, s, a);
+    KIVI_BY_GROUP(a.group, hipLaunchKernelGGL(append_flush_kernel<GS>, dim3((unsigned)a.rows), dim3(kBlock), 0, s, a))
     return hipGetLastError();
 }
 
 hipError_t launch_append_flush_ragged(const AppendArgs& a, int32_t batch, hipStream_t s) {
-    hipLaunchKernelGGL(append_flush_kernel, dim3((unsigned)a.rows), dim3(kBlock), 0, s, a);
+    KIVI_BY_GROUP(a.group, hipLaunchKernelGGL(append_flush_kernel<GS>, dim3((unsigned)a.rows), dim3(kBlock), 0, s, a))
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(seq_state_update_kernel, dim3((unsigned)((batch + 63) / 64)), dim3(64), 0, s, a, batch);

@@ -104,10 +104,10 @@ class Cache:
     def __init__(self, batch, kv_heads, token_cap, head_dim=128, group=32, residual_cap=128, device="cuda"):
         rows = batch * kv_heads
         u8, f16 = torch.uint8, torch.int16
-        tiles = token_cap // group                 # one 1024-byte tile of codes per token group
-        self.k_codes = torch.zeros((rows, tiles, group * head_dim // 4), dtype=u8, device=device)
-        self.v_codes = torch.zeros((rows, tiles, group * head_dim // 4), dtype=u8, device=device)
-        self.k_sz = torch.zeros((rows, tiles, head_dim, 2), dtype=f16, device=device)
+        tiles = token_cap // 32                    # one 1024-byte tile of codes per 32 tokens
+        self.k_codes = torch.zeros((rows, tiles, 32 * head_dim // 4), dtype=u8, device=device)
+        self.v_codes = torch.zeros((rows, tiles, 32 * head_dim // 4), dtype=u8, device=device)
+        self.k_sz = torch.zeros((rows, token_cap // group, head_dim, 2), dtype=f16, device=device)
         self.v_sz = torch.zeros((rows, token_cap, head_dim // group, 2), dtype=f16, device=device)
         self.k_res = torch.zeros((rows, residual_cap, head_dim), dtype=f16, device=device)
         self.v_res = torch.zeros((rows, residual_cap, head_dim), dtype=f16, device=device)

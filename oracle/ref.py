@@ -95,11 +95,11 @@ class RefCache:
         rows = batch * kv_heads
         self.batch, self.kv_heads, self.head_dim = batch, kv_heads, head_dim
         self.group, self.residual_cap, self.token_cap = group, residual_cap, token_cap
-        tiles = token_cap // group                 # one tile of codes per token group
-        self.k_codes = np.zeros((rows, tiles, group * head_dim // 4), np.uint8)
-        self.v_codes = np.zeros((rows, tiles, group * head_dim // 4), np.uint8)
-        self.k_sz = np.zeros((rows, tiles, head_dim, 2), np.uint16)
-        self.v_sz = np.zeros((rows, tiles * group, head_dim // group, 2), np.uint16)
+        tiles = token_cap // 32                    # one 1024-byte tile of codes per 32 tokens
+        self.k_codes = np.zeros((rows, tiles, 32 * head_dim // 4), np.uint8)
+        self.v_codes = np.zeros((rows, tiles, 32 * head_dim // 4), np.uint8)
+        self.k_sz = np.zeros((rows, token_cap // group, head_dim, 2), np.uint16)
+        self.v_sz = np.zeros((rows, token_cap, head_dim // group, 2), np.uint16)
         self.k_res = np.zeros((rows, residual_cap, head_dim), np.uint16)
         self.v_res = np.zeros((rows, residual_cap, head_dim), np.uint16)
         self.s = _CacheStruct(batch, kv_heads, head_dim, group, residual_cap, token_cap, 0, 0, 0,

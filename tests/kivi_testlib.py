@@ -38,10 +38,10 @@ def bits(t):
     return t.numpy().view(np.uint16)
 
 
-def ref_cache(batch, kv_heads, token_cap, k, v, n_quant, residual_cap=128):
+def ref_cache(batch, kv_heads, token_cap, k, v, n_quant, residual_cap=128, group=32):
     """Oracle cache prefilled from fp16 tensors k, v [B, H, T, D]."""
     B, H, T, D = k.shape
-    c = ref.RefCache(batch, kv_heads, D, 32, residual_cap, token_cap=token_cap)
+    c = ref.RefCache(batch, kv_heads, D, group, residual_cap, token_cap=token_cap)
     c.prefill(bits(k).reshape(B * H, T, D), bits(v).reshape(B * H, T, D), n_quant)
     return c
 
@@ -49,14 +49,15 @@ def ref_cache(batch, kv_heads, token_cap, k, v, n_quant, residual_cap=128):
 def assert_cache_equal(gpu, oracle, rows=None, upto=None, ring=True):
     """Bit-exact comparison of the packed history (tokens < upto) and the residual ring."""
     nq = oracle.n_quant if upto is None else upto
-    ng = nq // 32                                   # whole token groups (tiles)
+    ng = nq // 32                                   # whole 32-token code tiles
+    nk = nq // oracle.group                         # whole key groups (one pair per channel each)
     sel = slice(None) if rows is None else rows
     kc = gpu.k_codes[sel, :ng].cpu().numpy()
     vc = gpu.v_codes[sel, :ng].cpu().numpy()
-    ks = bits(gpu.k_sz[sel, :ng])
+    ks = bits(gpu.k_sz[sel, :nk])
     vs = bits(gpu.v_sz[sel, :nq])                   # value pairs are per token
     for name, a, b in (("k_codes", kc, oracle.k_codes[sel, :ng]), ("v_codes", vc, oracle.v_codes[sel, :ng]),
-                       ("k_sz", ks, oracle.k_sz[sel, :ng]), ("v_sz", vs, oracle.v_sz[sel, :nq])):
+                       ("k_sz", ks, oracle.k_sz[sel, :nk]), ("v_sz", vs, oracle.v_sz[sel, :nq])):
         bad = np.argwhere(a != b)
         assert bad.size == 0, f"{name}: {bad.shape[0]} mismatches, first at {bad[0].tolist()}: " \
                               f"gpu {a[tuple(bad[0])]} oracle {b[tuple(bad[0])]}"

@@ -122,9 +122,22 @@ def test_cache_bytes_matches_layout():
     assert (codes + pairs) // (rows * 4096) == 96
 
 
+@pytest.mark.parametrize("G,per_token", [(32, 96), (64, 80), (128, 72)])
+def test_group_sizes_supported_and_sized(G, per_token):
+    """Groups of 32, 64 and 128: key pairs per G tokens, value pairs per G channels."""
+    c = _cache(group=G, token_cap=1024, residual_cap=128, n_quant=G)
+    assert L.kivi_decode_attn_splits(C.byref(c), 2) >= 1
+    codes, pairs, _ = kivi.kivi_cache_bytes(c)
+    rows = 4
+    # bytes per quantized token per head: 64 code bytes + 4*128/G key-pair bytes + 4*128/G value-pair bytes
+    assert (codes + pairs) // (rows * 1024) == per_token
+
+
 @pytest.mark.parametrize("kw,code", [
     (dict(head_dim=64), -3),
     (dict(group=16), -3),
+    (dict(group=48), -2),          # channels are not whole groups
+    (dict(group=256), -2),
     (dict(head_dim=100), -2),
     (dict(token_cap=100), -2),
     (dict(residual_cap=100), -2),

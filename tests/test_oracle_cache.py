@@ -27,26 +27,28 @@ def _tokens(rows, T, seed):
     return k, v
 
 
-def _closed_form_state(n_tokens, R=R):
+def _closed_form_state(n_tokens, R=R, G=G):
     n_quant = 0 if n_tokens <= R else G * -(-(n_tokens - R) // G)
     return n_quant, n_tokens - n_quant, (n_quant % R)
 
 
-@pytest.mark.parametrize("R", [32, 64, 128, 256])
-def test_append_from_empty_matches_closed_form_and_prefill(R):
-    """The residual length R is a parameter: for every R, after n tokens the history holds
-    the fewest whole groups that leave at most R tokens in the ring."""
+@pytest.mark.parametrize("R,G", [(32, 32), (64, 32), (128, 32), (256, 32), (64, 64), (128, 64), (128, 128),
+                                 (256, 128)])
+def test_append_from_empty_matches_closed_form_and_prefill(R, G):
+    """The residual length R and the group size G are parameters: for every pair, after n
+    tokens the history holds the fewest whole groups of G that leave at most R tokens in
+    the ring."""
     B, H, T = 2, 3, 300
     k, v = _tokens(B * H, T, 1)
-    c = ref.RefCache(B, H, D, G, R, token_cap=320)
+    c = ref.RefCache(B, H, D, G, R, token_cap=384)
     flush_steps = []
     for t in range(T):
         if c.append(k[:, t], v[:, t]):
             flush_steps.append(t)
-        assert (c.n_quant, c.n_res, c.res_head) == _closed_form_state(t + 1, R)
+        assert (c.n_quant, c.n_res, c.res_head) == _closed_form_state(t + 1, R, G)
     # a flush happens exactly when the residual is full as the token arrives
     assert flush_steps == [R + i * G for i in range((T - R - 1) // G + 1)]
-    p = ref.RefCache(B, H, D, G, R, token_cap=320)
+    p = ref.RefCache(B, H, D, G, R, token_cap=384)
     p.prefill(k, v, c.n_quant)
     nq = c.n_quant
     assert np.array_equal(c.k_codes[:, : nq // G], p.k_codes[:, : nq // G])

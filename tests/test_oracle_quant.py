@@ -62,21 +62,21 @@ def test_hand_vectors_as_key_channel(vec):
 
 
 # ------------------------------------------------------------ random groups ----
-def _groups(kind, n, rng):
+def _groups(kind, n, rng, g=G):
     if kind == "normal":
-        x = rng.standard_normal((n, G))
+        x = rng.standard_normal((n, g))
     elif kind == "wide":
-        x = rng.standard_normal((n, G)) * 10.0 ** rng.uniform(-7.5, 4.6, (n, 1))
+        x = rng.standard_normal((n, g)) * 10.0 ** rng.uniform(-7.5, 4.6, (n, 1))
     elif kind == "grid":      # small dyadic grid: many exact ties
-        x = rng.integers(-12, 13, (n, G)) / 8.0
+        x = rng.integers(-12, 13, (n, g)) / 8.0
     elif kind == "levels":    # zero + multiples of a step, incl. half levels
         step = 2.0 ** rng.integers(-20, 8, (n, 1))
-        x = rng.uniform(-100, 100, (n, 1)).round() * step + rng.integers(0, 7, (n, G)) * step / 2
+        x = rng.uniform(-100, 100, (n, 1)).round() * step + rng.integers(0, 7, (n, g)) * step / 2
     elif kind == "outlier":
-        x = rng.standard_normal((n, G)) * np.exp(rng.uniform(np.log(100), np.log(7000), (n, 1)))
+        x = rng.standard_normal((n, g)) * np.exp(rng.uniform(np.log(100), np.log(7000), (n, 1)))
         x[:, 0] = rng.choice([-65504.0, 65504.0, 0.0], n)
     elif kind == "tiny":      # subnormal ranges
-        x = rng.integers(0, 9, (n, G)) * 2.0 ** -24 + rng.integers(-3, 3, (n, 1)) * 2.0 ** -14
+        x = rng.integers(0, 9, (n, g)) * 2.0 ** -24 + rng.integers(-3, 3, (n, 1)) * 2.0 ** -14
     else:
         raise ValueError(kind)
     return np.clip(x, -65504, 65504).astype(np.float16).view(np.uint16)
@@ -86,23 +86,29 @@ KINDS = ["normal", "wide", "grid", "levels", "outlier", "tiny"]
 
 
 def _quantize_as_values(x_bits):
-    """Run groups [n, 32] through the per-token value quantizer (4 groups per token)."""
-    n = x_bits.shape[0]
-    tokens = n // 4
-    tokens -= tokens % G                          # whole token groups (cache tiles)
-    c = ref.RefCache(1, 1, D, G, 128, token_cap=tokens)
-    c.quantize_v(x_bits[: tokens * 4].reshape(1, tokens, D), tokens)
-    vp = value_pairs(c.v_sz[0])                    # [tokens, 4, 2]
+    """Run groups [n, g] (g = 32, 64 or 128) through the per-token value quantizer with
+    value groups of g channels (128 / g groups per token)."""
+    n, g = x_bits.shape
+    per_tok = D // g
+    tokens = n // per_tok
+    tokens -= tokens % 128                        # whole token groups (cache tiles) for any g
+    c = ref.RefCache(1, 1, D, g, 128, token_cap=tokens)
+    c.quantize_v(x_bits[: tokens * per_tok].reshape(1, tokens, D), tokens)
+    vp = value_pairs(c.v_sz[0])                    # [tokens, per_tok, 2]
     s = vp[:, :, 0].reshape(-1)
     z = vp[:, :, 1].reshape(-1)
-    codes = unpack_value_codes(c.v_codes[0]).reshape(-1, G)
+    codes = unpack_value_codes(c.v_codes[0]).reshape(-1, g)
     return s, z, codes
 
 
+GROUPS = [32, 64, 128]
+
+
+@pytest.mark.parametrize("g", GROUPS)
 @pytest.mark.parametrize("kind", KINDS)
-def test_brute_force_nearest_level(kind):
-    rng = np.random.default_rng(100 + KINDS.index(kind))
-    x = _groups(kind, 160_000, rng)
+def test_brute_force_nearest_level(kind, g):
+    rng = np.random.default_rng(100 + KINDS.index(kind) + g)
+    x = _groups(kind, 160_000 * 32 // g, rng, g)
     s, z, codes = _quantize_as_values(x)
     x = x[: codes.shape[0]]
     X, S, Z = _units(x), _units(s)[:, None], _units(z)[:, None]
@@ -121,10 +127,11 @@ def test_brute_force_nearest_level(kind):
     assert (codes[exact_tie] % 2 == 0).all()
 
 
+@pytest.mark.parametrize("g", GROUPS)
 @pytest.mark.parametrize("kind", KINDS)
-def test_scale_is_nearest_fp16_of_range_over_3_and_zero_is_min(kind):
-    rng = np.random.default_rng(200 + KINDS.index(kind))
-    x = _groups(kind, 80_000, rng)
+def test_scale_is_nearest_fp16_of_range_over_3_and_zero_is_min(kind, g):
+    rng = np.random.default_rng(200 + KINDS.index(kind) + g)
+    x = _groups(kind, 80_000 * 32 // g, rng, g)
     s, z, _ = _quantize_as_values(x)
     x = x[: s.shape[0]]
     X = _units(x)
@@ -140,10 +147,11 @@ def test_scale_is_nearest_fp16_of_range_over_3_and_zero_is_min(kind):
     assert not (z == 0x8000).any()
 
 
+@pytest.mark.parametrize("g", GROUPS)
 @pytest.mark.parametrize("kind", KINDS)
-def test_reconstruction_invariants(kind):
-    rng = np.random.default_rng(300 + KINDS.index(kind))
-    x = _groups(kind, 80_000, rng)
+def test_reconstruction_invariants(kind, g):
+    rng = np.random.default_rng(300 + KINDS.index(kind) + g)
+    x = _groups(kind, 80_000 * 32 // g, rng, g)
     s, z, codes = _quantize_as_values(x)
     x = x[: codes.shape[0]]
     xf = x.view(np.float16).astype(np.float64)
@@ -183,25 +191,30 @@ def test_signed_zeros_do_not_depend_on_order():
     assert not (s1 == 0x8000).any() and not (z1 == 0x8000).any()
 
 
-def test_keys_per_channel_values_per_token_axes():
-    """Keys group along tokens for each channel, values along channels for each token."""
-    rng = np.random.default_rng(9)
-    k = rng.standard_normal((1, 64, D)).astype(np.float16).view(np.uint16)
-    c = ref.RefCache(1, 1, D, G, 128, token_cap=64)
-    c.quantize_k(k, 64)
-    c.quantize_v(k, 64)
+@pytest.mark.parametrize("Gs", GROUPS)
+def test_keys_per_channel_values_per_token_axes(Gs):
+    """Keys group along tokens for each channel (Gs tokens), values along channels for each
+    token (Gs channels), for every supported group size Gs; each stored pair and code is the
+    group quantizer applied to exactly that group."""
+    rng = np.random.default_rng(9 + Gs)
+    T = 2 * Gs
+    k = rng.standard_normal((1, T, D)).astype(np.float16).view(np.uint16)
+    c = ref.RefCache(1, 1, D, Gs, 128, token_cap=T)
+    c.quantize_k(k, T)
+    c.quantize_v(k, T)
     kf = k.view(np.float16).astype(np.float64)[0]
+    kcodes, vcodes = unpack_key_codes(c.k_codes[0]), unpack_value_codes(c.v_codes[0])
     for g in range(2):
-        for j in (0, 17, 127):
-            s, z, codes = ref.quant_group(k[0, g * G:(g + 1) * G, j])
+        for j in range(D):
+            s, z, codes = ref.quant_group(k[0, g * Gs:(g + 1) * Gs, j])
             assert c.k_sz[0, g, j].tolist() == [s, z]
-            assert np.array_equal(unpack_key_codes(c.k_codes[0])[g * G:(g + 1) * G, j], codes)
-            assert np.uint16(z).view(np.float16) == kf[g * G:(g + 1) * G, j].min()
-    for t in (0, 33, 63):
-        for kk in range(D // G):
-            s, z, codes = ref.quant_group(k[0, t, kk * G:(kk + 1) * G])
+            assert np.array_equal(kcodes[g * Gs:(g + 1) * Gs, j], codes)
+            assert np.uint16(z).view(np.float16) == kf[g * Gs:(g + 1) * Gs, j].min()
+    for t in range(T):
+        for kk in range(D // Gs):
+            s, z, codes = ref.quant_group(k[0, t, kk * Gs:(kk + 1) * Gs])
             assert value_pairs(c.v_sz[0])[t, kk].tolist() == [s, z]
-            assert np.array_equal(unpack_value_codes(c.v_codes[0])[t, kk * G:(kk + 1) * G], codes)
+            assert np.array_equal(vcodes[t, kk * Gs:(kk + 1) * Gs], codes)
 
 
 def test_per_channel_keys_isolate_outlier_channels():
