@@ -12,7 +12,9 @@ Prints ONE JSON line.  Metric: achieved HBM GB/s (algorithmic bytes / time) and 
 After the timed steps, the fp16 comparator (kivi_decode_attn_fp16: the same attention over
 an uncompressed fp16 cache of the starting context) is timed the same way and reported
 beside it ("fp16_comparator"; --no-fp16 skips it), and so is the ragged-batch path on a
-serving batch of 64 sequences at different lengths ("ragged_batch"; --no-ragged skips it).
+serving batch of 64 sequences at different lengths ("ragged_batch"; --no-ragged skips it),
+and attention alone over the same context quantized at group sizes 64 and 128
+("group_sizes"; --sweep-groups sets the list, --group the timed cache's own group size).
 """
 import argparse
 import json
@@ -28,9 +30,18 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode-attn over 2-bit KV: achieved HBM GB/s (% of peak) and tokens/s at 1 GPU"
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
-D, G = 128, 32
-QUANT_TOKEN_BYTES = 96         # per kv head: 32 B key codes + 16 B key pairs + 32 B value codes + 16 B value pairs
+D = 128
 RES_TOKEN_BYTES = 512          # per kv head: fp16 key + value
+
+
+def quant_token_bytes(g):
+    """Bytes of one quantized token per kv head at group size g: 32 B of key codes and
+    32 B of value codes, a 4-byte (scale, zero) per channel per g tokens for the keys and
+    per g channels of the token for the values (96 B at g = 32)."""
+    return 2 * D // 4 + D * 4 // g + (D // g) * 4
+
+
+QUANT_TOKEN_BYTES = quant_token_bytes(32)
 def counters_file(workload):
     return os.path.join(ROOT, "profiles", f"decode_attn_{workload}_counters.json")
 
@@ -39,16 +50,16 @@ def attn_bytes(w, n_quant, n_res):
     """Algorithmic HBM bytes of one decode-attention call: the packed history and the
     residual read once per kv head, q read and out written once per query head."""
     rows = w.batch * w.kv_heads
-    return rows * (n_quant * QUANT_TOKEN_BYTES + n_res * RES_TOKEN_BYTES) + 2 * w.batch * w.q_heads * D * 2
+    return rows * (n_quant * quant_token_bytes(w.group) + n_res * RES_TOKEN_BYTES) + 2 * w.batch * w.q_heads * D * 2
 
 
 def append_bytes(w, flushed):
-    """One append: read k_new, v_new and write them into the ring; a flush also reads 32
+    """One append: read k_new, v_new and write them into the ring; a flush also reads G
     ring tokens of keys and values and writes one group of codes and pairs."""
     rows = w.batch * w.kv_heads
     b = rows * 4 * D * 2
     if flushed:
-        b += rows * (G * RES_TOKEN_BYTES + G * QUANT_TOKEN_BYTES)
+        b += rows * w.group * (RES_TOKEN_BYTES + quant_token_bytes(w.group))
     return b
 
 
@@ -69,7 +80,7 @@ def cpu_baseline(w, k, v, n_heads, steps_tokens, threads):
     kn, vn = steps_tokens
     knh, vnh = host_bits(kn[0, :n_heads]), host_bits(vn[0, :n_heads])
     qh = host_bits(synth.query(w, step=1)[:1, :n_heads])
-    caches = [ref.RefCache(1, b1 - b0, D, G, w.residual_cap, token_cap=w.token_cap) for b0, b1 in bounds]
+    caches = [ref.RefCache(1, b1 - b0, D, w.group, w.residual_cap, token_cap=w.token_cap) for b0, b1 in bounds]
     with concurrent.futures.ThreadPoolExecutor(threads) as ex:
         t0 = time.perf_counter()
         list(ex.map(lambda i: caches[i].prefill(kh[bounds[i][0]:bounds[i][1]], vh[bounds[i][0]:bounds[i][1]],
@@ -85,8 +96,9 @@ def cpu_baseline(w, k, v, n_heads, steps_tokens, threads):
         flushed = list(ex.map(step, range(threads)))[0]
         step_s = time.perf_counter() - t0
     nq, nr = caches[0].n_quant, caches[0].n_res
-    nbytes = n_heads * (nq * QUANT_TOKEN_BYTES + nr * RES_TOKEN_BYTES) + 2 * n_heads * D * 2 \
-        + n_heads * 4 * D * 2 + (n_heads * G * (RES_TOKEN_BYTES + QUANT_TOKEN_BYTES) if flushed else 0)
+    qtb = quant_token_bytes(w.group)
+    nbytes = n_heads * (nq * qtb + nr * RES_TOKEN_BYTES) + 2 * n_heads * D * 2 \
+        + n_heads * 4 * D * 2 + (n_heads * w.group * (RES_TOKEN_BYTES + qtb) if flushed else 0)
     return {
         "value": nbytes / step_s / 1e9,
         "unit": "GB/s",
@@ -112,7 +124,7 @@ def ragged_measure(kivi, synth, dev, steps, warmup, seed=2402):
     cache = kivi.Cache(B, Hkv, hi, device=dev)
     states, byts = [], 2 * B * Hq * D * 2
     for b, L in enumerate(lengths):
-        nq = int((L - 64) // G * G)
+        nq = int((L - 64) // 32 * 32)
         w = synth.small(seed=seed + b, batch=1, q_heads=Hq, kv_heads=Hkv, context=int(L), n_quant=nq)
         k, v = synth.prefill_kv(w, device=dev)
         view = cache.sequence(b)
@@ -146,6 +158,44 @@ def ragged_measure(kivi, synth, dev, steps, warmup, seed=2402):
     }
 
 
+def time_attention(kivi, cache, queries, sm, steps, warmup):
+    """Mean duration (us) of kivi_decode_attn launches, kernel-recorded events."""
+    out = torch.empty_like(queries[0])
+    ws = cache.workspace(queries[0].shape[1])
+    for s in range(warmup):
+        kivi.kivi_decode_attn(cache, queries[s], sm, out=out, workspace=ws)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for pair in ev:
+        for e in pair:
+            e.record()
+    torch.cuda.synchronize()
+    for i in range(steps):
+        kivi.kivi_time_next_attention(*ev[i])
+        kivi.kivi_decode_attn(cache, queries[warmup + i], sm, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+
+
+def group_sweep(kivi, synth, w, k, v, queries, steps, warmup, groups):
+    """Attention alone (kivi_decode_attn) over the same prefill keys and values quantized at
+    other group sizes: the history is the largest whole number of groups that leaves at
+    least 32 tokens in the fp16 residual."""
+    import dataclasses
+    res = []
+    for g in groups:
+        nq = (w.context - 32) // g * g
+        wg = dataclasses.replace(w, group=g, n_quant=nq)
+        cache = kivi.Cache(wg.batch, wg.kv_heads, wg.token_cap, group=g, device=k.device)
+        kivi.kivi_prefill(k, v, nq, cache)
+        us = time_attention(kivi, cache, queries, synth.SM_SCALE_D128, steps, warmup)
+        b = attn_bytes(wg, nq, wg.n_res)
+        res.append({"group": g, "n_quant": nq, "n_res": wg.n_res, "splits": kivi.kivi_decode_attn_splits(cache, w.q_heads),
+                    "decode_attn_us": round(us, 2), "bytes_per_launch": int(b), "achieved": round(b / us / 1e3, 1),
+                    "unit": "GB/s", "frac": round(b / us / 1e3 / PEAK_HBM_GBS, 4)})
+        del cache
+    return res
+
+
 def read_traffic(workload):
     """HBM bytes per launch from committed rocprofv3 counters, if they were taken on the
     current kernel sources; else None."""
@@ -172,6 +222,9 @@ def main():
     ap.add_argument("--separate", action="store_true", help="time kivi_append_flush + kivi_decode_attn")
     ap.add_argument("--no-fp16", action="store_true", help="skip the fp16 comparator")
     ap.add_argument("--no-ragged", action="store_true", help="skip the ragged-batch measurement")
+    ap.add_argument("--group", type=int, default=32, help="group size of the timed cache (32, 64 or 128)")
+    ap.add_argument("--sweep-groups", default="64,128",
+                    help="group sizes of the attention-only sweep (comma list; empty: skip)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the decode hot path shards "
@@ -184,12 +237,14 @@ def main():
         raise SystemExit("bench.py times single-layer workloads")
     dev = torch.device("cuda:0")
     total_steps = args.warmup + args.steps
+    import dataclasses
+    if args.group != w.group:
+        w = dataclasses.replace(w, group=args.group, n_quant=(w.context - 32) // args.group * args.group)
     if total_steps > w.token_cap - w.context:
-        import dataclasses
         w = dataclasses.replace(w, decode_steps=total_steps)
 
     k, v = synth.prefill_kv(w, device=dev)
-    cache = kivi.Cache(w.batch, w.kv_heads, w.token_cap, device=dev)
+    cache = kivi.Cache(w.batch, w.kv_heads, w.token_cap, group=w.group, device=dev)
     kivi.kivi_prefill(k, v, w.n_quant, cache)
     steps_kv = [synth.step_kv(w, s, device=dev) for s in range(total_steps)]
     queries = [synth.query(w, step=s + 1, device=dev) for s in range(total_steps)]
@@ -286,7 +341,7 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": w.name, "batch": w.batch, "q_heads": w.q_heads, "kv_heads": w.kv_heads,
-            "head_dim": D, "group": G, "residual": w.residual_cap, "context_start": w.context,
+            "head_dim": D, "group": w.group, "residual": w.residual_cap, "context_start": w.context,
             "n_quant_start": w.n_quant, "splits": splits,
         },
         "pct_of_peak_hbm": round(100 * value / PEAK_HBM_GBS, 2),
@@ -309,9 +364,13 @@ def main():
         "cpu_baseline": None,
         "fp16_comparator": fp16,
         "ragged_batch": None,
+        "group_sizes": None,
     }
+    del cache, ws
+    groups = [int(x) for x in args.sweep_groups.split(",") if x.strip()]
+    if groups:
+        res["group_sizes"] = group_sweep(kivi, synth, w, k, v, queries, args.steps, args.warmup, groups)
     if not args.no_ragged:
-        del cache, ws
         res["ragged_batch"] = ragged_measure(kivi, synth, dev, args.steps, args.warmup)
     if args.cpu_heads > 0:
         kn, vn = steps_kv[0]
