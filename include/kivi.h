@@ -25,8 +25,9 @@
  *    on the host before anything is enqueued; on any error nothing is enqueued and the
  *    cache state fields are unchanged.  Nothing throws across this boundary.
  *  - Inputs must be finite (NaN/Inf are outside the contract and are not scanned).
- *  - This version implements head_dim == 128 and group == 32 (other valid shapes return
- *    KIVI_ERR_UNSUPPORTED).
+ *  - This version implements head_dim == 128 and group 32, 64 or 128 (other valid shapes
+ *    return KIVI_ERR_UNSUPPORTED).  The pages' configuration is G = 32, R = 128; G and R
+ *    are parameters of the descriptor.
  */
 #ifndef KIVI_H
 #define KIVI_H
@@ -53,23 +54,26 @@ enum {
  * The cache descriptor (host struct; the caller owns it and every buffer it points to).
  * row = b * kv_heads + h.  D = head_dim, G = group, R = residual_cap.
  *
- * Packed layout (four 2-bit codes per byte; D = 128, G = 32 here):
- *   k_codes, v_codes : uint8  [row][token_cap/G][1024]: one 1024-byte tile per 32-token
- *                      group.  Codes are packed in little-endian 32-bit words; word w of a
- *                      token holds channels 16w..16w+15, channel 16w + 4i + b in byte b at
- *                      bits 2i..2i+1, so masking a word with 0x03030303 << 2i yields the
- *                      codes of four consecutive channels, one per byte.  The two caches
- *                      order the words inside a tile differently:
- *                      v_codes: 16-byte chunk ((u*8 + q)*4 + h) holds words 2h and 2h+1
- *                        (channels 32h..32h+31) of token 4q+2u, then those of token
- *                        4q+2u+1 (q = 0..7, u = 0..1);
- *                      k_codes: 16-byte chunk (16k + n) holds words k and 4+k of token n,
- *                        then words k and 4+k of token 16+n (k = 0..3, n = 0..15).
+ * Packed layout (four 2-bit codes per byte; D = 128).  The codes are stored in tiles of
+ * 32 tokens whatever G is (a key group of G tokens spans G/32 tiles):
+ *   k_codes, v_codes : uint8  [row][token_cap/32][1024]: one 1024-byte tile per 32 tokens.
+ *                      k_codes: a little-endian 32-bit word holds channels 16w..16w+15 of
+ *                        one token, channel 16w + 4i + b in byte b at bits 2i..2i+1, so
+ *                        masking a word with 0x03030303 << 2i yields the codes of four
+ *                        consecutive channels, one per byte; 16-byte chunk (16k + n) of a
+ *                        tile holds words k and 4+k of its token n, then words k and 4+k of
+ *                        its token 16+n (k = 0..3, n = 0..15).
+ *                      v_codes: a byte holds one channel's codes for four consecutive
+ *                        tokens, token 4a+i at bits 2i..2i+1; 16-byte chunk (16k + n) of a
+ *                        tile covers its tokens 8k..8k+7, and the chunk's byte 4p + 2h + e
+ *                        holds channel n + 16(2p + e) for tokens 8k+4h..8k+4h+3 (k = 0..3,
+ *                        n = 0..15, p = 0..3, h and e = 0..1).
  *   k_sz             : fp16   [row][token_cap/G][D][2]  (scale, zero) of key token group
- *                      g, channel j  -- keys are quantized per-channel over G tokens.
- *   v_sz             : fp16   [row][token_cap/G][D/G][G][2]  (scale, zero) of value token
- *                      32g+t, channel group k -- values are quantized per-token over G
- *                      channels.
+ *                      g (tokens Gg..Gg+G-1), channel j -- keys are quantized per-channel
+ *                      over G tokens.
+ *   v_sz             : fp16   [row][token_cap][D/G][2]  (scale, zero) of value token t,
+ *                      channel group k (channels Gk..Gk+G-1) -- values are quantized
+ *                      per-token over G channels.
  *   k_res, v_res     : fp16   [row][R][D] residual ring; the n_res newest tokens, oldest
  *                      first, sit in slots (res_head + i) % R, i < n_res.
  * Dequantized value: zero + code * scale.  Quantizer: zero = group min, scale =
@@ -165,8 +169,8 @@ int kivi_decode_step(kivi_cache* cache, const uint16_t* k_new, const uint16_t* v
  * and res_head are ignored by these calls.  A sequence's rows are contiguous in every
  * buffer, so each sequence can be filled by the single-batch calls (kivi_prefill, ...) on
  * a descriptor with batch = 1 whose pointers start at its first row.  The kernels check
- * each state: one out of range (n_quant not a multiple of 32 or above token_cap, n_res
- * above residual_cap, res_head not a multiple of 32 below residual_cap) is not used, the
+ * each state: one out of range (n_quant not a multiple of G or above token_cap, n_res
+ * above residual_cap, res_head not a multiple of G below residual_cap) is not used, the
  * sequence attends over nothing and its flags get KIVI_SEQ_BAD_STATE.  flags bits are only
  * ever set (OR) by the library, never cleared. */
 #define KIVI_SEQ_CAPACITY 1    /* an append was skipped: its flush would pass token_cap */
@@ -174,7 +178,7 @@ int kivi_decode_step(kivi_cache* cache, const uint16_t* k_new, const uint16_t* v
 
 /* kivi_append_flush for every sequence of a ragged batch: one new token per sequence
  * (k_new, v_new: fp16 [batch][kv_heads][128]), a sequence whose ring is full first
- * flushing its oldest 32 ring tokens into a new group, then each sequence's state moved on
+ * flushing its oldest G ring tokens into a new group, then each sequence's state moved on
  * on the device (two kernel launches in stream order).  A sequence whose flush would pass
  * token_cap is left as it was and gets KIVI_SEQ_CAPACITY. */
 int kivi_append_flush_ragged(const kivi_cache* cache, int32_t* seq_state, const uint16_t* k_new,

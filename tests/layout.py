@@ -11,7 +11,7 @@ Value pairs: [token][channel group][scale, zero].
 """
 import numpy as np
 
-D, G = 128, 32
+D = 128          # codes are stored in 32-token tiles whatever the group size is
 
 
 def value_code_pos(t, j):
@@ -56,7 +56,7 @@ def unpack_key_codes(tiles):
 
 
 def value_pairs(v_sz):
-    """[..., tokens, 4, 2] value pairs (stored token-major already)."""
+    """[..., tokens, D/G, 2] value pairs (stored token-major already)."""
     return np.asarray(v_sz)
 
 
