@@ -137,11 +137,13 @@ int kivi_append_flush(kivi_cache* cache, const uint16_t* k_new, const uint16_t* 
  * The context is split into num_splits parts per row (0 = automatic) and the partial
  * softmax states are merged with a log-sum-exp merge inside the same kernel launch.
  * workspace: device scratch of at least kivi_decode_attn_workspace(cache, q_heads,
- * num_splits) bytes, 256-byte aligned, owned by the caller.  Its first
- * round_up(batch*q_heads*4, 256) bytes are per-row arrival counters that must be zero
- * before the first call that uses the workspace (clear it once after allocating it);
- * every completed call leaves them zero again.  Calls that share a workspace must not
- * run concurrently.  KIVI_ERR_SHAPE if the context is empty. */
+ * num_splits) bytes, 256-byte aligned, owned by the caller.  The whole workspace must be
+ * zero before the first call that uses it (clear it once after allocating it); calls keep
+ * it consistent afterwards.  Its first round_up(2*batch*q_heads*4, 256) bytes hold a
+ * per-row arrival counter (zero again after every completed call) and a per-row call
+ * epoch; the rest holds the split partials, each value stored with its call's tag.  Calls
+ * that share a workspace must not run concurrently.  KIVI_ERR_SHAPE if the context is
+ * empty. */
 int kivi_decode_attn(const kivi_cache* cache, const uint16_t* q, int32_t q_heads,
                      float sm_scale, uint16_t* out, float* lse, void* workspace,
                      size_t workspace_bytes, int32_t num_splits, void* stream);
@@ -201,8 +203,8 @@ int kivi_decode_attn_ragged(const kivi_cache* cache, int32_t* seq_state, const u
  * grouping, split-K and merge as kivi_decode_attn.
  * k, v: fp16 [batch][kv_heads][token_stride][128], tokens [0, tokens) of each row used,
  * 16-byte aligned, owned by the caller.  q, out, lse, workspace (at least
- * kivi_decode_attn_fp16_workspace(...) bytes, 256-byte aligned, leading arrival counters
- * zero before first use and left zero), num_splits (0 = automatic) and stream as in
+ * kivi_decode_attn_fp16_workspace(...) bytes, 256-byte aligned, zero before its first use,
+ * the same layout as kivi_decode_attn's), num_splits (0 = automatic) and stream as in
  * kivi_decode_attn.  KIVI_ERR_SHAPE if tokens < 1, tokens > token_stride, q_heads is not a
  * multiple of kv_heads or a pointer is misaligned. */
 int kivi_decode_attn_fp16(const uint16_t* k, const uint16_t* v, int32_t batch, int32_t kv_heads,

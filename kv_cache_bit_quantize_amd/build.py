@@ -20,6 +20,9 @@ FLAGS = [
     # matrix-instruction accumulators in ordinary VGPRs: the decode loop rescales them with
     # vector instructions, and accumulation registers would be copied back and forth
     "-mllvm", "-amdgpu-mfma-vgpr-form=1",
+    # single-lane atomics stay single instructions: the optimizer would turn a work request
+    # into a wave reduction whose result is broadcast (and waited for) at once
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wall", "-Wno-unused-command-line-argument",
 ]
 

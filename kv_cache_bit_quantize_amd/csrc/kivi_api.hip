@@ -13,11 +13,14 @@ using namespace kivi;
 
 namespace {
 
-// One round of resident workgroups on MI355X's 256 CUs: three per CU for the single-query
-// kernel, two for the query-group kernel (their register use sets three and two waves per SIMD).
-constexpr int64_t kTargetBlocks = 768;
-constexpr int64_t kTargetBlocksGroup = 512;
+// One round of resident workgroups on MI355X's 256 CUs: one 12-wave workgroup per CU for the
+// single-query 2-bit kernel, 512 for the query-group kernel (measured best), three 4-wave
+// workgroups per CU for the fp16 comparator.
+constexpr int64_t kTargetBlocks = 768;         // 256-thread workgroups: three per CU
+constexpr int64_t kTargetBlocksGroup = 512;    // query-group workgroups
+constexpr int64_t kTargetBlocksSingle = 256;   // single-query 2-bit workgroups (12 waves): one per CU
 constexpr int kMinGroupsPerSplit = 8;
+constexpr int kMinGroupsPerSplitSingle = 2 * kSqWaves;   // a pair of tiles for every wave
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -78,9 +81,10 @@ int64_t block_rows(const kivi_cache* c, int32_t q_heads) {
 // Split count for a context of `groups` key groups.
 int32_t auto_splits_for(const kivi_cache* c, int32_t q_heads, int64_t groups) {
     const int64_t rows = block_rows(c, q_heads);
-    const int64_t target = queries_per_block(q_heads / c->kv_heads) > 1 ? kTargetBlocksGroup : kTargetBlocks;
+    const bool group = queries_per_block(q_heads / c->kv_heads) > 1;
+    const int64_t target = group ? kTargetBlocksGroup : kTargetBlocksSingle;
     int64_t s = (target + rows - 1) / rows;
-    const int64_t cap = groups / kMinGroupsPerSplit;
+    const int64_t cap = groups / (group ? kMinGroupsPerSplit : kMinGroupsPerSplitSingle);
     if (s > cap) s = cap;
     if (s < 1) s = 1;
     if (s > kMaxSplits) s = kMaxSplits;
@@ -93,16 +97,18 @@ int32_t auto_splits(const kivi_cache* c, int32_t q_heads) { return auto_splits_f
 int32_t ragged_auto_splits(const kivi_cache* c, int32_t q_heads) {
     const int64_t groups = c->token_cap / kG;
     int64_t s = 4 * (int64_t)auto_splits_for(c, q_heads, groups);
-    const int64_t cap = groups / kMinGroupsPerSplit;
+    const bool group = queries_per_block(q_heads / c->kv_heads) > 1;
+    const int64_t cap = groups / (group ? kMinGroupsPerSplit : kMinGroupsPerSplitSingle);
     if (s > cap) s = cap;
     if (s < 1) s = 1;
     if (s > kMaxSplits) s = kMaxSplits;
     return (int32_t)s;
 }
 
-// leading area of the attention workspace: one arrival counter per query row
+// leading area of the attention workspace: one arrival counter per query row, then one call
+// epoch per query row (the tag of the last merged call's partials)
 size_t counter_bytes(const kivi_cache* c, int32_t q_heads) {
-    return ((size_t)c->batch * (size_t)q_heads * sizeof(uint32_t) + 255) & ~(size_t)255;
+    return (2 * (size_t)c->batch * (size_t)q_heads * sizeof(uint32_t) + 255) & ~(size_t)255;
 }
 
 QuantArgs quant_args(const kivi_cache* c, const uint16_t* src, int32_t tokens, int64_t stride,
@@ -206,7 +212,7 @@ int prepare_attn(const kivi_cache* c, const uint16_t* q, int32_t q_heads, float 
     a.k_res = c->k_res;
     a.v_res = c->v_res;
     a.counters = static_cast<uint32_t*>(workspace);
-    a.ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + counter_bytes(c, q_heads));
+    a.ws = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + counter_bytes(c, q_heads));
     a.out = out;
     a.lse = lse;
     a.sm_log2 = (float)((double)sm_scale * 1.4426950408889634);
@@ -230,7 +236,9 @@ int prepare_attn(const kivi_cache* c, const uint16_t* q, int32_t q_heads, float 
     a.k_ring = a.v_ring = nullptr;
     a.new_slot = 0;
     a.seq_state = seq_state;
-    a.slot_budget = (int32_t)kTargetBlocks;   // three resident workgroups per CU
+    // workgroups resident at once: three 4-wave query-group workgroups or one 12-wave
+    // single-query workgroup per CU
+    a.slot_budget = (int32_t)(a.nq > 1 ? kTargetBlocks : kTargetBlocksSingle);
     a.group = c->group;
     *pa = a;
     return KIVI_OK;
@@ -263,7 +271,7 @@ int32_t fp16_auto_splits(int32_t batch, int32_t kv_heads, int32_t tokens, int32_
 }
 
 size_t fp16_counter_bytes(int32_t batch, int32_t q_heads) {
-    return ((size_t)batch * (size_t)q_heads * sizeof(uint32_t) + 255) & ~(size_t)255;
+    return (2 * (size_t)batch * (size_t)q_heads * sizeof(uint32_t) + 255) & ~(size_t)255;
 }
 
 // Events for the next attention launch of this thread (kivi_time_next_attention).
@@ -444,7 +452,7 @@ int32_t kivi_decode_attn_splits(const kivi_cache* c, int32_t q_heads) {
 size_t kivi_decode_attn_workspace(const kivi_cache* c, int32_t q_heads, int32_t num_splits) {
     if (check_shape(c) != KIVI_OK || q_heads <= 0) return 0;
     const int32_t s = num_splits > 0 ? num_splits : auto_splits(c, q_heads);
-    const size_t bytes = (size_t)s * (size_t)c->batch * (size_t)q_heads * (size_t)(c->head_dim + 2) * sizeof(float);
+    const size_t bytes = (size_t)s * (size_t)c->batch * (size_t)q_heads * (size_t)(c->head_dim + 2) * sizeof(uint64_t);
     return counter_bytes(c, q_heads) + ((bytes + 255) & ~(size_t)255);
 }
 
@@ -458,7 +466,7 @@ size_t kivi_decode_attn_fp16_workspace(int32_t batch, int32_t kv_heads, int32_t 
                                        int32_t num_splits) {
     if (fp16_check(batch, kv_heads, tokens, q_heads) != KIVI_OK || num_splits < 0) return 0;
     const int32_t s = num_splits > 0 ? num_splits : fp16_auto_splits(batch, kv_heads, tokens, q_heads);
-    const size_t bytes = (size_t)s * (size_t)batch * (size_t)q_heads * (size_t)(kD + 2) * sizeof(float);
+    const size_t bytes = (size_t)s * (size_t)batch * (size_t)q_heads * (size_t)(kD + 2) * sizeof(uint64_t);
     return fp16_counter_bytes(batch, q_heads) + ((bytes + 255) & ~(size_t)255);
 }
 
@@ -481,7 +489,7 @@ int kivi_decode_attn_fp16(const uint16_t* k, const uint16_t* v, int32_t batch, i
     AttnArgs a{};
     a.q = q;
     a.counters = static_cast<uint32_t*>(workspace);
-    a.ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + fp16_counter_bytes(batch, q_heads));
+    a.ws = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + fp16_counter_bytes(batch, q_heads));
     a.out = out;
     a.lse = lse;
     a.sm_log2 = (float)((double)sm_scale * 1.4426950408889634);

@@ -4,13 +4,17 @@
 // residual: out = softmax(sm_scale * q.K^T) . V (error judged at the attention output:
 // article "Your KV cache doesn't have a bit problem...", paragraph 3).
 //
-// Work split: grid (splits, B*Hq).  A 256-thread workgroup owns one query row and a
-// contiguous range of key groups; each of its 4 waves walks a quarter of that range
-// with its own online softmax (log2 domain).  The split holding the last groups also
-// reads the fp16 residual, as separate softmax states.  The workgroup merges its states
-// in LDS and writes one partial (o[128], m, l); the last workgroup of the row to arrive
-// merges the row's partials with the log-sum-exp merge and writes the output, so one
-// launch does the whole call.
+// Work split: grid (splits, B*Hq), sized for one workgroup per CU.  A 12-wave workgroup owns
+// one query row and a contiguous range of key groups, taken two groups (64 tokens) at a time
+// by its waves from an LDS counter, each wave with its own online softmax (log2 domain).  A
+// CU favours its oldest waves when it issues; with one workgroup per CU and the pairs handed
+// out on demand, all of the CU's waves still finish together (with three 4-wave workgroups
+// per CU and fixed quarters, the youngest workgroup ended about 10% after the oldest).  The
+// split holding the last groups first reads the fp16 residual, as separate softmax states,
+// and its waves join the queue after it.  The workgroup merges its states in LDS and writes
+// one partial (o[128], m, l); the last workgroup of the row to arrive merges the row's
+// partials with the log-sum-exp merge and writes the output, so one launch does the whole
+// call.
 //
 // Inner loop: one wave-iteration = two 32-token groups (64 tokens).  The 2-bit codes make
 // the loop bound by HBM and by the instructions that turn codes into products, so both
@@ -27,11 +31,12 @@
 //    leaves lane L with the four digit sums of token L.
 //  * values, per token: p*(z + c*s) = p*z + (p*s)*c.  Each lane's token weight p*s is
 //    rounded to fp16 and stored in LDS in the A-operand order of v_mfma_f32_16x16x32_f16
-//    (row 0; the other rows read zeros).  The codes become B operands with one shift and
-//    one v_and_or_b32 per two tokens, placing a code at bits 8-9 or 6-7 of an fp16 whose
-//    exponent reads 1.0 (the exact halves 1 + c/4, 1 + c/16); the weights carry the
-//    matching factor 4 or 16 and a power of two keeping them in fp16 range.  The constant
-//    part, the sum of the weights, is accumulated on the side and subtracted at the end.
+//    (row 0; the other rows read zeros).  The codes become B operands by masking in place:
+//    token field i of a code byte under the mask 0x00030003 << 2i (the odd 16-channel
+//    blocks after one shift by 8) is the fp16 subnormal c * 4^i * 2^-24, which the matrix
+//    cores multiply exactly.  The weight carries 16 * 4^-i and a power of two vs keeping it
+//    in fp16 range, so every product is 2^-20 * vs * p*s*c, and o = C * 2^20 / vs + sum p*z
+//    with the zero-point part sum p*z accumulated on the vector units.
 #include <hip/hip_ext.h>
 
 #include "kivi_attn_common.h"
@@ -45,10 +50,11 @@ constexpr int kZeroOff = kWtOff + 2 * 4 * 4 * 16;  // 512 zero bytes
 constexpr int kAreaBytes = kZeroOff + 512;
 
 template <int GS>
-__global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
-    __shared__ __align__(16) uint8_t sh_area[2][kWaves][kAreaBytes];
-    __shared__ __align__(16) float sh_o[1][kSlots][kD];
-    __shared__ float sh_m[1][kSlots], sh_l[1][kSlots];
+__global__ __launch_bounds__(kSqBlock) void attn_split_kernel(AttnArgs a) {
+    __shared__ __align__(16) uint8_t sh_area[2][kSqWaves][kAreaBytes];
+    __shared__ __align__(16) float sh_o[1][kSqSlots][kD];
+    __shared__ float sh_m[1][kSqSlots], sh_l[1][kSqSlots];
+    __shared__ int sh_next;   // pair queue of the workgroup's range (pairs past the static ones)
 
     const int split = grid_split(a);
     const int64_t qrow = grid_row(a);
@@ -56,6 +62,7 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
     const int hq = (int)(qrow % a.q_heads);
     const int64_t kvrow = b * a.kv_heads + hq / a.ratio;
     if (a.k_new != nullptr && split == 0 && hq % a.ratio == 0) store_new_token(a, kvrow);
+    const uint32_t tag_v = partial_tag(a, qrow);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform, as the compiler sees it
     const int gh = lane >> 5;          // group of the wave-iteration this lane serves
@@ -105,11 +112,23 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
     const int n_groups = rs.n_quant / kG;
     const int g_lo = split * rs.groups_per_split;
     const int g_hi = min(n_groups, g_lo + rs.groups_per_split);
-    const int cnt = max(0, g_hi - g_lo);
-    const int per_wave = (cnt + kWaves - 1) / kWaves;
-    const int gb = g_lo + min(cnt, wave * per_wave);
-    const int ge = g_lo + min(cnt, (wave + 1) * per_wave);
-    const int iters = (ge - gb + 1) >> 1;
+    const int n_pairs = (max(0, g_hi - g_lo) + 1) >> 1;   // the workgroup's pairs of 32-token tiles
+    if (threadIdx.x == 0) sh_next = 0;
+    __syncthreads();
+
+    // ---- fp16 residual first (split rs.res_split), as separate states: its loads meet a memory
+    // system that is not loaded yet, and the waves that take it start on the pairs later
+    float mr[1] = {-INFINITY}, lr[1] = {0.0f};
+    if (split == rs.res_split)
+        residual_states<1, kSqWaves>(a, rs, qrow, kvrow, wave, &sh_o[0][kSqWaves + wave][0], kSqSlots * kD, mr, lr);
+
+    // Pair schedule: wave w takes pairs w and w + kSqWaves, then one pair per iteration from
+    // the workgroup's LDS counter, requested one iteration before it is needed.  Pairs are
+    // handed out in increasing order, so a wave stops at its first pair past the range and
+    // no pair is skipped.  The waves of a CU's workgroup thereby finish together however the
+    // CU's issue arbitration favours them.
+    int c_cur = wave, c_nxt = wave + kSqWaves, pend = 0;
+    if (c_cur < n_pairs && lane == 0) pend = atomicAdd(&sh_next, 1);
 
     const int64_t tok_base = kvrow * (int64_t)a.token_cap;
     const uint8_t* kc_row = a.k_codes + tok_base * kRowBytes;
@@ -129,9 +148,12 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
     };
     // Each stream has one register set and reloads the next iteration's data right after its
     // last use in this one, so every load still has most of an iteration to arrive.
-    auto group_of = [&](int it, int half) {
-        const int g0 = gb + 2 * it;
-        return half == 0 ? g0 : (g0 + 1 < ge ? g0 + 1 : gb);   // in-bounds address for an idle half
+    // first groups of the current and the next iteration (wave-uniform)
+    int g_cur0 = g_lo + 2 * c_cur;
+    int g_nxt0 = c_nxt < n_pairs ? g_lo + 2 * c_nxt : g_cur0;
+    auto group_of = [&](int which, int half) {   // which: 0 = current iteration, 1 = next
+        const int g0 = which ? g_nxt0 : g_cur0;
+        return half == 0 ? g0 : (g0 + 1 < g_hi ? g0 + 1 : g0);   // in-bounds address for an idle half
     };
     auto load_kp = [&](Loads& L, int it) {
         L.kp = *reinterpret_cast<const uint4*>(kp_row + (int64_t)(group_of(it, gh) / (GS / kG)) * kD + 4 * wl);
@@ -152,14 +174,16 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
     // again, from the L2), so the compiler knows how many loads are in flight at each use and
     // waits for exactly the one it needs.
     Loads cur;
-    if (iters > 0) {
+    uint32_t tag;
+    if (c_cur < n_pairs) {
         load_kp(cur, 0);
         load_kc(cur, 0);
         load_vp(cur, 0);
         load_vc(cur, 0);
-        for (int it = 0; it < iters; ++it) {
-            const int nxt = min(it + 1, iters - 1);
-            const bool gvalid = gb + 2 * it + gh < ge;
+        tag = settle_tag(tag_v);
+        for (int it = 0;;) {
+            constexpr int nxt = 1;
+            const bool gvalid = g_cur0 + gh < g_hi;
             uint8_t* area = &sh_area[it & 1][wave][0];
 
             // ---- q*s of this half's group as 30-bit fixed point, four signed byte digits,
@@ -279,7 +303,18 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
                 }
             }
             load_vc(cur, nxt);
+            ++it;
+            c_cur = c_nxt;
+            if (c_cur >= n_pairs) break;
+            int pv = pend;
+            asm volatile("" : "+v"(pv));   // the request is read here, one iteration after it was made
+            c_nxt = 2 * kSqWaves + __builtin_amdgcn_readfirstlane(pv);
+            if (lane == 0) pend = atomicAdd(&sh_next, 1);
+            g_cur0 = g_lo + 2 * c_cur;
+            g_nxt0 = c_nxt < n_pairs ? g_lo + 2 * c_nxt : g_cur0;
         }
+    } else {
+        tag = settle_tag(tag_v);
     }
 
     // ---- the wave's quantized-part state: o = P.V * 2^20 / vs + sum p*zero
@@ -296,26 +331,18 @@ __global__ __launch_bounds__(kBlock) void attn_split_kernel(AttnArgs a) {
         sh_l[0][wave] = lsum;
     }
 
-    // ---- fp16 residual (last split only), as separate states
-    float mr[1], lr[1];
-    if (split == rs.res_split) {
-        residual_states<1>(a, rs, qrow, kvrow, wave, &sh_o[0][kWaves + wave][0], kSlots * kD, mr, lr);
-    } else {
-        mr[0] = -INFINITY;
-        lr[0] = 0.0f;
-    }
     if (lane == 0) {
-        sh_m[0][kWaves + wave] = mr[0];
-        sh_l[0][kWaves + wave] = lr[0];
+        sh_m[0][kSqWaves + wave] = mr[0];
+        sh_l[0][kSqWaves + wave] = lr[0];
     }
     __syncthreads();
-    finish_block<1>(a, rs.splits, split, qrow, qrow, sh_o, sh_m, sh_l);
+    finish_block<1, kSqWaves>(a, rs.splits, split, qrow, qrow, tag, sh_o, sh_m, sh_l);
 }
 
 hipError_t launch_decode_attn(const AttnArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
     if (a.nq > 1) return launch_decode_attn_gqa(a, s, t0, t1);
-    KIVI_BY_GROUP(a.group, hipExtLaunchKernelGGL(attn_split_kernel<GS>, attn_grid(a, a.q_rows), dim3(kBlock), 0, s, t0,
-                                                 t1, 0, a))
+    KIVI_BY_GROUP(a.group, hipExtLaunchKernelGGL(attn_split_kernel<GS>, attn_grid(a, a.q_rows), dim3(kSqBlock), 0, s,
+                                                 t0, t1, 0, a))
     return hipGetLastError();
 }
 

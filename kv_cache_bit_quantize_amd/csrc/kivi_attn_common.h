@@ -12,8 +12,10 @@
 
 namespace kivi {
 
-constexpr int kWaves = kBlock / 64;  // waves of the single-query kernel's workgroup
+constexpr int kWaves = kBlock / 64;  // waves of a 256-thread workgroup (the fp16 comparator's)
 constexpr int kSlots = 2 * kWaves;   // its softmax states per workgroup and row: quantized, residual
+constexpr int kSqBlock = 64 * kSqWaves;   // threads of a single-query 2-bit attention workgroup
+constexpr int kSqSlots = 2 * kSqWaves;
 constexpr int kPart = kD + 2;        // floats per split partial: o[128], m, l
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -87,14 +89,34 @@ __device__ __forceinline__ void load_q32(const uint16_t* q, float scale, float (
 // the sc1 coherence bit), each coherent by itself.  Device-scope fences are avoided on
 // purpose: on this chip each one writes back and invalidates the whole L2 of the XCD, which
 // stalls every other workgroup streaming through it.
-__device__ __forceinline__ void store_coherent(float* p, float v) {
+__device__ __forceinline__ void store_coherent(uint64_t* p, uint64_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ float load_coherent(float* p) {
+__device__ __forceinline__ uint64_t load_coherent(uint64_t* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// s_waitcnt with vmcnt(0) and the other counters left free (expcnt 7, lgkmcnt 15)
-constexpr int kWaitVmcnt0 = 0x0F70;
+// A split partial's value with the call's tag: one 8-byte store, so a reader sees both or
+// neither.
+__device__ __forceinline__ uint64_t tagged(float v, uint32_t tag) {
+    return (uint64_t)__builtin_bit_cast(uint32_t, v) | ((uint64_t)tag << 32);
+}
+// The tag of this call's split partials for counter row `counter`: one more than the epoch
+// that the previous call's merging workgroup stored (0 in a cleared workspace).  Loaded when
+// the workgroup starts; it is needed only when the workgroup ends.
+__device__ __forceinline__ uint32_t partial_tag(const AttnArgs& a, int64_t counter) {
+    return __hip_atomic_load(&a.counters[a.q_rows + counter], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+}
+// The tag as a wave-uniform scalar, read where the caller places this call: after its first
+// loads are issued, so that the wait for the tag's load overlaps the wait for them (a later
+// first use, after the loop, could wait for every load in flight).
+__device__ __forceinline__ uint32_t settle_tag(uint32_t v) {
+    asm volatile("" : "+v"(v));
+    return __builtin_amdgcn_readfirstlane(v);
+}
+// Polls of a partial value whose store has not landed yet (each after a short sleep).  The
+// value was stored before its workgroup's arrival was counted, so it lands within a memory
+// round trip; the bound only guarantees that the loop ends.
+constexpr int kMaxPolls = 1 << 22;
 
 // The (scale, zero) pairs of one value token, kD / GS of them, loaded at their own width (a
 // wider load would read past the last token of the last row) and returned as one word per
@@ -306,22 +328,42 @@ __device__ __forceinline__ void store_new_token(const AttnArgs& a, int64_t kvrow
 
 // Log-sum-exp merge of the split partials of query rows qrow0..qrow0+NQ-1, by the whole
 // workgroup, with each thread's coherent loads issued together: a thread merges, for one
-// (row, channel), every lpp-th split online (lpp = 2 for one row, else 1), and thread
-// pairs combine in LDS.  out = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M),
+// (row, channel), every lpp-th split online (lpp = THREADS / 128 for one row, else 1), and
+// the lpp threads of a channel combine in LDS.  out = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M),
 // lse = (M + log2 L) ln 2.  Re-arms the arrival counter.
-constexpr int kMergeBatch = 16;
+constexpr int kMergeBatch = 8;
 template <int NQ, int THREADS = kBlock>
-__device__ __forceinline__ void merge_rows(const AttnArgs& a, int splits, int64_t qrow0, int64_t counter) {
-    constexpr int kLpp = NQ == 1 ? 2 : 1;
-    static_assert(kLpp == 1 || THREADS == 2 * kD, "two threads per channel need 256 threads");
-    __shared__ float sh_mo[kD + 2];
-    const int t = threadIdx.x, sub = kLpp == 2 ? (t >> 7) : 0;
+__device__ __forceinline__ void merge_rows(const AttnArgs& a, int splits, int64_t qrow0, int64_t counter,
+                                           uint32_t tag) {
+    constexpr int kLpp = NQ == 1 ? THREADS / kD : 1;
+    static_assert(NQ != 1 || (THREADS % kD == 0 && kLpp >= 2), "one row needs whole multiples of 128 threads");
+    __shared__ float sh_mo[kLpp > 1 ? kLpp - 1 : 1][kD + 2];
+    const int t = threadIdx.x, sub = kLpp > 1 ? t / kD : 0;
     const int64_t stride = a.q_rows * kPart;
-    for (int idx = kLpp == 2 ? (t & (kD - 1)) : t; idx < NQ * kD; idx += THREADS / kLpp) {
+    for (int idx = kLpp > 1 ? (t % kD) : t; idx < NQ * kD; idx += THREADS / kLpp) {
         const int r = idx / kD, j = idx % kD;
-        float* rowp = a.ws + (qrow0 + r) * kPart;
+        uint64_t* rowp = a.ws + (qrow0 + r) * kPart;
+        // a value of this call: loaded again until its tag is this call's
+        auto settle = [&](uint64_t* p, uint64_t v) {
+            for (int n = 0; (uint32_t)(v >> 32) != tag && n < kMaxPolls; ++n) {
+                __builtin_amdgcn_s_sleep(1);
+                v = load_coherent(p);
+            }
+            return __builtin_bit_cast(float, (uint32_t)v);
+        };
         float M = -INFINITY, L = 0.0f, O = 0.0f;
         for (int s0 = sub; s0 < splits; s0 += kLpp * kMergeBatch) {
+            uint64_t mv[kMergeBatch], lv[kMergeBatch], ov[kMergeBatch];
+#pragma unroll
+            for (int u = 0; u < kMergeBatch; ++u) {   // every load first, then the checks
+                const int s = s0 + kLpp * u;
+                if (s < splits) {
+                    uint64_t* ps = rowp + s * stride;
+                    mv[u] = load_coherent(ps + kD);
+                    lv[u] = load_coherent(ps + kD + 1);
+                    ov[u] = load_coherent(ps + j);
+                }
+            }
             float ms[kMergeBatch], ls[kMergeBatch], os[kMergeBatch];
 #pragma unroll
             for (int u = 0; u < kMergeBatch; ++u) {
@@ -329,10 +371,10 @@ __device__ __forceinline__ void merge_rows(const AttnArgs& a, int splits, int64_
                 ms[u] = -INFINITY;
                 ls[u] = os[u] = 0.0f;
                 if (s < splits) {
-                    float* ps = rowp + s * stride;
-                    ms[u] = load_coherent(ps + kD);
-                    ls[u] = load_coherent(ps + kD + 1);
-                    os[u] = load_coherent(ps + j);
+                    uint64_t* ps = rowp + s * stride;
+                    ms[u] = settle(ps + kD, mv[u]);
+                    ls[u] = settle(ps + kD + 1, lv[u]);
+                    os[u] = settle(ps + j, ov[u]);
                 }
             }
 #pragma unroll
@@ -345,39 +387,54 @@ __device__ __forceinline__ void merge_rows(const AttnArgs& a, int splits, int64_
                 M = mn;
             }
         }
-        if (kLpp == 2) {
-            if (sub == 1) {
-                sh_mo[j] = O;
+        if (kLpp > 1) {   // one iteration per thread here: the barrier is reached by all
+            if (sub > 0) {
+                sh_mo[sub - 1][j] = O;
                 if (j == 0) {
-                    sh_mo[kD] = M;
-                    sh_mo[kD + 1] = L;
+                    sh_mo[sub - 1][kD] = M;
+                    sh_mo[sub - 1][kD + 1] = L;
                 }
             }
             __syncthreads();
-            if (sub == 1) return;
-            const float m1 = sh_mo[kD], l1 = sh_mo[kD + 1], o1 = sh_mo[j];
-            const float mn = fmaxf(M, m1);
-            const float al = M == -INFINITY ? 0.0f : exp2f(M - mn), be = m1 == -INFINITY ? 0.0f : exp2f(m1 - mn);
-            L = fmaf(L, al, l1 * be);
-            O = fmaf(O, al, o1 * be);
-            M = mn;
+            if (sub > 0) return;
+#pragma unroll
+            for (int k = 0; k < kLpp - 1; ++k) {
+                const float m1 = sh_mo[k][kD], l1 = sh_mo[k][kD + 1], o1 = sh_mo[k][j];
+                const float mn = fmaxf(M, m1);
+                const float al = M == -INFINITY ? 0.0f : exp2f(M - mn), be = m1 == -INFINITY ? 0.0f : exp2f(m1 - mn);
+                L = fmaf(L, al, l1 * be);
+                O = fmaf(O, al, o1 * be);
+                M = mn;
+            }
         }
         a.out[(qrow0 + r) * kD + j] = (uint16_t)f2h(L > 0.0f ? O / L : 0.0f);
         if (j == 0 && a.lse != nullptr) a.lse[qrow0 + r] = (M + log2f(L)) * 0.69314718055994531f;
     }
-    if (t == 0) a.counters[counter] = 0u;
+    if (t == 0) {
+        a.counters[counter] = 0u;
+        a.counters[a.q_rows + counter] = tag;   // the next call's partials carry tag + 1
+    }
 }
 
 // End of a WAVES-wave workgroup: merge its 2*WAVES states per row (empty states skipped), then write the
 // output directly (one split) or the split partial, and let the last workgroup of the row
-// group to arrive merge the partials.  The counter add comes after every partial store of
-// this workgroup completed (the wait, then the barrier), and the merging workgroup issues its
-// coherent loads only after its own add returned the final count, so it reads every partial.
+// group to arrive merge the partials.  Every partial value carries the call's tag (tag, from
+// partial_tag at the workgroup's start), so the merging workgroup, which loads after its own
+// arrival returned the final count, tells a value of this call from a stale one.
 template <int NQ, int WAVES = kWaves>
 __device__ __forceinline__ void finish_block(const AttnArgs& a, int splits, int split, int64_t qrow0, int64_t counter,
-                                             const float (*sh_o)[2 * WAVES][kD], const float (*sh_m)[2 * WAVES],
-                                             const float (*sh_l)[2 * WAVES]) {
+                                             uint32_t tag, const float (*sh_o)[2 * WAVES][kD],
+                                             const float (*sh_m)[2 * WAVES], const float (*sh_l)[2 * WAVES]) {
     constexpr int kS = 2 * WAVES;
+    // The arrival is counted first, by the last wave, before the merge below and the partial
+    // stores: its round trip overlaps them, and the merging workgroup checks each value's tag
+    // and loads a value again until its store has landed.  A wave's memory operations
+    // complete in issue order, so the arrival is counted by the wave with the least other
+    // work here (none in a 12-wave workgroup with one query row).
+    constexpr int kArrive = 64 * (WAVES - 1);
+    uint32_t arrived = 0;
+    if (splits > 1 && threadIdx.x == kArrive)
+        arrived = __hip_atomic_fetch_add(&a.counters[counter], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     for (int idx = threadIdx.x; idx < NQ * kD; idx += 64 * WAVES) {
         const int r = idx / kD, j = idx % kD;
         float M = -INFINITY;
@@ -396,23 +453,19 @@ __device__ __forceinline__ void finish_block(const AttnArgs& a, int splits, int 
             a.out[(qrow0 + r) * kD + j] = (uint16_t)f2h(L > 0.0f ? O / L : 0.0f);
             if (j == 0 && a.lse != nullptr) a.lse[qrow0 + r] = (M + log2f(L)) * 0.69314718055994531f;
         } else {
-            float* part = a.ws + ((int64_t)split * a.q_rows + qrow0 + r) * kPart;
-            store_coherent(&part[j], O);
+            uint64_t* part = a.ws + ((int64_t)split * a.q_rows + qrow0 + r) * kPart;
+            store_coherent(&part[j], tagged(O, tag));
             if (j == 0) {
-                store_coherent(&part[kD], M);
-                store_coherent(&part[kD + 1], L);
+                store_coherent(&part[kD], tagged(M, tag));
+                store_coherent(&part[kD + 1], tagged(L, tag));
             }
         }
     }
     if (splits == 1) return;
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // the partial stores have completed
-    __syncthreads();
     __shared__ bool sh_last;
-    if (threadIdx.x == 0)
-        sh_last = __hip_atomic_fetch_add(&a.counters[counter], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                  (unsigned)(splits - 1);
+    if (threadIdx.x == kArrive) sh_last = arrived == (unsigned)(splits - 1);
     __syncthreads();
-    if (sh_last) merge_rows<NQ, 64 * WAVES>(a, splits, qrow0, counter);
+    if (sh_last) merge_rows<NQ, 64 * WAVES>(a, splits, qrow0, counter, tag);
 }
 
 }  // namespace kivi

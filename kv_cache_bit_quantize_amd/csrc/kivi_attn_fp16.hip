@@ -36,6 +36,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     const int64_t kvrow = grow / chunks;
     const int chunk = (int)(grow % chunks);
     const int64_t qrow0 = (kvrow / a.kv_heads) * a.q_heads + (kvrow % a.kv_heads) * a.ratio + chunk * NQ;
+    const uint32_t tag_v = partial_tag(a, grow);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int kt = lane >> 2, kq = lane & 3;        // logits: token kt, channels 32kq..32kq+31
@@ -101,9 +102,11 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     // use; every load is issued unconditionally (clamped past the end), so the compiler
     // counts the loads in flight exactly.
     Loads cur;
+    uint32_t tag;
     if (iters > 0) {
         load_k(cur, 0);
         load_v(cur, 0);
+        tag = settle_tag(tag_v);
         for (int it = 0; it < iters; ++it) {
             const int nxt = min(it + 1, iters - 1);
             const bool valid = tb + it * kF16Tok + kt < te;
@@ -162,6 +165,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
+    } else {
+        tag = settle_tag(tag_v);
     }
 
     // ---- the wave's state per query head: the four token groups' shares of o summed
@@ -187,7 +192,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
         }
     }
     __syncthreads();
-    finish_block<NQ>(a, a.splits, split, qrow0, grow, sh_o, sh_m, sh_l);
+    finish_block<NQ>(a, a.splits, split, qrow0, grow, tag, sh_o, sh_m, sh_l);
 }
 
 hipError_t launch_decode_attn_fp16(const AttnArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {

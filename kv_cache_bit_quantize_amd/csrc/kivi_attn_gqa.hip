@@ -54,6 +54,7 @@ __global__ __launch_bounds__(kGqaBlock) __attribute__((amdgpu_waves_per_eu(3))) 
     const int chunk = (int)(grow % chunks);
     const int64_t qrow0 = (kvrow / a.kv_heads) * a.q_heads + (kvrow % a.kv_heads) * a.ratio + chunk * NQ;
     if (a.k_new != nullptr && split == 0 && chunk == 0) store_new_token(a, kvrow);
+    const uint32_t tag_v = partial_tag(a, grow);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform, as the compiler sees it
     const int gh = lane >> 5, tt = lane & 31;        // token role (loads): token tt of group gh
@@ -356,13 +357,17 @@ __global__ __launch_bounds__(kGqaBlock) __attribute__((amdgpu_waves_per_eu(3))) 
     // pair's second half is idle: its groups are out of range, so its logits are -inf and its
     // weights zero.
     Loads set0, set1;
+    uint32_t tag;
     if (iters > 0) {
         load_all(set0, 0);
         load_all(set1, min(1, iters - 1));
+        tag = settle_tag(tag_v);
         for (int it = 0; it < iters; it += 2) {
             iteration(set0, it);
             iteration(set1, it + 1);
         }
+    } else {
+        tag = settle_tag(tag_v);
     }
 
     // ---- each query's quantized-part state: o = P.V * 2^20 / vs + sum p*zero
@@ -407,7 +412,7 @@ __global__ __launch_bounds__(kGqaBlock) __attribute__((amdgpu_waves_per_eu(3))) 
         }
     }
     __syncthreads();
-    finish_block<NQ, W>(a, rs.splits, split, qrow0, grow, sh_o, sh_m, sh_l);
+    finish_block<NQ, W>(a, rs.splits, split, qrow0, grow, tag, sh_o, sh_m, sh_l);
 }
 
 hipError_t launch_decode_attn_gqa(const AttnArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {

@@ -7,6 +7,7 @@
 namespace kivi {
 
 constexpr int kMaxSplits = 1024;   // upper bound on split-K partitions of one decode call
+constexpr int kSqWaves = 12;       // waves of a single-query attention workgroup (one per CU)
 
 struct QuantArgs {          // kivi_quantize_{k,v}
     int32_t group;              // tokens per key group / channels per value group
@@ -60,7 +61,8 @@ struct AttnArgs {
     const uint16_t* v_sz;
     const uint16_t* k_res;
     const uint16_t* v_res;
-    float* ws;                  // [splits][B*Hq][D+2] partial (o, m, l), log2 domain
+    uint64_t* ws;               // [splits][B*Hq][D+2] partial (o, m, l), log2 domain: each value's bits
+                                // in the low word, the call's tag in the high word
     uint32_t* counters;         // [B*Hq] arrival counters, zero between calls
     uint16_t* out;              // [B][Hq][D]
     float* lse;                 // [B][Hq] or null

@@ -76,7 +76,7 @@ def test_fp16_comparator_arguments():
     assert L.kivi_decode_attn_fp16_splits(1, 1, 100, 1) == 1      # short context: one split
     assert L.kivi_decode_attn_fp16_splits(1, 1, 0, 1) == -2
     need = L.kivi_decode_attn_fp16_workspace(1, 32, 131072, 32, 0)
-    assert need == 256 + ((24 * 32 * 130 * 4 + 255) // 256) * 256
+    assert need == 256 + ((24 * 32 * 130 * 8 + 255) // 256) * 256
     assert L.kivi_decode_attn_fp16_workspace(1, 1, 0, 1, 0) == 0
 
 
@@ -101,7 +101,7 @@ def test_ragged_arguments():
     # split count for the longest context the cache holds: 256 tokens = 8 groups -> 1 split
     assert L.kivi_decode_attn_ragged_splits(C.byref(c), 4) == 1
     big = _cache(batch=1, kv_heads=32, token_cap=131072, n_quant=0, n_res=0)
-    assert L.kivi_decode_attn_ragged_splits(C.byref(big), 32) == 96   # four times the uniform count
+    assert L.kivi_decode_attn_ragged_splits(C.byref(big), 32) == 32   # four times the uniform count (8)
     assert L.kivi_decode_attn_ragged_splits(C.byref(big), 31) == -2
 
 
@@ -247,8 +247,8 @@ def test_split_selection_and_workspace():
     c = _cache(batch=1, kv_heads=32, token_cap=131104, n_quant=131040, n_res=32)
     s = L.kivi_decode_attn_splits(C.byref(c), 32)
     assert 8 <= s <= 1024
-    assert L.kivi_decode_attn_workspace(C.byref(c), 32, 0) == 256 + ((s * 32 * 130 * 4 + 255) // 256) * 256
+    assert L.kivi_decode_attn_workspace(C.byref(c), 32, 0) == 256 + ((s * 32 * 130 * 8 + 255) // 256) * 256
     # very short history: one split
     c = _cache(n_quant=32, n_res=0)
     assert L.kivi_decode_attn_splits(C.byref(c), 2) == 1
-    assert L.kivi_decode_attn_workspace(C.byref(c), 2, 7) == 256 + ((7 * 2 * 2 * 130 * 4 + 255) // 256) * 256
+    assert L.kivi_decode_attn_workspace(C.byref(c), 2, 7) == 256 + ((7 * 2 * 2 * 130 * 8 + 255) // 256) * 256
