@@ -141,8 +141,9 @@ int kivi_append_flush(kivi_cache* cache, const uint16_t* k_new, const uint16_t* 
  * zero before the first call that uses it (clear it once after allocating it); calls keep
  * it consistent afterwards.  Its first round_up(2*batch*q_heads*4, 256) bytes hold a
  * per-row arrival counter (zero again after every completed call) and a per-row call
- * epoch; the rest holds the split partials, each value stored with its call's tag.  Calls
- * that share a workspace must not run concurrently.  KIVI_ERR_SHAPE if the context is
+ * epoch; the rest holds the split partials, each value stored with its call's tag.  A
+ * workspace serves one (batch, q_heads) shape: clear it again before using it for another.
+ * Calls that share a workspace must not run concurrently.  KIVI_ERR_SHAPE if the context is
  * empty. */
 int kivi_decode_attn(const kivi_cache* cache, const uint16_t* q, int32_t q_heads,
                      float sm_scale, uint16_t* out, float* lse, void* workspace,
