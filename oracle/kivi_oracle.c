@@ -253,9 +253,12 @@ void kivi_ref_prefill(kivi_ref_cache* c, const uint16_t* k, const uint16_t* v,
  * quantizes only whole token groups of history.  Reading of the flush policy: when a
  * token arrives and the residual already holds R tokens, the oldest `group` of them
  * become the next quantized token group (keys and values together), then the new
- * token enters the residual. */
+ * token enters the residual.  The other policy (flush_all; the summary page's ablation
+ * over the residual length, where the residual is the full-precision buffer that fills
+ * up): all R residual tokens become the next R/group token groups. */
 int32_t kivi_ref_append(kivi_ref_cache* c, const uint16_t* k_new, const uint16_t* v_new) {
-    int32_t d = c->head_dim, G = c->group, R = c->residual_cap;
+    int32_t d = c->head_dim, R = c->residual_cap;
+    int32_t G = c->flush_all ? R : c->group;   /* tokens flushed: whole groups either way */
     int32_t flushed = 0;
     if (c->n_res == R) {
         uint16_t* kt = (uint16_t*)malloc((size_t)G * d * 2);

@@ -61,6 +61,7 @@ void kivi_ref_quant_group(const uint16_t* x, ptrdiff_t stride, int32_t n,
 typedef struct kivi_ref_cache {
     int32_t batch, kv_heads, head_dim, group, residual_cap, token_cap;
     int32_t n_quant, n_res, res_head;
+    int32_t flush_all;   /* flush policy: 0 = the oldest group of a full residual, 1 = all of it */
     uint8_t *k_codes, *v_codes;
     uint16_t *k_sz, *v_sz;
     uint16_t *k_res, *v_res;
@@ -82,8 +83,9 @@ void kivi_ref_prefill(kivi_ref_cache* c, const uint16_t* k, const uint16_t* v,
                       int32_t tokens, int64_t src_row_stride, int32_t n_quant);
 
 /* One decode-time append of a token per row (k_new, v_new: fp16 [row][head_dim]).
- * If the residual is full, the oldest `group` residual tokens are first quantized
- * into the next token group.  Returns 1 if a flush happened, 0 if not. */
+ * If the residual is full, its oldest `group` tokens (flush_all: all residual_cap of
+ * them) are first quantized into the next token groups.  Returns 1 if a flush happened,
+ * 0 if not. */
 int32_t kivi_ref_append(kivi_ref_cache* c, const uint16_t* k_new, const uint16_t* v_new);
 
 /* Materialise the whole context of one row in logical order (quantized history then

@@ -81,7 +81,7 @@ class _CacheStruct(C.Structure):
     _fields_ = [
         ("batch", C.c_int32), ("kv_heads", C.c_int32), ("head_dim", C.c_int32),
         ("group", C.c_int32), ("residual_cap", C.c_int32), ("token_cap", C.c_int32),
-        ("n_quant", C.c_int32), ("n_res", C.c_int32), ("res_head", C.c_int32),
+        ("n_quant", C.c_int32), ("n_res", C.c_int32), ("res_head", C.c_int32), ("flush_all", C.c_int32),
         ("k_codes", C.c_void_p), ("v_codes", C.c_void_p),
         ("k_sz", C.c_void_p), ("v_sz", C.c_void_p),
         ("k_res", C.c_void_p), ("v_res", C.c_void_p),
@@ -91,7 +91,7 @@ class _CacheStruct(C.Structure):
 class RefCache:
     """Host-memory cache in the documented packed layout, driven by the C oracle."""
 
-    def __init__(self, batch, kv_heads, head_dim=128, group=32, residual_cap=128, token_cap=0):
+    def __init__(self, batch, kv_heads, head_dim=128, group=32, residual_cap=128, token_cap=0, flush_all=False):
         rows = batch * kv_heads
         self.batch, self.kv_heads, self.head_dim = batch, kv_heads, head_dim
         self.group, self.residual_cap, self.token_cap = group, residual_cap, token_cap
@@ -102,7 +102,7 @@ class RefCache:
         self.v_sz = np.zeros((rows, token_cap, head_dim // group, 2), np.uint16)
         self.k_res = np.zeros((rows, residual_cap, head_dim), np.uint16)
         self.v_res = np.zeros((rows, residual_cap, head_dim), np.uint16)
-        self.s = _CacheStruct(batch, kv_heads, head_dim, group, residual_cap, token_cap, 0, 0, 0,
+        self.s = _CacheStruct(batch, kv_heads, head_dim, group, residual_cap, token_cap, 0, 0, 0, int(flush_all),
                               self.k_codes.ctypes.data, self.v_codes.ctypes.data,
                               self.k_sz.ctypes.data, self.v_sz.ctypes.data,
                               self.k_res.ctypes.data, self.v_res.ctypes.data)

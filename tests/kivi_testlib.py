@@ -38,10 +38,10 @@ def bits(t):
     return t.numpy().view(np.uint16)
 
 
-def ref_cache(batch, kv_heads, token_cap, k, v, n_quant, residual_cap=128, group=32):
+def ref_cache(batch, kv_heads, token_cap, k, v, n_quant, residual_cap=128, group=32, flush_all=False):
     """Oracle cache prefilled from fp16 tensors k, v [B, H, T, D]."""
     B, H, T, D = k.shape
-    c = ref.RefCache(batch, kv_heads, D, group, residual_cap, token_cap=token_cap)
+    c = ref.RefCache(batch, kv_heads, D, group, residual_cap, token_cap=token_cap, flush_all=flush_all)
     c.prefill(bits(k).reshape(B * H, T, D), bits(v).reshape(B * H, T, D), n_quant)
     return c
 

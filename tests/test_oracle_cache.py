@@ -66,6 +66,57 @@ def test_append_from_empty_matches_closed_form_and_prefill(R, G):
         assert np.array_equal(c.v_res[:, slot], v[:, nq + i])
 
 
+def _closed_form_state_flush_all(n_tokens, R=R):
+    """Flush of the whole residual: after n tokens the ring holds ((n - 1) mod R) + 1 of
+    them (n >= 1) and the history the rest, always a whole number of residuals."""
+    n_res = (n_tokens - 1) % R + 1 if n_tokens > 0 else 0
+    return n_tokens - n_res, n_res, 0
+
+
+@pytest.mark.parametrize("R,G", [(32, 32), (64, 32), (128, 32), (128, 64), (128, 128), (256, 64)])
+def test_flush_all_from_empty_matches_closed_form_and_prefill(R, G):
+    """The other flush policy: a full residual is quantized whole (R / G groups at once).
+    The history grows by R at every flush, the ring's head stays at slot 0, and the cache
+    equals a prefill of the same tokens with that history."""
+    B, H, T = 2, 2, 700
+    k, v = _tokens(B * H, T, 7)
+    c = ref.RefCache(B, H, D, G, R, token_cap=768, flush_all=True)
+    flush_steps = []
+    for t in range(T):
+        if c.append(k[:, t], v[:, t]):
+            flush_steps.append(t)
+        assert (c.n_quant, c.n_res, c.res_head) == _closed_form_state_flush_all(t + 1, R)
+    assert flush_steps == list(range(R, T, R))
+    p = ref.RefCache(B, H, D, G, R, token_cap=768)
+    p.prefill(k, v, c.n_quant)
+    nq = c.n_quant
+    assert np.array_equal(c.k_codes[:, : nq // 32], p.k_codes[:, : nq // 32])
+    assert np.array_equal(c.v_codes[:, : nq // 32], p.v_codes[:, : nq // 32])
+    assert np.array_equal(c.k_sz[:, : nq // G], p.k_sz[:, : nq // G])
+    assert np.array_equal(c.v_sz[:, :nq], p.v_sz[:, :nq])
+    for i in range(c.n_res):
+        assert np.array_equal(c.k_res[:, (c.res_head + i) % R], k[:, nq + i])
+        assert np.array_equal(c.v_res[:, (c.res_head + i) % R], v[:, nq + i])
+
+
+def test_flush_all_from_a_prefilled_state_moves_the_head_by_whole_residuals():
+    """From a prefill whose ring does not start at slot 0 of a cycle: every flush moves R
+    tokens, so the head comes back to the same slot and the history stays a multiple of G."""
+    n_quant, n_res, steps = 96, 100, 300
+    k, v = _tokens(1, n_quant + n_res + steps, 8)
+    c = ref.RefCache(1, 1, D, G, R, token_cap=1024, flush_all=True)
+    c.prefill(k[:, : n_quant + n_res], v[:, : n_quant + n_res], n_quant)
+    flushes = [s for s in range(steps) if c.append(k[:, n_quant + n_res + s], v[:, n_quant + n_res + s])]
+    assert flushes == [28, 28 + R, 28 + 2 * R]
+    assert (c.n_quant, c.n_res, c.res_head) == (n_quant + 3 * R, n_res + steps - 3 * R, 0)
+    p = ref.RefCache(1, 1, D, G, R, token_cap=1024)
+    p.prefill(k, v, c.n_quant)
+    for row in range(1):
+        Kc, Vc = c.dequant_row(row)
+        Kp, Vp = p.dequant_row(row)
+        assert np.array_equal(Kc, Kp) and np.array_equal(Vc, Vp)
+
+
 @pytest.mark.parametrize("n_quant,n_res,steps,flushes", [
     (3968, 128, 64, [0, 32]),            # Llama-2-7B layer workload: steps 1 and 33
     (8064, 128, 128, [0, 32, 64, 96]),   # GQA workload: steps 1, 33, 65, 97
