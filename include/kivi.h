@@ -83,13 +83,19 @@ enum {
  * State: the first n_quant tokens of the context (a multiple of G) are in the quantized
  * history; the next n_res (0..R) are in the ring.  res_head is a multiple of G.
  */
+/* Flush policy (kivi_cache.flags).  Default (0): a full residual gives its oldest G tokens
+ * to the history when a token arrives.  KIVI_FLUSH_ALL: it gives all R of them (R/G groups),
+ * the other reading of the residual length of the pages' ablation (summary page, "Key
+ * points"): the full-precision buffer fills up to R and is then quantized as a whole. */
+#define KIVI_FLUSH_ALL 1
+
 typedef struct kivi_cache {
     int32_t batch, kv_heads, head_dim;
     int32_t group;           /* G */
     int32_t residual_cap;    /* R, a multiple of G */
     int32_t token_cap;       /* capacity of the quantized history in tokens, multiple of G */
     int32_t n_quant, n_res, res_head;
-    int32_t reserved;        /* must be 0 */
+    int32_t flags;           /* 0, or KIVI_FLUSH_ALL */
     uint8_t* k_codes;
     uint8_t* v_codes;
     uint16_t* k_sz;
@@ -121,9 +127,9 @@ int kivi_prefill(const uint16_t* k, const uint16_t* v, int32_t tokens, int64_t s
 
 /* One decode-time token per row (k_new, v_new: fp16 [row][D], contiguous).
  * The record keeps the newest R tokens in 16-bit floats and quantizes only grouped
- * history ("KV bytes basis").  If the ring already holds R tokens, the oldest G of them
- * become key token group n_quant/G and value tokens n_quant..n_quant+G-1 (flush), then
- * the new token enters the ring.  Updates n_quant, n_res and res_head on the host
+ * history ("KV bytes basis").  If the ring already holds R tokens, the oldest F of them
+ * (F = G, or R with KIVI_FLUSH_ALL) become key token groups n_quant/G.. and value tokens
+ * n_quant..n_quant+F-1 (flush), then the new token enters the ring.  Updates n_quant, n_res and res_head on the host
  * immediately (no device round trip).  *flushed (host, nullable) receives 1 if a group
  * was flushed, else 0.  KIVI_ERR_CAPACITY if a flush would pass token_cap. */
 int kivi_append_flush(kivi_cache* cache, const uint16_t* k_new, const uint16_t* v_new,
@@ -157,7 +163,7 @@ int kivi_decode_attn(const kivi_cache* cache, const uint16_t* q, int32_t q_heads
  * token straight from k_new / v_new while one workgroup per KV head writes it into its
  * ring slot; when a group must be flushed first it is the two launches of the separate
  * calls.  The workspace must fit the attention on the state after the append: when the
- * ring is full that is kivi_decode_attn_workspace of the cache with n_quant + group.
+ * ring is full that is kivi_decode_attn_workspace of the cache with n_quant + F.
  * Validation happens before anything is enqueued, so on error nothing changes. */
 int kivi_decode_step(kivi_cache* cache, const uint16_t* k_new, const uint16_t* v_new,
                      const uint16_t* q, int32_t q_heads, float sm_scale, uint16_t* out, float* lse,
@@ -181,7 +187,7 @@ int kivi_decode_step(kivi_cache* cache, const uint16_t* k_new, const uint16_t* v
 
 /* kivi_append_flush for every sequence of a ragged batch: one new token per sequence
  * (k_new, v_new: fp16 [batch][kv_heads][128]), a sequence whose ring is full first
- * flushing its oldest G ring tokens into a new group, then each sequence's state moved on
+ * flushing its oldest F ring tokens into new groups, then each sequence's state moved on
  * on the device (two kernel launches in stream order).  A sequence whose flush would pass
  * token_cap is left as it was and gets KIVI_SEQ_CAPACITY. */
 int kivi_append_flush_ragged(const kivi_cache* cache, int32_t* seq_state, const uint16_t* k_new,

@@ -27,7 +27,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 int check_shape(const kivi_cache* c) {
     if (c == nullptr) return KIVI_ERR_NULL;
     if (c->batch <= 0 || c->kv_heads <= 0 || c->head_dim <= 0 || c->group <= 0 ||
-        c->residual_cap <= 0 || c->token_cap < 0 || c->reserved != 0)
+        c->residual_cap <= 0 || c->token_cap < 0 || (c->flags & ~KIVI_FLUSH_ALL) != 0)
         return KIVI_ERR_SHAPE;
     if (c->head_dim % 4 != 0 || c->head_dim % c->group != 0 || c->residual_cap % c->group != 0 ||
         c->token_cap % c->group != 0)
@@ -139,8 +139,9 @@ int prepare_append(const kivi_cache* c, const uint16_t* k_new, const uint16_t* v
     if (k_new == nullptr || v_new == nullptr) return KIVI_ERR_NULL;
     if (!aligned16(k_new) || !aligned16(v_new)) return KIVI_ERR_SHAPE;
     const int G = c->group, R = c->residual_cap;
+    const int F = (c->flags & KIVI_FLUSH_ALL) ? R : G;   // tokens a flush moves
     const bool flush = c->n_res == R;
-    if (flush && c->n_quant + G > c->token_cap) return KIVI_ERR_CAPACITY;
+    if (flush && c->n_quant + F > c->token_cap) return KIVI_ERR_CAPACITY;
     int n_quant = c->n_quant, n_res = c->n_res, head = c->res_head;
     a->k_new = k_new;
     a->v_new = v_new;
@@ -149,9 +150,9 @@ int prepare_append(const kivi_cache* c, const uint16_t* k_new, const uint16_t* v
     a->flush_slot = head;
     a->flush_group = n_quant / G;
     if (flush) {
-        n_quant += G;
-        head = (head + G) % R;
-        n_res -= G;
+        n_quant += F;
+        head = (head + F) % R;
+        n_res -= F;
     }
     a->new_slot = (head + n_res) % R;
     a->token_cap = c->token_cap;
@@ -165,6 +166,7 @@ int prepare_append(const kivi_cache* c, const uint16_t* k_new, const uint16_t* v
     a->seq_state = nullptr;   // one state for the whole batch (the fields above)
     a->kv_heads = c->kv_heads;
     a->group = G;
+    a->flush_all = (c->flags & KIVI_FLUSH_ALL) ? 1 : 0;
     *next = *c;
     next->n_quant = n_quant;
     next->n_res = n_res + 1;
@@ -418,6 +420,7 @@ int kivi_append_flush_ragged(const kivi_cache* c, int32_t* seq_state, const uint
     a.seq_state = seq_state;
     a.kv_heads = c->kv_heads;
     a.group = c->group;
+    a.flush_all = (c->flags & KIVI_FLUSH_ALL) ? 1 : 0;
     return hip_status(launch_append_flush_ragged(a, c->batch, (hipStream_t)stream));
 }
 

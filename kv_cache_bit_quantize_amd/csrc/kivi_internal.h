@@ -51,6 +51,7 @@ struct AppendArgs {
     int32_t* seq_state;
     int32_t kv_heads;
     int32_t group;              // tokens per key group (= channels per value group): 32, 64 or 128
+    int32_t flush_all;          // a flush moves the whole residual (else its oldest group)
 };
 
 struct AttnArgs {

@@ -181,25 +181,28 @@ __global__ __launch_bounds__(kBlock) void residual_load_kernel(ResidualArgs a) {
     reinterpret_cast<uint4*>(a.v_res + d)[c] = reinterpret_cast<const uint4*>(a.v + so)[c];
 }
 
-// grid.x = rows.  Optional flush of ring slots [flush_slot, flush_slot+GS) into key group
-// flush_group / value tokens flush_group*GS.., then the new token into new_slot.  In a
-// ragged batch each row takes these from its sequence's state (flush when its ring is full);
-// a sequence whose state is out of range, or whose flush would pass token_cap, is skipped
-// and flagged.
+// grid (rows, groups of a flush).  Optional flush of the F ring tokens from flush_slot (F =
+// GS, or the whole ring with flush_all) into key groups flush_group.. / value tokens
+// flush_group*GS.., one workgroup per group, then the new token into new_slot.  In a ragged
+// batch each row takes these from its sequence's state (flush when its ring is full); a
+// sequence whose state is out of range, or whose flush would pass token_cap, is skipped and
+// flagged.
 template <int GS>
 __global__ __launch_bounds__(kBlock) void append_flush_kernel(AppendArgs a) {
     __shared__ uint4 tile4[GS * kD / 8];
     __shared__ float sh_mn[kD], sh_s[kD];
     const int64_t row = blockIdx.x;
+    const int part = blockIdx.y;   // which group of the flush this workgroup quantizes
     const int tid = threadIdx.x;
+    const int F = a.flush_all ? a.residual_cap : GS;   // tokens a flush moves
     int do_flush = a.do_flush, flush_slot = a.flush_slot, flush_group = a.flush_group, new_slot = a.new_slot;
     if (a.seq_state != nullptr) {
         int32_t* s = a.seq_state + 4 * (row / a.kv_heads);
         const int32_t nq = s[0], nr = s[1], rh = s[2];
         const bool ok = state_in_range(nq, nr, rh, a.token_cap, a.residual_cap, GS);
         const bool flush = nr == a.residual_cap;
-        if (!ok || (flush && nq + GS > a.token_cap)) {   // the whole workgroup leaves together
-            if (row % a.kv_heads == 0 && tid == 0)
+        if (!ok || (flush && nq + F > a.token_cap)) {   // the whole workgroup leaves together
+            if (row % a.kv_heads == 0 && part == 0 && tid == 0)
                 __hip_atomic_fetch_or(&s[3], ok ? kSeqCapacity : kSeqBadState, __ATOMIC_RELAXED,
                                       __HIP_MEMORY_SCOPE_AGENT);
             return;
@@ -207,30 +210,36 @@ __global__ __launch_bounds__(kBlock) void append_flush_kernel(AppendArgs a) {
         do_flush = flush;
         flush_slot = rh;
         flush_group = nq / GS;
-        const int head = flush ? (rh + GS) % a.residual_cap : rh;
-        new_slot = (head + (flush ? nr - GS : nr)) % a.residual_cap;
+        const int head = flush ? (rh + F) % a.residual_cap : rh;
+        new_slot = (head + (flush ? nr - F : nr)) % a.residual_cap;
     }
+    if (part > 0 && (!do_flush || part * GS >= F)) return;   // (no such group of this row's flush)
     if (do_flush) {
-        // the GS oldest ring tokens, contiguous: the ring length and its head are multiples of GS
-        const uint4* kr = reinterpret_cast<const uint4*>(a.k_res + (row * a.residual_cap + flush_slot) * kD);
+        // group `part` of the flush: GS ring tokens, contiguous (the ring length and its head
+        // are multiples of GS)
+        const int slot = (flush_slot + part * GS) % a.residual_cap;
+        const int group = flush_group + part;
+        const uint4* kr = reinterpret_cast<const uint4*>(a.k_res + (row * a.residual_cap + slot) * kD);
 #pragma unroll
         for (int i = tid; i < GS * kD / 8; i += kBlock) tile4[i] = kr[i];
         __syncthreads();
-        const int dst_tok = flush_group * GS;
+        const int dst_tok = group * GS;
         uint8_t* kc = a.k_codes + row * a.token_cap * kRowBytes + (int64_t)(dst_tok / kG) * kTileBytes;
-        uint32_t* kp = reinterpret_cast<uint32_t*>(a.k_sz) + (row * (a.token_cap / GS) + flush_group) * kD;
+        uint32_t* kp = reinterpret_cast<uint32_t*>(a.k_sz) + (row * (a.token_cap / GS) + group) * kD;
         quant_k_group<GS>(reinterpret_cast<const uint16_t*>(tile4), sh_mn, sh_s, kc, kp);
         // values: the same GS ring tokens as GS/32 value tiles
         __shared__ __align__(16) uint8_t sh_codes[kG][kD];
 #pragma unroll 1
         for (int tl = 0; tl < GS / kG; ++tl)
-            quant_v_tile<GS>(a.v_res + (row * a.residual_cap + flush_slot + tl * kG) * kD, kD, 0, kG, sh_codes,
+            quant_v_tile<GS>(a.v_res + (row * a.residual_cap + slot + tl * kG) * kD, kD, 0, kG, sh_codes,
                              a.v_codes + (row * a.token_cap + dst_tok + tl * kG) * kRowBytes,
                              reinterpret_cast<uint32_t*>(a.v_sz) +
                                  value_pair_index<GS>(row * a.token_cap + dst_tok + tl * kG, 0));
         __syncthreads();   // every read of the flushed slots is done before the overwrite
     }
-    if (tid < 32) {
+    // The new token goes to the first flushed group's first slot (or anywhere in the ring
+    // without a flush): part 0 stores it, after its reads of that group.
+    if (part == 0 && tid < 32) {
         const int c = tid & 15;
         const uint16_t* src = (tid < 16 ? a.k_new : a.v_new) + row * kD;
         uint16_t* dst = (tid < 16 ? a.k_res : a.v_res) + (row * a.residual_cap + new_slot) * kD;
@@ -247,10 +256,11 @@ __global__ __launch_bounds__(64) void seq_state_update_kernel(AppendArgs a, int3
     const int32_t nq = s[0], nr = s[1], rh = s[2], G = a.group;
     if (!state_in_range(nq, nr, rh, a.token_cap, a.residual_cap, G)) return;
     const bool flush = nr == a.residual_cap;
-    if (flush && nq + G > a.token_cap) return;
-    s[0] = flush ? nq + G : nq;
-    s[1] = (flush ? nr - G : nr) + 1;
-    s[2] = flush ? (rh + G) % a.residual_cap : rh;
+    const int32_t F = a.flush_all ? a.residual_cap : G;
+    if (flush && nq + F > a.token_cap) return;
+    s[0] = flush ? nq + F : nq;
+    s[1] = (flush ? nr - F : nr) + 1;
+    s[2] = flush ? (rh + F) % a.residual_cap : rh;
 }
 
 // ------------------------------------------------------------------ launchers ----
@@ -278,13 +288,19 @@ hipError_t launch_residual_load(const ResidualArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+// grid (rows, groups of the flush): a flush of the whole residual quantizes its R/G groups
+// in parallel
 hipError_t launch_append_flush(const AppendArgs& a, hipStream_t s) {
-    KIVI_BY_GROUP(a.group, hipLaunchKernelGGL(append_flush_kernel<GS>, dim3((unsigned)a.rows), dim3(kBlock), 0, s, a))
+    const unsigned parts = a.do_flush && a.flush_all ? (unsigned)(a.residual_cap / a.group) : 1u;
+    KIVI_BY_GROUP(a.group,
+                  hipLaunchKernelGGL(append_flush_kernel<GS>, dim3((unsigned)a.rows, parts), dim3(kBlock), 0, s, a))
     return hipGetLastError();
 }
 
 hipError_t launch_append_flush_ragged(const AppendArgs& a, int32_t batch, hipStream_t s) {
-    KIVI_BY_GROUP(a.group, hipLaunchKernelGGL(append_flush_kernel<GS>, dim3((unsigned)a.rows), dim3(kBlock), 0, s, a))
+    const unsigned parts = a.flush_all ? (unsigned)(a.residual_cap / a.group) : 1u;
+    KIVI_BY_GROUP(a.group,
+                  hipLaunchKernelGGL(append_flush_kernel<GS>, dim3((unsigned)a.rows, parts), dim3(kBlock), 0, s, a))
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(seq_state_update_kernel, dim3((unsigned)((batch + 63) / 64)), dim3(64), 0, s, a, batch);

@@ -22,6 +22,7 @@ EXPORTS = ["kivi_quantize_k_per_channel", "kivi_quantize_v_per_token", "kivi_pre
            "kivi_decode_attn_fp16_workspace", "kivi_append_flush_ragged", "kivi_decode_attn_ragged",
            "kivi_decode_attn_ragged_splits"]
 
+KIVI_FLUSH_ALL = 1        # kivi_cache.flags: a full residual is flushed whole (else its oldest group)
 KIVI_SEQ_CAPACITY = 1     # seq_state flags: an append was skipped (its flush would pass token_cap)
 KIVI_SEQ_BAD_STATE = 2    # seq_state flags: the sequence's state was out of range and not used
 
@@ -36,7 +37,7 @@ class kivi_cache(C.Structure):
     _fields_ = [
         ("batch", C.c_int32), ("kv_heads", C.c_int32), ("head_dim", C.c_int32), ("group", C.c_int32),
         ("residual_cap", C.c_int32), ("token_cap", C.c_int32),
-        ("n_quant", C.c_int32), ("n_res", C.c_int32), ("res_head", C.c_int32), ("reserved", C.c_int32),
+        ("n_quant", C.c_int32), ("n_res", C.c_int32), ("res_head", C.c_int32), ("flags", C.c_int32),
         ("k_codes", C.c_void_p), ("v_codes", C.c_void_p), ("k_sz", C.c_void_p), ("v_sz", C.c_void_p),
         ("k_res", C.c_void_p), ("v_res", C.c_void_p),
     ]
@@ -101,7 +102,8 @@ def _ptr(t):
 class Cache:
     """Device buffers of one KIVI cache (layout of include/kivi.h) and its descriptor."""
 
-    def __init__(self, batch, kv_heads, token_cap, head_dim=128, group=32, residual_cap=128, device="cuda"):
+    def __init__(self, batch, kv_heads, token_cap, head_dim=128, group=32, residual_cap=128, device="cuda",
+                 flush_all=False):
         rows = batch * kv_heads
         u8, f16 = torch.uint8, torch.int16
         tiles = token_cap // 32                    # one 1024-byte tile of codes per 32 tokens
@@ -111,8 +113,8 @@ class Cache:
         self.v_sz = torch.zeros((rows, token_cap, head_dim // group, 2), dtype=f16, device=device)
         self.k_res = torch.zeros((rows, residual_cap, head_dim), dtype=f16, device=device)
         self.v_res = torch.zeros((rows, residual_cap, head_dim), dtype=f16, device=device)
-        self.c = kivi_cache(batch, kv_heads, head_dim, group, residual_cap, token_cap, 0, 0, 0, 0,
-                            self.k_codes.data_ptr(), self.v_codes.data_ptr(), self.k_sz.data_ptr(),
+        self.c = kivi_cache(batch, kv_heads, head_dim, group, residual_cap, token_cap, 0, 0, 0,
+                            KIVI_FLUSH_ALL if flush_all else 0, self.k_codes.data_ptr(), self.v_codes.data_ptr(), self.k_sz.data_ptr(),
                             self.v_sz.data_ptr(), self.k_res.data_ptr(), self.v_res.data_ptr())
         self.device = torch.device(device)
         self._ws = None
@@ -131,7 +133,8 @@ class Cache:
         v = object.__new__(Cache)
         for name in ("k_codes", "v_codes", "k_sz", "v_sz", "k_res", "v_res"):
             setattr(v, name, getattr(self, name)[b * H:(b + 1) * H])
-        v.c = kivi_cache(1, H, self.c.head_dim, self.c.group, self.c.residual_cap, self.c.token_cap, 0, 0, 0, 0,
+        v.c = kivi_cache(1, H, self.c.head_dim, self.c.group, self.c.residual_cap, self.c.token_cap, 0, 0, 0,
+                         self.c.flags,
                          v.k_codes.data_ptr(), v.v_codes.data_ptr(), v.k_sz.data_ptr(), v.v_sz.data_ptr(),
                          v.k_res.data_ptr(), v.v_res.data_ptr())
         v.device = self.device
@@ -143,9 +146,10 @@ class Cache:
         next append (a decode step attends after its append, and a flush lengthens the history,
         which can raise the automatic split count)."""
         need = lib.kivi_decode_attn_workspace(C.byref(self.c), q_heads, num_splits)
-        if self.c.n_res == self.c.residual_cap and self.c.n_quant + self.c.group <= self.c.token_cap:
+        flush = self.c.residual_cap if self.c.flags & KIVI_FLUSH_ALL else self.c.group
+        if self.c.n_res == self.c.residual_cap and self.c.n_quant + flush <= self.c.token_cap:
             nxt = kivi_cache.from_buffer_copy(self.c)
-            nxt.n_quant += nxt.group
+            nxt.n_quant += flush
             need = max(need, lib.kivi_decode_attn_workspace(C.byref(nxt), q_heads, num_splits))
         if self._ws is None or self._ws.numel() < need:
             # zero-filled: the leading per-row arrival counters must start at zero

@@ -31,10 +31,10 @@ def test_every_declared_symbol_is_exported():
 
 def _cache(**kw):
     f = dict(batch=2, kv_heads=2, head_dim=128, group=32, residual_cap=128, token_cap=256,
-             n_quant=64, n_res=10, res_head=0, reserved=0)
+             n_quant=64, n_res=10, res_head=0, flags=0)
     f.update({k: v for k, v in kw.items() if k in f})
     c = kivi.kivi_cache(*[f[k] for k in ("batch", "kv_heads", "head_dim", "group", "residual_cap",
-                                         "token_cap", "n_quant", "n_res", "res_head", "reserved")])
+                                         "token_cap", "n_quant", "n_res", "res_head", "flags")])
     for name in ("k_codes", "v_codes", "k_sz", "v_sz", "k_res", "v_res"):
         setattr(c, name, kw.get(name, FAKE))
     return c
@@ -142,7 +142,7 @@ def test_group_sizes_supported_and_sized(G, per_token):
     (dict(token_cap=100), -2),
     (dict(residual_cap=100), -2),
     (dict(batch=0), -2),
-    (dict(reserved=1), -2),
+    (dict(flags=2), -2),             # unknown flag bits
 ])
 def test_shape_validation(kw, code):
     c = _cache(**kw)
@@ -198,6 +198,15 @@ def test_append_flush_errors_leave_state():
     assert L.kivi_append_flush(C.byref(c), C.c_void_p(FAKE + 8), C.c_void_p(FAKE), None, None) == -2
     c = _cache(k_res=0)
     assert L.kivi_append_flush(C.byref(c), C.c_void_p(FAKE), C.c_void_p(FAKE), None, None) == -1
+    # flush of the whole residual (128 tokens): room for one more group is not enough
+    whole = _cache(n_quant=160, n_res=128, res_head=0, flags=kivi.KIVI_FLUSH_ALL)
+    st = _state(whole)
+    assert L.kivi_append_flush(C.byref(whole), C.c_void_p(FAKE), C.c_void_p(FAKE), None, None) == -4
+    assert _state(whole) == st
+    steps = C.c_int32(7)
+    assert L.kivi_decode_step(C.byref(whole), C.c_void_p(FAKE), C.c_void_p(FAKE), C.c_void_p(FAKE), 2, 0.1,
+                              C.c_void_p(FAKE), None, C.c_void_p(FAKE), 1 << 30, 0, C.byref(steps), None) == -4
+    assert _state(whole) == st and steps.value == 7
 
 
 def test_decode_attn_argument_errors():
