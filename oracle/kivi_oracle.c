@@ -95,6 +95,15 @@ static float rne_float(float t) {
  * stored as +0 whatever the order of -0 and +0 in the group. */
 void kivi_ref_quant_group(const uint16_t* x, ptrdiff_t stride, int32_t n,
                           uint16_t* scale, uint16_t* zero, uint8_t* codes) {
+    kivi_ref_quant_group_bits(x, stride, n, 2, scale, zero, codes);
+}
+
+/* The same quantizer with 2^bits levels (bits = 2 or 4): s = (max-min)/(2^bits - 1), codes
+ * clamped to 2^bits - 1.  KIVI-2 names the 2-bit member of the family; the width is the
+ * scheme's parameter. */
+void kivi_ref_quant_group_bits(const uint16_t* x, ptrdiff_t stride, int32_t n, int32_t bits,
+                               uint16_t* scale, uint16_t* zero, uint8_t* codes) {
+    const float top = (float)((1 << bits) - 1);   /* the highest code */
     float mn = INFINITY, mx = -INFINITY;
     for (int32_t i = 0; i < n; ++i) {
         float v = kivi_ref_f16_to_f32(x[i * stride]);
@@ -104,7 +113,7 @@ void kivi_ref_quant_group(const uint16_t* x, ptrdiff_t stride, int32_t n,
     if (mn == 0.0f) mn = 0.0f;             /* canonical +0 zero point */
     if (mx == 0.0f) mx = 0.0f;             /* so a zero range, hence a zero scale, is +0 */
     float range = mx - mn;
-    float s32 = range / 3.0f;
+    float s32 = range / top;
     uint16_t s16 = kivi_ref_f32_to_f16(s32);
     float s = kivi_ref_f16_to_f32(s16);
     *scale = s16;
@@ -115,7 +124,7 @@ void kivi_ref_quant_group(const uint16_t* x, ptrdiff_t stride, int32_t n,
         float d = v - mn;
         float t = d / s;
         float r = rne_float(t);
-        if (r > 3.0f) r = 3.0f;
+        if (r > top) r = top;
         codes[i] = (uint8_t)r;
     }
 }
@@ -148,28 +157,36 @@ static int64_t value_code_byte(int32_t t, int32_t j) {
 }
 static int value_code_shift(int32_t t) { return 2 * (t % 4); }
 
-static int64_t code_byte(int key, int32_t t, int32_t j) {
+/* 4-bit codes, keys and values alike: token-major, head_dim/2 bytes per token; channel j
+ * of token t in byte j/2, the even channel in the low nibble. */
+static int bits_of(const kivi_ref_cache* c) { return c->bits == 4 ? 4 : 2; }
+
+static int64_t code_byte(const kivi_ref_cache* c, int key, int32_t t, int32_t j) {
+    if (bits_of(c) == 4) return (int64_t)t * (c->head_dim / 2) + j / 2;
     return key ? key_code_byte(t, j) : value_code_byte(t, j);
 }
-static int code_shift(int key, int32_t t, int32_t j) {
+static int code_shift(const kivi_ref_cache* c, int key, int32_t t, int32_t j) {
+    if (bits_of(c) == 4) return 4 * (j % 2);
     return key ? key_code_shift(j) : value_code_shift(t);
 }
 
-static void put_code(uint8_t* codes_row, int key, int32_t t, int32_t j, uint8_t code) {
-    uint8_t* byte = codes_row + code_byte(key, t, j);
-    int sh = code_shift(key, t, j);
-    *byte = (uint8_t)((*byte & ~(3u << sh)) | ((unsigned)code << sh));
+static void put_code(const kivi_ref_cache* c, uint8_t* codes_row, int key, int32_t t, int32_t j, uint8_t code) {
+    uint8_t* byte = codes_row + code_byte(c, key, t, j);
+    int sh = code_shift(c, key, t, j);
+    unsigned mask = (1u << bits_of(c)) - 1u;
+    *byte = (uint8_t)((*byte & ~(mask << sh)) | ((unsigned)code << sh));
 }
 
-static uint8_t get_code(const uint8_t* codes_row, int key, int32_t t, int32_t j) {
-    return (uint8_t)((codes_row[code_byte(key, t, j)] >> code_shift(key, t, j)) & 3u);
+static uint8_t get_code(const kivi_ref_cache* c, const uint8_t* codes_row, int key, int32_t t, int32_t j) {
+    unsigned mask = (1u << bits_of(c)) - 1u;
+    return (uint8_t)((codes_row[code_byte(c, key, t, j)] >> code_shift(c, key, t, j)) & mask);
 }
 
 static uint8_t* k_codes_row(const kivi_ref_cache* c, int64_t row) {
-    return c->k_codes + row * c->token_cap * (c->head_dim / 4);
+    return c->k_codes + row * c->token_cap * (c->head_dim * bits_of(c) / 8);
 }
 static uint8_t* v_codes_row(const kivi_ref_cache* c, int64_t row) {
-    return c->v_codes + row * c->token_cap * (c->head_dim / 4);
+    return c->v_codes + row * c->token_cap * (c->head_dim * bits_of(c) / 8);
 }
 /* (scale, zero) of key token group g, channel j */
 static uint16_t* k_pair(const kivi_ref_cache* c, int64_t row, int32_t g, int32_t j) {
@@ -202,9 +219,9 @@ void kivi_ref_quantize_k(kivi_ref_cache* c, const uint16_t* src, int32_t tokens,
             int32_t cg = (dst_off + t0) / G;          /* destination token group */
             for (int32_t j = 0; j < d; ++j) {
                 uint16_t* pr = k_pair(c, row, cg, j);
-                kivi_ref_quant_group(s_row + (int64_t)t0 * d + j, d, G, &pr[0], &pr[1], codes);
+                kivi_ref_quant_group_bits(s_row + (int64_t)t0 * d + j, d, G, bits_of(c), &pr[0], &pr[1], codes);
                 for (int32_t i = 0; i < G; ++i)
-                    put_code(k_codes_row(c, row), 1, dst_off + t0 + i, j, codes[i]);
+                    put_code(c, k_codes_row(c, row), 1, dst_off + t0 + i, j, codes[i]);
             }
         }
     }
@@ -221,9 +238,9 @@ void kivi_ref_quantize_v(kivi_ref_cache* c, const uint16_t* src, int32_t tokens,
         for (int32_t t = 0; t < tokens; ++t) {
             for (int32_t k = 0; k < d / G; ++k) {
                 uint16_t* pr = v_pair(c, row, dst_off + t, k);
-                kivi_ref_quant_group(s_row + (int64_t)t * d + k * G, 1, G, &pr[0], &pr[1], codes);
+                kivi_ref_quant_group_bits(s_row + (int64_t)t * d + k * G, 1, G, bits_of(c), &pr[0], &pr[1], codes);
                 for (int32_t i = 0; i < G; ++i)
-                    put_code(v_codes_row(c, row), 0, dst_off + t, k * G + i, codes[i]);
+                    put_code(c, v_codes_row(c, row), 0, dst_off + t, k * G + i, codes[i]);
             }
         }
     }
@@ -307,8 +324,8 @@ void kivi_ref_dequant_row(const kivi_ref_cache* c, int32_t row, double* K, doubl
         for (int32_t j = 0; j < d; ++j) {
             const uint16_t* kp = k_pair(c, row, t / G, j);
             const uint16_t* vp = v_pair(c, row, t, j / G);
-            double kc = get_code(k_codes_row(c, row), 1, t, j);
-            double vc = get_code(v_codes_row(c, row), 0, t, j);
+            double kc = get_code(c, k_codes_row(c, row), 1, t, j);
+            double vc = get_code(c, v_codes_row(c, row), 0, t, j);
             K[(int64_t)t * d + j] = (double)kivi_ref_f16_to_f32(kp[1]) + kc * (double)kivi_ref_f16_to_f32(kp[0]);
             V[(int64_t)t * d + j] = (double)kivi_ref_f16_to_f32(vp[1]) + vc * (double)kivi_ref_f16_to_f32(vp[0]);
         }

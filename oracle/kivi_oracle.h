@@ -40,9 +40,14 @@ void     kivi_ref_f32_to_f16_array(const float* x, uint16_t* out, size_t n);
  * codes[i] receives the code of x[i*stride] (one code per byte, unpacked). */
 void kivi_ref_quant_group(const uint16_t* x, ptrdiff_t stride, int32_t n,
                           uint16_t* scale, uint16_t* zero, uint8_t* codes);
+/* The same quantizer with 2^bits levels (bits = 2 or 4): scale = (max - min)/(2^bits - 1),
+ * codes clamped to 2^bits - 1. */
+void kivi_ref_quant_group_bits(const uint16_t* x, ptrdiff_t stride, int32_t n, int32_t bits,
+                               uint16_t* scale, uint16_t* zero, uint8_t* codes);
 
 /* ---- the cache (host memory, same documented layout as the device cache) ----
- * row = b*kv_heads + h.
+ * row = b*kv_heads + h.  With bits = 4, k_codes and v_codes are [row][token_cap][head_dim/2]
+ * bytes instead (channel j of token t in byte j/2, the even channel in the low nibble).
  *   k_codes, v_codes : [row][token_cap/32][1024] bytes, one 1024-byte tile per 32-token
  *                      group (head_dim 128).
  *                      k_codes: a little-endian 32-bit word holds channels 16w..16w+15 of
@@ -62,6 +67,7 @@ typedef struct kivi_ref_cache {
     int32_t batch, kv_heads, head_dim, group, residual_cap, token_cap;
     int32_t n_quant, n_res, res_head;
     int32_t flush_all;   /* flush policy: 0 = the oldest group of a full residual, 1 = all of it */
+    int32_t bits;        /* code width: 2 (default; 0 reads as 2) or 4 */
     uint8_t *k_codes, *v_codes;
     uint16_t *k_sz, *v_sz;
     uint16_t *k_res, *v_res;

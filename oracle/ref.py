@@ -31,6 +31,7 @@ def lib():
         L.kivi_ref_f16_to_f32.restype = f32
         L.kivi_ref_f32_to_f16_array.argtypes = [p, p, C.c_size_t]
         L.kivi_ref_quant_group.argtypes = [p, C.c_ssize_t, i32, p, p, p]
+        L.kivi_ref_quant_group_bits.argtypes = [p, C.c_ssize_t, i32, i32, p, p, p]
         L.kivi_ref_quantize_k.argtypes = [p, p, i32, i64, i32]
         L.kivi_ref_quantize_v.argtypes = [p, p, i32, i64, i32]
         L.kivi_ref_prefill.argtypes = [p, p, p, i32, i64, i32]
@@ -67,12 +68,15 @@ def f16_to_f32_scalar(h):
 
 
 # ---------------------------------------------------------- quantizer ---------
-def quant_group(x_bits):
-    """One group of fp16 bit patterns -> (scale bits, zero bits, codes[n])."""
+def quant_group(x_bits, bits=2):
+    """One group of fp16 bit patterns -> (scale bits, zero bits, codes[n]); 2^bits levels."""
     x = _c(x_bits, np.uint16).ravel()
     s, z = C.c_uint16(), C.c_uint16()
     codes = np.zeros(x.size, np.uint8)
-    lib().kivi_ref_quant_group(_ptr(x), 1, x.size, C.byref(s), C.byref(z), _ptr(codes))
+    if bits == 2:
+        lib().kivi_ref_quant_group(_ptr(x), 1, x.size, C.byref(s), C.byref(z), _ptr(codes))
+    else:
+        lib().kivi_ref_quant_group_bits(_ptr(x), 1, x.size, bits, C.byref(s), C.byref(z), _ptr(codes))
     return s.value, z.value, codes
 
 
@@ -82,6 +86,7 @@ class _CacheStruct(C.Structure):
         ("batch", C.c_int32), ("kv_heads", C.c_int32), ("head_dim", C.c_int32),
         ("group", C.c_int32), ("residual_cap", C.c_int32), ("token_cap", C.c_int32),
         ("n_quant", C.c_int32), ("n_res", C.c_int32), ("res_head", C.c_int32), ("flush_all", C.c_int32),
+        ("bits", C.c_int32),
         ("k_codes", C.c_void_p), ("v_codes", C.c_void_p),
         ("k_sz", C.c_void_p), ("v_sz", C.c_void_p),
         ("k_res", C.c_void_p), ("v_res", C.c_void_p),
@@ -91,18 +96,24 @@ class _CacheStruct(C.Structure):
 class RefCache:
     """Host-memory cache in the documented packed layout, driven by the C oracle."""
 
-    def __init__(self, batch, kv_heads, head_dim=128, group=32, residual_cap=128, token_cap=0, flush_all=False):
+    def __init__(self, batch, kv_heads, head_dim=128, group=32, residual_cap=128, token_cap=0, flush_all=False,
+                 bits=2):
         rows = batch * kv_heads
         self.batch, self.kv_heads, self.head_dim = batch, kv_heads, head_dim
         self.group, self.residual_cap, self.token_cap = group, residual_cap, token_cap
-        tiles = token_cap // 32                    # one 1024-byte tile of codes per 32 tokens
-        self.k_codes = np.zeros((rows, tiles, 32 * head_dim // 4), np.uint8)
-        self.v_codes = np.zeros((rows, tiles, 32 * head_dim // 4), np.uint8)
+        self.bits = bits
+        if bits == 4:                              # token-major, two codes per byte
+            self.k_codes = np.zeros((rows, token_cap, head_dim // 2), np.uint8)
+            self.v_codes = np.zeros((rows, token_cap, head_dim // 2), np.uint8)
+        else:                                      # one 1024-byte tile of codes per 32 tokens
+            tiles = token_cap // 32
+            self.k_codes = np.zeros((rows, tiles, 32 * head_dim // 4), np.uint8)
+            self.v_codes = np.zeros((rows, tiles, 32 * head_dim // 4), np.uint8)
         self.k_sz = np.zeros((rows, token_cap // group, head_dim, 2), np.uint16)
         self.v_sz = np.zeros((rows, token_cap, head_dim // group, 2), np.uint16)
         self.k_res = np.zeros((rows, residual_cap, head_dim), np.uint16)
         self.v_res = np.zeros((rows, residual_cap, head_dim), np.uint16)
-        self.s = _CacheStruct(batch, kv_heads, head_dim, group, residual_cap, token_cap, 0, 0, 0, int(flush_all),
+        self.s = _CacheStruct(batch, kv_heads, head_dim, group, residual_cap, token_cap, 0, 0, 0, int(flush_all), bits,
                               self.k_codes.ctypes.data, self.v_codes.ctypes.data,
                               self.k_sz.ctypes.data, self.v_sz.ctypes.data,
                               self.k_res.ctypes.data, self.v_res.ctypes.data)
