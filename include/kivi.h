@@ -68,6 +68,9 @@ enum {
  *                        tile covers its tokens 8k..8k+7, and the chunk's byte 4p + 2h + e
  *                        holds channel n + 16(2p + e) for tokens 8k+4h..8k+4h+3 (k = 0..3,
  *                        n = 0..15, p = 0..3, h and e = 0..1).
+ *   (KIVI_CODES_4BIT)  k_codes, v_codes : uint8 [row][token_cap][D/2] instead: a token's
+ *                      codes in D/2 bytes, channel j in byte j/2, the even channel in the
+ *                      low nibble.
  *   k_sz             : fp16   [row][token_cap/G][D][2]  (scale, zero) of key token group
  *                      g (tokens Gg..Gg+G-1), channel j -- keys are quantized per-channel
  *                      over G tokens.
@@ -88,6 +91,10 @@ enum {
  * the other reading of the residual length of the pages' ablation (summary page, "Key
  * points"): the full-precision buffer fills up to R and is then quantized as a whole. */
 #define KIVI_FLUSH_ALL 1
+/* Code width (kivi_cache.flags).  Default (0): 2-bit codes, four levels (KIVI-2, the
+ * summary page's and the record's scheme).  KIVI_CODES_4BIT: 4-bit codes, sixteen levels
+ * with the same rules (scale = (max - min)/15, codes clamped at 15), in the layout below. */
+#define KIVI_CODES_4BIT 2
 
 typedef struct kivi_cache {
     int32_t batch, kv_heads, head_dim;
@@ -95,7 +102,7 @@ typedef struct kivi_cache {
     int32_t residual_cap;    /* R, a multiple of G */
     int32_t token_cap;       /* capacity of the quantized history in tokens, multiple of G */
     int32_t n_quant, n_res, res_head;
-    int32_t flags;           /* 0, or KIVI_FLUSH_ALL */
+    int32_t flags;           /* 0, or KIVI_FLUSH_ALL and/or KIVI_CODES_4BIT */
     uint8_t* k_codes;
     uint8_t* v_codes;
     uint16_t* k_sz;

@@ -27,7 +27,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 int check_shape(const kivi_cache* c) {
     if (c == nullptr) return KIVI_ERR_NULL;
     if (c->batch <= 0 || c->kv_heads <= 0 || c->head_dim <= 0 || c->group <= 0 ||
-        c->residual_cap <= 0 || c->token_cap < 0 || (c->flags & ~KIVI_FLUSH_ALL) != 0)
+        c->residual_cap <= 0 || c->token_cap < 0 || (c->flags & ~(KIVI_FLUSH_ALL | KIVI_CODES_4BIT)) != 0)
         return KIVI_ERR_SHAPE;
     if (c->head_dim % 4 != 0 || c->head_dim % c->group != 0 || c->residual_cap % c->group != 0 ||
         c->token_cap % c->group != 0)
@@ -64,7 +64,12 @@ int hip_status(hipError_t e) { return e == hipSuccess ? KIVI_OK : KIVI_ERR_HIP; 
 
 // Query heads one workgroup takes: a KV head's query group (or an equal share of it) goes
 // to one workgroup, which streams the KV head's cache once for all of them.
-int32_t queries_per_block(int32_t ratio) {
+int32_t code_bits(const kivi_cache* c) { return (c->flags & KIVI_CODES_4BIT) ? 4 : 2; }
+
+// query heads per workgroup for a GQA ratio (the 4-bit kernel keeps at most two heads' state
+// in registers)
+int32_t queries_per_block(int32_t ratio, int32_t bits = 2) {
+    if (bits == 4) return ratio % 2 == 0 ? 2 : 1;
     if (ratio % 4 == 0) return 4;
     if (ratio % 3 == 0) return 3;
     if (ratio % 2 == 0) return 2;
@@ -74,17 +79,22 @@ int32_t queries_per_block(int32_t ratio) {
 // workgroup rows of the attention grid
 int64_t block_rows(const kivi_cache* c, int32_t q_heads) {
     const int32_t ratio = q_heads / c->kv_heads;
-    const int32_t nq = queries_per_block(ratio);
+    const int32_t nq = queries_per_block(ratio, code_bits(c));
     return nq > 1 ? (int64_t)c->batch * c->kv_heads * (ratio / nq) : (int64_t)c->batch * q_heads;
 }
 
 // Split count for a context of `groups` key groups.
 int32_t auto_splits_for(const kivi_cache* c, int32_t q_heads, int64_t groups) {
     const int64_t rows = block_rows(c, q_heads);
-    const bool group = queries_per_block(q_heads / c->kv_heads) > 1;
-    const int64_t target = group ? kTargetBlocksGroup : kTargetBlocksSingle;
+    const bool group = queries_per_block(q_heads / c->kv_heads, code_bits(c)) > 1;
+    int64_t target = group ? kTargetBlocksGroup : kTargetBlocksSingle;
+    int64_t min_tiles = group ? kMinGroupsPerSplit : kMinGroupsPerSplitSingle;
+    if (code_bits(c) == 4) {   // 4-wave workgroups, a key group for every wave
+        target = group ? kTargetBlocksGroup : kTargetBlocks;
+        min_tiles = 4 * (c->group / kG);
+    }
     int64_t s = (target + rows - 1) / rows;
-    const int64_t cap = groups / (group ? kMinGroupsPerSplit : kMinGroupsPerSplitSingle);
+    const int64_t cap = groups / min_tiles;
     if (s > cap) s = cap;
     if (s < 1) s = 1;
     if (s > kMaxSplits) s = kMaxSplits;
@@ -97,8 +107,9 @@ int32_t auto_splits(const kivi_cache* c, int32_t q_heads) { return auto_splits_f
 int32_t ragged_auto_splits(const kivi_cache* c, int32_t q_heads) {
     const int64_t groups = c->token_cap / kG;
     int64_t s = 4 * (int64_t)auto_splits_for(c, q_heads, groups);
-    const bool group = queries_per_block(q_heads / c->kv_heads) > 1;
-    const int64_t cap = groups / (group ? kMinGroupsPerSplit : kMinGroupsPerSplitSingle);
+    const bool group = queries_per_block(q_heads / c->kv_heads, code_bits(c)) > 1;
+    const int64_t min_tiles = code_bits(c) == 4 ? 4 * (c->group / kG) : (group ? kMinGroupsPerSplit : kMinGroupsPerSplitSingle);
+    const int64_t cap = groups / min_tiles;
     if (s > cap) s = cap;
     if (s < 1) s = 1;
     if (s > kMaxSplits) s = kMaxSplits;
@@ -125,6 +136,7 @@ QuantArgs quant_args(const kivi_cache* c, const uint16_t* src, int32_t tokens, i
     a.k_sz = c->k_sz;
     a.v_sz = c->v_sz;
     a.group = c->group;
+    a.bits = code_bits(c);
     return a;
 }
 
@@ -167,6 +179,7 @@ int prepare_append(const kivi_cache* c, const uint16_t* k_new, const uint16_t* v
     a->kv_heads = c->kv_heads;
     a->group = G;
     a->flush_all = (c->flags & KIVI_FLUSH_ALL) ? 1 : 0;
+    a->bits = code_bits(c);
     *next = *c;
     next->n_quant = n_quant;
     next->n_res = n_res + 1;
@@ -232,7 +245,7 @@ int prepare_attn(const kivi_cache* c, const uint16_t* q, int32_t q_heads, float 
     const int32_t res_groups = (c->n_res * 512 + 96 * kG - 1) / (96 * kG);
     a.groups_per_split = (groups + res_groups + splits - 1) / splits;
     a.q_rows = (int64_t)c->batch * q_heads;
-    a.nq = queries_per_block(a.ratio);
+    a.nq = queries_per_block(a.ratio, code_bits(c));
     a.block_rows = block_rows(c, q_heads);
     a.k_new = a.v_new = nullptr;
     a.k_ring = a.v_ring = nullptr;
@@ -240,8 +253,9 @@ int prepare_attn(const kivi_cache* c, const uint16_t* q, int32_t q_heads, float 
     a.seq_state = seq_state;
     // workgroups resident at once: three 4-wave query-group workgroups or one 12-wave
     // single-query workgroup per CU
-    a.slot_budget = (int32_t)(a.nq > 1 ? kTargetBlocks : kTargetBlocksSingle);
+    a.slot_budget = (int32_t)(a.nq > 1 || code_bits(c) == 4 ? kTargetBlocks : kTargetBlocksSingle);
     a.group = c->group;
+    a.bits = code_bits(c);
     *pa = a;
     return KIVI_OK;
 }
@@ -308,7 +322,7 @@ int kivi_cache_bytes(const kivi_cache* shape, size_t* codes, size_t* pairs, size
     if (codes == nullptr || pairs == nullptr || residual == nullptr) return KIVI_ERR_NULL;
     const int64_t rows = rows_of(shape), D = shape->head_dim, G = shape->group;
     const int64_t T = shape->token_cap, R = shape->residual_cap;
-    *codes = (size_t)(2 * rows * T * (D / 4));
+    *codes = (size_t)(2 * rows * T * (D * code_bits(shape) / 8));
     *pairs = (size_t)(rows * (T / G) * D * 4 + rows * T * (D / G) * 4);
     *residual = (size_t)(2 * rows * R * D * 2);
     return KIVI_OK;
@@ -421,6 +435,7 @@ int kivi_append_flush_ragged(const kivi_cache* c, int32_t* seq_state, const uint
     a.kv_heads = c->kv_heads;
     a.group = c->group;
     a.flush_all = (c->flags & KIVI_FLUSH_ALL) ? 1 : 0;
+    a.bits = code_bits(c);
     return hip_status(launch_append_flush_ragged(a, c->batch, (hipStream_t)stream));
 }
 

@@ -340,6 +340,7 @@ __global__ __launch_bounds__(kSqBlock) void attn_split_kernel(AttnArgs a) {
 }
 
 hipError_t launch_decode_attn(const AttnArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+    if (a.bits == 4) return launch_decode_attn_q4(a, s, t0, t1);
     if (a.nq > 1) return launch_decode_attn_gqa(a, s, t0, t1);
     KIVI_BY_GROUP(a.group, hipExtLaunchKernelGGL(attn_split_kernel<GS>, attn_grid(a, a.q_rows), dim3(kSqBlock), 0, s,
                                                  t0, t1, 0, a))

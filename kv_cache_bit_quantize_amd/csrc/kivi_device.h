@@ -22,7 +22,8 @@ __host__ __device__ constexpr bool group_supported(int g) { return g == 32 || g 
         default: return hipErrorInvalidValue;   \
     }
 
-constexpr int kRowBytes = kD / 4;   // packed code bytes per token
+constexpr int kRowBytes = kD / 4;   // packed code bytes per token (2-bit codes)
+constexpr int kRowBytes4 = kD / 2;  // 4-bit codes: token-major, channel j in byte j/2 (even channel low)
 constexpr int kBlock = 256;         // threads per workgroup (4 wave64)
 
 // Packed code layout (include/kivi.h).  A row holds one 1024-byte tile per 32-token group.
@@ -69,7 +70,8 @@ __device__ __forceinline__ uint32_t f2h(float f) {   // v_cvt_f16_f32: RNE, subn
 // ---------------------------------------------------------------------------------
 // Asymmetric 2-bit group quantizer (KIVI title, "asymmetric 2bit"; record "Methodology").
 // zero = min, scale = fp16(fp32(max - min) / 3), both with signed zeros read as +0;
-// code = clamp(rne(fp32(x - min) / scale), 0, 3), 0 when the stored scale is 0.
+// code = clamp(rne(fp32(x - min) / scale), 0, 3), 0 when the stored scale is 0.  The 4-bit
+// member of the family divides by 15 and clamps at 15.
 // Every operation is one IEEE binary32 operation: no contraction, true division.
 // ---------------------------------------------------------------------------------
 struct GroupQ {
@@ -78,13 +80,15 @@ struct GroupQ {
     uint32_t pair;  // fp16 scale in bits 0..15, fp16 zero in bits 16..31 (memory order)
 };
 
+// TOP: the highest code, 3 for 2-bit codes, 15 for 4-bit codes (the same rules otherwise)
+template <int TOP = 3>
 __device__ __forceinline__ GroupQ group_params(float mn, float mx) {
 #pragma clang fp contract(off)
     GroupQ q;
     mn = mn + 0.0f;                 // -0 + +0 = +0 under round-to-nearest
     mx = mx + 0.0f;
     float range = mx - mn;
-    float s32 = range / 3.0f;
+    float s32 = range / (float)TOP;
     uint32_t sh = f2h(s32);
     q.mn = mn;
     q.s = h2f(sh);
@@ -92,13 +96,14 @@ __device__ __forceinline__ GroupQ group_params(float mn, float mx) {
     return q;
 }
 
+template <int TOP = 3>
 __device__ __forceinline__ uint32_t code_of(float x, const GroupQ& q) {
 #pragma clang fp contract(off)
     if (q.s == 0.0f) return 0u;
     float d = x - q.mn;
     float t = d / q.s;
     float r = __builtin_rintf(t);   // v_rndne_f32: ties to even
-    r = __builtin_fminf(r, 3.0f);
+    r = __builtin_fminf(r, (float)TOP);
     return (uint32_t)r;
 }
 

@@ -11,6 +11,7 @@ constexpr int kSqWaves = 12;       // waves of a single-query attention workgrou
 
 struct QuantArgs {          // kivi_quantize_{k,v}
     int32_t group;              // tokens per key group / channels per value group
+    int32_t bits;               // code width: 2 or 4
     const uint16_t* src;
     int64_t src_row_stride;
     int64_t rows;
@@ -52,6 +53,7 @@ struct AppendArgs {
     int32_t kv_heads;
     int32_t group;              // tokens per key group (= channels per value group): 32, 64 or 128
     int32_t flush_all;          // a flush moves the whole residual (else its oldest group)
+    int32_t bits;               // code width: 2 or 4
 };
 
 struct AttnArgs {
@@ -94,6 +96,7 @@ struct AttnArgs {
     int32_t* seq_state;
     int32_t slot_budget;        // ragged batch: workgroups resident at once (the plan's target)
     int32_t group;              // tokens per key group (= channels per value group): 32, 64 or 128
+    int32_t bits;               // code width: 2 or 4
 };
 
 // bits of a sequence's flags word (ragged calls; only ever set, by the kernels)
@@ -111,6 +114,8 @@ hipError_t launch_append_flush_ragged(const AppendArgs& a, int32_t batch, hipStr
 hipError_t launch_decode_attn(const AttnArgs& a, hipStream_t s, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 hipError_t launch_decode_attn_gqa(const AttnArgs& a, hipStream_t s, hipEvent_t t0 = nullptr,
                                   hipEvent_t t1 = nullptr);
+hipError_t launch_decode_attn_q4(const AttnArgs& a, hipStream_t s, hipEvent_t t0 = nullptr,
+                                 hipEvent_t t1 = nullptr);
 hipError_t launch_decode_attn_fp16(const AttnArgs& a, hipStream_t s, hipEvent_t t0 = nullptr,
                                    hipEvent_t t1 = nullptr);
 

@@ -128,6 +128,98 @@ __device__ void quant_v_tile(const uint16_t* __restrict__ src_lo, int64_t src_to
     __syncthreads();   // sh_codes may be reused by the caller
 }
 
+// ---- 4-bit codes (the scheme's 4-bit member: sixteen levels).  Token-major: a token's 128
+// codes in 64 bytes, channel j in byte j/2, the even channel in the low nibble.
+
+// One key token group of GS tokens held in LDS as fp16 [GS][128] -> its GS token rows of
+// codes (from codes_dst, 64 bytes each) + 128 pairs.  All 256 threads.
+template <int GS>
+__device__ void quant_k4_group(const uint16_t* __restrict__ tile, float* sh_mn, float* sh_s,
+                               uint8_t* __restrict__ codes_dst, uint32_t* __restrict__ pairs_dst) {
+    const int tid = threadIdx.x;
+    if (tid < kD) {
+        float mn = h2f(tile[tid]), mx = mn;
+#pragma unroll 8
+        for (int t = 1; t < GS; ++t) {
+            const float v = h2f(tile[t * kD + tid]);
+            mn = __builtin_fminf(mn, v);
+            mx = __builtin_fmaxf(mx, v);
+        }
+        const GroupQ q = group_params<15>(mn, mx);
+        pairs_dst[tid] = q.pair;
+        sh_mn[tid] = q.mn;
+        sh_s[tid] = q.s;
+    }
+    __syncthreads();
+    // item -> (token t, 16-channel chunk w): 8 bytes of codes, channel 16w + c at bit 4c
+    for (int i = tid; i < GS * 8; i += kBlock) {
+        const int t = i >> 3, w = i & 7;
+        const uint4* src = reinterpret_cast<const uint4*>(tile + t * kD + w * 16);
+        const uint4 a = src[0], b = src[1];
+        const uint32_t h[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            const int j = w * 16 + c;
+            const GroupQ q{sh_mn[j], sh_s[j], 0u};
+            const uint32_t code = code_of<15>(h2f((c & 1) ? (h[c >> 1] >> 16) : (h[c >> 1] & 0xffffu)), q);
+            if (c < 8) lo |= code << (4 * c);
+            else hi |= code << (4 * (c - 8));
+        }
+        *reinterpret_cast<uint2*>(codes_dst + (int64_t)t * kRowBytes4 + w * 8) = make_uint2(lo, hi);
+    }
+    __syncthreads();   // the LDS tile and sh_mn / sh_s may be reused by the caller
+}
+
+// Value tokens [0, n) from src (token t at src + t*src_tok_stride, 128 fp16 channels) ->
+// 4-bit codes (token rows of 64 bytes from codes_dst) and (scale, zero) words (pairs_dst:
+// the word of token 0, group 0).  All 256 threads: four per token (32 channels each), 64
+// tokens a pass; a group of GS channels is reduced over its GS/32 adjacent lanes.
+template <int GS>
+__device__ void quant_v4_tokens(const uint16_t* __restrict__ src, int64_t src_tok_stride, int n,
+                                uint8_t* __restrict__ codes_dst, uint32_t* __restrict__ pairs_dst) {
+    const int tid = threadIdx.x, qd = tid & 3;
+    for (int base = 0; base < n; base += kBlock / 4) {
+        const int t = base + (tid >> 2);
+        const bool live = t < n;
+        float v[32];
+        const uint4* p = reinterpret_cast<const uint4*>(src + (int64_t)(live ? t : 0) * src_tok_stride + qd * 32);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint4 x = p[i];
+            const uint32_t h[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                v[8 * i + 2 * k] = h2f(h[k] & 0xffffu);
+                v[8 * i + 2 * k + 1] = h2f(h[k] >> 16);
+            }
+        }
+        float mn = v[0], mx = v[0];
+#pragma unroll
+        for (int i = 1; i < 32; ++i) {
+            mn = __builtin_fminf(mn, v[i]);
+            mx = __builtin_fmaxf(mx, v[i]);
+        }
+#pragma unroll
+        for (int m = 1; m < GS / 32; m <<= 1) {
+            mn = __builtin_fminf(mn, __shfl_xor(mn, m, 64));
+            mx = __builtin_fmaxf(mx, __shfl_xor(mx, m, 64));
+        }
+        const GroupQ q = group_params<15>(mn, mx);
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            w[i] = 0;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) w[i] |= code_of<15>(v[8 * i + c], q) << (4 * c);
+        }
+        if (live) {
+            *reinterpret_cast<uint4*>(codes_dst + (int64_t)t * kRowBytes4 + qd * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+            if (qd % (GS / 32) == 0) pairs_dst[value_pair_index<GS>(t, qd / (GS / 32))] = q.pair;
+        }
+    }
+}
+
 // ------------------------------------------------------------------ kernels ------
 
 // grid.x = rows * (tokens / GS); one key token group per workgroup.
@@ -166,6 +258,36 @@ __global__ __launch_bounds__(kBlock) void quantize_v_kernel(QuantArgs a) {
                      reinterpret_cast<uint32_t*>(a.v_sz) + value_pair_index<GS>(row * a.token_cap + t0, 0));
 }
 
+// 4-bit codes: grid.x = rows * (tokens / GS); one key token group per workgroup.
+template <int GS>
+__global__ __launch_bounds__(kBlock) void quantize_k4_kernel(QuantArgs a) {
+    __shared__ uint4 tile4[GS * kD / 8];
+    __shared__ float sh_mn[kD], sh_s[kD];
+    const int groups = a.tokens / GS;
+    const int64_t row = blockIdx.x / groups;
+    const int g = blockIdx.x % groups;
+    const uint4* s4 = reinterpret_cast<const uint4*>(a.src + row * a.src_row_stride + (int64_t)g * GS * kD);
+#pragma unroll
+    for (int i = threadIdx.x; i < GS * kD / 8; i += kBlock) tile4[i] = s4[i];
+    __syncthreads();
+    const int dst_tok = a.dst_token_off + g * GS;
+    quant_k4_group<GS>(reinterpret_cast<const uint16_t*>(tile4), sh_mn, sh_s,
+                       a.k_codes + (row * a.token_cap + dst_tok) * kRowBytes4,
+                       reinterpret_cast<uint32_t*>(a.k_sz) + (row * (a.token_cap / GS) + dst_tok / GS) * kD);
+}
+
+// 4-bit codes: grid.x = rows * ceil(tokens / 64); 64 value tokens per workgroup.
+template <int GS>
+__global__ __launch_bounds__(kBlock) void quantize_v4_kernel(QuantArgs a) {
+    const int per_row = (a.tokens + 63) / 64;
+    const int64_t row = blockIdx.x / per_row;
+    const int base = (int)(blockIdx.x % per_row) * 64;
+    const int n = min(64, a.tokens - base);
+    const int64_t dst = row * a.token_cap + a.dst_token_off + base;
+    quant_v4_tokens<GS>(a.src + row * a.src_row_stride + (int64_t)base * kD, kD, n, a.v_codes + dst * kRowBytes4,
+                        reinterpret_cast<uint32_t*>(a.v_sz) + value_pair_index<GS>(dst, 0));
+}
+
 // grid.x = ceil(rows * n * 16 / 256): copy tokens [first, first+n) of each row into ring
 // slots 0..n-1, keys and values.
 __global__ __launch_bounds__(kBlock) void residual_load_kernel(ResidualArgs a) {
@@ -187,7 +309,7 @@ __global__ __launch_bounds__(kBlock) void residual_load_kernel(ResidualArgs a) {
 // batch each row takes these from its sequence's state (flush when its ring is full); a
 // sequence whose state is out of range, or whose flush would pass token_cap, is skipped and
 // flagged.
-template <int GS>
+template <int GS, int BITS>
 __global__ __launch_bounds__(kBlock) void append_flush_kernel(AppendArgs a) {
     __shared__ uint4 tile4[GS * kD / 8];
     __shared__ float sh_mn[kD], sh_s[kD];
@@ -224,17 +346,25 @@ __global__ __launch_bounds__(kBlock) void append_flush_kernel(AppendArgs a) {
         for (int i = tid; i < GS * kD / 8; i += kBlock) tile4[i] = kr[i];
         __syncthreads();
         const int dst_tok = group * GS;
-        uint8_t* kc = a.k_codes + row * a.token_cap * kRowBytes + (int64_t)(dst_tok / kG) * kTileBytes;
         uint32_t* kp = reinterpret_cast<uint32_t*>(a.k_sz) + (row * (a.token_cap / GS) + group) * kD;
-        quant_k_group<GS>(reinterpret_cast<const uint16_t*>(tile4), sh_mn, sh_s, kc, kp);
-        // values: the same GS ring tokens as GS/32 value tiles
-        __shared__ __align__(16) uint8_t sh_codes[kG][kD];
+        if constexpr (BITS == 4) {
+            quant_k4_group<GS>(reinterpret_cast<const uint16_t*>(tile4), sh_mn, sh_s,
+                               a.k_codes + (row * a.token_cap + dst_tok) * kRowBytes4, kp);
+            quant_v4_tokens<GS>(a.v_res + (row * a.residual_cap + slot) * kD, kD, GS,
+                                a.v_codes + (row * a.token_cap + dst_tok) * kRowBytes4,
+                                reinterpret_cast<uint32_t*>(a.v_sz) + value_pair_index<GS>(row * a.token_cap + dst_tok, 0));
+        } else {
+            uint8_t* kc = a.k_codes + row * a.token_cap * kRowBytes + (int64_t)(dst_tok / kG) * kTileBytes;
+            quant_k_group<GS>(reinterpret_cast<const uint16_t*>(tile4), sh_mn, sh_s, kc, kp);
+            // values: the same GS ring tokens as GS/32 value tiles
+            __shared__ __align__(16) uint8_t sh_codes[kG][kD];
 #pragma unroll 1
-        for (int tl = 0; tl < GS / kG; ++tl)
-            quant_v_tile<GS>(a.v_res + (row * a.residual_cap + slot + tl * kG) * kD, kD, 0, kG, sh_codes,
-                             a.v_codes + (row * a.token_cap + dst_tok + tl * kG) * kRowBytes,
-                             reinterpret_cast<uint32_t*>(a.v_sz) +
-                                 value_pair_index<GS>(row * a.token_cap + dst_tok + tl * kG, 0));
+            for (int tl = 0; tl < GS / kG; ++tl)
+                quant_v_tile<GS>(a.v_res + (row * a.residual_cap + slot + tl * kG) * kD, kD, 0, kG, sh_codes,
+                                 a.v_codes + (row * a.token_cap + dst_tok + tl * kG) * kRowBytes,
+                                 reinterpret_cast<uint32_t*>(a.v_sz) +
+                                     value_pair_index<GS>(row * a.token_cap + dst_tok + tl * kG, 0));
+        }
         __syncthreads();   // every read of the flushed slots is done before the overwrite
     }
     // The new token goes to the first flushed group's first slot (or anywhere in the ring
@@ -268,12 +398,21 @@ __global__ __launch_bounds__(64) void seq_state_update_kernel(AppendArgs a, int3
 hipError_t launch_quantize_k(const QuantArgs& a, hipStream_t s) {
     const int64_t blocks = a.rows * (int64_t)(a.tokens / a.group);
     if (blocks == 0) return hipSuccess;
-    KIVI_BY_GROUP(a.group, hipLaunchKernelGGL(quantize_k_kernel<GS>, dim3((unsigned)blocks), dim3(kBlock), 0, s, a))
+    if (a.bits == 4) {
+        KIVI_BY_GROUP(a.group, hipLaunchKernelGGL(quantize_k4_kernel<GS>, dim3((unsigned)blocks), dim3(kBlock), 0, s, a))
+    } else {
+        KIVI_BY_GROUP(a.group, hipLaunchKernelGGL(quantize_k_kernel<GS>, dim3((unsigned)blocks), dim3(kBlock), 0, s, a))
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_quantize_v(const QuantArgs& a, hipStream_t s) {
     if (a.tokens <= 0) return hipSuccess;
+    if (a.bits == 4) {
+        const int64_t blocks4 = a.rows * (int64_t)((a.tokens + 63) / 64);
+        KIVI_BY_GROUP(a.group, hipLaunchKernelGGL(quantize_v4_kernel<GS>, dim3((unsigned)blocks4), dim3(kBlock), 0, s, a))
+        return hipGetLastError();
+    }
     const int64_t n_tiles = (a.dst_token_off + a.tokens - 1) / kG - a.dst_token_off / kG + 1;
     const int64_t blocks = a.rows * n_tiles;
     if (blocks == 0) return hipSuccess;
@@ -292,15 +431,23 @@ hipError_t launch_residual_load(const ResidualArgs& a, hipStream_t s) {
 // in parallel
 hipError_t launch_append_flush(const AppendArgs& a, hipStream_t s) {
     const unsigned parts = a.do_flush && a.flush_all ? (unsigned)(a.residual_cap / a.group) : 1u;
-    KIVI_BY_GROUP(a.group,
-                  hipLaunchKernelGGL(append_flush_kernel<GS>, dim3((unsigned)a.rows, parts), dim3(kBlock), 0, s, a))
+    const dim3 grid((unsigned)a.rows, parts);
+    if (a.bits == 4) {
+        KIVI_BY_GROUP(a.group, hipLaunchKernelGGL((append_flush_kernel<GS, 4>), grid, dim3(kBlock), 0, s, a))
+    } else {
+        KIVI_BY_GROUP(a.group, hipLaunchKernelGGL((append_flush_kernel<GS, 2>), grid, dim3(kBlock), 0, s, a))
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_append_flush_ragged(const AppendArgs& a, int32_t batch, hipStream_t s) {
     const unsigned parts = a.flush_all ? (unsigned)(a.residual_cap / a.group) : 1u;
-    KIVI_BY_GROUP(a.group,
-                  hipLaunchKernelGGL(append_flush_kernel<GS>, dim3((unsigned)a.rows, parts), dim3(kBlock), 0, s, a))
+    const dim3 grid((unsigned)a.rows, parts);
+    if (a.bits == 4) {
+        KIVI_BY_GROUP(a.group, hipLaunchKernelGGL((append_flush_kernel<GS, 4>), grid, dim3(kBlock), 0, s, a))
+    } else {
+        KIVI_BY_GROUP(a.group, hipLaunchKernelGGL((append_flush_kernel<GS, 2>), grid, dim3(kBlock), 0, s, a))
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(seq_state_update_kernel, dim3((unsigned)((batch + 63) / 64)), dim3(64), 0, s, a, batch);

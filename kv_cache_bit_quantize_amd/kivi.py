@@ -23,6 +23,7 @@ EXPORTS = ["kivi_quantize_k_per_channel", "kivi_quantize_v_per_token", "kivi_pre
            "kivi_decode_attn_ragged_splits"]
 
 KIVI_FLUSH_ALL = 1        # kivi_cache.flags: a full residual is flushed whole (else its oldest group)
+KIVI_CODES_4BIT = 2       # kivi_cache.flags: 4-bit codes (sixteen levels), token-major nibbles
 KIVI_SEQ_CAPACITY = 1     # seq_state flags: an append was skipped (its flush would pass token_cap)
 KIVI_SEQ_BAD_STATE = 2    # seq_state flags: the sequence's state was out of range and not used
 
@@ -103,18 +104,25 @@ class Cache:
     """Device buffers of one KIVI cache (layout of include/kivi.h) and its descriptor."""
 
     def __init__(self, batch, kv_heads, token_cap, head_dim=128, group=32, residual_cap=128, device="cuda",
-                 flush_all=False):
+                 flush_all=False, bits=2):
+        if bits not in (2, 4):
+            raise ValueError("bits must be 2 or 4")
         rows = batch * kv_heads
         u8, f16 = torch.uint8, torch.int16
-        tiles = token_cap // 32                    # one 1024-byte tile of codes per 32 tokens
-        self.k_codes = torch.zeros((rows, tiles, 32 * head_dim // 4), dtype=u8, device=device)
-        self.v_codes = torch.zeros((rows, tiles, 32 * head_dim // 4), dtype=u8, device=device)
+        if bits == 4:                              # token-major, two codes per byte
+            self.k_codes = torch.zeros((rows, token_cap, head_dim // 2), dtype=u8, device=device)
+            self.v_codes = torch.zeros((rows, token_cap, head_dim // 2), dtype=u8, device=device)
+        else:                                      # one 1024-byte tile of codes per 32 tokens
+            tiles = token_cap // 32
+            self.k_codes = torch.zeros((rows, tiles, 32 * head_dim // 4), dtype=u8, device=device)
+            self.v_codes = torch.zeros((rows, tiles, 32 * head_dim // 4), dtype=u8, device=device)
         self.k_sz = torch.zeros((rows, token_cap // group, head_dim, 2), dtype=f16, device=device)
         self.v_sz = torch.zeros((rows, token_cap, head_dim // group, 2), dtype=f16, device=device)
         self.k_res = torch.zeros((rows, residual_cap, head_dim), dtype=f16, device=device)
         self.v_res = torch.zeros((rows, residual_cap, head_dim), dtype=f16, device=device)
+        flags = (KIVI_FLUSH_ALL if flush_all else 0) | (KIVI_CODES_4BIT if bits == 4 else 0)
         self.c = kivi_cache(batch, kv_heads, head_dim, group, residual_cap, token_cap, 0, 0, 0,
-                            KIVI_FLUSH_ALL if flush_all else 0, self.k_codes.data_ptr(), self.v_codes.data_ptr(), self.k_sz.data_ptr(),
+                            flags, self.k_codes.data_ptr(), self.v_codes.data_ptr(), self.k_sz.data_ptr(),
                             self.v_sz.data_ptr(), self.k_res.data_ptr(), self.v_res.data_ptr())
         self.device = torch.device(device)
         self._ws = None

@@ -38,18 +38,21 @@ def bits(t):
     return t.numpy().view(np.uint16)
 
 
-def ref_cache(batch, kv_heads, token_cap, k, v, n_quant, residual_cap=128, group=32, flush_all=False):
+_u16 = bits      # for functions whose code-width keyword is also named `bits`
+
+
+def ref_cache(batch, kv_heads, token_cap, k, v, n_quant, residual_cap=128, group=32, flush_all=False, bits=2):
     """Oracle cache prefilled from fp16 tensors k, v [B, H, T, D]."""
     B, H, T, D = k.shape
-    c = ref.RefCache(batch, kv_heads, D, group, residual_cap, token_cap=token_cap, flush_all=flush_all)
-    c.prefill(bits(k).reshape(B * H, T, D), bits(v).reshape(B * H, T, D), n_quant)
+    c = ref.RefCache(batch, kv_heads, D, group, residual_cap, token_cap=token_cap, flush_all=flush_all, bits=bits)
+    c.prefill(_u16(k).reshape(B * H, T, D), _u16(v).reshape(B * H, T, D), n_quant)
     return c
 
 
 def assert_cache_equal(gpu, oracle, rows=None, upto=None, ring=True):
     """Bit-exact comparison of the packed history (tokens < upto) and the residual ring."""
     nq = oracle.n_quant if upto is None else upto
-    ng = nq // 32                                   # whole 32-token code tiles
+    ng = nq if getattr(oracle, "bits", 2) == 4 else nq // 32   # 4-bit: token rows; 2-bit: 32-token tiles
     nk = nq // oracle.group                         # whole key groups (one pair per channel each)
     sel = slice(None) if rows is None else rows
     kc = gpu.k_codes[sel, :ng].cpu().numpy()

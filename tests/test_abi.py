@@ -111,6 +111,17 @@ def test_status_strings():
     assert kivi.status_str(-99) == "unknown status"
 
 
+def test_four_bit_codes_double_the_code_bytes():
+    """KIVI_CODES_4BIT: 64 code bytes per token and head for keys and for values, the same
+    pairs (160 bytes per quantized token and head at G = 32)."""
+    two, four = _cache(token_cap=1024), _cache(token_cap=1024, flags=kivi.KIVI_CODES_4BIT)
+    c2, p2, r2 = kivi.kivi_cache_bytes(two)
+    c4, p4, r4 = kivi.kivi_cache_bytes(four)
+    assert c4 == 2 * c2 and p4 == p2 and r4 == r2
+    assert (c4 + p4) // (4 * 1024) == 160
+    assert L.kivi_decode_attn_splits(C.byref(four), 2) >= 1
+
+
 def test_cache_bytes_matches_layout():
     c = _cache(batch=3, kv_heads=4, token_cap=4096)
     codes, pairs, res = kivi.kivi_cache_bytes(c)
@@ -142,7 +153,7 @@ def test_group_sizes_supported_and_sized(G, per_token):
     (dict(token_cap=100), -2),
     (dict(residual_cap=100), -2),
     (dict(batch=0), -2),
-    (dict(flags=2), -2),             # unknown flag bits
+    (dict(flags=4), -2),             # unknown flag bits
 ])
 def test_shape_validation(kw, code):
     c = _cache(**kw)

@@ -17,11 +17,11 @@ SRC = os.path.join(ROOT, "oracle", "kivi_oracle.c")
 
 # (name, text in the oracle, planted replacement, run the slow exhaustive pins too)
 MUTATIONS = [
-    ("scale_over_4", "float s32 = range / 3.0f;", "float s32 = range / 4.0f;", False),
+    ("scale_over_levels", "float s32 = range / top;", "float s32 = range / (top + 1.0f);", False),
     ("ties_away_from_zero", "return (fmodf(f, 2.0f) == 0.0f) ? f : f + 1.0f;", "return f + 1.0f;", False),
     ("codes_from_fp32_scale", "float s = kivi_ref_f16_to_f32(s16);", "float s = s32;", False),
     ("reciprocal_multiply", "float t = d / s;", "float t = d * (1.0f / s);", False),
-    ("no_clamp", "if (r > 3.0f) r = 3.0f;", "", False),
+    ("no_clamp", "if (r > top) r = top;", "", False),
     ("zero_is_max", "*zero = kivi_ref_f32_to_f16(mn);", "*zero = kivi_ref_f32_to_f16(mx);", False),
     ("keep_negative_zero", "if (mn == 0.0f) mn = 0.0f;", "", False),
     ("keep_negative_zero_max", "if (mx == 0.0f) mx = 0.0f;", "", False),
@@ -65,6 +65,14 @@ MUTATIONS = [
     ("f16_ties_away", "return (fmod(f, 2.0) == 0.0) ? f : f + 1.0;", "return f + 1.0;", True),
     ("f16_subnormals_flushed", "double n = rne_double(a * ldexp(1.0, 24));", "double n = 0.0;", True),
     ("bytes_meta_per_element", "*meta = (elems / group) * 2 * 2;", "*meta = elems * 2;", False),
+    ("four_bit_high_nibble_first", "if (bits_of(c) == 4) return 4 * (j % 2);",
+     "if (bits_of(c) == 4) return 4 * (1 - j % 2);", False),
+    ("four_bit_channel_major", "if (bits_of(c) == 4) return (int64_t)t * (c->head_dim / 2) + j / 2;",
+     "if (bits_of(c) == 4) return (int64_t)(j / 2) * c->token_cap + t;", False),
+    ("four_bit_as_two_bit_levels", "kivi_ref_quant_group_bits(s_row + (int64_t)t * d + k * G, 1, G, bits_of(c),",
+     "kivi_ref_quant_group_bits(s_row + (int64_t)t * d + k * G, 1, G, 2,", False),
+    ("four_bit_keys_as_two_bit_levels", "kivi_ref_quant_group_bits(s_row + (int64_t)t0 * d + j, d, G, bits_of(c),",
+     "kivi_ref_quant_group_bits(s_row + (int64_t)t0 * d + j, d, G, 2,", False),
 ]
 
 
@@ -85,7 +93,8 @@ def _build(src_text, out_dir):
 def _run_pins(lib, slow):
     env = dict(os.environ, KIVI_ORACLE_LIB=lib)
     files = [os.path.join(ROOT, "tests", f) for f in
-             ("test_oracle_quant.py", "test_oracle_attn.py", "test_oracle_cache.py", "test_oracle_fp16.py")]
+             ("test_oracle_quant.py", "test_oracle_quant4.py", "test_oracle_attn.py", "test_oracle_cache.py",
+              "test_oracle_fp16.py")]
     cmd = [sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
            "-m", "not gpu" if slow else "not gpu and not slow", *files]
     return subprocess.run(cmd, env=env, cwd=ROOT, capture_output=True, text=True, timeout=600)
