@@ -13,8 +13,10 @@ After the timed steps, the fp16 comparator (kivi_decode_attn_fp16: the same atte
 an uncompressed fp16 cache of the starting context) is timed the same way and reported
 beside it ("fp16_comparator"; --no-fp16 skips it), and so is the ragged-batch path on a
 serving batch of 64 sequences at different lengths ("ragged_batch"; --no-ragged skips it),
-and attention alone over the same context quantized at group sizes 64 and 128
-("group_sizes"; --sweep-groups sets the list, --group the timed cache's own group size).
+attention alone over the same context quantized at group sizes 64 and 128
+("group_sizes"; --sweep-groups sets the list, --group the timed cache's own group size),
+and attention alone over the same context in 4-bit codes ("four_bit"; --four-bit-groups
+sets its group sizes, empty skips it).
 """
 import argparse
 import json
@@ -34,11 +36,12 @@ D = 128
 RES_TOKEN_BYTES = 512          # per kv head: fp16 key + value
 
 
-def quant_token_bytes(g):
-    """Bytes of one quantized token per kv head at group size g: 32 B of key codes and
-    32 B of value codes, a 4-byte (scale, zero) per channel per g tokens for the keys and
-    per g channels of the token for the values (96 B at g = 32)."""
-    return 2 * D // 4 + D * 4 // g + (D // g) * 4
+def quant_token_bytes(g, bits=2):
+    """Bytes of one quantized token per kv head at group size g: D*bits/8 bytes of key codes
+    and as many of value codes (32 + 32 B at 2 bits, 64 + 64 B at 4), a 4-byte (scale, zero)
+    per channel per g tokens for the keys and per g channels of the token for the values
+    (96 B at g = 32 and 2 bits, 160 B at 4 bits)."""
+    return 2 * D * bits // 8 + D * 4 // g + (D // g) * 4
 
 
 QUANT_TOKEN_BYTES = quant_token_bytes(32)
@@ -46,11 +49,12 @@ def counters_file(workload):
     return os.path.join(ROOT, "profiles", f"decode_attn_{workload}_counters.json")
 
 
-def attn_bytes(w, n_quant, n_res):
+def attn_bytes(w, n_quant, n_res, bits=2):
     """Algorithmic HBM bytes of one decode-attention call: the packed history and the
     residual read once per kv head, q read and out written once per query head."""
     rows = w.batch * w.kv_heads
-    return rows * (n_quant * quant_token_bytes(w.group) + n_res * RES_TOKEN_BYTES) + 2 * w.batch * w.q_heads * D * 2
+    return (rows * (n_quant * quant_token_bytes(w.group, bits) + n_res * RES_TOKEN_BYTES)
+            + 2 * w.batch * w.q_heads * D * 2)
 
 
 def append_bytes(w, flushed):
@@ -176,20 +180,21 @@ def time_attention(kivi, cache, queries, sm, steps, warmup):
     return float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
 
 
-def group_sweep(kivi, synth, w, k, v, queries, steps, warmup, groups):
+def group_sweep(kivi, synth, w, k, v, queries, steps, warmup, groups, bits=2):
     """Attention alone (kivi_decode_attn) over the same prefill keys and values quantized at
-    other group sizes: the history is the largest whole number of groups that leaves at
-    least 32 tokens in the fp16 residual."""
+    other group sizes or code widths: the history is the largest whole number of groups
+    that leaves at least 32 tokens in the fp16 residual."""
     import dataclasses
     res = []
     for g in groups:
         nq = (w.context - 32) // g * g
         wg = dataclasses.replace(w, group=g, n_quant=nq)
-        cache = kivi.Cache(wg.batch, wg.kv_heads, wg.token_cap, group=g, device=k.device)
+        cache = kivi.Cache(wg.batch, wg.kv_heads, wg.token_cap, group=g, device=k.device, bits=bits)
         kivi.kivi_prefill(k, v, nq, cache)
         us = time_attention(kivi, cache, queries, synth.SM_SCALE_D128, steps, warmup)
-        b = attn_bytes(wg, nq, wg.n_res)
-        res.append({"group": g, "n_quant": nq, "n_res": wg.n_res, "splits": kivi.kivi_decode_attn_splits(cache, w.q_heads),
+        b = attn_bytes(wg, nq, wg.n_res, bits)
+        res.append({"bits": bits, "group": g, "n_quant": nq, "n_res": wg.n_res,
+                    "splits": kivi.kivi_decode_attn_splits(cache, w.q_heads),
                     "decode_attn_us": round(us, 2), "bytes_per_launch": int(b), "achieved": round(b / us / 1e3, 1),
                     "unit": "GB/s", "frac": round(b / us / 1e3 / PEAK_HBM_GBS, 4)})
         del cache
@@ -225,6 +230,8 @@ def main():
     ap.add_argument("--group", type=int, default=32, help="group size of the timed cache (32, 64 or 128)")
     ap.add_argument("--sweep-groups", default="64,128",
                     help="group sizes of the attention-only sweep (comma list; empty: skip)")
+    ap.add_argument("--four-bit-groups", default="32",
+                    help="group sizes of the 4-bit attention-only measurement (comma list; empty: skip)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the decode hot path shards "
@@ -365,11 +372,15 @@ def main():
         "fp16_comparator": fp16,
         "ragged_batch": None,
         "group_sizes": None,
+        "four_bit": None,
     }
     del cache, ws
     groups = [int(x) for x in args.sweep_groups.split(",") if x.strip()]
     if groups:
         res["group_sizes"] = group_sweep(kivi, synth, w, k, v, queries, args.steps, args.warmup, groups)
+    groups4 = [int(x) for x in args.four_bit_groups.split(",") if x.strip()]
+    if groups4:
+        res["four_bit"] = group_sweep(kivi, synth, w, k, v, queries, args.steps, args.warmup, groups4, bits=4)
     if not args.no_ragged:
         res["ragged_batch"] = ragged_measure(kivi, synth, dev, args.steps, args.warmup)
     if args.cpu_heads > 0:

@@ -70,7 +70,8 @@ enum {
  *                        n = 0..15, p = 0..3, h and e = 0..1).
  *   (KIVI_CODES_4BIT)  k_codes, v_codes : uint8 [row][token_cap][D/2] instead: a token's
  *                      codes in D/2 bytes, channel j in byte j/2, the even channel in the
- *                      low nibble.
+ *                      low nibble.  A 4-bit cache holds at most 2^26 tokens a row
+ *                      (token_cap above that: KIVI_ERR_UNSUPPORTED).
  *   k_sz             : fp16   [row][token_cap/G][D][2]  (scale, zero) of key token group
  *                      g (tokens Gg..Gg+G-1), channel j -- keys are quantized per-channel
  *                      over G tokens.

@@ -22,6 +22,8 @@ constexpr int64_t kTargetBlocksSingle = 256;   // single-query 2-bit workgroups 
 constexpr int kMinGroupsPerSplit = 8;
 constexpr int kMinGroupsPerSplitSingle = 2 * kSqWaves;   // a pair of tiles for every wave
 
+constexpr int32_t kMaxTokenCap4 = 1 << 26;
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int check_shape(const kivi_cache* c) {
@@ -33,6 +35,8 @@ int check_shape(const kivi_cache* c) {
         c->token_cap % c->group != 0)
         return KIVI_ERR_SHAPE;
     if (c->head_dim != kD || !group_supported(c->group)) return KIVI_ERR_UNSUPPORTED;
+    // 4-bit rows are addressed with 32-bit byte offsets: token_cap * 64 < 2^32
+    if ((c->flags & KIVI_CODES_4BIT) && c->token_cap > kMaxTokenCap4) return KIVI_ERR_UNSUPPORTED;
     return KIVI_OK;
 }
 

@@ -4,14 +4,17 @@
 // 2-bit one, KIVI-2, and its ablation varies the scheme's parameters): the same call shape,
 // query grouping, split-K, fp16 residual and log-sum-exp merge as the 2-bit kernels.  A
 // 4-bit cache holds twice the code bytes per token, so the contraction runs on the vector
-// units: each key and value element is dequantized in fp32 (code x scale + zero: the
-// product of a 4-bit code and an fp16 scale is exact in fp32) and used in an fp32 fused
-// multiply-add chain with the fp16 query.
+// units, with the dequantization folded into both products:
+//  * keys, per group: q.(z + c*s) = q.z + (q*s).c.  Once per group the wave forms q*s for
+//    the 128 channels in fp32 (a product of two fp16 values, exact) into LDS and q.z as one
+//    wave sum; per token each code then costs one byte-to-float conversion and one fma;
+//  * values, per token: p*(z + c*s) = (p*s)*c + p*z, the p*z part summed per lane and
+//    added to its channels at the end.
 //
 // Work split: grid (splits, kv heads x query chunks of NQ heads); a split owns whole key
 // groups, each of its 4 waves a contiguous run of them, 16 tokens per wave-iteration:
-//  * logits: lane 4t + c holds token t and channels [32c, 32c+32) (16 bytes of codes); the
-//    group's (scale, zero) words pass through LDS once per group and the lane keeps its 32;
+//  * logits: lane 4t + c holds token t and channels [32c, 32c+32) (16 bytes of codes) and
+//    keeps the group's q*s of those channels in registers;
 //  * online softmax per query head (log2 domain), the probabilities into LDS;
 //  * P.V: lane 16g + c holds tokens 4g..4g+3 and channels [8c, 8c+8) (4 bytes of codes and
 //    the token's (scale, zero) word of those channels).
@@ -29,7 +32,7 @@ template <int NQ, int GS>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) void attn_q4_kernel(AttnArgs a) {
     constexpr int kIt = GS / kQ4Tok;   // iterations per key group
     __shared__ __align__(16) float sh_p[kWaves][NQ][kQ4Tok];
-    __shared__ __align__(16) uint32_t sh_kp[kWaves][kD];
+    __shared__ __align__(16) float sh_qs[kWaves][NQ][kD];   // q*s of the wave's current key group
     __shared__ __align__(16) float sh_o[NQ][kSlots][kD];
     __shared__ float sh_m[NQ][kSlots], sh_l[NQ][kSlots];
 
@@ -58,19 +61,14 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     const int n_groups = kg_lo + min(cnt, (wave + 1) * per_wave) - kgb;
     const int n_it = n_groups * kIt;
 
-    // query channels 32kq..32kq+31 of the NQ heads, packed fp16 pairs
-    uint32_t qp[NQ][16];
+    // query channels 2*lane and 2*lane+1 of the NQ heads (the channels whose key pairs this
+    // lane loads)
+    float q0[NQ], q1[NQ];
 #pragma unroll
     for (int r = 0; r < NQ; ++r) {
-        const uint4* src = reinterpret_cast<const uint4*>(a.q + (qrow0 + r) * kD + 32 * kq);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint4 x = src[i];
-            qp[r][4 * i] = x.x;
-            qp[r][4 * i + 1] = x.y;
-            qp[r][4 * i + 2] = x.z;
-            qp[r][4 * i + 3] = x.w;
-        }
+        const uint32_t x = *reinterpret_cast<const uint32_t*>(a.q + (qrow0 + r) * kD + 2 * lane);
+        q0[r] = h2f(x & 0xffffu);
+        q1[r] = h2f(x >> 16);
     }
 
     const int64_t tok0 = kvrow * (int64_t)a.token_cap;
@@ -85,15 +83,20 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
         uint32_t vp[4];   // (scale, zero) word of those tokens and channels
     };
     auto tok = [&](int it) { return t_b + min(it, n_it - 1) * kQ4Tok; };   // clamped past the end
+    // byte offsets inside a row fit 32 bits (token_cap <= 2^26 for 4-bit caches), so the
+    // loads take the row pointer as their scalar base and per-token steps as immediates
     auto load_k = [&](Loads& L, int it) {
-        L.k = *reinterpret_cast<const uint4*>(kc_row + (int64_t)(tok(it) + kt) * kRowBytes4 + 16 * kq);
+        const uint32_t off = (uint32_t)(tok(it) + kt) * kRowBytes4 + 16 * kq;
+        L.k = *reinterpret_cast<const uint4*>(kc_row + off);
     };
     auto load_v = [&](Loads& L, int it) {
+        const uint32_t t = (uint32_t)(tok(it) + 4 * vg);
+        const uint8_t* cp = vc_row + (t * kRowBytes4 + 4 * vc);
+        const uint32_t* pp = vp_row + (t * (kD / GS) + (8 * vc) / GS);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const int64_t t = tok(it) + 4 * vg + u;
-            L.v[u] = *reinterpret_cast<const uint32_t*>(vc_row + t * kRowBytes4 + 4 * vc);
-            L.vp[u] = vp_row[t * (kD / GS) + (8 * vc) / GS];
+            L.v[u] = *reinterpret_cast<const uint32_t*>(cp + u * kRowBytes4);
+            L.vp[u] = pp[u * (kD / GS)];
         }
     };
     // (scale, zero) words of key group gi of the wave, channels 2*lane and 2*lane+1
@@ -101,16 +104,16 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
         return *reinterpret_cast<const uint2*>(kp_row + (int64_t)(kgb + min(gi, n_groups - 1)) * kD + 2 * lane);
     };
 
-    float m[NQ], lsum[NQ], o[NQ][8];
+    float m[NQ], lsum[NQ], o[NQ][8], oz[NQ];   // oz: sum of p*z of the lane's tokens and channel group
 #pragma unroll
     for (int r = 0; r < NQ; ++r) {
         m[r] = -INFINITY;
         lsum[r] = 0.0f;
+        oz[r] = 0.0f;
 #pragma unroll
         for (int c = 0; c < 8; ++c) o[r][c] = 0.0f;
     }
     float* pw = &sh_p[wave][0][0];
-    uint32_t* kpw = &sh_kp[wave][0];
     auto wave_sync = []() {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -125,47 +128,53 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
         uint2 kpn = load_kp(0);
         tag = settle_tag(tag_v);
         for (int gi = 0; gi < n_groups; ++gi) {
-            // this group's (scale, zero) words through LDS; this lane keeps its 32 channels'
-            *reinterpret_cast<uint2*>(kpw + 2 * lane) = kpn;
-            wave_sync();
-            uint32_t kpr[32];
+            // this group's q*s into LDS (channels 2*lane, 2*lane+1) and q.z over the wave
+            float qz[NQ];
+            {
+                const float s0 = h2f(kpn.x & 0xffffu), z0 = h2f(kpn.x >> 16);
+                const float s1 = h2f(kpn.y & 0xffffu), z1 = h2f(kpn.y >> 16);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const uint4 x = *reinterpret_cast<const uint4*>(kpw + 32 * kq + 4 * i);
-                kpr[4 * i] = x.x;
-                kpr[4 * i + 1] = x.y;
-                kpr[4 * i + 2] = x.z;
-                kpr[4 * i + 3] = x.w;
+                for (int r = 0; r < NQ; ++r) {
+                    *reinterpret_cast<float2*>(&sh_qs[wave][r][2 * lane]) = make_float2(q0[r] * s0, q1[r] * s1);
+                    qz[r] = wave_sum(fmaf(q0[r], z0, q1[r] * z1));
+                }
             }
-            wave_sync();   // every lane has read the words before the next group's are written
+            wave_sync();
+            float qs[NQ][32];   // q*s of channels 32kq..32kq+31
+#pragma unroll
+            for (int r = 0; r < NQ; ++r) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float4 x = *reinterpret_cast<const float4*>(&sh_qs[wave][r][32 * kq + 4 * i]);
+                    qs[r][4 * i] = x.x;
+                    qs[r][4 * i + 1] = x.y;
+                    qs[r][4 * i + 2] = x.z;
+                    qs[r][4 * i + 3] = x.w;
+                }
+            }
+            wave_sync();   // every lane has read the group's q*s before the next group's are written
             kpn = load_kp(gi + 1);
 #pragma unroll 1
             for (int j = 0; j < kIt; ++j) {
                 const int it = gi * kIt + j;
-                // ---- logits: 32 channels of token kt for every query head
+                // ---- logits: 32 channels of token kt for every query head (q.z once per token)
                 const uint32_t cw[4] = {cur.k.x, cur.k.y, cur.k.z, cur.k.w};
                 float d[NQ];
 #pragma unroll
-                for (int r = 0; r < NQ; ++r) d[r] = 0.0f;
+                for (int r = 0; r < NQ; ++r) d[r] = kq == 0 ? qz[r] : 0.0f;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    // word i: channels 8i..8i+7 of the quarter, channel 8i + c at bit 4c;
-                    // the even channels' codes as bytes of lo, the odd ones' of hi
-                    const uint32_t lo = cw[i] & 0x0F0F0F0Fu, hi = (cw[i] >> 4) & 0x0F0F0F0Fu;
+                    // word i: channels 8i..8i+7 of the quarter, channel 8i + c at bit 4c; the
+                    // even channels' codes as the bytes of lo, the odd ones' of hi
+                    uint32_t lo = cw[i] & 0x0F0F0F0Fu, hi = (cw[i] >> 4) & 0x0F0F0F0Fu;
+                    // opaque to the optimizer, so each code converts with one v_cvt_f32_ubyteN
+                    asm volatile("" : "+v"(lo), "+v"(hi));
 #pragma unroll
                     for (int c = 0; c < 8; ++c) {
-                        const int jj = 8 * i + c;
                         const float code = (float)((((c & 1) ? hi : lo) >> (8 * (c >> 1))) & 0xFFu);
-                        const float kv = fmaf(code, h2f(kpr[jj] & 0xffffu), h2f(kpr[jj] >> 16));
 #pragma unroll
-                        for (int r = 0; r < NQ; ++r) {
-                            const uint32_t qh = qp[r][jj >> 1];
-                            d[r] = fmaf(h2f((jj & 1) ? (qh >> 16) : (qh & 0xffffu)), kv, d[r]);
-                        }
+                        for (int r = 0; r < NQ; ++r) d[r] = fmaf(qs[r][8 * i + c], code, d[r]);
                     }
-                    // one word at a time: without the fence the compiler keeps the
-                    // dequantized keys of all four words live at once
-                    __builtin_amdgcn_sched_barrier(0);
                 }
                 load_k(cur, it + 1);
                 // ---- online softmax per query head over the 16 tokens
@@ -177,6 +186,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
                         const float al = m[r] == -INFINITY ? 0.0f : exp2f(m[r] - mnew);
 #pragma unroll
                         for (int c = 0; c < 8; ++c) o[r][c] *= al;
+                        oz[r] *= al;
                         lsum[r] *= al;
                         m[r] = mnew;
                     }
@@ -186,19 +196,32 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
                 }
                 wave_sync();
                 // ---- P.V: tokens 4vg..4vg+3, channels 8vc..8vc+7
+                float pv[NQ][4];
+#pragma unroll
+                for (int r = 0; r < NQ; ++r) {
+                    const float4 x = *reinterpret_cast<const float4*>(pw + r * kQ4Tok + 4 * vg);
+                    pv[r][0] = x.x;
+                    pv[r][1] = x.y;
+                    pv[r][2] = x.z;
+                    pv[r][3] = x.w;
+                }
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const float s = h2f(cur.vp[u] & 0xffffu), z = h2f(cur.vp[u] >> 16);
-                    const uint32_t lo = cur.v[u] & 0x0F0F0F0Fu, hi = (cur.v[u] >> 4) & 0x0F0F0F0Fu;
-                    float pt[NQ];
+                    uint32_t lo = cur.v[u] & 0x0F0F0F0Fu, hi = (cur.v[u] >> 4) & 0x0F0F0F0Fu;
+                    asm volatile("" : "+v"(lo), "+v"(hi));
+                    float ps[NQ];
 #pragma unroll
-                    for (int r = 0; r < NQ; ++r) pt[r] = pw[r * kQ4Tok + 4 * vg + u];
+                    for (int r = 0; r < NQ; ++r) {
+                        const float pt = pv[r][u];
+                        ps[r] = pt * s;
+                        oz[r] = fmaf(pt, z, oz[r]);
+                    }
 #pragma unroll
                     for (int c = 0; c < 8; ++c) {
                         const float code = (float)((((c & 1) ? hi : lo) >> (8 * (c >> 1))) & 0xFFu);
-                        const float val = fmaf(code, s, z);
 #pragma unroll
-                        for (int r = 0; r < NQ; ++r) o[r][c] = fmaf(pt[r], val, o[r][c]);
+                        for (int r = 0; r < NQ; ++r) o[r][c] = fmaf(ps[r], code, o[r][c]);
                     }
                 }
                 load_v(cur, it + 1);
@@ -215,7 +238,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     for (int r = 0; r < NQ; ++r) {
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-            float x = o[r][c] + xor16_f(o[r][c]);
+            const float oc = o[r][c] + oz[r];   // the lane's p*z share belongs to each of its channels
+            float x = oc + xor16_f(oc);
             x += __shfl_xor(x, 32, 64);
             o[r][c] = x;
         }

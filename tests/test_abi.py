@@ -122,6 +122,17 @@ def test_four_bit_codes_double_the_code_bytes():
     assert L.kivi_decode_attn_splits(C.byref(four), 2) >= 1
 
 
+def test_four_bit_rows_hold_at_most_2_26_tokens():
+    """4-bit rows are addressed with 32-bit byte offsets: token_cap up to 2^26 is accepted,
+    beyond it every call that checks the cache reports KIVI_ERR_UNSUPPORTED (-3)."""
+    ok = _cache(token_cap=1 << 26, flags=kivi.KIVI_CODES_4BIT)
+    big = _cache(token_cap=(1 << 26) + 32, flags=kivi.KIVI_CODES_4BIT)
+    two_bit = _cache(token_cap=(1 << 26) + 32)
+    assert L.kivi_decode_attn_splits(C.byref(ok), 2) >= 1
+    assert L.kivi_decode_attn_splits(C.byref(two_bit), 2) >= 1
+    assert L.kivi_decode_attn_splits(C.byref(big), 2) == -3
+
+
 def test_cache_bytes_matches_layout():
     c = _cache(batch=3, kv_heads=4, token_cap=4096)
     codes, pairs, res = kivi.kivi_cache_bytes(c)
