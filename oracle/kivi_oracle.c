@@ -13,6 +13,8 @@
  *      fields "KV bytes basis", "Quant method", "Methodology".
  *  [C] "Your KV cache doesn't have a bit problem, it has a geometry problem",
  *      paragraphs 1-4.
+ *  [D] GrooveSquid summary of "KVQuant: Towards 10 Million Context Length LLM Inference
+ *      with KV Cache Quantization": medium-difficulty summary.
  */
 #include "kivi_oracle.h"
 
@@ -388,6 +390,62 @@ void kivi_ref_decode_attn(const kivi_ref_cache* c, const uint16_t* q, int32_t q_
         kivi_ref_attn_dense(qd, K, V, n, d, (double)sm_scale, out + r * d, lse ? lse + r : NULL);
     }
     free(K);
+    free(V);
+    free(qd);
+}
+
+/* Rotary position embedding of one vector at position pos.  [C] paragraph 4 and [D] advise
+ * quantizing keys before RoPE is applied, so the rotation comes after dequantization; the
+ * pages name RoPE without writing it out.  Reading: the rotary embedding with the
+ * rotate-half pairing of the Llama-2 models the pages measure -- channel i < d/2 pairs
+ * with channel i + d/2, pair i turns at frequency w_i = base^(-2i/d), and a token at
+ * position pos is turned by the angle pos*w_i:
+ *   out_i = x_i cos - x_{i+d/2} sin,   out_{i+d/2} = x_{i+d/2} cos + x_i sin.
+ * All in binary64 with the C library's pow, cos and sin. */
+void kivi_ref_rope(const double* x, int32_t d, int64_t pos, double base, double* out) {
+    int32_t h = d / 2;
+    for (int32_t i = 0; i < h; ++i) {
+        double w = pow(base, -2.0 * (double)i / (double)d);
+        double a = (double)pos * w;
+        double cs = cos(a), sn = sin(a);
+        double x0 = x[i], x1 = x[i + h];
+        out[i] = x0 * cs - x1 * sn;
+        out[i + h] = x1 * cs + x0 * sn;
+    }
+}
+
+/* Decode attention over a cache of pre-RoPE keys: every key is dequantized (history) or
+ * read (fp16 residual), then turned by kivi_ref_rope at its position in the sequence --
+ * history token t at position t, the i-th oldest residual token at n_quant + i -- and
+ * the query (already rotated by the caller at its own position) attends over the turned
+ * keys as in kivi_ref_decode_attn.  Values carry no position and are used as they are. */
+void kivi_ref_decode_attn_rope(const kivi_ref_cache* c, const uint16_t* q, int32_t q_heads,
+                               float sm_scale, double rope_base, double* out, double* lse,
+                               const int64_t* rows, int64_t n_rows) {
+    int32_t d = c->head_dim;
+    int32_t n = c->n_quant + c->n_res;
+    int32_t ratio = q_heads / c->kv_heads;
+    int64_t total = (int64_t)c->batch * q_heads;
+    double* K = (double*)malloc((size_t)n * d * sizeof(double));
+    double* Kr = (double*)malloc((size_t)n * d * sizeof(double));
+    double* V = (double*)malloc((size_t)n * d * sizeof(double));
+    double* qd = (double*)malloc((size_t)d * sizeof(double));
+    int64_t last_kv_row = -1;
+    int64_t count = rows ? n_rows : total;
+    for (int64_t idx = 0; idx < count; ++idx) {
+        int64_t r = rows ? rows[idx] : idx;
+        int64_t b = r / q_heads, hq = r % q_heads;
+        int64_t kv_row = b * c->kv_heads + hq / ratio;
+        if (kv_row != last_kv_row) {
+            kivi_ref_dequant_row(c, (int32_t)kv_row, K, V);
+            for (int32_t t = 0; t < n; ++t) kivi_ref_rope(K + (int64_t)t * d, d, t, rope_base, Kr + (int64_t)t * d);
+            last_kv_row = kv_row;
+        }
+        for (int32_t j = 0; j < d; ++j) qd[j] = kivi_ref_f16_to_f32(q[r * d + j]);
+        kivi_ref_attn_dense(qd, Kr, V, n, d, (double)sm_scale, out + r * d, lse ? lse + r : NULL);
+    }
+    free(K);
+    free(Kr);
     free(V);
     free(qd);
 }

@@ -110,6 +110,14 @@ void kivi_ref_decode_attn(const kivi_ref_cache* c, const uint16_t* q, int32_t q_
                           float sm_scale, double* out, double* lse,
                           const int64_t* rows, int64_t n_rows);
 
+/* Rotary position embedding (rotate-half pairing, w_i = base^(-2i/d)) of x[d] at pos. */
+void kivi_ref_rope(const double* x, int32_t d, int64_t pos, double base, double* out);
+
+/* kivi_ref_decode_attn over pre-RoPE keys, each turned at its sequence position. */
+void kivi_ref_decode_attn_rope(const kivi_ref_cache* c, const uint16_t* q, int32_t q_heads,
+                               float sm_scale, double rope_base, double* out, double* lse,
+                               const int64_t* rows, int64_t n_rows);
+
 /* Partial softmax state of one query over keys [t0, t1) of a dense context, and the
  * log-sum-exp merge of such partials.  Used to pin the split-K merge. */
 void kivi_ref_attn_partial(const double* q, const double* K, const double* V, int32_t t0,

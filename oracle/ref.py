@@ -40,6 +40,8 @@ def lib():
         L.kivi_ref_dequant_row.argtypes = [p, i32, p, p]
         L.kivi_ref_attn_dense.argtypes = [p, p, p, i32, i32, f64, p, p]
         L.kivi_ref_decode_attn.argtypes = [p, p, i32, f32, p, p, p, i64]
+        L.kivi_ref_rope.argtypes = [p, i32, i64, f64, p]
+        L.kivi_ref_decode_attn_rope.argtypes = [p, p, i32, f32, f64, p, p, p, i64]
         L.kivi_ref_attn_partial.argtypes = [p, p, p, i32, i32, i32, f64, p, p, p]
         L.kivi_ref_attn_merge.argtypes = [p, p, p, i32, i32, p, p]
         L.kivi_ref_bytes_per_token.argtypes = [i64, i64, i64, i64, p, p, p]
@@ -174,7 +176,28 @@ class RefCache:
         return out, lse
 
 
+    def decode_attn_rope(self, q, sm_scale, rope_base, rows=None):
+        """decode_attn over pre-RoPE keys, each turned at its sequence position (history
+        token t at t, the i-th oldest residual token at n_quant + i)."""
+        q = _c(q, np.uint16)
+        B, Hq, D = q.shape
+        out = np.full((B, Hq, D), np.nan)
+        lse = np.full((B, Hq), np.nan)
+        r = None if rows is None else _c(rows, np.int64)
+        lib().kivi_ref_decode_attn_rope(C.byref(self.s), _ptr(q), Hq, float(sm_scale), float(rope_base),
+                                        _ptr(out), _ptr(lse), _ptr(r), 0 if r is None else r.size)
+        return out, lse
+
+
 # ---------------------------------------------------------- attention ---------
+def rope(x, pos, base):
+    """Rotary embedding of x [d] (float64) at position pos."""
+    x = _c(x, np.float64)
+    out = np.empty_like(x)
+    lib().kivi_ref_rope(_ptr(x), x.size, int(pos), float(base), _ptr(out))
+    return out
+
+
 def attn_dense(q, K, V, sm_scale):
     q, K, V = _c(q, np.float64), _c(K, np.float64), _c(V, np.float64)
     out = np.empty(K.shape[1])

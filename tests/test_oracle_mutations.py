@@ -65,6 +65,14 @@ MUTATIONS = [
     ("f16_ties_away", "return (fmod(f, 2.0) == 0.0) ? f : f + 1.0;", "return f + 1.0;", True),
     ("f16_subnormals_flushed", "double n = rne_double(a * ldexp(1.0, 24));", "double n = 0.0;", True),
     ("bytes_meta_per_element", "*meta = (elems / group) * 2 * 2;", "*meta = elems * 2;", False),
+    ("rope_sin_sign", "out[i] = x0 * cs - x1 * sn;", "out[i] = x0 * cs + x1 * sn;", False),
+    ("rope_partner_sign", "out[i + h] = x1 * cs + x0 * sn;", "out[i + h] = x1 * cs - x0 * sn;", False),
+    ("rope_frequency_exponent", "double w = pow(base, -2.0 * (double)i / (double)d);",
+     "double w = pow(base, -1.0 * (double)i / (double)d);", False),
+    ("rope_residual_positions_restart",
+     "kivi_ref_rope(K + (int64_t)t * d, d, t, rope_base, Kr + (int64_t)t * d);",
+     "kivi_ref_rope(K + (int64_t)t * d, d, t < c->n_quant ? t : t - c->n_quant, rope_base, Kr + (int64_t)t * d);",
+     False),
     ("four_bit_high_nibble_first", "if (bits_of(c) == 4) return 4 * (j % 2);",
      "if (bits_of(c) == 4) return 4 * (1 - j % 2);", False),
     ("four_bit_channel_major", "if (bits_of(c) == 4) return (int64_t)t * (c->head_dim / 2) + j / 2;",
@@ -94,7 +102,7 @@ def _run_pins(lib, slow):
     env = dict(os.environ, KIVI_ORACLE_LIB=lib)
     files = [os.path.join(ROOT, "tests", f) for f in
              ("test_oracle_quant.py", "test_oracle_quant4.py", "test_oracle_attn.py", "test_oracle_cache.py",
-              "test_oracle_fp16.py")]
+              "test_oracle_fp16.py", "test_oracle_rope.py")]
     cmd = [sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
            "-m", "not gpu" if slow else "not gpu and not slow", *files]
     return subprocess.run(cmd, env=env, cwd=ROOT, capture_output=True, text=True, timeout=600)
