@@ -163,6 +163,23 @@ int kivi_decode_attn(const kivi_cache* cache, const uint16_t* q, int32_t q_heads
                      float sm_scale, uint16_t* out, float* lse, void* workspace,
                      size_t workspace_bytes, int32_t num_splits, void* stream);
 
+/* Decode attention over a cache of pre-RoPE keys ("Your KV cache doesn't have a bit
+ * problem...", paragraph 4, and the KVQuant summary on GrooveSquid advise quantizing keys
+ * before the rotary position embedding; keys are then stored and appended as given, and the
+ * rotation happens here, after dequantization).  Same arguments, results, workspace and
+ * error behaviour as kivi_decode_attn, plus rope_base (> 0, finite; 10000 for Llama-2):
+ * every key -- history token t at position t, the i-th oldest residual token at
+ * n_quant + i -- is turned by the rotary embedding in rotate-half form (channel i < D/2
+ * with channel i + D/2, angle position * rope_base^(-2i/D)) before q . k.  q is used as
+ * given: the caller rotates it at its own position.  Values are not rotated.  The split
+ * count for num_splits == 0 is kivi_decode_attn_rope_splits(); size the workspace with
+ * kivi_decode_attn_workspace(cache, q_heads, that count).  2-bit caches take token_cap
+ * <= 2^27 here (KIVI_ERR_UNSUPPORTED beyond).  One query head per workgroup; no ragged or
+ * fused-append form (append with kivi_append_flush, then call this). */
+int kivi_decode_attn_rope(const kivi_cache* cache, const uint16_t* q, int32_t q_heads, float sm_scale,
+                          float rope_base, uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
+                          int32_t num_splits, void* stream);
+
 /* One whole decode step: kivi_append_flush(cache, k_new, v_new, flushed, stream) followed by
  * kivi_decode_attn(cache, q, ...) on the updated cache, with the same arguments, results,
  * state update and errors as those two calls (record "KV bytes basis": the newest R tokens
@@ -245,6 +262,10 @@ int32_t kivi_decode_attn_splits(const kivi_cache* cache, int32_t q_heads);
 
 /* Workspace bytes kivi_decode_attn needs for this shape and split count (0 = auto). */
 size_t kivi_decode_attn_workspace(const kivi_cache* cache, int32_t q_heads, int32_t num_splits);
+
+/* Split count kivi_decode_attn_rope uses for num_splits == 0 (depends on shapes only);
+ * a negative KIVI_ERR_* code for an invalid shape or state. */
+int32_t kivi_decode_attn_rope_splits(const kivi_cache* cache, int32_t q_heads);
 
 /* Split count kivi_decode_attn_ragged uses for num_splits == 0 (shape only). */
 int32_t kivi_decode_attn_ragged_splits(const kivi_cache* cache, int32_t q_heads);

@@ -8,7 +8,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkivi.so")
 SOURCES = ["kivi_api.hip", "kivi_quant.hip", "kivi_attn.hip", "kivi_attn_gqa.hip", "kivi_attn_fp16.hip",
-           "kivi_attn_q4.hip"]
+           "kivi_attn_q4.hip", "kivi_attn_rope.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

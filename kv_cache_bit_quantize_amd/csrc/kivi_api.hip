@@ -23,6 +23,8 @@ constexpr int kMinGroupsPerSplit = 8;
 constexpr int kMinGroupsPerSplitSingle = 2 * kSqWaves;   // a pair of tiles for every wave
 
 constexpr int32_t kMaxTokenCap4 = 1 << 26;
+constexpr int32_t kMaxTokenCapRope2 = 1 << 27;   // 2-bit rows under 32-bit byte offsets (pre-RoPE kernel)
+constexpr int64_t kWavesRope = 4;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -195,6 +197,17 @@ void commit_state(kivi_cache* c, const kivi_cache& next) {
     c->n_quant = next.n_quant;
     c->n_res = next.n_res;
     c->res_head = next.res_head;
+}
+
+// Pre-RoPE attention: one query head per 4-wave workgroup, a key group for every wave.
+int32_t rope_auto_splits(const kivi_cache* c, int32_t q_heads) {
+    const int64_t rows = (int64_t)c->batch * q_heads;
+    const int64_t groups = c->n_quant / c->group;
+    int64_t s = (kTargetBlocks + rows - 1) / rows;
+    if (s > groups / kWavesRope) s = groups / kWavesRope;
+    if (s < 1) s = 1;
+    if (s > kMaxSplits) s = kMaxSplits;
+    return (int32_t)s;
 }
 
 // Validates a decode-attention call on cache state *c (or, with seq_state, on the
@@ -547,6 +560,36 @@ int kivi_decode_attn(const kivi_cache* c, const uint16_t* q, int32_t q_heads, fl
     hipEvent_t t0, t1;
     take_timing(&t0, &t1);
     return hip_status(launch_decode_attn(a, (hipStream_t)stream, t0, t1));
+}
+
+int kivi_decode_attn_rope(const kivi_cache* c, const uint16_t* q, int32_t q_heads, float sm_scale,
+                          float rope_base, uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
+                          int32_t num_splits, void* stream) {
+    if (!std::isfinite(rope_base) || !(rope_base > 0.0f)) return KIVI_ERR_SHAPE;
+    int st = check_shape(c);
+    if (st != KIVI_OK) return st;
+    if (!(c->flags & KIVI_CODES_4BIT) && c->token_cap > kMaxTokenCapRope2) return KIVI_ERR_UNSUPPORTED;
+    if ((st = check_state(c)) != KIVI_OK) return st;
+    if (q_heads <= 0 || q_heads % c->kv_heads != 0) return KIVI_ERR_SHAPE;
+    if (num_splits < 0 || num_splits > kMaxSplits) return KIVI_ERR_SHAPE;
+    AttnArgs a;
+    st = prepare_attn(c, q, q_heads, sm_scale, out, lse, workspace, workspace_bytes,
+                      num_splits > 0 ? num_splits : rope_auto_splits(c, q_heads), &a);
+    if (st != KIVI_OK) return st;
+    a.nq = 1;
+    a.block_rows = a.q_rows;
+    a.rope_base = (double)rope_base;
+    hipEvent_t t0, t1;
+    take_timing(&t0, &t1);
+    return hip_status(launch_decode_attn_rope(a, (hipStream_t)stream, t0, t1));
+}
+
+int32_t kivi_decode_attn_rope_splits(const kivi_cache* c, int32_t q_heads) {
+    int st = check_shape(c);
+    if (st != KIVI_OK) return st;
+    if ((st = check_state(c)) != KIVI_OK) return st;
+    if (q_heads <= 0 || q_heads % c->kv_heads != 0) return KIVI_ERR_SHAPE;
+    return rope_auto_splits(c, q_heads);
 }
 
 int kivi_decode_step(kivi_cache* c, const uint16_t* k_new, const uint16_t* v_new, const uint16_t* q,

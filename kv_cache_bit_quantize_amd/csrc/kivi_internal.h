@@ -54,6 +54,7 @@ struct AppendArgs {
     int32_t group;              // tokens per key group (= channels per value group): 32, 64 or 128
     int32_t flush_all;          // a flush moves the whole residual (else its oldest group)
     int32_t bits;               // code width: 2 or 4
+    double rope_base;           // pre-RoPE keys (kivi_decode_attn_rope): the rotary base, else 0
 };
 
 struct AttnArgs {
@@ -97,6 +98,7 @@ struct AttnArgs {
     int32_t slot_budget;        // ragged batch: workgroups resident at once (the plan's target)
     int32_t group;              // tokens per key group (= channels per value group): 32, 64 or 128
     int32_t bits;               // code width: 2 or 4
+    double rope_base;           // pre-RoPE keys (kivi_decode_attn_rope): the rotary base, else 0
 };
 
 // bits of a sequence's flags word (ragged calls; only ever set, by the kernels)
@@ -114,6 +116,7 @@ hipError_t launch_append_flush_ragged(const AppendArgs& a, int32_t batch, hipStr
 hipError_t launch_decode_attn(const AttnArgs& a, hipStream_t s, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 hipError_t launch_decode_attn_gqa(const AttnArgs& a, hipStream_t s, hipEvent_t t0 = nullptr,
                                   hipEvent_t t1 = nullptr);
+hipError_t launch_decode_attn_rope(const AttnArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
 hipError_t launch_decode_attn_q4(const AttnArgs& a, hipStream_t s, hipEvent_t t0 = nullptr,
                                  hipEvent_t t1 = nullptr);
 hipError_t launch_decode_attn_fp16(const AttnArgs& a, hipStream_t s, hipEvent_t t0 = nullptr,

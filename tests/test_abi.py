@@ -21,7 +21,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 17
+    assert len(names) == 19
     out = os.popen(f"nm -D --defined-only {kivi.LIB_PATH}").read()
     exported = set(re.findall(r" T (kivi_\w+)$", out, re.M))
     assert set(names) <= exported, set(names) - exported
@@ -283,3 +283,30 @@ def test_split_selection_and_workspace():
     c = _cache(n_quant=32, n_res=0)
     assert L.kivi_decode_attn_splits(C.byref(c), 2) == 1
     assert L.kivi_decode_attn_workspace(C.byref(c), 2, 7) == 256 + ((7 * 2 * 2 * 130 * 8 + 255) // 256) * 256
+
+
+def test_rope_attention_arguments():
+    """kivi_decode_attn_rope rejects bad arguments on the host (no kernel is launched)."""
+    f = L.kivi_decode_attn_rope
+    c = _cache()
+    P = C.c_void_p(FAKE)
+    ws = C.c_void_p(FAKE)
+    big = 1 << 30
+    for base in (0.0, -1.0, float("nan"), float("inf")):
+        assert f(C.byref(c), P, 4, 0.1, base, P, None, ws, big, 0, None) == -2
+    assert f(C.byref(c), None, 4, 0.1, 10000.0, P, None, ws, big, 0, None) == -1
+    assert f(C.byref(c), P, 3, 0.1, 10000.0, P, None, ws, big, 0, None) == -2      # q_heads % kv_heads
+    assert f(C.byref(c), P, 4, 0.1, 10000.0, P, None, ws, 16, 0, None) == -5       # workspace too small
+    assert f(C.byref(_cache(head_dim=64)), P, 4, 0.1, 10000.0, P, None, ws, big, 0, None) == -3
+    # 2-bit rows beyond 2^27 tokens are not addressed by this kernel
+    assert f(C.byref(_cache(token_cap=(1 << 27) + 32)), P, 4, 0.1, 10000.0, P, None, ws, big, 0, None) == -3
+    assert f(C.byref(_cache(n_quant=40)), P, 4, 0.1, 10000.0, P, None, ws, big, 0, None) == -7
+
+
+def test_rope_splits():
+    c = _cache(batch=1, kv_heads=32, token_cap=131072, n_quant=131040, n_res=32)
+    s = L.kivi_decode_attn_rope_splits(C.byref(c), 32)
+    assert s == 768 // 32                              # 4-wave workgroups, 768 at once
+    small = _cache(token_cap=256, n_quant=64, n_res=10)
+    assert L.kivi_decode_attn_rope_splits(C.byref(small), 4) == 1   # two key groups: fewer than the 4 waves
+    assert L.kivi_decode_attn_rope_splits(C.byref(c), 33) == -2

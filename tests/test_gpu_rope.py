@@ -1,0 +1,107 @@
+"""GPU parity of attention over pre-RoPE keys (kivi_decode_attn_rope) against the oracle's
+kivi_ref_decode_attn_rope: keys dequantized, turned by the rotary embedding at their
+sequence positions, dense fp64 attention.  Bar: per row max |o_gpu - o_ref| / max |o_ref|
+<= 2e-3, lse within 2e-3 + 2^-18 |lse|.  Covers both code widths, the three group sizes,
+MHA and GQA, explicit split counts, caches with only history or only residual, a decode
+loop whose flushes move the residual ring, another rotary base, and the 131,072-token
+shape (angles past 10^5 radians) on sampled rows."""
+import numpy as np
+import pytest
+import torch
+
+from kivi_testlib import assert_attn_close, assert_lse_close, bits, gpu_or_skip, ref_cache
+from kv_cache_bit_quantize_amd import synth
+
+pytestmark = pytest.mark.gpu
+SM = synth.SM_SCALE_D128
+D = 128
+BASE = 10000.0
+
+
+def _kivi():
+    from kv_cache_bit_quantize_amd import kivi
+    return kivi
+
+
+def _setup(w, dev, code_bits=2):
+    kivi = _kivi()
+    k, v = synth.prefill_kv(w, device=dev)
+    cache = kivi.Cache(w.batch, w.kv_heads, w.token_cap, group=w.group, residual_cap=w.residual_cap, device=dev,
+                       bits=code_bits)
+    kivi.kivi_prefill(k, v, w.n_quant, cache)
+    torch.cuda.synchronize()
+    rc = ref_cache(w.batch, w.kv_heads, w.token_cap, k.cpu(), v.cpu(), w.n_quant, residual_cap=w.residual_cap,
+                   group=w.group, bits=code_bits)
+    return cache, rc
+
+
+def _check(cache, rc, q, base=BASE, splits=0, rows=None, what=""):
+    out, lse = _kivi().kivi_decode_attn_rope(cache, q, SM, base, lse=True, num_splits=splits)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = rc.decode_attn_rope(bits(q), SM, base, rows=rows)
+    assert_attn_close(out, ref_out, rows=rows, what=what)
+    assert_lse_close(lse, ref_lse, rows=rows)
+
+
+@pytest.mark.parametrize("code_bits", [2, 4])
+@pytest.mark.parametrize("G", [32, 64, 128])
+@pytest.mark.parametrize("q_heads,kv_heads,splits", [(4, 4, 0), (8, 2, 0), (6, 2, 3), (2, 2, 7)])
+def test_attention(code_bits, G, q_heads, kv_heads, splits):
+    dev = gpu_or_skip()
+    w = synth.small(seed=600 + G + q_heads + splits, batch=2, q_heads=q_heads, kv_heads=kv_heads,
+                    context=16 * G + 77, n_quant=16 * G, group=G)
+    cache, rc = _setup(w, dev, code_bits)
+    _check(cache, rc, synth.query(w, device=dev), splits=splits,
+           what=f"rope {code_bits}-bit G={G} {q_heads}/{kv_heads} splits={splits}")
+
+
+@pytest.mark.parametrize("code_bits", [2, 4])
+def test_residual_only_and_history_only(code_bits):
+    dev = gpu_or_skip()
+    for nq, ctx in ((0, 100), (512, 512), (32, 33)):
+        w = synth.small(seed=620 + nq + ctx, batch=1, q_heads=4, kv_heads=2, context=ctx, n_quant=nq)
+        cache, rc = _setup(w, dev, code_bits)
+        _check(cache, rc, synth.query(w, device=dev), what=f"rope {code_bits}-bit n_quant={nq} context={ctx}")
+
+
+def test_other_base():
+    dev = gpu_or_skip()
+    w = synth.small(seed=630, batch=1, q_heads=4, kv_heads=4, context=2048 + 50, n_quant=2048)
+    cache, rc = _setup(w, dev)
+    _check(cache, rc, synth.query(w, device=dev), base=500000.0, what="rope base 5e5")
+
+
+@pytest.mark.parametrize("code_bits,G,R", [(2, 32, 128), (4, 64, 128), (2, 32, 64)])
+def test_decode_loop(code_bits, G, R):
+    """append_flush then attention each step: flushes move tokens from the ring (positions
+    n_quant + i) into the history (positions t) and the ring head advances."""
+    dev = gpu_or_skip()
+    kivi = _kivi()
+    steps = R + 40
+    w = synth.small(seed=640 + G + R, batch=2, q_heads=8, kv_heads=2, context=4 * G + R - 7, n_quant=4 * G,
+                    group=G, residual_cap=R, decode_steps=steps + R)
+    cache, rc = _setup(w, dev, code_bits)
+    for s in range(steps):
+        kn, vn = synth.step_kv(w, s, device=dev)
+        kivi.kivi_append_flush(cache, kn, vn)
+        rc.append(bits(kn).reshape(-1, D), bits(vn).reshape(-1, D))
+        assert cache.state == (rc.n_quant, rc.n_res, rc.res_head), s
+        _check(cache, rc, synth.query(w, step=s + 1, device=dev), what=f"rope loop {code_bits}-bit step {s}")
+
+
+def test_long_context_sampled_rows():
+    """131,072 tokens, positions up to 131,071 (pair 0 turns 1 radian per position)."""
+    dev = gpu_or_skip()
+    kivi = _kivi()
+    w = synth.WORKLOADS["long-128k"]
+    k, v = synth.prefill_kv(w, device=dev)
+    cache = kivi.Cache(w.batch, w.kv_heads, w.token_cap, device=dev)
+    kivi.kivi_prefill(k, v, w.n_quant, cache)
+    q = synth.query(w, device=dev)
+    out, lse = kivi.kivi_decode_attn_rope(cache, q, SM, BASE, lse=True)
+    torch.cuda.synchronize()
+    rows = [0, 13, 31]
+    rc = ref_cache(1, len(rows), w.token_cap, k[0, rows].cpu()[None], v[0, rows].cpu()[None], w.n_quant)
+    ref_out, ref_lse = rc.decode_attn_rope(bits(q[:, rows].contiguous()), SM, BASE)
+    assert_attn_close(out[:, rows], ref_out, what="rope long-128k sampled rows")
+    assert_lse_close(lse[:, rows], ref_lse)
