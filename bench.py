@@ -15,8 +15,9 @@ beside it ("fp16_comparator"; --no-fp16 skips it), and so is the ragged-batch pa
 serving batch of 64 sequences at different lengths ("ragged_batch"; --no-ragged skips it),
 attention alone over the same context quantized at group sizes 64 and 128
 ("group_sizes"; --sweep-groups sets the list, --group the timed cache's own group size),
-and attention alone over the same context in 4-bit codes ("four_bit"; --four-bit-groups
-sets its group sizes, empty skips it).
+attention alone over the same context in 4-bit codes ("four_bit"; --four-bit-groups
+sets its group sizes, empty skips it), and attention over the same context stored as
+pre-RoPE keys, turned at their positions inside the kernel ("pre_rope"; --no-rope skips it).
 """
 import argparse
 import json
@@ -162,12 +163,20 @@ def ragged_measure(kivi, synth, dev, steps, warmup, seed=2402):
     }
 
 
-def time_attention(kivi, cache, queries, sm, steps, warmup):
-    """Mean duration (us) of kivi_decode_attn launches, kernel-recorded events."""
+def time_attention(kivi, cache, queries, sm, steps, warmup, rope_base=None):
+    """Mean duration (us) of kivi_decode_attn (or, with rope_base, kivi_decode_attn_rope)
+    launches, kernel-recorded events."""
     out = torch.empty_like(queries[0])
-    ws = cache.workspace(queries[0].shape[1])
+    hq = queries[0].shape[1]
+    if rope_base is None:
+        ws = cache.workspace(hq)
+        call = lambda q: kivi.kivi_decode_attn(cache, q, sm, out=out, workspace=ws)
+    else:
+        splits = kivi.kivi_decode_attn_rope_splits(cache, hq)
+        ws = cache.workspace(hq, splits)
+        call = lambda q: kivi.kivi_decode_attn_rope(cache, q, sm, rope_base, out=out, num_splits=splits, workspace=ws)
     for s in range(warmup):
-        kivi.kivi_decode_attn(cache, queries[s], sm, out=out, workspace=ws)
+        call(queries[s])
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     for pair in ev:
         for e in pair:
@@ -175,9 +184,26 @@ def time_attention(kivi, cache, queries, sm, steps, warmup):
     torch.cuda.synchronize()
     for i in range(steps):
         kivi.kivi_time_next_attention(*ev[i])
-        kivi.kivi_decode_attn(cache, queries[warmup + i], sm, out=out, workspace=ws)
+        call(queries[warmup + i])
     torch.cuda.synchronize()
     return float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+
+
+def rope_measure(kivi, synth, w, k, v, queries, steps, warmup, base=10000.0):
+    """Attention over the same prefill stored as pre-RoPE keys (2-bit, G = 32), each key
+    turned at its position inside the kernel.  Same algorithmic bytes as the plain call; the
+    kernel is bound by its vector work, reported against the HBM peak like the others."""
+    nq = (w.context - 32) // 32 * 32
+    cache = kivi.Cache(w.batch, w.kv_heads, w.token_cap, device=k.device)
+    kivi.kivi_prefill(k, v, nq, cache)
+    us = time_attention(kivi, cache, queries, synth.SM_SCALE_D128, steps, warmup, rope_base=base)
+    b = attn_bytes(w, nq, w.context - nq)
+    res = {"kernel": "attn_rope_kernel", "rope_base": base, "n_quant": nq, "n_res": w.context - nq,
+           "splits": kivi.kivi_decode_attn_rope_splits(cache, w.q_heads), "decode_attn_us": round(us, 2),
+           "bytes_per_launch": int(b), "achieved": round(b / us / 1e3, 1), "unit": "GB/s",
+           "frac": round(b / us / 1e3 / PEAK_HBM_GBS, 4)}
+    del cache
+    return res
 
 
 def group_sweep(kivi, synth, w, k, v, queries, steps, warmup, groups, bits=2):
@@ -230,6 +256,7 @@ def main():
     ap.add_argument("--group", type=int, default=32, help="group size of the timed cache (32, 64 or 128)")
     ap.add_argument("--sweep-groups", default="64,128",
                     help="group sizes of the attention-only sweep (comma list; empty: skip)")
+    ap.add_argument("--no-rope", action="store_true", help="skip the pre-RoPE attention measurement")
     ap.add_argument("--four-bit-groups", default="32",
                     help="group sizes of the 4-bit attention-only measurement (comma list; empty: skip)")
     args = ap.parse_args()
@@ -373,6 +400,7 @@ def main():
         "ragged_batch": None,
         "group_sizes": None,
         "four_bit": None,
+        "pre_rope": None,
     }
     del cache, ws
     groups = [int(x) for x in args.sweep_groups.split(",") if x.strip()]
@@ -381,6 +409,8 @@ def main():
     groups4 = [int(x) for x in args.four_bit_groups.split(",") if x.strip()]
     if groups4:
         res["four_bit"] = group_sweep(kivi, synth, w, k, v, queries, args.steps, args.warmup, groups4, bits=4)
+    if not args.no_rope:
+        res["pre_rope"] = rope_measure(kivi, synth, w, k, v, queries, args.steps, args.warmup)
     if not args.no_ragged:
         res["ragged_batch"] = ragged_measure(kivi, synth, dev, args.steps, args.warmup)
     if args.cpu_heads > 0:
