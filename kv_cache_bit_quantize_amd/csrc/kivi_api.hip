@@ -19,12 +19,14 @@ namespace {
 constexpr int64_t kTargetBlocks = 768;         // 256-thread workgroups: three per CU
 constexpr int64_t kTargetBlocksGroup = 512;    // query-group workgroups
 constexpr int64_t kTargetBlocksSingle = 256;   // single-query 2-bit workgroups (12 waves): one per CU
+constexpr int64_t kTargetBlocksQ4 = 1024;      // single-query 4-bit workgroups (4 waves): four per CU
 constexpr int kMinGroupsPerSplit = 8;
 constexpr int kMinGroupsPerSplitSingle = 2 * kSqWaves;   // a pair of tiles for every wave
 
 constexpr int32_t kMaxTokenCap4 = 1 << 26;
 constexpr int32_t kMaxTokenCapRope2 = 1 << 27;   // 2-bit rows under 32-bit byte offsets (pre-RoPE kernel)
 constexpr int64_t kWavesRope = 4;
+constexpr int64_t kTargetBlocksRope = 768;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -96,7 +98,9 @@ int32_t auto_splits_for(const kivi_cache* c, int32_t q_heads, int64_t groups) {
     int64_t target = group ? kTargetBlocksGroup : kTargetBlocksSingle;
     int64_t min_tiles = group ? kMinGroupsPerSplit : kMinGroupsPerSplitSingle;
     if (code_bits(c) == 4) {   // 4-wave workgroups, a key group for every wave
-        target = group ? kTargetBlocksGroup : kTargetBlocks;
+        // one query head: four workgroups per CU (88 VGPRs; at 131,072 tokens 32 splits took
+        // 124-128 us against 129-146 us for 24 on three boxes)
+        target = group ? kTargetBlocksGroup : kTargetBlocksQ4;
         min_tiles = 4 * (c->group / kG);
     }
     int64_t s = (target + rows - 1) / rows;
@@ -199,11 +203,13 @@ void commit_state(kivi_cache* c, const kivi_cache& next) {
     c->res_head = next.res_head;
 }
 
-// Pre-RoPE attention: one query head per 4-wave workgroup, a key group for every wave.
+// Pre-RoPE attention: one query head per 4-wave workgroup, a key group for every wave, and
+// one round of three workgroups per CU (the kernel's 157-164 VGPRs leave room for three; at
+// 131,072 tokens and 32 heads 24 splits took 168 us, 16 splits 201 us, 32 splits 190 us).
 int32_t rope_auto_splits(const kivi_cache* c, int32_t q_heads) {
     const int64_t rows = (int64_t)c->batch * q_heads;
     const int64_t groups = c->n_quant / c->group;
-    int64_t s = (kTargetBlocks + rows - 1) / rows;
+    int64_t s = (kTargetBlocksRope + rows - 1) / rows;
     if (s > groups / kWavesRope) s = groups / kWavesRope;
     if (s < 1) s = 1;
     if (s > kMaxSplits) s = kMaxSplits;

@@ -115,6 +115,7 @@ __global__ __launch_bounds__(kBlock) void attn_rope_kernel(AttnArgs a) {
     __shared__ __align__(16) float2 sh_ed[GS][kRpPairs];     // exp(i*d*w) for offsets d < G
     __shared__ __align__(16) float2 sh_e0[kWaves][kRpPairs]; // exp(i*t0*w) of the wave's group
     __shared__ __align__(16) float sh_p[kWaves][kRpTok];
+    __shared__ __align__(16) float sh_ps[kWaves][kD / GS][kRpTok];   // 2-bit: p*s per (value group, token)
     __shared__ __align__(16) float sh_o[1][kSlots][kD];
     __shared__ float sh_m[1][kSlots], sh_l[1][kSlots];
 
@@ -186,14 +187,19 @@ __global__ __launch_bounds__(kBlock) void attn_rope_kernel(AttnArgs a) {
     // P.V lanes.  2-bit: lane (kk, n, hh) reads bytes 8hh..8hh+7 of chunk (16k + n) of the
     // tile, k = 2*(t0%32/16) + kk: tokens 8kk + 4h + i of the iteration (h = 0..1, i = 0..3)
     // and channels n + 16(4hh + m) (m = 0..3, in word m/2, byte 2h + m%2, bits 2i); with
-    // G = 32 channels m = 0, 1 are in value group 2hh and m = 2, 3 in group 2hh + 1.
+    // G = 32 channels m = 0, 1 are in value group 2hh and m = 2, 3 in group 2hh + 1.  Each
+    // (token, value group) of the iteration has one lane of the softmax octets that loads its
+    // (scale, zero) word and forms p*s (into LDS) and p*z (summed in that lane): octet t8,
+    // lane k8 < 2*NG takes token t8 + 8*(k8 / NG) and group k8 % NG (NG = 128/G groups).
     // 4-bit: lane (vg, vc) reads tokens 4vg..4vg+3 and channels 8vc..8vc+7 (one group).
-    constexpr int kVTok = BITS == 2 ? 8 : 4;              // P.V tokens per lane
+    constexpr int kNG = kD / GS;                          // value groups per token
     constexpr int kVGrp = (BITS == 2 && GS == 32) ? 2 : 1;  // value groups per lane and token
     constexpr int kVCh = BITS == 2 ? 4 : 8;               // channels per lane
     const int kk = lane >> 5, vn = (lane >> 1) & 15, hh = lane & 1;
     const int vg = lane >> 4, vc = lane & 15;
-    struct VLoad { uint32_t c[4]; uint32_t p[kVTok * kVGrp]; };
+    const bool combo = BITS == 2 && k8 < 2 * kNG;
+    const int c_tok = t8 + 8 * (min(k8, 2 * kNG - 1) / kNG), c_grp = min(k8, 2 * kNG - 1) % kNG;
+    struct VLoad { uint32_t c[4]; uint32_t p[4]; };
     auto load_v = [&](VLoad& L, int it) {
         const uint32_t t0 = (uint32_t)tok(it);
         if constexpr (BITS == 2) {
@@ -201,21 +207,11 @@ __global__ __launch_bounds__(kBlock) void attn_rope_kernel(AttnArgs a) {
             const uint2 x = *reinterpret_cast<const uint2*>(vc_row + off);
             L.c[0] = x.x;
             L.c[1] = x.y;
-#pragma unroll
-            for (int u = 0; u < kVTok; ++u) {
-                const uint32_t tt = t0 + 8 * kk + u;
-                if constexpr (GS == 32) {
-                    const uint2 y = *reinterpret_cast<const uint2*>(vp_row + tt * 4 + 2 * hh);
-                    L.p[2 * u] = y.x;
-                    L.p[2 * u + 1] = y.y;
-                } else {
-                    L.p[u] = vp_row[tt * (kD / GS) + (GS == 64 ? hh : 0)];
-                }
-            }
+            L.p[0] = vp_row[(t0 + c_tok) * kNG + c_grp];   // this lane's (token, group) pair
         } else {
             const uint32_t t = t0 + 4 * vg;
 #pragma unroll
-            for (int u = 0; u < kVTok; ++u) {
+            for (int u = 0; u < 4; ++u) {
                 L.c[u] = *reinterpret_cast<const uint32_t*>(vc_row + (t + u) * kRowBytes4 + 4 * vc);
                 L.p[u] = vp_row[(t + u) * (kD / GS) + (8 * vc) / GS];
             }
@@ -236,11 +232,9 @@ __global__ __launch_bounds__(kBlock) void attn_rope_kernel(AttnArgs a) {
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     };
 
-    float m = -INFINITY, lsum = 0.0f, o[kVCh], oz[kVGrp];
+    float m = -INFINITY, lsum = 0.0f, o[kVCh], oz = 0.0f;   // oz: 2-bit, the lane's (token, group) p*z; 4-bit, its tokens'
 #pragma unroll
     for (int c = 0; c < kVCh; ++c) o[c] = 0.0f;
-#pragma unroll
-    for (int g = 0; g < kVGrp; ++g) oz[g] = 0.0f;
     float* pw = &sh_p[wave][0];
 
     uint32_t tag;
@@ -314,8 +308,7 @@ __global__ __launch_bounds__(kBlock) void attn_rope_kernel(AttnArgs a) {
                     const float al = m == -INFINITY ? 0.0f : exp2f(m - mnew);
 #pragma unroll
                     for (int c = 0; c < kVCh; ++c) o[c] *= al;
-#pragma unroll
-                    for (int g = 0; g < kVGrp; ++g) oz[g] *= al;
+                    oz *= al;
                     lsum *= al;
                     m = mnew;
                 }
@@ -325,29 +318,38 @@ __global__ __launch_bounds__(kBlock) void attn_rope_kernel(AttnArgs a) {
                     pw[t8] = p0;
                     pw[8 + t8] = p1;
                 }
+                if constexpr (BITS == 2) {
+                    if (combo) {
+                        const float pc = c_tok < 8 ? p0 : p1;
+                        sh_ps[wave][c_grp][c_tok] = pc * h2f(vl.p[0] & 0xffffu);
+                        oz = fmaf(pc, h2f(vl.p[0] >> 16), oz);
+                    }
+                }
                 wave_sync();
                 // ---- P.V, dequantization folded: (p*s)*c + p*z
                 if constexpr (BITS == 2) {
-                    const float4 pa = *reinterpret_cast<const float4*>(pw + 8 * kk);
-                    const float4 pb = *reinterpret_cast<const float4*>(pw + 8 * kk + 4);
-                    const float pt[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+                    // p*s of the lane's 8 tokens in each of its value groups
+                    float ps[kVGrp][8];
 #pragma unroll
-                    for (int h = 0; h < 2; ++h) {
+                    for (int g = 0; g < kVGrp; ++g) {
+                        const int grp = GS == 32 ? 2 * hh + g : (GS == 64 ? hh : 0);
+                        const float4 a0 = *reinterpret_cast<const float4*>(&sh_ps[wave][grp][8 * kk]);
+                        const float4 a1 = *reinterpret_cast<const float4*>(&sh_ps[wave][grp][8 * kk + 4]);
+                        ps[g][0] = a0.x; ps[g][1] = a0.y; ps[g][2] = a0.z; ps[g][3] = a0.w;
+                        ps[g][4] = a1.x; ps[g][5] = a1.y; ps[g][6] = a1.z; ps[g][7] = a1.w;
+                    }
+#pragma unroll
+                    for (int w2 = 0; w2 < 2; ++w2) {
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
-                            const int u = 4 * h + i;
-                            float ps[kVGrp];
+                            // token field i of word w2: byte 2h + e = channel 2*w2 + e, token 4h + i
+                            uint32_t y = (vl.c[w2] >> (2 * i)) & 0x03030303u;
+                            asm volatile("" : "+v"(y));   // one v_cvt_f32_ubyteN per code
 #pragma unroll
-                            for (int g = 0; g < kVGrp; ++g) {
-                                const uint32_t pr = vl.p[kVGrp * u + g];
-                                ps[g] = pt[u] * h2f(pr & 0xffffu);
-                                oz[g] = fmaf(pt[u], h2f(pr >> 16), oz[g]);
-                            }
-#pragma unroll
-                            for (int mm = 0; mm < 4; ++mm) {
-                                const uint32_t code = (vl.c[mm >> 1] >> (8 * (2 * h + (mm & 1)) + 2 * i)) & 3u;
-                                const int g = kVGrp == 2 ? (mm >> 1) : 0;
-                                o[mm] = fmaf(ps[g], (float)code, o[mm]);
+                            for (int b = 0; b < 4; ++b) {
+                                const int mm = 2 * w2 + (b & 1), u = 4 * (b >> 1) + i;
+                                const int g = kVGrp == 2 ? w2 : 0;
+                                o[mm] = fmaf(ps[g][u], (float)((y >> (8 * b)) & 0xFFu), o[mm]);
                             }
                         }
                     }
@@ -358,7 +360,7 @@ __global__ __launch_bounds__(kBlock) void attn_rope_kernel(AttnArgs a) {
                     for (int u = 0; u < 4; ++u) {
                         const float s = h2f(vl.p[u] & 0xffffu), z = h2f(vl.p[u] >> 16);
                         const float ps = pt[u] * s;
-                        oz[0] = fmaf(pt[u], z, oz[0]);
+                        oz = fmaf(pt[u], z, oz);
                         uint32_t lo = vl.c[u] & 0x0F0F0F0Fu, hi = (vl.c[u] >> 4) & 0x0F0F0F0Fu;
                         asm volatile("" : "+v"(lo), "+v"(hi));
 #pragma unroll
@@ -378,16 +380,30 @@ __global__ __launch_bounds__(kBlock) void attn_rope_kernel(AttnArgs a) {
 
     // ---- the wave's state: p*z shares added to their channels, lanes of a channel summed
     if constexpr (BITS == 2) {
+        // sum of p*z per value group over the wave's tokens, then the lane's groups picked by
+        // compare-and-select (an index from hh would put the array in scratch memory)
+        float zl[kVGrp];
+#pragma unroll
+        for (int g2 = 0; g2 < kVGrp; ++g2) zl[g2] = 0.0f;
+#pragma unroll
+        for (int g = 0; g < kNG; ++g) {
+            const float t = wave_sum(combo && c_grp == g ? oz : 0.0f);
+#pragma unroll
+            for (int g2 = 0; g2 < kVGrp; ++g2) {
+                const int want = GS == 32 ? 2 * hh + g2 : (GS == 64 ? hh : 0);
+                zl[g2] = g == want ? t : zl[g2];
+            }
+        }
 #pragma unroll
         for (int mm = 0; mm < 4; ++mm) {
-            float x = o[mm] + oz[kVGrp == 2 ? (mm >> 1) : 0];
+            float x = o[mm];
             x += __shfl_xor(x, 32, 64);                  // the two 8-token rows (kk)
-            if (kk == 0) sh_o[0][wave][vn + 16 * (4 * hh + mm)] = x;
+            if (kk == 0) sh_o[0][wave][vn + 16 * (4 * hh + mm)] = x + zl[kVGrp == 2 ? (mm >> 1) : 0];
         }
     } else {
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-            float x = o[c] + oz[0];
+            float x = o[c] + oz;
             x += xor16_f(x);
             x += __shfl_xor(x, 32, 64);                  // the four token quads (vg)
             if (lane < 16) sh_o[0][wave][8 * vc + c] = x;

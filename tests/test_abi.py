@@ -306,7 +306,7 @@ def test_rope_attention_arguments():
 def test_rope_splits():
     c = _cache(batch=1, kv_heads=32, token_cap=131072, n_quant=131040, n_res=32)
     s = L.kivi_decode_attn_rope_splits(C.byref(c), 32)
-    assert s == 768 // 32                              # 4-wave workgroups, 768 at once
+    assert s == 768 // 32                              # 4-wave workgroups, three per CU
     small = _cache(token_cap=256, n_quant=64, n_res=10)
     assert L.kivi_decode_attn_rope_splits(C.byref(small), 4) == 1   # two key groups: fewer than the 4 waves
     assert L.kivi_decode_attn_rope_splits(C.byref(c), 33) == -2
