@@ -56,8 +56,16 @@ MUTATIONS = [
     ("no_softmax_scale", "logit[t] = sm_scale * acc;", "logit[t] = acc;", False),
     ("no_normalisation", "for (int32_t j = 0; j < d; ++j) out[j] /= l;", "", False),
     ("lse_without_max", "if (lse) *lse = m + log(l);", "if (lse) *lse = log(l);", False),
-    ("gqa_modulo_mapping", "int64_t kv_row = b * c->kv_heads + hq / ratio;",
-     "int64_t kv_row = b * c->kv_heads + hq % c->kv_heads;", False),
+    ("gqa_modulo_mapping",
+     "int64_t kv_row = b * c->kv_heads + hq / ratio;\n        if (kv_row != last_kv_row) {\n"
+     "            kivi_ref_dequant_row(c, (int32_t)kv_row, K, V);\n            last_kv_row = kv_row;",
+     "int64_t kv_row = b * c->kv_heads + hq % c->kv_heads;\n        if (kv_row != last_kv_row) {\n"
+     "            kivi_ref_dequant_row(c, (int32_t)kv_row, K, V);\n            last_kv_row = kv_row;", False),
+    ("rope_gqa_modulo_mapping",
+     "int64_t kv_row = b * c->kv_heads + hq / ratio;\n        if (kv_row != last_kv_row) {\n"
+     "            kivi_ref_dequant_row(c, (int32_t)kv_row, K, V);\n            for (int32_t t = 0;",
+     "int64_t kv_row = b * c->kv_heads + hq % c->kv_heads;\n        if (kv_row != last_kv_row) {\n"
+     "            kivi_ref_dequant_row(c, (int32_t)kv_row, K, V);\n            for (int32_t t = 0;", False),
     ("flush_newest_tokens", "int32_t slot = (c->res_head + i) % R;",
      "int32_t slot = (c->res_head + R - G + i) % R;", False),
     ("ring_head_not_advanced", "c->res_head = (c->res_head + G) % R;", "", False),
