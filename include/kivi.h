@@ -174,11 +174,21 @@ int kivi_decode_attn(const kivi_cache* cache, const uint16_t* q, int32_t q_heads
  * given: the caller rotates it at its own position.  Values are not rotated.  The split
  * count for num_splits == 0 is kivi_decode_attn_rope_splits(); size the workspace with
  * kivi_decode_attn_workspace(cache, q_heads, that count).  2-bit caches take token_cap
- * <= 2^27 here (KIVI_ERR_UNSUPPORTED beyond).  One query head per workgroup; no ragged or
- * fused-append form (append with kivi_append_flush, then call this). */
+ * <= 2^27 here (KIVI_ERR_UNSUPPORTED beyond).  One query head per workgroup; no fused-append
+ * form (append with kivi_append_flush, then call this). */
 int kivi_decode_attn_rope(const kivi_cache* cache, const uint16_t* q, int32_t q_heads, float sm_scale,
                           float rope_base, uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
                           int32_t num_splits, void* stream);
+
+/* kivi_decode_attn_rope for a ragged batch (per-sequence states as for
+ * kivi_decode_attn_ragged): each sequence's keys are turned at that sequence's own positions
+ * (history token t at t, the i-th oldest residual token at its n_quant + i).  num_splits == 0:
+ * kivi_decode_attn_rope_ragged_splits; size the workspace with kivi_decode_attn_workspace(cache,
+ * q_heads, that count).  A sequence with an empty context gets out = 0 and lse = -inf; a
+ * state out of range is skipped and flagged KIVI_SEQ_BAD_STATE. */
+int kivi_decode_attn_rope_ragged(const kivi_cache* cache, int32_t* seq_state, const uint16_t* q, int32_t q_heads,
+                                 float sm_scale, float rope_base, uint16_t* out, float* lse, void* workspace,
+                                 size_t workspace_bytes, int32_t num_splits, void* stream);
 
 /* One whole decode step: kivi_append_flush(cache, k_new, v_new, flushed, stream) followed by
  * kivi_decode_attn(cache, q, ...) on the updated cache, with the same arguments, results,
@@ -266,6 +276,9 @@ size_t kivi_decode_attn_workspace(const kivi_cache* cache, int32_t q_heads, int3
 /* Split count kivi_decode_attn_rope uses for num_splits == 0 (depends on shapes only);
  * a negative KIVI_ERR_* code for an invalid shape or state. */
 int32_t kivi_decode_attn_rope_splits(const kivi_cache* cache, int32_t q_heads);
+
+/* Split count kivi_decode_attn_rope_ragged uses for num_splits == 0 (shape only). */
+int32_t kivi_decode_attn_rope_ragged_splits(const kivi_cache* cache, int32_t q_heads);
 
 /* Split count kivi_decode_attn_ragged uses for num_splits == 0 (shape only). */
 int32_t kivi_decode_attn_ragged_splits(const kivi_cache* cache, int32_t q_heads);

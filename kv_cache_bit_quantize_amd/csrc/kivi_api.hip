@@ -206,10 +206,19 @@ void commit_state(kivi_cache* c, const kivi_cache& next) {
 // Pre-RoPE attention: one query head per 4-wave workgroup, a key group for every wave, and
 // one round of three workgroups per CU (the kernel's 157-164 VGPRs leave room for three; at
 // 131,072 tokens and 32 heads 24 splits took 168 us, 16 splits 201 us, 32 splits 190 us).
-int32_t rope_auto_splits(const kivi_cache* c, int32_t q_heads) {
+int32_t rope_splits_for(const kivi_cache* c, int32_t q_heads, int64_t groups) {
     const int64_t rows = (int64_t)c->batch * q_heads;
-    const int64_t groups = c->n_quant / c->group;
     int64_t s = (kTargetBlocksRope + rows - 1) / rows;
+    if (s > groups / kWavesRope) s = groups / kWavesRope;
+    if (s < 1) s = 1;
+    if (s > kMaxSplits) s = kMaxSplits;
+    return (int32_t)s;
+}
+int32_t rope_auto_splits(const kivi_cache* c, int32_t q_heads) { return rope_splits_for(c, q_heads, c->n_quant / c->group); }
+// ragged batch: room for four times the splits of the longest context the cache can hold
+int32_t rope_ragged_splits(const kivi_cache* c, int32_t q_heads) {
+    const int64_t groups = c->token_cap / c->group;
+    int64_t s = 4 * (int64_t)rope_splits_for(c, q_heads, groups);
     if (s > groups / kWavesRope) s = groups / kWavesRope;
     if (s < 1) s = 1;
     if (s > kMaxSplits) s = kMaxSplits;
@@ -568,26 +577,51 @@ int kivi_decode_attn(const kivi_cache* c, const uint16_t* q, int32_t q_heads, fl
     return hip_status(launch_decode_attn(a, (hipStream_t)stream, t0, t1));
 }
 
-int kivi_decode_attn_rope(const kivi_cache* c, const uint16_t* q, int32_t q_heads, float sm_scale,
-                          float rope_base, uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
-                          int32_t num_splits, void* stream) {
+// pre-RoPE attention, uniform (seq_state == nullptr) or ragged
+int decode_attn_rope(const kivi_cache* c, int32_t* seq_state, const uint16_t* q, int32_t q_heads, float sm_scale,
+                     float rope_base, uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
+                     int32_t num_splits, void* stream) {
     if (!std::isfinite(rope_base) || !(rope_base > 0.0f)) return KIVI_ERR_SHAPE;
     int st = check_shape(c);
     if (st != KIVI_OK) return st;
     if (!(c->flags & KIVI_CODES_4BIT) && c->token_cap > kMaxTokenCapRope2) return KIVI_ERR_UNSUPPORTED;
-    if ((st = check_state(c)) != KIVI_OK) return st;
+    if (seq_state == nullptr && (st = check_state(c)) != KIVI_OK) return st;
     if (q_heads <= 0 || q_heads % c->kv_heads != 0) return KIVI_ERR_SHAPE;
     if (num_splits < 0 || num_splits > kMaxSplits) return KIVI_ERR_SHAPE;
+    const int32_t splits =
+        num_splits > 0 ? num_splits : (seq_state != nullptr ? rope_ragged_splits(c, q_heads) : rope_auto_splits(c, q_heads));
     AttnArgs a;
-    st = prepare_attn(c, q, q_heads, sm_scale, out, lse, workspace, workspace_bytes,
-                      num_splits > 0 ? num_splits : rope_auto_splits(c, q_heads), &a);
+    st = prepare_attn(c, q, q_heads, sm_scale, out, lse, workspace, workspace_bytes, splits, &a, seq_state);
     if (st != KIVI_OK) return st;
     a.nq = 1;
     a.block_rows = a.q_rows;
+    a.slot_budget = (int32_t)kTargetBlocksRope;
     a.rope_base = (double)rope_base;
     hipEvent_t t0, t1;
     take_timing(&t0, &t1);
     return hip_status(launch_decode_attn_rope(a, (hipStream_t)stream, t0, t1));
+}
+
+int kivi_decode_attn_rope(const kivi_cache* c, const uint16_t* q, int32_t q_heads, float sm_scale,
+                          float rope_base, uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
+                          int32_t num_splits, void* stream) {
+    return decode_attn_rope(c, nullptr, q, q_heads, sm_scale, rope_base, out, lse, workspace, workspace_bytes,
+                            num_splits, stream);
+}
+
+int kivi_decode_attn_rope_ragged(const kivi_cache* c, int32_t* seq_state, const uint16_t* q, int32_t q_heads,
+                                 float sm_scale, float rope_base, uint16_t* out, float* lse, void* workspace,
+                                 size_t workspace_bytes, int32_t num_splits, void* stream) {
+    if (seq_state == nullptr) return KIVI_ERR_NULL;
+    return decode_attn_rope(c, seq_state, q, q_heads, sm_scale, rope_base, out, lse, workspace, workspace_bytes,
+                            num_splits, stream);
+}
+
+int32_t kivi_decode_attn_rope_ragged_splits(const kivi_cache* c, int32_t q_heads) {
+    const int st = check_shape(c);
+    if (st != KIVI_OK) return st;
+    if (q_heads <= 0 || q_heads % c->kv_heads != 0) return KIVI_ERR_SHAPE;
+    return rope_ragged_splits(c, q_heads);
 }
 
 int32_t kivi_decode_attn_rope_splits(const kivi_cache* c, int32_t q_heads) {

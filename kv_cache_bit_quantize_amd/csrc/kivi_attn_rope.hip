@@ -133,6 +133,7 @@ __global__ __launch_bounds__(kBlock) void attn_rope_kernel(AttnArgs a) {
     __syncthreads();
 
     const RowState rs = row_state(a, kvrow, split);
+    if (split >= rs.splits) return;   // (ragged batch) this row uses fewer splits: the whole workgroup leaves
     const int n_kg = rs.n_quant / GS;
     const int per_split = (n_kg + rs.splits - 1) / rs.splits;
     const int kg_lo = min(n_kg, split * per_split), kg_hi = min(n_kg, kg_lo + per_split);

@@ -20,7 +20,8 @@ EXPORTS = ["kivi_quantize_k_per_channel", "kivi_quantize_v_per_token", "kivi_pre
            "kivi_decode_attn", "kivi_decode_step", "kivi_decode_attn_splits", "kivi_decode_attn_workspace", "kivi_cache_bytes",
            "kivi_status_str", "kivi_time_next_attention", "kivi_decode_attn_fp16", "kivi_decode_attn_fp16_splits",
            "kivi_decode_attn_fp16_workspace", "kivi_append_flush_ragged", "kivi_decode_attn_ragged",
-           "kivi_decode_attn_ragged_splits", "kivi_decode_attn_rope", "kivi_decode_attn_rope_splits"]
+           "kivi_decode_attn_ragged_splits", "kivi_decode_attn_rope", "kivi_decode_attn_rope_splits",
+           "kivi_decode_attn_rope_ragged", "kivi_decode_attn_rope_ragged_splits"]
 
 KIVI_FLUSH_ALL = 1        # kivi_cache.flags: a full residual is flushed whole (else its oldest group)
 KIVI_CODES_4BIT = 2       # kivi_cache.flags: 4-bit codes (sixteen levels), token-major nibbles
@@ -67,6 +68,9 @@ def _load():
     L.kivi_decode_attn_ragged.argtypes = [cp, p, p, i32, C.c_float, p, p, p, C.c_size_t, i32, p]
     L.kivi_decode_attn_rope.argtypes = [cp, p, i32, C.c_float, C.c_float, p, p, p, C.c_size_t, i32, p]
     L.kivi_decode_attn_rope_splits.argtypes = [cp, i32]
+    L.kivi_decode_attn_rope_ragged.argtypes = [cp, p, p, i32, C.c_float, C.c_float, p, p, p, C.c_size_t, i32, p]
+    L.kivi_decode_attn_rope_ragged_splits.argtypes = [cp, i32]
+    L.kivi_decode_attn_rope_ragged_splits.restype = i32
     L.kivi_decode_attn_rope_splits.restype = i32
     L.kivi_decode_attn_ragged_splits.argtypes = [cp, i32]
     L.kivi_decode_attn_ragged_splits.restype = i32
@@ -310,6 +314,36 @@ def kivi_decode_attn_ragged(cache, state, q, sm_scale, out=None, lse=None, num_s
                                        _ptr(lse) if want_lse else None, _ptr(ws), ws.numel() * ws.element_size(),
                                        num_splits, _stream(q)), "kivi_decode_attn_ragged")
     return (out, lse) if want_lse else out
+
+
+def kivi_decode_attn_rope_ragged(cache, state, q, sm_scale, rope_base=10000.0, out=None, lse=None, num_splits=0,
+                                 workspace=None):
+    """kivi_decode_attn_rope with per-sequence states (state: int32 [B, 4] from seq_state):
+    each sequence's keys turned at its own positions."""
+    if not q.is_contiguous() or q.dtype != torch.float16:
+        raise ValueError("expected contiguous float16 q [B, Hq, D]")
+    if state.dtype != torch.int32 or not state.is_contiguous():
+        raise ValueError("expected contiguous int32 state [B, 4]")
+    B, Hq, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    want_lse = lse is not None and lse is not False
+    if lse is True:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    splits = num_splits if num_splits > 0 else kivi_decode_attn_rope_ragged_splits(cache, Hq)
+    ws = workspace if workspace is not None else cache.workspace(Hq, splits)
+    _check(lib.kivi_decode_attn_rope_ragged(C.byref(cache.c), _ptr(state), _ptr(q), Hq, float(sm_scale),
+                                            float(rope_base), _ptr(out), _ptr(lse) if want_lse else None, _ptr(ws),
+                                            ws.numel() * ws.element_size(), splits, _stream(q)),
+           "kivi_decode_attn_rope_ragged")
+    return (out, lse) if want_lse else out
+
+
+def kivi_decode_attn_rope_ragged_splits(cache, q_heads):
+    s = lib.kivi_decode_attn_rope_ragged_splits(C.byref(cache.c), q_heads)
+    if s < 0:
+        raise KiviError(s, "kivi_decode_attn_rope_ragged_splits")
+    return s
 
 
 def kivi_decode_attn_ragged_splits(cache, q_heads):

@@ -21,7 +21,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 19
+    assert len(names) == 21
     out = os.popen(f"nm -D --defined-only {kivi.LIB_PATH}").read()
     exported = set(re.findall(r" T (kivi_\w+)$", out, re.M))
     assert set(names) <= exported, set(names) - exported
@@ -310,3 +310,15 @@ def test_rope_splits():
     small = _cache(token_cap=256, n_quant=64, n_res=10)
     assert L.kivi_decode_attn_rope_splits(C.byref(small), 4) == 1   # two key groups: fewer than the 4 waves
     assert L.kivi_decode_attn_rope_splits(C.byref(c), 33) == -2
+
+
+def test_rope_ragged_arguments():
+    f = L.kivi_decode_attn_rope_ragged
+    c = _cache(n_quant=0, n_res=0)
+    P = C.c_void_p(FAKE)
+    big = 1 << 30
+    assert f(C.byref(c), None, P, 4, 0.1, 10000.0, P, None, P, big, 0, None) == -1    # no states
+    assert f(C.byref(c), P, P, 4, 0.1, 0.0, P, None, P, big, 0, None) == -2          # base
+    assert f(C.byref(c), P, P, 4, 0.1, 10000.0, P, None, P, 16, 0, None) == -5       # workspace
+    s = L.kivi_decode_attn_rope_ragged_splits(C.byref(_cache(token_cap=4096)), 4)
+    assert 1 <= s <= 4096 // 32 // 4                    # at least a key group for each of 4 waves

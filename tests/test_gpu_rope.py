@@ -4,13 +4,15 @@ sequence positions, dense fp64 attention.  Bar: per row max |o_gpu - o_ref| / ma
 <= 2e-3, lse within 2e-3 + 2^-18 |lse|.  Covers both code widths, the three group sizes,
 MHA and GQA, explicit split counts, caches with only history or only residual, a decode
 loop whose flushes move the residual ring, another rotary base, and the 131,072-token
-shape (angles past 10^5 radians) on sampled rows."""
+shape (angles past 10^5 radians) on sampled rows, and ragged batches (each sequence turned at
+its own positions)."""
 import numpy as np
 import pytest
 import torch
 
 from kivi_testlib import assert_attn_close, assert_lse_close, bits, gpu_or_skip, ref_cache
 from kv_cache_bit_quantize_amd import synth
+from oracle import ref
 
 pytestmark = pytest.mark.gpu
 SM = synth.SM_SCALE_D128
@@ -23,15 +25,15 @@ def _kivi():
     return kivi
 
 
-def _setup(w, dev, code_bits=2):
+def _setup(w, dev, code_bits=2, flush_all=False):
     kivi = _kivi()
     k, v = synth.prefill_kv(w, device=dev)
     cache = kivi.Cache(w.batch, w.kv_heads, w.token_cap, group=w.group, residual_cap=w.residual_cap, device=dev,
-                       bits=code_bits)
+                       bits=code_bits, flush_all=flush_all)
     kivi.kivi_prefill(k, v, w.n_quant, cache)
     torch.cuda.synchronize()
     rc = ref_cache(w.batch, w.kv_heads, w.token_cap, k.cpu(), v.cpu(), w.n_quant, residual_cap=w.residual_cap,
-                   group=w.group, bits=code_bits)
+                   group=w.group, bits=code_bits, flush_all=flush_all)
     return cache, rc
 
 
@@ -71,8 +73,9 @@ def test_other_base():
     _check(cache, rc, synth.query(w, device=dev), base=500000.0, what="rope base 5e5")
 
 
-@pytest.mark.parametrize("code_bits,G,R", [(2, 32, 128), (4, 64, 128), (2, 32, 64)])
-def test_decode_loop(code_bits, G, R):
+@pytest.mark.parametrize("code_bits,G,R,flush_all", [(2, 32, 128, False), (4, 64, 128, False), (2, 32, 64, False),
+                                                     (2, 32, 64, True)])
+def test_decode_loop(code_bits, G, R, flush_all):
     """append_flush then attention each step: flushes move tokens from the ring (positions
     n_quant + i) into the history (positions t) and the ring head advances."""
     dev = gpu_or_skip()
@@ -80,13 +83,60 @@ def test_decode_loop(code_bits, G, R):
     steps = R + 40
     w = synth.small(seed=640 + G + R, batch=2, q_heads=8, kv_heads=2, context=4 * G + R - 7, n_quant=4 * G,
                     group=G, residual_cap=R, decode_steps=steps + R)
-    cache, rc = _setup(w, dev, code_bits)
+    cache, rc = _setup(w, dev, code_bits, flush_all)
     for s in range(steps):
         kn, vn = synth.step_kv(w, s, device=dev)
         kivi.kivi_append_flush(cache, kn, vn)
         rc.append(bits(kn).reshape(-1, D), bits(vn).reshape(-1, D))
         assert cache.state == (rc.n_quant, rc.n_res, rc.res_head), s
         _check(cache, rc, synth.query(w, step=s + 1, device=dev), what=f"rope loop {code_bits}-bit step {s}")
+
+
+@pytest.mark.parametrize("code_bits", [2, 4])
+def test_ragged_batch(code_bits):
+    """Sequences of different lengths, one empty at first: each sequence's keys turned at its
+    own positions, appends with flushes in between."""
+    dev = gpu_or_skip()
+    kivi = _kivi()
+    H, cap = 2, 2048
+    lengths = [(0, 0), (1024, 100), (0, 37), (1856, 128), (96, 5)]
+    B = len(lengths)
+    cache = kivi.Cache(B, H, cap, device=dev, bits=code_bits)
+    refs, states = [], []
+    for b, (nq, nr) in enumerate(lengths):
+        view = cache.sequence(b)
+        if nq + nr > 0:
+            wb = synth.small(seed=660 + b, batch=1, q_heads=4, kv_heads=H, context=nq + nr, n_quant=nq)
+            k, v = synth.prefill_kv(wb, device=dev)
+            kivi.kivi_prefill(k, v, nq, view)
+            refs.append(ref_cache(1, H, cap, k.cpu(), v.cpu(), nq, bits=code_bits))
+        else:
+            refs.append(ref.RefCache(1, H, D, 32, 128, token_cap=cap, bits=code_bits))
+        states.append(view.state)
+    state = kivi.seq_state(states, device=dev)
+    sw = synth.small(seed=669, batch=B, q_heads=4, kv_heads=H, context=1, n_quant=0)
+    q0 = synth.query(sw, device=dev)
+    out, lse = kivi.kivi_decode_attn_rope_ragged(cache, state, q0, SM, BASE, lse=True)
+    torch.cuda.synchronize()
+    assert not out[0].any() and bool(torch.isinf(lse[0]).all() and (lse[0] < 0).all())   # empty: 0, -inf
+    for b in range(1, B):
+        ref_out, ref_lse = refs[b].decode_attn_rope(bits(q0[b:b + 1]), SM, BASE)
+        assert_attn_close(out[b:b + 1], ref_out, what=f"rope ragged {code_bits}-bit prefill seq {b}")
+        assert_lse_close(lse[b:b + 1], ref_lse)
+    for s in range(40):
+        kn, vn = synth.step_kv(sw, s, device=dev)
+        q = synth.query(sw, step=s + 1, device=dev)
+        kivi.kivi_append_flush_ragged(cache, state, kn, vn)
+        out, lse = kivi.kivi_decode_attn_rope_ragged(cache, state, q, SM, BASE, lse=True)
+        torch.cuda.synchronize()
+        host = state.cpu().numpy()
+        for b, rc in enumerate(refs):
+            rc.append(bits(kn[b]).reshape(-1, D), bits(vn[b]).reshape(-1, D))
+            assert tuple(host[b, :3]) == (rc.n_quant, rc.n_res, rc.res_head), (s, b)
+            ref_out, ref_lse = rc.decode_attn_rope(bits(q[b:b + 1]), SM, BASE)
+            assert_attn_close(out[b:b + 1], ref_out, what=f"rope ragged {code_bits}-bit step {s} seq {b}")
+            assert_lse_close(lse[b:b + 1], ref_lse)
+    assert int(np.count_nonzero(state[:, 3].cpu().numpy())) == 0
 
 
 def test_long_context_sampled_rows():
