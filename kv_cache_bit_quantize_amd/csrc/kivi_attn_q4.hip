@@ -279,11 +279,9 @@ hipError_t launch_decode_attn_q4(const AttnArgs& a, hipStream_t s, hipEvent_t t0
     const dim3 grid = attn_grid(a, a.block_rows);
 #define KIVI_Q4_NQ(NQv)                                                                                         \
     KIVI_BY_GROUP(a.group, hipExtLaunchKernelGGL((attn_q4_kernel<NQv, GS>), grid, dim3(kBlock), 0, s, t0, t1, 0, a))
-    switch (a.nq) {
+    switch (a.nq) {   // the host takes at most two query heads per workgroup for 4-bit caches
         case 1: KIVI_Q4_NQ(1) break;
         case 2: KIVI_Q4_NQ(2) break;
-        case 3: KIVI_Q4_NQ(3) break;
-        case 4: KIVI_Q4_NQ(4) break;
         default: return hipErrorInvalidValue;
     }
 #undef KIVI_Q4_NQ
