@@ -2,20 +2,25 @@
 //
 // The 4-bit member of the quantizer family (sixteen levels; the KIVI summary page names the
 // 2-bit one, KIVI-2, and its ablation varies the scheme's parameters): the same call shape,
-// query grouping, split-K, fp16 residual and log-sum-exp merge as the 2-bit kernels.  A
-// 4-bit cache holds twice the code bytes per token, so the contraction runs on the vector
-// units, with the dequantization folded into both products:
+// query grouping, split-K, fp16 residual and log-sum-exp merge as the 2-bit kernels, with
+// the dequantization folded into both products:
 //  * keys, per group: q.(z + c*s) = q.z + (q*s).c.  Once per group the wave forms q*s for
-//    the 128 channels in fp32 (a product of two fp16 values, exact) into LDS and q.z as one
-//    wave sum; per token each code then costs one byte-to-float conversion and one fma;
-//  * values, per token: p*(z + c*s) = (p*s)*c + p*z, the p*z part summed per lane and
-//    added to its channels at the end.
+//    the 128 channels in fp32 (a product of two fp16 values, exact), turns it into 30-bit
+//    fixed point with one exponent per head and stores its four signed byte digits as digit
+//    planes in LDS.  The (q*s).c products then run on the matrix cores,
+//    v_mfma_i32_16x16x64_i8, exactly: B is the 16 tokens' codes (a lane's 8 bytes of one
+//    token row, low and high nibbles masked into bytes, which sets the channel order of the
+//    planes), A the digit planes (rows 4r..4r+3 head r's digits, other rows zero), so lane
+//    16r + n ends with head r's four digit sums of token n.  q.z is one wave sum per group;
+//  * values, per token: p*(z + c*s) = (p*s)*c + p*z on the vector units (one byte-to-float
+//    conversion and one fma per code; the token-major rows do not give the value matrix
+//    operand, which needs 8 tokens of one channel per lane), the p*z part summed per lane
+//    and added to its channels at the end.
 //
 // Work split: grid (splits, kv heads x query chunks of NQ heads); a split owns whole key
 // groups, each of its 4 waves a contiguous run of them, 16 tokens per wave-iteration:
-//  * logits: lane 4t + c holds token t and channels [32c, 32c+32) (16 bytes of codes) and
-//    keeps the group's q*s of those channels in registers;
-//  * online softmax per query head (log2 domain), the probabilities into LDS;
+//  * logits as above, online softmax per query head (log2 domain) over DPP row r, the
+//    probabilities into LDS;
 //  * P.V: lane 16g + c holds tokens 4g..4g+3 and channels [8c, 8c+8) (4 bytes of codes and
 //    the token's (scale, zero) word of those channels).
 // Code loads are issued one iteration ahead, the next group's (scale, zero) words one group
@@ -32,7 +37,11 @@ template <int NQ, int GS>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) void attn_q4_kernel(AttnArgs a) {
     constexpr int kIt = GS / kQ4Tok;   // iterations per key group
     __shared__ __align__(16) float sh_p[kWaves][NQ][kQ4Tok];
-    __shared__ __align__(16) float sh_qs[kWaves][NQ][kD];   // q*s of the wave's current key group
+    // digit planes of q*s for the wave's current key group: [head][digit][16-channel block w]
+    // [position p], position p holding channel 16w + (p & 8) + 2(p & 3) + ((p >> 2) & 1), the
+    // order in which a masked token-major code word enters the matrix instruction
+    __shared__ __align__(16) uint8_t sh_dg[kWaves][NQ][4][8][16];
+    __shared__ __align__(16) uint8_t sh_zero[16];           // the A operand of unused rows
     __shared__ __align__(16) float sh_o[NQ][kSlots][kD];
     __shared__ float sh_m[NQ][kSlots], sh_l[NQ][kSlots];
 
@@ -46,7 +55,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     const uint32_t tag_v = partial_tag(a, grow);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int kt = lane >> 2, kq = lane & 3;
+    const int mrow = lane & 15, kb = lane >> 4;   // matrix roles: token / A row, K block
     const int vg = lane >> 4, vc = lane & 15;
 
     const RowState rs = row_state(a, kvrow, split);
@@ -78,7 +87,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     const uint32_t* vp_row = reinterpret_cast<const uint32_t*>(a.v_sz) + tok0 * (kD / GS);
     const int t_b = kgb * GS;
     struct Loads {
-        uint4 k;          // key codes of token kt, channels 32kq..32kq+31
+        uint2 kc[2];      // key codes of token mrow, channels 16(kb + 4h)..+15 (h = 0, 1)
         uint32_t v[4];    // value codes of tokens 4vg+u, channels 8vc..8vc+7
         uint32_t vp[4];   // (scale, zero) word of those tokens and channels
     };
@@ -86,8 +95,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     // byte offsets inside a row fit 32 bits (token_cap <= 2^26 for 4-bit caches), so the
     // loads take the row pointer as their scalar base and per-token steps as immediates
     auto load_k = [&](Loads& L, int it) {
-        const uint32_t off = (uint32_t)(tok(it) + kt) * kRowBytes4 + 16 * kq;
-        L.k = *reinterpret_cast<const uint4*>(kc_row + off);
+        const uint8_t* r = kc_row + (uint32_t)(tok(it) + mrow) * kRowBytes4 + 8 * kb;
+        L.kc[0] = *reinterpret_cast<const uint2*>(r);
+        L.kc[1] = *reinterpret_cast<const uint2*>(r + 32);
     };
     auto load_v = [&](Loads& L, int it) {
         const uint32_t t = (uint32_t)(tok(it) + 4 * vg);
@@ -120,6 +130,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     };
 
+    if (lane < 16) sh_zero[lane] = 0;
     uint32_t tag;
     if (n_groups > 0) {
         Loads cur;
@@ -128,60 +139,68 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
         uint2 kpn = load_kp(0);
         tag = settle_tag(tag_v);
         for (int gi = 0; gi < n_groups; ++gi) {
-            // this group's q*s into LDS (channels 2*lane, 2*lane+1) and q.z over the wave
-            float qz[NQ];
+            // this group's q*s (channels 2*lane, 2*lane+1; a product of two fp16 values, exact
+            // in fp32) as 30-bit fixed point with one exponent per head (|q*s| * 2^sh < 2^29,
+            // truncated: off by less than 2^-29 of the group's largest term), split into four
+            // signed base-256 digits and stored into the digit planes; q.z over the wave
+            float qz[NQ], unit[NQ];   // unit: 2^-sh, the weight of digit 0
             {
                 const float s0 = h2f(kpn.x & 0xffffu), z0 = h2f(kpn.x >> 16);
                 const float s1 = h2f(kpn.y & 0xffffu), z1 = h2f(kpn.y >> 16);
+                const int w = lane >> 3, q = 2 * (lane & 7);           // channel 2*lane = 16w + q
+                const int p0 = (q & 8) + ((q & 6) >> 1), p1 = p0 + 4;  // positions of channels q, q + 1
 #pragma unroll
                 for (int r = 0; r < NQ; ++r) {
-                    *reinterpret_cast<float2*>(&sh_qs[wave][r][2 * lane]) = make_float2(q0[r] * s0, q1[r] * s1);
+                    const float x0 = q0[r] * s0, x1 = q1[r] * s1;
+                    float mx = half_max(fmaxf(fabsf(x0), fabsf(x1)));
+                    mx = fmaxf(readlane_f(mx, 0), readlane_f(mx, 32));
+                    const int sh = min(29 - __builtin_amdgcn_frexp_expf(mx), 100);
+                    const float fs = __builtin_ldexpf(1.0f, sh);
+                    unit[r] = __builtin_ldexpf(1.0f, -sh);
+                    const uint32_t d0 = ((uint32_t)(int)(x0 * fs) + 0x80808080u) ^ 0x80808080u;
+                    const uint32_t d1 = ((uint32_t)(int)(x1 * fs) + 0x80808080u) ^ 0x80808080u;
+#pragma unroll
+                    for (int dd = 0; dd < 4; ++dd) {
+                        sh_dg[wave][r][dd][w][p0] = (uint8_t)(d0 >> (8 * dd));
+                        sh_dg[wave][r][dd][w][p1] = (uint8_t)(d1 >> (8 * dd));
+                    }
                     qz[r] = wave_sum(fmaf(q0[r], z0, q1[r] * z1));
                 }
             }
             wave_sync();
-            float qs[NQ][32];   // q*s of channels 32kq..32kq+31
-#pragma unroll
-            for (int r = 0; r < NQ; ++r) {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const float4 x = *reinterpret_cast<const float4*>(&sh_qs[wave][r][32 * kq + 4 * i]);
-                    qs[r][4 * i] = x.x;
-                    qs[r][4 * i + 1] = x.y;
-                    qs[r][4 * i + 2] = x.z;
-                    qs[r][4 * i + 3] = x.w;
-                }
-            }
-            wave_sync();   // every lane has read the group's q*s before the next group's are written
             kpn = load_kp(gi + 1);
 #pragma unroll 1
             for (int j = 0; j < kIt; ++j) {
                 const int it = gi * kIt + j;
-                // ---- logits: 32 channels of token kt for every query head (q.z once per token)
-                const uint32_t cw[4] = {cur.k.x, cur.k.y, cur.k.z, cur.k.w};
-                float d[NQ];
+                // ---- logits on the matrix cores: B = the 16 tokens' codes (a lane's 8 bytes of
+                // token mrow, low and high nibbles masked into bytes), A = the digit planes (rows
+                // 4r..4r+3: head r's digits 0..3, other rows zero); K = 64 channels per
+                // instruction.  Lane 16r + n ends with the four digit sums of head r, token n.
+                v4i cacc = {0, 0, 0, 0};
 #pragma unroll
-                for (int r = 0; r < NQ; ++r) d[r] = kq == 0 ? qz[r] : 0.0f;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    // word i: channels 8i..8i+7 of the quarter, channel 8i + c at bit 4c; the
-                    // even channels' codes as the bytes of lo, the odd ones' of hi
-                    uint32_t lo = cw[i] & 0x0F0F0F0Fu, hi = (cw[i] >> 4) & 0x0F0F0F0Fu;
-                    // opaque to the optimizer, so each code converts with one v_cvt_f32_ubyteN
-                    asm volatile("" : "+v"(lo), "+v"(hi));
-#pragma unroll
-                    for (int c = 0; c < 8; ++c) {
-                        const float code = (float)((((c & 1) ? hi : lo) >> (8 * (c >> 1))) & 0xFFu);
-#pragma unroll
-                        for (int r = 0; r < NQ; ++r) d[r] = fmaf(qs[r][8 * i + c], code, d[r]);
-                    }
+                for (int h = 0; h < 2; ++h) {
+                    const uint32_t d0 = cur.kc[h].x, d1 = cur.kc[h].y;
+                    const v4i bop = {(int)(d0 & 0x0F0F0F0Fu), (int)((d0 >> 4) & 0x0F0F0F0Fu), (int)(d1 & 0x0F0F0F0Fu),
+                                     (int)((d1 >> 4) & 0x0F0F0F0Fu)};
+                    const uint8_t* ap = mrow < 4 * NQ ? &sh_dg[wave][mrow >> 2][mrow & 3][kb + 4 * h][0] : sh_zero;
+                    cacc = __builtin_amdgcn_mfma_i32_16x16x64_i8(*reinterpret_cast<const v4i*>(ap), bop, cacc, 0, 0, 0);
                 }
                 load_k(cur, it + 1);
-                // ---- online softmax per query head over the 16 tokens
+                const int hr = lane >> 4;   // the head whose digit sums this lane holds
+                float lg = -INFINITY;
+                if (hr < NQ) {
+                    // digit sums: |S| < 128 * 128 * 15, the total one binary32 rounding
+                    const int hw = cacc[3] * 256 + cacc[2], lw = cacc[1] * 256 + cacc[0];
+                    const float tot = fmaf((float)hw, 65536.0f, (float)lw);
+                    const float u = (NQ > 1 && hr == 1) ? unit[NQ - 1] : unit[0];
+                    const float z = (NQ > 1 && hr == 1) ? qz[NQ - 1] : qz[0];
+                    lg = fmaf(tot, u, z) * a.sm_log2;
+                }
+                // ---- online softmax per query head over the 16 tokens (head r: DPP row r)
+                const float rmx = row_max(lg);
 #pragma unroll
                 for (int r = 0; r < NQ; ++r) {
-                    const float lg = quad_sum(d[r]) * a.sm_log2;
-                    const float mnew = fmaxf(m[r], wave_max_quads(lg));
+                    const float mnew = fmaxf(m[r], readlane_f(rmx, 16 * r));
                     if (mnew != m[r]) {
                         const float al = m[r] == -INFINITY ? 0.0f : exp2f(m[r] - mnew);
 #pragma unroll
@@ -190,9 +209,11 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
                         lsum[r] *= al;
                         m[r] = mnew;
                     }
-                    const float p = exp2f(lg - m[r]);
-                    lsum[r] += p;   // every lane of the token's quad adds it: divided by 4 below
-                    if (kq == 0) pw[r * kQ4Tok + kt] = p;
+                    if (hr == r) {
+                        const float p = exp2f(lg - m[r]);
+                        lsum[r] += p;   // the lanes of head r's row, one token each
+                        pw[r * kQ4Tok + mrow] = p;
+                    }
                 }
                 wave_sync();
                 // ---- P.V: tokens 4vg..4vg+3, channels 8vc..8vc+7
@@ -243,7 +264,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
             x += __shfl_xor(x, 32, 64);
             o[r][c] = x;
         }
-        const float l = wave_sum(lsum[r]) * 0.25f;
+        const float l = wave_sum(lsum[r]);
         if (lane < 16) {
 #pragma unroll
             for (int c = 0; c < 8; ++c) sh_o[r][wave][8 * vc + c] = o[r][c];
