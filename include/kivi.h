@@ -174,8 +174,8 @@ int kivi_decode_attn(const kivi_cache* cache, const uint16_t* q, int32_t q_heads
  * given: the caller rotates it at its own position.  Values are not rotated.  The split
  * count for num_splits == 0 is kivi_decode_attn_rope_splits(); size the workspace with
  * kivi_decode_attn_workspace(cache, q_heads, that count).  2-bit caches take token_cap
- * <= 2^27 here (KIVI_ERR_UNSUPPORTED beyond).  One query head per workgroup; no fused-append
- * form (append with kivi_append_flush, then call this). */
+ * <= 2^27 here (KIVI_ERR_UNSUPPORTED beyond).  One query head per workgroup.  The fused form
+ * with the append is kivi_decode_step_rope. */
 int kivi_decode_attn_rope(const kivi_cache* cache, const uint16_t* q, int32_t q_heads, float sm_scale,
                           float rope_base, uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
                           int32_t num_splits, void* stream);
@@ -204,6 +204,17 @@ int kivi_decode_step(kivi_cache* cache, const uint16_t* k_new, const uint16_t* v
                      const uint16_t* q, int32_t q_heads, float sm_scale, uint16_t* out, float* lse,
                      void* workspace, size_t workspace_bytes, int32_t num_splits, int32_t* flushed,
                      void* stream);
+
+/* kivi_decode_step with pre-RoPE attention: kivi_append_flush(cache, k_new, v_new, flushed,
+ * stream) (the new key pre-RoPE, as stored) followed by kivi_decode_attn_rope(cache, q, ...)
+ * on the updated cache, the new token at position n_quant + n_res - 1 of the updated state;
+ * the same arguments, results, state update and errors as those two calls, one kernel
+ * launch when no group is flushed (as in kivi_decode_step).  num_splits == 0 takes
+ * kivi_decode_attn_rope_splits() of the updated state; the workspace must fit that count. */
+int kivi_decode_step_rope(kivi_cache* cache, const uint16_t* k_new, const uint16_t* v_new, const uint16_t* q,
+                          int32_t q_heads, float sm_scale, float rope_base, uint16_t* out, float* lse,
+                          void* workspace, size_t workspace_bytes, int32_t num_splits, int32_t* flushed,
+                          void* stream);
 
 /* ---- Ragged batches: sequences of one batch at different lengths.
  * The per-sequence cache state lives in device memory, seq_state: int32 [batch][4] =

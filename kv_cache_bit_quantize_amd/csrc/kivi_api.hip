@@ -577,10 +577,11 @@ int kivi_decode_attn(const kivi_cache* c, const uint16_t* q, int32_t q_heads, fl
     return hip_status(launch_decode_attn(a, (hipStream_t)stream, t0, t1));
 }
 
-// pre-RoPE attention, uniform (seq_state == nullptr) or ragged
-int decode_attn_rope(const kivi_cache* c, int32_t* seq_state, const uint16_t* q, int32_t q_heads, float sm_scale,
-                     float rope_base, uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
-                     int32_t num_splits, void* stream) {
+// Validates a pre-RoPE attention call, uniform (seq_state == nullptr) or ragged, and fills
+// its arguments.
+int prepare_attn_rope(const kivi_cache* c, int32_t* seq_state, const uint16_t* q, int32_t q_heads, float sm_scale,
+                      float rope_base, uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
+                      int32_t num_splits, AttnArgs* pa) {
     if (!std::isfinite(rope_base) || !(rope_base > 0.0f)) return KIVI_ERR_SHAPE;
     int st = check_shape(c);
     if (st != KIVI_OK) return st;
@@ -590,13 +591,22 @@ int decode_attn_rope(const kivi_cache* c, int32_t* seq_state, const uint16_t* q,
     if (num_splits < 0 || num_splits > kMaxSplits) return KIVI_ERR_SHAPE;
     const int32_t splits =
         num_splits > 0 ? num_splits : (seq_state != nullptr ? rope_ragged_splits(c, q_heads) : rope_auto_splits(c, q_heads));
-    AttnArgs a;
-    st = prepare_attn(c, q, q_heads, sm_scale, out, lse, workspace, workspace_bytes, splits, &a, seq_state);
+    st = prepare_attn(c, q, q_heads, sm_scale, out, lse, workspace, workspace_bytes, splits, pa, seq_state);
     if (st != KIVI_OK) return st;
-    a.nq = 1;
-    a.block_rows = a.q_rows;
-    a.slot_budget = (int32_t)kTargetBlocksRope;
-    a.rope_base = (double)rope_base;
+    pa->nq = 1;
+    pa->block_rows = pa->q_rows;
+    pa->slot_budget = (int32_t)kTargetBlocksRope;
+    pa->rope_base = (double)rope_base;
+    return KIVI_OK;
+}
+
+int decode_attn_rope(const kivi_cache* c, int32_t* seq_state, const uint16_t* q, int32_t q_heads, float sm_scale,
+                     float rope_base, uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
+                     int32_t num_splits, void* stream) {
+    AttnArgs a;
+    const int st = prepare_attn_rope(c, seq_state, q, q_heads, sm_scale, rope_base, out, lse, workspace,
+                                     workspace_bytes, num_splits, &a);
+    if (st != KIVI_OK) return st;
     hipEvent_t t0, t1;
     take_timing(&t0, &t1);
     return hip_status(launch_decode_attn_rope(a, (hipStream_t)stream, t0, t1));
@@ -630,6 +640,35 @@ int32_t kivi_decode_attn_rope_splits(const kivi_cache* c, int32_t q_heads) {
     if ((st = check_state(c)) != KIVI_OK) return st;
     if (q_heads <= 0 || q_heads % c->kv_heads != 0) return KIVI_ERR_SHAPE;
     return rope_auto_splits(c, q_heads);
+}
+
+int kivi_decode_step_rope(kivi_cache* c, const uint16_t* k_new, const uint16_t* v_new, const uint16_t* q,
+                          int32_t q_heads, float sm_scale, float rope_base, uint16_t* out, float* lse,
+                          void* workspace, size_t workspace_bytes, int32_t num_splits, int32_t* flushed,
+                          void* stream) {
+    AppendArgs ap;
+    kivi_cache next;
+    int st = prepare_append(c, k_new, v_new, &ap, &next);
+    if (st != KIVI_OK) return st;
+    AttnArgs at;   // pre-RoPE attention on the state after the append
+    st = prepare_attn_rope(&next, nullptr, q, q_heads, sm_scale, rope_base, out, lse, workspace, workspace_bytes,
+                           num_splits, &at);
+    if (st != KIVI_OK) return st;
+    if (ap.do_flush) {
+        if ((st = hip_status(launch_append_flush(ap, (hipStream_t)stream))) != KIVI_OK) return st;
+    } else {
+        at.k_new = k_new;
+        at.v_new = v_new;
+        at.k_ring = c->k_res;
+        at.v_ring = c->v_res;
+        at.new_slot = ap.new_slot;
+    }
+    hipEvent_t t0, t1;
+    take_timing(&t0, &t1);
+    if ((st = hip_status(launch_decode_attn_rope(at, (hipStream_t)stream, t0, t1))) != KIVI_OK) return st;
+    commit_state(c, next);
+    if (flushed != nullptr) *flushed = ap.do_flush;
+    return KIVI_OK;
 }
 
 int kivi_decode_step(kivi_cache* c, const uint16_t* k_new, const uint16_t* v_new, const uint16_t* q,

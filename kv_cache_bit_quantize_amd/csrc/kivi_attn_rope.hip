@@ -79,7 +79,8 @@ __device__ __forceinline__ void codes8(uint32_t w, int h, float (&c)[8]) {
 
 // Softmax state of query row qrow over the fp16 residual ring, keys turned at positions
 // n_quant + i.  Wave w takes the ring's logical tokens w, w + 4, ...; lane m holds pair m
-// (channels m, m + 64) for the logit (a wave sum) and the same two channels for P.V.
+// (channels m, m + 64) for the logit (a wave sum) and the same two channels for P.V.  In a
+// fused decode step the last residual token is the new one, read from k_new / v_new.
 __device__ void residual_rope_states(const AttnArgs& a, const RowState& rs, int64_t qrow, int64_t kvrow, int wave,
                                      const double* w_pair, float* o_dst, float& mr, float& lr) {
     const int lane = threadIdx.x & 63;
@@ -90,8 +91,9 @@ __device__ void residual_rope_states(const AttnArgs& a, const RowState& rs, int6
     lr = 0.0f;
     for (int i = wave; i < rs.n_res; i += kWaves) {
         const int slot = (rs.res_head + i) % a.residual_cap;
-        const uint16_t* kr = a.k_res + (kvrow * a.residual_cap + slot) * kD;
-        const uint16_t* vr = a.v_res + (kvrow * a.residual_cap + slot) * kD;
+        const bool fresh = a.k_new != nullptr && i == rs.n_res - 1;
+        const uint16_t* kr = fresh ? a.k_new + kvrow * kD : a.k_res + (kvrow * a.residual_cap + slot) * kD;
+        const uint16_t* vr = fresh ? a.v_new + kvrow * kD : a.v_res + (kvrow * a.residual_cap + slot) * kD;
         const float2 e = turn((double)(rs.n_quant + i) * wm);
         const float wr = fmaf(q0, e.x, q1 * e.y), wi = fmaf(q0, e.y, -q1 * e.x);   // conj(Q) * e
         const float part = fmaf(wr, h2f(kr[lane]), -wi * h2f(kr[lane + kRpPairs]));
@@ -122,6 +124,7 @@ __global__ __launch_bounds__(kBlock) void attn_rope_kernel(AttnArgs a) {
     const int split = grid_split(a);
     const int64_t qrow = grid_row(a);
     const int64_t kvrow = (qrow / a.q_heads) * a.kv_heads + (qrow % a.q_heads) / a.ratio;
+    if (a.k_new != nullptr && split == 0 && (qrow % a.q_heads) % a.ratio == 0) store_new_token(a, kvrow);
     const uint32_t tag_v = partial_tag(a, qrow);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

@@ -21,7 +21,7 @@ EXPORTS = ["kivi_quantize_k_per_channel", "kivi_quantize_v_per_token", "kivi_pre
            "kivi_status_str", "kivi_time_next_attention", "kivi_decode_attn_fp16", "kivi_decode_attn_fp16_splits",
            "kivi_decode_attn_fp16_workspace", "kivi_append_flush_ragged", "kivi_decode_attn_ragged",
            "kivi_decode_attn_ragged_splits", "kivi_decode_attn_rope", "kivi_decode_attn_rope_splits",
-           "kivi_decode_attn_rope_ragged", "kivi_decode_attn_rope_ragged_splits"]
+           "kivi_decode_attn_rope_ragged", "kivi_decode_attn_rope_ragged_splits", "kivi_decode_step_rope"]
 
 KIVI_FLUSH_ALL = 1        # kivi_cache.flags: a full residual is flushed whole (else its oldest group)
 KIVI_CODES_4BIT = 2       # kivi_cache.flags: 4-bit codes (sixteen levels), token-major nibbles
@@ -68,6 +68,8 @@ def _load():
     L.kivi_decode_attn_ragged.argtypes = [cp, p, p, i32, C.c_float, p, p, p, C.c_size_t, i32, p]
     L.kivi_decode_attn_rope.argtypes = [cp, p, i32, C.c_float, C.c_float, p, p, p, C.c_size_t, i32, p]
     L.kivi_decode_attn_rope_splits.argtypes = [cp, i32]
+    L.kivi_decode_step_rope.argtypes = [cp, p, p, p, i32, C.c_float, C.c_float, p, p, p, C.c_size_t, i32,
+                                         C.POINTER(i32), p]
     L.kivi_decode_attn_rope_ragged.argtypes = [cp, p, p, i32, C.c_float, C.c_float, p, p, p, C.c_size_t, i32, p]
     L.kivi_decode_attn_rope_ragged_splits.argtypes = [cp, i32]
     L.kivi_decode_attn_rope_ragged_splits.restype = i32
@@ -275,6 +277,39 @@ def kivi_decode_step(cache, k_new, v_new, q, sm_scale, out=None, lse=None, num_s
     _check(lib.kivi_decode_step(C.byref(cache.c), _ptr(k_new), _ptr(v_new), _ptr(q), Hq, float(sm_scale),
                                 _ptr(out), _ptr(lse) if want_lse else None, _ptr(ws), ws.numel() * ws.element_size(),
                                 num_splits, C.byref(flushed), _stream(q)), "kivi_decode_step")
+    return (out, lse, bool(flushed.value)) if want_lse else (out, bool(flushed.value))
+
+
+def kivi_decode_step_rope(cache, k_new, v_new, q, sm_scale, rope_base=10000.0, out=None, lse=None, num_splits=0,
+                          workspace=None):
+    """kivi_append_flush(cache, k_new, v_new) then kivi_decode_attn_rope(cache, q, ...), one launch
+    when no group is flushed.  Returns (out, flushed) or (out, lse, flushed) if `lse`."""
+    for t in (k_new, v_new):
+        if not t.is_contiguous() or t.dtype != torch.float16:
+            raise ValueError("expected contiguous float16 [B, Hkv, D]")
+    if not q.is_contiguous() or q.dtype != torch.float16:
+        raise ValueError("expected contiguous float16 q [B, Hq, D]")
+    B, Hq, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    want_lse = lse is not None and lse is not False
+    if lse is True:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    splits = num_splits
+    if splits <= 0:   # the library's choice on the state after the append
+        nxt = kivi_cache.from_buffer_copy(cache.c)
+        flush = nxt.residual_cap if nxt.flags & KIVI_FLUSH_ALL else nxt.group
+        if nxt.n_res == nxt.residual_cap and nxt.n_quant + flush <= nxt.token_cap:
+            nxt.n_quant += flush
+        splits = lib.kivi_decode_attn_rope_splits(C.byref(nxt), Hq)
+        if splits < 0:
+            raise KiviError(splits, "kivi_decode_attn_rope_splits")
+    ws = workspace if workspace is not None else cache.workspace(Hq, splits)
+    flushed = C.c_int32(0)
+    _check(lib.kivi_decode_step_rope(C.byref(cache.c), _ptr(k_new), _ptr(v_new), _ptr(q), Hq, float(sm_scale),
+                                     float(rope_base), _ptr(out), _ptr(lse) if want_lse else None, _ptr(ws),
+                                     ws.numel() * ws.element_size(), splits, C.byref(flushed), _stream(q)),
+           "kivi_decode_step_rope")
     return (out, lse, bool(flushed.value)) if want_lse else (out, bool(flushed.value))
 
 

@@ -21,7 +21,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 21
+    assert len(names) == 22
     out = os.popen(f"nm -D --defined-only {kivi.LIB_PATH}").read()
     exported = set(re.findall(r" T (kivi_\w+)$", out, re.M))
     assert set(names) <= exported, set(names) - exported
@@ -322,3 +322,17 @@ def test_rope_ragged_arguments():
     assert f(C.byref(c), P, P, 4, 0.1, 10000.0, P, None, P, 16, 0, None) == -5       # workspace
     s = L.kivi_decode_attn_rope_ragged_splits(C.byref(_cache(token_cap=4096)), 4)
     assert 1 <= s <= 4096 // 32 // 4                    # at least a key group for each of 4 waves
+
+
+def test_rope_step_arguments_leave_the_state():
+    """kivi_decode_step_rope validates the append and the attention before enqueueing
+    anything and leaves the cache state as it was on an error."""
+    f = L.kivi_decode_step_rope
+    c = _cache(n_quant=64, n_res=10)
+    P = C.c_void_p(FAKE)
+    big = 1 << 30
+    fl = C.c_int32(7)
+    assert f(C.byref(c), P, P, P, 4, 0.1, 0.0, P, None, P, big, 0, C.byref(fl), None) == -2      # base
+    assert f(C.byref(c), None, P, P, 4, 0.1, 10000.0, P, None, P, big, 0, C.byref(fl), None) == -1  # k_new
+    assert f(C.byref(c), P, P, P, 4, 0.1, 10000.0, P, None, P, 16, 0, C.byref(fl), None) == -5    # workspace
+    assert _state(c) == (64, 10, 0) and fl.value == 7

@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 import torch
 
-from kivi_testlib import assert_attn_close, assert_lse_close, bits, gpu_or_skip, ref_cache
+from kivi_testlib import assert_attn_close, assert_cache_equal, assert_lse_close, bits, gpu_or_skip, ref_cache
 from kv_cache_bit_quantize_amd import synth
 from oracle import ref
 
@@ -73,11 +73,14 @@ def test_other_base():
     _check(cache, rc, synth.query(w, device=dev), base=500000.0, what="rope base 5e5")
 
 
-@pytest.mark.parametrize("code_bits,G,R,flush_all", [(2, 32, 128, False), (4, 64, 128, False), (2, 32, 64, False),
-                                                     (2, 32, 64, True)])
-def test_decode_loop(code_bits, G, R, flush_all):
-    """append_flush then attention each step: flushes move tokens from the ring (positions
-    n_quant + i) into the history (positions t) and the ring head advances."""
+@pytest.mark.parametrize("code_bits,G,R,flush_all,fused", [
+    (2, 32, 128, False, True), (4, 64, 128, False, False), (2, 32, 64, False, False), (2, 32, 64, True, True),
+    (4, 32, 128, False, True),
+])
+def test_decode_loop(code_bits, G, R, flush_all, fused):
+    """append then attention each step (kivi_decode_step_rope, or the two separate calls):
+    flushes move tokens from the ring (positions n_quant + i) into the history (positions t)
+    and the ring head advances; the fused step reads the new token from the caller's buffers."""
     dev = gpu_or_skip()
     kivi = _kivi()
     steps = R + 40
@@ -86,10 +89,23 @@ def test_decode_loop(code_bits, G, R, flush_all):
     cache, rc = _setup(w, dev, code_bits, flush_all)
     for s in range(steps):
         kn, vn = synth.step_kv(w, s, device=dev)
-        kivi.kivi_append_flush(cache, kn, vn)
-        rc.append(bits(kn).reshape(-1, D), bits(vn).reshape(-1, D))
-        assert cache.state == (rc.n_quant, rc.n_res, rc.res_head), s
-        _check(cache, rc, synth.query(w, step=s + 1, device=dev), what=f"rope loop {code_bits}-bit step {s}")
+        q = synth.query(w, step=s + 1, device=dev)
+        f_ref = rc.append(bits(kn).reshape(-1, D), bits(vn).reshape(-1, D))
+        if fused:
+            out, lse, f = kivi.kivi_decode_step_rope(cache, kn, vn, q, SM, BASE, lse=True)
+            assert bool(f) == bool(f_ref), s
+            assert cache.state == (rc.n_quant, rc.n_res, rc.res_head), s
+            torch.cuda.synchronize()
+            ref_out, ref_lse = rc.decode_attn_rope(bits(q), SM, BASE)
+            assert_attn_close(out, ref_out, what=f"rope step {code_bits}-bit step {s}")
+            assert_lse_close(lse, ref_lse)
+            if f or s % 32 == 0:   # the new token reached its ring slot
+                torch.cuda.synchronize()
+                assert_cache_equal(cache, rc)
+        else:
+            kivi.kivi_append_flush(cache, kn, vn)
+            assert cache.state == (rc.n_quant, rc.n_res, rc.res_head), s
+            _check(cache, rc, q, what=f"rope loop {code_bits}-bit step {s}")
 
 
 @pytest.mark.parametrize("code_bits", [2, 4])
