@@ -16,8 +16,10 @@ serving batch of 64 sequences at different lengths ("ragged_batch"; --no-ragged 
 attention alone over the same context quantized at group sizes 64 and 128
 ("group_sizes"; --sweep-groups sets the list, --group the timed cache's own group size),
 attention alone over the same context in 4-bit codes ("four_bit"; --four-bit-groups
-sets its group sizes, empty skips it), and attention over the same context stored as
-pre-RoPE keys, turned at their positions inside the kernel ("pre_rope"; --no-rope skips it).
+sets its group sizes, empty skips it), attention over the same context stored as
+pre-RoPE keys, turned at their positions inside the kernel ("pre_rope"; --no-rope skips it),
+and the two prefill quantizers over the same context ("prefill_quantize": one
+kivi_quantize_k_per_channel and one kivi_quantize_v_per_token call each, one kernel per call).
 """
 import argparse
 import json
@@ -206,6 +208,35 @@ def rope_measure(kivi, synth, w, k, v, queries, steps, warmup, base=10000.0):
     return res
 
 
+def prefill_measure(kivi, w, k, v, steps, warmup):
+    """The prefill quantizers over the history of the prefill (n_quant tokens of every row,
+    read in place from the [B, H, context, D] tensors), each call one kernel on torch's
+    current stream, timed with events around it.  Algorithmic bytes per token and row: 256
+    read, 32 of codes and 512/G of pairs written."""
+    nq = w.n_quant
+    cache = kivi.Cache(w.batch, w.kv_heads, w.token_cap, device=k.device)
+    rows = w.batch * w.kv_heads
+    byts = rows * nq * (D * 2 + D // 4 + (D * 4) // w.group)
+    res = {}
+    for name, fn, src in (("keys", kivi.kivi_quantize_k_per_channel, k), ("values", kivi.kivi_quantize_v_per_token, v)):
+        x = src[:, :, :nq]
+        for _ in range(warmup):
+            fn(x, cache)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        for a, b in ev:
+            a.record()
+            fn(x, cache)
+            b.record()
+        torch.cuda.synchronize()
+        us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+        res[name] = {"us": round(us, 2), "bytes_per_call": int(byts), "achieved": round(byts / us / 1e3, 1),
+                     "unit": "GB/s", "frac": round(byts / us / 1e3 / PEAK_HBM_GBS, 4)}
+    res["tokens"] = nq
+    del cache
+    return res
+
+
 def group_sweep(kivi, synth, w, k, v, queries, steps, warmup, groups, bits=2):
     """Attention alone (kivi_decode_attn) over the same prefill keys and values quantized at
     other group sizes or code widths: the history is the largest whole number of groups
@@ -257,6 +288,7 @@ def main():
     ap.add_argument("--sweep-groups", default="64,128",
                     help="group sizes of the attention-only sweep (comma list; empty: skip)")
     ap.add_argument("--no-rope", action="store_true", help="skip the pre-RoPE attention measurement")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill quantizer measurement")
     ap.add_argument("--four-bit-groups", default="32",
                     help="group sizes of the 4-bit attention-only measurement (comma list; empty: skip)")
     args = ap.parse_args()
@@ -401,6 +433,7 @@ def main():
         "group_sizes": None,
         "four_bit": None,
         "pre_rope": None,
+        "prefill_quantize": None,
     }
     del cache, ws
     groups = [int(x) for x in args.sweep_groups.split(",") if x.strip()]
@@ -411,6 +444,8 @@ def main():
         res["four_bit"] = group_sweep(kivi, synth, w, k, v, queries, args.steps, args.warmup, groups4, bits=4)
     if not args.no_rope:
         res["pre_rope"] = rope_measure(kivi, synth, w, k, v, queries, args.steps, args.warmup)
+    if not args.no_prefill:
+        res["prefill_quantize"] = prefill_measure(kivi, w, k, v, min(args.steps, 20), min(args.warmup, 3))
     if not args.no_ragged:
         res["ragged_batch"] = ragged_measure(kivi, synth, dev, args.steps, args.warmup)
     if args.cpu_heads > 0:
