@@ -113,22 +113,12 @@ __global__ __launch_bounds__(kSqBlock) void attn_split_kernel(AttnArgs a) {
     const int g_lo = split * rs.groups_per_split;
     const int g_hi = min(n_groups, g_lo + rs.groups_per_split);
     const int n_pairs = (max(0, g_hi - g_lo) + 1) >> 1;   // the workgroup's pairs of 32-token tiles
-    if (threadIdx.x == 0) sh_next = 0;
-    __syncthreads();
-
-    // ---- fp16 residual first (split rs.res_split), as separate states: its loads meet a memory
-    // system that is not loaded yet, and the waves that take it start on the pairs later
-    float mr[1] = {-INFINITY}, lr[1] = {0.0f};
-    if (split == rs.res_split)
-        residual_states<1, kSqWaves>(a, rs, qrow, kvrow, wave, &sh_o[0][kSqWaves + wave][0], kSqSlots * kD, mr, lr);
-
     // Pair schedule: wave w takes pairs w and w + kSqWaves, then one pair per iteration from
     // the workgroup's LDS counter, requested one iteration before it is needed.  Pairs are
     // handed out in increasing order, so a wave stops at its first pair past the range and
     // no pair is skipped.  The waves of a CU's workgroup thereby finish together however the
     // CU's issue arbitration favours them.
     int c_cur = wave, c_nxt = wave + kSqWaves, pend = 0;
-    if (c_cur < n_pairs && lane == 0) pend = atomicAdd(&sh_next, 1);
 
     const int64_t tok_base = kvrow * (int64_t)a.token_cap;
     const uint8_t* kc_row = a.k_codes + tok_base * kRowBytes;
@@ -174,12 +164,24 @@ __global__ __launch_bounds__(kSqBlock) void attn_split_kernel(AttnArgs a) {
     // again, from the L2), so the compiler knows how many loads are in flight at each use and
     // waits for exactly the one it needs.
     Loads cur;
-    uint32_t tag;
-    if (c_cur < n_pairs) {
+    if (c_cur < n_pairs) {   // the first iteration's loads, in flight during the set-up below
         load_kp(cur, 0);
         load_kc(cur, 0);
         load_vp(cur, 0);
         load_vc(cur, 0);
+    }
+    if (threadIdx.x == 0) sh_next = 0;
+    __syncthreads();
+
+    // ---- fp16 residual first (split rs.res_split), as separate states: its loads meet a memory
+    // system that is not loaded yet, and the waves that take it start on the pairs later
+    float mr[1] = {-INFINITY}, lr[1] = {0.0f};
+    if (split == rs.res_split)
+        residual_states<1, kSqWaves>(a, rs, qrow, kvrow, wave, &sh_o[0][kSqWaves + wave][0], kSqSlots * kD, mr, lr);
+    if (c_cur < n_pairs && lane == 0) pend = atomicAdd(&sh_next, 1);
+
+    uint32_t tag;
+    if (c_cur < n_pairs) {
         tag = settle_tag(tag_v);
         for (int it = 0;;) {
             constexpr int nxt = 1;
