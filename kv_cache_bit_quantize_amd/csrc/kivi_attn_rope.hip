@@ -130,11 +130,6 @@ __global__ __launch_bounds__(kBlock) void attn_rope_kernel(AttnArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int t8 = lane >> 3, k8 = lane & 7;
 
-    if (threadIdx.x < kRpPairs) sh_w[threadIdx.x] = pow(a.rope_base, -2.0 * (double)threadIdx.x / (double)kD);
-    __syncthreads();
-    for (int i = threadIdx.x; i < GS * kRpPairs; i += kBlock) sh_ed[i / kRpPairs][i % kRpPairs] = turn((double)(i / kRpPairs) * sh_w[i % kRpPairs]);
-    __syncthreads();
-
     const RowState rs = row_state(a, kvrow, split);
     if (split >= rs.splits) return;   // (ragged batch) this row uses fewer splits: the whole workgroup leaves
     const int n_kg = rs.n_quant / GS;
@@ -241,14 +236,22 @@ __global__ __launch_bounds__(kBlock) void attn_rope_kernel(AttnArgs a) {
     for (int c = 0; c < kVCh; ++c) o[c] = 0.0f;
     float* pw = &sh_p[wave][0];
 
-    uint32_t tag;
-    if (n_groups > 0) {
-        KLoad kl;
-        VLoad vl;
-        PLoad pn;
+    KLoad kl;
+    VLoad vl;
+    PLoad pn;
+    if (n_groups > 0) {   // the first iteration's loads, in flight while the turn tables are built
         load_k(kl, 0);
         load_v(vl, 0);
         load_kp(pn, 0);
+    }
+    // pair frequencies and the in-group turns exp(i*d*w)
+    if (threadIdx.x < kRpPairs) sh_w[threadIdx.x] = pow(a.rope_base, -2.0 * (double)threadIdx.x / (double)kD);
+    __syncthreads();
+    for (int i = threadIdx.x; i < GS * kRpPairs; i += kBlock) sh_ed[i / kRpPairs][i % kRpPairs] = turn((double)(i / kRpPairs) * sh_w[i % kRpPairs]);
+    __syncthreads();
+
+    uint32_t tag;
+    if (n_groups > 0) {
         tag = settle_tag(tag_v);
         for (int gi = 0; gi < n_groups; ++gi) {
             // ---- turn of the group start for the 64 pairs (lane = pair), through LDS
