@@ -51,3 +51,21 @@ def key_values(fname):
         k, v = [s.strip() for s in line.split(":", 1)]
         out[k] = float(v) if "." in v else int(v)
     return out
+
+
+def layout_tiles():
+    """Entries of layout_tiles.txt: ("onehot", kind, t, j, offset, shift) and
+    ("pattern", kind, offset, byte)."""
+    out = []
+    for line in open(os.path.join(GOLDEN, "layout_tiles.txt")):
+        line = line.split("#", 1)[0].strip()
+        if not line:
+            continue
+        f = line.split()
+        if f[0] == "onehot":
+            out.append(("onehot", f[1], int(f[2]), int(f[3]), int(f[4]), int(f[5])))
+        elif f[0] == "pattern":
+            out.append(("pattern", f[1], int(f[2]), int(f[3], 16)))
+        else:
+            raise ValueError(f"layout_tiles.txt: unknown entry {line!r}")
+    return out
