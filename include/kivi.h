@@ -143,22 +143,34 @@ int kivi_prefill(const uint16_t* k, const uint16_t* v, int32_t tokens, int64_t s
 int kivi_append_flush(kivi_cache* cache, const uint16_t* k_new, const uint16_t* v_new,
                       int32_t* flushed, void* stream);
 
-/* Fused decode attention over the whole cache (dequantized history followed by the
- * residual), one query per head: out = softmax(sm_scale * q.K^T) . V.
+/* Fused decode attention over the whole cache, one query per head: the quantized history,
+ * dequantized (zero + code * scale), followed by the fp16 residual ring, oldest first (record
+ * "KV bytes basis": the grouped history quantized and the newest tokens kept in 16-bit
+ * floats; the 2-bit bytes counted per token are what this call streams), with the error
+ * judged at this output ("Your KV cache doesn't have a bit problem...", paragraph 3):
+ * out = softmax(sm_scale * q.K^T) . V.
  * q: fp16 [batch][q_heads][D]; q_heads a multiple of kv_heads, query head hq reads kv
  * head hq / (q_heads / kv_heads).  out: fp16 [batch][q_heads][D].  lse (nullable): fp32
  * [batch][q_heads], natural log of the softmax denominator including sm_scale.
  * The context is split into num_splits parts per row (0 = automatic) and the partial
  * softmax states are merged with a log-sum-exp merge inside the same kernel launch.
+ *
  * workspace: device scratch of at least kivi_decode_attn_workspace(cache, q_heads,
  * num_splits) bytes, 256-byte aligned, owned by the caller.  The whole workspace must be
  * zero before the first call that uses it (clear it once after allocating it); calls keep
- * it consistent afterwards.  Its first round_up(2*batch*q_heads*4, 256) bytes hold a
- * per-row arrival counter (zero again after every completed call) and a per-row call
- * epoch; the rest holds the split partials, each value stored with its call's tag.  A
- * workspace serves one (batch, q_heads) shape: clear it again before using it for another.
- * Calls that share a workspace must not run concurrently.  KIVI_ERR_SHAPE if the context is
- * empty. */
+ * it consistent afterwards.  Layout: a 32-bit status word at byte 0 (in a 256-byte block),
+ * then a per-query-row arrival counter (zero again after every completed call) and a
+ * per-query-row call epoch (round_up(8*batch*q_heads, 256) bytes), then the split partials,
+ * each value stored with its call's tag.  The tag of a call's partials for a group of query
+ * rows is one more than the largest epoch of those rows, and the merge sets each row's epoch
+ * to it, so every attention entry point of this header (plain, pre-RoPE, ragged, fused step,
+ * 2- or 4-bit) may use one workspace in any order for caches of one (batch, q_heads) shape;
+ * clear it again before using it for another shape.  Calls that share a workspace must not run
+ * concurrently.  Status word: the kernels OR in KIVI_WS_POLL_TIMEOUT when a merge gave up
+ * waiting for a split partial (the merge polls each value a bounded number of times); the
+ * rows concerned get out = NaN and lse = NaN.  The library never clears the word.
+ * KIVI_ERR_SHAPE if the context is empty. */
+#define KIVI_WS_POLL_TIMEOUT 1
 int kivi_decode_attn(const kivi_cache* cache, const uint16_t* q, int32_t q_heads,
                      float sm_scale, uint16_t* out, float* lse, void* workspace,
                      size_t workspace_bytes, int32_t num_splits, void* stream);
@@ -275,6 +287,14 @@ int kivi_decode_attn_fp16(const uint16_t* k, const uint16_t* v, int32_t batch, i
  * KIVI_ERR_NULL if exactly one of the two is NULL.  No device access. */
 int kivi_time_next_attention(void* start_event, void* stop_event);
 
+/* Testing hook of the merge's bounded wait (not a step of the method): the next attention call
+ * of the calling thread that passes validation polls each split partial at most max_polls
+ * times (0 = the library's bound) and waits for the tag tag_skew above its own (0 = its own).
+ * With tag_skew != 0 no partial ever matches, so a multi-split call takes the give-up path
+ * (NaN rows, KIVI_WS_POLL_TIMEOUT) after max_polls short sleeps per value, and every kernel
+ * still ends.  KIVI_ERR_SHAPE if max_polls < 0.  No device access. */
+int kivi_test_next_attention_merge(int32_t max_polls, uint32_t tag_skew);
+
 /* Host-only helpers (no device access; safe without a GPU). */
 
 /* Split count that kivi_decode_attn uses for num_splits == 0 (depends on shapes only).
@@ -283,6 +303,18 @@ int32_t kivi_decode_attn_splits(const kivi_cache* cache, int32_t q_heads);
 
 /* Workspace bytes kivi_decode_attn needs for this shape and split count (0 = auto). */
 size_t kivi_decode_attn_workspace(const kivi_cache* cache, int32_t q_heads, int32_t num_splits);
+
+/* Split count that kivi_decode_step (pre_rope == 0) or kivi_decode_step_rope (pre_rope != 0)
+ * uses for num_splits == 0: the attention's choice on the state after the step's append
+ * (record "KV bytes basis": a full ring first gives its oldest tokens to the grouped history,
+ * which lengthens it).  A negative KIVI_ERR_* code for an invalid shape or state, or
+ * KIVI_ERR_CAPACITY if that append would pass token_cap. */
+int32_t kivi_decode_step_splits(const kivi_cache* cache, int32_t q_heads, int32_t pre_rope);
+
+/* Workspace bytes that kivi_decode_step / kivi_decode_step_rope (pre_rope != 0) needs with
+ * num_splits (0 = kivi_decode_step_splits): kivi_decode_attn_workspace of the state after the
+ * append.  0 for an invalid shape or state, or an append past token_cap. */
+size_t kivi_decode_step_workspace(const kivi_cache* cache, int32_t q_heads, int32_t num_splits, int32_t pre_rope);
 
 /* Split count kivi_decode_attn_rope uses for num_splits == 0 (depends on shapes only);
  * a negative KIVI_ERR_* code for an invalid shape or state. */
@@ -301,7 +333,12 @@ size_t kivi_decode_attn_fp16_workspace(int32_t batch, int32_t kv_heads, int32_t 
                                        int32_t num_splits);
 
 /* Buffer sizes (bytes) for a cache of this shape (pointer fields are ignored):
- * codes = k_codes + v_codes, pairs = k_sz + v_sz, residual = k_res + v_res. */
+ * codes = k_codes + v_codes, pairs = k_sz + v_sz, residual = k_res + v_res.  The record
+ * kv-efficiency/kivi-2bit-llama2-13b-mha-4k ("KV bytes basis") counts the 2-bit codes as
+ * layers x kv heads x head_dim x 2 (K and V) x 2 bits per token and the residual as the
+ * newest R tokens in 16-bit floats; codes and residual here are those counts for this cache's
+ * capacity (token_cap and residual_cap), and pairs adds the fp16 (scale, zero) per group that
+ * the record leaves out (4 bytes per G elements). */
 int kivi_cache_bytes(const kivi_cache* shape, size_t* codes, size_t* pairs, size_t* residual);
 
 /* Static description of an error code. */

@@ -126,10 +126,30 @@ int32_t ragged_auto_splits(const kivi_cache* c, int32_t q_heads) {
     return (int32_t)s;
 }
 
-// leading area of the attention workspace: one arrival counter per query row, then one call
-// epoch per query row (the tag of the last merged call's partials)
-size_t counter_bytes(const kivi_cache* c, int32_t q_heads) {
-    return (2 * (size_t)c->batch * (size_t)q_heads * sizeof(uint32_t) + 255) & ~(size_t)255;
+// Leading area of an attention workspace: the status word in a 256-byte block of its own, then
+// one arrival counter per query row and one call epoch per query row (the tag of the last
+// partials merged for that row), rounded up to 256 bytes.
+constexpr size_t kStatusBytes = 256;
+size_t header_bytes(int64_t q_rows) {
+    return kStatusBytes + ((2 * (size_t)q_rows * sizeof(uint32_t) + 255) & ~(size_t)255);
+}
+size_t counter_bytes(const kivi_cache* c, int32_t q_heads) { return header_bytes((int64_t)c->batch * q_heads); }
+
+// Test hook of the merge's bounded wait (kivi_test_next_attention_merge): consumed by the next
+// attention call of this thread that passes validation.
+thread_local int32_t t_merge_polls = 0;
+thread_local uint32_t t_merge_skew = 0;
+void take_merge_test(AttnArgs* a) {
+    a->max_polls = t_merge_polls;
+    a->tag_skew = t_merge_skew;
+    t_merge_polls = 0;
+    t_merge_skew = 0;
+}
+// Header pointers of a workspace
+void set_header(AttnArgs* a, void* workspace, size_t header) {
+    a->status = static_cast<uint32_t*>(workspace);
+    a->counters = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + kStatusBytes);
+    a->ws = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + header);
 }
 
 QuantArgs quant_args(const kivi_cache* c, const uint16_t* src, int32_t tokens, int64_t stride,
@@ -150,6 +170,25 @@ QuantArgs quant_args(const kivi_cache* c, const uint16_t* src, int32_t tokens, i
     return a;
 }
 
+// The state after one append (record "KV bytes basis": the newest R tokens stay in 16-bit
+// floats, only grouped history is quantized): a full ring first gives its oldest F tokens
+// (F = G, or R with KIVI_FLUSH_ALL) to the history, then the new token enters the ring.
+// *flush tells whether a flush happens.  Expects a valid shape and state.
+int post_append_state(const kivi_cache* c, kivi_cache* next, bool* flush) {
+    const int G = c->group, R = c->residual_cap;
+    const int F = (c->flags & KIVI_FLUSH_ALL) ? R : G;   // tokens a flush moves
+    *flush = c->n_res == R;
+    if (*flush && c->n_quant + F > c->token_cap) return KIVI_ERR_CAPACITY;
+    *next = *c;
+    if (*flush) {
+        next->n_quant += F;
+        next->res_head = (c->res_head + F) % R;
+        next->n_res -= F;
+    }
+    next->n_res += 1;
+    return KIVI_OK;
+}
+
 // Validates an append and fills its arguments; *next receives the state after it.
 int prepare_append(const kivi_cache* c, const uint16_t* k_new, const uint16_t* v_new, AppendArgs* a,
                    kivi_cache* next) {
@@ -161,22 +200,15 @@ int prepare_append(const kivi_cache* c, const uint16_t* k_new, const uint16_t* v
     if (k_new == nullptr || v_new == nullptr) return KIVI_ERR_NULL;
     if (!aligned16(k_new) || !aligned16(v_new)) return KIVI_ERR_SHAPE;
     const int G = c->group, R = c->residual_cap;
-    const int F = (c->flags & KIVI_FLUSH_ALL) ? R : G;   // tokens a flush moves
-    const bool flush = c->n_res == R;
-    if (flush && c->n_quant + F > c->token_cap) return KIVI_ERR_CAPACITY;
-    int n_quant = c->n_quant, n_res = c->n_res, head = c->res_head;
+    bool flush = false;
+    if ((st = post_append_state(c, next, &flush)) != KIVI_OK) return st;
     a->k_new = k_new;
     a->v_new = v_new;
     a->rows = rows_of(c);
     a->do_flush = flush ? 1 : 0;
-    a->flush_slot = head;
-    a->flush_group = n_quant / G;
-    if (flush) {
-        n_quant += F;
-        head = (head + F) % R;
-        n_res -= F;
-    }
-    a->new_slot = (head + n_res) % R;
+    a->flush_slot = c->res_head;
+    a->flush_group = c->n_quant / G;
+    a->new_slot = (next->res_head + next->n_res - 1) % R;
     a->token_cap = c->token_cap;
     a->residual_cap = R;
     a->k_codes = c->k_codes;
@@ -190,10 +222,6 @@ int prepare_append(const kivi_cache* c, const uint16_t* k_new, const uint16_t* v
     a->group = G;
     a->flush_all = (c->flags & KIVI_FLUSH_ALL) ? 1 : 0;
     a->bits = code_bits(c);
-    *next = *c;
-    next->n_quant = n_quant;
-    next->n_res = n_res + 1;
-    next->res_head = head;
     return KIVI_OK;
 }
 
@@ -258,8 +286,7 @@ int prepare_attn(const kivi_cache* c, const uint16_t* q, int32_t q_heads, float 
     a.v_sz = c->v_sz;
     a.k_res = c->k_res;
     a.v_res = c->v_res;
-    a.counters = static_cast<uint32_t*>(workspace);
-    a.ws = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + counter_bytes(c, q_heads));
+    set_header(&a, workspace, counter_bytes(c, q_heads));
     a.out = out;
     a.lse = lse;
     a.sm_log2 = (float)((double)sm_scale * 1.4426950408889634);
@@ -288,6 +315,7 @@ int prepare_attn(const kivi_cache* c, const uint16_t* q, int32_t q_heads, float 
     a.slot_budget = (int32_t)(a.nq > 1 || code_bits(c) == 4 ? kTargetBlocks : kTargetBlocksSingle);
     a.group = c->group;
     a.bits = code_bits(c);
+    take_merge_test(&a);
     *pa = a;
     return KIVI_OK;
 }
@@ -318,9 +346,7 @@ int32_t fp16_auto_splits(int32_t batch, int32_t kv_heads, int32_t tokens, int32_
     return (int32_t)s;
 }
 
-size_t fp16_counter_bytes(int32_t batch, int32_t q_heads) {
-    return (2 * (size_t)batch * (size_t)q_heads * sizeof(uint32_t) + 255) & ~(size_t)255;
-}
+size_t fp16_counter_bytes(int32_t batch, int32_t q_heads) { return header_bytes((int64_t)batch * q_heads); }
 
 // Events for the next attention launch of this thread (kivi_time_next_attention).
 thread_local hipEvent_t t_timing[2] = {nullptr, nullptr};
@@ -538,8 +564,7 @@ int kivi_decode_attn_fp16(const uint16_t* k, const uint16_t* v, int32_t batch, i
     if (reinterpret_cast<uintptr_t>(workspace) & 255u) return KIVI_ERR_WORKSPACE;
     AttnArgs a{};
     a.q = q;
-    a.counters = static_cast<uint32_t*>(workspace);
-    a.ws = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + fp16_counter_bytes(batch, q_heads));
+    set_header(&a, workspace, fp16_counter_bytes(batch, q_heads));
     a.out = out;
     a.lse = lse;
     a.sm_log2 = (float)((double)sm_scale * 1.4426950408889634);
@@ -555,9 +580,17 @@ int kivi_decode_attn_fp16(const uint16_t* k, const uint16_t* v, int32_t batch, i
     a.kv_stride = token_stride;
     a.n_tokens = tokens;
     a.tokens_per_split = (tokens + splits - 1) / splits;
+    take_merge_test(&a);
     hipEvent_t t0, t1;
     take_timing(&t0, &t1);
     return hip_status(launch_decode_attn_fp16(a, (hipStream_t)stream, t0, t1));
+}
+
+int kivi_test_next_attention_merge(int32_t max_polls, uint32_t tag_skew) {
+    if (max_polls < 0) return KIVI_ERR_SHAPE;
+    t_merge_polls = max_polls;
+    t_merge_skew = tag_skew;
+    return KIVI_OK;
 }
 
 int kivi_time_next_attention(void* start_event, void* stop_event) {
@@ -640,6 +673,27 @@ int32_t kivi_decode_attn_rope_splits(const kivi_cache* c, int32_t q_heads) {
     if ((st = check_state(c)) != KIVI_OK) return st;
     if (q_heads <= 0 || q_heads % c->kv_heads != 0) return KIVI_ERR_SHAPE;
     return rope_auto_splits(c, q_heads);
+}
+
+int32_t kivi_decode_step_splits(const kivi_cache* c, int32_t q_heads, int32_t pre_rope) {
+    int st = check_shape(c);
+    if (st != KIVI_OK) return st;
+    if ((st = check_state(c)) != KIVI_OK) return st;
+    if (q_heads <= 0 || q_heads % c->kv_heads != 0) return KIVI_ERR_SHAPE;
+    kivi_cache next;
+    bool flush;
+    if ((st = post_append_state(c, &next, &flush)) != KIVI_OK) return st;
+    return pre_rope ? rope_auto_splits(&next, q_heads) : auto_splits(&next, q_heads);
+}
+
+size_t kivi_decode_step_workspace(const kivi_cache* c, int32_t q_heads, int32_t num_splits, int32_t pre_rope) {
+    if (num_splits < 0) return 0;
+    const int32_t s = num_splits > 0 ? num_splits : kivi_decode_step_splits(c, q_heads, pre_rope);
+    if (s < 0) return 0;
+    kivi_cache next;
+    bool flush;
+    if (post_append_state(c, &next, &flush) != KIVI_OK) return 0;
+    return kivi_decode_attn_workspace(&next, q_heads, s);
 }
 
 int kivi_decode_step_rope(kivi_cache* c, const uint16_t* k_new, const uint16_t* v_new, const uint16_t* q,

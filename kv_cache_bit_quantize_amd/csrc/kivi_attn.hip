@@ -62,7 +62,7 @@ __global__ __launch_bounds__(kSqBlock) void attn_split_kernel(AttnArgs a) {
     const int hq = (int)(qrow % a.q_heads);
     const int64_t kvrow = b * a.kv_heads + hq / a.ratio;
     if (a.k_new != nullptr && split == 0 && hq % a.ratio == 0) store_new_token(a, kvrow);
-    const uint32_t tag_v = partial_tag(a, qrow);
+    const TagLoads<1> tag_v = partial_tag<1>(a, qrow);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform, as the compiler sees it
     const int gh = lane >> 5;          // group of the wave-iteration this lane serves
@@ -338,7 +338,7 @@ __global__ __launch_bounds__(kSqBlock) void attn_split_kernel(AttnArgs a) {
         sh_l[0][kSqWaves + wave] = lr[0];
     }
     __syncthreads();
-    finish_block<1, kSqWaves>(a, rs.splits, split, qrow, qrow, tag, sh_o, sh_m, sh_l);
+    finish_block<1, kSqWaves>(a, rs.splits, split, qrow, tag, sh_o, sh_m, sh_l);
 }
 
 hipError_t launch_decode_attn(const AttnArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {

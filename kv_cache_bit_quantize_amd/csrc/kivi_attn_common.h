@@ -100,23 +100,44 @@ __device__ __forceinline__ uint64_t load_coherent(uint64_t* p) {
 __device__ __forceinline__ uint64_t tagged(float v, uint32_t tag) {
     return (uint64_t)__builtin_bit_cast(uint32_t, v) | ((uint64_t)tag << 32);
 }
-// The tag of this call's split partials for counter row `counter`: one more than the epoch
-// that the previous call's merging workgroup stored (0 in a cleared workspace).  Loaded when
-// the workgroup starts; it is needed only when the workgroup ends.
-__device__ __forceinline__ uint32_t partial_tag(const AttnArgs& a, int64_t counter) {
-    return __hip_atomic_load(&a.counters[a.q_rows + counter], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+// The tag of this call's split partials for query rows qrow0..qrow0+NQ-1: one more than the
+// largest call epoch of those rows.  A row's epoch is the tag of the last partials merged for
+// it (0 in a cleared workspace), whichever kernel wrote them, so the tag is above every tag
+// left in the rows' partial slots, also when entry points that group query rows differently
+// (one row per workgroup, or a KV head's query group) share a workspace.  The epochs are
+// loaded when the workgroup starts; they are needed only when it ends (settle_tag).
+template <int NQ>
+struct TagLoads {
+    uint32_t e[NQ];
+};
+template <int NQ>
+__device__ __forceinline__ TagLoads<NQ> partial_tag(const AttnArgs& a, int64_t qrow0) {
+    TagLoads<NQ> t;
+#pragma unroll
+    for (int r = 0; r < NQ; ++r)
+        t.e[r] = __hip_atomic_load(&a.counters[a.q_rows + qrow0 + r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return t;
 }
 // The tag as a wave-uniform scalar, read where the caller places this call: after its first
-// loads are issued, so that the wait for the tag's load overlaps the wait for them (a later
-// first use, after the loop, could wait for every load in flight).
-__device__ __forceinline__ uint32_t settle_tag(uint32_t v) {
-    asm volatile("" : "+v"(v));
-    return __builtin_amdgcn_readfirstlane(v);
+// loads are issued, so that the wait for the epochs overlaps the wait for them (a later first
+// use, after the loop, could wait for every load in flight).
+template <int NQ>
+__device__ __forceinline__ uint32_t settle_tag(TagLoads<NQ> t) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int r = 0; r < NQ; ++r) {
+        uint32_t v = t.e[r];
+        asm volatile("" : "+v"(v));
+        m = max(m, v);
+    }
+    return __builtin_amdgcn_readfirstlane(m) + 1u;
 }
 // Polls of a partial value whose store has not landed yet (each after a short sleep).  The
 // value was stored before its workgroup's arrival was counted, so it lands within a memory
-// round trip; the bound only guarantees that the loop ends.
+// round trip; the bound only guarantees that the loop ends.  A merge that reaches it writes
+// NaN for the row and sets kWsPollTimeout in the workspace's status word.
 constexpr int kMaxPolls = 1 << 22;
+constexpr uint32_t kWsPollTimeout = 1u;   // the status word's bit (KIVI_WS_POLL_TIMEOUT)
 
 // The (scale, zero) pairs of one value token, kD / GS of them, loaded at their own width (a
 // wider load would read past the last token of the last row) and returned as one word per
@@ -330,25 +351,39 @@ __device__ __forceinline__ void store_new_token(const AttnArgs& a, int64_t kvrow
 // workgroup, with each thread's coherent loads issued together: a thread merges, for one
 // (row, channel), every lpp-th split online (lpp = THREADS / 128 for one row, else 1), and
 // the lpp threads of a channel combine in LDS.  out = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M),
-// lse = (M + log2 L) ln 2.  Re-arms the arrival counter.
+// lse = (M + log2 L) ln 2.  A value whose tag is not this call's after the poll bound marks
+// its row lost (sh_lost, cleared by the caller): the row's out and lse are written as NaN and
+// the workspace status word gets kWsPollTimeout.  Re-arms the arrival counter and moves every
+// row's epoch to this call's tag.
 constexpr int kMergeBatch = 8;
 template <int NQ, int THREADS = kBlock>
-__device__ __forceinline__ void merge_rows(const AttnArgs& a, int splits, int64_t qrow0, int64_t counter,
-                                           uint32_t tag) {
+__device__ __forceinline__ void merge_rows(const AttnArgs& a, int splits, int64_t qrow0, uint32_t tag, int* sh_lost) {
     constexpr int kLpp = NQ == 1 ? THREADS / kD : 1;
     static_assert(NQ != 1 || (THREADS % kD == 0 && kLpp >= 2), "one row needs whole multiples of 128 threads");
+    constexpr int kSweep = THREADS / kLpp;                  // (row, channel) pairs per pass
+    constexpr int kIters = (NQ * kD + kSweep - 1) / kSweep;
     __shared__ float sh_mo[kLpp > 1 ? kLpp - 1 : 1][kD + 2];
     const int t = threadIdx.x, sub = kLpp > 1 ? t / kD : 0;
     const int64_t stride = a.q_rows * kPart;
-    for (int idx = kLpp > 1 ? (t % kD) : t; idx < NQ * kD; idx += THREADS / kLpp) {
+    const uint32_t want = tag + a.tag_skew;                 // tag_skew: a test hook, 0 otherwise
+    const int max_polls = a.max_polls > 0 ? a.max_polls : kMaxPolls;
+    float Mi[kIters], Li[kIters], Oi[kIters];
+#pragma unroll
+    for (int it = 0; it < kIters; ++it) {
+        const int idx = (kLpp > 1 ? (t % kD) : t) + it * kSweep;
+        Mi[it] = -INFINITY;
+        Li[it] = Oi[it] = 0.0f;
+        if (idx >= NQ * kD) continue;
         const int r = idx / kD, j = idx % kD;
         uint64_t* rowp = a.ws + (qrow0 + r) * kPart;
-        // a value of this call: loaded again until its tag is this call's
+        bool lost = false;
+        // a value of this call: loaded again until its tag is this call's, at most max_polls times
         auto settle = [&](uint64_t* p, uint64_t v) {
-            for (int n = 0; (uint32_t)(v >> 32) != tag && n < kMaxPolls; ++n) {
+            for (int n = 0; (uint32_t)(v >> 32) != want && n < max_polls; ++n) {
                 __builtin_amdgcn_s_sleep(1);
                 v = load_coherent(p);
             }
+            lost |= (uint32_t)(v >> 32) != want;
             return __builtin_bit_cast(float, (uint32_t)v);
         };
         float M = -INFINITY, L = 0.0f, O = 0.0f;
@@ -387,43 +422,54 @@ __device__ __forceinline__ void merge_rows(const AttnArgs& a, int splits, int64_
                 M = mn;
             }
         }
-        if (kLpp > 1) {   // one iteration per thread here: the barrier is reached by all
-            if (sub > 0) {
-                sh_mo[sub - 1][j] = O;
-                if (j == 0) {
-                    sh_mo[sub - 1][kD] = M;
-                    sh_mo[sub - 1][kD + 1] = L;
-                }
-            }
-            __syncthreads();
-            if (sub > 0) return;
-#pragma unroll
-            for (int k = 0; k < kLpp - 1; ++k) {
-                const float m1 = sh_mo[k][kD], l1 = sh_mo[k][kD + 1], o1 = sh_mo[k][j];
-                const float mn = fmaxf(M, m1);
-                const float al = M == -INFINITY ? 0.0f : exp2f(M - mn), be = m1 == -INFINITY ? 0.0f : exp2f(m1 - mn);
-                L = fmaf(L, al, l1 * be);
-                O = fmaf(O, al, o1 * be);
-                M = mn;
+        if (lost) sh_lost[r] = 1;
+        if (kLpp > 1 && sub > 0) {
+            sh_mo[sub - 1][j] = O;
+            if (j == 0) {
+                sh_mo[sub - 1][kD] = M;
+                sh_mo[sub - 1][kD + 1] = L;
             }
         }
-        a.out[(qrow0 + r) * kD + j] = (uint16_t)f2h(L > 0.0f ? O / L : 0.0f);
-        if (j == 0 && a.lse != nullptr) a.lse[qrow0 + r] = (M + log2f(L)) * 0.69314718055994531f;
+        Mi[it] = M;
+        Li[it] = L;
+        Oi[it] = O;
     }
-    if (t == 0) {
-        a.counters[counter] = 0u;
-        a.counters[a.q_rows + counter] = tag;   // the next call's partials carry tag + 1
+    __syncthreads();
+    if (sub > 0) return;
+#pragma unroll
+    for (int it = 0; it < kIters; ++it) {
+        const int idx = (kLpp > 1 ? (t % kD) : t) + it * kSweep;
+        if (idx >= NQ * kD) continue;
+        const int r = idx / kD, j = idx % kD;
+        float M = Mi[it], L = Li[it], O = Oi[it];
+#pragma unroll
+        for (int k = 0; k < kLpp - 1; ++k) {
+            const float m1 = sh_mo[k][kD], l1 = sh_mo[k][kD + 1], o1 = sh_mo[k][j];
+            const float mn = fmaxf(M, m1);
+            const float al = M == -INFINITY ? 0.0f : exp2f(M - mn), be = m1 == -INFINITY ? 0.0f : exp2f(m1 - mn);
+            L = fmaf(L, al, l1 * be);
+            O = fmaf(O, al, o1 * be);
+            M = mn;
+        }
+        const bool lost = sh_lost[r] != 0;
+        a.out[(qrow0 + r) * kD + j] = lost ? 0x7E00u : (uint16_t)f2h(L > 0.0f ? O / L : 0.0f);
+        if (j == 0 && a.lse != nullptr) a.lse[qrow0 + r] = lost ? __builtin_nanf("") : (M + log2f(L)) * 0.69314718055994531f;
     }
+    if (t < NQ) {
+        if (sh_lost[t]) __hip_atomic_fetch_or(a.status, kWsPollTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        a.counters[a.q_rows + qrow0 + t] = tag;   // the next call's partials for this row carry a larger tag
+    }
+    if (t == 0) a.counters[qrow0] = 0u;
 }
 
 // End of a WAVES-wave workgroup: merge its 2*WAVES states per row (empty states skipped), then write the
 // output directly (one split) or the split partial, and let the last workgroup of the row
 // group to arrive merge the partials.  Every partial value carries the call's tag (tag, from
 // partial_tag at the workgroup's start), so the merging workgroup, which loads after its own
-// arrival returned the final count, tells a value of this call from a stale one.
+// arrival returned the final count, tells a value of this call from a stale one.  The
+// arrival counter of a row group is the one of its first query row, in every kernel.
 template <int NQ, int WAVES = kWaves>
-__device__ __forceinline__ void finish_block(const AttnArgs& a, int splits, int split, int64_t qrow0, int64_t counter,
-                                             uint32_t tag, const float (*sh_o)[2 * WAVES][kD],
+__device__ __forceinline__ void finish_block(const AttnArgs& a, int splits, int split, int64_t qrow0, uint32_t tag, const float (*sh_o)[2 * WAVES][kD],
                                              const float (*sh_m)[2 * WAVES], const float (*sh_l)[2 * WAVES]) {
     constexpr int kS = 2 * WAVES;
     // The arrival is counted first, by the last wave, before the merge below and the partial
@@ -434,7 +480,7 @@ __device__ __forceinline__ void finish_block(const AttnArgs& a, int splits, int 
     constexpr int kArrive = 64 * (WAVES - 1);
     uint32_t arrived = 0;
     if (splits > 1 && threadIdx.x == kArrive)
-        arrived = __hip_atomic_fetch_add(&a.counters[counter], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        arrived = __hip_atomic_fetch_add(&a.counters[qrow0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     for (int idx = threadIdx.x; idx < NQ * kD; idx += 64 * WAVES) {
         const int r = idx / kD, j = idx % kD;
         float M = -INFINITY;
@@ -463,9 +509,11 @@ __device__ __forceinline__ void finish_block(const AttnArgs& a, int splits, int 
     }
     if (splits == 1) return;
     __shared__ bool sh_last;
+    __shared__ int sh_lost[NQ];
     if (threadIdx.x == kArrive) sh_last = arrived == (unsigned)(splits - 1);
+    if (threadIdx.x < NQ) sh_lost[threadIdx.x] = 0;
     __syncthreads();
-    if (sh_last) merge_rows<NQ, 64 * WAVES>(a, splits, qrow0, counter, tag);
+    if (sh_last) merge_rows<NQ, 64 * WAVES>(a, splits, qrow0, tag, sh_lost);
 }
 
 }  // namespace kivi

@@ -36,7 +36,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     const int64_t kvrow = grow / chunks;
     const int chunk = (int)(grow % chunks);
     const int64_t qrow0 = (kvrow / a.kv_heads) * a.q_heads + (kvrow % a.kv_heads) * a.ratio + chunk * NQ;
-    const uint32_t tag_v = partial_tag(a, grow);
+    const TagLoads<NQ> tag_v = partial_tag<NQ>(a, qrow0);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int kt = lane >> 2, kq = lane & 3;        // logits: token kt, channels 32kq..32kq+31
@@ -192,7 +192,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
         }
     }
     __syncthreads();
-    finish_block<NQ>(a, a.splits, split, qrow0, grow, tag, sh_o, sh_m, sh_l);
+    finish_block<NQ>(a, a.splits, split, qrow0, tag, sh_o, sh_m, sh_l);
 }
 
 hipError_t launch_decode_attn_fp16(const AttnArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {

@@ -52,7 +52,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     const int chunk = (int)(grow % chunks);
     const int64_t qrow0 = (kvrow / a.kv_heads) * a.q_heads + (kvrow % a.kv_heads) * a.ratio + chunk * NQ;
     if (a.k_new != nullptr && split == 0 && chunk == 0) store_new_token(a, kvrow);
-    const uint32_t tag_v = partial_tag(a, grow);
+    const TagLoads<NQ> tag_v = partial_tag<NQ>(a, qrow0);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int mrow = lane & 15, kb = lane >> 4;   // matrix roles: token / A row, K block
@@ -293,7 +293,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
         }
     }
     __syncthreads();
-    finish_block<NQ>(a, rs.splits, split, qrow0, grow, tag, sh_o, sh_m, sh_l);
+    finish_block<NQ>(a, rs.splits, split, qrow0, tag, sh_o, sh_m, sh_l);
 }
 
 hipError_t launch_decode_attn_q4(const AttnArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {

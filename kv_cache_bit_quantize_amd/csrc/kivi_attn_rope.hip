@@ -125,7 +125,7 @@ __global__ __launch_bounds__(kBlock) void attn_rope_kernel(AttnArgs a) {
     const int64_t qrow = grid_row(a);
     const int64_t kvrow = (qrow / a.q_heads) * a.kv_heads + (qrow % a.q_heads) / a.ratio;
     if (a.k_new != nullptr && split == 0 && (qrow % a.q_heads) % a.ratio == 0) store_new_token(a, kvrow);
-    const uint32_t tag_v = partial_tag(a, qrow);
+    const TagLoads<1> tag_v = partial_tag<1>(a, qrow);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int t8 = lane >> 3, k8 = lane & 7;
@@ -429,7 +429,7 @@ __global__ __launch_bounds__(kBlock) void attn_rope_kernel(AttnArgs a) {
         sh_l[0][kWaves + wave] = lr;
     }
     __syncthreads();
-    finish_block<1>(a, rs.splits, split, qrow, qrow, tag, sh_o, sh_m, sh_l);
+    finish_block<1>(a, rs.splits, split, qrow, tag, sh_o, sh_m, sh_l);
 }
 
 hipError_t launch_decode_attn_rope(const AttnArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {

@@ -67,7 +67,10 @@ struct AttnArgs {
     const uint16_t* v_res;
     uint64_t* ws;               // [splits][B*Hq][D+2] partial (o, m, l), log2 domain: each value's bits
                                 // in the low word, the call's tag in the high word
-    uint32_t* counters;         // [B*Hq] arrival counters, zero between calls
+    uint32_t* counters;         // [B*Hq] arrival counters (zero between calls), then [B*Hq] call epochs
+    uint32_t* status;           // the workspace's status word (bits ORed in: kWsPollTimeout)
+    int32_t max_polls;          // polls of a partial before the merge gives up (0: the default bound)
+    uint32_t tag_skew;          // test hook: the merge waits for tag + tag_skew (0 in every real call)
     uint16_t* out;              // [B][Hq][D]
     float* lse;                 // [B][Hq] or null
     float sm_log2;              // sm_scale * log2(e)

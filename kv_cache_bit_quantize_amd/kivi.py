@@ -21,7 +21,8 @@ EXPORTS = ["kivi_quantize_k_per_channel", "kivi_quantize_v_per_token", "kivi_pre
            "kivi_status_str", "kivi_time_next_attention", "kivi_decode_attn_fp16", "kivi_decode_attn_fp16_splits",
            "kivi_decode_attn_fp16_workspace", "kivi_append_flush_ragged", "kivi_decode_attn_ragged",
            "kivi_decode_attn_ragged_splits", "kivi_decode_attn_rope", "kivi_decode_attn_rope_splits",
-           "kivi_decode_attn_rope_ragged", "kivi_decode_attn_rope_ragged_splits", "kivi_decode_step_rope"]
+           "kivi_decode_attn_rope_ragged", "kivi_decode_attn_rope_ragged_splits", "kivi_decode_step_rope",
+           "kivi_decode_step_splits", "kivi_decode_step_workspace", "kivi_test_next_attention_merge"]
 
 KIVI_FLUSH_ALL = 1        # kivi_cache.flags: a full residual is flushed whole (else its oldest group)
 KIVI_CODES_4BIT = 2       # kivi_cache.flags: 4-bit codes (sixteen levels), token-major nibbles
@@ -80,12 +81,19 @@ def _load():
     L.kivi_decode_attn_fp16_splits.restype = i32
     L.kivi_decode_attn_fp16_workspace.argtypes = [i32, i32, i32, i32, i32]
     L.kivi_decode_attn_fp16_workspace.restype = C.c_size_t
+    L.kivi_decode_step_splits.argtypes = [cp, i32, i32]
+    L.kivi_decode_step_splits.restype = i32
+    L.kivi_decode_step_workspace.argtypes = [cp, i32, i32, i32]
+    L.kivi_decode_step_workspace.restype = C.c_size_t
+    L.kivi_test_next_attention_merge.argtypes = [i32, C.c_uint32]
     L.kivi_status_str.restype = C.c_char_p
     for name in EXPORTS:
         L[name].restype = L[name].restype if name in ("kivi_decode_attn_splits", "kivi_decode_attn_workspace",
                                                       "kivi_status_str", "kivi_decode_attn_fp16_splits",
                                                       "kivi_decode_attn_fp16_workspace",
-                                                      "kivi_decode_attn_ragged_splits") else C.c_int
+                                                      "kivi_decode_attn_ragged_splits",
+                                                      "kivi_decode_step_splits",
+                                                      "kivi_decode_step_workspace") else C.c_int
     return L
 
 
@@ -159,15 +167,10 @@ class Cache:
         return v
 
     def workspace(self, q_heads, num_splits=0):
-        """Attention workspace for this cache, also large enough for the state after the
-        next append (a decode step attends after its append, and a flush lengthens the history,
-        which can raise the automatic split count)."""
-        need = lib.kivi_decode_attn_workspace(C.byref(self.c), q_heads, num_splits)
-        flush = self.c.residual_cap if self.c.flags & KIVI_FLUSH_ALL else self.c.group
-        if self.c.n_res == self.c.residual_cap and self.c.n_quant + flush <= self.c.token_cap:
-            nxt = kivi_cache.from_buffer_copy(self.c)
-            nxt.n_quant += flush
-            need = max(need, lib.kivi_decode_attn_workspace(C.byref(nxt), q_heads, num_splits))
+        """Attention workspace for this cache, also large enough for a decode step (which
+        attends on the state after its append; the library sizes both)."""
+        need = max(lib.kivi_decode_attn_workspace(C.byref(self.c), q_heads, num_splits),
+                   lib.kivi_decode_step_workspace(C.byref(self.c), q_heads, num_splits, 0))
         if self._ws is None or self._ws.numel() < need:
             # zero-filled: the leading per-row arrival counters must start at zero
             self._ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=self.device)
@@ -297,13 +300,9 @@ def kivi_decode_step_rope(cache, k_new, v_new, q, sm_scale, rope_base=10000.0, o
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
     splits = num_splits
     if splits <= 0:   # the library's choice on the state after the append
-        nxt = kivi_cache.from_buffer_copy(cache.c)
-        flush = nxt.residual_cap if nxt.flags & KIVI_FLUSH_ALL else nxt.group
-        if nxt.n_res == nxt.residual_cap and nxt.n_quant + flush <= nxt.token_cap:
-            nxt.n_quant += flush
-        splits = lib.kivi_decode_attn_rope_splits(C.byref(nxt), Hq)
+        splits = lib.kivi_decode_step_splits(C.byref(cache.c), Hq, 1)
         if splits < 0:
-            raise KiviError(splits, "kivi_decode_attn_rope_splits")
+            raise KiviError(splits, "kivi_decode_step_splits")
     ws = workspace if workspace is not None else cache.workspace(Hq, splits)
     flushed = C.c_int32(0)
     _check(lib.kivi_decode_step_rope(C.byref(cache.c), _ptr(k_new), _ptr(v_new), _ptr(q), Hq, float(sm_scale),
@@ -424,6 +423,31 @@ def kivi_decode_attn_fp16_splits(batch, kv_heads, tokens, q_heads):
 
 def kivi_decode_attn_fp16_workspace(batch, kv_heads, tokens, q_heads, num_splits=0):
     return lib.kivi_decode_attn_fp16_workspace(batch, kv_heads, tokens, q_heads, num_splits)
+
+
+def kivi_decode_step_splits(cache, q_heads, pre_rope=False):
+    s = lib.kivi_decode_step_splits(C.byref(cache.c), q_heads, int(bool(pre_rope)))
+    if s < 0:
+        raise KiviError(s, "kivi_decode_step_splits")
+    return s
+
+
+def kivi_decode_step_workspace(cache, q_heads, num_splits=0, pre_rope=False):
+    return lib.kivi_decode_step_workspace(C.byref(cache.c), q_heads, num_splits, int(bool(pre_rope)))
+
+
+def kivi_test_next_attention_merge(max_polls, tag_skew):
+    """Testing hook: the next attention call of this thread polls each split partial at most
+    max_polls times and waits for its tag + tag_skew (tag_skew != 0: the give-up path)."""
+    _check(lib.kivi_test_next_attention_merge(int(max_polls), int(tag_skew)), "kivi_test_next_attention_merge")
+
+
+WS_POLL_TIMEOUT = 1   # workspace status word bit (KIVI_WS_POLL_TIMEOUT)
+
+
+def workspace_status(ws):
+    """The workspace's status word (its first 32-bit word; KIVI_WS_POLL_TIMEOUT bits)."""
+    return int(ws[:4].view(torch.int32).item())
 
 
 def kivi_decode_attn_splits(cache, q_heads):

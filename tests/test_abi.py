@@ -21,7 +21,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 22
+    assert len(names) == 25
     out = os.popen(f"nm -D --defined-only {kivi.LIB_PATH}").read()
     exported = set(re.findall(r" T (kivi_\w+)$", out, re.M))
     assert set(names) <= exported, set(names) - exported
@@ -76,7 +76,7 @@ def test_fp16_comparator_arguments():
     assert L.kivi_decode_attn_fp16_splits(1, 1, 100, 1) == 1      # short context: one split
     assert L.kivi_decode_attn_fp16_splits(1, 1, 0, 1) == -2
     need = L.kivi_decode_attn_fp16_workspace(1, 32, 131072, 32, 0)
-    assert need == 256 + ((24 * 32 * 130 * 8 + 255) // 256) * 256
+    assert need == 256 + 256 + ((24 * 32 * 130 * 8 + 255) // 256) * 256
     assert L.kivi_decode_attn_fp16_workspace(1, 1, 0, 1, 0) == 0
 
 
@@ -278,11 +278,44 @@ def test_split_selection_and_workspace():
     c = _cache(batch=1, kv_heads=32, token_cap=131104, n_quant=131040, n_res=32)
     s = L.kivi_decode_attn_splits(C.byref(c), 32)
     assert 8 <= s <= 1024
-    assert L.kivi_decode_attn_workspace(C.byref(c), 32, 0) == 256 + ((s * 32 * 130 * 8 + 255) // 256) * 256
+    # header: a 256-byte status block, then 8 bytes per query row rounded up to 256
+    assert L.kivi_decode_attn_workspace(C.byref(c), 32, 0) == 256 + 256 + ((s * 32 * 130 * 8 + 255) // 256) * 256
     # very short history: one split
     c = _cache(n_quant=32, n_res=0)
     assert L.kivi_decode_attn_splits(C.byref(c), 2) == 1
-    assert L.kivi_decode_attn_workspace(C.byref(c), 2, 7) == 256 + ((7 * 2 * 2 * 130 * 8 + 255) // 256) * 256
+    assert L.kivi_decode_attn_workspace(C.byref(c), 2, 7) == 256 + 256 + ((7 * 2 * 2 * 130 * 8 + 255) // 256) * 256
+    # 40 rows of 16 x 40 heads: the row header takes 16 * 40 * 8 = 5,120 bytes
+    c = _cache(batch=16, kv_heads=40, token_cap=4096, n_quant=3968, n_res=128)
+    assert L.kivi_decode_attn_workspace(C.byref(c), 40, 1) == 256 + 5120 + ((640 * 130 * 8 + 255) // 256) * 256
+
+
+def test_decode_step_split_and_workspace_helpers():
+    """The step's helpers answer for the state after its append: a full ring flushes first."""
+    full = _cache(batch=1, kv_heads=32, token_cap=131104, n_quant=131008, n_res=128, res_head=0)
+    after = _cache(batch=1, kv_heads=32, token_cap=131104, n_quant=131040, n_res=97, res_head=32)
+    assert L.kivi_decode_step_splits(C.byref(full), 32, 0) == L.kivi_decode_attn_splits(C.byref(after), 32)
+    assert L.kivi_decode_step_splits(C.byref(full), 32, 1) == L.kivi_decode_attn_rope_splits(C.byref(after), 32)
+    for s in (0, 3):
+        assert L.kivi_decode_step_workspace(C.byref(full), 32, s, 0) == L.kivi_decode_attn_workspace(
+            C.byref(after), 32, s if s else L.kivi_decode_attn_splits(C.byref(after), 32))
+    # room in the ring: the history does not change
+    c = _cache(batch=1, kv_heads=32, token_cap=131104, n_quant=131040, n_res=32)
+    assert L.kivi_decode_step_splits(C.byref(c), 32, 0) == L.kivi_decode_attn_splits(C.byref(c), 32)
+    # flush-all moves R tokens
+    fa = _cache(token_cap=512, n_quant=64, n_res=128, flags=kivi.KIVI_FLUSH_ALL)
+    fa_after = _cache(token_cap=512, n_quant=192, n_res=1, res_head=0, flags=kivi.KIVI_FLUSH_ALL)
+    assert L.kivi_decode_step_workspace(C.byref(fa), 4, 0, 0) == L.kivi_decode_attn_workspace(C.byref(fa_after), 4, 0)
+    # errors: a flush past token_cap, a bad state, a bad head count
+    assert L.kivi_decode_step_splits(C.byref(_cache(n_quant=256, n_res=128)), 4, 0) == -4
+    assert L.kivi_decode_step_workspace(C.byref(_cache(n_quant=256, n_res=128)), 4, 0, 0) == 0
+    assert L.kivi_decode_step_splits(C.byref(_cache(n_res=129)), 4, 0) == -7
+    assert L.kivi_decode_step_splits(C.byref(_cache()), 3, 0) == -2
+    assert L.kivi_decode_step_workspace(C.byref(_cache()), 4, -1, 0) == 0
+
+
+def test_merge_test_hook_arguments():
+    assert L.kivi_test_next_attention_merge(-1, 0) == -2
+    assert L.kivi_test_next_attention_merge(0, 0) == kivi.KIVI_OK   # no device access; clears the setting
 
 
 def test_rope_attention_arguments():
