@@ -17,8 +17,10 @@
  *
  * Conventions for every call:
  *  - Pointers are DEVICE pointers unless marked (host).  The caller allocates and frees
- *    every buffer; the library allocates nothing, on any path, and keeps no mutable
- *    global state.  fp16 data are IEEE binary16 bit patterns (uint16_t).
+ *    every buffer; the library allocates nothing, on any path.  Its only mutable global
+ *    state is the per-device scratch of kivi_decode_attn_noalloc (static device memory of
+ *    the library) and the per-thread settings of the measurement and testing hooks.  fp16
+ *    data are IEEE binary16 bit patterns (uint16_t).
  *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue work on
  *    it and never synchronise the device.
  *  - Return value: KIVI_OK (0) or a negative KIVI_ERR_* code.  Arguments are validated
@@ -174,6 +176,24 @@ int kivi_append_flush(kivi_cache* cache, const uint16_t* k_new, const uint16_t* 
 int kivi_decode_attn(const kivi_cache* cache, const uint16_t* q, int32_t q_heads,
                      float sm_scale, uint16_t* out, float* lse, void* workspace,
                      size_t workspace_bytes, int32_t num_splits, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): kivi_decode_attn with the library's own scratch in
+ * place of the caller's workspace.  Same arguments (minus workspace and workspace_bytes),
+ * results, kernels, split count and errors as kivi_decode_attn; the caller still passes q,
+ * out and lse.  The scratch is KIVI_NOALLOC_SCRATCH_BYTES of static device memory per device,
+ * held until the process ends; a call whose kivi_decode_attn_workspace(cache, q_heads,
+ * num_splits) exceeds it returns KIVI_ERR_WORKSPACE.  The call uses the scratch of the device
+ * current on the calling thread (its first call there takes the scratch's address and clears
+ * it on `stream`); it allocates nothing and calls no allocating routine.  Every call on one
+ * device shares that scratch and leaves its contents for the next: calls of one (batch,
+ * q_heads) shape keep it consistent as a workspace is kept, and a call of another shape first
+ * clears what earlier calls used (one small kernel on `stream`).  Calls that overlap on one
+ * device (other threads, other streams) race on the scratch: the caller serialises them.  The
+ * scratch's status word (see kivi_decode_attn) is not readable from the host. */
+#define KIVI_NOALLOC_SCRATCH_BYTES (8u << 20)
+int kivi_decode_attn_noalloc(const kivi_cache* cache, const uint16_t* q, int32_t q_heads, float sm_scale,
+                             uint16_t* out, float* lse, int32_t num_splits, void* stream);
 
 /* Decode attention over a cache of pre-RoPE keys ("Your KV cache doesn't have a bit
  * problem...", paragraph 4, and the KVQuant summary on GrooveSquid advise quantizing keys

@@ -8,8 +8,37 @@
 #include "kivi_internal.h"
 
 #include <cmath>
+#include <mutex>
 
 using namespace kivi;
+
+// Scratch of kivi_decode_attn_noalloc: a workspace the library owns, one copy per device (the
+// code object's static device memory), for callers that cannot allocate.  Host code takes its
+// device address from hipGetSymbolAddress (per device, at the first call on that device) and
+// never uses this name as an address.
+constexpr size_t kNoAllocScratchBytes = size_t(8) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+// zero n 16-byte words at p (the scratch's set-up, and its clearing when the shape changes)
+__global__ void zero_words_kernel(uint4* p, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+        p[i] = make_uint4(0, 0, 0, 0);
+}
+
+// Per-device record of the scratch: its device address (0 until the first call on the device),
+// the query-row count of the last call (the header and partial slots are laid out by it) and the
+// high-water mark of the bytes any call has used.
+struct NoAllocScratch {
+    void* ptr = nullptr;
+    int64_t q_rows = -1;
+    size_t used = 0;
+};
+constexpr int kNoAllocDevices = 64;
+std::mutex g_noalloc_mu;
+NoAllocScratch g_noalloc[kNoAllocDevices];
+
+}  // namespace
 
 namespace {
 
@@ -598,6 +627,45 @@ int kivi_time_next_attention(void* start_event, void* stop_event) {
     t_timing[0] = static_cast<hipEvent_t>(start_event);
     t_timing[1] = static_cast<hipEvent_t>(stop_event);
     return KIVI_OK;
+}
+
+int kivi_decode_attn_noalloc(const kivi_cache* c, const uint16_t* q, int32_t q_heads, float sm_scale, uint16_t* out,
+                             float* lse, int32_t num_splits, void* stream) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return KIVI_ERR_HIP;
+    if (dev < 0 || dev >= kNoAllocDevices) return KIVI_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_noalloc_mu);
+    NoAllocScratch& sc = g_noalloc[dev];
+    if (sc.ptr == nullptr) {   // set-up on this device, with it current
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return KIVI_ERR_HIP;
+        sc.ptr = p;
+        sc.q_rows = -1;
+        sc.used = kNoAllocScratchBytes;   // cleared whole before the first call uses it
+    }
+    AttnArgs a;
+    // validation, split count and the size check (KIVI_ERR_WORKSPACE beyond the scratch's size)
+    int st = prepare_attn(c, q, q_heads, sm_scale, out, lse, sc.ptr, kNoAllocScratchBytes, num_splits, &a);
+    if (st != KIVI_OK) return st;
+    const size_t need = kivi_decode_attn_workspace(c, q_heads, a.splits);
+    hipStream_t s = (hipStream_t)stream;
+    if (sc.q_rows != a.q_rows) {
+        // another shape: the counters, epochs and partial slots move, so everything any call has
+        // written is cleared first (same stream, before the attention); with an unchanged shape the
+        // scratch stays consistent from call to call, as a workspace does
+        const size_t bytes = sc.used > need ? sc.used : need;
+        const size_t words = bytes / 16;
+        const unsigned blocks = (unsigned)((words + 255) / 256 < 1024 ? (words + 255) / 256 : 1024);
+        hipLaunchKernelGGL(zero_words_kernel, dim3(blocks), dim3(256), 0, s, static_cast<uint4*>(sc.ptr), words);
+        if ((st = hip_status(hipGetLastError())) != KIVI_OK) return st;
+        sc.q_rows = a.q_rows;
+        sc.used = need;
+    } else if (need > sc.used) {
+        sc.used = need;
+    }
+    hipEvent_t t0, t1;
+    take_timing(&t0, &t1);
+    return hip_status(launch_decode_attn(a, s, t0, t1));
 }
 
 int kivi_decode_attn(const kivi_cache* c, const uint16_t* q, int32_t q_heads, float sm_scale, uint16_t* out,

@@ -22,7 +22,8 @@ EXPORTS = ["kivi_quantize_k_per_channel", "kivi_quantize_v_per_token", "kivi_pre
            "kivi_decode_attn_fp16_workspace", "kivi_append_flush_ragged", "kivi_decode_attn_ragged",
            "kivi_decode_attn_ragged_splits", "kivi_decode_attn_rope", "kivi_decode_attn_rope_splits",
            "kivi_decode_attn_rope_ragged", "kivi_decode_attn_rope_ragged_splits", "kivi_decode_step_rope",
-           "kivi_decode_step_splits", "kivi_decode_step_workspace", "kivi_test_next_attention_merge"]
+           "kivi_decode_step_splits", "kivi_decode_step_workspace", "kivi_test_next_attention_merge",
+           "kivi_decode_attn_noalloc"]
 
 KIVI_FLUSH_ALL = 1        # kivi_cache.flags: a full residual is flushed whole (else its oldest group)
 KIVI_CODES_4BIT = 2       # kivi_cache.flags: 4-bit codes (sixteen levels), token-major nibbles
@@ -86,6 +87,7 @@ def _load():
     L.kivi_decode_step_workspace.argtypes = [cp, i32, i32, i32]
     L.kivi_decode_step_workspace.restype = C.c_size_t
     L.kivi_test_next_attention_merge.argtypes = [i32, C.c_uint32]
+    L.kivi_decode_attn_noalloc.argtypes = [cp, p, i32, C.c_float, p, p, i32, p]
     L.kivi_status_str.restype = C.c_char_p
     for name in EXPORTS:
         L[name].restype = L[name].restype if name in ("kivi_decode_attn_splits", "kivi_decode_attn_workspace",
@@ -232,6 +234,22 @@ def kivi_decode_attn(cache, q, sm_scale, out=None, lse=None, num_splits=0, works
                                 _ptr(lse) if want_lse else None, _ptr(ws), ws.numel() * ws.element_size(),
                                 num_splits, _stream(q)), "kivi_decode_attn")
     return (out, lse) if want_lse else out
+
+
+NOALLOC_SCRATCH_BYTES = 8 << 20    # KIVI_NOALLOC_SCRATCH_BYTES
+
+
+def kivi_decode_attn_noalloc(cache, q, sm_scale, out, lse=None, num_splits=0):
+    """kivi_decode_attn on the library's per-device scratch (no workspace): q fp16 [B, Hq, D],
+    out fp16 [B, Hq, D] and lse fp32 [B, Hq] (or None) supplied by the caller."""
+    if not q.is_contiguous() or q.dtype != torch.float16:
+        raise ValueError("expected contiguous float16 q [B, Hq, D]")
+    if not out.is_contiguous() or out.shape != q.shape or out.dtype != torch.float16:
+        raise ValueError("expected contiguous float16 out of q's shape")
+    Hq = q.shape[1]
+    _check(lib.kivi_decode_attn_noalloc(C.byref(cache.c), _ptr(q), Hq, float(sm_scale), _ptr(out), _ptr(lse),
+                                        num_splits, _stream(q)), "kivi_decode_attn_noalloc")
+    return (out, lse) if lse is not None else out
 
 
 def kivi_decode_attn_rope_splits(cache, q_heads):
