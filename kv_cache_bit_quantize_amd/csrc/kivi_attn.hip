@@ -58,10 +58,11 @@ __global__ __launch_bounds__(kSqBlock) void attn_split_kernel(AttnArgs a) {
 
     const int split = grid_split(a);
     const int64_t qrow = grid_row(a);
-    const int64_t b = qrow / a.q_heads;
-    const int hq = (int)(qrow % a.q_heads);
-    const int64_t kvrow = b * a.kv_heads + hq / a.ratio;
-    if (a.k_new != nullptr && split == 0 && hq % a.ratio == 0) store_new_token(a, kvrow);
+    // Query row b*Hq + h reads kv row b*Hkv + h/ratio = qrow/ratio (Hq = Hkv*ratio): one 32-bit
+    // division, none for one query per kv head.  The set-up before the first loads is kept short:
+    // each of its instructions delays them, and a CU issues it for three waves per SIMD.
+    const int64_t kvrow = a.ratio == 1 ? qrow : (int64_t)((uint32_t)qrow / (uint32_t)a.ratio);
+    if (a.k_new != nullptr && split == 0 && (uint32_t)qrow % (uint32_t)a.ratio == 0) store_new_token(a, kvrow);
     const TagLoads<1> tag_v = partial_tag<1>(a, qrow);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform, as the compiler sees it

@@ -200,7 +200,10 @@ __device__ __forceinline__ int32_t batch_units(const AttnArgs& a, int64_t batch)
     return __builtin_amdgcn_readfirstlane(u);
 }
 __device__ __forceinline__ RowState row_state(const AttnArgs& a, int64_t kvrow, int split) {
-    if (a.seq_state == nullptr) return {a.n_quant, a.n_res, a.res_head, a.groups_per_split, a.splits - 1, a.splits};
+    // (the uniform case is the likely one: its code is laid out first, so the set-up before a
+    // kernel's first loads does not jump over the ragged plan's)
+    if (__builtin_expect(a.seq_state == nullptr, 1))
+        return {a.n_quant, a.n_res, a.res_head, a.groups_per_split, a.splits - 1, a.splits};
     int32_t* s = a.seq_state + 4 * (kvrow / a.kv_heads);
     int32_t nq = s[0], nr = s[1], rh = s[2];
     if (!state_in_range(nq, nr, rh, a.token_cap, a.residual_cap, a.group)) {
