@@ -48,9 +48,12 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     const int split = grid_split(a);
     const int64_t grow = grid_row(a);                 // (batch, kv head, query chunk)
     const int chunks = a.ratio / NQ;
-    const int64_t kvrow = grow / chunks;
-    const int chunk = (int)(grow % chunks);
-    const int64_t qrow0 = (kvrow / a.kv_heads) * a.q_heads + (kvrow % a.kv_heads) * a.ratio + chunk * NQ;
+    // grow = kvrow*chunks + chunk and Hq = Hkv*ratio = Hkv*chunks*NQ, so the first query row is
+    // kvrow*ratio + chunk*NQ = grow*NQ: one 32-bit division (none when a kv head's query group
+    // is one workgroup) before the first loads
+    const int64_t kvrow = chunks == 1 ? grow : (int64_t)((uint32_t)grow / (uint32_t)chunks);
+    const int chunk = (int)(grow - kvrow * chunks);
+    const int64_t qrow0 = grow * NQ;
     if (a.k_new != nullptr && split == 0 && chunk == 0) store_new_token(a, kvrow);
     const TagLoads<NQ> tag_v = partial_tag<NQ>(a, qrow0);
     const int lane = threadIdx.x & 63;

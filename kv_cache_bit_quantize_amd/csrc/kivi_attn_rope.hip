@@ -123,8 +123,9 @@ __global__ __launch_bounds__(kBlock) void attn_rope_kernel(AttnArgs a) {
 
     const int split = grid_split(a);
     const int64_t qrow = grid_row(a);
-    const int64_t kvrow = (qrow / a.q_heads) * a.kv_heads + (qrow % a.q_heads) / a.ratio;
-    if (a.k_new != nullptr && split == 0 && (qrow % a.q_heads) % a.ratio == 0) store_new_token(a, kvrow);
+    // query row b*Hq + h reads kv row b*Hkv + h/ratio = qrow/ratio (Hq = Hkv*ratio)
+    const int64_t kvrow = a.ratio == 1 ? qrow : (int64_t)((uint32_t)qrow / (uint32_t)a.ratio);
+    if (a.k_new != nullptr && split == 0 && (uint32_t)qrow % (uint32_t)a.ratio == 0) store_new_token(a, kvrow);
     const TagLoads<1> tag_v = partial_tag<1>(a, qrow);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
