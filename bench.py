@@ -119,6 +119,46 @@ def cpu_baseline(w, k, v, n_heads, steps_tokens, threads):
     }
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_single_thread(synth, names, dev_seed_heads=1):
+    """The oracle on one host thread: one decode step (append + fp64 attention) of the first kv
+    head of batch row 0 of each named workload (the whole cache for the 1 x 1 tiny one)."""
+    from oracle import ref
+    res = []
+    for name in names:
+        w = synth.WORKLOADS[name]
+        k, v = synth.prefill_kv(w, tokens=w.context)
+        kh = k[0, :1].contiguous().view(torch.int16).numpy().view(np.uint16)
+        vh = v[0, :1].contiguous().view(torch.int16).numpy().view(np.uint16)
+        kn, vn = synth.step_kv(w, 0)
+        knh = kn[0, :1].contiguous().view(torch.int16).numpy().view(np.uint16)
+        vnh = vn[0, :1].contiguous().view(torch.int16).numpy().view(np.uint16)
+        ratio = w.q_heads // w.kv_heads
+        qh = synth.query(w, step=1)[:1, :ratio].contiguous().view(torch.int16).numpy().view(np.uint16)
+        c = ref.RefCache(1, 1, D, w.group, w.residual_cap, token_cap=w.token_cap)
+        c.prefill(kh, vh, w.n_quant)
+        t0 = time.perf_counter()
+        f = c.append(knh, vnh)
+        c.decode_attn(qh, synth.SM_SCALE_D128)
+        sec = time.perf_counter() - t0
+        nbytes = c.n_quant * quant_token_bytes(w.group) + c.n_res * RES_TOKEN_BYTES + 2 * ratio * D * 2 + 4 * D * 2 \
+            + (w.group * (RES_TOKEN_BYTES + quant_token_bytes(w.group)) if f else 0)
+        res.append({"workload": name, "sample": f"1 of {w.batch * w.kv_heads} kv heads ({ratio} query heads), "
+                    f"{c.n_quant} + {c.n_res} tokens", "seconds": round(sec, 4),
+                    "value": round(nbytes / sec / 1e9, 4), "unit": "GB/s", "cores": 1})
+        del k, v
+    return res
+
+
 def ragged_measure(kivi, synth, dev, steps, warmup, seed=2402):
     """Ragged batch (sequences at different lengths, per-sequence state on the device): the
     query-group serving shape (batch 64, 32 query heads over 8 kv heads) with context lengths
@@ -258,6 +298,177 @@ def group_sweep(kivi, synth, w, k, v, queries, steps, warmup, groups, bits=2):
     return res
 
 
+FLUSH_BYTES = 1 << 30          # untimed read between flushed launches: 4x the 256 MB Infinity Cache
+
+
+def stats_us(ms_list):
+    """mean / median / min of launch durations given in ms, in us"""
+    a = np.asarray(ms_list, dtype=np.float64) * 1e3
+    return {"mean": round(float(a.mean()), 2), "median": round(float(np.median(a)), 2), "min": round(float(a.min()), 2)}
+
+
+def event_pairs(n):
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
+    for pair in ev:
+        for e in pair:
+            e.record()
+    return ev
+
+
+def read_ceiling(kivi, dev, sizes, reps=20):
+    """The chip's streaming-read rate: kivi_read_probe (a plain grid-stride 16-byte read) over
+    buffers of the given sizes, each read's duration from events its own dispatch records."""
+    res = []
+    for nbytes in sizes:
+        nbytes = nbytes // 16 * 16
+        buf = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+        sink = kivi.kivi_read_probe(buf)
+        for _ in range(3):
+            kivi.kivi_read_probe(buf, sink)
+        ev = event_pairs(reps)
+        torch.cuda.synchronize()
+        for i in range(reps):
+            kivi.kivi_time_next_attention(*ev[i])
+            kivi.kivi_read_probe(buf, sink)
+        torch.cuda.synchronize()
+        st = stats_us([a.elapsed_time(b) for a, b in ev])
+        res.append({"bytes": nbytes, "us": st, "achieved": round(nbytes / st["median"] / 1e3, 1), "unit": "GB/s",
+                    "frac": round(nbytes / st["median"] / 1e3 / PEAK_HBM_GBS, 4)})
+        del buf
+    return res
+
+
+def decode_steps_measure(kivi, synth, name, dev, steps, warmup, flush_buf, sink):
+    """One single-layer workload's decode steps (kivi_decode_step: append, and attention of one
+    query per head over the cache, fused into one launch when nothing is flushed), timed two
+    ways: back to back (the wall clock of all steps and the attention kernels' own events; the
+    working set may partly stay in the 256 MB Infinity Cache from one step to the next:
+    "unflushed"), and with an untimed 1 GiB read between steps, so each attention kernel reads
+    the cache from HBM ("flushed", kernel events only)."""
+    w = synth.WORKLOADS[name]
+    k, v = synth.prefill_kv(w, device=dev)
+    res = {"workload": name, "batch": w.batch, "q_heads": w.q_heads, "kv_heads": w.kv_heads,
+           "context_start": w.context}
+    for mode in ("unflushed", "flushed"):
+        cache = kivi.Cache(w.batch, w.kv_heads, w.token_cap, device=dev)
+        kivi.kivi_prefill(k, v, w.n_quant, cache)
+        n = min(steps, w.decode_steps - warmup)
+        kvs = [synth.step_kv(w, s, device=dev) for s in range(warmup + n)]
+        qs = [synth.query(w, step=s + 1, device=dev) for s in range(warmup + n)]
+        out = torch.empty_like(qs[0])
+        ws = cache.workspace(w.q_heads)
+        for s in range(warmup):
+            kivi.kivi_decode_step(cache, *kvs[s], qs[s], synth.SM_SCALE_D128, out=out, workspace=ws)
+        ev = event_pairs(n)
+        flags, byts = [], []
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(n):
+            if mode == "flushed":
+                kivi.kivi_read_probe(flush_buf, sink)
+            nq, nr, _ = cache.state
+            kivi.kivi_time_next_attention(*ev[i])
+            _, f = kivi.kivi_decode_step(cache, *kvs[warmup + i], qs[warmup + i], synth.SM_SCALE_D128, out=out,
+                                         workspace=ws)
+            flags.append(f)
+            nq2, nr2, _ = cache.state
+            byts.append(attn_bytes(w, nq2, nr2) + append_bytes(w, f))
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        one = [i for i in range(n) if not flags[i]]
+        st = stats_us([ev[i][0].elapsed_time(ev[i][1]) for i in one])
+        b = float(np.mean([byts[i] for i in one]))
+        r = {"steps": n, "flush_steps": int(sum(map(bool, flags))), "decode_attn_us": st,
+             "bytes_per_launch": int(b), "achieved": round(b / st["mean"] / 1e3, 1), "unit": "GB/s",
+             "frac": round(b / st["mean"] / 1e3 / PEAK_HBM_GBS, 4)}
+        if mode == "unflushed":
+            r["ms_per_step"] = round(wall / n * 1e3, 5)
+            r["wall_GBps"] = round(sum(byts) / wall / 1e9, 1)
+            r["tokens_per_s"] = round(w.batch * n / wall, 1)
+        res[mode] = r
+        del cache, ws
+    res["kernel"] = "attn_split_kernel (append fused)" if w.q_heads == w.kv_heads else "attn_gqa_kernel (append fused)"
+    del k, v
+    return res
+
+
+def llama13b_measure(kivi, synth, dev, steps, warmup):
+    """The 40-layer Llama-2-13B-shaped cache (16 sequences x 40 kv heads, 3,968 quantized + 128
+    fp16 tokens per layer, 11.4 GB): one step is attention of one query per head over all 40
+    layers, 40 back-to-back kivi_decode_attn calls on one stream (no append), timed by events
+    around the step; then the same 40 calls captured once in a HIP graph and replayed, every
+    replay's outputs checked against the eager step's.  The working set is 45x the Infinity
+    Cache, so no flush is needed."""
+    w = synth.WORKLOADS["llama2-13b-cache"]
+    caches, queries, outs = [], [], []
+    for layer in range(w.layers):
+        k, v = synth.prefill_kv(w, layer=layer, device=dev)
+        c = kivi.Cache(w.batch, w.kv_heads, w.token_cap, device=dev)
+        kivi.kivi_prefill(k, v, w.n_quant, c)
+        del k, v
+        caches.append(c)
+        queries.append(synth.query(w, layer=layer, device=dev))
+        outs.append(torch.empty_like(queries[-1]))
+    wss = [c.workspace(w.q_heads) for c in caches]
+    per_layer = attn_bytes(w, w.n_quant, w.n_res)
+    step_bytes = w.layers * per_layer
+
+    def step():
+        for c, q, o, ws in zip(caches, queries, outs, wss):
+            kivi.kivi_decode_attn(c, q, synth.SM_SCALE_D128, out=o, workspace=ws)
+    for _ in range(warmup):
+        step()
+    ev = event_pairs(steps)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        ev[i][0].record()
+        step()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    eager = stats_us([a.elapsed_time(b) for a, b in ev])
+    ref = [o.clone() for o in outs]
+    # the same step as one HIP graph
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    ev = event_pairs(steps)
+    worst = 0.0
+    for i in range(steps):
+        for o in outs:
+            o.zero_()
+        ev[i][0].record()
+        g.replay()
+        ev[i][1].record()
+        torch.cuda.synchronize()
+        # the kernel's waves take tile pairs from a queue, so the fp32 partition of each sum (and
+        # an output's last fp16 bit) can differ between runs: compare at the parity bar
+        for o, r in zip(outs, ref):
+            d = (o.float() - r.float()).abs().amax(-1) / r.float().abs().amax(-1).clamp_min(1e-30)
+            worst = max(worst, float(d.max()))
+    graph = stats_us([a.elapsed_time(b) for a, b in ev])
+    res = {"workload": "llama2-13b-cache", "layers": w.layers, "batch": w.batch, "q_heads": w.q_heads,
+           "kv_heads": w.kv_heads, "n_quant": w.n_quant, "n_res": w.n_res,
+           "splits": kivi.kivi_decode_attn_splits(caches[0], w.q_heads),
+           "bytes_per_step": int(step_bytes), "steps": steps,
+           "eager": {"step_us": eager, "achieved": round(step_bytes / eager["median"] / 1e3, 1),
+                     "frac": round(step_bytes / eager["median"] / 1e3 / PEAK_HBM_GBS, 4),
+                     "tokens_per_s": round(w.batch * 1e6 / eager["median"], 1)},
+           "graph": {"step_us": graph, "achieved": round(step_bytes / graph["median"] / 1e3, 1),
+                     "frac": round(step_bytes / graph["median"] / 1e3 / PEAK_HBM_GBS, 4),
+                     "tokens_per_s": round(w.batch * 1e6 / graph["median"], 1),
+                     "replay_vs_eager_max_row_rel_err": worst, "replays_match_eager": bool(worst <= 2e-3)},
+           "unit": "GB/s", "timing": "events around each step (40 launches)"}
+    del caches, wss, g
+    return res
+
+
 def read_traffic(workload):
     """HBM bytes per launch from committed rocprofv3 counters, if they were taken on the
     current kernel sources; else None."""
@@ -291,6 +502,9 @@ def main():
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill quantizer measurement")
     ap.add_argument("--four-bit-groups", default="32",
                     help="group sizes of the 4-bit attention-only measurement (comma list; empty: skip)")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the other workloads (llama2-7b-layer, gqa-mistral-7b, llama2-13b-cache)")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the decode hot path shards "
@@ -364,6 +578,25 @@ def main():
     achieved = float(np.mean(launch_b)) / (attn_ms.mean() / 1e3) / 1e9
     splits = kivi.kivi_decode_attn_splits(cache, w.q_heads) if args.splits == 0 else args.splits
 
+    # the same attention with an untimed 1 GiB read before each launch (Infinity Cache evicted)
+    flush_buf = torch.ones(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    sink = kivi.kivi_read_probe(flush_buf)
+    evf = event_pairs(args.steps)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        kivi.kivi_read_probe(flush_buf, sink)
+        kivi.kivi_time_next_attention(*evf[i])
+        kivi.kivi_decode_attn(cache, queries[args.warmup + i], synth.SM_SCALE_D128, out=out, num_splits=args.splits,
+                              workspace=ws)
+    torch.cuda.synchronize()
+    nq_end, nr_end, _ = cache.state
+    flushed_b = attn_bytes(w, nq_end, nr_end)
+    flushed = stats_us([a.elapsed_time(b) for a, b in evf])
+    flushed = {"decode_attn_us": flushed, "bytes_per_launch": int(flushed_b),
+               "achieved": round(flushed_b / flushed["mean"] / 1e3, 1), "unit": "GB/s",
+               "frac": round(flushed_b / flushed["mean"] / 1e3 / PEAK_HBM_GBS, 4),
+               "note": "kivi_decode_attn alone, an untimed 1 GiB read before each launch"}
+
     # fp16 comparator: kivi_decode_attn_fp16 over the prefill's own fp16 keys and values (the
     # context the timed steps start from), the same queries, every launch timed the same way
     fp16 = None
@@ -403,7 +636,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp32",
+        "dtype": "int8+fp16",
+        "dtype_detail": "2-bit codes; key logits exact on int8 MFMA (q*scale as 30-bit fixed-point digits, int32 "
+                        "sums); P.V on fp16 MFMA with fp16-rounded p*scale weights, fp32 accumulation; softmax, "
+                        "residual and merge in fp32; fp16 output",
         "data": "synthetic",
         "config": {
             "workload": w.name, "batch": w.batch, "q_heads": w.q_heads, "kv_heads": w.kv_heads,
@@ -414,7 +650,10 @@ def main():
         "tokens_per_s": round(w.batch * args.steps / elapsed, 1),
         "step_path": "separate append_flush + decode_attn" if args.separate else "fused decode_step",
         "decode_attn_us": round(float(attn_ms.mean()) * 1e3, 2),
+        "decode_attn_stats_us": stats_us(attn_ms),
         "event_timed_launches": len(one_launch),
+        "cache_state": "unflushed: back-to-back steps; the 403 MB working set exceeds the 256 MB Infinity Cache",
+        "decode_attn_flushed": flushed,
         "attn_timing": "kernel start and end recorded by the dispatch (hipExtLaunchKernel events)",
         "flush_steps": int(sum(bool(f) for f in flags)),
         "roofline": {
@@ -434,6 +673,8 @@ def main():
         "four_bit": None,
         "pre_rope": None,
         "prefill_quantize": None,
+        "read_ceiling": None,
+        "workloads": None,
     }
     del cache, ws
     groups = [int(x) for x in args.sweep_groups.split(",") if x.strip()]
@@ -448,10 +689,23 @@ def main():
         res["prefill_quantize"] = prefill_measure(kivi, w, k, v, min(args.steps, 20), min(args.warmup, 3))
     if not args.no_ragged:
         res["ragged_batch"] = ragged_measure(kivi, synth, dev, args.steps, args.warmup)
+    if not args.no_ceiling:
+        res["read_ceiling"] = read_ceiling(kivi, dev, [int(np.mean(launch_b)), FLUSH_BYTES])
+    if not args.no_workloads:
+        del k, v
+        torch.cuda.empty_cache()
+        res["workloads"] = {
+            name: decode_steps_measure(kivi, synth, name, dev, args.steps, args.warmup, flush_buf, sink)
+            for name in ("llama2-7b-layer", "gqa-mistral-7b")}
+        res["workloads"]["llama2-13b-cache"] = llama13b_measure(kivi, synth, dev, max(20, min(args.steps, 30)),
+                                                                min(args.warmup, 5))
+        k, v = synth.prefill_kv(w, device=dev)
     if args.cpu_heads > 0:
         kn, vn = steps_kv[0]
         res["cpu_baseline"] = cpu_baseline(w, k, v, min(args.cpu_heads, w.kv_heads), (kn, vn),
                                            min(args.cpu_threads, os.cpu_count() or 1))
+        res["cpu_baseline"]["cpu_model"] = cpu_model()
+        res["cpu_baseline"]["single_thread"] = cpu_single_thread(synth, ["tiny", "llama2-7b-layer", "long-128k"])
     print(json.dumps(res), flush=True)
 
 

@@ -298,14 +298,25 @@ int kivi_decode_attn_fp16(const uint16_t* k, const uint16_t* v, int32_t batch, i
                           size_t workspace_bytes, int32_t num_splits, void* stream);
 
 /* Measurement hook, for callers that time the attention kernel itself (not a step of the
- * method).  The next decode-attention kernel that kivi_decode_attn or kivi_decode_step
- * launches from the calling thread records its own start in start_event and its end in
+ * method).  The next decode-attention kernel that an attention call (kivi_decode_attn,
+ * kivi_decode_step and the other attention entry points) or kivi_read_probe launches from
+ * the calling thread records its own start in start_event and its end in
  * stop_event (hipEvent_t handles, created by the caller with timing enabled), taken by the
  * dispatch itself with no marker command in the stream, so hipEventElapsedTime(start, stop)
  * is that kernel's duration.  The setting is consumed by that one launch (a flush kernel
  * launched before it by kivi_decode_step is not timed); both NULL clears it.
  * KIVI_ERR_NULL if exactly one of the two is NULL.  No device access. */
 int kivi_time_next_attention(void* start_event, void* stop_event);
+
+/* Measurement helper (not a step of the method): reads `bytes` (a multiple of 16) of device
+ * memory at src (16-byte aligned) once, in a plain grid-stride sweep of 16-byte loads, and
+ * writes one word per workgroup to sink (device, at least kivi_read_probe_sink_bytes() bytes)
+ * so that the loads are kept.  Timed, it gives the chip's streaming-read rate, the ceiling
+ * beside the published HBM peak; untimed over more than the 256 MB Infinity Cache, it evicts
+ * a working set from that cache between timed launches.  KIVI_ERR_NULL / KIVI_ERR_SHAPE on
+ * bad arguments; nothing is enqueued then. */
+int kivi_read_probe(const void* src, size_t bytes, uint32_t* sink, void* stream);
+size_t kivi_read_probe_sink_bytes(void);
 
 /* Testing hook of the merge's bounded wait (not a step of the method): the next attention call
  * of the calling thread that passes validation polls each split partial at most max_polls

@@ -120,12 +120,28 @@ int64_t block_rows(const kivi_cache* c, int32_t q_heads) {
     return nq > 1 ? (int64_t)c->batch * c->kv_heads * (ratio / nq) : (int64_t)c->batch * q_heads;
 }
 
-// Split count for a context of `groups` key groups.
-int32_t auto_splits_for(const kivi_cache* c, int32_t q_heads, int64_t groups) {
+// Waves per workgroup of the single-query 2-bit kernel for a uniform batch: one 12-wave
+// workgroup per CU when the query rows are no more than the CUs (the rows are split across
+// them), else 4-wave workgroups, three per CU, so that up to 768 rows run in one round.
+int32_t single_query_waves(const kivi_cache* c, int32_t q_heads) {
+    const bool single = code_bits(c) == 2 && queries_per_block(q_heads / c->kv_heads) == 1;
+    return single && (int64_t)c->batch * q_heads > kTargetBlocksSingle ? kSqWavesMany : kSqWaves;
+}
+
+// Split count for a context of `groups` key groups (waves: the single-query kernel's).
+int32_t auto_splits_for(const kivi_cache* c, int32_t q_heads, int64_t groups, int32_t waves = kSqWaves) {
     const int64_t rows = block_rows(c, q_heads);
     const bool group = queries_per_block(q_heads / c->kv_heads, code_bits(c)) > 1;
     int64_t target = group ? kTargetBlocksGroup : kTargetBlocksSingle;
     int64_t min_tiles = group ? kMinGroupsPerSplit : kMinGroupsPerSplitSingle;
+    if (!group && code_bits(c) == 2 && waves == kSqWavesMany) {
+        // three workgroups per CU, a pair of tiles for every wave; as many splits as keep the
+        // call within one round (the rows alone already fill a round at 384 rows and more)
+        int64_t s = kTargetBlocks / rows;
+        const int64_t cap = groups / (2 * kSqWavesMany);
+        if (s > cap) s = cap;
+        return (int32_t)(s < 1 ? 1 : s);
+    }
     if (code_bits(c) == 4) {   // 4-wave workgroups, a key group for every wave
         // one query head: four workgroups per CU (88 VGPRs; at 131,072 tokens 32 splits took
         // 124-128 us against 129-146 us for 24 on three boxes)
@@ -140,7 +156,9 @@ int32_t auto_splits_for(const kivi_cache* c, int32_t q_heads, int64_t groups) {
     return (int32_t)s;
 }
 // (contexts are counted in 32-token code tiles, the attention kernels' unit of work)
-int32_t auto_splits(const kivi_cache* c, int32_t q_heads) { return auto_splits_for(c, q_heads, c->n_quant / kG); }
+int32_t auto_splits(const kivi_cache* c, int32_t q_heads) {
+    return auto_splits_for(c, q_heads, c->n_quant / kG, single_query_waves(c, q_heads));
+}
 // ragged batch: room for four times the splits of the longest context the cache can hold;
 // the kernels plan from the real lengths how many of them each sequence uses
 int32_t ragged_auto_splits(const kivi_cache* c, int32_t q_heads) {
@@ -344,6 +362,8 @@ int prepare_attn(const kivi_cache* c, const uint16_t* q, int32_t q_heads, float 
     a.slot_budget = (int32_t)(a.nq > 1 || code_bits(c) == 4 ? kTargetBlocks : kTargetBlocksSingle);
     a.group = c->group;
     a.bits = code_bits(c);
+    // ragged batches keep one 12-wave workgroup per CU (their plan shares a round of 256)
+    a.sq_waves = seq_state == nullptr ? single_query_waves(c, q_heads) : kSqWaves;
     take_merge_test(&a);
     *pa = a;
     return KIVI_OK;
@@ -620,6 +640,17 @@ int kivi_test_next_attention_merge(int32_t max_polls, uint32_t tag_skew) {
     t_merge_polls = max_polls;
     t_merge_skew = tag_skew;
     return KIVI_OK;
+}
+
+size_t kivi_read_probe_sink_bytes(void) { return (size_t)kProbeBlocks * sizeof(uint32_t); }
+
+int kivi_read_probe(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+    if (src == nullptr || sink == nullptr) return KIVI_ERR_NULL;
+    if (bytes % 16 != 0 || !aligned16(src) || (reinterpret_cast<uintptr_t>(sink) & 3u)) return KIVI_ERR_SHAPE;
+    if (bytes == 0) return KIVI_OK;
+    hipEvent_t t0, t1;
+    take_timing(&t0, &t1);
+    return hip_status(launch_read_probe(src, bytes, sink, (hipStream_t)stream, t0, t1));
 }
 
 int kivi_time_next_attention(void* start_event, void* stop_event) {

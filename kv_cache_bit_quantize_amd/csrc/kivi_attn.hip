@@ -49,8 +49,13 @@ constexpr int kWtOff = 2 * kGroupTbl;             // value weights [group][chgro
 constexpr int kZeroOff = kWtOff + 2 * 4 * 4 * 16;  // 512 zero bytes
 constexpr int kAreaBytes = kZeroOff + 512;
 
-template <int GS>
-__global__ __launch_bounds__(kSqBlock) void attn_split_kernel(AttnArgs a) {
+// W: waves per workgroup.  12 (one workgroup per CU) when the call has few rows and splits
+// them; 4 (three workgroups per CU) when a uniform batch has more query rows than the chip has
+// CUs, so that its rows run in one round of resident workgroups instead of several rounds that
+// each pay the start-up again.
+template <int GS, int W>
+__global__ __launch_bounds__(64 * W) void attn_split_kernel(AttnArgs a) {
+    constexpr int kSqWaves = W, kSqSlots = 2 * W;
     __shared__ __align__(16) uint8_t sh_area[2][kSqWaves][kAreaBytes];
     __shared__ __align__(16) float sh_o[1][kSqSlots][kD];
     __shared__ float sh_m[1][kSqSlots], sh_l[1][kSqSlots];
@@ -345,8 +350,13 @@ __global__ __launch_bounds__(kSqBlock) void attn_split_kernel(AttnArgs a) {
 hipError_t launch_decode_attn(const AttnArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
     if (a.bits == 4) return launch_decode_attn_q4(a, s, t0, t1);
     if (a.nq > 1) return launch_decode_attn_gqa(a, s, t0, t1);
-    KIVI_BY_GROUP(a.group, hipExtLaunchKernelGGL(attn_split_kernel<GS>, attn_grid(a, a.q_rows), dim3(kSqBlock), 0, s,
-                                                 t0, t1, 0, a))
+    if (a.sq_waves == 4) {
+        KIVI_BY_GROUP(a.group, hipExtLaunchKernelGGL((attn_split_kernel<GS, 4>), attn_grid(a, a.q_rows), dim3(64 * 4), 0,
+                                                     s, t0, t1, 0, a))
+    } else {
+        KIVI_BY_GROUP(a.group, hipExtLaunchKernelGGL((attn_split_kernel<GS, kSqWaves>), attn_grid(a, a.q_rows),
+                                                     dim3(64 * kSqWaves), 0, s, t0, t1, 0, a))
+    }
     return hipGetLastError();
 }
 

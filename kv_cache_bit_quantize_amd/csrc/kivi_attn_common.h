@@ -14,8 +14,6 @@ namespace kivi {
 
 constexpr int kWaves = kBlock / 64;  // waves of a 256-thread workgroup (the fp16 comparator's)
 constexpr int kSlots = 2 * kWaves;   // its softmax states per workgroup and row: quantized, residual
-constexpr int kSqBlock = 64 * kSqWaves;   // threads of a single-query 2-bit attention workgroup
-constexpr int kSqSlots = 2 * kSqWaves;
 constexpr int kPart = kD + 2;        // floats per split partial: o[128], m, l
 
 typedef int v4i __attribute__((ext_vector_type(4)));

@@ -8,6 +8,7 @@ namespace kivi {
 
 constexpr int kMaxSplits = 1024;   // upper bound on split-K partitions of one decode call
 constexpr int kSqWaves = 12;       // waves of a single-query attention workgroup (one per CU)
+constexpr int kSqWavesMany = 4;    // ... for a uniform batch with more query rows than CUs (three per CU)
 
 struct QuantArgs {          // kivi_quantize_{k,v}
     int32_t group;              // tokens per key group / channels per value group
@@ -55,6 +56,7 @@ struct AppendArgs {
     int32_t flush_all;          // a flush moves the whole residual (else its oldest group)
     int32_t bits;               // code width: 2 or 4
     double rope_base;           // pre-RoPE keys (kivi_decode_attn_rope): the rotary base, else 0
+    int32_t sq_waves;           // single-query 2-bit kernel: waves per workgroup (kSqWaves or kSqWavesMany)
 };
 
 struct AttnArgs {
@@ -102,12 +104,19 @@ struct AttnArgs {
     int32_t group;              // tokens per key group (= channels per value group): 32, 64 or 128
     int32_t bits;               // code width: 2 or 4
     double rope_base;           // pre-RoPE keys (kivi_decode_attn_rope): the rotary base, else 0
+    int32_t sq_waves;           // single-query 2-bit kernel: waves per workgroup (kSqWaves or kSqWavesMany)
 };
 
 // bits of a sequence's flags word (ragged calls; only ever set, by the kernels)
 constexpr int32_t kSeqCapacity = 1;   // a flush would pass token_cap: the append was skipped
 constexpr int32_t kSeqBadState = 2;   // the state was out of range: the sequence was skipped
 
+
+// measurement helper: a plain streaming read of `bytes` (a multiple of 16) at src, one word per
+// workgroup (kProbeBlocks of them) written to sink
+constexpr int kProbeBlocks = 256;    // one 16-wave workgroup per CU
+hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, hipStream_t s, hipEvent_t t0 = nullptr,
+                             hipEvent_t t1 = nullptr);
 
 hipError_t launch_quantize_k(const QuantArgs& a, hipStream_t s);
 hipError_t launch_quantize_v(const QuantArgs& a, hipStream_t s);

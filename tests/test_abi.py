@@ -21,7 +21,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 26
+    assert len(names) == 28
     out = os.popen(f"nm -D --defined-only {kivi.LIB_PATH}").read()
     exported = set(re.findall(r" T (kivi_\w+)$", out, re.M))
     assert set(names) <= exported, set(names) - exported
@@ -311,6 +311,16 @@ def test_decode_step_split_and_workspace_helpers():
     assert L.kivi_decode_step_splits(C.byref(_cache(n_res=129)), 4, 0) == -7
     assert L.kivi_decode_step_splits(C.byref(_cache()), 3, 0) == -2
     assert L.kivi_decode_step_workspace(C.byref(_cache()), 4, -1, 0) == 0
+
+
+def test_read_probe_arguments():
+    P = C.c_void_p(FAKE)
+    assert L.kivi_read_probe(None, 16, P, None) == -1
+    assert L.kivi_read_probe(P, 16, None, None) == -1
+    assert L.kivi_read_probe(P, 24, P, None) == -2            # not a multiple of 16
+    assert L.kivi_read_probe(C.c_void_p(FAKE + 8), 16, P, None) == -2
+    assert L.kivi_read_probe(P, 0, P, None) == 0              # nothing to read, nothing enqueued
+    assert L.kivi_read_probe_sink_bytes() >= 4
 
 
 def test_merge_test_hook_arguments():

@@ -1,7 +1,11 @@
 """GPU parity of the fused decode attention against the fp64 CPU oracle.
 
 Bar: per output row, max |o_gpu - o_ref| / max |o_ref| <= 2e-3 (fp32 accumulation and
-fp16 output against fp64), and |exp(lse_gpu - lse_ref) - 1| <= 2e-3."""
+fp16 output against fp64), and |lse_gpu - lse_ref| <= 2e-3 + 2^-18 |lse_ref|: the absolute
+part is the same 2e-3, the relative part allows for binary32 logits (each logit is a sum of
+128 folded products whose terms can exceed the logit several-fold, so its rounding error is
+a few 2^-24 of the terms' magnitude; with 10^2..7*10^3 outlier channels logits reach
+thousands, where 2e-3 absolute would ask for ~8 binary32 ulps; kivi_testlib.LSE_REL)."""
 import numpy as np
 import pytest
 import torch
@@ -159,6 +163,16 @@ def test_split_count_does_not_change_the_result():
     for s, o in outs.items():
         rel = ((o - base).abs().max(-1).values / base.abs().max(-1).values).max().item()
         assert rel <= 1e-3, (s, rel)
+
+
+@pytest.mark.parametrize("batch,heads,splits", [(20, 16, 0), (20, 16, 3), (26, 16, 0), (40, 16, 1)])
+def test_more_query_rows_than_cus(batch, heads, splits):
+    """More query rows than the chip's 256 CUs: the single-query kernel runs 4-wave workgroups,
+    three per CU (320 rows: 2 splits each; 416 and 640 rows: one), all rows against the oracle."""
+    dev = gpu_or_skip()
+    w = synth.small(seed=60 + batch, batch=batch, q_heads=heads, kv_heads=heads, context=1536 + 45, n_quant=1536)
+    cache, rc, q = _setup(w, dev)
+    _check(cache, rc, q, splits=splits, what=f"{batch * heads} rows splits={splits}")
 
 
 def test_llama2_7b_layer_all_rows():
