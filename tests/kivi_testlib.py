@@ -97,3 +97,61 @@ def assert_lse_close(lse_gpu, lse_ref, rows=None, tol=ATTN_TOL):
     ratio = np.abs(g - r) / bound
     worst = int(np.argmax(ratio))
     assert ratio.max() <= 1.0, f"lse row {worst}: |d| {abs(g[worst] - r[worst]):.3e} > {bound[worst]:.3e} (lse {r[worst]:.1f})"
+
+
+class SlicedRef:
+    """One oracle cache per slice of the batch's sequences, driven from host threads (the
+    oracle's C calls release the GIL), so that whole full-size caches can be checked in
+    seconds.  Sequences are independent in the method, so the slices hold exactly what one
+    oracle cache over the whole batch would."""
+
+    def __init__(self, batch, kv_heads, token_cap, k, v, n_quant, parts=16, residual_cap=128, group=32, bits=2):
+        import concurrent.futures
+        parts = max(1, min(parts, batch))
+        self.kv_heads = kv_heads
+        self.bounds = [(i * batch // parts, (i + 1) * batch // parts) for i in range(parts)]
+        self.pool = concurrent.futures.ThreadPoolExecutor(parts)
+        k, v = k.cpu(), v.cpu()
+        self.parts = list(self.pool.map(
+            lambda b: ref_cache(b[1] - b[0], kv_heads, token_cap, k[b[0]:b[1]], v[b[0]:b[1]], n_quant,
+                                residual_cap=residual_cap, group=group, bits=bits), self.bounds))
+
+    @property
+    def state(self):
+        p = self.parts[0]
+        return p.n_quant, p.n_res, p.res_head
+
+    def append(self, k_new, v_new):
+        """k_new, v_new: fp16 [B, Hkv, D] (any device).  Returns the flush flag."""
+        kn, vn = _u16(k_new), _u16(v_new)
+        H = self.kv_heads
+        flags = list(self.pool.map(lambda i: self.parts[i].append(
+            kn[self.bounds[i][0]:self.bounds[i][1]].reshape(-1, kn.shape[-1]),
+            vn[self.bounds[i][0]:self.bounds[i][1]].reshape(-1, vn.shape[-1])), range(len(self.parts))))
+        assert all(f == flags[0] for f in flags)
+        return flags[0]
+
+    def decode_attn(self, q, sm_scale):
+        qb = _u16(q)
+        res = list(self.pool.map(lambda i: self.parts[i].decode_attn(qb[self.bounds[i][0]:self.bounds[i][1]], sm_scale),
+                                 range(len(self.parts))))
+        return np.concatenate([r[0] for r in res]), np.concatenate([r[1] for r in res])
+
+    def assert_cache_equal(self, gpu, ring=True):
+        """Bit-exact comparison of the whole packed history and the residual ring, slice by slice."""
+        H = self.kv_heads
+        for (b0, b1), p in zip(self.bounds, self.parts):
+            nq = p.n_quant
+            ng = nq // 32
+            nk = nq // p.group
+            sel = slice(b0 * H, b1 * H)
+            for name, a, b in (("k_codes", gpu.k_codes[sel, :ng].cpu().numpy(), p.k_codes[:, :ng]),
+                               ("v_codes", gpu.v_codes[sel, :ng].cpu().numpy(), p.v_codes[:, :ng]),
+                               ("k_sz", _u16(gpu.k_sz[sel, :nk]), p.k_sz[:, :nk]),
+                               ("v_sz", _u16(gpu.v_sz[sel, :nq]), p.v_sz[:, :nq])):
+                bad = np.argwhere(a != b)
+                assert bad.size == 0, f"{name} rows {b0 * H}..: {bad.shape[0]} mismatches, first at {bad[0].tolist()}"
+            if ring:
+                assert np.array_equal(_u16(gpu.k_res[sel]), p.k_res)
+                assert np.array_equal(_u16(gpu.v_res[sel]), p.v_res)
+        assert gpu.state == self.state

@@ -1,0 +1,149 @@
+"""GPU parity at the workloads' full sizes, on every row, against the fp64 oracle.
+
+The configuration tests elsewhere use keys with outlier channels (10^2..7*10^3), which make
+the softmax nearly one-hot, and check sampled rows of the largest caches.  Here:
+  * the 131,072-token context with outlier-free keys (logits O(1): the softmax spreads over the
+    whole context, so the rescaling of the running sums and the fp16 rounding of every P.V
+    weight accumulate over ~21 tile pairs per wave) and with q = 0 (out = the mean of all
+    131,072 value rows), at the production split count, all 32 rows and lse;
+  * the gqa-mistral-7b decode loop, all 2,048 query rows on every 8th step and the whole cache
+    (codes, pairs, rings) bit-exact after every flush;
+  * the 40-layer llama2-13b cache: codes and pairs of all 40 layers, each compared whole, and
+    attention over all 640 rows of one layer;
+  * the ragged serving batch of the benchmark (64 sequences of 512..8,192 tokens, 32 query /
+    8 kv heads), every sequence.
+Bars as in the other attention tests: per row max |o_gpu - o_ref| / max |o_ref| <= 2e-3,
+|lse_gpu - lse_ref| <= 2e-3 + 2^-18 |lse_ref|; codes, pairs and rings bit-exact.  The oracle
+runs on 16 host threads (SlicedRef)."""
+import numpy as np
+import pytest
+import torch
+
+from kivi_testlib import SlicedRef, assert_attn_close, assert_lse_close, bits, gpu_or_skip, ref_cache
+from kv_cache_bit_quantize_amd import synth
+
+pytestmark = pytest.mark.gpu
+SM = synth.SM_SCALE_D128
+D = 128
+
+
+def _kivi():
+    from kv_cache_bit_quantize_amd import kivi
+    return kivi
+
+
+@pytest.mark.timeout(600)
+def test_long_128k_diffuse_and_zero_query():
+    dev = gpu_or_skip()
+    kivi = _kivi()
+    import dataclasses
+    w = dataclasses.replace(synth.WORKLOADS["long-128k"], outliers=0)
+    k, v = synth.prefill_kv(w, device=dev)
+    cache = kivi.Cache(w.batch, w.kv_heads, w.token_cap, device=dev)
+    kivi.kivi_prefill(k, v, w.n_quant, cache)
+    # one kv head per oracle slice: a batch of 1 x 32 heads has the row layout of 32 x 1 head
+    T = k.shape[2]
+    rc = SlicedRef(w.kv_heads, 1, w.token_cap, k.reshape(w.kv_heads, 1, T, D), v.reshape(w.kv_heads, 1, T, D),
+                   w.n_quant, parts=16)
+    del k, v
+    splits = kivi.kivi_decode_attn_splits(cache, w.q_heads)
+    assert splits >= 8
+    q = synth.query(w, device=dev)
+    for name, qq in (("diffuse", q), ("q=0", torch.zeros_like(q))):
+        out, lse = kivi.kivi_decode_attn(cache, qq, SM, lse=True)
+        torch.cuda.synchronize()
+        ref_out, ref_lse = rc.decode_attn(qq.reshape(w.kv_heads, 1, D), SM)
+        ref_out, ref_lse = ref_out.reshape(1, w.q_heads, D), ref_lse.reshape(1, w.q_heads)
+        if name == "diffuse":   # logits O(1): lse is about ln(131,072) = 11.8 plus a few
+            assert float(np.max(ref_lse)) < 20.0
+        assert_attn_close(out, ref_out, what=f"long-128k {name} splits={splits}")
+        assert_lse_close(lse, ref_lse)
+
+
+@pytest.mark.timeout(600)
+def test_gqa_mistral_128_steps_all_rows():
+    dev = gpu_or_skip()
+    kivi = _kivi()
+    w = synth.WORKLOADS["gqa-mistral-7b"]
+    k, v = synth.prefill_kv(w, device=dev)
+    cache = kivi.Cache(w.batch, w.kv_heads, w.token_cap, device=dev)
+    kivi.kivi_prefill(k, v, w.n_quant, cache)
+    rc = SlicedRef(w.batch, w.kv_heads, w.token_cap, k, v, w.n_quant, parts=16)
+    del k, v
+    flushes = 0
+    for s in range(w.decode_steps):
+        kn, vn = synth.step_kv(w, s, device=dev)
+        q = synth.query(w, step=s + 1, device=dev)
+        out, lse, f = kivi.kivi_decode_step(cache, kn, vn, q, SM, lse=True)
+        assert bool(f) == bool(rc.append(kn, vn)), s
+        if f:
+            flushes += 1
+            torch.cuda.synchronize()
+            rc.assert_cache_equal(cache)
+        if s % 8 == 7 or f:
+            torch.cuda.synchronize()
+            ref_out, ref_lse = rc.decode_attn(q, SM)
+            assert_attn_close(out, ref_out, what=f"gqa-mistral step {s}")
+            assert_lse_close(lse, ref_lse)
+    assert flushes == 4
+    torch.cuda.synchronize()
+    rc.assert_cache_equal(cache)
+
+
+@pytest.mark.timeout(600)
+def test_llama2_13b_all_layers_codes_and_one_layer_all_rows():
+    dev = gpu_or_skip()
+    kivi = _kivi()
+    w = synth.WORKLOADS["llama2-13b-cache"]
+    cache = kivi.Cache(w.batch, w.kv_heads, w.token_cap, device=dev)
+    for layer in range(w.layers):
+        k, v = synth.prefill_kv(w, layer=layer, device=dev)
+        cache.set_state(0, 0, 0)
+        kivi.kivi_prefill(k, v, w.n_quant, cache)
+        rc = SlicedRef(w.batch, w.kv_heads, w.token_cap, k, v, w.n_quant, parts=16)
+        torch.cuda.synchronize()
+        rc.assert_cache_equal(cache)
+        if layer == 21:
+            q = synth.query(w, layer=layer, device=dev)
+            out, lse = kivi.kivi_decode_attn(cache, q, SM, lse=True)
+            torch.cuda.synchronize()
+            ref_out, ref_lse = rc.decode_attn(q, SM)
+            assert_attn_close(out, ref_out, what="13b layer 21 all rows")
+            assert_lse_close(lse, ref_lse)
+        del k, v, rc
+
+
+@pytest.mark.timeout(600)
+def test_ragged_bench_batch_every_sequence():
+    """The ragged serving batch that the benchmark times: 64 sequences, context lengths uniform
+    in [512, 8192] (seeded as there), 64..95 of each sequence's tokens in the fp16 residual."""
+    dev = gpu_or_skip()
+    kivi = _kivi()
+    import concurrent.futures
+    B, Hq, Hkv, lo, hi, seed = 64, 32, 8, 512, 8192, 2402
+    lengths = np.random.default_rng(seed).integers(lo, hi + 1, size=B)
+    cache = kivi.Cache(B, Hkv, hi, device=dev)
+    states, inputs = [], []
+    for b, L in enumerate(lengths):
+        nq = int((L - 64) // 32 * 32)
+        ws = synth.small(seed=seed + b, batch=1, q_heads=Hq, kv_heads=Hkv, context=int(L), n_quant=nq)
+        k, v = synth.prefill_kv(ws, device=dev)
+        view = cache.sequence(b)
+        kivi.kivi_prefill(k, v, nq, view)
+        states.append(view.state)
+        inputs.append((k.cpu(), v.cpu(), nq))
+    state = kivi.seq_state(states, device=dev)
+    with concurrent.futures.ThreadPoolExecutor(16) as ex:
+        refs = list(ex.map(lambda t: ref_cache(1, Hkv, hi, t[0], t[1], t[2]), inputs))
+    qw = synth.small(seed=seed + 999, batch=B, q_heads=Hq, kv_heads=Hkv, context=1, n_quant=0)
+    q = synth.query(qw, step=0, device=dev)
+    out, lse = kivi.kivi_decode_attn_ragged(cache, state, q, SM, lse=True)
+    torch.cuda.synchronize()
+    qb = bits(q)
+    with concurrent.futures.ThreadPoolExecutor(16) as ex:
+        res = list(ex.map(lambda b: refs[b].decode_attn(qb[b:b + 1], SM), range(B)))
+    ref_out = np.concatenate([r[0] for r in res])
+    ref_lse = np.concatenate([r[1] for r in res])
+    assert_attn_close(out, ref_out, what="ragged bench batch")
+    assert_lse_close(lse, ref_lse)
+    assert int(state[:, 3].abs().sum().item()) == 0
