@@ -140,6 +140,83 @@ def summarize(args):
     print(json.dumps(result))
 
 
+CU_NUM, SIMD_NUM, XCD_NUM = 256, 1024, 8     # MI355X
+
+
+def _all_per_dispatch(paths):
+    """{(kernel name, counter): [value per dispatch]} over several counter_collection csvs."""
+    out = {}
+    for path in paths:
+        rows = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                key = (r["Dispatch_Id"], r["Kernel_Name"], r["Counter_Name"])
+                rows[key] = rows.get(key, 0.0) + float(r["Counter_Value"])
+        for (_, name, counter), val in rows.items():
+            out.setdefault((name, counter), []).append(val)
+    return out
+
+
+def counters(args):
+    """Per-dispatch averages of the counters in the given csvs for every attention kernel, and
+    the figures derived from them (the expressions rocprofv3 lists for its derived metrics)."""
+    data = _all_per_dispatch(args.csv)
+    kernels = sorted({n for n, _ in data if "attn_" in n and "kernel" in n})
+    lines = [f"# {args.title}\n", "Commands (from the repository root, on one MI355X; one rocprofv3 run per counter set):\n",
+             "```"]
+    lines += [c for c in args.command]
+    lines += [f"python3 -m kv_cache_bit_quantize_amd.traffic counters {' '.join(args.csv)} --title '{args.title}' "
+              f"--out {args.out} --command ...", "```\n"]
+    summary = {}
+    for k in kernels:
+        avg = {c: sum(v) / len(v) for (n, c), v in data.items() if n == k}
+        nd = min(len(v) for (n, c), v in data.items() if n == k)   # dispatches per counter set
+        # the csv's GRBM_GUI_ACTIVE is summed over the XCDs; rocprofv3's derived metrics take
+        # its largest per-XCD value, the kernel's busy cycles
+        g = avg.get("GRBM_GUI_ACTIVE")
+        g = g / XCD_NUM if g else g
+        d = {}
+        if g:
+            if "SQ_ACTIVE_INST_VALU" in avg:
+                d["VALU busy (SQ_ACTIVE_INST_VALU / CUs / GRBM_GUI_ACTIVE)"] = avg["SQ_ACTIVE_INST_VALU"] / CU_NUM / g
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+                d["MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES / SIMDs / GRBM_GUI_ACTIVE)"] = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / SIMD_NUM / g
+            if "SQ_WAVE_CYCLES" in avg:
+                d["waves per CU (4 SQ_WAVE_CYCLES / CUs / GRBM_GUI_ACTIVE)"] = 4 * avg["SQ_WAVE_CYCLES"] / CU_NUM / g
+            if "SQ_LDS_BANK_CONFLICT" in avg:
+                d["LDS bank-conflict share of time (SQ_LDS_BANK_CONFLICT / CUs / GRBM_GUI_ACTIVE)"] = \
+                    avg["SQ_LDS_BANK_CONFLICT"] / CU_NUM / g
+            if "SQ_ACTIVE_INST_LDS" in avg:
+                d["LDS instruction busy (SQ_ACTIVE_INST_LDS / CUs / GRBM_GUI_ACTIVE)"] = avg["SQ_ACTIVE_INST_LDS"] / CU_NUM / g
+        if "SQ_WAIT_INST_ANY" in avg and "SQ_WAVE_CYCLES" in avg:
+            d["wave time waiting on an instruction's operands (SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES)"] = \
+                avg["SQ_WAIT_INST_ANY"] / avg["SQ_WAVE_CYCLES"]
+        if "SQ_LDS_BANK_CONFLICT" in avg and "SQ_LDS_IDX_ACTIVE" in avg:
+            d["LDS conflict cycles per active LDS cycle"] = avg["SQ_LDS_BANK_CONFLICT"] / max(
+                1.0, avg["SQ_LDS_IDX_ACTIVE"] - avg["SQ_LDS_BANK_CONFLICT"])
+        if "TCC_HIT_sum" in avg and "TCC_MISS_sum" in avg:
+            d["L2 hit rate (TCC_HIT / (TCC_HIT + TCC_MISS))"] = avg["TCC_HIT_sum"] / max(1.0, avg["TCC_HIT_sum"] + avg["TCC_MISS_sum"])
+        if "SQC_ICACHE_MISSES" in avg and "SQC_ICACHE_REQ" in avg:
+            d["instruction cache miss rate (SQC_ICACHE_MISSES / SQC_ICACHE_REQ)"] = avg["SQC_ICACHE_MISSES"] / max(1.0, avg["SQC_ICACHE_REQ"])
+        if "SQ_INSTS_VALU" in avg and "SQ_WAVES" in avg:
+            d["vector instructions per wave"] = avg["SQ_INSTS_VALU"] / avg["SQ_WAVES"]
+        summary[k] = {"dispatches": nd, "counters": avg, "derived": d}
+        lines.append(f"## `{k}` (averages over {nd} dispatches per counter run)\n")
+        lines.append("| counter | average per dispatch |\n|---|---|")
+        lines += [f"| {c} | {v:.6g} |" for c, v in sorted(avg.items())]
+        if g:
+            d["busy cycles per XCD (GRBM_GUI_ACTIVE / 8)"] = g
+        if d:
+            lines.append("\n| derived | value |\n|---|---|")
+            lines += [f"| {c} | {v:.4g} |" for c, v in d.items()]
+        lines.append("")
+    with open(args.out + ".md", "w") as f:
+        f.write("\n".join(lines) + "\n")
+    with open(args.out + ".json", "w") as f:
+        json.dump(summary, f, indent=1)
+    print(json.dumps({k: v["derived"] for k, v in summary.items()}, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -152,7 +229,15 @@ def main():
     s.add_argument("write_csv")
     s.add_argument("--meta", default="gpurun_out/traffic/meta.json")
     s.add_argument("--out", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("csv", nargs="+")
+    c.add_argument("--title", required=True)
+    c.add_argument("--out", required=True)
+    c.add_argument("--command", nargs="*", default=[], help="the rocprofv3 commands that wrote the csvs")
     a = ap.parse_args()
+    if a.cmd == "counters":
+        counters(a)
+        return
     if a.cmd == "run":
         os.makedirs(os.path.dirname(os.path.abspath(a.meta)), exist_ok=True)
         run(a)
