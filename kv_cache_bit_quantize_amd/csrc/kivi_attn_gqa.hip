@@ -33,8 +33,8 @@ struct GqaLds {
     static constexpr int kZeroBytes = kKeyGroup + 256;  // covers every offset a zero row reads at
 };
 
-// Four waves per workgroup (six, at two workgroups per compute unit, measured slower).  The
-// kernel is built for three waves per SIMD.
+// Four waves per workgroup (six and eight, at two workgroups per compute unit, measured
+// slower or no faster).
 constexpr int kGqaWaves = 4;
 constexpr int kGqaBlock = 64 * kGqaWaves;
 
@@ -166,11 +166,12 @@ __global__ __launch_bounds__(kGqaBlock) __attribute__((amdgpu_waves_per_eu(3))) 
     };
 
     __syncthreads();   // the zero area is written
-    // Two register sets of loads, used by alternate iterations: each stream reloads its set
-    // for two iterations ahead right after its last use, so every load has more than an
-    // iteration to arrive (one workgroup per KV head leaves a 512-head batch at about two
-    // waves per SIMD, so the deeper prefetch is what hides the memory latency).
-    constexpr int kPrefetch = 2;
+    // One register set of loads: each stream reloads it for the next iteration right after its
+    // last use in this one, so every load has most of an iteration to arrive.  (Two sets, two
+    // iterations ahead, with the loop body unrolled twice over them, took 168 VGPRs and ran
+    // 92.6 us against 86.2 us for this form at the gqa-mistral-7b shape: the two waves per
+    // SIMD that a 512-workgroup batch leaves are held by their vector work, not by latency.)
+    constexpr int kPrefetch = 1;
     auto load_all = [&](Loads& L, int it) {
         load_kp(L, it);
         load_kc(L, it);
@@ -356,19 +357,15 @@ __global__ __launch_bounds__(kGqaBlock) __attribute__((amdgpu_waves_per_eu(3))) 
     // Every load is issued unconditionally (past the end it reads the last iteration's data
     // again, from the L2) and the loop has one exit, at its head, so both paths into the head
     // have issued the same loads: the compiler then knows how many loads are in flight at
-    // each use and waits for exactly the one it needs.  With an odd iteration count the last
-    // pair's second half is idle: its groups are out of range, so its logits are -inf and its
-    // weights zero.
-    Loads set0, set1;
+    // each use and waits for exactly the one it needs.  When a wave's range has an odd number
+    // of groups, its last iteration's second half is idle: that group is out of range, so its
+    // logits are -inf and its weights zero.
+    Loads set0;
     uint32_t tag;
     if (iters > 0) {
         load_all(set0, 0);
-        load_all(set1, min(1, iters - 1));
         tag = settle_tag(tag_v);
-        for (int it = 0; it < iters; it += 2) {
-            iteration(set0, it);
-            iteration(set1, it + 1);
-        }
+        for (int it = 0; it < iters; ++it) iteration(set0, it);
     } else {
         tag = settle_tag(tag_v);
     }
