@@ -28,21 +28,41 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC, *srcs, "-o", LIB + ".tmp"]
-    if verbose:
-        print(" ".join(cmd), flush=True)
+def _run(cmd):
     r = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass does not know the packed-fp32 feature and says so; drop that line
     noise = "'-packed-fp32-ops' is not a recognized feature"
     err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{err}")
+        raise RuntimeError(f"hipcc failed ({r.returncode}): {' '.join(cmd)}\n{err}")
+    return err
+
+
+def build(verbose: bool = False, out: str = LIB, extra_flags=(), jobs: int = 8) -> str:
+    """Compile every source to an object file (in parallel, each with its own gfx950 code
+    object) and link them into ``out``.  ``extra_flags`` go on every compile and the link,
+    e.g. ``-Xarch_host -fsanitize=address`` for a build whose host code is sanitized."""
+    import concurrent.futures
+    import tempfile
+    with tempfile.TemporaryDirectory(prefix="kivi_build_") as tmp:
+        objs, cmds = [], []
+        for s in SOURCES:
+            obj = os.path.join(tmp, os.path.splitext(s)[0] + ".o")
+            objs.append(obj)
+            cmds.append([HIPCC, *FLAGS, *extra_flags, "-c", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+                         os.path.join(CSRC, s), "-o", obj])
+        link = [HIPCC, *FLAGS, *extra_flags, *objs, "-o", out + ".tmp"]
+        if verbose:
+            for c in cmds + [link]:
+                print(" ".join(c), flush=True)
+        with concurrent.futures.ThreadPoolExecutor(max(1, jobs)) as pool:
+            errs = list(pool.map(_run, cmds))
+        errs.append(_run(link))
+    err = "\n".join(e for e in errs if e.strip())
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(out + ".tmp", out)
+    return out
 
 
 if __name__ == "__main__":

@@ -10,7 +10,9 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libkivi.so")
+# the in-tree build, or another build of the same sources named by KIVI_LIBRARY (for example
+# one with host-side sanitizers)
+LIB_PATH = os.environ.get("KIVI_LIBRARY", os.path.join(_PKG, "libkivi.so"))
 
 KIVI_OK = 0
 _STATUS_NAMES = {0: "KIVI_OK", -1: "KIVI_ERR_NULL", -2: "KIVI_ERR_SHAPE", -3: "KIVI_ERR_UNSUPPORTED",
@@ -123,6 +125,17 @@ def _ptr(t):
     return C.c_void_p(t.data_ptr()) if t is not None else None
 
 
+def _zeros(shape, dtype, device):
+    """Every cache buffer and workspace is allocated here and every output the wrappers
+    allocate in _empty, so that a caller can route them to its own allocator (a pool, or
+    buffers with guard bands) by replacing these two functions."""
+    return torch.zeros(shape, dtype=dtype, device=device)
+
+
+def _empty(shape, dtype, device):
+    return torch.empty(shape, dtype=dtype, device=device)
+
+
 class Cache:
     """Device buffers of one KIVI cache (layout of include/kivi.h) and its descriptor."""
 
@@ -133,16 +146,16 @@ class Cache:
         rows = batch * kv_heads
         u8, f16 = torch.uint8, torch.int16
         if bits == 4:                              # token-major, two codes per byte
-            self.k_codes = torch.zeros((rows, token_cap, head_dim // 2), dtype=u8, device=device)
-            self.v_codes = torch.zeros((rows, token_cap, head_dim // 2), dtype=u8, device=device)
+            self.k_codes = _zeros((rows, token_cap, head_dim // 2), dtype=u8, device=device)
+            self.v_codes = _zeros((rows, token_cap, head_dim // 2), dtype=u8, device=device)
         else:                                      # one 1024-byte tile of codes per 32 tokens
             tiles = token_cap // 32
-            self.k_codes = torch.zeros((rows, tiles, 32 * head_dim // 4), dtype=u8, device=device)
-            self.v_codes = torch.zeros((rows, tiles, 32 * head_dim // 4), dtype=u8, device=device)
-        self.k_sz = torch.zeros((rows, token_cap // group, head_dim, 2), dtype=f16, device=device)
-        self.v_sz = torch.zeros((rows, token_cap, head_dim // group, 2), dtype=f16, device=device)
-        self.k_res = torch.zeros((rows, residual_cap, head_dim), dtype=f16, device=device)
-        self.v_res = torch.zeros((rows, residual_cap, head_dim), dtype=f16, device=device)
+            self.k_codes = _zeros((rows, tiles, 32 * head_dim // 4), dtype=u8, device=device)
+            self.v_codes = _zeros((rows, tiles, 32 * head_dim // 4), dtype=u8, device=device)
+        self.k_sz = _zeros((rows, token_cap // group, head_dim, 2), dtype=f16, device=device)
+        self.v_sz = _zeros((rows, token_cap, head_dim // group, 2), dtype=f16, device=device)
+        self.k_res = _zeros((rows, residual_cap, head_dim), dtype=f16, device=device)
+        self.v_res = _zeros((rows, residual_cap, head_dim), dtype=f16, device=device)
         flags = (KIVI_FLUSH_ALL if flush_all else 0) | (KIVI_CODES_4BIT if bits == 4 else 0)
         self.c = kivi_cache(batch, kv_heads, head_dim, group, residual_cap, token_cap, 0, 0, 0,
                             flags, self.k_codes.data_ptr(), self.v_codes.data_ptr(), self.k_sz.data_ptr(),
@@ -179,7 +192,7 @@ class Cache:
                    lib.kivi_decode_step_workspace(C.byref(self.c), q_heads, num_splits, 0))
         if self._ws is None or self._ws.numel() < need:
             # zero-filled: the leading per-row arrival counters must start at zero
-            self._ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=self.device)
+            self._ws = _zeros(max(need, 256), dtype=torch.uint8, device=self.device)
         return self._ws
 
 
@@ -229,10 +242,10 @@ def kivi_decode_attn(cache, q, sm_scale, out=None, lse=None, num_splits=0, works
         raise ValueError("expected contiguous float16 q [B, Hq, D]")
     B, Hq, D = q.shape
     if out is None:
-        out = torch.empty_like(q)
+        out = _empty(q.shape, dtype=q.dtype, device=q.device)
     want_lse = lse is not None and lse is not False
     if lse is True:
-        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+        lse = _empty((B, Hq), dtype=torch.float32, device=q.device)
     ws = workspace if workspace is not None else cache.workspace(Hq, num_splits)
     _check(lib.kivi_decode_attn(C.byref(cache.c), _ptr(q), Hq, float(sm_scale), _ptr(out),
                                 _ptr(lse) if want_lse else None, _ptr(ws), ws.numel() * ws.element_size(),
@@ -271,10 +284,10 @@ def kivi_decode_attn_rope(cache, q, sm_scale, rope_base=10000.0, out=None, lse=N
         raise ValueError("expected contiguous float16 q [B, Hq, D]")
     B, Hq, D = q.shape
     if out is None:
-        out = torch.empty_like(q)
+        out = _empty(q.shape, dtype=q.dtype, device=q.device)
     want_lse = lse is not None and lse is not False
     if lse is True:
-        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+        lse = _empty((B, Hq), dtype=torch.float32, device=q.device)
     splits = num_splits if num_splits > 0 else kivi_decode_attn_rope_splits(cache, Hq)
     ws = workspace if workspace is not None else cache.workspace(Hq, splits)
     _check(lib.kivi_decode_attn_rope(C.byref(cache.c), _ptr(q), Hq, float(sm_scale), float(rope_base), _ptr(out),
@@ -293,10 +306,10 @@ def kivi_decode_step(cache, k_new, v_new, q, sm_scale, out=None, lse=None, num_s
         raise ValueError("expected contiguous float16 q [B, Hq, D]")
     B, Hq, D = q.shape
     if out is None:
-        out = torch.empty_like(q)
+        out = _empty(q.shape, dtype=q.dtype, device=q.device)
     want_lse = lse is not None and lse is not False
     if lse is True:
-        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+        lse = _empty((B, Hq), dtype=torch.float32, device=q.device)
     ws = workspace if workspace is not None else cache.workspace(Hq, num_splits)
     flushed = C.c_int32(0)
     _check(lib.kivi_decode_step(C.byref(cache.c), _ptr(k_new), _ptr(v_new), _ptr(q), Hq, float(sm_scale),
@@ -316,10 +329,10 @@ def kivi_decode_step_rope(cache, k_new, v_new, q, sm_scale, rope_base=10000.0, o
         raise ValueError("expected contiguous float16 q [B, Hq, D]")
     B, Hq, D = q.shape
     if out is None:
-        out = torch.empty_like(q)
+        out = _empty(q.shape, dtype=q.dtype, device=q.device)
     want_lse = lse is not None and lse is not False
     if lse is True:
-        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+        lse = _empty((B, Hq), dtype=torch.float32, device=q.device)
     splits = num_splits
     if splits <= 0:   # the library's choice on the state after the append
         splits = lib.kivi_decode_step_splits(C.byref(cache.c), Hq, 1)
@@ -360,10 +373,10 @@ def kivi_decode_attn_ragged(cache, state, q, sm_scale, out=None, lse=None, num_s
         raise ValueError("expected contiguous int32 state [B, 4]")
     B, Hq, D = q.shape
     if out is None:
-        out = torch.empty_like(q)
+        out = _empty(q.shape, dtype=q.dtype, device=q.device)
     want_lse = lse is not None and lse is not False
     if lse is True:
-        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+        lse = _empty((B, Hq), dtype=torch.float32, device=q.device)
     splits = num_splits if num_splits > 0 else kivi_decode_attn_ragged_splits(cache, Hq)
     ws = workspace if workspace is not None else cache.workspace(Hq, splits)
     _check(lib.kivi_decode_attn_ragged(C.byref(cache.c), _ptr(state), _ptr(q), Hq, float(sm_scale), _ptr(out),
@@ -382,10 +395,10 @@ def kivi_decode_attn_rope_ragged(cache, state, q, sm_scale, rope_base=10000.0, o
         raise ValueError("expected contiguous int32 state [B, 4]")
     B, Hq, D = q.shape
     if out is None:
-        out = torch.empty_like(q)
+        out = _empty(q.shape, dtype=q.dtype, device=q.device)
     want_lse = lse is not None and lse is not False
     if lse is True:
-        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+        lse = _empty((B, Hq), dtype=torch.float32, device=q.device)
     splits = num_splits if num_splits > 0 else kivi_decode_attn_rope_ragged_splits(cache, Hq)
     ws = workspace if workspace is not None else cache.workspace(Hq, splits)
     _check(lib.kivi_decode_attn_rope_ragged(C.byref(cache.c), _ptr(state), _ptr(q), Hq, float(sm_scale),
@@ -422,13 +435,13 @@ def kivi_decode_attn_fp16(k, v, q, sm_scale, tokens=None, out=None, lse=None, nu
     tokens = T_cap if tokens is None else tokens
     Hq = q.shape[1]
     if out is None:
-        out = torch.empty_like(q)
+        out = _empty(q.shape, dtype=q.dtype, device=q.device)
     want_lse = lse is not None and lse is not False
     if lse is True:
-        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+        lse = _empty((B, Hq), dtype=torch.float32, device=q.device)
     if workspace is None:
         need = lib.kivi_decode_attn_fp16_workspace(B, Hkv, tokens, Hq, num_splits)
-        workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=q.device)
+        workspace = _zeros(max(need, 256), dtype=torch.uint8, device=q.device)
     _check(lib.kivi_decode_attn_fp16(_ptr(k), _ptr(v), B, Hkv, tokens, T_cap, _ptr(q), Hq, float(sm_scale), _ptr(out),
                                      _ptr(lse) if want_lse else None, _ptr(workspace),
                                      workspace.numel() * workspace.element_size(), num_splits, _stream(q)),
@@ -478,7 +491,7 @@ def kivi_read_probe(buf, sink=None):
     if not buf.is_contiguous():
         raise ValueError("expected a contiguous tensor")
     if sink is None:
-        sink = torch.empty(lib.kivi_read_probe_sink_bytes() // 4, dtype=torch.int32, device=buf.device)
+        sink = _empty(lib.kivi_read_probe_sink_bytes() // 4, dtype=torch.int32, device=buf.device)
     _check(lib.kivi_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(buf)),
            "kivi_read_probe")
     return sink

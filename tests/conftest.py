@@ -19,6 +19,37 @@ def oracle_lib():
     return ref.lib()
 
 
+@pytest.fixture(autouse=True)
+def guard_bands(request):
+    """GPU tests: every buffer the binding allocates gets canary guard bands (kivi_testlib.Guard),
+    checked after every library call and at the end of the test."""
+    if request.node.get_closest_marker("gpu") is None:
+        yield None
+        return
+    import torch
+    if not torch.cuda.is_available():
+        yield None
+        return
+    from kivi_testlib import Guard
+    from kv_cache_bit_quantize_amd import kivi
+    guard = Guard()
+    check = kivi._check
+
+    def checked(status, where):
+        check(status, where)
+        guard.check(where)
+
+    mp = pytest.MonkeyPatch()
+    mp.setattr(kivi, "_zeros", guard.zeros)
+    mp.setattr(kivi, "_empty", guard.empty)
+    mp.setattr(kivi, "_check", checked)
+    try:
+        yield guard
+    finally:
+        mp.undo()
+    guard.check("the test")
+
+
 def pytest_sessionfinish(session, exitstatus):
     """Write the worst attention errors seen by the GPU parity tests (if any ran)."""
     try:

@@ -99,6 +99,57 @@ def assert_lse_close(lse_gpu, lse_ref, rows=None, tol=ATTN_TOL):
     assert ratio.max() <= 1.0, f"lse row {worst}: |d| {abs(g[worst] - r[worst]):.3e} > {bound[worst]:.3e} (lse {r[worst]:.1f})"
 
 
+class Guard:
+    """Guard bands around every device buffer the binding allocates (cache buffers,
+    workspaces, outputs): each buffer is the middle of a larger allocation whose first and
+    last MARGIN bytes hold the CANARY byte, and check() fails if any of them changed, i.e. a
+    kernel wrote outside the buffer it was handed.  Outputs start filled with the canary too,
+    so an output element the kernel never wrote fails the parity comparison.  Buffers are
+    tracked by weak reference and drop out once freed."""
+    MARGIN = 4096           # bytes on each side; keeps the buffer 4096-byte aligned
+    CANARY = 0xA5
+
+    def __init__(self):
+        import weakref
+        self._weak = weakref.ref
+        self.items = []     # (weakref to the buffer, bytes, description)
+
+    def _alloc(self, shape, dtype, device, zero):
+        shape = (shape,) if isinstance(shape, int) else tuple(shape)
+        n = int(np.prod(shape, dtype=np.int64)) * torch.empty((), dtype=dtype).element_size()
+        raw = torch.full((n + 2 * self.MARGIN,), self.CANARY, dtype=torch.uint8, device=device)
+        t = raw[self.MARGIN:self.MARGIN + n].view(dtype).view(shape)
+        if zero:
+            t.zero_()
+        self.items.append((self._weak(t), n, f"{dtype} {list(shape)}"))
+        return t
+
+    def zeros(self, shape, dtype, device):
+        return self._alloc(shape, dtype, device, True)
+
+    def empty(self, shape, dtype, device):
+        return self._alloc(shape, dtype, device, False)
+
+    def check(self, where=""):
+        live = []
+        for ref_, n, what in self.items:
+            t = ref_()
+            if t is not None:
+                raw = torch.empty(0, dtype=torch.uint8, device=t.device).set_(t.untyped_storage())
+                live.append((raw, n, what))
+        self.items = [it for it in self.items if it[0]() is not None]
+        if not live:
+            return
+        if any(raw.is_cuda for raw, _, _ in live):
+            torch.cuda.synchronize()
+        M, Cb = self.MARGIN, self.CANARY
+        bad = torch.stack([torch.stack([(raw[:M] != Cb).any(), (raw[M + n:] != Cb).any()])
+                           for raw, n, _ in live]).cpu()
+        for (raw, n, what), (lo, hi) in zip(live, bad.tolist()):
+            assert not (lo or hi), f"after {where}: a write {'before' if lo else 'past the end of'} the {what} " \
+                                   f"buffer ({n} bytes) changed its guard band"
+
+
 class SlicedRef:
     """One oracle cache per slice of the batch's sequences, driven from host threads (the
     oracle's C calls release the GIL), so that whole full-size caches can be checked in

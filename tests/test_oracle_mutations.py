@@ -106,13 +106,17 @@ def _build(src_text, out_dir):
     return lib
 
 
-def _run_pins(lib, slow):
+def _run_pins(lib, slow, workers=0):
     env = dict(os.environ, KIVI_ORACLE_LIB=lib)
     files = [os.path.join(ROOT, "tests", f) for f in
-             ("test_oracle_quant.py", "test_oracle_quant4.py", "test_oracle_attn.py", "test_oracle_cache.py",
-              "test_oracle_fp16.py", "test_oracle_rope.py")]
+             # cheap pins first: with -x a caught mistake stops at its first failing pin, and
+             # the brute-force quantizer pins take most of the time
+             ("test_oracle_cache.py", "test_oracle_attn.py", "test_oracle_rope.py", "test_oracle_fp16.py",
+              "test_oracle_quant4.py", "test_oracle_quant.py")]
     cmd = [sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
            "-m", "not gpu" if slow else "not gpu and not slow", *files]
+    if workers:
+        cmd[3:3] = ["-n", str(workers)]
     return subprocess.run(cmd, env=env, cwd=ROOT, capture_output=True, text=True, timeout=600)
 
 
@@ -141,5 +145,5 @@ def test_unmutated_copy_passes():
     with open(SRC) as f:
         text = f.read()
     with tempfile.TemporaryDirectory() as d:
-        r = _run_pins(_build(text, d), False)
+        r = _run_pins(_build(text, d), False, workers=max(1, min(8, os.cpu_count() or 1)))
     assert r.returncode == 0, r.stdout[-3000:]
