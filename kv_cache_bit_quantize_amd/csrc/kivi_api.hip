@@ -360,6 +360,8 @@ int prepare_attn(const kivi_cache* c, const uint16_t* q, int32_t q_heads, float 
     // workgroups resident at once: three 4-wave query-group workgroups or one 12-wave
     // single-query workgroup per CU
     a.slot_budget = (int32_t)(a.nq > 1 || code_bits(c) == 4 ? kTargetBlocks : kTargetBlocksSingle);
+    // the ragged plan counts query rows in 32 bits (and launches them in one grid dimension)
+    if (seq_state != nullptr && a.q_rows > INT32_MAX) return KIVI_ERR_SHAPE;
     a.group = c->group;
     a.bits = code_bits(c);
     // ragged batches keep one 12-wave workgroup per CU (their plan shares a round of 256)

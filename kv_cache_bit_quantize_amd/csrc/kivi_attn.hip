@@ -53,7 +53,7 @@ constexpr int kAreaBytes = kZeroOff + 512;
 // them; 4 (three workgroups per CU) when a uniform batch has more query rows than the chip has
 // CUs, so that its rows run in one round of resident workgroups instead of several rounds that
 // each pay the start-up again.
-template <int GS, int W>
+template <int GS, int W, bool RAGGED>
 __global__ __launch_bounds__(64 * W) void attn_split_kernel(AttnArgs a) {
     constexpr int kSqWaves = W, kSqSlots = 2 * W;
     __shared__ __align__(16) uint8_t sh_area[2][kSqWaves][kAreaBytes];
@@ -61,8 +61,11 @@ __global__ __launch_bounds__(64 * W) void attn_split_kernel(AttnArgs a) {
     __shared__ float sh_m[1][kSqSlots], sh_l[1][kSqSlots];
     __shared__ int sh_next;   // pair queue of the workgroup's range (pairs past the static ones)
 
-    const int split = grid_split(a);
-    const int64_t qrow = grid_row(a);
+    // (ragged batch: the plan uses sh_o, unused until the end)
+    const WorkItem wi = work_item<RAGGED>(a, reinterpret_cast<int32_t*>(&sh_o[0][0][0]));
+    if (RAGGED && wi.split < 0) return;   // (ragged batch) past the plan's last item
+    const int split = wi.split;
+    const int64_t qrow = wi.row;
     // Query row b*Hq + h reads kv row b*Hkv + h/ratio = qrow/ratio (Hq = Hkv*ratio): one 32-bit
     // division, none for one query per kv head.  The set-up before the first loads is kept short:
     // each of its instructions delays them, and a CU issues it for three waves per SIMD.
@@ -113,8 +116,7 @@ __global__ __launch_bounds__(64 * W) void attn_split_kernel(AttnArgs a) {
     float lsum = 0.0f, m = -INFINITY;
     float vs = 0.0f;                   // power-of-two factor keeping the value weights in fp16 range
 
-    const RowState rs = row_state(a, kvrow, split);
-    if (split >= rs.splits) return;   // (ragged batch) this row uses fewer splits: the whole workgroup leaves
+    const RowState rs = RAGGED ? wi.rs : row_state(a);
     const int n_groups = rs.n_quant / kG;
     const int g_lo = split * rs.groups_per_split;
     const int g_hi = min(n_groups, g_lo + rs.groups_per_split);
@@ -350,11 +352,14 @@ __global__ __launch_bounds__(64 * W) void attn_split_kernel(AttnArgs a) {
 hipError_t launch_decode_attn(const AttnArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
     if (a.bits == 4) return launch_decode_attn_q4(a, s, t0, t1);
     if (a.nq > 1) return launch_decode_attn_gqa(a, s, t0, t1);
-    if (a.sq_waves == 4) {
-        KIVI_BY_GROUP(a.group, hipExtLaunchKernelGGL((attn_split_kernel<GS, 4>), attn_grid(a, a.q_rows), dim3(64 * 4), 0,
-                                                     s, t0, t1, 0, a))
+    if (a.seq_state != nullptr) {   // ragged batches: one 12-wave workgroup per CU
+        KIVI_BY_GROUP(a.group, hipExtLaunchKernelGGL((attn_split_kernel<GS, kSqWaves, true>), attn_grid(a, a.q_rows),
+                                                     dim3(64 * kSqWaves), 0, s, t0, t1, 0, a))
+    } else if (a.sq_waves == 4) {
+        KIVI_BY_GROUP(a.group, hipExtLaunchKernelGGL((attn_split_kernel<GS, 4, false>), attn_grid(a, a.q_rows),
+                                                     dim3(64 * 4), 0, s, t0, t1, 0, a))
     } else {
-        KIVI_BY_GROUP(a.group, hipExtLaunchKernelGGL((attn_split_kernel<GS, kSqWaves>), attn_grid(a, a.q_rows),
+        KIVI_BY_GROUP(a.group, hipExtLaunchKernelGGL((attn_split_kernel<GS, kSqWaves, false>), attn_grid(a, a.q_rows),
                                                      dim3(64 * kSqWaves), 0, s, t0, t1, 0, a))
     }
     return hipGetLastError();

@@ -153,69 +153,291 @@ __device__ __forceinline__ uint4 load_value_pairs(const uint32_t* p) {
     }
 }
 
-// Grid of a decode-attention launch.  Workgroups go to the XCDs round-robin by linear id.
-// Normally x = split: a row's splits spread over the XCDs.  In a ragged batch the
-// sequences use different numbers of splits, so x = row instead (a sequence's kv heads are
-// consecutive rows, so every XCD gets a share of every sequence whatever its length).
-// The layout is chosen in launch code and kernels alike from a.seq_state.
-inline dim3 attn_grid(const AttnArgs& a, int64_t rows) {
-    return a.seq_state != nullptr ? dim3((unsigned)rows, (unsigned)a.splits) : dim3((unsigned)a.splits, (unsigned)rows);
-}
-__device__ __forceinline__ int grid_split(const AttnArgs& a) {
-    return a.seq_state != nullptr ? (int)blockIdx.y : (int)blockIdx.x;
-}
-__device__ __forceinline__ int64_t grid_row(const AttnArgs& a) {
-    return a.seq_state != nullptr ? (int64_t)blockIdx.x : (int64_t)blockIdx.y;
-}
-
-// The cache state one workgroup attends over: the call's, or (ragged batch) its sequence's,
-// with the number of splits its row uses, its key groups per split and the split that also
-// reads the residual.  A sequence state out of range gives an empty context (nothing is
-// read) and sets the sequence's kSeqBadState flag.
-//
-// Ragged batch plan, the same in every workgroup: the batch's work W (key groups, with the
-// residual counted as groups by its bytes) is read from all sequence states; a workgroup
-// should take about W * rows_per_sequence / slot_budget of it, so that the whole batch fits
-// one round of resident workgroups with even shares; a sequence uses floor(its work / that
-// share) splits (at least one, at most the grid's).  Workgroups past their row's count do
-// nothing.
+// The cache state one workgroup attends over, with the number of splits its row uses, its
+// key groups per split and the split that also reads the residual.
 struct RowState {
     int32_t n_quant, n_res, res_head, groups_per_split, res_split, splits;
 };
+// One workgroup's work: its grid row (a query row, or a query-group row), its split of that
+// row's context, and (ragged batch) the state of the row's sequence; split < 0: no work.
+struct WorkItem {
+    int64_t row;
+    int split;
+    RowState rs;
+};
+
+// Grid of a decode-attention launch.  Uniform batch: x = split, y = row (workgroups go to the
+// XCDs round-robin by linear id, so a row's splits spread over them).  Ragged batch: one
+// dimension, one workgroup per item of the plan below, at most max(slot_budget, rows) of them.
+inline dim3 attn_grid(const AttnArgs& a, int64_t rows) {
+    if (a.seq_state != nullptr) return dim3((unsigned)(rows > a.slot_budget ? rows : a.slot_budget));
+    return dim3((unsigned)a.splits, (unsigned)rows);
+}
+__device__ __forceinline__ RowState row_state(const AttnArgs& a) {
+    return {a.n_quant, a.n_res, a.res_head, a.groups_per_split, a.splits - 1, a.splits};
+}
+
 // key groups the residual counts as (512 bytes per fp16 token against 96 per 2-bit token)
 __device__ __forceinline__ int32_t residual_units(int32_t n_res) { return (n_res * 512 + 96 * kG - 1) / (96 * kG); }
-// The batch's total work, by each wave: lane i reads sequence i's state (one coalesced
-// 16-byte load per lane and 64 sequences), then a wave sum.
-__device__ __forceinline__ int32_t batch_units(const AttnArgs& a, int64_t batch) {
-    const int lane = threadIdx.x & 63;
-    int32_t u = 0;
-    for (int64_t b = lane; b < batch; b += 64) {
-        const int4 st = *reinterpret_cast<const int4*>(a.seq_state + 4 * b);
-        if (state_in_range(st.x, st.y, st.z, a.token_cap, a.residual_cap, a.group)) u += st.x / kG + residual_units(st.y);
-    }
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) u += __shfl_xor(u, m, 64);
-    return __builtin_amdgcn_readfirstlane(u);
+// work of sequence b in key groups (its residual counted by its bytes); 0 for a state out of range
+__device__ __forceinline__ int32_t seq_units(const AttnArgs& a, int64_t b) {
+    const int4 st = *reinterpret_cast<const int4*>(a.seq_state + 4 * b);
+    return state_in_range(st.x, st.y, st.z, a.token_cap, a.residual_cap, a.group) ? st.x / kG + residual_units(st.y) : 0;
 }
-__device__ __forceinline__ RowState row_state(const AttnArgs& a, int64_t kvrow, int split) {
-    // (the uniform case is the likely one: its code is laid out first, so the set-up before a
-    // kernel's first loads does not jump over the ragged plan's)
-    if (__builtin_expect(a.seq_state == nullptr, 1))
-        return {a.n_quant, a.n_res, a.res_head, a.groups_per_split, a.splits - 1, a.splits};
-    int32_t* s = a.seq_state + 4 * (kvrow / a.kv_heads);
-    int32_t nq = s[0], nr = s[1], rh = s[2];
-    if (!state_in_range(nq, nr, rh, a.token_cap, a.residual_cap, a.group)) {
-        if (split == 0 && threadIdx.x == 0)
-            __hip_atomic_fetch_or(&s[3], kSeqBadState, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        nq = nr = rh = 0;
+// Integer reductions and scan over the wave without LDS traffic (the plan below runs them
+// back to back, so each step's latency counts): DPP inside 16-lane rows, then readlane of
+// the four rows' results.
+template <int CTRL>
+__device__ __forceinline__ int32_t dpp_i(int32_t v) { return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false); }
+__device__ __forceinline__ int32_t wave_sum(int32_t v) {
+    v += dpp_i<0xB1>(v);    // lane^1
+    v += dpp_i<0x4E>(v);    // lane^2
+    v += dpp_i<0x141>(v);   // the other quad of the half-row
+    v += dpp_i<0x140>(v);   // the other half-row
+    return (__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
+           (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
+}
+__device__ __forceinline__ int32_t wave_max(int32_t v) {
+    v = max(v, dpp_i<0xB1>(v));
+    v = max(v, dpp_i<0x4E>(v));
+    v = max(v, dpp_i<0x141>(v));
+    v = max(v, dpp_i<0x140>(v));
+    return max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+               max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+// sum of values below 2^47 per lane, as two 32-bit sums of 16-bit and 31-bit parts
+__device__ __forceinline__ int64_t wave_sum64(int64_t v) {
+    const int64_t lo = wave_sum((int32_t)(v & 0xffff)), hi = wave_sum((int32_t)(v >> 16));
+    return (hi << 16) + lo;
+}
+// inclusive prefix sum over the 64 lanes: inside each 16-lane row (shifts right by 1, 2, 4
+// and 8; lanes without a source add 0), then the totals of the rows below
+__device__ __forceinline__ int32_t wave_prefix(int32_t v) {
+    v += dpp_i<0x111>(v);
+    v += dpp_i<0x112>(v);
+    v += dpp_i<0x114>(v);
+    v += dpp_i<0x118>(v);
+    const int32_t r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31),
+                  r2 = __builtin_amdgcn_readlane(v, 47);
+    const int row = (threadIdx.x & 63) >> 4;
+    return v + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
+}
+// ceil(u / s), u < 2^24: the product with the reciprocal is within one of the quotient
+__device__ __forceinline__ int32_t ceil_div_small(int32_t u, int32_t s, float rcp) {
+    int32_t q = (int32_t)((float)u * rcp);
+    q += (int32_t)(q * s < u);
+    q -= (int32_t)((q > 0) & ((q - 1) * s >= u));   // (bitwise: no branches)
+    return q;
+}
+// splits of a sequence of u units at a share of s units: ceil(u / s), at least 1, at most cap
+__device__ __forceinline__ int32_t seq_splits(int32_t u, int32_t s, float rcp, int32_t cap) {
+    return min(cap, max(1, ceil_div_small(u, s, rcp)));
+}
+
+// Ragged batch plan, computed alike by every wave of every workgroup from the sequence states
+// (device memory, so a serving loop steps them without the host).  Sequence b's work u_b is
+// its key groups plus its residual counted as groups by its bytes.  For a share s, sequence b
+// takes a_b = ceil(u_b / s) splits (at least one, at most the workspace's a.splits) on each of
+// its rows_per_seq grid rows; the plan uses the smallest s for which the items, rows_per_seq *
+// sum a_b, fit the resident workgroups (a.slot_budget), found by bisection between
+// rows_per_seq*W/budget (below it the items cannot fit) and rows_per_seq*W/(budget -
+// rows_per_seq*batch) (every sequence rounds up by less than one split).  So the whole batch
+// runs in one round and no item exceeds the share.
+//
+// Placement.  The hardware deals a launch's workgroups to the XCDs in turn and, inside an
+// XCD, to its CUs in turn, so workgroups i, i + kCus, i + 2 kCus, ... share a CU.  With up
+// to 64 sequences the items are ranked by size (the sequence's groups per split, largest
+// first; a sequence's items are consecutive ranks, split-major, its rows one after another)
+// and dealt in a snake: rounds of kCus workgroups take ranks in order, every other round in
+// reverse, so each CU gets a large, a middle and a small item instead of whatever sizes
+// sequence order puts together.  Larger batches take the items in sequence order.  Either
+// way workgroup i finds its item with a prefix sum over the wave, and workgroups past the
+// last item have none.  A state out of range counts as empty (one split that reads nothing)
+// and its split-0 first-row item sets the sequence's kSeqBadState flag.
+constexpr int kPlanRegs = 4;    // sequences lane + 64j, j < kPlanRegs, keep their work in registers
+// One wave's plan (lds: 128 free words)
+__device__ __forceinline__ WorkItem ragged_plan(const AttnArgs& a, int32_t* lds) {
+    const int lane = threadIdx.x & 63;
+    // (the host keeps a ragged grid's rows below 2^31: 32-bit divisions)
+    const int32_t batch = (int32_t)((uint32_t)a.q_rows / (uint32_t)a.q_heads);
+    const int32_t rps = (int32_t)((uint32_t)a.block_rows / (uint32_t)batch);
+    const int32_t cap = a.splits;
+    // the lane's own sequence's state stays in registers for the item's state below
+    int4 st0 = make_int4(0, 0, 0, 0);
+    if (lane < batch) st0 = *reinterpret_cast<const int4*>(a.seq_state + 4 * lane);
+    const bool ok0 = lane < batch && state_in_range(st0.x, st0.y, st0.z, a.token_cap, a.residual_cap, a.group);
+    int32_t u[kPlanRegs];
+    u[0] = ok0 ? st0.x / kG + residual_units(st0.y) : 0;
+    int64_t w = u[0];
+    int32_t umax = u[0];
+#pragma unroll
+    for (int j = 1; j < kPlanRegs; ++j) {
+        const int64_t b = lane + 64 * j;
+        u[j] = b < batch ? seq_units(a, b) : 0;
+        w += u[j];
+        umax = max(umax, u[j]);
     }
-    const int32_t units = nq / kG + residual_units(nr);
-    const int64_t batch = a.q_rows / a.q_heads;
-    const int64_t total = batch_units(a, batch);
-    const int64_t rows_per_seq = a.block_rows / batch;
-    const int64_t share = max((int64_t)1, (total * rows_per_seq + a.slot_budget - 1) / a.slot_budget);
-    const int32_t active = (int32_t)max((int64_t)1, min((int64_t)a.splits, (int64_t)units / share));
-    return {nq, nr, rh, (units + active - 1) / active, active - 1, active};
+    for (int64_t b = lane + 64 * kPlanRegs; b < batch; b += 64) {
+        const int32_t x = seq_units(a, b);
+        w += x;
+        umax = max(umax, x);
+    }
+    const int64_t total = wave_sum64(w) * rps;   // item-units of the whole batch
+    umax = max(1, wave_max(umax));
+    // most splits (summed over sequences) that fit the budget
+    const int32_t most = a.slot_budget / rps;
+    // sum of a_b at share s, saturated past `most` (only the comparison with it matters)
+    auto splits_at = [&](int32_t s) {
+        const float rcp = __builtin_amdgcn_rcpf((float)s);
+        int32_t c = lane < batch ? seq_splits(u[0], s, rcp, cap) : 0;
+        if (batch > 64) {
+#pragma unroll
+            for (int j = 1; j < kPlanRegs; ++j) {
+                const int32_t x = seq_splits(u[j], s, rcp, cap);
+                c += lane + 64 * j < batch ? x : 0;
+            }
+            for (int64_t b = lane + 64 * kPlanRegs; b < batch && c <= most; b += 64)
+                c += seq_splits(seq_units(a, b), s, rcp, cap);
+        }
+        return wave_sum(min(c, most + 1));
+    };
+    int64_t hi = umax;
+    const int64_t room = (int64_t)a.slot_budget - (int64_t)rps * batch;
+    if (room > 0) hi = min(hi, max((int64_t)1, (total + room - 1) / room));
+    int32_t lo = (int32_t)min(hi, max((int64_t)1, (total + a.slot_budget - 1) / a.slot_budget));
+    while (lo < hi) {
+        const int32_t mid = lo + (int32_t)(hi - lo) / 2;
+        if (splits_at(mid) <= most) hi = mid;
+        else lo = mid + 1;
+    }
+    const int32_t share = __builtin_amdgcn_readfirstlane(lo);
+    const float rcp = __builtin_amdgcn_rcpf((float)share);
+
+    // the item's sequence k (a lane of chunk 0, or of a later chunk), its split and row
+    // (items are fewer than 2^31: 32-bit divisions)
+    auto item = [&](int64_t seq, int32_t a_k, int32_t u_k, int32_t local, int4 st) -> WorkItem {
+        const int split = (int)((uint32_t)local / (uint32_t)rps);
+        const int32_t r = local - split * rps;
+        int32_t nq = st.x, nr = st.y, rh = st.z;
+        if (!state_in_range(nq, nr, rh, a.token_cap, a.residual_cap, a.group)) {
+            if (split == 0 && r == 0 && threadIdx.x == 0)
+                __hip_atomic_fetch_or(&a.seq_state[4 * seq + 3], kSeqBadState, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            nq = nr = rh = 0;
+        }
+        return {seq * rps + r, split, {nq, nr, rh, (u_k + a_k - 1) / a_k, a_k - 1, a_k}};
+    };
+    auto lane_state = [&](int k) {
+        return make_int4(__builtin_amdgcn_readlane(st0.x, k), __builtin_amdgcn_readlane(st0.y, k),
+                         __builtin_amdgcn_readlane(st0.z, k), 0);
+    };
+    const int64_t g = blockIdx.x;
+    if (batch <= 64) {
+        // items ranked by size: sequence b's first rank is the items of every sequence with
+        // larger items, or equal ones and a lower index
+        const bool live = lane < batch;
+        const int32_t ab = live ? seq_splits(u[0], share, rcp, cap) : 0;
+        const int32_t key = live ? (u[0] + ab - 1) / ab : -1;
+        const int32_t cnt = ab * rps;
+        // (every lane reads every entry: broadcast LDS reads; a wave's LDS accesses complete in
+        // issue order)
+        lds[lane] = key;
+        lds[64 + lane] = cnt;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // four entries per read, all reads unrolled so that they overlap (entries past the
+        // batch hold key -1 and count 0 and add nothing)
+        int32_t start = 0;
+        const int4* lk = reinterpret_cast<const int4*>(lds);
+        const int4* lc = reinterpret_cast<const int4*>(lds + 64);
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int4 k4 = lk[q], c4 = lc[q];
+            const int32_t kq[4] = {k4.x, k4.y, k4.z, k4.w}, cq[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                // (bitwise, so that the compiler emits selects, not a branch per entry)
+                const bool ahead = (kq[e] > key) | ((kq[e] == key) & (4 * q + e < lane));
+                start += ahead ? cq[e] : 0;
+            }
+        }
+        // this workgroup's rank: its position, reversed inside every odd whole round of kCus
+        const int64_t round = g / kCus;
+        const int64_t rank = (round & 1) && (round + 1) * kCus <= (int64_t)gridDim.x ? round * kCus + (kCus - 1) - (g - round * kCus) : g;
+        const uint64_t hit = __ballot(live && start <= rank && rank < start + cnt);
+        if (hit == 0) return {0, -1, {0, 0, 0, 0, 0, 0}};   // past the last item
+        const int k = __builtin_ctzll(hit);
+        const int32_t a_k = __builtin_amdgcn_readlane(ab, k), u_k = __builtin_amdgcn_readlane(u[0], k);
+        return item(k, a_k, u_k, (int32_t)rank - __builtin_amdgcn_readlane(start, k), lane_state(k));
+    }
+    // more sequences: items in sequence order; global split index gs, row r of the sequence
+    const int64_t gs = (uint32_t)g / (uint32_t)rps;
+    const int32_t r = (int32_t)(g - gs * rps);
+    int64_t before = 0;   // splits of the sequences before this 64-sequence chunk
+    for (int64_t b0 = 0; b0 < batch; b0 += 64) {
+        const int64_t b = b0 + lane;
+        const int64_t j = b0 / 64;
+        int32_t ub = 0;
+#pragma unroll
+        for (int t = 0; t < kPlanRegs; ++t)
+            if (t == j) ub = u[t];
+        if (j >= kPlanRegs && b < batch) ub = seq_units(a, b);
+        const int32_t ab = b < batch ? seq_splits(ub, share, rcp, cap) : 0;
+        const int32_t incl = wave_prefix(ab);  // inclusive prefix of a_b over the chunk
+        // sequences of the chunk that end at or before split gs
+        const uint64_t done = __ballot(b < batch && before + incl <= gs);
+        const int k = __popcll(done);
+        const int64_t last = min((int64_t)64, batch - b0);
+        if (k < last) {
+            // (wave-uniform; kept in scalar registers through the kernel)
+            const int32_t a_k = __builtin_amdgcn_readlane(ab, k);
+            const int32_t u_k = __builtin_amdgcn_readlane(ub, k);
+            const int32_t incl_k = __builtin_amdgcn_readlane(incl, k);
+            const int64_t seq = b0 + k;
+            const int32_t local = (int32_t)(gs - (before + incl_k - a_k)) * rps + r;
+            return item(seq, a_k, u_k, local, j == 0 ? lane_state(k) : *reinterpret_cast<const int4*>(a.seq_state + 4 * seq));
+        }
+        before += __builtin_amdgcn_readlane(incl, 63);
+    }
+    return {0, -1, {0, 0, 0, 0, 0, 0}};   // past the last item
+}
+
+// The workgroup's item: wave 0 plans (the plan is the same in every wave, and every wave's
+// vector instructions share the CU's SIMDs with the other workgroups' waves) and leaves the
+// item in LDS for the others.  lds: 128 words that nothing else uses until the plan is done;
+// the second barrier keeps every wave's reads ahead of any later write to them.
+__device__ __forceinline__ WorkItem ragged_item(const AttnArgs& a, int32_t* lds) {
+    if (threadIdx.x < 64) {
+        const WorkItem wi = ragged_plan(a, lds);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (threadIdx.x == 0) {
+            lds[0] = (int32_t)(uint32_t)(uint64_t)wi.row;
+            lds[1] = (int32_t)(uint32_t)((uint64_t)wi.row >> 32);
+            lds[2] = wi.split;
+            lds[3] = wi.rs.n_quant;
+            lds[4] = wi.rs.n_res;
+            lds[5] = wi.rs.res_head;
+            lds[6] = wi.rs.groups_per_split;
+            lds[7] = wi.rs.res_split;
+            lds[8] = wi.rs.splits;
+        }
+    }
+    __syncthreads();
+    int32_t v[9];
+#pragma unroll
+    for (int i = 0; i < 9; ++i) v[i] = __builtin_amdgcn_readfirstlane(lds[i]);
+    __syncthreads();
+    return {(int64_t)(((uint64_t)(uint32_t)v[1] << 32) | (uint32_t)v[0]), v[2], {v[3], v[4], v[5], v[6], v[7], v[8]}};
+}
+
+// The work of this workgroup: uniform batch, row y and split x of the grid (the state is the
+// call's, row_state); ragged batch, the plan's item (lds: as ragged_item's).
+template <bool RAGGED>
+__device__ __forceinline__ WorkItem work_item(const AttnArgs& a, int32_t* lds) {
+    if constexpr (RAGGED) return ragged_item(a, lds);
+    else return {(int64_t)blockIdx.y, (int)blockIdx.x, {0, 0, 0, 0, 0, 0}};
 }
 
 // Softmax states of query rows qrow0..qrow0+NQ-1 over the fp16 residual ring.  Called by one
@@ -242,13 +464,27 @@ __device__ void residual_states(const AttnArgs& a, const RowState& rs, int64_t q
         lr[r] = 0.0f;
         o[r][0] = o[r][1] = 0.0f;
     }
+    if (wave * kG >= rs.n_res) return;
     auto token_slot = [&](int i) { return (rs.res_head + i) % a.residual_cap; };
     auto is_new = [&](int i) { return a.k_new != nullptr && i == rs.n_res - 1; };
+    // Memory round trips are what this phase waits on, so each chunk has one: the queries'
+    // channels [32qq, 32qq+32) are loaded once, first, then each chunk issues its key loads and
+    // all 32 value rows together (a wave's loads complete in issue order, so the logits wait
+    // for the keys while the values are still arriving).
+    uint4 qx[NQ][4];
+#pragma unroll
+    for (int r = 0; r < NQ; ++r) {
+        const uint4* qp = reinterpret_cast<const uint4*>(a.q + (qrow0 + r) * kD + qq * 32);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qx[r][i] = qp[i];
+    }
     for (int base = wave * kG; base < rs.n_res; base += WAVES * kG) {
-        // ---- logits of tokens 2tp, 2tp+1 for every row
+        const int nt = min(kG, rs.n_res - base);
+        // ---- keys of tokens 2tp, 2tp+1 (channel quarter qq) and the lane's two channels 2l,
+        // 2l+1 of all the chunk's value rows (past the end: the last row again)
         const int i0 = base + 2 * tp, i1 = i0 + 1;
         const bool ok0 = i0 < rs.n_res, ok1 = i1 < rs.n_res;
-        const int j0 = ok0 ? i0 : 0, j1 = ok1 ? i1 : 0;
+        const int j0 = ok0 ? i0 : base, j1 = ok1 ? i1 : base;
         const int64_t rn = kvrow * kD + qq * 32;
         const uint4* k0 = reinterpret_cast<const uint4*>(
             is_new(j0) ? a.k_new + rn : a.k_res + (kvrow * a.residual_cap + token_slot(j0)) * kD + qq * 32);
@@ -260,16 +496,22 @@ __device__ void residual_states(const AttnArgs& a, const RowState& rs, int64_t q
             kx0[i] = k0[i];
             kx1[i] = k1[i];
         }
+        uint32_t vv[kG];
+#pragma unroll
+        for (int u = 0; u < kG; ++u) {
+            const int i = base + min(u, nt - 1);
+            const uint16_t* row = is_new(i) ? a.v_new + kvrow * kD : a.v_res + (kvrow * a.residual_cap + token_slot(i)) * kD;
+            vv[u] = reinterpret_cast<const uint32_t*>(row)[lane];
+        }
+        // ---- logits of tokens 2tp, 2tp+1 for every row
         float al[NQ];
 #pragma unroll
         for (int r = 0; r < NQ; ++r) {
             // q.k on packed halves: each fp16 product is exact in fp32, summed in fp32
-            const uint4* qp = reinterpret_cast<const uint4*>(a.q + (qrow0 + r) * kD + qq * 32);
             float d0 = 0.0f, d1 = 0.0f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const uint4 qx = qp[i];
-                const uint32_t qh[4] = {qx.x, qx.y, qx.z, qx.w};
+                const uint32_t qh[4] = {qx[r][i].x, qx[r][i].y, qx[r][i].z, qx[r][i].w};
                 const uint32_t w0[4] = {kx0[i].x, kx0[i].y, kx0[i].z, kx0[i].w};
                 const uint32_t w1[4] = {kx1[i].x, kx1[i].y, kx1[i].z, kx1[i].w};
 #pragma unroll
@@ -295,31 +537,26 @@ __device__ void residual_states(const AttnArgs& a, const RowState& rs, int64_t q
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // ---- P.V: lane l takes channels 2l, 2l+1 of the chunk's 32 token rows
+        // ---- P.V: lane l takes channels 2l, 2l+1 of the chunk's token rows
 #pragma unroll
         for (int r = 0; r < NQ; ++r) {
             o[r][0] *= al[r];
             o[r][1] *= al[r];
         }
-        const int nt = min(kG, rs.n_res - base);
-        for (int t0 = 0; t0 < nt; t0 += 8) {
-            uint32_t vv[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int i = base + min(t0 + u, nt - 1);
-                const uint16_t* row = is_new(i) ? a.v_new + kvrow * kD : a.v_res + (kvrow * a.residual_cap + token_slot(i)) * kD;
-                vv[u] = reinterpret_cast<const uint32_t*>(row)[lane];
-            }
+        for (int t0 = 0; t0 < kG; t0 += 8) {
+            if (t0 < nt) {
 #pragma unroll
-            for (int r = 0; r < NQ; ++r) {
-                const float4 pa = *reinterpret_cast<const float4*>(o_dst + r * o_stride + t0);
-                const float4 pb = *reinterpret_cast<const float4*>(o_dst + r * o_stride + t0 + 4);
-                const float pt[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+                for (int r = 0; r < NQ; ++r) {
+                    const float4 pa = *reinterpret_cast<const float4*>(o_dst + r * o_stride + t0);
+                    const float4 pb = *reinterpret_cast<const float4*>(o_dst + r * o_stride + t0 + 4);
+                    const float pt[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const float pu = t0 + u < nt ? pt[u] : 0.0f;
-                    o[r][0] = fmaf(pu, h2f(vv[u] & 0xffffu), o[r][0]);
-                    o[r][1] = fmaf(pu, h2f(vv[u] >> 16), o[r][1]);
+                    for (int u = 0; u < 8; ++u) {
+                        const float pu = t0 + u < nt ? pt[u] : 0.0f;
+                        o[r][0] = fmaf(pu, h2f(vv[t0 + u] & 0xffffu), o[r][0]);
+                        o[r][1] = fmaf(pu, h2f(vv[t0 + u] >> 16), o[r][1]);
+                    }
                 }
             }
         }
@@ -327,12 +564,10 @@ __device__ void residual_states(const AttnArgs& a, const RowState& rs, int64_t q
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
-    if (wave * kG < rs.n_res) {
 #pragma unroll
-        for (int r = 0; r < NQ; ++r) {
-            o_dst[r * o_stride + 2 * lane] = o[r][0];
-            o_dst[r * o_stride + 2 * lane + 1] = o[r][1];
-        }
+    for (int r = 0; r < NQ; ++r) {
+        o_dst[r * o_stride + 2 * lane] = o[r][0];
+        o_dst[r * o_stride + 2 * lane + 1] = o[r][1];
     }
 }
 

@@ -38,7 +38,7 @@ struct GqaLds {
 constexpr int kGqaWaves = 4;
 constexpr int kGqaBlock = 64 * kGqaWaves;
 
-template <int NQ, int GS>
+template <int NQ, int GS, bool RAGGED>
 __global__ __launch_bounds__(kGqaBlock) __attribute__((amdgpu_waves_per_eu(3))) void attn_gqa_kernel(AttnArgs a) {
     using Lds = GqaLds<NQ>;
     constexpr int W = kGqaWaves, S = 2 * kGqaWaves;
@@ -47,8 +47,11 @@ __global__ __launch_bounds__(kGqaBlock) __attribute__((amdgpu_waves_per_eu(3))) 
     __shared__ __align__(16) float sh_o[NQ][S][kD];
     __shared__ float sh_m[NQ][S], sh_l[NQ][S];
 
-    const int split = grid_split(a);
-    const int64_t grow = grid_row(a);                 // (batch, kv head, query chunk)
+    // (ragged batch: the plan uses sh_o, unused until the end)
+    const WorkItem wi = work_item<RAGGED>(a, reinterpret_cast<int32_t*>(&sh_o[0][0][0]));
+    if (RAGGED && wi.split < 0) return;   // (ragged batch) past the plan's last item
+    const int split = wi.split;
+    const int64_t grow = wi.row;                      // (batch, kv head, query chunk)
     const int chunks = a.ratio / NQ;
     // grow = kvrow*chunks + chunk and Hq = Hkv*ratio = Hkv*chunks*NQ, so the first query row is
     // kvrow*ratio + chunk*NQ = grow*NQ: one 32-bit division (none when a kv head's query group
@@ -119,8 +122,7 @@ __global__ __launch_bounds__(kGqaBlock) __attribute__((amdgpu_waves_per_eu(3))) 
     float lsum = 0.0f, m = -INFINITY;          // query qh's running sum and max
     float vs = 0.0f;                    // power-of-two factor keeping the value weights in fp16 range
 
-    const RowState rs = row_state(a, kvrow, split);
-    if (split >= rs.splits) return;   // (ragged batch) this row uses fewer splits: the whole workgroup leaves
+    const RowState rs = RAGGED ? wi.rs : row_state(a);
     const int n_groups = rs.n_quant / kG;
     const int g_lo = split * rs.groups_per_split;
     const int g_hi = min(n_groups, g_lo + rs.groups_per_split);
@@ -417,18 +419,20 @@ __global__ __launch_bounds__(kGqaBlock) __attribute__((amdgpu_waves_per_eu(3))) 
 
 hipError_t launch_decode_attn_gqa(const AttnArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
     const dim3 grid = attn_grid(a, a.block_rows);
+#define KIVI_GQA_NQ(NQv)                                                                                          \
+    if (a.seq_state != nullptr)                                                                                   \
+        KIVI_BY_GROUP(a.group, hipExtLaunchKernelGGL((attn_gqa_kernel<NQv, GS, true>), grid, dim3(kGqaBlock), 0, s, \
+                                                     t0, t1, 0, a))                                               \
+    else                                                                                                          \
+        KIVI_BY_GROUP(a.group, hipExtLaunchKernelGGL((attn_gqa_kernel<NQv, GS, false>), grid, dim3(kGqaBlock), 0, s, \
+                                                     t0, t1, 0, a))
     switch (a.nq) {
-        case 2:
-            KIVI_BY_GROUP(a.group, hipExtLaunchKernelGGL(attn_gqa_kernel<2, GS>, grid, dim3(kGqaBlock), 0, s, t0, t1, 0, a))
-            break;
-        case 3:
-            KIVI_BY_GROUP(a.group, hipExtLaunchKernelGGL(attn_gqa_kernel<3, GS>, grid, dim3(kGqaBlock), 0, s, t0, t1, 0, a))
-            break;
-        case 4:
-            KIVI_BY_GROUP(a.group, hipExtLaunchKernelGGL(attn_gqa_kernel<4, GS>, grid, dim3(kGqaBlock), 0, s, t0, t1, 0, a))
-            break;
+        case 2: KIVI_GQA_NQ(2) break;
+        case 3: KIVI_GQA_NQ(3) break;
+        case 4: KIVI_GQA_NQ(4) break;
         default: return hipErrorInvalidValue;
     }
+#undef KIVI_GQA_NQ
     return hipGetLastError();
 }
 

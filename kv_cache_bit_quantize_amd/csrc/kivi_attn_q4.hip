@@ -33,7 +33,7 @@ namespace kivi {
 
 constexpr int kQ4Tok = 16;   // tokens per wave-iteration
 
-template <int NQ, int GS>
+template <int NQ, int GS, bool RAGGED>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) void attn_q4_kernel(AttnArgs a) {
     constexpr int kIt = GS / kQ4Tok;   // iterations per key group
     __shared__ __align__(16) float sh_p[kWaves][NQ][kQ4Tok];
@@ -45,8 +45,11 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     __shared__ __align__(16) float sh_o[NQ][kSlots][kD];
     __shared__ float sh_m[NQ][kSlots], sh_l[NQ][kSlots];
 
-    const int split = grid_split(a);
-    const int64_t grow = grid_row(a);                 // (batch, kv head, query chunk)
+    // (ragged batch: the plan uses sh_o, unused until the end)
+    const WorkItem wi = work_item<RAGGED>(a, reinterpret_cast<int32_t*>(&sh_o[0][0][0]));
+    if (RAGGED && wi.split < 0) return;   // (ragged batch) past the plan's last item
+    const int split = wi.split;
+    const int64_t grow = wi.row;                      // (batch, kv head, query chunk)
     const int chunks = a.ratio / NQ;
     // grow = kvrow*chunks + chunk and Hq = Hkv*ratio = Hkv*chunks*NQ, so the first query row is
     // kvrow*ratio + chunk*NQ = grow*NQ: one 32-bit division (none when a kv head's query group
@@ -61,8 +64,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     const int mrow = lane & 15, kb = lane >> 4;   // matrix roles: token / A row, K block
     const int vg = lane >> 4, vc = lane & 15;
 
-    const RowState rs = row_state(a, kvrow, split);
-    if (split >= rs.splits) return;   // (ragged batch) this row uses fewer splits
+    const RowState rs = RAGGED ? wi.rs : row_state(a);
     // whole key groups: this split's share, then this wave's
     const int n_kg = rs.n_quant / GS;
     const int per_split = (n_kg + rs.splits - 1) / rs.splits;
@@ -302,7 +304,12 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
 hipError_t launch_decode_attn_q4(const AttnArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
     const dim3 grid = attn_grid(a, a.block_rows);
 #define KIVI_Q4_NQ(NQv)                                                                                         \
-    KIVI_BY_GROUP(a.group, hipExtLaunchKernelGGL((attn_q4_kernel<NQv, GS>), grid, dim3(kBlock), 0, s, t0, t1, 0, a))
+    if (a.seq_state != nullptr)                                                                                 \
+        KIVI_BY_GROUP(a.group, hipExtLaunchKernelGGL((attn_q4_kernel<NQv, GS, true>), grid, dim3(kBlock), 0, s, t0, \
+                                                     t1, 0, a))                                                 \
+    else                                                                                                        \
+        KIVI_BY_GROUP(a.group, hipExtLaunchKernelGGL((attn_q4_kernel<NQv, GS, false>), grid, dim3(kBlock), 0, s, t0, \
+                                                     t1, 0, a))
     switch (a.nq) {   // the host takes at most two query heads per workgroup for 4-bit caches
         case 1: KIVI_Q4_NQ(1) break;
         case 2: KIVI_Q4_NQ(2) break;

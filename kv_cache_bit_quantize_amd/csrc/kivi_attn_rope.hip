@@ -110,7 +110,7 @@ __device__ void residual_rope_states(const AttnArgs& a, const RowState& rs, int6
     o_dst[lane + kRpPairs] = o1;
 }
 
-template <int BITS, int GS>
+template <int BITS, int GS, bool RAGGED>
 __global__ __launch_bounds__(kBlock) void attn_rope_kernel(AttnArgs a) {
     constexpr int kIt = GS / kRpTok;   // iterations per key group
     __shared__ double sh_w[kRpPairs];                        // pair frequencies
@@ -121,8 +121,11 @@ __global__ __launch_bounds__(kBlock) void attn_rope_kernel(AttnArgs a) {
     __shared__ __align__(16) float sh_o[1][kSlots][kD];
     __shared__ float sh_m[1][kSlots], sh_l[1][kSlots];
 
-    const int split = grid_split(a);
-    const int64_t qrow = grid_row(a);
+    // (ragged batch: the plan uses sh_o, unused until the end)
+    const WorkItem wi = work_item<RAGGED>(a, reinterpret_cast<int32_t*>(&sh_o[0][0][0]));
+    if (RAGGED && wi.split < 0) return;   // (ragged batch) past the plan's last item
+    const int split = wi.split;
+    const int64_t qrow = wi.row;
     // query row b*Hq + h reads kv row b*Hkv + h/ratio = qrow/ratio (Hq = Hkv*ratio)
     const int64_t kvrow = a.ratio == 1 ? qrow : (int64_t)((uint32_t)qrow / (uint32_t)a.ratio);
     if (a.k_new != nullptr && split == 0 && (uint32_t)qrow % (uint32_t)a.ratio == 0) store_new_token(a, kvrow);
@@ -131,8 +134,7 @@ __global__ __launch_bounds__(kBlock) void attn_rope_kernel(AttnArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int t8 = lane >> 3, k8 = lane & 7;
 
-    const RowState rs = row_state(a, kvrow, split);
-    if (split >= rs.splits) return;   // (ragged batch) this row uses fewer splits: the whole workgroup leaves
+    const RowState rs = RAGGED ? wi.rs : row_state(a);
     const int n_kg = rs.n_quant / GS;
     const int per_split = (n_kg + rs.splits - 1) / rs.splits;
     const int kg_lo = min(n_kg, split * per_split), kg_hi = min(n_kg, kg_lo + per_split);
@@ -435,11 +437,16 @@ __global__ __launch_bounds__(kBlock) void attn_rope_kernel(AttnArgs a) {
 
 hipError_t launch_decode_attn_rope(const AttnArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
     const dim3 grid = attn_grid(a, a.q_rows);
+#define KIVI_ROPE(BITSv, RAGGEDv)                                                                                  \
+    KIVI_BY_GROUP(a.group, hipExtLaunchKernelGGL((attn_rope_kernel<BITSv, GS, RAGGEDv>), grid, dim3(kBlock), 0, s, t0, t1, \
+                                                 0, a))
+    const bool ragged = a.seq_state != nullptr;
     if (a.bits == 4) {
-        KIVI_BY_GROUP(a.group, hipExtLaunchKernelGGL((attn_rope_kernel<4, GS>), grid, dim3(kBlock), 0, s, t0, t1, 0, a))
+        if (ragged) KIVI_ROPE(4, true) else KIVI_ROPE(4, false)
     } else {
-        KIVI_BY_GROUP(a.group, hipExtLaunchKernelGGL((attn_rope_kernel<2, GS>), grid, dim3(kBlock), 0, s, t0, t1, 0, a))
+        if (ragged) KIVI_ROPE(2, true) else KIVI_ROPE(2, false)
     }
+#undef KIVI_ROPE
     return hipGetLastError();
 }
 

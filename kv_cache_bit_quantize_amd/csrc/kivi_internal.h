@@ -7,6 +7,7 @@
 namespace kivi {
 
 constexpr int kMaxSplits = 1024;   // upper bound on split-K partitions of one decode call
+constexpr int kCus = 256;          // compute units of the device (8 XCDs of 32)
 constexpr int kSqWaves = 12;       // waves of a single-query attention workgroup (one per CU)
 constexpr int kSqWavesMany = 4;    // ... for a uniform batch with more query rows than CUs (three per CU)
 
