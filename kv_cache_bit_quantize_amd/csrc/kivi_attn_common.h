@@ -128,7 +128,11 @@ __device__ __forceinline__ uint32_t settle_tag(TagLoads<NQ> t) {
         asm volatile("" : "+v"(v));
         m = max(m, v);
     }
-    return __builtin_amdgcn_readfirstlane(m) + 1u;
+    // (pinned to a scalar register here: otherwise the compiler may move the read down to the
+    // tag's first use, after the loop, and hold the epochs in a vector register until then)
+    uint32_t tag = __builtin_amdgcn_readfirstlane(m) + 1u;
+    asm volatile("" : "+s"(tag));
+    return tag;
 }
 // Polls of a partial value whose store has not landed yet (each after a short sleep).  The
 // value was stored before its workgroup's arrival was counted, so it lands within a memory

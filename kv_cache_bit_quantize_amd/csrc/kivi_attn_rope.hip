@@ -111,13 +111,17 @@ __device__ void residual_rope_states(const AttnArgs& a, const RowState& rs, int6
 }
 
 template <int BITS, int GS, bool RAGGED>
-__global__ __launch_bounds__(kBlock) void attn_rope_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) void attn_rope_kernel(AttnArgs a) {
     constexpr int kIt = GS / kRpTok;   // iterations per key group
     __shared__ double sh_w[kRpPairs];                        // pair frequencies
     __shared__ __align__(16) float2 sh_ed[GS][kRpPairs];     // exp(i*d*w) for offsets d < G
     __shared__ __align__(16) float2 sh_e0[kWaves][kRpPairs]; // exp(i*t0*w) of the wave's group
-    __shared__ __align__(16) float sh_p[kWaves][kRpTok];
-    __shared__ __align__(16) float sh_ps[kWaves][kD / GS][kRpTok];   // 2-bit: p*s per (value group, token)
+    __shared__ __align__(16) float sh_p[kWaves][kRpTok];                // 4-bit: the iteration's weights
+    // 2-bit values on the matrix cores: per wave the tile's 32 logits and its value weights
+    // [channel group][32 tokens] (fp16, the A operand's weight row), and zero rows
+    __shared__ __align__(16) float sh_lg[kWaves][kG];
+    __shared__ __align__(16) uint8_t sh_wt[kWaves][4 * 64];
+    __shared__ __align__(16) uint8_t sh_zr[4 * 64];
     __shared__ __align__(16) float sh_o[1][kSlots][kD];
     __shared__ float sh_m[1][kSlots], sh_l[1][kSlots];
 
@@ -144,19 +148,14 @@ __global__ __launch_bounds__(kBlock) void attn_rope_kernel(AttnArgs a) {
     const int n_groups = kg_lo + min(cnt, (wave + 1) * per_wave) - kgb;
     const int n_it = n_groups * kIt;
 
-    // the lane's query pairs: channels 8k8..8k8+7 and 64+8k8..64+8k8+7
-    float qlo[8], qhi[8];
+    // the lane's query pairs: channels 8k8..8k8+7 and 64+8k8..64+8k8+7, kept as packed fp16
+    // (converted once per key group)
+    uint32_t qlo2[4], qhi2[4];
     {
         const uint4 x = *reinterpret_cast<const uint4*>(a.q + qrow * kD + 8 * k8);
         const uint4 y = *reinterpret_cast<const uint4*>(a.q + qrow * kD + kRpPairs + 8 * k8);
-        const uint32_t xs[4] = {x.x, x.y, x.z, x.w}, ys[4] = {y.x, y.y, y.z, y.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            qlo[2 * i] = h2f(xs[i] & 0xffffu);
-            qlo[2 * i + 1] = h2f(xs[i] >> 16);
-            qhi[2 * i] = h2f(ys[i] & 0xffffu);
-            qhi[2 * i + 1] = h2f(ys[i] >> 16);
-        }
+        qlo2[0] = x.x; qlo2[1] = x.y; qlo2[2] = x.z; qlo2[3] = x.w;
+        qhi2[0] = y.x; qhi2[1] = y.y; qhi2[2] = y.z; qhi2[3] = y.w;
     }
 
     const int64_t tok0 = kvrow * (int64_t)a.token_cap;
@@ -186,32 +185,30 @@ __global__ __launch_bounds__(kBlock) void attn_rope_kernel(AttnArgs a) {
             }
         }
     };
-    // P.V lanes.  2-bit: lane (kk, n, hh) reads bytes 8hh..8hh+7 of chunk (16k + n) of the
-    // tile, k = 2*(t0%32/16) + kk: tokens 8kk + 4h + i of the iteration (h = 0..1, i = 0..3)
-    // and channels n + 16(4hh + m) (m = 0..3, in word m/2, byte 2h + m%2, bits 2i); with
-    // G = 32 channels m = 0, 1 are in value group 2hh and m = 2, 3 in group 2hh + 1.  Each
-    // (token, value group) of the iteration has one lane of the softmax octets that loads its
-    // (scale, zero) word and forms p*s (into LDS) and p*z (summed in that lane): octet t8,
-    // lane k8 < 2*NG takes token t8 + 8*(k8 / NG) and group k8 % NG (NG = 128/G groups).
+    // P.V lanes.  2-bit: per 32-token tile (every second iteration), on the matrix cores as
+    // in the 2-bit kernels: lane l holds chunk l of the tile's value codes (the B operands of
+    // all eight 16-channel blocks) and, for l < 32, token l's (scale, zero) pairs.
     // 4-bit: lane (vg, vc) reads tokens 4vg..4vg+3 and channels 8vc..8vc+7 (one group).
-    constexpr int kNG = kD / GS;                          // value groups per token
-    constexpr int kVGrp = (BITS == 2 && GS == 32) ? 2 : 1;  // value groups per lane and token
-    constexpr int kVCh = BITS == 2 ? 4 : 8;               // channels per lane
-    const int kk = lane >> 5, vn = (lane >> 1) & 15, hh = lane & 1;
+    constexpr int kVCh = BITS == 2 ? 1 : 8;               // channels per lane (4-bit)
     const int vg = lane >> 4, vc = lane & 15;
-    const bool combo = BITS == 2 && k8 < 2 * kNG;
-    const int c_tok = t8 + 8 * (min(k8, 2 * kNG - 1) / kNG), c_grp = min(k8, 2 * kNG - 1) % kNG;
     struct VLoad { uint32_t c[4]; uint32_t p[4]; };
     auto load_v = [&](VLoad& L, int it) {
-        const uint32_t t0 = (uint32_t)tok(it);
         if constexpr (BITS == 2) {
-            const uint32_t off = (t0 / kG) * kTileBytes + ((2 * ((t0 % kG) / 16) + kk) * 16 + vn) * 16 + 8 * hh;
-            const uint2 x = *reinterpret_cast<const uint2*>(vc_row + off);
+            // the tile of iteration it (past the end: the wave's last tile), so tokens
+            // t0 + (lane & 31) are in the wave's groups
+            const uint32_t t0 = (uint32_t)tok(it) & ~(uint32_t)(kG - 1);
+            const uint4 x = reinterpret_cast<const uint4*>(vc_row + (t0 / kG) * kTileBytes)[lane];
+            const uint4 y = load_value_pairs<GS>(vp_row + value_pair_index<GS>((int64_t)t0 + (lane & 31), 0));
             L.c[0] = x.x;
             L.c[1] = x.y;
-            L.p[0] = vp_row[(t0 + c_tok) * kNG + c_grp];   // this lane's (token, group) pair
+            L.c[2] = x.z;
+            L.c[3] = x.w;
+            L.p[0] = y.x;
+            L.p[1] = y.y;
+            L.p[2] = y.z;
+            L.p[3] = y.w;
         } else {
-            const uint32_t t = t0 + 4 * vg;
+            const uint32_t t = (uint32_t)tok(it) + 4 * vg;
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 L.c[u] = *reinterpret_cast<const uint32_t*>(vc_row + (t + u) * kRowBytes4 + 4 * vc);
@@ -234,17 +231,27 @@ __global__ __launch_bounds__(kBlock) void attn_rope_kernel(AttnArgs a) {
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     };
 
-    float m = -INFINITY, lsum = 0.0f, o[kVCh], oz = 0.0f;   // oz: 2-bit, the lane's (token, group) p*z; 4-bit, its tokens'
+    float m = -INFINITY, lsum = 0.0f, o[kVCh], oz = 0.0f;   // o, oz: 4-bit, the lane's channels and its tokens' p*z
 #pragma unroll
     for (int c = 0; c < kVCh; ++c) o[c] = 0.0f;
     float* pw = &sh_p[wave][0];
+    // 2-bit: accumulators of the eight 16-channel blocks, block v in row v%4 of cv[v/4] (its
+    // A operand has the weights in that row, zeros elsewhere); p*zero per 32-channel group;
+    // vs, a power of two keeping the fp16 weights in range.  Lane l < 32 takes token l of a
+    // tile for the weights, whose A-operand slots order tokens 8kg..8kg+7 as 0,4,1,5,2,6,3,7
+    // (the order the masked code fields produce them in); token 4a + i meets its code as the
+    // fp16 subnormal c * 4^i * 2^-24, so its weight carries 16 * 4^-i.
+    v4f cv[2] = {(v4f){0.0f, 0.0f, 0.0f, 0.0f}, (v4f){0.0f, 0.0f, 0.0f, 0.0f}};
+    float zk[4] = {0.0f, 0.0f, 0.0f, 0.0f}, vs = 0.0f;
+    uint8_t* wt = &sh_wt[wave][0];
+    if (BITS == 2 && threadIdx.x < 16) reinterpret_cast<uint4*>(sh_zr)[threadIdx.x] = make_uint4(0, 0, 0, 0);
 
     KLoad kl;
     VLoad vl;
     PLoad pn;
     if (n_groups > 0) {   // the first iteration's loads, in flight while the turn tables are built
         load_k(kl, 0);
-        load_v(vl, 0);
+        if constexpr (BITS != 2) load_v(vl, 0);
         load_kp(pn, 0);
     }
     // pair frequencies and the in-group turns exp(i*d*w)
@@ -269,8 +276,9 @@ __global__ __launch_bounds__(kBlock) void attn_rope_kernel(AttnArgs a) {
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const float2 e = sh_e0[wave][8 * k8 + j];
-                    const float wr = fmaf(qlo[j], e.x, qhi[j] * e.y);    // W = conj(Q) * e
-                    const float wi = fmaf(qlo[j], e.y, -qhi[j] * e.x);
+                    const float qlo = h2f(qlo2[j >> 1] >> (16 * (j & 1))), qhi = h2f(qhi2[j >> 1] >> (16 * (j & 1)));
+                    const float wr = fmaf(qlo, e.x, qhi * e.y);    // W = conj(Q) * e
+                    const float wi = fmaf(qlo, e.y, -qhi * e.x);
                     const float slo = h2f(plo[j] & 0xffffu), zlo = h2f(plo[j] >> 16);
                     const float shi = h2f(phi[j] & 0xffffu), zhi = h2f(phi[j] >> 16);
                     ur[j] = fmaf(wr, zlo, -wi * zhi);                    // U = W * (zlo + i*zhi)
@@ -283,9 +291,14 @@ __global__ __launch_bounds__(kBlock) void attn_rope_kernel(AttnArgs a) {
             }
             wave_sync();   // every lane has read the turns before the next group's are written
             load_kp(pn, gi + 1);
-#pragma unroll 1
+            // (unrolled by two: a tile's even and odd iterations have code of their own, so the
+            // tile's value loads, issued at the top of its odd iteration, are live for one)
+#pragma unroll 2
             for (int j = 0; j < kIt; ++j) {
                 const int it = gi * kIt + j;
+                if constexpr (BITS == 2) {
+                    if (j & 1) load_v(vl, it);
+                }
                 // ---- logits of tokens t8 and 8 + t8 (pass 0, 1), this lane's 8 pairs
                 float lg[2];
 #pragma unroll
@@ -316,51 +329,73 @@ __global__ __launch_bounds__(kBlock) void attn_rope_kernel(AttnArgs a) {
                 const float mnew = fmaxf(m, mx);
                 if (mnew != m) {
                     const float al = m == -INFINITY ? 0.0f : exp2f(m - mnew);
+                    if constexpr (BITS == 2) {
+                        cv[0] *= al;
+                        cv[1] *= al;
 #pragma unroll
-                    for (int c = 0; c < kVCh; ++c) o[c] *= al;
-                    oz *= al;
+                        for (int k = 0; k < 4; ++k) zk[k] *= al;
+                    } else {
+#pragma unroll
+                        for (int c = 0; c < kVCh; ++c) o[c] *= al;
+                        oz *= al;
+                    }
                     lsum *= al;
                     m = mnew;
                 }
-                const float p0 = exp2f(lg[0] - m), p1 = exp2f(lg[1] - m);
-                if (k8 == 0) {
-                    lsum += p0 + p1;
-                    pw[t8] = p0;
-                    pw[8 + t8] = p1;
-                }
                 if constexpr (BITS == 2) {
-                    if (combo) {
-                        const float pc = c_tok < 8 ? p0 : p1;
-                        sh_ps[wave][c_grp][c_tok] = pc * h2f(vl.p[0] & 0xffffu);
-                        oz = fmaf(pc, h2f(vl.p[0] >> 16), oz);
+                    // logits of the tile's tokens 16(j%2) + t8 and 16(j%2) + 8 + t8
+                    if (k8 == 0) {
+                        sh_lg[wave][16 * (j & 1) + t8] = lg[0];
+                        sh_lg[wave][16 * (j & 1) + 8 + t8] = lg[1];
+                    }
+                } else {
+                    const float p0 = exp2f(lg[0] - m), p1 = exp2f(lg[1] - m);
+                    if (k8 == 0) {
+                        lsum += p0 + p1;
+                        pw[t8] = p0;
+                        pw[8 + t8] = p1;
                     }
                 }
                 wave_sync();
                 // ---- P.V, dequantization folded: (p*s)*c + p*z
                 if constexpr (BITS == 2) {
-                    // p*s of the lane's 8 tokens in each of its value groups
-                    float ps[kVGrp][8];
+                    if (j & 1) {   // the tile's 32 logits are in: its weights, then 8 matrix instructions
+                        const int tt = lane & 31, mrow = lane & 15, kgrp = lane >> 4;
+                        const float p = lane < kG ? exp2f(sh_lg[wave][tt] - m) : 0.0f;   // token tt (lanes < 32)
+                        lsum += p;
 #pragma unroll
-                    for (int g = 0; g < kVGrp; ++g) {
-                        const int grp = GS == 32 ? 2 * hh + g : (GS == 64 ? hh : 0);
-                        const float4 a0 = *reinterpret_cast<const float4*>(&sh_ps[wave][grp][8 * kk]);
-                        const float4 a1 = *reinterpret_cast<const float4*>(&sh_ps[wave][grp][8 * kk + 4]);
-                        ps[g][0] = a0.x; ps[g][1] = a0.y; ps[g][2] = a0.z; ps[g][3] = a0.w;
-                        ps[g][4] = a1.x; ps[g][5] = a1.y; ps[g][6] = a1.z; ps[g][7] = a1.w;
-                    }
-#pragma unroll
-                    for (int w2 = 0; w2 < 2; ++w2) {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            // token field i of word w2: byte 2h + e = channel 2*w2 + e, token 4h + i
-                            uint32_t y = (vl.c[w2] >> (2 * i)) & 0x03030303u;
-                            asm volatile("" : "+v"(y));   // one v_cvt_f32_ubyteN per code
-#pragma unroll
-                            for (int b = 0; b < 4; ++b) {
-                                const int mm = 2 * w2 + (b & 1), u = 4 * (b >> 1) + i;
-                                const int g = kVGrp == 2 ? w2 : 0;
-                                o[mm] = fmaf(ps[g][u], (float)((y >> (8 * b)) & 0xFFu), o[mm]);
+                        for (int k = 0; k < 4; ++k) zk[k] = fmaf(p, h2f(vl.p[k] >> 16), zk[k]);
+                        // the largest scale, on the fp16 bit patterns (scales are never negative)
+                        const float smax = lane < kG ? h2f(max_u16x2(max_u16x2(vl.p[0], vl.p[1]), max_u16x2(vl.p[2], vl.p[3])) & 0xffffu) : 0.0f;
+                        // weights 16*p*s*vs must stay below 2^15: shrink vs (a power of two) if needed
+                        if (__builtin_amdgcn_ballot_w64(smax * vs > 2048.0f || vs == 0.0f)) {
+                            const float gm = wave_max_xor(smax, 1, 32);
+                            const float nvs = __builtin_ldexpf(1.0f, 11 - __builtin_amdgcn_frexp_expf(gm));
+                            if (vs != 0.0f && nvs < vs) {
+                                const float r = nvs / vs;
+                                cv[0] *= r;
+                                cv[1] *= r;
                             }
+                            if (vs == 0.0f || nvs < vs) vs = nvs;
+                        }
+                        if (lane < kG) {
+                            const int w_off = (tt >> 3) * 16 + (((tt & 3) << 1) | ((tt >> 2) & 1)) * 2;
+                            const float f = p * (__builtin_ldexpf(16.0f, -2 * (tt & 3)) * vs);
+#pragma unroll
+                            for (int k = 0; k < 4; ++k)
+                                *reinterpret_cast<_Float16*>(wt + w_off + k * 64) = (_Float16)(f * h2f(vl.p[k] & 0xffffu));
+                        }
+                        wave_sync();
+                        constexpr uint32_t kF0 = 0x00030003u, kF1 = 0x000C000Cu, kF2 = 0x00300030u, kF3 = 0x00C000C0u;
+#pragma unroll
+                        for (int v = 0; v < 8; ++v) {
+                            // word v/2 holds blocks v (even) and v+1 in alternate bytes; token field
+                            // i of each byte, masked in place, is the fp16 subnormal c * 4^i * 2^-24
+                            const uint32_t x = (v & 1) ? vl.c[v >> 1] >> 8 : vl.c[v >> 1];
+                            const v8h bop = __builtin_bit_cast(v8h, make_uint4(x & kF0, x & kF1, x & kF2, x & kF3));
+                            const uint8_t* arow = (mrow == (v & 3) ? wt : sh_zr) + (v >> 1) * 64 + 16 * kgrp;
+                            const v8h aop = *reinterpret_cast<const v8h*>(arow);
+                            cv[v >> 2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop, cv[v >> 2], 0, 0, 0);
                         }
                     }
                 } else {
@@ -379,8 +414,8 @@ __global__ __launch_bounds__(kBlock) void attn_rope_kernel(AttnArgs a) {
                             o[c] = fmaf(ps, code, o[c]);
                         }
                     }
+                    load_v(vl, it + 1);
                 }
-                load_v(vl, it + 1);
                 wave_sync();
             }
         }
@@ -390,25 +425,13 @@ __global__ __launch_bounds__(kBlock) void attn_rope_kernel(AttnArgs a) {
 
     // ---- the wave's state: p*z shares added to their channels, lanes of a channel summed
     if constexpr (BITS == 2) {
-        // sum of p*z per value group over the wave's tokens, then the lane's groups picked by
-        // compare-and-select (an index from hh would put the array in scratch memory)
-        float zl[kVGrp];
+        // o = P.V * 2^20 / vs + sum p*zero; block v's row sits in row v%4 of cv[v/4] (lanes 0..15)
 #pragma unroll
-        for (int g2 = 0; g2 < kVGrp; ++g2) zl[g2] = 0.0f;
+        for (int k = 0; k < 4; ++k) zk[k] = wave_sum(zk[k]);
+        const float inv = vs != 0.0f ? 1048576.0f / vs : 0.0f;
+        if (lane < 16) {
 #pragma unroll
-        for (int g = 0; g < kNG; ++g) {
-            const float t = wave_sum(combo && c_grp == g ? oz : 0.0f);
-#pragma unroll
-            for (int g2 = 0; g2 < kVGrp; ++g2) {
-                const int want = GS == 32 ? 2 * hh + g2 : (GS == 64 ? hh : 0);
-                zl[g2] = g == want ? t : zl[g2];
-            }
-        }
-#pragma unroll
-        for (int mm = 0; mm < 4; ++mm) {
-            float x = o[mm];
-            x += __shfl_xor(x, 32, 64);                  // the two 8-token rows (kk)
-            if (kk == 0) sh_o[0][wave][vn + 16 * (4 * hh + mm)] = x + zl[kVGrp == 2 ? (mm >> 1) : 0];
+            for (int v = 0; v < 8; ++v) sh_o[0][wave][16 * v + lane] = fmaf(cv[v >> 2][v & 3], inv, zk[v >> 1]);
         }
     } else {
 #pragma unroll
