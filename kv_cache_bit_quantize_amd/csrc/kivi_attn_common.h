@@ -157,6 +157,15 @@ __device__ __forceinline__ uint4 load_value_pairs(const uint32_t* p) {
     }
 }
 
+// Wave priority from the loop iterations a wave has left (s_setprio takes an immediate):
+// waves with more left issue first, in four steps that close in towards the end.
+__device__ __forceinline__ void set_priority_for(int left) {
+    if (left >= 6) __builtin_amdgcn_s_setprio(3);
+    else if (left >= 4) __builtin_amdgcn_s_setprio(2);
+    else if (left >= 2) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
+}
+
 // The cache state one workgroup attends over, with the number of splits its row uses, its
 // key groups per split and the split that also reads the residual.
 struct RowState {

@@ -367,7 +367,15 @@ __global__ __launch_bounds__(kGqaBlock) __attribute__((amdgpu_waves_per_eu(3))) 
     if (iters > 0) {
         load_all(set0, 0);
         tag = settle_tag(tag_v);
-        for (int it = 0; it < iters; ++it) iteration(set0, it);
+        // The SIMDs issue the oldest waves first, so of a CU's workgroups the first launched
+        // runs ahead and the last finishes alone, with too few waves to hide its loads.  Each
+        // wave instead takes a priority from the iterations it has left (most left, highest),
+        // so the waves sharing a SIMD draw level and finish together.
+        for (int it = 0; it < iters; ++it) {
+            set_priority_for(iters - it);
+            iteration(set0, it);
+        }
+        __builtin_amdgcn_s_setprio(0);
     } else {
         tag = settle_tag(tag_v);
     }
@@ -398,7 +406,9 @@ __global__ __launch_bounds__(kGqaBlock) __attribute__((amdgpu_waves_per_eu(3))) 
     __builtin_amdgcn_sched_barrier(0);
     float mr[NQ], lr[NQ];
     if (split == rs.res_split) {
+        __builtin_amdgcn_s_setprio(2);   // the residual is work the other splits do not have
         residual_states<NQ, W>(a, rs, qrow0, kvrow, wave, &sh_o[0][W + wave][0], S * kD, mr, lr);
+        __builtin_amdgcn_s_setprio(0);
     } else {
 #pragma unroll
         for (int r = 0; r < NQ; ++r) {

@@ -144,6 +144,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
         uint2 kpn = load_kp(0);
         tag = settle_tag(tag_v);
         for (int gi = 0; gi < n_groups; ++gi) {
+            set_priority_for(n_groups - gi);   // (as in the query-group kernel: most work left issues first)
             // this group's q*s (channels 2*lane, 2*lane+1; a product of two fp16 values, exact
             // in fp32) as 30-bit fixed point with one exponent per head (|q*s| * 2^sh < 2^29,
             // truncated: off by less than 2^-29 of the group's largest term), split into four
@@ -281,8 +282,11 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     }
     // ---- fp16 residual (split rs.res_split), as separate states
     float mr[NQ], lr[NQ];
+    __builtin_amdgcn_s_setprio(0);
     if (split == rs.res_split) {
+        __builtin_amdgcn_s_setprio(2);   // the residual is work the other splits do not have
         residual_states<NQ>(a, rs, qrow0, kvrow, wave, &sh_o[0][kWaves + wave][0], kSlots * kD, mr, lr);
+        __builtin_amdgcn_s_setprio(0);
     } else {
 #pragma unroll
         for (int r = 0; r < NQ; ++r) {

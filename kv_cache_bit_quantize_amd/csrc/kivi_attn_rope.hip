@@ -264,6 +264,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     if (n_groups > 0) {
         tag = settle_tag(tag_v);
         for (int gi = 0; gi < n_groups; ++gi) {
+            set_priority_for(n_groups - gi);   // (as in the query-group kernel: most work left issues first)
             // ---- turn of the group start for the 64 pairs (lane = pair), through LDS
             sh_e0[wave][lane] = turn((double)((kgb + gi) * GS) * sh_w[lane]);
             wave_sync();
@@ -449,7 +450,12 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     }
     // ---- fp16 residual (split rs.res_split), keys turned at n_quant + i
     float mr = -INFINITY, lr = 0.0f;
-    if (split == rs.res_split) residual_rope_states(a, rs, qrow, kvrow, wave, sh_w, &sh_o[0][kWaves + wave][0], mr, lr);
+    __builtin_amdgcn_s_setprio(0);
+    if (split == rs.res_split) {
+        __builtin_amdgcn_s_setprio(2);   // the residual is work the other splits do not have
+        residual_rope_states(a, rs, qrow, kvrow, wave, sh_w, &sh_o[0][kWaves + wave][0], mr, lr);
+        __builtin_amdgcn_s_setprio(0);
+    }
     if (lane == 0) {
         sh_m[0][kWaves + wave] = mr;
         sh_l[0][kWaves + wave] = lr;
