@@ -170,7 +170,9 @@ int kivi_append_flush(kivi_cache* cache, const uint16_t* k_new, const uint16_t* 
  * clear it again before using it for another shape.  Calls that share a workspace must not run
  * concurrently.  Status word: the kernels OR in KIVI_WS_POLL_TIMEOUT when a merge gave up
  * waiting for a split partial (the merge polls each value a bounded number of times); the
- * rows concerned get out = NaN and lse = NaN.  The library never clears the word.
+ * rows concerned get out = NaN and lse = NaN.  The library never clears the word.  The next
+ * word of the block holds the work share the last ragged call planned with, where the next
+ * ragged call starts its search (any value there is safe: the plan checks it).
  * KIVI_ERR_SHAPE if the context is empty. */
 #define KIVI_WS_POLL_TIMEOUT 1
 int kivi_decode_attn(const kivi_cache* cache, const uint16_t* q, int32_t q_heads,

@@ -275,6 +275,8 @@ __device__ __forceinline__ WorkItem ragged_plan(const AttnArgs& a, int32_t* lds)
     const int32_t batch = (int32_t)((uint32_t)a.q_rows / (uint32_t)a.q_heads);
     const int32_t rps = (int32_t)((uint32_t)a.block_rows / (uint32_t)batch);
     const int32_t cap = a.splits;
+    // the share of the last ragged call on this workspace: a starting point (checked below)
+    const int32_t hint = (int32_t)a.status[1];
     // the lane's own sequence's state stays in registers for the item's state below
     int4 st0 = make_int4(0, 0, 0, 0);
     if (lane < batch) st0 = *reinterpret_cast<const int4*>(a.seq_state + 4 * lane);
@@ -318,6 +320,16 @@ __device__ __forceinline__ WorkItem ragged_plan(const AttnArgs& a, int32_t* lds)
     const int64_t room = (int64_t)a.slot_budget - (int64_t)rps * batch;
     if (room > 0) hi = min(hi, max((int64_t)1, (total + room - 1) / room));
     int32_t lo = (int32_t)min(hi, max((int64_t)1, (total + a.slot_budget - 1) / a.slot_budget));
+    // in a decode loop the smallest share that fits seldom moves: test the last call's first
+    // (whatever the word holds, the bisection below still finds the smallest share that fits)
+    if (hint >= lo && hint <= hi) {
+        if (splits_at(hint) <= most) {
+            hi = hint;
+            if (hint > lo && splits_at(hint - 1) > most) lo = hint;
+        } else {
+            lo = hint + 1;
+        }
+    }
     while (lo < hi) {
         const int32_t mid = lo + (int32_t)(hi - lo) / 2;
         if (splits_at(mid) <= most) hi = mid;
@@ -325,6 +337,7 @@ __device__ __forceinline__ WorkItem ragged_plan(const AttnArgs& a, int32_t* lds)
     }
     const int32_t share = __builtin_amdgcn_readfirstlane(lo);
     const float rcp = __builtin_amdgcn_rcpf((float)share);
+    if (blockIdx.x == 0 && lane == 0) a.status[1] = (uint32_t)share;   // the next call's starting point
 
     // the item's sequence k (a lane of chunk 0, or of a later chunk), its split and row
     // (items are fewer than 2^31: 32-bit divisions)
