@@ -555,15 +555,17 @@ __device__ void residual_states(const AttnArgs& a, const RowState& rs, int64_t q
             const float p1 = ok1 ? exp2f(l1 - m_new) : 0.0f;
             lr[r] = lr[r] * al[r] + wave_sum(qq == 0 ? p0 + p1 : 0.0f);   // one share per token pair
             mr[r] = m_new;
-            if (qq == 0) {
-                o_dst[r * o_stride + 2 * tp] = p0;
-                o_dst[r * o_stride + 2 * tp + 1] = p1;
-            }
+            // the pair's weights as packed fp16, rounded to nearest (the quantized part's
+            // weights are fp16 too)
+            if (qq == 0)
+                reinterpret_cast<uint32_t*>(o_dst + r * o_stride)[tp] =
+                    __builtin_bit_cast(uint32_t, (h2v){(_Float16)p0, (_Float16)p1});
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // ---- P.V: lane l takes channels 2l, 2l+1 of the chunk's token rows
+        // ---- P.V: lane l takes channels 2l, 2l+1 of the chunk's token rows, two tokens per
+        // packed dot product (tokens past the end carry weight 0)
 #pragma unroll
         for (int r = 0; r < NQ; ++r) {
             o[r][0] *= al[r];
@@ -572,16 +574,21 @@ __device__ void residual_states(const AttnArgs& a, const RowState& rs, int64_t q
 #pragma unroll
         for (int t0 = 0; t0 < kG; t0 += 8) {
             if (t0 < nt) {
+                // channel 2l of tokens t, t+1 in one register, channel 2l+1 in another
+                uint32_t c0[4], c1[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    c0[u] = __builtin_amdgcn_perm(vv[t0 + 2 * u + 1], vv[t0 + 2 * u], 0x05040100u);
+                    c1[u] = __builtin_amdgcn_perm(vv[t0 + 2 * u + 1], vv[t0 + 2 * u], 0x07060302u);
+                }
 #pragma unroll
                 for (int r = 0; r < NQ; ++r) {
-                    const float4 pa = *reinterpret_cast<const float4*>(o_dst + r * o_stride + t0);
-                    const float4 pb = *reinterpret_cast<const float4*>(o_dst + r * o_stride + t0 + 4);
-                    const float pt[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+                    const uint4 pw = reinterpret_cast<const uint4*>(o_dst + r * o_stride)[t0 / 8];
+                    const uint32_t pp[4] = {pw.x, pw.y, pw.z, pw.w};
 #pragma unroll
-                    for (int u = 0; u < 8; ++u) {
-                        const float pu = t0 + u < nt ? pt[u] : 0.0f;
-                        o[r][0] = fmaf(pu, h2f(vv[t0 + u] & 0xffffu), o[r][0]);
-                        o[r][1] = fmaf(pu, h2f(vv[t0 + u] >> 16), o[r][1]);
+                    for (int u = 0; u < 4; ++u) {
+                        o[r][0] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2v, pp[u]), __builtin_bit_cast(h2v, c0[u]), o[r][0], false);
+                        o[r][1] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2v, pp[u]), __builtin_bit_cast(h2v, c1[u]), o[r][1], false);
                     }
                 }
             }
