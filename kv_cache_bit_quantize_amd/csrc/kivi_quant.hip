@@ -15,11 +15,58 @@
 
 namespace kivi {
 
+constexpr int kQSlots = kD + kD / 16;   // key-group threshold slots in LDS (quant_k_group)
+
+// 2-bit codes without a division.  The code of x is min(rint(fl(d / s)), 3) with d = fl(x - mn),
+// fl the binary32 rounding and rint ties-to-even, so it steps only where fl(d / s) crosses 0.5,
+// 1.5 and 2.5.  With round-to-nearest-even those crossings sit at fixed points of the exact
+// quotient: code >= 1 iff d/s > 0.5 + 2^-25 (the midpoint above 0.5, whose tie goes to 0.5),
+// code >= 2 iff d/s >= 1.5 - 2^-24 (the midpoint below 1.5, whose tie goes to 1.5), code >= 3
+// iff d/s > 2.5 + 2^-23.  For s > 0 each is a comparison of d with m*s, exact in binary64 (s
+// has 11 significant bits, m at most 25), and for a binary32 d, d > T iff d > RD(T) and
+// d >= T iff d >= RU(T) (RD, RU: the binary32 neighbours of T below and above).  So three
+// thresholds per group give every code of the group with three comparisons, for every finite
+// input (s = 0, a constant group, gives code 0).
+struct GroupT {
+    float mn, t1, t2, t3;
+    uint32_t pair;
+};
+__device__ __forceinline__ float f32_down(double x) {   // the largest binary32 <= x (x >= 0)
+    const float f = (float)x;
+    return (double)f > x ? __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, f) - 1u) : f;
+}
+__device__ __forceinline__ float f32_up(double x) {     // the smallest binary32 >= x (x >= 0)
+    const float f = (float)x;
+    return (double)f < x ? __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, f) + 1u) : f;
+}
+__device__ __forceinline__ GroupT group_thresholds(float mn, float mx) {
+    const GroupQ q = group_params(mn, mx);
+    GroupT g;
+    g.mn = q.mn;
+    g.pair = q.pair;
+    if (q.s == 0.0f) {
+        g.t1 = g.t2 = g.t3 = __builtin_inff();
+    } else {
+        const double s = (double)q.s;
+        g.t1 = f32_down(s * (0.5 + 0x1p-25));
+        g.t2 = f32_up(s * (1.5 - 0x1p-24));
+        g.t3 = f32_down(s * (2.5 + 0x1p-23));
+    }
+    return g;
+}
+__device__ __forceinline__ uint32_t code2_of(float x, float mn, float t1, float t2, float t3) {
+#pragma clang fp contract(off)
+    const float d = x - mn;
+    return (uint32_t)(d > t1) + (uint32_t)(d >= t2) + (uint32_t)(d > t3);
+}
+
 // One key token group of GS tokens held in LDS as fp16 [GS][128] -> its GS/32 code tiles +
 // 128 pairs.  Called by all 256 threads of the workgroup; ends with the codes and pairs
-// stored.
+// stored.  sh_q: LDS [kQSlots], each channel's minimum and code thresholds (group_thresholds),
+// channel j at j + j/16 (the 16-channel blocks one slot apart: the eight blocks a wave reads at
+// once then sit in different banks).
 template <int GS>
-__device__ void quant_k_group(const uint16_t* __restrict__ tile, float* sh_mn, float* sh_s,
+__device__ void quant_k_group(const uint16_t* __restrict__ tile, float4* sh_q,
                               uint8_t* __restrict__ codes_dst,      // the group's first code tile
                               uint32_t* __restrict__ pairs_dst) {   // 128 (scale, zero) words
     const int tid = threadIdx.x;
@@ -31,10 +78,9 @@ __device__ void quant_k_group(const uint16_t* __restrict__ tile, float* sh_mn, f
             mn = __builtin_fminf(mn, v);
             mx = __builtin_fmaxf(mx, v);
         }
-        GroupQ q = group_params(mn, mx);
-        pairs_dst[tid] = q.pair;
-        sh_mn[tid] = q.mn;
-        sh_s[tid] = q.s;
+        const GroupT g = group_thresholds(mn, mx);
+        pairs_dst[tid] = g.pair;
+        sh_q[tid + (tid >> 4)] = make_float4(g.mn, g.t1, g.t2, g.t3);
     }
     __syncthreads();
     // thread -> (token t, 16-channel word w) of each 32-token tile: 32 tokens x 8 words
@@ -48,9 +94,8 @@ __device__ void quant_k_group(const uint16_t* __restrict__ tile, float* sh_mn, f
 #pragma unroll
         for (int c = 0; c < 16; ++c) {
             uint32_t bits = (c & 1) ? (h[c >> 1] >> 16) : (h[c >> 1] & 0xffffu);
-            int j = w * 16 + c;
-            GroupQ q{sh_mn[j], sh_s[j], 0u};
-            word |= code_of(h2f(bits), q) << code_bit(c);
+            const float4 g = sh_q[w * 17 + c];
+            word |= code2_of(h2f(bits), g.x, g.y, g.z, g.w) << code_bit(c);
         }
         *reinterpret_cast<uint32_t*>(codes_dst + tl * kTileBytes + key_word_offset(t, w)) = word;
     }
@@ -95,13 +140,13 @@ __device__ void quant_v_tile(const uint16_t* __restrict__ src_lo, int64_t src_to
         mn = __builtin_fminf(mn, __shfl_xor(mn, m, 64));
         mx = __builtin_fmaxf(mx, __shfl_xor(mx, m, 64));
     }
-    const GroupQ q = group_params(mn, mx);
+    const GroupT q = group_thresholds(mn, mx);
     uint32_t packed[4];
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
         packed[w] = 0;
 #pragma unroll
-        for (int b = 0; b < 4; ++b) packed[w] |= code_of(v[4 * w + b], q) << (8 * b);
+        for (int b = 0; b < 4; ++b) packed[w] |= code2_of(v[4 * w + b], q.mn, q.t1, q.t2, q.t3) << (8 * b);
     }
     *reinterpret_cast<uint4*>(&sh_codes[t][cb * 16]) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
     if (live && cb % (GS / 16) == 0) pairs_dst[value_pair_index<GS>(t, cb / (GS / 16))] = q.pair;
@@ -226,7 +271,7 @@ __device__ void quant_v4_tokens(const uint16_t* __restrict__ src, int64_t src_to
 template <int GS>
 __global__ __launch_bounds__(kBlock) void quantize_k_kernel(QuantArgs a) {
     __shared__ uint4 tile4[GS * kD / 8];
-    __shared__ float sh_mn[kD], sh_s[kD];
+    __shared__ float4 sh_q[kQSlots];
     const int groups = a.tokens / GS;
     const int64_t row = blockIdx.x / groups;
     const int g = blockIdx.x % groups;
@@ -238,7 +283,7 @@ __global__ __launch_bounds__(kBlock) void quantize_k_kernel(QuantArgs a) {
     const int dst_tok = a.dst_token_off + g * GS;
     uint8_t* codes = a.k_codes + row * a.token_cap * kRowBytes + (int64_t)(dst_tok / kG) * kTileBytes;
     uint32_t* pairs = reinterpret_cast<uint32_t*>(a.k_sz) + (row * (a.token_cap / GS) + dst_tok / GS) * kD;
-    quant_k_group<GS>(reinterpret_cast<const uint16_t*>(tile4), sh_mn, sh_s, codes, pairs);
+    quant_k_group<GS>(reinterpret_cast<const uint16_t*>(tile4), sh_q, codes, pairs);
 }
 
 // grid.x = rows * (32-token tiles touched by [dst_token_off, dst_token_off + tokens)).
@@ -312,7 +357,9 @@ __global__ __launch_bounds__(kBlock) void residual_load_kernel(ResidualArgs a) {
 template <int GS, int BITS>
 __global__ __launch_bounds__(kBlock) void append_flush_kernel(AppendArgs a) {
     __shared__ uint4 tile4[GS * kD / 8];
-    __shared__ float sh_mn[kD], sh_s[kD];
+    __shared__ float4 sh_q[kQSlots];   // 2-bit keys: minimum and thresholds; 4-bit: minimum and scale arrays
+    float* sh_mn = reinterpret_cast<float*>(sh_q);
+    float* sh_s = sh_mn + kD;
     const int64_t row = blockIdx.x;
     const int part = blockIdx.y;   // which group of the flush this workgroup quantizes
     const int tid = threadIdx.x;
@@ -355,7 +402,7 @@ __global__ __launch_bounds__(kBlock) void append_flush_kernel(AppendArgs a) {
                                 reinterpret_cast<uint32_t*>(a.v_sz) + value_pair_index<GS>(row * a.token_cap + dst_tok, 0));
         } else {
             uint8_t* kc = a.k_codes + row * a.token_cap * kRowBytes + (int64_t)(dst_tok / kG) * kTileBytes;
-            quant_k_group<GS>(reinterpret_cast<const uint16_t*>(tile4), sh_mn, sh_s, kc, kp);
+            quant_k_group<GS>(reinterpret_cast<const uint16_t*>(tile4), sh_q, kc, kp);
             // values: the same GS ring tokens as GS/32 value tiles
             __shared__ __align__(16) uint8_t sh_codes[kG][kD];
 #pragma unroll 1
