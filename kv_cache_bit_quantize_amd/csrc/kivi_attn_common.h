@@ -470,9 +470,9 @@ __device__ __forceinline__ WorkItem work_item(const AttnArgs& a, int32_t* lds) {
 // whole wave of a WAVES-wave workgroup; wave w takes the ring's logical tokens
 // [32w + 32*WAVES*i, 32w + 32*WAVES*i + 32).  Per such
 // chunk, two phases:
-//  * logits: lane 4*tp + qq holds tokens 2tp, 2tp+1 and channels [32qq, 32qq+32) and forms
-//    q.k with v_dot2_f32_f16 on packed halves for every row; the chunk's probabilities go to
-//    LDS (o_dst, channels 0..31 of each row, as scratch);
+//  * logits: q.K^T on the matrix cores, 16 tokens per instruction (rows: the queries), the
+//    softmax over the lanes that hold the chunk's tokens; the chunk's weights go to LDS as
+//    fp16 (o_dst, the first 64 bytes of each row, as scratch);
 //  * P.V, channel-parallel: lane l accumulates channels 2l, 2l+1 of every row over the
 //    chunk's tokens (token rows loaded 256 bytes per instruction, probabilities read from LDS
 //    as broadcasts), so no cross-lane sums are needed.
@@ -482,7 +482,7 @@ __device__ __forceinline__ WorkItem work_item(const AttnArgs& a, int32_t* lds) {
 template <int NQ, int WAVES = kWaves>
 __device__ void residual_states(const AttnArgs& a, const RowState& rs, int64_t qrow0, int64_t kvrow, int wave,
                                 float* o_dst, int o_stride, float (&mr)[NQ], float (&lr)[NQ]) {
-    const int lane = threadIdx.x & 63, tp = lane >> 2, qq = lane & 3;
+    const int lane = threadIdx.x & 63, mrow = lane & 15, kq = lane >> 4;
     float o[NQ][2];
 #pragma unroll
     for (int r = 0; r < NQ; ++r) {
@@ -493,34 +493,31 @@ __device__ void residual_states(const AttnArgs& a, const RowState& rs, int64_t q
     if (wave * kG >= rs.n_res) return;
     auto token_slot = [&](int i) { return (rs.res_head + i) % a.residual_cap; };
     auto is_new = [&](int i) { return a.k_new != nullptr && i == rs.n_res - 1; };
-    // Memory round trips are what this phase waits on, so each chunk has one: the queries'
-    // channels [32qq, 32qq+32) are loaded once, first, then each chunk issues its key loads and
-    // all 32 value rows together (a wave's loads complete in issue order, so the logits wait
-    // for the keys while the values are still arriving).
-    uint4 qx[NQ][4];
+    // Memory round trips are what this phase waits on, so each chunk has one: the queries are
+    // loaded once, first, then each chunk issues its key loads and all 32 value rows together
+    // (a wave's loads complete in issue order, so the logits wait for the keys while the values
+    // are still arriving).
+    // Logits on the matrix cores (v_mfma_f32_16x16x32_f16, C = Q.K^T per 16-token tile): the A
+    // operand's row m is query m (rows past NQ zero), the lane holding its channels
+    // 32ks + 8kq .. +7 for each 32-channel step ks; the B operand's column n is the tile's token
+    // n, whose 16 bytes of channels the lane loads from its row.  Query r's logit of token n
+    // lands in lane n (< 16), accumulator entry r.
+    uint4 qa[4];
 #pragma unroll
-    for (int r = 0; r < NQ; ++r) {
-        const uint4* qp = reinterpret_cast<const uint4*>(a.q + (qrow0 + r) * kD + qq * 32);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) qx[r][i] = qp[i];
-    }
+    for (int ks = 0; ks < 4; ++ks)
+        qa[ks] = mrow < NQ ? *reinterpret_cast<const uint4*>(a.q + (qrow0 + mrow) * kD + 32 * ks + 8 * kq)
+                           : make_uint4(0, 0, 0, 0);
     for (int base = wave * kG; base < rs.n_res; base += WAVES * kG) {
         const int nt = min(kG, rs.n_res - base);
-        // ---- keys of tokens 2tp, 2tp+1 (channel quarter qq) and the lane's two channels 2l,
-        // 2l+1 of all the chunk's value rows (past the end: the last row again)
-        const int i0 = base + 2 * tp, i1 = i0 + 1;
-        const bool ok0 = i0 < rs.n_res, ok1 = i1 < rs.n_res;
-        const int j0 = ok0 ? i0 : base, j1 = ok1 ? i1 : base;
-        const int64_t rn = kvrow * kD + qq * 32;
-        const uint4* k0 = reinterpret_cast<const uint4*>(
-            is_new(j0) ? a.k_new + rn : a.k_res + (kvrow * a.residual_cap + token_slot(j0)) * kD + qq * 32);
-        const uint4* k1 = reinterpret_cast<const uint4*>(
-            is_new(j1) ? a.k_new + rn : a.k_res + (kvrow * a.residual_cap + token_slot(j1)) * kD + qq * 32);
-        uint4 kx0[4], kx1[4];
+        // ---- keys of tokens base + mrow and base + 16 + mrow, and the lane's two channels 2l,
+        // 2l+1 of all the chunk's value rows (past the end: the chunk's first row again)
+        uint4 kb[2][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            kx0[i] = k0[i];
-            kx1[i] = k1[i];
+        for (int tt = 0; tt < 2; ++tt) {
+            const int i = base + 16 * tt + mrow, j = i < rs.n_res ? i : base;
+            const uint16_t* kr = is_new(j) ? a.k_new + kvrow * kD : a.k_res + (kvrow * a.residual_cap + token_slot(j)) * kD;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) kb[tt][ks] = *reinterpret_cast<const uint4*>(kr + 32 * ks + 8 * kq);
         }
         uint32_t vv[kG];
 #pragma unroll
@@ -529,37 +526,35 @@ __device__ void residual_states(const AttnArgs& a, const RowState& rs, int64_t q
             const uint16_t* row = is_new(i) ? a.v_new + kvrow * kD : a.v_res + (kvrow * a.residual_cap + token_slot(i)) * kD;
             vv[u] = reinterpret_cast<const uint32_t*>(row)[lane];
         }
-        // ---- logits of tokens 2tp, 2tp+1 for every row
+        v4f acc[2];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            acc[tt] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, qa[ks]),
+                                                                 __builtin_bit_cast(v8h, kb[tt][ks]), acc[tt], 0, 0, 0);
+        }
+        // ---- softmax over the chunk's tokens for every row (lanes 0..15: tokens mrow and
+        // 16 + mrow; the reductions run over the lanes of the first 16-lane row)
+        const bool ok0 = lane < 16 && base + mrow < rs.n_res, ok1 = lane < 16 && base + 16 + mrow < rs.n_res;
+        _Float16* wts = reinterpret_cast<_Float16*>(o_dst);
         float al[NQ];
 #pragma unroll
         for (int r = 0; r < NQ; ++r) {
-            // q.k on packed halves: each fp16 product is exact in fp32, summed in fp32
-            float d0 = 0.0f, d1 = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t qh[4] = {qx[r][i].x, qx[r][i].y, qx[r][i].z, qx[r][i].w};
-                const uint32_t w0[4] = {kx0[i].x, kx0[i].y, kx0[i].z, kx0[i].w};
-                const uint32_t w1[4] = {kx1[i].x, kx1[i].y, kx1[i].z, kx1[i].w};
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    d0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2v, qh[k]), __builtin_bit_cast(h2v, w0[k]), d0, false);
-                    d1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2v, qh[k]), __builtin_bit_cast(h2v, w1[k]), d1, false);
-                }
-            }
-            d0 = quad_sum(d0) * a.sm_log2;   // over the 4 channel quarters
-            d1 = quad_sum(d1) * a.sm_log2;
-            const float l0 = ok0 ? d0 : -INFINITY, l1 = ok1 ? d1 : -INFINITY;
-            const float m_new = fmaxf(mr[r], wave_max_quads(fmaxf(l0, l1)));
+            const float l0 = ok0 ? acc[0][r] * a.sm_log2 : -INFINITY, l1 = ok1 ? acc[1][r] * a.sm_log2 : -INFINITY;
+            const float m_new = fmaxf(mr[r], readlane_f(row_max(fmaxf(l0, l1)), 0));
             al[r] = (mr[r] == -INFINITY) ? 0.0f : exp2f(mr[r] - m_new);
             const float p0 = ok0 ? exp2f(l0 - m_new) : 0.0f;
             const float p1 = ok1 ? exp2f(l1 - m_new) : 0.0f;
-            lr[r] = lr[r] * al[r] + wave_sum(qq == 0 ? p0 + p1 : 0.0f);   // one share per token pair
+            lr[r] = lr[r] * al[r] + readlane_f(row_sum(p0 + p1), 0);
             mr[r] = m_new;
-            // the pair's weights as packed fp16, rounded to nearest (the quantized part's
-            // weights are fp16 too)
-            if (qq == 0)
-                reinterpret_cast<uint32_t*>(o_dst + r * o_stride)[tp] =
-                    __builtin_bit_cast(uint32_t, (h2v){(_Float16)p0, (_Float16)p1});
+            // the weights as fp16, rounded to nearest (the quantized part's weights are fp16
+            // too), at [row][token] of the scratch
+            if (lane < 16) {
+                wts[r * 2 * o_stride + mrow] = (_Float16)p0;
+                wts[r * 2 * o_stride + 16 + mrow] = (_Float16)p1;
+            }
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
