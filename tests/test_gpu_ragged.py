@@ -139,3 +139,22 @@ def test_ragged_bad_state_and_capacity():
     assert np.array_equal(after[1:, :3], before[1:, :3])
     assert after[:, 3].tolist() == [0, kivi.KIVI_SEQ_BAD_STATE, kivi.KIVI_SEQ_BAD_STATE, kivi.KIVI_SEQ_CAPACITY]
     assert_cache_equal(_seq_view(cache, 3, after[3]), refs[3])   # untouched
+
+
+@pytest.mark.parametrize("batch,q_heads,kv_heads", [(130, 8, 2), (300, 1, 1)])
+def test_many_sequences(batch, q_heads, kv_heads):
+    """Batches past the plan's ranked placement (more than 64 sequences: items in sequence
+    order, found chunk by chunk) and past the sequences it keeps in registers (more than 256),
+    for query groups and for one query per kv head; short random contexts with empty ones."""
+    dev = gpu_or_skip()
+    kivi = _kivi()
+    rng = np.random.default_rng(batch)
+    lengths = [(32 * int(rng.integers(0, 9)), int(rng.integers(0, 129))) for _ in range(batch)]
+    lengths[3] = (0, 0)
+    lengths[-1] = (256, 128)
+    cache, state, refs, sw = _ragged(41, lengths, q_heads, kv_heads, 512, dev)
+    q = synth.query(sw, device=dev)
+    out, lse = kivi.kivi_decode_attn_ragged(cache, state, q, SM, lse=True)
+    torch.cuda.synchronize()
+    _check_attn(out, lse, q, refs, f"ragged batch {batch} {q_heads}/{kv_heads}")
+    assert torch.count_nonzero(state[:, 3]).item() == 0
