@@ -207,7 +207,7 @@ __global__ __launch_bounds__(64 * W) void attn_split_kernel(AttnArgs a) {
                 mx = fmaxf(mx, fabsf(qs[i]));
             }
             az = half_sum(az);
-            mx = half_max(mx);
+            mx = half_max_nonneg(mx);
             const int sh = min(29 - __builtin_amdgcn_frexp_expf(mx), 100);   // |q*s| * 2^sh < 2^29
             const float fs = __builtin_ldexpf(cls_div, sh);
             uint32_t dg[4];
@@ -257,10 +257,9 @@ __global__ __launch_bounds__(64 * W) void attn_split_kernel(AttnArgs a) {
 
             // ---- online softmax over the wave's 64 tokens (rescale only when the max rises)
             float mloc = half_max(lg);
-            mloc = fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mloc), 0)),
-                         __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mloc), 32)));
+            mloc = fmax_ieee(readlane_f(mloc, 0), readlane_f(mloc, 32));
             if (mloc > m) {
-                const float al = exp2f(m - mloc);
+                const float al = exp2_fast(m - mloc);
     #pragma unroll
                 for (int v = 0; v < 8; ++v) cv[v] *= al;
     #pragma unroll
@@ -268,7 +267,7 @@ __global__ __launch_bounds__(64 * W) void attn_split_kernel(AttnArgs a) {
                 lsum *= al;
                 m = mloc;
             }
-            const float p = exp2f(lg - m);       // this lane's token
+            const float p = exp2_fast(lg - m);   // this lane's token
             lsum += p;
             const uint32_t vpr[4] = {cur.vp.x, cur.vp.y, cur.vp.z, cur.vp.w};
     #pragma unroll

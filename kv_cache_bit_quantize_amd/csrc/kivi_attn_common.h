@@ -62,10 +62,10 @@ __device__ __forceinline__ float row_sum(float v) {
     return v + mirror_f(v);
 }
 __device__ __forceinline__ float row_max(float v) {
-    v = __builtin_fmaxf(v, xor1_f(v));
-    v = __builtin_fmaxf(v, xor2_f(v));
-    v = __builtin_fmaxf(v, hmirror_f(v));
-    return __builtin_fmaxf(v, mirror_f(v));
+    v = fmax_ieee(v, perm_f<0xB1>(v));
+    v = fmax_ieee(v, perm_f<0x4E>(v));
+    v = fmax_ieee(v, perm_f<0x141>(v));
+    return fmax_ieee(v, perm_f<0x140>(v));
 }
 
 __device__ __forceinline__ void load_q32(const uint16_t* q, float scale, float (&qv)[32]) {
@@ -543,10 +543,10 @@ __device__ void residual_states(const AttnArgs& a, const RowState& rs, int64_t q
 #pragma unroll
         for (int r = 0; r < NQ; ++r) {
             const float l0 = ok0 ? acc[0][r] * a.sm_log2 : -INFINITY, l1 = ok1 ? acc[1][r] * a.sm_log2 : -INFINITY;
-            const float m_new = fmaxf(mr[r], readlane_f(row_max(fmaxf(l0, l1)), 0));
-            al[r] = (mr[r] == -INFINITY) ? 0.0f : exp2f(mr[r] - m_new);
-            const float p0 = ok0 ? exp2f(l0 - m_new) : 0.0f;
-            const float p1 = ok1 ? exp2f(l1 - m_new) : 0.0f;
+            const float m_new = fmax_ieee(mr[r], readlane_f(row_max(fmax_ieee(l0, l1)), 0));
+            al[r] = (mr[r] == -INFINITY) ? 0.0f : exp2_fast(mr[r] - m_new);
+            const float p0 = ok0 ? exp2_fast(l0 - m_new) : 0.0f;
+            const float p1 = ok1 ? exp2_fast(l1 - m_new) : 0.0f;
             lr[r] = lr[r] * al[r] + readlane_f(row_sum(p0 + p1), 0);
             mr[r] = m_new;
             // the weights as fp16, rounded to nearest (the quantized part's weights are fp16

@@ -213,7 +213,7 @@ __global__ __launch_bounds__(kGqaBlock) __attribute__((amdgpu_waves_per_eu(3))) 
                                                                        __builtin_bit_cast(h2v, z23), 0.0f, false),
                                                 false);
             az = half_sum4(az4);
-            mx = half_max(mx);
+            mx = half_max_nonneg(mx);
             sh = min(29 - __builtin_amdgcn_frexp_expf(mx), 100);   // |q*s| * 2^sh < 2^29
             const float ff = __builtin_ldexpf(csl, sh);
             float sf[4];
@@ -285,8 +285,8 @@ __global__ __launch_bounds__(kGqaBlock) __attribute__((amdgpu_waves_per_eu(3))) 
         load_kc(cur, nxt);
 
         // ---- online softmax per query over the 64 tokens (rescale only when a max rises)
-        const float mnew = fmaxf(m, row_max(fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3]))));
-        const float al = mnew == m ? 1.0f : exp2f(m - mnew);
+        const float mnew = fmax_ieee(m, row_max(fmax_ieee(fmax_ieee(lg[0], lg[1]), fmax_ieee(lg[2], lg[3]))));
+        const float al = mnew == m ? 1.0f : exp2_fast(m - mnew);
         if (__builtin_amdgcn_ballot_w64(al < 1.0f)) {
 #pragma unroll
             for (int r = 0; r < NQ; ++r) {
@@ -302,7 +302,7 @@ __global__ __launch_bounds__(kGqaBlock) __attribute__((amdgpu_waves_per_eu(3))) 
         float p[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            p[t] = lg[t] == -INFINITY ? 0.0f : exp2f(lg[t] - m);
+            p[t] = lg[t] == -INFINITY ? 0.0f : exp2_fast(lg[t] - m);
             lsum += p[t];
         }
         // value pairs of this lane's 4 tokens 16t + n: zero-point sums

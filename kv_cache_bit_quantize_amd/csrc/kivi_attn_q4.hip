@@ -158,8 +158,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
 #pragma unroll
                 for (int r = 0; r < NQ; ++r) {
                     const float x0 = q0[r] * s0, x1 = q1[r] * s1;
-                    float mx = half_max(fmaxf(fabsf(x0), fabsf(x1)));
-                    mx = fmaxf(readlane_f(mx, 0), readlane_f(mx, 32));
+                    float mx = half_max_nonneg(fmaxf(fabsf(x0), fabsf(x1)));
+                    mx = fmax_ieee(readlane_f(mx, 0), readlane_f(mx, 32));
                     const int sh = min(29 - __builtin_amdgcn_frexp_expf(mx), 100);
                     const float fs = __builtin_ldexpf(1.0f, sh);
                     unit[r] = __builtin_ldexpf(1.0f, -sh);
@@ -206,9 +206,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
                 const float rmx = row_max(lg);
 #pragma unroll
                 for (int r = 0; r < NQ; ++r) {
-                    const float mnew = fmaxf(m[r], readlane_f(rmx, 16 * r));
+                    const float mnew = fmax_ieee(m[r], readlane_f(rmx, 16 * r));
                     if (mnew != m[r]) {
-                        const float al = m[r] == -INFINITY ? 0.0f : exp2f(m[r] - mnew);
+                        const float al = m[r] == -INFINITY ? 0.0f : exp2_fast(m[r] - mnew);
 #pragma unroll
                         for (int c = 0; c < 8; ++c) o[r][c] *= al;
                         oz[r] *= al;
@@ -216,7 +216,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
                         m[r] = mnew;
                     }
                     if (hr == r) {
-                        const float p = exp2f(lg - m[r]);
+                        const float p = exp2_fast(lg - m[r]);
                         lsum[r] += p;   // the lanes of head r's row, one token each
                         pw[r * kQ4Tok + mrow] = p;
                     }

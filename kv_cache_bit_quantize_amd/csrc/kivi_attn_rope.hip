@@ -99,8 +99,8 @@ __device__ void residual_rope_states(const AttnArgs& a, const RowState& rs, int6
         const float part = fmaf(wr, h2f(kr[lane]), -wi * h2f(kr[lane + kRpPairs]));
         const float lg = wave_sum(part) * a.sm_log2;
         const float mnew = fmaxf(mr, lg);
-        const float al = mr == -INFINITY ? 0.0f : exp2f(mr - mnew);
-        const float p = exp2f(lg - mnew);
+        const float al = mr == -INFINITY ? 0.0f : exp2_fast(mr - mnew);
+        const float p = exp2_fast(lg - mnew);
         lr = fmaf(lr, al, p);
         o0 = fmaf(o0, al, p * h2f(vr[lane]));
         o1 = fmaf(o1, al, p * h2f(vr[lane + kRpPairs]));
@@ -323,13 +323,13 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
                 }
                 load_k(kl, it + 1);
                 // ---- online softmax over the 16 tokens (values equal inside each octet)
-                float mx = fmaxf(lg[0], lg[1]);
-                mx = fmaxf(mx, ror8_f(mx));
-                mx = fmaxf(mx, xor16_f(mx));
-                mx = fmaxf(readlane_f(mx, 0), readlane_f(mx, 32));
-                const float mnew = fmaxf(m, mx);
+                float mx = fmax_ieee(lg[0], lg[1]);
+                mx = fmax_ieee(mx, perm_f<0x128>(mx));   // lane (i+8)%16 of the row
+                mx = fmax_ieee(mx, xor16_f(mx));
+                mx = fmax_ieee(readlane_f(mx, 0), readlane_f(mx, 32));
+                const float mnew = fmax_ieee(m, mx);
                 if (mnew != m) {
-                    const float al = m == -INFINITY ? 0.0f : exp2f(m - mnew);
+                    const float al = m == -INFINITY ? 0.0f : exp2_fast(m - mnew);
                     if constexpr (BITS == 2) {
                         cv[0] *= al;
                         cv[1] *= al;
@@ -350,7 +350,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
                         sh_lg[wave][16 * (j & 1) + 8 + t8] = lg[1];
                     }
                 } else {
-                    const float p0 = exp2f(lg[0] - m), p1 = exp2f(lg[1] - m);
+                    const float p0 = exp2_fast(lg[0] - m), p1 = exp2_fast(lg[1] - m);
                     if (k8 == 0) {
                         lsum += p0 + p1;
                         pw[t8] = p0;
@@ -362,7 +362,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
                 if constexpr (BITS == 2) {
                     if (j & 1) {   // the tile's 32 logits are in: its weights, then 8 matrix instructions
                         const int tt = lane & 31, mrow = lane & 15, kgrp = lane >> 4;
-                        const float p = lane < kG ? exp2f(sh_lg[wave][tt] - m) : 0.0f;   // token tt (lanes < 32)
+                        const float p = lane < kG ? exp2_fast(sh_lg[wave][tt] - m) : 0.0f;   // token tt (lanes < 32)
                         lsum += p;
 #pragma unroll
                         for (int k = 0; k < 4; ++k) zk[k] = fmaf(p, h2f(vl.p[k] >> 16), zk[k]);

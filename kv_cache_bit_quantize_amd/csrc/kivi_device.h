@@ -115,6 +115,25 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
+// The same move for a pattern in which every lane has a source lane (quad_perm, the mirrors):
+// no lane keeps its old value, so none is set up first.
+template <int CTRL>
+__device__ __forceinline__ float perm_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t perm_u(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+// IEEE 754 maximum (a NaN operand gives NaN).  Unlike fmaxf, which must first quiet a
+// signalling NaN in each operand that does not come straight from arithmetic (an extra
+// v_max_f32 x, x, x per cross-lane move), it is one v_maximum3_f32.
+__device__ __forceinline__ float fmax_ieee(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+// 2^x by the hardware exponential alone (v_exp_f32).  exp2f adds a range reduction (a
+// compare, two selects, an add and a scale) so that results below 2^-126 come out as
+// subnormals; here they are zero.  Every use is a softmax weight or rescale factor relative
+// to the running maximum, where a factor below 2^-126 is far under the output's resolution.
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float xor1_f(float v) { return dpp_f<0xB1>(v); }    // quad_perm [1,0,3,2]
 __device__ __forceinline__ float xor2_f(float v) { return dpp_f<0x4E>(v); }    // quad_perm [2,3,0,1]
 __device__ __forceinline__ float hmirror_f(float v) { return dpp_f<0x141>(v); } // lane i <-> 7-i in 8
@@ -149,11 +168,23 @@ __device__ __forceinline__ float half_sum(float v) {
     return v + xor16_f(v);
 }
 __device__ __forceinline__ float half_max(float v) {
-    v = __builtin_fmaxf(v, xor1_f(v));
-    v = __builtin_fmaxf(v, xor2_f(v));
-    v = __builtin_fmaxf(v, hmirror_f(v));
-    v = __builtin_fmaxf(v, mirror_f(v));
-    return __builtin_fmaxf(v, xor16_f(v));
+    v = fmax_ieee(v, perm_f<0xB1>(v));
+    v = fmax_ieee(v, perm_f<0x4E>(v));
+    v = fmax_ieee(v, perm_f<0x141>(v));
+    v = fmax_ieee(v, perm_f<0x140>(v));
+    return fmax_ieee(v, xor16_f(v));
+}
+// half_max for values that are never negative: their bit patterns order as unsigned
+// integers do, and an integer maximum takes its cross-lane operand directly (one
+// v_max_u32 with a DPP source per step)
+__device__ __forceinline__ float half_max_nonneg(float f) {
+    uint32_t v = __builtin_bit_cast(uint32_t, f);
+    v = max(v, perm_u<0xB1>(v));
+    v = max(v, perm_u<0x4E>(v));
+    v = max(v, perm_u<0x141>(v));
+    v = max(v, perm_u<0x140>(v));
+    v = max(v, (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F));
+    return __builtin_bit_cast(float, v);
 }
 // max over lanes that differ in bits 2..5, for values already equal inside each quad;
 // the result is wave-uniform
