@@ -98,8 +98,10 @@ __global__ __launch_bounds__(kGqaBlock) __attribute__((amdgpu_waves_per_eu(3))) 
     // a zero the compiler cannot see: fma(h, f, kZero) stays one mixed-precision fma (a
     // literal zero would turn it into a multiply with a separate conversion)
     const float kZero = __builtin_bit_cast(float, in_vgpr(0u));
-    // after half_sum4, the lane of a half-wave that holds query r's sum
-    auto q_lane = [](int r) { return (r >> 1) | ((r & 1) << 1); };
+    // after half_sum4, lane (r >> 1) | ((r & 1) << 1) of a half-wave holds query r's sum: the
+    // byte address of this lane's query's sum in the first half (a query past NQ reads a sum
+    // of zeros; its logits are -inf anyway)
+    const int zsrc = 4 * ((qh >> 1) | ((qh & 1) << 1));
 
     // key A operand of group g, channel half kh: row 4h + d = digit plane (h, d) of the group
     // (rows of absent queries read zeros) at kbase + g*kKeyGroup + 64*kh
@@ -187,7 +189,7 @@ __global__ __launch_bounds__(kGqaBlock) __attribute__((amdgpu_waves_per_eu(3))) 
         // ---- q_r*s of this half's group as 30-bit fixed point (one exponent for the NQ
         // queries), four signed byte digits per channel, stored as digit planes; q_r.z as
         // packed dot products
-        float az;    // after the reduction: q_r.z of the half's group, r as q_lane gives
+        float az;    // after the reduction: q_r.z of the half's group, in the lane zsrc names for r
         int sh;
         {
             const uint32_t pr[4] = {cur.kp.x, cur.kp.y, cur.kp.z, cur.kp.w};
@@ -256,12 +258,8 @@ __global__ __launch_bounds__(kGqaBlock) __attribute__((amdgpu_waves_per_eu(3))) 
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
             kscale[g] = __builtin_ldexpf(1.0f, -__builtin_amdgcn_readlane(sh, 32 * g));
-            float zs[NQ];
-#pragma unroll
-            for (int r = 0; r < NQ; ++r) zs[r] = readlane_f(az, 32 * g + q_lane(r));
-            float z = zs[0];
-#pragma unroll
-            for (int r = 1; r < NQ; ++r) z = qh == r ? zs[r] : z;
+            // one cross-lane read through the LDS crossbar (no vector-ALU selects)
+            const float z = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(zsrc + 128 * g, __builtin_bit_cast(int, az)));
             azq[g] = z * a.sm_log2;
         }
         float lg[4];
