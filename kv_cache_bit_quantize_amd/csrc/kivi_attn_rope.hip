@@ -115,7 +115,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     constexpr int kIt = GS / kRpTok;   // iterations per key group
     __shared__ double sh_w[kRpPairs];                        // pair frequencies
     __shared__ __align__(16) float2 sh_ed[GS][kRpPairs];     // exp(i*d*w) for offsets d < G
-    __shared__ __align__(16) float2 sh_e0[kWaves][kRpPairs]; // exp(i*t0*w) of the wave's group
+    // the folded products U, V, X (real and imaginary parts) of the wave's group, per pair;
+    // pair p at p + 4*(p/32), so that the eight 8-pair runs the lanes read at once start in
+    // different 16-byte bank slots
+    __shared__ __align__(16) float sh_f[kWaves][6][kRpPairs + 8];
     __shared__ __align__(16) float sh_p[kWaves][kRpTok];                // 4-bit: the iteration's weights
     // 2-bit values on the matrix cores: per wave the tile's 32 logits and its value weights
     // [channel group][32 tokens] (fp16, the A operand's weight row), and zero rows
@@ -148,15 +151,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     const int n_groups = kg_lo + min(cnt, (wave + 1) * per_wave) - kgb;
     const int n_it = n_groups * kIt;
 
-    // the lane's query pairs: channels 8k8..8k8+7 and 64+8k8..64+8k8+7, kept as packed fp16
-    // (converted once per key group)
-    uint32_t qlo2[4], qhi2[4];
-    {
-        const uint4 x = *reinterpret_cast<const uint4*>(a.q + qrow * kD + 8 * k8);
-        const uint4 y = *reinterpret_cast<const uint4*>(a.q + qrow * kD + kRpPairs + 8 * k8);
-        qlo2[0] = x.x; qlo2[1] = x.y; qlo2[2] = x.z; qlo2[3] = x.w;
-        qhi2[0] = y.x; qhi2[1] = y.y; qhi2[2] = y.z; qhi2[3] = y.w;
-    }
+    // the query pair the lane folds once per group: channels lane and 64 + lane
+    const float q_lo = h2f(a.q[qrow * kD + lane]), q_hi = h2f(a.q[qrow * kD + kRpPairs + lane]);
 
     const int64_t tok0 = kvrow * (int64_t)a.token_cap;
     const uint8_t* kc_row = a.k_codes + tok0 * (BITS == 2 ? kRowBytes : kRowBytes4);
@@ -216,14 +212,12 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
             }
         }
     };
-    // key (scale, zero) words of group gi of the wave, channels 8k8.. and 64+8k8..
-    struct PLoad { uint4 lo[2], hi[2]; };
+    // key (scale, zero) words of group gi of the wave, channels lane and 64 + lane
+    struct PLoad { uint32_t lo, hi; };
     auto load_kp = [&](PLoad& L, int gi) {
         const uint32_t* g = kp_row + (int64_t)(kgb + min(gi, n_groups - 1)) * kD;
-        L.lo[0] = *reinterpret_cast<const uint4*>(g + 8 * k8);
-        L.lo[1] = *reinterpret_cast<const uint4*>(g + 8 * k8 + 4);
-        L.hi[0] = *reinterpret_cast<const uint4*>(g + kRpPairs + 8 * k8);
-        L.hi[1] = *reinterpret_cast<const uint4*>(g + kRpPairs + 8 * k8 + 4);
+        L.lo = g[lane];
+        L.hi = g[kRpPairs + lane];
     };
     auto wave_sync = []() {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -262,36 +256,41 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
 
     uint32_t tag;
     if (n_groups > 0) {
+        const double w_lane = sh_w[lane];   // the frequency of the lane's pair
+        const int f_slot = lane + 4 * (lane >> 5), f_run = 8 * k8 + 4 * (k8 >> 2);
         tag = settle_tag(tag_v);
         for (int gi = 0; gi < n_groups; ++gi) {
             set_priority_for(n_groups - gi);   // (as in the query-group kernel: most work left issues first)
-            // ---- turn of the group start for the 64 pairs (lane = pair), through LDS
-            sh_e0[wave][lane] = turn((double)((kgb + gi) * GS) * sh_w[lane]);
+            // ---- the group's folded products, pair = lane: each is needed by the 8 lanes that
+            // take the pair's channels, so it is formed once and shared through LDS
+            {
+                const float2 e = turn((double)((kgb + gi) * GS) * w_lane);   // exp(i*t0*w)
+                const float wr = fmaf(q_lo, e.x, q_hi * e.y);    // W = conj(Q) * e
+                const float wi = fmaf(q_lo, e.y, -q_hi * e.x);
+                const float slo = h2f(pn.lo & 0xffffu), zlo = h2f(pn.lo >> 16);
+                const float shi = h2f(pn.hi & 0xffffu), zhi = h2f(pn.hi >> 16);
+                float(*f)[kRpPairs + 8] = sh_f[wave];
+                f[0][f_slot] = fmaf(wr, zlo, -wi * zhi);   // U = W * (zlo + i*zhi)
+                f[1][f_slot] = fmaf(wr, zhi, wi * zlo);
+                f[2][f_slot] = wr * slo;                   // V = W * slo
+                f[3][f_slot] = wi * slo;
+                f[4][f_slot] = -wi * shi;                  // X = i * W * shi
+                f[5][f_slot] = wr * shi;
+            }
+            load_kp(pn, gi + 1);
             wave_sync();
+            // the lane's pairs 8k8..8k8+7
             float ur[8], ui[8], vr[8], vi[8], xr[8], xi[8];
             {
-                const uint32_t plo[8] = {pn.lo[0].x, pn.lo[0].y, pn.lo[0].z, pn.lo[0].w,
-                                         pn.lo[1].x, pn.lo[1].y, pn.lo[1].z, pn.lo[1].w};
-                const uint32_t phi[8] = {pn.hi[0].x, pn.hi[0].y, pn.hi[0].z, pn.hi[0].w,
-                                         pn.hi[1].x, pn.hi[1].y, pn.hi[1].z, pn.hi[1].w};
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const float2 e = sh_e0[wave][8 * k8 + j];
-                    const float qlo = h2f(qlo2[j >> 1] >> (16 * (j & 1))), qhi = h2f(qhi2[j >> 1] >> (16 * (j & 1)));
-                    const float wr = fmaf(qlo, e.x, qhi * e.y);    // W = conj(Q) * e
-                    const float wi = fmaf(qlo, e.y, -qhi * e.x);
-                    const float slo = h2f(plo[j] & 0xffffu), zlo = h2f(plo[j] >> 16);
-                    const float shi = h2f(phi[j] & 0xffffu), zhi = h2f(phi[j] >> 16);
-                    ur[j] = fmaf(wr, zlo, -wi * zhi);                    // U = W * (zlo + i*zhi)
-                    ui[j] = fmaf(wr, zhi, wi * zlo);
-                    vr[j] = wr * slo;                                    // V = W * slo
-                    vi[j] = wi * slo;
-                    xr[j] = -wi * shi;                                   // X = i * W * shi
-                    xi[j] = wr * shi;
-                }
+                auto run = [&](int c, float (&d)[8]) {
+                    const float4 lo = *reinterpret_cast<const float4*>(&sh_f[wave][c][f_run]);
+                    const float4 hi = *reinterpret_cast<const float4*>(&sh_f[wave][c][f_run + 4]);
+                    d[0] = lo.x; d[1] = lo.y; d[2] = lo.z; d[3] = lo.w;
+                    d[4] = hi.x; d[5] = hi.y; d[6] = hi.z; d[7] = hi.w;
+                };
+                run(0, ur); run(1, ui); run(2, vr); run(3, vi); run(4, xr); run(5, xi);
             }
-            wave_sync();   // every lane has read the turns before the next group's are written
-            load_kp(pn, gi + 1);
+            wave_sync();   // every lane has read the products before the next group's are written
             // (unrolled by two: a tile's even and odd iterations have code of their own, so the
             // tile's value loads, issued at the top of its odd iteration, are live for one)
 #pragma unroll 2
