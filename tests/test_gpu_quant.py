@@ -143,6 +143,26 @@ def test_value_tokens_ragged(tokens):
     assert np.array_equal(bits(cache.v_sz), rc.v_sz)
 
 
+def test_value_calls_fill_tiles_in_pieces():
+    """Values quantized by separate calls over adjacent destination ranges, the later range
+    first: each call merges its tokens' codes into the words the other calls wrote (the
+    ranges split code bytes, 16-token blocks and 32-token tiles)."""
+    dev = gpu_or_skip()
+    kivi = _kivi()
+    rng = np.random.default_rng(77)
+    n = 95
+    x = rng.standard_normal((2, 1, n, D)).astype(np.float16)
+    xt = torch.from_numpy(x).to(dev)
+    cache = kivi.Cache(2, 1, 128, device=dev)
+    for lo, hi in ((35, 95), (18, 35), (17, 18), (0, 17)):
+        kivi.kivi_quantize_v_per_token(xt[:, :, lo:hi], cache, dst_token_off=5 + lo)
+    torch.cuda.synchronize()
+    rc = ref.RefCache(2, 1, D, G, 128, token_cap=128)
+    rc.quantize_v(x.view(np.uint16).reshape(2, n, D), n, dst_off=5)
+    assert np.array_equal(cache.v_codes.cpu().numpy(), rc.v_codes)
+    assert np.array_equal(bits(cache.v_sz), rc.v_sz)
+
+
 def test_prefill_llama2_7b_layer_full_cache():
     dev = gpu_or_skip()
     cache, rc = _prefill_both(synth.WORKLOADS["llama2-7b-layer"], dev)
