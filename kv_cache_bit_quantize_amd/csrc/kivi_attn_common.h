@@ -144,15 +144,15 @@ constexpr uint32_t kWsPollTimeout = 1u;   // the status word's bit (KIVI_WS_POLL
 // The (scale, zero) pairs of one value token, kD / GS of them, loaded at their own width (a
 // wider load would read past the last token of the last row) and returned as one word per
 // 32-channel block: word k is the pair of the group that holds channels 32k..32k+31.
-template <int GS>
+template <int GS, bool STREAM>
 __device__ __forceinline__ uint4 load_value_pairs(const uint32_t* p) {
     if constexpr (GS == 32) {
-        return *reinterpret_cast<const uint4*>(p);
+        return STREAM ? stream_load16(p) : *reinterpret_cast<const uint4*>(p);
     } else if constexpr (GS == 64) {
-        const uint2 x = *reinterpret_cast<const uint2*>(p);
+        const uint2 x = STREAM ? stream_load8(p) : *reinterpret_cast<const uint2*>(p);
         return make_uint4(x.x, x.x, x.y, x.y);
     } else {
-        const uint32_t x = *p;
+        const uint32_t x = STREAM ? stream_load4(p) : *p;
         return make_uint4(x, x, x, x);
     }
 }

@@ -194,7 +194,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
             // t0 + (lane & 31) are in the wave's groups
             const uint32_t t0 = (uint32_t)tok(it) & ~(uint32_t)(kG - 1);
             const uint4 x = reinterpret_cast<const uint4*>(vc_row + (t0 / kG) * kTileBytes)[lane];
-            const uint4 y = load_value_pairs<GS>(vp_row + value_pair_index<GS>((int64_t)t0 + (lane & 31), 0));
+            const uint4 y = load_value_pairs<GS, false>(vp_row + value_pair_index<GS>((int64_t)t0 + (lane & 31), 0));
             L.c[0] = x.x;
             L.c[1] = x.y;
             L.c[2] = x.z;
