@@ -14,7 +14,8 @@ L2 and infinity cache between attention launches.
         OUT/write/run_counter_collection.csv --out profiles/decode_attn_long-128k_counters
 
 The summary gives the attention kernel's HBM bytes per launch next to its algorithmic
-bytes, and records the hash of the kernel sources it was taken on.
+bytes, and records the hash of the kernel sources it was taken on.  `counters` summarizes other
+counter runs of the attention kernels, `trace` a kernel-trace run of bench.py.
 """
 import argparse
 import csv
@@ -217,6 +218,52 @@ def counters(args):
     print(json.dumps({k: v["derived"] for k, v in summary.items()}, indent=1))
 
 
+def trace(args):
+    """Markdown summary of a rocprofv3 --kernel-trace --stats run of bench.py: the library's
+    kernels from the stats csv, and the dispatches of one kernel from the trace csv split into
+    those right after a read_probe_kernel (the benchmark's flushed launches) and the others."""
+    lines = [f"# {args.title}\n", "Command (from the repository root, on one MI355X):\n", "```", args.command, "```\n",
+             "Library kernels (`run_kernel_stats.csv`; the prefill kernels run once per cache the benchmark "
+             "builds, outside the timed steps):\n", "| kernel | calls | average us | min us | max us |",
+             "|---|---|---|---|---|"]
+    with open(args.stats_csv) as f:
+        for r in csv.DictReader(f):
+            if "kivi::" not in r["Name"]:
+                continue
+            name = r["Name"].split("(")[0].replace("void ", "")
+            lines.append(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                         f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+    rows = []
+    with open(args.trace_csv) as f:
+        for r in csv.DictReader(f):
+            rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]))
+    rows.sort()
+    steps, flushed, name = [], [], None
+    for i, (t0, t1, k) in enumerate(rows):
+        if args.kernel not in k:
+            continue
+        name = k.split("(")[0].replace("void ", "")
+        after_probe = i > 0 and "read_probe_kernel" in rows[i - 1][2]
+        (flushed if after_probe else steps).append((t1 - t0) / 1e3)
+    if name:
+        st = sorted(steps)
+        med = st[len(st) // 2] if len(st) % 2 else 0.5 * (st[len(st) // 2 - 1] + st[len(st) // 2])
+        lines.append("")
+        lines.append(f"`{name}` has two kinds of dispatch in this run (`run_kernel_trace.csv`): {len(steps)} "
+                     f"dispatches not preceded by a read (the decode steps, warm-up included), average "
+                     f"{sum(steps) / len(steps):.2f} us, median {med:.2f} us, min {st[0]:.2f} us; and {len(flushed)} "
+                     f"attention-only launches each after a 1 GiB read by `read_probe_kernel` (the benchmark's "
+                     f"flushed measurement), average {sum(flushed) / max(1, len(flushed)):.2f} us.")
+        if args.bytes:
+            lines.append("")
+            lines.append(f"At {args.bytes} algorithmic bytes per launch, the decode steps' average is "
+                         f"{args.bytes / (sum(steps) / len(steps)) / 1e3:.1f} GB/s "
+                         f"({args.bytes / (sum(steps) / len(steps)) / 1e3 / 8000:.3f} of the 8 TB/s HBM peak).")
+    with open(args.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -234,7 +281,18 @@ def main():
     c.add_argument("--title", required=True)
     c.add_argument("--out", required=True)
     c.add_argument("--command", nargs="*", default=[], help="the rocprofv3 commands that wrote the csvs")
+    t = sub.add_parser("trace")
+    t.add_argument("stats_csv")
+    t.add_argument("trace_csv")
+    t.add_argument("--kernel", required=True, help="substring of the kernel whose dispatches are split")
+    t.add_argument("--bytes", type=int, default=0, help="algorithmic bytes per launch of that kernel")
+    t.add_argument("--title", required=True)
+    t.add_argument("--command", required=True, help="the rocprofv3 command that wrote the csvs")
+    t.add_argument("--out", required=True)
     a = ap.parse_args()
+    if a.cmd == "trace":
+        trace(a)
+        return
     if a.cmd == "counters":
         counters(a)
         return
