@@ -148,7 +148,7 @@ __global__ __launch_bounds__(64 * W) void attn_split_kernel(AttnArgs a) {
     // last use in this one, so every load still has most of an iteration to arrive.
     // first groups of the current and the next iteration (wave-uniform)
     int g_cur0 = g_lo + 2 * c_cur;
-    int g_nxt0 = c_nxt < n_pairs ? g_lo + 2 * c_nxt : g_cur0;
+    int g_nxt0 = c_nxt < n_pairs ? g_lo + 2 * c_nxt : 0;
     auto group_of = [&](int which, int half) {   // which: 0 = current iteration, 1 = next
         const int g0 = which ? g_nxt0 : g_cur0;
         return half == 0 ? g0 : (g0 + 1 < g_hi ? g0 + 1 : g0);   // in-bounds address for an idle half
@@ -170,9 +170,11 @@ __global__ __launch_bounds__(64 * W) void attn_split_kernel(AttnArgs a) {
         L.vp = load_value_pairs<GS, true>(vp_row + value_pair_index<GS>((int64_t)group_of(it, gh) * kG + tt, 0));
     };
 
-    // Every load is issued unconditionally (past the end it reads the last iteration's data
-    // again, from the L2), so the compiler knows how many loads are in flight at each use and
-    // waits for exactly the one it needs.
+    // Every load is issued unconditionally, so the compiler knows how many loads are in flight
+    // at each use and waits for exactly the one it needs.  Past the end a wave reads the row's
+    // first two groups: the row's 96 waves share those lines, so they mostly come from the L2
+    // (re-reading the wave's own last pair, which the non-temporal loads do not keep, cost
+    // 3.7% more HBM bytes and about 1 us at the 131,072-token context).
     Loads cur;
     if (c_cur < n_pairs) {   // the first iteration's loads, in flight during the set-up below
         load_kp(cur, 0);
@@ -322,7 +324,7 @@ __global__ __launch_bounds__(64 * W) void attn_split_kernel(AttnArgs a) {
             c_nxt = 2 * kSqWaves + __builtin_amdgcn_readfirstlane(pv);
             if (lane == 0) pend = atomicAdd(&sh_next, 1);
             g_cur0 = g_lo + 2 * c_cur;
-            g_nxt0 = c_nxt < n_pairs ? g_lo + 2 * c_nxt : g_cur0;
+            g_nxt0 = c_nxt < n_pairs ? g_lo + 2 * c_nxt : 0;
         }
     } else {
         tag = settle_tag(tag_v);
