@@ -316,24 +316,34 @@ def event_pairs(n):
 
 
 def read_ceiling(kivi, dev, sizes, reps=20):
-    """The chip's streaming-read rate: kivi_read_probe (a plain grid-stride 16-byte read) over
-    buffers of the given sizes, each read's duration from events its own dispatch records."""
+    """The chip's streaming-read rate: a grid-stride 16-byte read (kivi_read_probe_stream, with the
+    non-temporal loads the decode kernels stream the cache with; kivi_read_probe, with plain
+    loads, beside it) over buffers of the given sizes, each read's duration from events its
+    own dispatch records."""
     res = []
     for nbytes in sizes:
         nbytes = nbytes // 16 * 16
         buf = torch.ones(nbytes, dtype=torch.uint8, device=dev)
-        sink = kivi.kivi_read_probe(buf)
-        for _ in range(3):
-            kivi.kivi_read_probe(buf, sink)
-        ev = event_pairs(reps)
-        torch.cuda.synchronize()
-        for i in range(reps):
-            kivi.kivi_time_next_attention(*ev[i])
-            kivi.kivi_read_probe(buf, sink)
-        torch.cuda.synchronize()
-        st = stats_us([a.elapsed_time(b) for a, b in ev])
-        res.append({"bytes": nbytes, "us": st, "achieved": round(nbytes / st["median"] / 1e3, 1), "unit": "GB/s",
-                    "frac": round(nbytes / st["median"] / 1e3 / PEAK_HBM_GBS, 4)})
+        entry = {"bytes": nbytes}
+        for streaming in (True, False):
+            sink = kivi.kivi_read_probe(buf, streaming=streaming)
+            for _ in range(3):
+                kivi.kivi_read_probe(buf, sink, streaming=streaming)
+            ev = event_pairs(reps)
+            torch.cuda.synchronize()
+            for i in range(reps):
+                kivi.kivi_time_next_attention(*ev[i])
+                kivi.kivi_read_probe(buf, sink, streaming=streaming)
+            torch.cuda.synchronize()
+            st = stats_us([a.elapsed_time(b) for a, b in ev])
+            r = {"us": st, "achieved": round(nbytes / st["median"] / 1e3, 1), "unit": "GB/s",
+                 "frac": round(nbytes / st["median"] / 1e3 / PEAK_HBM_GBS, 4)}
+            if streaming:
+                entry.update(r)
+                entry["loads"] = "non-temporal"
+            else:
+                entry["plain_loads"] = r
+        res.append(entry)
         del buf
     return res
 

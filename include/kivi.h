@@ -301,7 +301,7 @@ int kivi_decode_attn_fp16(const uint16_t* k, const uint16_t* v, int32_t batch, i
 
 /* Measurement hook, for callers that time the attention kernel itself (not a step of the
  * method).  The next decode-attention kernel that an attention call (kivi_decode_attn,
- * kivi_decode_step and the other attention entry points) or kivi_read_probe launches from
+ * kivi_decode_step and the other attention entry points) or a read probe launches from
  * the calling thread records its own start in start_event and its end in
  * stop_event (hipEvent_t handles, created by the caller with timing enabled), taken by the
  * dispatch itself with no marker command in the stream, so hipEventElapsedTime(start, stop)
@@ -319,6 +319,11 @@ int kivi_time_next_attention(void* start_event, void* stop_event);
  * bad arguments; nothing is enqueued then. */
 int kivi_read_probe(const void* src, size_t bytes, uint32_t* sink, void* stream);
 size_t kivi_read_probe_sink_bytes(void);
+
+/* kivi_read_probe with non-temporal loads (the hint the decode kernels stream the cache with):
+ * the fastest plain read measured, so its rate is the read ceiling; it does not evict the
+ * Infinity Cache.  Same arguments, errors and timing hook as kivi_read_probe. */
+int kivi_read_probe_stream(const void* src, size_t bytes, uint32_t* sink, void* stream);
 
 /* Testing hook of the merge's bounded wait (not a step of the method): the next attention call
  * of the calling thread that passes validation polls each split partial at most max_polls

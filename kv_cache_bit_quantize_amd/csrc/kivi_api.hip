@@ -646,13 +646,21 @@ int kivi_test_next_attention_merge(int32_t max_polls, uint32_t tag_skew) {
 
 size_t kivi_read_probe_sink_bytes(void) { return (size_t)kProbeBlocks * sizeof(uint32_t); }
 
-int kivi_read_probe(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+static int read_probe(const void* src, size_t bytes, uint32_t* sink, bool streaming, void* stream) {
     if (src == nullptr || sink == nullptr) return KIVI_ERR_NULL;
     if (bytes % 16 != 0 || !aligned16(src) || (reinterpret_cast<uintptr_t>(sink) & 3u)) return KIVI_ERR_SHAPE;
     if (bytes == 0) return KIVI_OK;
     hipEvent_t t0, t1;
     take_timing(&t0, &t1);
-    return hip_status(launch_read_probe(src, bytes, sink, (hipStream_t)stream, t0, t1));
+    return hip_status(launch_read_probe(src, bytes, sink, streaming, (hipStream_t)stream, t0, t1));
+}
+
+int kivi_read_probe(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+    return read_probe(src, bytes, sink, false, stream);
+}
+
+int kivi_read_probe_stream(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+    return read_probe(src, bytes, sink, true, stream);
 }
 
 int kivi_time_next_attention(void* start_event, void* stop_event) {

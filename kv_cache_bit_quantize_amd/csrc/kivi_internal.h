@@ -113,11 +113,11 @@ constexpr int32_t kSeqCapacity = 1;   // a flush would pass token_cap: the appen
 constexpr int32_t kSeqBadState = 2;   // the state was out of range: the sequence was skipped
 
 
-// measurement helper: a plain streaming read of `bytes` (a multiple of 16) at src, one word per
-// workgroup (kProbeBlocks of them) written to sink
+// measurement helper: one streaming read of `bytes` (a multiple of 16) at src, plain loads or
+// (streaming) non-temporal ones, one word per workgroup (kProbeBlocks of them) written to sink
 constexpr int kProbeBlocks = 256;    // one 16-wave workgroup per CU
-hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, hipStream_t s, hipEvent_t t0 = nullptr,
-                             hipEvent_t t1 = nullptr);
+hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, bool streaming, hipStream_t s,
+                             hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 
 hipError_t launch_quantize_k(const QuantArgs& a, hipStream_t s);
 hipError_t launch_quantize_v(const QuantArgs& a, hipStream_t s);

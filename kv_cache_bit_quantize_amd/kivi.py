@@ -25,7 +25,8 @@ EXPORTS = ["kivi_quantize_k_per_channel", "kivi_quantize_v_per_token", "kivi_pre
            "kivi_decode_attn_ragged_splits", "kivi_decode_attn_rope", "kivi_decode_attn_rope_splits",
            "kivi_decode_attn_rope_ragged", "kivi_decode_attn_rope_ragged_splits", "kivi_decode_step_rope",
            "kivi_decode_step_splits", "kivi_decode_step_workspace", "kivi_test_next_attention_merge",
-           "kivi_decode_attn_noalloc", "kivi_read_probe", "kivi_read_probe_sink_bytes"]
+           "kivi_decode_attn_noalloc", "kivi_read_probe", "kivi_read_probe_sink_bytes",
+           "kivi_read_probe_stream"]
 
 KIVI_FLUSH_ALL = 1        # kivi_cache.flags: a full residual is flushed whole (else its oldest group)
 KIVI_CODES_4BIT = 2       # kivi_cache.flags: 4-bit codes (sixteen levels), token-major nibbles
@@ -91,6 +92,7 @@ def _load():
     L.kivi_test_next_attention_merge.argtypes = [i32, C.c_uint32]
     L.kivi_decode_attn_noalloc.argtypes = [cp, p, i32, C.c_float, p, p, i32, p]
     L.kivi_read_probe.argtypes = [p, C.c_size_t, p, p]
+    L.kivi_read_probe_stream.argtypes = [p, C.c_size_t, p, p]
     L.kivi_read_probe_sink_bytes.argtypes = []
     L.kivi_read_probe_sink_bytes.restype = C.c_size_t
     L.kivi_status_str.restype = C.c_char_p
@@ -485,15 +487,17 @@ def workspace_status(ws):
     return int(ws[:4].view(torch.int32).item())
 
 
-def kivi_read_probe(buf, sink=None):
-    """Measurement helper: one plain streaming read of the whole (contiguous) device tensor
-    `buf` on the current stream; returns the sink tensor the kernel wrote to."""
+def kivi_read_probe(buf, sink=None, streaming=False):
+    """Measurement helper: one streaming read of the whole (contiguous) device tensor `buf` on
+    the current stream, with plain loads (kivi_read_probe) or non-temporal ones
+    (kivi_read_probe_stream); returns the sink tensor the kernel wrote to."""
     if not buf.is_contiguous():
         raise ValueError("expected a contiguous tensor")
     if sink is None:
         sink = _empty(lib.kivi_read_probe_sink_bytes() // 4, dtype=torch.int32, device=buf.device)
-    _check(lib.kivi_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(buf)),
-           "kivi_read_probe")
+    fn = lib.kivi_read_probe_stream if streaming else lib.kivi_read_probe
+    _check(fn(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(buf)),
+           "kivi_read_probe_stream" if streaming else "kivi_read_probe")
     return sink
 
 

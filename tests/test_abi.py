@@ -21,7 +21,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 28
+    assert len(names) == 29
     out = os.popen(f"nm -D --defined-only {kivi.LIB_PATH}").read()
     exported = set(re.findall(r" T (kivi_\w+)$", out, re.M))
     assert set(names) <= exported, set(names) - exported
@@ -321,6 +321,10 @@ def test_read_probe_arguments():
     assert L.kivi_read_probe(C.c_void_p(FAKE + 8), 16, P, None) == -2
     assert L.kivi_read_probe(P, 0, P, None) == 0              # nothing to read, nothing enqueued
     assert L.kivi_read_probe_sink_bytes() >= 4
+    for fn in (L.kivi_read_probe, L.kivi_read_probe_stream):
+        assert fn(None, 16, P, None) == -1
+        assert fn(P, 24, P, None) == -2
+        assert fn(P, 0, P, None) == 0
 
 
 def test_merge_test_hook_arguments():
