@@ -103,10 +103,11 @@ int hip_status(hipError_t e) { return e == hipSuccess ? KIVI_OK : KIVI_ERR_HIP; 
 // to one workgroup, which streams the KV head's cache once for all of them.
 int32_t code_bits(const kivi_cache* c) { return (c->flags & KIVI_CODES_4BIT) ? 4 : 2; }
 
-// query heads per workgroup for a GQA ratio (the 4-bit kernel keeps at most two heads' state
-// in registers)
+// query heads per workgroup for a GQA ratio (the 4-bit kernel: one, two or four; with four
+// heads it needs 106 VGPRs, and a kv head's four query heads in one workgroup read its codes
+// once: gqa-mistral-7b 233 us against 245-251 us with two heads per workgroup)
 int32_t queries_per_block(int32_t ratio, int32_t bits = 2) {
-    if (bits == 4) return ratio % 2 == 0 ? 2 : 1;
+    if (bits == 4) return ratio % 4 == 0 ? 4 : (ratio % 2 == 0 ? 2 : 1);
     if (ratio % 4 == 0) return 4;
     if (ratio % 3 == 0) return 3;
     if (ratio % 2 == 0) return 2;

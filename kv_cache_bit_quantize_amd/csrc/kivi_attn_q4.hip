@@ -198,8 +198,13 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
                     // digit sums: |S| < 128 * 128 * 15, the total one binary32 rounding
                     const int hw = cacc[3] * 256 + cacc[2], lw = cacc[1] * 256 + cacc[0];
                     const float tot = fmaf((float)hw, 65536.0f, (float)lw);
-                    const float u = (NQ > 1 && hr == 1) ? unit[NQ - 1] : unit[0];
-                    const float z = (NQ > 1 && hr == 1) ? qz[NQ - 1] : qz[0];
+                    float u = unit[0], z = qz[0];
+#pragma unroll
+                    for (int r = 1; r < NQ; ++r)
+                        if (hr == r) {
+                            u = unit[r];
+                            z = qz[r];
+                        }
                     lg = fmaf(tot, u, z) * a.sm_log2;
                 }
                 // ---- online softmax per query head over the 16 tokens (head r: DPP row r)
@@ -314,9 +319,10 @@ hipError_t launch_decode_attn_q4(const AttnArgs& a, hipStream_t s, hipEvent_t t0
     else                                                                                                        \
         KIVI_BY_GROUP(a.group, hipExtLaunchKernelGGL((attn_q4_kernel<NQv, GS, false>), grid, dim3(kBlock), 0, s, t0, \
                                                      t1, 0, a))
-    switch (a.nq) {   // the host takes at most two query heads per workgroup for 4-bit caches
+    switch (a.nq) {   // the host takes one, two or four query heads per workgroup for 4-bit caches
         case 1: KIVI_Q4_NQ(1) break;
         case 2: KIVI_Q4_NQ(2) break;
+        case 4: KIVI_Q4_NQ(4) break;
         default: return hipErrorInvalidValue;
     }
 #undef KIVI_Q4_NQ
