@@ -21,10 +21,14 @@
 // groups, each of its 4 waves a contiguous run of them, 16 tokens per wave-iteration:
 //  * logits as above, online softmax per query head (log2 domain) over DPP row r, the
 //    probabilities into LDS;
-//  * P.V: lane 16g + c holds tokens 4g..4g+3 and channels [8c, 8c+8) (4 bytes of codes and
-//    the token's (scale, zero) word of those channels).
+//  * P.V: lane 16g + c holds tokens g, g+4, g+8, g+12 and channels [8c, 8c+8) (4 bytes of
+//    codes and the token's (scale, zero) word of those channels).
 // Code loads are issued one iteration ahead, the next group's (scale, zero) words one group
-// ahead, all unconditionally (clamped past the end).
+// ahead, all unconditionally (clamped past the end).  Each code load instruction reads whole
+// rows (a lane 16 bytes of a token's key codes, four lanes the row; a value load four
+// consecutive rows), so the codes and key pairs stream with non-temporal loads: 107.5-108 us
+// at the 131,072-token context against 121.3-121.7 us with plain loads of half rows (same box;
+// the hint on loads that split rows between instructions had been 9% slower).
 #include <hip/hip_ext.h>
 
 #include "kivi_attn_common.h"
@@ -92,31 +96,32 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     const uint32_t* vp_row = reinterpret_cast<const uint32_t*>(a.v_sz) + tok0 * (kD / GS);
     const int t_b = kgb * GS;
     struct Loads {
-        uint2 kc[2];      // key codes of token mrow, channels 16(kb + 4h)..+15 (h = 0, 1)
-        uint32_t v[4];    // value codes of tokens 4vg+u, channels 8vc..8vc+7
+        uint2 kc[2];      // key codes of token mrow, channels 16(2kb + h)..+15 (h = 0, 1)
+        uint32_t v[4];    // value codes of tokens vg+4u, channels 8vc..8vc+7
         uint32_t vp[4];   // (scale, zero) word of those tokens and channels
     };
     auto tok = [&](int it) { return t_b + min(it, n_it - 1) * kQ4Tok; };   // clamped past the end
     // byte offsets inside a row fit 32 bits (token_cap <= 2^26 for 4-bit caches), so the
     // loads take the row pointer as their scalar base and per-token steps as immediates
     auto load_k = [&](Loads& L, int it) {
-        const uint8_t* r = kc_row + (uint32_t)(tok(it) + mrow) * kRowBytes4 + 8 * kb;
-        L.kc[0] = *reinterpret_cast<const uint2*>(r);
-        L.kc[1] = *reinterpret_cast<const uint2*>(r + 32);
+        const uint8_t* r = kc_row + (uint32_t)(tok(it) + mrow) * kRowBytes4 + 16 * kb;
+        const uint4 x = stream_load16(r);
+        L.kc[0] = make_uint2(x.x, x.y);
+        L.kc[1] = make_uint2(x.z, x.w);
     };
     auto load_v = [&](Loads& L, int it) {
-        const uint32_t t = (uint32_t)(tok(it) + 4 * vg);
+        const uint32_t t = (uint32_t)(tok(it) + vg);
         const uint8_t* cp = vc_row + (t * kRowBytes4 + 4 * vc);
         const uint32_t* pp = vp_row + (t * (kD / GS) + (8 * vc) / GS);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            L.v[u] = *reinterpret_cast<const uint32_t*>(cp + u * kRowBytes4);
-            L.vp[u] = pp[u * (kD / GS)];
+            L.v[u] = stream_load4(cp + 4 * u * kRowBytes4);
+            L.vp[u] = pp[4 * u * (kD / GS)];
         }
     };
     // (scale, zero) words of key group gi of the wave, channels 2*lane and 2*lane+1
     auto load_kp = [&](int gi) {
-        return *reinterpret_cast<const uint2*>(kp_row + (int64_t)(kgb + min(gi, n_groups - 1)) * kD + 2 * lane);
+        return stream_load8(kp_row + (int64_t)(kgb + min(gi, n_groups - 1)) * kD + 2 * lane);
     };
 
     float m[NQ], lsum[NQ], o[NQ][8], oz[NQ];   // oz: sum of p*z of the lane's tokens and channel group
@@ -188,7 +193,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
                     const uint32_t d0 = cur.kc[h].x, d1 = cur.kc[h].y;
                     const v4i bop = {(int)(d0 & 0x0F0F0F0Fu), (int)((d0 >> 4) & 0x0F0F0F0Fu), (int)(d1 & 0x0F0F0F0Fu),
                                      (int)((d1 >> 4) & 0x0F0F0F0Fu)};
-                    const uint8_t* ap = mrow < 4 * NQ ? &sh_dg[wave][mrow >> 2][mrow & 3][kb + 4 * h][0] : sh_zero;
+                    const uint8_t* ap = mrow < 4 * NQ ? &sh_dg[wave][mrow >> 2][mrow & 3][2 * kb + h][0] : sh_zero;
                     cacc = __builtin_amdgcn_mfma_i32_16x16x64_i8(*reinterpret_cast<const v4i*>(ap), bop, cacc, 0, 0, 0);
                 }
                 load_k(cur, it + 1);
@@ -223,11 +228,11 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
                     if (hr == r) {
                         const float p = exp2_fast(lg - m[r]);
                         lsum[r] += p;   // the lanes of head r's row, one token each
-                        pw[r * kQ4Tok + mrow] = p;
+                        pw[r * kQ4Tok + 4 * (mrow & 3) + (mrow >> 2)] = p;   // token mrow at 4 (mrow % 4) + mrow / 4
                     }
                 }
                 wave_sync();
-                // ---- P.V: tokens 4vg..4vg+3, channels 8vc..8vc+7
+                // ---- P.V: tokens vg + 4u (u = 0..3; their weights sit at 4vg + u), channels 8vc..8vc+7
                 float pv[NQ][4];
 #pragma unroll
                 for (int r = 0; r < NQ; ++r) {

@@ -67,12 +67,13 @@ __device__ __forceinline__ uint32_t f2h(float f) {   // v_cvt_f16_f32: RNE, subn
     return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
-// Loads with the non-temporal hint, for cache streams read once per call.  Where they pay is
-// measured per kernel: the 2-bit single-query and uniform query-group attention use them (the
-// long-context call 11% faster); the 4-bit, pre-RoPE, fp16 and ragged kernels and the prefill
-// quantizers measured slower with them and keep plain loads (the query-group calls of the
-// 4-bit and pre-RoPE kernels re-read a kv head from several workgroups, which the hint
-// keeps from the caches).
+// Loads with the non-temporal hint, for cache streams read once per call.  They pay where each
+// load instruction reads whole cache lines: the 2-bit single-query and uniform query-group
+// attention (the long-context call 11% faster) and the 4-bit attention (once its loads read
+// whole rows: 11% faster).  Where a line is split between instructions the hint lets it go
+// before the second one and the line is read twice: the pre-RoPE, fp16 and ragged kernels and
+// the prefill quantizers measured slower with it and keep plain loads (the pre-RoPE kernel's
+// query-group calls also re-read a kv head from several workgroups).
 typedef uint32_t u32x4_nt __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_nt __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint4 stream_load16(const void* p) {
