@@ -63,8 +63,9 @@ __device__ __forceinline__ uint32_t code2_of(float x, float mn, float t1, float 
 }
 
 // The same rule on the fp16 inputs themselves, two at a time.  The thresholds are the exact
-// binary32 products t1 = s/2, t2 = 3s/2, t3 = 5s/2 (s has 11 significant bits, so the
-// neighbours above reduce to these), and each step is [fl(x - mn) > s/2], [fl(x - mn) > u2]
+// binary32 products t1 = s/2, t2 = 3s/2, t3 = 5s/2 (s has 11 significant bits, so the binary32
+// neighbours of (0.5 + 2^-25)s, (1.5 - 2^-24)s and (2.5 + 2^-23)s are these products
+// themselves), and each step is [fl(x - mn) > s/2], [fl(x - mn) > u2]
 // (u2 the binary32 below 3s/2) or [fl(x - mn) > 5s/2]: monotone in x, so it holds exactly for
 // the fp16 x above one fp16 bound V.  fl(y) <= u iff y <= u + ulp(u)/2 when u is even (s/2
 // and 5s/2 are: the midpoint's tie rounds to them) and y < u + ulp(u)/2 when u is odd (u2:
@@ -76,7 +77,9 @@ __device__ __forceinline__ uint32_t code2_of(float x, float mn, float t1, float 
 // one step down where that overshoots.  A constant group (s = 0) gets V = inf.  Then x > V is
 // the sign of the fp16 difference V - x: rounding keeps the sign of a nonzero difference
 // (overflow to inf and underflow to -0 included), equal values give +0, and V is never -0.
-// So a pair of codes is three packed fp16 subtractions, three packed shifts and one add.
+// So a pair of codes is three packed fp16 subtractions, three packed shifts and one add.  A
+// restatement of these bounds gives the division's code for every finite fp16 minimum and
+// every positive fp16 scale (tests/test_code_bounds.py checks a spread of them on the CPU).
 __device__ __forceinline__ uint32_t prev_f16(uint32_t h) {   // the fp16 below h (h not -inf)
     return (h & 0x7fffu) == 0 ? 0x8001u : ((h & 0x8000u) ? h + 1u : h - 1u);
 }
