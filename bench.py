@@ -518,7 +518,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the decode hot path shards "
-              "by batch or kv head with no communication, see DESIGN.md.", file=sys.stderr)
+              "by batch or kv head with no communication.", file=sys.stderr)
         sys.exit(2)
 
     from kv_cache_bit_quantize_amd import kivi, synth

@@ -121,14 +121,12 @@ def summarize(args):
     with open(args.out + ".md", "w") as f:
         f.write(f"# HBM traffic of decode attention, {meta['workload']}\n\n")
         f.write("Commands (from the repository root, on one MI355X):\n\n```\n")
-        for c in ("FETCH_SIZE", "WRITE_SIZE"):
-            d = "fetch" if c == "FETCH_SIZE" else "write"
-            f.write(f"rocprofv3 --pmc {c} --output-format csv -d gpurun_out/traffic/{d} -o run -- "
+        for c, path in (("FETCH_SIZE", args.fetch_csv), ("WRITE_SIZE", args.write_csv)):
+            f.write(f"rocprofv3 --pmc {c} --output-format csv -d {os.path.dirname(path)} -o run -- "
                     f"python3 -m kv_cache_bit_quantize_amd.traffic run --workload {meta['workload']} "
-                    f"--meta gpurun_out/traffic/meta.json\n")
-        f.write("python3 -m kv_cache_bit_quantize_amd.traffic summarize gpurun_out/traffic/fetch/run_counter_collection.csv "
-                f"gpurun_out/traffic/write/run_counter_collection.csv --meta gpurun_out/traffic/meta.json "
-                f"--out {args.out}\n```\n\n")
+                    f"--meta {args.meta}\n")
+        f.write(f"python3 -m kv_cache_bit_quantize_amd.traffic summarize {args.fetch_csv} {args.write_csv} "
+                f"--meta {args.meta} --out {args.out}\n```\n\n")
         f.write("| counter | attention KiB/dispatch | 1 GiB copy KiB/dispatch | scale | attention bytes/launch |\n")
         f.write("|---|---|---|---|---|\n")
         for c in ("FETCH_SIZE", "WRITE_SIZE"):
@@ -270,11 +268,11 @@ def main():
     r = sub.add_parser("run")
     r.add_argument("--workload", default="long-128k")
     r.add_argument("--launches", type=int, default=5)
-    r.add_argument("--meta", default="gpurun_out/traffic/meta.json")
+    r.add_argument("--meta", default="prof/traffic/meta.json")
     s = sub.add_parser("summarize")
     s.add_argument("fetch_csv")
     s.add_argument("write_csv")
-    s.add_argument("--meta", default="gpurun_out/traffic/meta.json")
+    s.add_argument("--meta", default="prof/traffic/meta.json")
     s.add_argument("--out", required=True)
     c = sub.add_parser("counters")
     c.add_argument("csv", nargs="+")

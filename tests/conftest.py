@@ -51,14 +51,15 @@ def guard_bands(request):
 
 
 def pytest_sessionfinish(session, exitstatus):
-    """Write the worst attention errors seen by the GPU parity tests (if any ran)."""
+    """Write the worst attention errors seen by the GPU parity tests (if any ran) to the json
+    file KIVI_PARITY_REPORT names (nothing when it is unset)."""
     try:
         from kivi_testlib import REPORT
     except Exception:
         return
-    if REPORT:
+    path = os.environ.get("KIVI_PARITY_REPORT")
+    if REPORT and path:
         import json
-        out = os.path.join(ROOT, "gpurun_out")
-        os.makedirs(out, exist_ok=True)
-        with open(os.path.join(out, "parity_report.json"), "w") as f:
+        os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
+        with open(path, "w") as f:
             json.dump(dict(sorted(REPORT.items())), f, indent=1)
