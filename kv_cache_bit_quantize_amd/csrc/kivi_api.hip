@@ -51,7 +51,7 @@ constexpr int64_t kTargetBlocksSingle = 256;   // single-query 2-bit workgroups 
 constexpr int64_t kTargetBlocksQ4 = 1024;      // single-query 4-bit workgroups (4 waves): four per CU
 // 4-bit query-group workgroups (four query heads, 106 VGPRs): two rounds of four per CU.  On
 // gqa-mistral-7b (512 kv rows) one split took 233 us, 2 / 4 / 6 / 8 splits 194-205 / 183-199 /
-// 189-203 / 200 us on two boxes, 12 splits 234 us
+// 189-203 / 200 us on two GPUs, 12 splits 234 us
 constexpr int64_t kTargetBlocksQ4Group = 2048;
 constexpr int kMinGroupsPerSplit = 8;
 constexpr int kMinGroupsPerSplitSingle = 2 * kSqWaves;   // a pair of tiles for every wave
@@ -149,7 +149,7 @@ int32_t auto_splits_for(const kivi_cache* c, int32_t q_heads, int64_t groups, in
     }
     if (code_bits(c) == 4) {   // 4-wave workgroups, a key group for every wave
         // one query head: four workgroups per CU (88 VGPRs; at 131,072 tokens 32 splits took
-        // 124-128 us against 129-146 us for 24 on three boxes)
+        // 124-128 us against 129-146 us for 24 on three GPUs)
         target = group ? kTargetBlocksQ4Group : kTargetBlocksQ4;
         min_tiles = 4 * (c->group / kG);
     }

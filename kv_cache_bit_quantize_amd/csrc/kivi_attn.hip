@@ -154,7 +154,7 @@ __global__ __launch_bounds__(64 * W) void attn_split_kernel(AttnArgs a) {
         return half == 0 ? g0 : (g0 + 1 < g_hi ? g0 + 1 : g0);   // in-bounds address for an idle half
     };
     // the cache streams through with non-temporal loads: 403 MB at the 131,072-token context in
-    // 64.1-64.4 us against 72.4-72.6 us with plain loads (same box, same outputs)
+    // 64.1-64.4 us against 72.4-72.6 us with plain loads (same GPU, same outputs)
     auto load_kp = [&](Loads& L, int it) {
         L.kp = stream_load16(kp_row + (int64_t)(group_of(it, gh) / (GS / kG)) * kD + 4 * wl);
     };

@@ -27,7 +27,7 @@
 // ahead, all unconditionally (clamped past the end).  Each code load instruction reads whole
 // rows (a lane 16 bytes of a token's key codes, four lanes the row; a value load four
 // consecutive rows), so the codes and key pairs stream with non-temporal loads: 107.5-108 us
-// at the 131,072-token context against 121.3-121.7 us with plain loads of half rows (same box;
+// at the 131,072-token context against 121.3-121.7 us with plain loads of half rows (same GPU;
 // the hint on loads that split rows between instructions had been 9% slower).
 #include <hip/hip_ext.h>
 
