@@ -200,3 +200,27 @@ def test_long_context_sampled_rows():
     ref_out, ref_lse = rc.decode_attn(bits(q[:, rows].contiguous()), SM)
     assert_attn_close(out[:, rows], ref_out, what="4-bit long-128k sampled rows")
     assert_lse_close(lse[:, rows], ref_lse)
+
+
+def test_gqa_mistral_sampled_kv_rows():
+    """The gqa-mistral-7b shape (64 sequences, 32 query / 8 kv heads, 8,064 history + 128
+    residual tokens) in 4-bit codes, at the call's own split count (four query heads per
+    workgroup): the four query heads of kv rows 0, 261 and 511 against the oracle."""
+    dev = gpu_or_skip()
+    kivi = _kivi()
+    w = synth.WORKLOADS["gqa-mistral-7b"]
+    k, v = synth.prefill_kv(w, device=dev)
+    cache = kivi.Cache(w.batch, w.kv_heads, w.token_cap, device=dev, bits=4)
+    kivi.kivi_prefill(k, v, w.n_quant, cache)
+    assert kivi.kivi_decode_attn_splits(cache, w.q_heads) > 1
+    q = synth.query(w, device=dev)
+    out, lse = kivi.kivi_decode_attn(cache, q, SM, lse=True)
+    torch.cuda.synchronize()
+    ratio = w.q_heads // w.kv_heads
+    for kvrow in (0, 261, 511):
+        b, h = divmod(kvrow, w.kv_heads)
+        rc = ref_cache(1, 1, w.token_cap, k[b:b + 1, h:h + 1].cpu(), v[b:b + 1, h:h + 1].cpu(), w.n_quant, bits=4)
+        qs = q[b:b + 1, ratio * h:ratio * (h + 1)].contiguous()
+        ref_out, ref_lse = rc.decode_attn(bits(qs), SM)
+        assert_attn_close(out[b:b + 1, ratio * h:ratio * (h + 1)], ref_out, what=f"4-bit gqa-mistral-7b kv row {kvrow}")
+        assert_lse_close(lse[b:b + 1, ratio * h:ratio * (h + 1)], ref_lse)
