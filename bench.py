@@ -240,7 +240,9 @@ def rope_measure(kivi, synth, w, k, v, queries, steps, warmup, base=10000.0):
     kivi.kivi_prefill(k, v, nq, cache)
     us = time_attention(kivi, cache, queries, synth.SM_SCALE_D128, steps, warmup, rope_base=base)
     b = attn_bytes(w, nq, w.context - nq)
-    res = {"kernel": "attn_rope_kernel", "rope_base": base, "n_quant": nq, "n_res": w.context - nq,
+    ratio = w.q_heads // w.kv_heads
+    kernel = "attn_rope_group_kernel" if ratio % 2 == 0 else "attn_rope_kernel"   # 2-bit, uniform batch
+    res = {"kernel": kernel, "rope_base": base, "n_quant": nq, "n_res": w.context - nq,
            "splits": kivi.kivi_decode_attn_rope_splits(cache, w.q_heads), "decode_attn_us": round(us, 2),
            "bytes_per_launch": int(b), "achieved": round(b / us / 1e3, 1), "unit": "GB/s",
            "frac": round(b / us / 1e3 / PEAK_HBM_GBS, 4)}

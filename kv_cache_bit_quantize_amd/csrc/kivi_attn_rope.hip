@@ -20,8 +20,9 @@
 // its cosine and sine taken in binary32.  The per-pair products make this path bound by the
 // vector units rather than by HBM.
 //
-// Work split: grid (splits, query rows), one query head per workgroup (a GQA group's heads
-// each read their KV head); a split owns whole key groups, each of its 4 waves a contiguous
+// Work split: grid (splits, query rows), one query head per workgroup (4-bit codes, ragged
+// batches and odd GQA ratios; a GQA group's heads each read their KV head; the query-group
+// form further down takes the rest); a split owns whole key groups, each of its 4 waves a contiguous
 // run of them, 16 tokens per wave-iteration in two passes of 8 (lane 8t + k: token t of the
 // pass, pairs [8k, 8k+8)).  P.V follows the code layout of the cache's width: 2-bit value
 // tiles (lane: one 8-token row of chunks, 4 channels), 4-bit token rows (lane: 4 tokens, 8
@@ -463,12 +464,371 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     finish_block<1>(a, rs.splits, split, qrow, tag, sh_o, sh_m, sh_l);
 }
 
+// Query-group form for 2-bit codes and a uniform batch: the NQ query heads qrow0..qrow0+NQ-1
+// of one kv head in one workgroup, which dequantizes and turns each key once for all of them.
+// The group's folded products then carry no query: with E0 = exp(i*t0*w), U = E0*(z_i +
+// i*z_{i+64}), V = E0*s_i and X = i*E0*s_{i+64}, a token's turned key pair is R = (U + V*c +
+// X*c') * exp(i*d*w) (four fmas and a complex product), and head h adds Re(conj(Q_h)*R) =
+// q_{h,i}*Re R + q_{h,i+64}*Im R (two fmas) to its logit: 10 + 2*NQ operations per pair and
+// token with the two code conversions, against 8 for each head in a workgroup of its own.
+// A lane's 2*NQ partial logits per 16 tokens (two tokens, NQ heads) are summed over the
+// token's 8 lanes by halving exchanges (token_head_sums), after which each lane holds one
+// (token, head) sum.  P.V shares each value tile's 8 matrix instructions among the heads:
+// head h's weights go in row 4*(v%4) + h of block v's A operand, so that the accumulators'
+// register h is head h.
+
+// Sums over the 8 lanes of a token (k8 = lane & 7) of 2*NQ values, v[ps][h] = token ps's
+// partial logit of head h.  Each step a lane keeps half of its values and adds its partner's
+// copies of them, while the partner keeps the other half: partners k8 ^ 7 (the half-row
+// mirror), then k8 ^ 1, then k8 ^ 2 (for two heads a plain sum over k8 ^ 2).  Index n = 2h + ps
+// ends in the lane with n = k8 (four heads) or n = 2*(k8 >> 2) + (k8 & 1) (two heads).
+template <int NQ>
+__device__ __forceinline__ float token_head_sums(const float (&v)[2][NQ], int k8) {
+    const bool b0 = k8 & 1, b1 = k8 & 2, b2 = k8 & 4;
+    if constexpr (NQ == 4) {
+        float w[4];   // w[m]: index m + 4*b2
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const float lo = v[m & 1][m >> 1], hi = v[m & 1][(m >> 1) + 2];
+            w[m] = (b2 ? hi : lo) + hmirror_f(b2 ? lo : hi);
+        }
+        float x[2];   // x[u]: index 4*b2 + 2u + b0
+#pragma unroll
+        for (int u = 0; u < 2; ++u) x[u] = (b0 ? w[2 * u + 1] : w[2 * u]) + xor1_f(b0 ? w[2 * u] : w[2 * u + 1]);
+        return (b1 ? x[1] : x[0]) + xor2_f(b1 ? x[0] : x[1]);
+    } else {
+        float w[2];   // w[m]: index m + 2*b2
+#pragma unroll
+        for (int m = 0; m < 2; ++m) w[m] = (b2 ? v[m][1] : v[m][0]) + hmirror_f(b2 ? v[m][0] : v[m][1]);
+        const float x = (b0 ? w[1] : w[0]) + xor1_f(b0 ? w[0] : w[1]);
+        return x + xor2_f(x);
+    }
+}
+
+template <int GS, int NQ>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(GS == 128 ? 1 : 2))) void attn_rope_group_kernel(AttnArgs a) {
+    static_assert(NQ == 2 || NQ == 4, "two or four query heads per workgroup");
+    constexpr int kIt = GS / kRpTok;   // iterations per key group
+    constexpr int NH = NQ / 2;         // P.V weights: heads per lane, lane >> 5 picks which
+    __shared__ double sh_w[kRpPairs];
+    __shared__ __align__(16) float2 sh_ed[GS][kRpPairs];
+    __shared__ __align__(16) float sh_f[kWaves][6][kRpPairs + 8];
+    __shared__ __align__(16) float sh_lg[kWaves][NQ][kG];
+    __shared__ __align__(16) uint8_t sh_wt[kWaves][NQ][4 * 64];
+    __shared__ __align__(16) uint8_t sh_zr[4 * 64];
+    __shared__ __align__(16) float sh_o[NQ][kSlots][kD];
+    __shared__ float sh_m[NQ][kSlots], sh_l[NQ][kSlots];
+
+    const int split = blockIdx.x;
+    const int64_t qrow0 = (int64_t)blockIdx.y * NQ;
+    const int64_t kvrow = (int64_t)((uint32_t)qrow0 / (uint32_t)a.ratio);
+    if (a.k_new != nullptr && split == 0 && (uint32_t)qrow0 % (uint32_t)a.ratio == 0) store_new_token(a, kvrow);
+    const TagLoads<NQ> tag_v = partial_tag<NQ>(a, qrow0);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int t8 = lane >> 3, k8 = lane & 7;
+
+    const RowState rs = row_state(a);
+    const int n_kg = rs.n_quant / GS;
+    const int per_split = (n_kg + rs.splits - 1) / rs.splits;
+    const int kg_lo = min(n_kg, split * per_split), kg_hi = min(n_kg, kg_lo + per_split);
+    const int cnt = kg_hi - kg_lo;
+    const int per_wave = (cnt + kWaves - 1) / kWaves;
+    const int kgb = kg_lo + min(cnt, wave * per_wave);
+    const int n_groups = kg_lo + min(cnt, (wave + 1) * per_wave) - kgb;
+    const int n_it = n_groups * kIt;
+
+    // the lane's pairs 8k8..8k8+7 of every head: Q = q_i + i*q_{i+64}
+    float qr[NQ][8], qi[NQ][8];
+#pragma unroll
+    for (int h = 0; h < NQ; ++h)
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+            qr[h][jj] = h2f(a.q[(qrow0 + h) * kD + 8 * k8 + jj]);
+            qi[h][jj] = h2f(a.q[(qrow0 + h) * kD + kRpPairs + 8 * k8 + jj]);
+        }
+
+    const int64_t tok0 = kvrow * (int64_t)a.token_cap;
+    const uint8_t* kc_row = a.k_codes + tok0 * kRowBytes;
+    const uint8_t* vc_row = a.v_codes + tok0 * kRowBytes;
+    const uint32_t* kp_row = reinterpret_cast<const uint32_t*>(a.k_sz) + kvrow * (int64_t)(a.token_cap / GS) * kD;
+    const uint32_t* vp_row = reinterpret_cast<const uint32_t*>(a.v_sz) + tok0 * (kD / GS);
+    const int t_b = kgb * GS;
+    auto tok = [&](int it) { return t_b + min(it, n_it - 1) * kRpTok; };   // clamped past the end
+
+    // key codes of the two pass tokens, as in the one-head kernel
+    struct KLoad { uint32_t lo[2], hi[2]; };
+    auto load_k = [&](KLoad& L, int it) {
+#pragma unroll
+        for (int ps = 0; ps < 2; ++ps) {
+            const uint32_t t = (uint32_t)(tok(it) + 8 * ps + t8);
+            const uint32_t off = (t / kG) * kTileBytes + (16 * (k8 >> 1) + t % 16) * 16 + 8 * ((t % kG) / 16);
+            const uint2 x = *reinterpret_cast<const uint2*>(kc_row + off);
+            L.lo[ps] = x.x;
+            L.hi[ps] = x.y;
+        }
+    };
+    // value tile of iteration it: lane l holds chunk l of the codes and token l % 32's pairs
+    struct VLoad { uint32_t c[4]; uint32_t p[4]; };
+    auto load_v = [&](VLoad& L, int it) {
+        const uint32_t t0 = (uint32_t)tok(it) & ~(uint32_t)(kG - 1);
+        const uint4 x = reinterpret_cast<const uint4*>(vc_row + (t0 / kG) * kTileBytes)[lane];
+        const uint4 y = load_value_pairs<GS, false>(vp_row + value_pair_index<GS>((int64_t)t0 + (lane & 31), 0));
+        L.c[0] = x.x;
+        L.c[1] = x.y;
+        L.c[2] = x.z;
+        L.c[3] = x.w;
+        L.p[0] = y.x;
+        L.p[1] = y.y;
+        L.p[2] = y.z;
+        L.p[3] = y.w;
+    };
+    struct PLoad { uint32_t lo, hi; };
+    auto load_kp = [&](PLoad& L, int gi) {
+        const uint32_t* g = kp_row + (int64_t)(kgb + min(gi, n_groups - 1)) * kD;
+        L.lo = g[lane];
+        L.hi = g[kRpPairs + lane];
+    };
+    auto wave_sync = []() {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+
+    // running maxima (wave-uniform), P.V accumulators (register h: head h), and per lane the
+    // sums and p*zero shares of heads NH*(lane >> 5) + u
+    float m[NQ];
+#pragma unroll
+    for (int h = 0; h < NQ; ++h) m[h] = -INFINITY;
+    v4f cv[2] = {(v4f){0.0f, 0.0f, 0.0f, 0.0f}, (v4f){0.0f, 0.0f, 0.0f, 0.0f}};
+    float zk[NH][4], ls[NH], vs = 0.0f;
+#pragma unroll
+    for (int u = 0; u < NH; ++u) {
+        ls[u] = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) zk[u][k] = 0.0f;
+    }
+    const bool hp = lane >= 32;
+    if (threadIdx.x < 16) reinterpret_cast<uint4*>(sh_zr)[threadIdx.x] = make_uint4(0, 0, 0, 0);
+
+    KLoad kl;
+    VLoad vl;
+    PLoad pn;
+    if (n_groups > 0) {
+        load_k(kl, 0);
+        load_kp(pn, 0);
+    }
+    if (threadIdx.x < kRpPairs) sh_w[threadIdx.x] = pow(a.rope_base, -2.0 * (double)threadIdx.x / (double)kD);
+    __syncthreads();
+    for (int i = threadIdx.x; i < GS * kRpPairs; i += kBlock) sh_ed[i / kRpPairs][i % kRpPairs] = turn((double)(i / kRpPairs) * sh_w[i % kRpPairs]);
+    __syncthreads();
+
+    uint32_t tag;
+    if (n_groups > 0) {
+        const double w_lane = sh_w[lane];
+        const int f_slot = lane + 4 * (lane >> 5), f_run = 8 * k8 + 4 * (k8 >> 2);
+        const int h_lane = NQ == 4 ? k8 >> 1 : k8 >> 2;   // the (token, head) sum a lane ends with
+        const bool lg_store = NQ == 4 || (k8 & 2) == 0;
+        tag = settle_tag(tag_v);
+        for (int gi = 0; gi < n_groups; ++gi) {
+            set_priority_for(n_groups - gi);
+            {
+                const float2 e = turn((double)((kgb + gi) * GS) * w_lane);   // E0 = exp(i*t0*w)
+                const float slo = h2f(pn.lo & 0xffffu), zlo = h2f(pn.lo >> 16);
+                const float shi = h2f(pn.hi & 0xffffu), zhi = h2f(pn.hi >> 16);
+                float(*f)[kRpPairs + 8] = sh_f[wave];
+                f[0][f_slot] = fmaf(e.x, zlo, -e.y * zhi);   // U = E0 * (zlo + i*zhi)
+                f[1][f_slot] = fmaf(e.x, zhi, e.y * zlo);
+                f[2][f_slot] = e.x * slo;                    // V = E0 * slo
+                f[3][f_slot] = e.y * slo;
+                f[4][f_slot] = -e.y * shi;                   // X = i * E0 * shi
+                f[5][f_slot] = e.x * shi;
+            }
+            load_kp(pn, gi + 1);
+            wave_sync();
+            float ur[8], ui[8], vr[8], vi[8], xr[8], xi[8];
+            {
+                auto run = [&](int c, float (&d)[8]) {
+                    const float4 lo = *reinterpret_cast<const float4*>(&sh_f[wave][c][f_run]);
+                    const float4 hi = *reinterpret_cast<const float4*>(&sh_f[wave][c][f_run + 4]);
+                    d[0] = lo.x; d[1] = lo.y; d[2] = lo.z; d[3] = lo.w;
+                    d[4] = hi.x; d[5] = hi.y; d[6] = hi.z; d[7] = hi.w;
+                };
+                run(0, ur); run(1, ui); run(2, vr); run(3, vi); run(4, xr); run(5, xi);
+            }
+            wave_sync();
+#pragma unroll 2
+            for (int j = 0; j < kIt; ++j) {
+                const int it = gi * kIt + j;
+                if (j & 1) load_v(vl, it);
+                // ---- partial logits of tokens t8 and 8 + t8, the lane's 8 pairs, every head
+                float part[2][NQ];
+#pragma unroll
+                for (int ps = 0; ps < 2; ++ps) {
+                    float c1[8], c2[8];
+                    codes8<2>(kl.lo[ps], k8 & 1, c1);
+                    codes8<2>(kl.hi[ps], k8 & 1, c2);
+                    const float2* ed = &sh_ed[kRpTok * j + 8 * ps + t8][8 * k8];
+#pragma unroll
+                    for (int h = 0; h < NQ; ++h) part[ps][h] = 0.0f;
+#pragma unroll
+                    for (int jj = 0; jj < 8; ++jj) {
+                        const float2 e = ed[jj];
+                        const float kr = fmaf(xr[jj], c2[jj], fmaf(vr[jj], c1[jj], ur[jj]));
+                        const float ki = fmaf(xi[jj], c2[jj], fmaf(vi[jj], c1[jj], ui[jj]));
+                        const float rr = fmaf(kr, e.x, -ki * e.y);   // R = (kr + i*ki) * exp(i*d*w)
+                        const float ri = fmaf(kr, e.y, ki * e.x);
+#pragma unroll
+                        for (int h = 0; h < NQ; ++h) part[ps][h] = fmaf(qr[h][jj], rr, fmaf(qi[h][jj], ri, part[ps][h]));
+                    }
+                }
+                load_k(kl, it + 1);
+                const float lg = token_head_sums<NQ>(part, k8) * a.sm_log2;   // token 8(k8&1) + t8, head h_lane
+                if (lg_store) sh_lg[wave][h_lane][16 * (j & 1) + 8 * (k8 & 1) + t8] = lg;
+                // ---- running maxima: over the lanes that hold a head's 16 sums, then per head
+                float mx = fmax_ieee(lg, perm_f<0xB1>(lg));
+                if constexpr (NQ == 2) mx = fmax_ieee(mx, perm_f<0x4E>(mx));
+                mx = fmax_ieee(mx, perm_f<0x128>(mx));   // lane (i+8)%16 of the row
+                mx = fmax_ieee(mx, xor16_f(mx));
+                float al[NQ];
+                bool moved = false;
+#pragma unroll
+                for (int h = 0; h < NQ; ++h) {
+                    const int src = NQ == 4 ? 2 * h : 4 * h;
+                    const float mnew = fmax_ieee(m[h], fmax_ieee(readlane_f(mx, src), readlane_f(mx, 32 + src)));
+                    al[h] = mnew == m[h] ? 1.0f : (m[h] == -INFINITY ? 0.0f : exp2_fast(m[h] - mnew));
+                    moved |= mnew != m[h];
+                    m[h] = mnew;
+                }
+                if (moved) {
+#pragma unroll
+                    for (int h = 0; h < NQ; ++h) {
+                        cv[0][h] *= al[h];
+                        cv[1][h] *= al[h];
+                    }
+#pragma unroll
+                    for (int u = 0; u < NH; ++u) {
+                        const float a_u = hp ? al[NH + u] : al[u];
+                        ls[u] *= a_u;
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) zk[u][k] *= a_u;
+                    }
+                }
+                wave_sync();
+                // ---- P.V of the tile, once its 32 logits are in
+                if (j & 1) {
+                    const int tt = lane & 31, mrow = lane & 15, kgrp = lane >> 4;
+                    float p[NH];
+#pragma unroll
+                    for (int u = 0; u < NH; ++u) {
+                        const float mh = hp ? m[NH + u] : m[u];
+                        p[u] = exp2_fast(sh_lg[wave][NH * (int)hp + u][tt] - mh);
+                        ls[u] += p[u];
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) zk[u][k] = fmaf(p[u], h2f(vl.p[k] >> 16), zk[u][k]);
+                    }
+                    const float smax = h2f(max_u16x2(max_u16x2(vl.p[0], vl.p[1]), max_u16x2(vl.p[2], vl.p[3])) & 0xffffu);
+                    if (__builtin_amdgcn_ballot_w64(smax * vs > 2048.0f || vs == 0.0f)) {
+                        const float gm = wave_max_xor(smax, 1, 32);
+                        const float nvs = __builtin_ldexpf(1.0f, 11 - __builtin_amdgcn_frexp_expf(gm));
+                        if (vs != 0.0f && nvs < vs) {
+                            const float r = nvs / vs;
+                            cv[0] *= r;
+                            cv[1] *= r;
+                        }
+                        if (vs == 0.0f || nvs < vs) vs = nvs;
+                    }
+                    const int w_off = (tt >> 3) * 16 + (((tt & 3) << 1) | ((tt >> 2) & 1)) * 2;
+                    const float sc = __builtin_ldexpf(16.0f, -2 * (tt & 3)) * vs;
+#pragma unroll
+                    for (int u = 0; u < NH; ++u) {
+                        uint8_t* wt = &sh_wt[wave][NH * (int)hp + u][0];
+                        const float f = p[u] * sc;
+#pragma unroll
+                        for (int k = 0; k < 4; ++k)
+                            *reinterpret_cast<_Float16*>(wt + w_off + k * 64) = (_Float16)(f * h2f(vl.p[k] & 0xffffu));
+                    }
+                    wave_sync();
+                    constexpr uint32_t kF0 = 0x00030003u, kF1 = 0x000C000Cu, kF2 = 0x00300030u, kF3 = 0x00C000C0u;
+                    const int hr = mrow & 3;
+                    const uint8_t* wrow = hr < NQ ? &sh_wt[wave][hr < NQ ? hr : 0][0] : sh_zr;
+#pragma unroll
+                    for (int v = 0; v < 8; ++v) {
+                        const uint32_t x = (v & 1) ? vl.c[v >> 1] >> 8 : vl.c[v >> 1];
+                        const v8h bop = __builtin_bit_cast(v8h, make_uint4(x & kF0, x & kF1, x & kF2, x & kF3));
+                        const uint8_t* arow = ((mrow >> 2) == (v & 3) ? wrow : sh_zr) + (v >> 1) * 64 + 16 * kgrp;
+                        const v8h aop = *reinterpret_cast<const v8h*>(arow);
+                        cv[v >> 2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop, cv[v >> 2], 0, 0, 0);
+                    }
+                }
+                wave_sync();
+            }
+        }
+    } else {
+        tag = settle_tag(tag_v);
+    }
+
+    // ---- the wave's states: o = P.V * 2^20 / vs + sum p*zero; lane l holds channels
+    // 16g + c and 16(g + 4) + c (g = l >> 4, c = l & 15) of every head
+    {
+        float zt[NQ][4], lt[NQ];
+#pragma unroll
+        for (int u = 0; u < NH; ++u) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float s = wave_sum_xor(zk[u][k], 1, 16);   // over each half-wave
+                zt[u][k] = readlane_f(s, 0);
+                zt[NH + u][k] = readlane_f(s, 32);
+            }
+            const float s = wave_sum_xor(ls[u], 1, 16);
+            lt[u] = readlane_f(s, 0);
+            lt[NH + u] = readlane_f(s, 32);
+        }
+        const float inv = vs != 0.0f ? 1048576.0f / vs : 0.0f;
+        const int g = lane >> 4, c = lane & 15;
+#pragma unroll
+        for (int h = 0; h < NQ; ++h) {
+            sh_o[h][wave][16 * g + c] = fmaf(cv[0][h], inv, zt[h][g >> 1]);
+            sh_o[h][wave][16 * (g + 4) + c] = fmaf(cv[1][h], inv, zt[h][(g + 4) >> 1]);
+            if (lane == 0) {
+                sh_m[h][wave] = n_groups > 0 ? m[h] : -INFINITY;
+                sh_l[h][wave] = lt[h];
+            }
+        }
+    }
+    // ---- fp16 residual (split rs.res_split), keys turned at n_quant + i, head by head
+    __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+    for (int h = 0; h < NQ; ++h) {
+        float mr = -INFINITY, lr = 0.0f;
+        if (split == rs.res_split) {
+            __builtin_amdgcn_s_setprio(2);
+            residual_rope_states(a, rs, qrow0 + h, kvrow, wave, sh_w, &sh_o[h][kWaves + wave][0], mr, lr);
+            __builtin_amdgcn_s_setprio(0);
+        }
+        if (lane == 0) {
+            sh_m[h][kWaves + wave] = mr;
+            sh_l[h][kWaves + wave] = lr;
+        }
+    }
+    __syncthreads();
+    finish_block<NQ>(a, rs.splits, split, qrow0, tag, sh_o, sh_m, sh_l);
+}
+
 hipError_t launch_decode_attn_rope(const AttnArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
     const dim3 grid = attn_grid(a, a.q_rows);
 #define KIVI_ROPE(BITSv, RAGGEDv)                                                                                  \
     KIVI_BY_GROUP(a.group, hipExtLaunchKernelGGL((attn_rope_kernel<BITSv, GS, RAGGEDv>), grid, dim3(kBlock), 0, s, t0, t1, \
                                                  0, a))
     const bool ragged = a.seq_state != nullptr;
+    if (a.nq > 1) {   // (2-bit codes, uniform batch)
+        const dim3 ggrid = attn_grid(a, a.block_rows);
+        if (a.nq == 4)
+            KIVI_BY_GROUP(a.group, hipExtLaunchKernelGGL((attn_rope_group_kernel<GS, 4>), ggrid, dim3(kBlock), 0, s, t0, t1, 0, a))
+        else
+            KIVI_BY_GROUP(a.group, hipExtLaunchKernelGGL((attn_rope_group_kernel<GS, 2>), ggrid, dim3(kBlock), 0, s, t0, t1, 0, a))
+        return hipGetLastError();
+    }
     if (a.bits == 4) {
         if (ragged) KIVI_ROPE(4, true) else KIVI_ROPE(4, false)
     } else {

@@ -2,7 +2,8 @@
 kivi_ref_decode_attn_rope: keys dequantized, turned by the rotary embedding at their
 sequence positions, dense fp64 attention.  Bar: per row max |o_gpu - o_ref| / max |o_ref|
 <= 2e-3, lse within 2e-3 + 2^-18 |lse|.  Covers both code widths, the three group sizes,
-MHA and GQA, explicit split counts, caches with only history or only residual, a decode
+MHA and GQA (query-group ratios 4 and 2, whose 2-bit calls take a kv head's query heads in
+one workgroup, and ratio 3), explicit split counts, caches with only history or only residual, a decode
 loop whose flushes move the residual ring, another rotary base, and the 131,072-token
 shape (angles past 10^5 radians) on sampled rows, and ragged batches (each sequence turned at
 its own positions)."""
@@ -47,7 +48,7 @@ def _check(cache, rc, q, base=BASE, splits=0, rows=None, what=""):
 
 @pytest.mark.parametrize("code_bits", [2, 4])
 @pytest.mark.parametrize("G", [32, 64, 128])
-@pytest.mark.parametrize("q_heads,kv_heads,splits", [(4, 4, 0), (8, 2, 0), (6, 2, 3), (2, 2, 7)])
+@pytest.mark.parametrize("q_heads,kv_heads,splits", [(4, 4, 0), (8, 2, 0), (6, 2, 3), (2, 2, 7), (4, 2, 5)])
 def test_attention(code_bits, G, q_heads, kv_heads, splits):
     dev = gpu_or_skip()
     w = synth.small(seed=600 + G + q_heads + splits, batch=2, q_heads=q_heads, kv_heads=kv_heads,
@@ -171,3 +172,26 @@ def test_long_context_sampled_rows():
     ref_out, ref_lse = rc.decode_attn_rope(bits(q[:, rows].contiguous()), SM, BASE)
     assert_attn_close(out[:, rows], ref_out, what="rope long-128k sampled rows")
     assert_lse_close(lse[:, rows], ref_lse)
+
+
+def test_gqa_mistral_sampled_kv_rows():
+    """The gqa-mistral-7b shape (64 sequences, 32 query / 8 kv heads, 8,064 history + 128
+    residual tokens) in 2-bit codes at the call's own split count (four query heads per
+    workgroup): the four query heads of kv rows 0, 261 and 511 against the oracle."""
+    dev = gpu_or_skip()
+    kivi = _kivi()
+    w = synth.WORKLOADS["gqa-mistral-7b"]
+    k, v = synth.prefill_kv(w, device=dev)
+    cache = kivi.Cache(w.batch, w.kv_heads, w.token_cap, device=dev)
+    kivi.kivi_prefill(k, v, w.n_quant, cache)
+    q = synth.query(w, device=dev)
+    out, lse = kivi.kivi_decode_attn_rope(cache, q, SM, BASE, lse=True)
+    torch.cuda.synchronize()
+    ratio = w.q_heads // w.kv_heads
+    for kvrow in (0, 261, 511):
+        b, h = divmod(kvrow, w.kv_heads)
+        rc = ref_cache(1, 1, w.token_cap, k[b:b + 1, h:h + 1].cpu(), v[b:b + 1, h:h + 1].cpu(), w.n_quant)
+        qs = q[b:b + 1, ratio * h:ratio * (h + 1)].contiguous()
+        ref_out, ref_lse = rc.decode_attn_rope(bits(qs), SM, BASE)
+        assert_attn_close(out[b:b + 1, ratio * h:ratio * (h + 1)], ref_out, what=f"rope gqa-mistral-7b kv row {kvrow}")
+        assert_lse_close(lse[b:b + 1, ratio * h:ratio * (h + 1)], ref_lse)
