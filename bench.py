@@ -20,6 +20,8 @@ sets its group sizes, empty skips it), attention over the same context stored as
 pre-RoPE keys, turned at their positions inside the kernel ("pre_rope"; --no-rope skips it),
 and the two prefill quantizers over the same context ("prefill_quantize": one
 kivi_quantize_k_per_channel and one kivi_quantize_v_per_token call each, one kernel per call).
+The other workloads ("workloads"; --no-workloads skips them) are timed by their decode steps,
+and the grouped-query one also by its pre-RoPE call ("pre_rope" of its entry).
 """
 import argparse
 import json
@@ -400,6 +402,11 @@ def decode_steps_measure(kivi, synth, name, dev, steps, warmup, flush_buf, sink)
         res[mode] = r
         del cache, ws
     res["kernel"] = "attn_split_kernel (append fused)" if w.q_heads == w.kv_heads else "attn_gqa_kernel (append fused)"
+    if w.q_heads != w.kv_heads:
+        # the same prefill as pre-RoPE keys: the query-group form of the pre-RoPE call
+        qs = [synth.query(w, step=s + 1, device=dev) for s in range(warmup + steps)]
+        res["pre_rope"] = rope_measure(kivi, synth, w, k, v, qs, steps, warmup)
+        del qs
     del k, v
     return res
 
