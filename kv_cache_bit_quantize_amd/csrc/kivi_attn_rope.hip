@@ -15,10 +15,11 @@
 // group).  Once per group a lane forms, for each of its pairs, W = conj(Q)*exp(i*t0*w) and
 // the folded products U = W*(z_i + i*z_{i+64}), V = W*s_i, X = i*W*s_{i+64}, so that for a
 // token with codes (c, c') W*K = U + V*c + X*c'; per token it then adds
-// Re((U + V*c + X*c') * exp(i*d*w)), with exp(i*d*w) from an LDS table.  The turn of the
-// group start is reduced modulo 2*pi in binary64 (positions reach 2^17 and more radians),
-// its cosine and sine taken in binary32.  The per-pair products make this path bound by the
-// vector units rather than by HBM.
+// Re((U + V*c + X*c') * exp(i*d*w)), with exp(i*d*w) from an LDS table.  Where the turn of
+// a group start is taken from its angle, the angle is reduced modulo 2*pi in binary64
+// (positions reach 2^17 and more radians) and its cosine and sine taken in binary32; a wave's
+// next groups turn by products with exp(i*G*w) (GroupTurn).  The per-pair products make this
+// path bound by the vector units rather than by HBM.
 //
 // Work split: grid (splits, query rows), one query head per workgroup (4-bit codes, ragged
 // batches and odd GQA ratios; a GQA group's heads each read their KV head; the query-group
@@ -48,6 +49,27 @@ __device__ __forceinline__ float2 turn(double theta) {
     sincosf((float)r, &s, &c);
     return make_float2(c, s);
 }
+
+// The turns exp(i*t0*w) of a wave's consecutive key groups (t0 = G*g): the first from the
+// angle (turn), each next one as the product with exp(i*G*w), and again from the angle every
+// kReanchor groups.  A product in binary32 moves the phase and the length by a few units of
+// 2^-24, so the turn drifts by under 1e-5 between anchors, far below the logits' tolerance,
+// and a group's turn costs four operations instead of a reduction and a sincos.
+constexpr int kReanchor = 16;
+struct GroupTurn {
+    float2 e, step;
+    double w;
+    __device__ __forceinline__ void init(double w_pair, int gs) {
+        w = w_pair;
+        step = turn((double)gs * w_pair);
+    }
+    // the turn of group g, the wave's gi-th (groups gi - 1 and gi consecutive for gi > 0)
+    __device__ __forceinline__ float2 next(int gi, int64_t t0) {
+        if (gi % kReanchor == 0) e = turn((double)t0 * w);
+        else e = make_float2(fmaf(e.x, step.x, -e.y * step.y), fmaf(e.x, step.y, e.y * step.x));
+        return e;
+    }
+};
 
 // Codes of the 8 channels base..base+7 of one token word (see the layouts in the header):
 // 2-bit key word (16 channels, channel 16w + 4i + b in byte b at bits 2i): the lane's 8
@@ -257,7 +279,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
 
     uint32_t tag;
     if (n_groups > 0) {
-        const double w_lane = sh_w[lane];   // the frequency of the lane's pair
+        GroupTurn gt;
+        gt.init(sh_w[lane], GS);   // the frequency of the lane's pair
         const int f_slot = lane + 4 * (lane >> 5), f_run = 8 * k8 + 4 * (k8 >> 2);
         tag = settle_tag(tag_v);
         for (int gi = 0; gi < n_groups; ++gi) {
@@ -265,7 +288,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
             // ---- the group's folded products, pair = lane: each is needed by the 8 lanes that
             // take the pair's channels, so it is formed once and shared through LDS
             {
-                const float2 e = turn((double)((kgb + gi) * GS) * w_lane);   // exp(i*t0*w)
+                const float2 e = gt.next(gi, (int64_t)(kgb + gi) * GS);   // exp(i*t0*w)
                 const float wr = fmaf(q_lo, e.x, q_hi * e.y);    // W = conj(Q) * e
                 const float wi = fmaf(q_lo, e.y, -q_hi * e.x);
                 const float slo = h2f(pn.lo & 0xffffu), zlo = h2f(pn.lo >> 16);
@@ -625,7 +648,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(GS == 12
 
     uint32_t tag;
     if (n_groups > 0) {
-        const double w_lane = sh_w[lane];
+        GroupTurn gt;
+        gt.init(sh_w[lane], GS);
         const int f_slot = lane + 4 * (lane >> 5), f_run = 8 * k8 + 4 * (k8 >> 2);
         const int h_lane = NQ == 4 ? k8 >> 1 : k8 >> 2;   // the (token, head) sum a lane ends with
         const bool lg_store = NQ == 4 || (k8 & 2) == 0;
@@ -633,7 +657,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(GS == 12
         for (int gi = 0; gi < n_groups; ++gi) {
             set_priority_for(n_groups - gi);
             {
-                const float2 e = turn((double)((kgb + gi) * GS) * w_lane);   // E0 = exp(i*t0*w)
+                const float2 e = gt.next(gi, (int64_t)(kgb + gi) * GS);   // E0 = exp(i*t0*w)
                 const float slo = h2f(pn.lo & 0xffffu), zlo = h2f(pn.lo >> 16);
                 const float shi = h2f(pn.hi & 0xffffu), zhi = h2f(pn.hi >> 16);
                 float(*f)[kRpPairs + 8] = sh_f[wave];
