@@ -287,17 +287,17 @@ void commit_state(kivi_cache* c, const kivi_cache& next) {
 // Pre-RoPE attention: one query head per 4-wave workgroup, a key group for every wave, and
 // one round of three workgroups per CU (the kernel's 157-164 VGPRs leave room for three; at
 // 131,072 tokens and 32 heads 24 splits took 168 us, 16 splits 201 us, 32 splits 190 us).
-// With 2-bit codes and a uniform batch a kv head's query heads share a workgroup, four or two
-// of them (rope_queries_per_block), which turns each key once for all of them; at 219 VGPRs
+// With 2-bit codes a kv head's query heads share a workgroup, four or two of them
+// (rope_queries_per_block), which turns each key once for all of them; at 219 VGPRs
 // two such workgroups fit per CU, and one round of them is the target (gqa-mistral-7b: one
 // split, 224-265 us, against 247-275 us for two and 279-301 us for three or four).
-int32_t rope_queries_per_block(const kivi_cache* c, int32_t q_heads, bool ragged) {
-    if (ragged || code_bits(c) != 2) return 1;
+int32_t rope_queries_per_block(const kivi_cache* c, int32_t q_heads) {
+    if (code_bits(c) != 2) return 1;
     const int32_t ratio = q_heads / c->kv_heads;
     return ratio % 4 == 0 ? 4 : (ratio % 2 == 0 ? 2 : 1);
 }
-int32_t rope_splits_for(const kivi_cache* c, int32_t q_heads, int64_t groups, bool ragged) {
-    const int32_t nq = rope_queries_per_block(c, q_heads, ragged);
+int32_t rope_splits_for(const kivi_cache* c, int32_t q_heads, int64_t groups) {
+    const int32_t nq = rope_queries_per_block(c, q_heads);
     const int64_t rows = (int64_t)c->batch * q_heads / nq;
     const int64_t target = nq > 1 ? kTargetBlocksRopeGroup : kTargetBlocksRope;
     int64_t s = (target + rows - 1) / rows;
@@ -306,11 +306,11 @@ int32_t rope_splits_for(const kivi_cache* c, int32_t q_heads, int64_t groups, bo
     if (s > kMaxSplits) s = kMaxSplits;
     return (int32_t)s;
 }
-int32_t rope_auto_splits(const kivi_cache* c, int32_t q_heads) { return rope_splits_for(c, q_heads, c->n_quant / c->group, false); }
+int32_t rope_auto_splits(const kivi_cache* c, int32_t q_heads) { return rope_splits_for(c, q_heads, c->n_quant / c->group); }
 // ragged batch: room for four times the splits of the longest context the cache can hold
 int32_t rope_ragged_splits(const kivi_cache* c, int32_t q_heads) {
     const int64_t groups = c->token_cap / c->group;
-    int64_t s = 4 * (int64_t)rope_splits_for(c, q_heads, groups, true);
+    int64_t s = 4 * (int64_t)rope_splits_for(c, q_heads, groups);
     if (s > groups / kWavesRope) s = groups / kWavesRope;
     if (s < 1) s = 1;
     if (s > kMaxSplits) s = kMaxSplits;
@@ -752,9 +752,9 @@ int prepare_attn_rope(const kivi_cache* c, int32_t* seq_state, const uint16_t* q
         num_splits > 0 ? num_splits : (seq_state != nullptr ? rope_ragged_splits(c, q_heads) : rope_auto_splits(c, q_heads));
     st = prepare_attn(c, q, q_heads, sm_scale, out, lse, workspace, workspace_bytes, splits, pa, seq_state);
     if (st != KIVI_OK) return st;
-    pa->nq = rope_queries_per_block(c, q_heads, seq_state != nullptr);
+    pa->nq = rope_queries_per_block(c, q_heads);
     pa->block_rows = pa->q_rows / pa->nq;
-    pa->slot_budget = (int32_t)kTargetBlocksRope;
+    pa->slot_budget = (int32_t)(pa->nq > 1 ? kTargetBlocksRopeGroup : kTargetBlocksRope);
     pa->rope_base = (double)rope_base;
     return KIVI_OK;
 }

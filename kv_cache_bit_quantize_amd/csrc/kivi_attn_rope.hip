@@ -21,8 +21,8 @@
 // next groups turn by products with exp(i*G*w) (GroupTurn).  The per-pair products make this
 // path bound by the vector units rather than by HBM.
 //
-// Work split: grid (splits, query rows), one query head per workgroup (4-bit codes, ragged
-// batches and odd GQA ratios; a GQA group's heads each read their KV head; the query-group
+// Work split: grid (splits, query rows), one query head per workgroup (4-bit codes and odd
+// GQA ratios; a GQA group's heads each read their KV head; the query-group
 // form further down takes the rest); a split owns whole key groups, each of its 4 waves a contiguous
 // run of them, 16 tokens per wave-iteration in two passes of 8 (lane 8t + k: token t of the
 // pass, pairs [8k, 8k+8)).  P.V follows the code layout of the cache's width: 2-bit value
@@ -487,7 +487,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     finish_block<1>(a, rs.splits, split, qrow, tag, sh_o, sh_m, sh_l);
 }
 
-// Query-group form for 2-bit codes and a uniform batch: the NQ query heads qrow0..qrow0+NQ-1
+// Query-group form for 2-bit codes: the NQ query heads qrow0..qrow0+NQ-1
 // of one kv head in one workgroup, which dequantizes and turns each key once for all of them.
 // The group's folded products then carry no query: with E0 = exp(i*t0*w), U = E0*(z_i +
 // i*z_{i+64}), V = E0*s_i and X = i*E0*s_{i+64}, a token's turned key pair is R = (U + V*c +
@@ -528,7 +528,7 @@ __device__ __forceinline__ float token_head_sums(const float (&v)[2][NQ], int k8
     }
 }
 
-template <int GS, int NQ>
+template <int GS, int NQ, bool RAGGED>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(GS == 128 ? 1 : 2))) void attn_rope_group_kernel(AttnArgs a) {
     static_assert(NQ == 2 || NQ == 4, "two or four query heads per workgroup");
     constexpr int kIt = GS / kRpTok;   // iterations per key group
@@ -542,8 +542,11 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(GS == 12
     __shared__ __align__(16) float sh_o[NQ][kSlots][kD];
     __shared__ float sh_m[NQ][kSlots], sh_l[NQ][kSlots];
 
-    const int split = blockIdx.x;
-    const int64_t qrow0 = (int64_t)blockIdx.y * NQ;
+    // (ragged batch: the plan uses sh_o, unused until the end)
+    const WorkItem wi = work_item<RAGGED>(a, reinterpret_cast<int32_t*>(&sh_o[0][0][0]));
+    if (RAGGED && wi.split < 0) return;   // (ragged batch) past the plan's last item
+    const int split = wi.split;
+    const int64_t qrow0 = wi.row * NQ;   // grid row = kvrow*(ratio/NQ) + chunk
     const int64_t kvrow = (int64_t)((uint32_t)qrow0 / (uint32_t)a.ratio);
     if (a.k_new != nullptr && split == 0 && (uint32_t)qrow0 % (uint32_t)a.ratio == 0) store_new_token(a, kvrow);
     const TagLoads<NQ> tag_v = partial_tag<NQ>(a, qrow0);
@@ -551,7 +554,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(GS == 12
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int t8 = lane >> 3, k8 = lane & 7;
 
-    const RowState rs = row_state(a);
+    const RowState rs = RAGGED ? wi.rs : row_state(a);
     const int n_kg = rs.n_quant / GS;
     const int per_split = (n_kg + rs.splits - 1) / rs.splits;
     const int kg_lo = min(n_kg, split * per_split), kg_hi = min(n_kg, kg_lo + per_split);
@@ -845,12 +848,17 @@ hipError_t launch_decode_attn_rope(const AttnArgs& a, hipStream_t s, hipEvent_t 
     KIVI_BY_GROUP(a.group, hipExtLaunchKernelGGL((attn_rope_kernel<BITSv, GS, RAGGEDv>), grid, dim3(kBlock), 0, s, t0, t1, \
                                                  0, a))
     const bool ragged = a.seq_state != nullptr;
-    if (a.nq > 1) {   // (2-bit codes, uniform batch)
+    if (a.nq > 1) {   // (2-bit codes)
         const dim3 ggrid = attn_grid(a, a.block_rows);
-        if (a.nq == 4)
-            KIVI_BY_GROUP(a.group, hipExtLaunchKernelGGL((attn_rope_group_kernel<GS, 4>), ggrid, dim3(kBlock), 0, s, t0, t1, 0, a))
-        else
-            KIVI_BY_GROUP(a.group, hipExtLaunchKernelGGL((attn_rope_group_kernel<GS, 2>), ggrid, dim3(kBlock), 0, s, t0, t1, 0, a))
+#define KIVI_ROPE_GROUP(NQv, RAGGEDv)                                                                              \
+    KIVI_BY_GROUP(a.group, hipExtLaunchKernelGGL((attn_rope_group_kernel<GS, NQv, RAGGEDv>), ggrid, dim3(kBlock), 0, s, \
+                                                 t0, t1, 0, a))
+        if (a.nq == 4) {
+            if (ragged) KIVI_ROPE_GROUP(4, true) else KIVI_ROPE_GROUP(4, false)
+        } else {
+            if (ragged) KIVI_ROPE_GROUP(2, true) else KIVI_ROPE_GROUP(2, false)
+        }
+#undef KIVI_ROPE_GROUP
         return hipGetLastError();
     }
     if (a.bits == 4) {
