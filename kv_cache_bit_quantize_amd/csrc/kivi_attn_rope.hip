@@ -21,8 +21,7 @@
 // next groups turn by products with exp(i*G*w) (GroupTurn).  The per-pair products make this
 // path bound by the vector units rather than by HBM.
 //
-// Work split: grid (splits, query rows), one query head per workgroup (4-bit codes and odd
-// GQA ratios; a GQA group's heads each read their KV head; the query-group
+// Work split: grid (splits, query rows), one query head per workgroup (odd GQA ratios; a GQA group's heads each read their KV head; the query-group
 // form further down takes the rest); a split owns whole key groups, each of its 4 waves a contiguous
 // run of them, 16 tokens per wave-iteration in two passes of 8 (lane 8t + k: token t of the
 // pass, pairs [8k, 8k+8)).  P.V follows the code layout of the cache's width: 2-bit value
@@ -487,7 +486,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     finish_block<1>(a, rs.splits, split, qrow, tag, sh_o, sh_m, sh_l);
 }
 
-// Query-group form for 2-bit codes: the NQ query heads qrow0..qrow0+NQ-1
+// Query-group form: the NQ query heads qrow0..qrow0+NQ-1
 // of one kv head in one workgroup, which dequantizes and turns each key once for all of them.
 // The group's folded products then carry no query: with E0 = exp(i*t0*w), U = E0*(z_i +
 // i*z_{i+64}), V = E0*s_i and X = i*E0*s_{i+64}, a token's turned key pair is R = (U + V*c +
@@ -496,9 +495,11 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
 // token with the two code conversions, against 8 for each head in a workgroup of its own.
 // A lane's 2*NQ partial logits per 16 tokens (two tokens, NQ heads) are summed over the
 // token's 8 lanes by halving exchanges (token_head_sums), after which each lane holds one
-// (token, head) sum.  P.V shares each value tile's 8 matrix instructions among the heads:
-// head h's weights go in row 4*(v%4) + h of block v's A operand, so that the accumulators'
-// register h is head h.
+// (token, head) sum.  2-bit P.V shares each value tile's 8 matrix instructions among the
+// heads: head h's weights go in row 4*(v%4) + h of block v's A operand, so that the
+// accumulators' register h is head h.  4-bit P.V runs on the vector units as in the one-head
+// kernel, each lane's value codes converted once for all heads; every lane forms the weight
+// of the (token, head) sum it holds and passes it through LDS.
 
 // Sums over the 8 lanes of a token (k8 = lane & 7) of 2*NQ values, v[ps][h] = token ps's
 // partial logit of head h.  Each step a lane keeps half of its values and adds its partner's
@@ -528,17 +529,18 @@ __device__ __forceinline__ float token_head_sums(const float (&v)[2][NQ], int k8
     }
 }
 
-template <int GS, int NQ, bool RAGGED>
+template <int BITS, int GS, int NQ, bool RAGGED>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(GS == 128 ? 1 : 2))) void attn_rope_group_kernel(AttnArgs a) {
     static_assert(NQ == 2 || NQ == 4, "two or four query heads per workgroup");
     constexpr int kIt = GS / kRpTok;   // iterations per key group
-    constexpr int NH = NQ / 2;         // P.V weights: heads per lane, lane >> 5 picks which
+    constexpr int NH = NQ / 2;         // 2-bit P.V weights: heads per lane, lane >> 5 picks which
     __shared__ double sh_w[kRpPairs];
     __shared__ __align__(16) float2 sh_ed[GS][kRpPairs];
     __shared__ __align__(16) float sh_f[kWaves][6][kRpPairs + 8];
     __shared__ __align__(16) float sh_lg[kWaves][NQ][kG];
     __shared__ __align__(16) uint8_t sh_wt[kWaves][NQ][4 * 64];
     __shared__ __align__(16) uint8_t sh_zr[4 * 64];
+    __shared__ __align__(16) float sh_p[kWaves][NQ][kRpTok];   // 4-bit: the iteration's weights
     __shared__ __align__(16) float sh_o[NQ][kSlots][kD];
     __shared__ float sh_m[NQ][kSlots], sh_l[NQ][kSlots];
 
@@ -575,8 +577,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(GS == 12
         }
 
     const int64_t tok0 = kvrow * (int64_t)a.token_cap;
-    const uint8_t* kc_row = a.k_codes + tok0 * kRowBytes;
-    const uint8_t* vc_row = a.v_codes + tok0 * kRowBytes;
+    const uint8_t* kc_row = a.k_codes + tok0 * (BITS == 2 ? kRowBytes : kRowBytes4);
+    const uint8_t* vc_row = a.v_codes + tok0 * (BITS == 2 ? kRowBytes : kRowBytes4);
     const uint32_t* kp_row = reinterpret_cast<const uint32_t*>(a.k_sz) + kvrow * (int64_t)(a.token_cap / GS) * kD;
     const uint32_t* vp_row = reinterpret_cast<const uint32_t*>(a.v_sz) + tok0 * (kD / GS);
     const int t_b = kgb * GS;
@@ -588,26 +590,44 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(GS == 12
 #pragma unroll
         for (int ps = 0; ps < 2; ++ps) {
             const uint32_t t = (uint32_t)(tok(it) + 8 * ps + t8);
-            const uint32_t off = (t / kG) * kTileBytes + (16 * (k8 >> 1) + t % 16) * 16 + 8 * ((t % kG) / 16);
-            const uint2 x = *reinterpret_cast<const uint2*>(kc_row + off);
-            L.lo[ps] = x.x;
-            L.hi[ps] = x.y;
+            if constexpr (BITS == 2) {
+                const uint32_t off = (t / kG) * kTileBytes + (16 * (k8 >> 1) + t % 16) * 16 + 8 * ((t % kG) / 16);
+                const uint2 x = *reinterpret_cast<const uint2*>(kc_row + off);
+                L.lo[ps] = x.x;
+                L.hi[ps] = x.y;
+            } else {
+                const uint8_t* r = kc_row + t * kRowBytes4;
+                L.lo[ps] = *reinterpret_cast<const uint32_t*>(r + 4 * k8);
+                L.hi[ps] = *reinterpret_cast<const uint32_t*>(r + kRowBytes4 / 2 + 4 * k8);
+            }
         }
     };
-    // value tile of iteration it: lane l holds chunk l of the codes and token l % 32's pairs
+    // 2-bit: the value tile of iteration it, lane l holding chunk l of the codes and token
+    // l % 32's pairs.  4-bit: lane (vg, vc) reads tokens 4vg..4vg+3 of the iteration and
+    // channels 8vc..8vc+7, as in the one-head kernel.
+    const int vg = lane >> 4, vc = lane & 15;
     struct VLoad { uint32_t c[4]; uint32_t p[4]; };
     auto load_v = [&](VLoad& L, int it) {
-        const uint32_t t0 = (uint32_t)tok(it) & ~(uint32_t)(kG - 1);
-        const uint4 x = reinterpret_cast<const uint4*>(vc_row + (t0 / kG) * kTileBytes)[lane];
-        const uint4 y = load_value_pairs<GS, false>(vp_row + value_pair_index<GS>((int64_t)t0 + (lane & 31), 0));
-        L.c[0] = x.x;
-        L.c[1] = x.y;
-        L.c[2] = x.z;
-        L.c[3] = x.w;
-        L.p[0] = y.x;
-        L.p[1] = y.y;
-        L.p[2] = y.z;
-        L.p[3] = y.w;
+        if constexpr (BITS == 2) {
+            const uint32_t t0 = (uint32_t)tok(it) & ~(uint32_t)(kG - 1);
+            const uint4 x = reinterpret_cast<const uint4*>(vc_row + (t0 / kG) * kTileBytes)[lane];
+            const uint4 y = load_value_pairs<GS, false>(vp_row + value_pair_index<GS>((int64_t)t0 + (lane & 31), 0));
+            L.c[0] = x.x;
+            L.c[1] = x.y;
+            L.c[2] = x.z;
+            L.c[3] = x.w;
+            L.p[0] = y.x;
+            L.p[1] = y.y;
+            L.p[2] = y.z;
+            L.p[3] = y.w;
+        } else {
+            const uint32_t t = (uint32_t)tok(it) + 4 * vg;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                L.c[u] = *reinterpret_cast<const uint32_t*>(vc_row + (t + u) * kRowBytes4 + 4 * vc);
+                L.p[u] = vp_row[(t + u) * (kD / GS) + (8 * vc) / GS];
+            }
+        }
     };
     struct PLoad { uint32_t lo, hi; };
     auto load_kp = [&](PLoad& L, int gi) {
@@ -635,13 +655,23 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(GS == 12
         for (int k = 0; k < 4; ++k) zk[u][k] = 0.0f;
     }
     const bool hp = lane >= 32;
-    if (threadIdx.x < 16) reinterpret_cast<uint4*>(sh_zr)[threadIdx.x] = make_uint4(0, 0, 0, 0);
+    // 4-bit: the lane's channels of every head, and their p*zero share; the sum of the
+    // weights of the (token, head) sums the lane holds (head h_lane below)
+    float o4[NQ][8], oz4[NQ], ls4 = 0.0f;
+#pragma unroll
+    for (int h = 0; h < NQ; ++h) {
+        oz4[h] = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) o4[h][c] = 0.0f;
+    }
+    if (BITS == 2 && threadIdx.x < 16) reinterpret_cast<uint4*>(sh_zr)[threadIdx.x] = make_uint4(0, 0, 0, 0);
 
     KLoad kl;
     VLoad vl;
     PLoad pn;
     if (n_groups > 0) {
         load_k(kl, 0);
+        if constexpr (BITS != 2) load_v(vl, 0);
         load_kp(pn, 0);
     }
     if (threadIdx.x < kRpPairs) sh_w[threadIdx.x] = pow(a.rope_base, -2.0 * (double)threadIdx.x / (double)kD);
@@ -687,14 +717,16 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(GS == 12
 #pragma unroll 2
             for (int j = 0; j < kIt; ++j) {
                 const int it = gi * kIt + j;
-                if (j & 1) load_v(vl, it);
+                if constexpr (BITS == 2) {
+                    if (j & 1) load_v(vl, it);
+                }
                 // ---- partial logits of tokens t8 and 8 + t8, the lane's 8 pairs, every head
                 float part[2][NQ];
 #pragma unroll
                 for (int ps = 0; ps < 2; ++ps) {
                     float c1[8], c2[8];
-                    codes8<2>(kl.lo[ps], k8 & 1, c1);
-                    codes8<2>(kl.hi[ps], k8 & 1, c2);
+                    codes8<BITS>(kl.lo[ps], k8 & 1, c1);
+                    codes8<BITS>(kl.hi[ps], k8 & 1, c2);
                     const float2* ed = &sh_ed[kRpTok * j + 8 * ps + t8][8 * k8];
 #pragma unroll
                     for (int h = 0; h < NQ; ++h) part[ps][h] = 0.0f;
@@ -711,7 +743,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(GS == 12
                 }
                 load_k(kl, it + 1);
                 const float lg = token_head_sums<NQ>(part, k8) * a.sm_log2;   // token 8(k8&1) + t8, head h_lane
-                if (lg_store) sh_lg[wave][h_lane][16 * (j & 1) + 8 * (k8 & 1) + t8] = lg;
+                if (BITS == 2 && lg_store) sh_lg[wave][h_lane][16 * (j & 1) + 8 * (k8 & 1) + t8] = lg;
                 // ---- running maxima: over the lanes that hold a head's 16 sums, then per head
                 float mx = fmax_ieee(lg, perm_f<0xB1>(lg));
                 if constexpr (NQ == 2) mx = fmax_ieee(mx, perm_f<0x4E>(mx));
@@ -728,22 +760,66 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(GS == 12
                     m[h] = mnew;
                 }
                 if (moved) {
+                    if constexpr (BITS == 2) {
 #pragma unroll
-                    for (int h = 0; h < NQ; ++h) {
-                        cv[0][h] *= al[h];
-                        cv[1][h] *= al[h];
+                        for (int h = 0; h < NQ; ++h) {
+                            cv[0][h] *= al[h];
+                            cv[1][h] *= al[h];
+                        }
+#pragma unroll
+                        for (int u = 0; u < NH; ++u) {
+                            const float a_u = hp ? al[NH + u] : al[u];
+                            ls[u] *= a_u;
+#pragma unroll
+                            for (int k = 0; k < 4; ++k) zk[u][k] *= a_u;
+                        }
+                    } else {
+                        float a_l = al[0];   // the factor of the lane's own head
+#pragma unroll
+                        for (int h = 1; h < NQ; ++h) a_l = h_lane == h ? al[h] : a_l;
+                        ls4 *= a_l;
+#pragma unroll
+                        for (int h = 0; h < NQ; ++h) {
+                            oz4[h] *= al[h];
+#pragma unroll
+                            for (int c = 0; c < 8; ++c) o4[h][c] *= al[h];
+                        }
                     }
+                }
+                if constexpr (BITS != 2) {
+                    // the weight of the lane's (token, head) sum, into LDS for the P.V lanes
+                    float m_l = m[0];
 #pragma unroll
-                    for (int u = 0; u < NH; ++u) {
-                        const float a_u = hp ? al[NH + u] : al[u];
-                        ls[u] *= a_u;
-#pragma unroll
-                        for (int k = 0; k < 4; ++k) zk[u][k] *= a_u;
+                    for (int h = 1; h < NQ; ++h) m_l = h_lane == h ? m[h] : m_l;
+                    const float p = exp2_fast(lg - m_l);
+                    if (lg_store) {
+                        ls4 += p;
+                        sh_p[wave][h_lane][8 * (k8 & 1) + t8] = p;
                     }
                 }
                 wave_sync();
-                // ---- P.V of the tile, once its 32 logits are in
-                if (j & 1) {
+                // ---- P.V: 2-bit, of the tile once its 32 logits are in; 4-bit, of the
+                // iteration's 16 tokens on the vector units, (p*s)*c + p*z
+                if constexpr (BITS != 2) {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const float sv = h2f(vl.p[u] & 0xffffu), zv = h2f(vl.p[u] >> 16);
+                        uint32_t lo = vl.c[u] & 0x0F0F0F0Fu, hi = (vl.c[u] >> 4) & 0x0F0F0F0Fu;
+                        asm volatile("" : "+v"(lo), "+v"(hi));
+                        float code[8];
+#pragma unroll
+                        for (int c = 0; c < 8; ++c) code[c] = (float)((((c & 1) ? hi : lo) >> (8 * (c >> 1))) & 0xFFu);
+#pragma unroll
+                        for (int h = 0; h < NQ; ++h) {
+                            const float pt = sh_p[wave][h][4 * vg + u];
+                            const float ps = pt * sv;
+                            oz4[h] = fmaf(pt, zv, oz4[h]);
+#pragma unroll
+                            for (int c = 0; c < 8; ++c) o4[h][c] = fmaf(ps, code[c], o4[h][c]);
+                        }
+                    }
+                    load_v(vl, it + 1);
+                } else if (j & 1) {
                     const int tt = lane & 31, mrow = lane & 15, kgrp = lane >> 4;
                     float p[NH];
 #pragma unroll
@@ -795,9 +871,30 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(GS == 12
         tag = settle_tag(tag_v);
     }
 
-    // ---- the wave's states: o = P.V * 2^20 / vs + sum p*zero; lane l holds channels
-    // 16g + c and 16(g + 4) + c (g = l >> 4, c = l & 15) of every head
-    {
+    // ---- the wave's states.  2-bit: o = P.V * 2^20 / vs + sum p*zero; lane l holds channels
+    // 16g + c and 16(g + 4) + c (g = l >> 4, c = l & 15) of every head.  4-bit: lanes of a
+    // channel run summed (over the token quads), each head's weight sums over the lanes that
+    // held its (token, head) sums.
+    if constexpr (BITS != 2) {
+        float v = ls4 + __shfl_xor(ls4, 1, 64);
+        if constexpr (NQ == 2) v += __shfl_xor(v, 2, 64);
+        v = wave_sum_xor(v, 8, 32);
+#pragma unroll
+        for (int h = 0; h < NQ; ++h) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                float x = o4[h][c] + oz4[h];
+                x += xor16_f(x);
+                x += __shfl_xor(x, 32, 64);   // the four token quads (vg)
+                if (lane < 16) sh_o[h][wave][8 * vc + c] = x;
+            }
+            const float lt = readlane_f(v, NQ == 4 ? 2 * h : 4 * h);
+            if (lane == 0) {
+                sh_m[h][wave] = n_groups > 0 ? m[h] : -INFINITY;
+                sh_l[h][wave] = lt;
+            }
+        }
+    } else {
         float zt[NQ][4], lt[NQ];
 #pragma unroll
         for (int u = 0; u < NH; ++u) {
@@ -848,15 +945,19 @@ hipError_t launch_decode_attn_rope(const AttnArgs& a, hipStream_t s, hipEvent_t 
     KIVI_BY_GROUP(a.group, hipExtLaunchKernelGGL((attn_rope_kernel<BITSv, GS, RAGGEDv>), grid, dim3(kBlock), 0, s, t0, t1, \
                                                  0, a))
     const bool ragged = a.seq_state != nullptr;
-    if (a.nq > 1) {   // (2-bit codes)
+    if (a.nq > 1) {
         const dim3 ggrid = attn_grid(a, a.block_rows);
-#define KIVI_ROPE_GROUP(NQv, RAGGEDv)                                                                              \
-    KIVI_BY_GROUP(a.group, hipExtLaunchKernelGGL((attn_rope_group_kernel<GS, NQv, RAGGEDv>), ggrid, dim3(kBlock), 0, s, \
-                                                 t0, t1, 0, a))
-        if (a.nq == 4) {
-            if (ragged) KIVI_ROPE_GROUP(4, true) else KIVI_ROPE_GROUP(4, false)
+#define KIVI_ROPE_GROUP(BITSv, NQv)                                                                                 \
+    if (ragged)                                                                                                      \
+        KIVI_BY_GROUP(a.group, hipExtLaunchKernelGGL((attn_rope_group_kernel<BITSv, GS, NQv, true>), ggrid, dim3(kBlock), \
+                                                     0, s, t0, t1, 0, a))                                           \
+    else                                                                                                             \
+        KIVI_BY_GROUP(a.group, hipExtLaunchKernelGGL((attn_rope_group_kernel<BITSv, GS, NQv, false>), ggrid, dim3(kBlock), \
+                                                     0, s, t0, t1, 0, a))
+        if (a.bits == 4) {
+            if (a.nq == 4) { KIVI_ROPE_GROUP(4, 4) } else { KIVI_ROPE_GROUP(4, 2) }
         } else {
-            if (ragged) KIVI_ROPE_GROUP(2, true) else KIVI_ROPE_GROUP(2, false)
+            if (a.nq == 4) { KIVI_ROPE_GROUP(2, 4) } else { KIVI_ROPE_GROUP(2, 2) }
         }
 #undef KIVI_ROPE_GROUP
         return hipGetLastError();

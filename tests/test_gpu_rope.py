@@ -174,15 +174,16 @@ def test_long_context_sampled_rows():
     assert_lse_close(lse[:, rows], ref_lse)
 
 
-def test_gqa_mistral_sampled_kv_rows():
+@pytest.mark.parametrize("code_bits", [2, 4])
+def test_gqa_mistral_sampled_kv_rows(code_bits):
     """The gqa-mistral-7b shape (64 sequences, 32 query / 8 kv heads, 8,064 history + 128
-    residual tokens) in 2-bit codes at the call's own split count (four query heads per
-    workgroup): the four query heads of kv rows 0, 261 and 511 against the oracle."""
+    residual tokens) at the call's own split count (four query heads per workgroup): the four
+    query heads of kv rows 0, 261 and 511 against the oracle."""
     dev = gpu_or_skip()
     kivi = _kivi()
     w = synth.WORKLOADS["gqa-mistral-7b"]
     k, v = synth.prefill_kv(w, device=dev)
-    cache = kivi.Cache(w.batch, w.kv_heads, w.token_cap, device=dev)
+    cache = kivi.Cache(w.batch, w.kv_heads, w.token_cap, device=dev, bits=code_bits)
     kivi.kivi_prefill(k, v, w.n_quant, cache)
     q = synth.query(w, device=dev)
     out, lse = kivi.kivi_decode_attn_rope(cache, q, SM, BASE, lse=True)
@@ -190,8 +191,10 @@ def test_gqa_mistral_sampled_kv_rows():
     ratio = w.q_heads // w.kv_heads
     for kvrow in (0, 261, 511):
         b, h = divmod(kvrow, w.kv_heads)
-        rc = ref_cache(1, 1, w.token_cap, k[b:b + 1, h:h + 1].cpu(), v[b:b + 1, h:h + 1].cpu(), w.n_quant)
+        rc = ref_cache(1, 1, w.token_cap, k[b:b + 1, h:h + 1].cpu(), v[b:b + 1, h:h + 1].cpu(), w.n_quant,
+                       bits=code_bits)
         qs = q[b:b + 1, ratio * h:ratio * (h + 1)].contiguous()
         ref_out, ref_lse = rc.decode_attn_rope(bits(qs), SM, BASE)
-        assert_attn_close(out[b:b + 1, ratio * h:ratio * (h + 1)], ref_out, what=f"rope gqa-mistral-7b kv row {kvrow}")
+        assert_attn_close(out[b:b + 1, ratio * h:ratio * (h + 1)], ref_out,
+                          what=f"rope {code_bits}-bit gqa-mistral-7b kv row {kvrow}")
         assert_lse_close(lse[b:b + 1, ratio * h:ratio * (h + 1)], ref_lse)
