@@ -132,6 +132,59 @@ __device__ void residual_rope_states(const AttnArgs& a, const RowState& rs, int6
     o_dst[lane + kRpPairs] = o1;
 }
 
+// residual_rope_states for the NQ query heads qrow0..qrow0+NQ-1 of kv row kvrow: each key is
+// turned once, R = K * exp(i*p*w) per pair (lane m: pair m), and head h's logit is the wave
+// sum of Re(conj(Q_h) * R); the NQ sums are taken together (half_sum4, then one read of each
+// half-wave per head).  States of head h go to o_dst[h], mr[h], lr[h].
+template <int NQ>
+__device__ void residual_rope_group_states(const AttnArgs& a, const RowState& rs, int64_t qrow0, int64_t kvrow, int wave,
+                                           const double* w_pair, float* const (&o_dst)[NQ], float (&mr)[NQ], float (&lr)[NQ]) {
+    static_assert(NQ <= 4, "up to four heads");
+    const int lane = threadIdx.x & 63;
+    float q0[NQ], q1[NQ], o0[NQ], o1[NQ];
+#pragma unroll
+    for (int h = 0; h < NQ; ++h) {
+        q0[h] = h2f(a.q[(qrow0 + h) * kD + lane]);
+        q1[h] = h2f(a.q[(qrow0 + h) * kD + lane + kRpPairs]);
+        o0[h] = o1[h] = 0.0f;
+        mr[h] = -INFINITY;
+        lr[h] = 0.0f;
+    }
+    const double wm = w_pair[lane];
+    for (int i = wave; i < rs.n_res; i += kWaves) {
+        const int slot = (rs.res_head + i) % a.residual_cap;
+        const bool fresh = a.k_new != nullptr && i == rs.n_res - 1;
+        const uint16_t* kr = fresh ? a.k_new + kvrow * kD : a.k_res + (kvrow * a.residual_cap + slot) * kD;
+        const uint16_t* vr = fresh ? a.v_new + kvrow * kD : a.v_res + (kvrow * a.residual_cap + slot) * kD;
+        const float2 e = turn((double)(rs.n_quant + i) * wm);
+        const float k0 = h2f(kr[lane]), k1 = h2f(kr[lane + kRpPairs]);
+        const float rr = fmaf(k0, e.x, -k1 * e.y), ri = fmaf(k0, e.y, k1 * e.x);   // R = K * e
+        float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int h = 0; h < NQ; ++h) part[h] = fmaf(q0[h], rr, q1[h] * ri);
+        // lane b0 + 2*b1 of each half-wave holds the half's sum of part[2*b0 + b1]
+        const float x = half_sum4(part);
+        const float v0 = h2f(vr[lane]), v1 = h2f(vr[lane + kRpPairs]);
+#pragma unroll
+        for (int h = 0; h < NQ; ++h) {
+            const int src = (h >> 1) | ((h & 1) << 1);
+            const float lg = (readlane_f(x, src) + readlane_f(x, 32 + src)) * a.sm_log2;
+            const float mnew = fmaxf(mr[h], lg);
+            const float al = mr[h] == -INFINITY ? 0.0f : exp2_fast(mr[h] - mnew);
+            const float p = exp2_fast(lg - mnew);
+            lr[h] = fmaf(lr[h], al, p);
+            o0[h] = fmaf(o0[h], al, p * v0);
+            o1[h] = fmaf(o1[h], al, p * v1);
+            mr[h] = mnew;
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < NQ; ++h) {
+        o_dst[h][lane] = o0[h];
+        o_dst[h][lane + kRpPairs] = o1[h];
+    }
+}
+
 template <int BITS, int GS, bool RAGGED>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) void attn_rope_kernel(AttnArgs a) {
     constexpr int kIt = GS / kRpTok;   // iterations per key group
@@ -920,19 +973,29 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(GS == 12
             }
         }
     }
-    // ---- fp16 residual (split rs.res_split), keys turned at n_quant + i, head by head
+    // ---- fp16 residual (split rs.res_split), keys turned at n_quant + i once for all heads
     __builtin_amdgcn_s_setprio(0);
+    {
+        float mr[NQ], lr[NQ];
 #pragma unroll
-    for (int h = 0; h < NQ; ++h) {
-        float mr = -INFINITY, lr = 0.0f;
+        for (int h = 0; h < NQ; ++h) {
+            mr[h] = -INFINITY;
+            lr[h] = 0.0f;
+        }
         if (split == rs.res_split) {
             __builtin_amdgcn_s_setprio(2);
-            residual_rope_states(a, rs, qrow0 + h, kvrow, wave, sh_w, &sh_o[h][kWaves + wave][0], mr, lr);
+            float* dst[NQ];
+#pragma unroll
+            for (int h = 0; h < NQ; ++h) dst[h] = &sh_o[h][kWaves + wave][0];
+            residual_rope_group_states<NQ>(a, rs, qrow0, kvrow, wave, sh_w, dst, mr, lr);
             __builtin_amdgcn_s_setprio(0);
         }
         if (lane == 0) {
-            sh_m[h][kWaves + wave] = mr;
-            sh_l[h][kWaves + wave] = lr;
+#pragma unroll
+            for (int h = 0; h < NQ; ++h) {
+                sh_m[h][kWaves + wave] = mr[h];
+                sh_l[h][kWaves + wave] = lr[h];
+            }
         }
     }
     __syncthreads();
