@@ -111,21 +111,33 @@ __device__ void residual_rope_states(const AttnArgs& a, const RowState& rs, int6
     float o0 = 0.0f, o1 = 0.0f;
     mr = -INFINITY;
     lr = 0.0f;
-    for (int i = wave; i < rs.n_res; i += kWaves) {
+    // the key and value channels lane, lane + 64 of residual token i, loaded a token ahead
+    struct RLoad { uint16_t k0, k1, v0, v1; };
+    auto load = [&](RLoad& L, int i) {
         const int slot = (rs.res_head + i) % a.residual_cap;
         const bool fresh = a.k_new != nullptr && i == rs.n_res - 1;
         const uint16_t* kr = fresh ? a.k_new + kvrow * kD : a.k_res + (kvrow * a.residual_cap + slot) * kD;
         const uint16_t* vr = fresh ? a.v_new + kvrow * kD : a.v_res + (kvrow * a.residual_cap + slot) * kD;
+        L.k0 = kr[lane];
+        L.k1 = kr[lane + kRpPairs];
+        L.v0 = vr[lane];
+        L.v1 = vr[lane + kRpPairs];
+    };
+    RLoad nx;
+    if (wave < rs.n_res) load(nx, wave);
+    for (int i = wave; i < rs.n_res; i += kWaves) {
+        const RLoad cur = nx;
+        if (i + kWaves < rs.n_res) load(nx, i + kWaves);
         const float2 e = turn((double)(rs.n_quant + i) * wm);
         const float wr = fmaf(q0, e.x, q1 * e.y), wi = fmaf(q0, e.y, -q1 * e.x);   // conj(Q) * e
-        const float part = fmaf(wr, h2f(kr[lane]), -wi * h2f(kr[lane + kRpPairs]));
+        const float part = fmaf(wr, h2f(cur.k0), -wi * h2f(cur.k1));
         const float lg = wave_sum(part) * a.sm_log2;
         const float mnew = fmaxf(mr, lg);
         const float al = mr == -INFINITY ? 0.0f : exp2_fast(mr - mnew);
         const float p = exp2_fast(lg - mnew);
         lr = fmaf(lr, al, p);
-        o0 = fmaf(o0, al, p * h2f(vr[lane]));
-        o1 = fmaf(o1, al, p * h2f(vr[lane + kRpPairs]));
+        o0 = fmaf(o0, al, p * h2f(cur.v0));
+        o1 = fmaf(o1, al, p * h2f(cur.v1));
         mr = mnew;
     }
     o_dst[lane] = o0;
@@ -151,20 +163,32 @@ __device__ void residual_rope_group_states(const AttnArgs& a, const RowState& rs
         lr[h] = 0.0f;
     }
     const double wm = w_pair[lane];
-    for (int i = wave; i < rs.n_res; i += kWaves) {
+    // the key and value channels lane, lane + 64 of residual token i, loaded a token ahead
+    struct RLoad { uint16_t k0, k1, v0, v1; };
+    auto load = [&](RLoad& L, int i) {
         const int slot = (rs.res_head + i) % a.residual_cap;
         const bool fresh = a.k_new != nullptr && i == rs.n_res - 1;
         const uint16_t* kr = fresh ? a.k_new + kvrow * kD : a.k_res + (kvrow * a.residual_cap + slot) * kD;
         const uint16_t* vr = fresh ? a.v_new + kvrow * kD : a.v_res + (kvrow * a.residual_cap + slot) * kD;
+        L.k0 = kr[lane];
+        L.k1 = kr[lane + kRpPairs];
+        L.v0 = vr[lane];
+        L.v1 = vr[lane + kRpPairs];
+    };
+    RLoad nx;
+    if (wave < rs.n_res) load(nx, wave);
+    for (int i = wave; i < rs.n_res; i += kWaves) {
+        const RLoad cur = nx;
+        if (i + kWaves < rs.n_res) load(nx, i + kWaves);
         const float2 e = turn((double)(rs.n_quant + i) * wm);
-        const float k0 = h2f(kr[lane]), k1 = h2f(kr[lane + kRpPairs]);
+        const float k0 = h2f(cur.k0), k1 = h2f(cur.k1);
         const float rr = fmaf(k0, e.x, -k1 * e.y), ri = fmaf(k0, e.y, k1 * e.x);   // R = K * e
         float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int h = 0; h < NQ; ++h) part[h] = fmaf(q0[h], rr, q1[h] * ri);
         // lane b0 + 2*b1 of each half-wave holds the half's sum of part[2*b0 + b1]
         const float x = half_sum4(part);
-        const float v0 = h2f(vr[lane]), v1 = h2f(vr[lane + kRpPairs]);
+        const float v0 = h2f(cur.v0), v1 = h2f(cur.v1);
 #pragma unroll
         for (int h = 0; h < NQ; ++h) {
             const int src = (h >> 1) | ((h & 1) << 1);
