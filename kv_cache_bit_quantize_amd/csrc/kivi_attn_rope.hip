@@ -21,7 +21,8 @@
 // next groups turn by products with exp(i*G*w) (GroupTurn).  The per-pair products make this
 // path bound by the vector units rather than by HBM.
 //
-// Work split: grid (splits, query rows), one query head per workgroup (odd GQA ratios; a GQA group's heads each read their KV head; the query-group
+// Work split: grid (splits, query rows), one query head per workgroup (GQA ratios divisible by
+// neither 2 nor 3; a GQA group's heads each read their KV head; the query-group
 // form further down takes the rest); a split owns whole key groups, each of its 4 waves a contiguous
 // run of them, 16 tokens per wave-iteration in two passes of 8 (lane 8t + k: token t of the
 // pass, pairs [8k, 8k+8)).  P.V follows the code layout of the cache's width: 2-bit value
@@ -608,16 +609,19 @@ __device__ __forceinline__ float token_head_sums(const float (&v)[2][NQ], int k8
 
 template <int BITS, int GS, int NQ, bool RAGGED>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(GS == 128 ? 1 : 2))) void attn_rope_group_kernel(AttnArgs a) {
-    static_assert(NQ == 2 || NQ == 4, "two or four query heads per workgroup");
+    static_assert(NQ >= 2 && NQ <= 4, "two to four query heads per workgroup");
     constexpr int kIt = GS / kRpTok;   // iterations per key group
-    constexpr int NH = NQ / 2;         // 2-bit P.V weights: heads per lane, lane >> 5 picks which
+    // heads as the lanes see them: three take the four-head layout, the fourth head idle (its
+    // queries zero, its sums and weights never used)
+    constexpr int NP = NQ == 2 ? 2 : 4;
+    constexpr int NH = NP / 2;         // 2-bit P.V weights: heads per lane, lane >> 5 picks which
     __shared__ double sh_w[kRpPairs];
     __shared__ __align__(16) float2 sh_ed[GS][kRpPairs];
     __shared__ __align__(16) float sh_f[kWaves][6][kRpPairs + 8];
-    __shared__ __align__(16) float sh_lg[kWaves][NQ][kG];
-    __shared__ __align__(16) uint8_t sh_wt[kWaves][NQ][4 * 64];
+    __shared__ __align__(16) float sh_lg[kWaves][NP][kG];
+    __shared__ __align__(16) uint8_t sh_wt[kWaves][NP][4 * 64];
     __shared__ __align__(16) uint8_t sh_zr[4 * 64];
-    __shared__ __align__(16) float sh_p[kWaves][NQ][kRpTok];   // 4-bit: the iteration's weights
+    __shared__ __align__(16) float sh_p[kWaves][NP][kRpTok];   // 4-bit: the iteration's weights
     __shared__ __align__(16) float sh_o[NQ][kSlots][kD];
     __shared__ float sh_m[NQ][kSlots], sh_l[NQ][kSlots];
 
@@ -720,9 +724,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(GS == 12
 
     // running maxima (wave-uniform), P.V accumulators (register h: head h), and per lane the
     // sums and p*zero shares of heads NH*(lane >> 5) + u
-    float m[NQ];
+    float m[NP];
 #pragma unroll
-    for (int h = 0; h < NQ; ++h) m[h] = -INFINITY;
+    for (int h = 0; h < NP; ++h) m[h] = -INFINITY;
     v4f cv[2] = {(v4f){0.0f, 0.0f, 0.0f, 0.0f}, (v4f){0.0f, 0.0f, 0.0f, 0.0f}};
     float zk[NH][4], ls[NH], vs = 0.0f;
 #pragma unroll
@@ -761,8 +765,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(GS == 12
         GroupTurn gt;
         gt.init(sh_w[lane], GS);
         const int f_slot = lane + 4 * (lane >> 5), f_run = 8 * k8 + 4 * (k8 >> 2);
-        const int h_lane = NQ == 4 ? k8 >> 1 : k8 >> 2;   // the (token, head) sum a lane ends with
-        const bool lg_store = NQ == 4 || (k8 & 2) == 0;
+        const int h_lane = NP == 4 ? k8 >> 1 : k8 >> 2;   // the (token, head) sum a lane ends with
+        const bool lg_store = (NP == 4 || (k8 & 2) == 0) && h_lane < NQ;
         tag = settle_tag(tag_v);
         for (int gi = 0; gi < n_groups; ++gi) {
             set_priority_for(n_groups - gi);
@@ -798,7 +802,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(GS == 12
                     if (j & 1) load_v(vl, it);
                 }
                 // ---- partial logits of tokens t8 and 8 + t8, the lane's 8 pairs, every head
-                float part[2][NQ];
+                float part[2][NP];
 #pragma unroll
                 for (int ps = 0; ps < 2; ++ps) {
                     float c1[8], c2[8];
@@ -806,7 +810,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(GS == 12
                     codes8<BITS>(kl.hi[ps], k8 & 1, c2);
                     const float2* ed = &sh_ed[kRpTok * j + 8 * ps + t8][8 * k8];
 #pragma unroll
-                    for (int h = 0; h < NQ; ++h) part[ps][h] = 0.0f;
+                    for (int h = 0; h < NP; ++h) part[ps][h] = 0.0f;
 #pragma unroll
                     for (int jj = 0; jj < 8; ++jj) {
                         const float2 e = ed[jj];
@@ -819,18 +823,20 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(GS == 12
                     }
                 }
                 load_k(kl, it + 1);
-                const float lg = token_head_sums<NQ>(part, k8) * a.sm_log2;   // token 8(k8&1) + t8, head h_lane
+                const float lg = token_head_sums<NP>(part, k8) * a.sm_log2;   // token 8(k8&1) + t8, head h_lane
                 if (BITS == 2 && lg_store) sh_lg[wave][h_lane][16 * (j & 1) + 8 * (k8 & 1) + t8] = lg;
                 // ---- running maxima: over the lanes that hold a head's 16 sums, then per head
                 float mx = fmax_ieee(lg, perm_f<0xB1>(lg));
-                if constexpr (NQ == 2) mx = fmax_ieee(mx, perm_f<0x4E>(mx));
+                if constexpr (NP == 2) mx = fmax_ieee(mx, perm_f<0x4E>(mx));
                 mx = fmax_ieee(mx, perm_f<0x128>(mx));   // lane (i+8)%16 of the row
                 mx = fmax_ieee(mx, xor16_f(mx));
-                float al[NQ];
+                float al[NP];
                 bool moved = false;
 #pragma unroll
+                for (int h = NQ; h < NP; ++h) al[h] = 1.0f;
+#pragma unroll
                 for (int h = 0; h < NQ; ++h) {
-                    const int src = NQ == 4 ? 2 * h : 4 * h;
+                    const int src = NP == 4 ? 2 * h : 4 * h;
                     const float mnew = fmax_ieee(m[h], fmax_ieee(readlane_f(mx, src), readlane_f(mx, 32 + src)));
                     al[h] = mnew == m[h] ? 1.0f : (m[h] == -INFINITY ? 0.0f : exp2_fast(m[h] - mnew));
                     moved |= mnew != m[h];
@@ -902,7 +908,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(GS == 12
 #pragma unroll
                     for (int u = 0; u < NH; ++u) {
                         const float mh = hp ? m[NH + u] : m[u];
-                        p[u] = exp2_fast(sh_lg[wave][NH * (int)hp + u][tt] - mh);
+                        p[u] = NH * (int)hp + u < NQ ? exp2_fast(sh_lg[wave][NH * (int)hp + u][tt] - mh) : 0.0f;
                         ls[u] += p[u];
 #pragma unroll
                         for (int k = 0; k < 4; ++k) zk[u][k] = fmaf(p[u], h2f(vl.p[k] >> 16), zk[u][k]);
@@ -954,7 +960,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(GS == 12
     // held its (token, head) sums.
     if constexpr (BITS != 2) {
         float v = ls4 + __shfl_xor(ls4, 1, 64);
-        if constexpr (NQ == 2) v += __shfl_xor(v, 2, 64);
+        if constexpr (NP == 2) v += __shfl_xor(v, 2, 64);
         v = wave_sum_xor(v, 8, 32);
 #pragma unroll
         for (int h = 0; h < NQ; ++h) {
@@ -965,14 +971,14 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(GS == 12
                 x += __shfl_xor(x, 32, 64);   // the four token quads (vg)
                 if (lane < 16) sh_o[h][wave][8 * vc + c] = x;
             }
-            const float lt = readlane_f(v, NQ == 4 ? 2 * h : 4 * h);
+            const float lt = readlane_f(v, NP == 4 ? 2 * h : 4 * h);
             if (lane == 0) {
                 sh_m[h][wave] = n_groups > 0 ? m[h] : -INFINITY;
                 sh_l[h][wave] = lt;
             }
         }
     } else {
-        float zt[NQ][4], lt[NQ];
+        float zt[NP][4], lt[NP];
 #pragma unroll
         for (int u = 0; u < NH; ++u) {
 #pragma unroll
@@ -1042,9 +1048,9 @@ hipError_t launch_decode_attn_rope(const AttnArgs& a, hipStream_t s, hipEvent_t 
         KIVI_BY_GROUP(a.group, hipExtLaunchKernelGGL((attn_rope_group_kernel<BITSv, GS, NQv, false>), ggrid, dim3(kBlock), \
                                                      0, s, t0, t1, 0, a))
         if (a.bits == 4) {
-            if (a.nq == 4) { KIVI_ROPE_GROUP(4, 4) } else { KIVI_ROPE_GROUP(4, 2) }
+            if (a.nq == 4) { KIVI_ROPE_GROUP(4, 4) } else if (a.nq == 3) { KIVI_ROPE_GROUP(4, 3) } else { KIVI_ROPE_GROUP(4, 2) }
         } else {
-            if (a.nq == 4) { KIVI_ROPE_GROUP(2, 4) } else { KIVI_ROPE_GROUP(2, 2) }
+            if (a.nq == 4) { KIVI_ROPE_GROUP(2, 4) } else if (a.nq == 3) { KIVI_ROPE_GROUP(2, 3) } else { KIVI_ROPE_GROUP(2, 2) }
         }
 #undef KIVI_ROPE_GROUP
         return hipGetLastError();

@@ -2,8 +2,8 @@
 kivi_ref_decode_attn_rope: keys dequantized, turned by the rotary embedding at their
 sequence positions, dense fp64 attention.  Bar: per row max |o_gpu - o_ref| / max |o_ref|
 <= 2e-3, lse within 2e-3 + 2^-18 |lse|.  Covers both code widths, the three group sizes,
-MHA and GQA (query-group ratios 4 and 2, whose 2-bit calls take a kv head's query heads in
-one workgroup, and ratio 3), explicit split counts, caches with only history or only residual, a decode
+MHA and GQA (ratios 4, 3 and 2, whose calls take a kv head's query heads in one workgroup),
+explicit split counts, caches with only history or only residual, a decode
 loop whose flushes move the residual ring, another rotary base, and the 131,072-token
 shape (angles past 10^5 radians) on sampled rows, and ragged batches (each sequence turned at
 its own positions)."""
@@ -48,7 +48,7 @@ def _check(cache, rc, q, base=BASE, splits=0, rows=None, what=""):
 
 @pytest.mark.parametrize("code_bits", [2, 4])
 @pytest.mark.parametrize("G", [32, 64, 128])
-@pytest.mark.parametrize("q_heads,kv_heads,splits", [(4, 4, 0), (8, 2, 0), (6, 2, 3), (2, 2, 7), (4, 2, 5)])
+@pytest.mark.parametrize("q_heads,kv_heads,splits", [(4, 4, 0), (8, 2, 0), (6, 2, 3), (2, 2, 7), (4, 2, 5), (3, 1, 0)])
 def test_attention(code_bits, G, q_heads, kv_heads, splits):
     dev = gpu_or_skip()
     w = synth.small(seed=600 + G + q_heads + splits, batch=2, q_heads=q_heads, kv_heads=kv_heads,
