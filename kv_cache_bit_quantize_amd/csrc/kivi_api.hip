@@ -288,9 +288,10 @@ void commit_state(kivi_cache* c, const kivi_cache& next) {
 // one round of three workgroups per CU (the kernel's 157-164 VGPRs leave room for three; at
 // 131,072 tokens and 32 heads 24 splits took 168 us, 16 splits 201 us, 32 splits 190 us).
 // With a GQA ratio divisible by two or three a kv head's query heads share a workgroup, four,
-// three or two of them (rope_queries_per_block), which turns each key once for all of them; at 219 VGPRs
-// two such workgroups fit per CU, and one round of them is the target (gqa-mistral-7b: one
-// split, 224-265 us, against 247-275 us for two and 279-301 us for three or four).
+// three or two of them (rope_queries_per_block), which turns each key once for all of them; at
+// 180-256 VGPRs two such workgroups fit per CU, and one round of them is the target
+// (gqa-mistral-7b: one split, 224-265 us, against 247-275 us for two and 279-301 us for three
+// or four).
 int32_t rope_queries_per_block(const kivi_cache* c, int32_t q_heads) {
     const int32_t ratio = q_heads / c->kv_heads;
     return ratio % 4 == 0 ? 4 : (ratio % 3 == 0 ? 3 : (ratio % 2 == 0 ? 2 : 1));
