@@ -357,6 +357,16 @@ def test_rope_splits():
     small = _cache(token_cap=256, n_quant=64, n_res=10)
     assert L.kivi_decode_attn_rope_splits(C.byref(small), 4) == 1   # two key groups: fewer than the 4 waves
     assert L.kivi_decode_attn_rope_splits(C.byref(c), 33) == -2
+    # grouped-query shapes take a kv head's query heads (four, three or two) in one workgroup,
+    # two workgroups per CU: one round of 512, whatever the code width
+    for flags in (0, kivi.KIVI_CODES_4BIT):
+        g = _cache(batch=64, kv_heads=8, token_cap=8192, n_quant=8160, n_res=32, flags=flags)
+        assert L.kivi_decode_attn_rope_splits(C.byref(g), 32) == 1      # 512 workgroup rows
+        assert L.kivi_decode_attn_rope_splits(C.byref(g), 24) == 1      # ratio 3: 512 rows
+        g = _cache(batch=32, kv_heads=8, token_cap=8192, n_quant=8160, n_res=32, flags=flags)
+        assert L.kivi_decode_attn_rope_splits(C.byref(g), 24) == 2      # 256 rows
+        assert L.kivi_decode_attn_rope_splits(C.byref(g), 16) == 2      # ratio 2: 256 rows
+        assert L.kivi_decode_attn_rope_splits(C.byref(g), 8) == 3       # ratio 1: 256 rows of one head, 768 target
 
 
 def test_rope_ragged_arguments():
