@@ -188,6 +188,13 @@ class SlicedRef:
                                  range(len(self.parts))))
         return np.concatenate([r[0] for r in res]), np.concatenate([r[1] for r in res])
 
+    def decode_attn_rope(self, q, sm_scale, rope_base):
+        qb = _u16(q)
+        res = list(self.pool.map(
+            lambda i: self.parts[i].decode_attn_rope(qb[self.bounds[i][0]:self.bounds[i][1]], sm_scale, rope_base),
+            range(len(self.parts))))
+        return np.concatenate([r[0] for r in res]), np.concatenate([r[1] for r in res])
+
     def assert_cache_equal(self, gpu, ring=True):
         """Bit-exact comparison of the whole packed history and the residual ring, slice by slice."""
         H = self.kv_heads

@@ -4,14 +4,14 @@ sequence positions, dense fp64 attention.  Bar: per row max |o_gpu - o_ref| / ma
 <= 2e-3, lse within 2e-3 + 2^-18 |lse|.  Covers both code widths, the three group sizes,
 MHA and GQA (ratios 4, 3 and 2, whose calls take a kv head's query heads in one workgroup),
 explicit split counts, caches with only history or only residual, a decode
-loop whose flushes move the residual ring, another rotary base, and the 131,072-token
-shape (angles past 10^5 radians) on sampled rows, and ragged batches (each sequence turned at
-its own positions)."""
+loop whose flushes move the residual ring, another rotary base, the 131,072-token shape
+(angles past 10^5 radians) on sampled rows, the whole gqa-mistral-7b cache in both widths,
+and ragged batches (each sequence turned at its own positions)."""
 import numpy as np
 import pytest
 import torch
 
-from kivi_testlib import assert_attn_close, assert_cache_equal, assert_lse_close, bits, gpu_or_skip, ref_cache
+from kivi_testlib import SlicedRef, assert_attn_close, assert_cache_equal, assert_lse_close, bits, gpu_or_skip, ref_cache
 from kv_cache_bit_quantize_amd import synth
 from oracle import ref
 
@@ -198,3 +198,25 @@ def test_gqa_mistral_sampled_kv_rows(code_bits):
         assert_attn_close(out[b:b + 1, ratio * h:ratio * (h + 1)], ref_out,
                           what=f"rope {code_bits}-bit gqa-mistral-7b kv row {kvrow}")
         assert_lse_close(lse[b:b + 1, ratio * h:ratio * (h + 1)], ref_lse)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("code_bits", [2, 4])
+def test_gqa_mistral_all_rows(code_bits):
+    """The gqa-mistral-7b cache (64 sequences x 8 kv heads, 8,064 history + 128 residual
+    tokens) in one call at its own split count: all 2,048 query rows and their lse against
+    the oracle (one oracle cache per slice of the sequences, on host threads)."""
+    dev = gpu_or_skip()
+    kivi = _kivi()
+    w = synth.WORKLOADS["gqa-mistral-7b"]
+    k, v = synth.prefill_kv(w, device=dev)
+    cache = kivi.Cache(w.batch, w.kv_heads, w.token_cap, device=dev, bits=code_bits)
+    kivi.kivi_prefill(k, v, w.n_quant, cache)
+    q = synth.query(w, device=dev)
+    out, lse = kivi.kivi_decode_attn_rope(cache, q, SM, BASE, lse=True)
+    torch.cuda.synchronize()
+    rc = SlicedRef(w.batch, w.kv_heads, w.token_cap, k, v, w.n_quant, parts=16, bits=code_bits)
+    del k, v
+    ref_out, ref_lse = rc.decode_attn_rope(q, SM, BASE)
+    assert_attn_close(out, ref_out, what=f"rope {code_bits}-bit gqa-mistral-7b all rows")
+    assert_lse_close(lse, ref_lse)
