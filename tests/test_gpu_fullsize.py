@@ -11,7 +11,7 @@ the softmax nearly one-hot, and check sampled rows of the largest caches.  Here:
   * the 40-layer llama2-13b cache: codes and pairs of all 40 layers, each compared whole, and
     attention over all 640 rows of one layer;
   * the ragged serving batch of the benchmark (64 sequences of 512..8,192 tokens, 32 query /
-    8 kv heads), every sequence.
+    8 kv heads), every sequence, plain and as pre-RoPE keys.
 Bars as in the other attention tests: per row max |o_gpu - o_ref| / max |o_ref| <= 2e-3,
 |lse_gpu - lse_ref| <= 2e-3 + 2^-18 |lse_ref|; codes, pairs and rings bit-exact.  The oracle
 runs on 16 host threads (SlicedRef)."""
@@ -114,9 +114,12 @@ def test_llama2_13b_all_layers_codes_and_one_layer_all_rows():
 
 
 @pytest.mark.timeout(600)
-def test_ragged_bench_batch_every_sequence():
+@pytest.mark.parametrize("pre_rope", [False, True])
+def test_ragged_bench_batch_every_sequence(pre_rope):
     """The ragged serving batch that the benchmark times: 64 sequences, context lengths uniform
-    in [512, 8192] (seeded as there), 64..95 of each sequence's tokens in the fp16 residual."""
+    in [512, 8192] (seeded as there), 64..95 of each sequence's tokens in the fp16 residual;
+    plain attention, and attention over the same cache as pre-RoPE keys (each sequence's keys
+    turned at its own positions, base 10000)."""
     dev = gpu_or_skip()
     kivi = _kivi()
     import concurrent.futures
@@ -137,13 +140,19 @@ def test_ragged_bench_batch_every_sequence():
         refs = list(ex.map(lambda t: ref_cache(1, Hkv, hi, t[0], t[1], t[2]), inputs))
     qw = synth.small(seed=seed + 999, batch=B, q_heads=Hq, kv_heads=Hkv, context=1, n_quant=0)
     q = synth.query(qw, step=0, device=dev)
-    out, lse = kivi.kivi_decode_attn_ragged(cache, state, q, SM, lse=True)
+    if pre_rope:
+        out, lse = kivi.kivi_decode_attn_rope_ragged(cache, state, q, SM, 10000.0, lse=True)
+    else:
+        out, lse = kivi.kivi_decode_attn_ragged(cache, state, q, SM, lse=True)
     torch.cuda.synchronize()
     qb = bits(q)
     with concurrent.futures.ThreadPoolExecutor(16) as ex:
-        res = list(ex.map(lambda b: refs[b].decode_attn(qb[b:b + 1], SM), range(B)))
+        if pre_rope:
+            res = list(ex.map(lambda b: refs[b].decode_attn_rope(qb[b:b + 1], SM, 10000.0), range(B)))
+        else:
+            res = list(ex.map(lambda b: refs[b].decode_attn(qb[b:b + 1], SM), range(B)))
     ref_out = np.concatenate([r[0] for r in res])
     ref_lse = np.concatenate([r[1] for r in res])
-    assert_attn_close(out, ref_out, what="ragged bench batch")
+    assert_attn_close(out, ref_out, what=f"ragged bench batch{' pre-RoPE' if pre_rope else ''}")
     assert_lse_close(lse, ref_lse)
     assert int(state[:, 3].abs().sum().item()) == 0
