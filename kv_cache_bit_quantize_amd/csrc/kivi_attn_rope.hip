@@ -884,21 +884,54 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(GS == 12
                 // ---- P.V: 2-bit, of the tile once its 32 logits are in; 4-bit, of the
                 // iteration's 16 tokens on the vector units, (p*s)*c + p*z
                 if constexpr (BITS != 2) {
+                    // Two tokens per instruction: v_dot2_f32_f16 of the pair's weights
+                    // p*s*vs (fp16) with their codes of one channel, placed in the low bits of
+                    // each half as the fp16 subnormals c * 2^-24 (channel 2b) and 16c * 2^-24
+                    // (2b + 1), no conversion.  vs, a power of two shared by the wave, keeps
+                    // the weights below 2^14.
+                    float smax = 0.0f;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) smax = fmaxf(smax, h2f(vl.p[u] & 0xffffu));
+                    if (__builtin_amdgcn_ballot_w64(smax * vs > 16384.0f || (vs == 0.0f && smax > 0.0f))) {
+                        const float gm = wave_max_xor(smax, 1, 32);
+                        const float nvs = __builtin_ldexpf(1.0f, 14 - __builtin_amdgcn_frexp_expf(gm));
+                        if (vs != 0.0f && nvs < vs) {
+                            const float r = nvs / vs;
+#pragma unroll
+                            for (int h = 0; h < NQ; ++h)
+#pragma unroll
+                                for (int c = 0; c < 8; ++c) o4[h][c] *= r;
+                        }
+                        if (vs == 0.0f || nvs < vs) vs = nvs;
+                    }
+                    uint32_t cl[2][4], ch[2][4];   // [token pair][byte]: channels 8vc + 2b, 8vc + 2b + 1
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+#pragma unroll
+                        for (int b = 0; b < 4; ++b) {
+                            // byte b of the pair's first word in byte 0, of its second in byte 2
+                            const uint32_t x = __builtin_amdgcn_perm(vl.c[2 * j + 1], vl.c[2 * j], 0x0C000C00u | ((4u + b) << 16) | b);
+                            cl[j][b] = x & 0x000F000Fu;
+                            ch[j][b] = x & 0x00F000F0u;
+                        }
+                    float sv[4], zv[4];
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
-                        const float sv = h2f(vl.p[u] & 0xffffu), zv = h2f(vl.p[u] >> 16);
-                        uint32_t lo = vl.c[u] & 0x0F0F0F0Fu, hi = (vl.c[u] >> 4) & 0x0F0F0F0Fu;
-                        asm volatile("" : "+v"(lo), "+v"(hi));
-                        float code[8];
+                        sv[u] = h2f(vl.p[u] & 0xffffu) * vs;
+                        zv[u] = h2f(vl.p[u] >> 16);
+                    }
 #pragma unroll
-                        for (int c = 0; c < 8; ++c) code[c] = (float)((((c & 1) ? hi : lo) >> (8 * (c >> 1))) & 0xFFu);
+                    for (int h = 0; h < NQ; ++h) {
+                        const float4 pt = *reinterpret_cast<const float4*>(&sh_p[wave][h][4 * vg]);
+                        oz4[h] = fmaf(pt.x, zv[0], fmaf(pt.y, zv[1], fmaf(pt.z, zv[2], fmaf(pt.w, zv[3], oz4[h]))));
+                        const h2v w0 = {(_Float16)(pt.x * sv[0]), (_Float16)(pt.y * sv[1])};
+                        const h2v w1 = {(_Float16)(pt.z * sv[2]), (_Float16)(pt.w * sv[3])};
 #pragma unroll
-                        for (int h = 0; h < NQ; ++h) {
-                            const float pt = sh_p[wave][h][4 * vg + u];
-                            const float ps = pt * sv;
-                            oz4[h] = fmaf(pt, zv, oz4[h]);
-#pragma unroll
-                            for (int c = 0; c < 8; ++c) o4[h][c] = fmaf(ps, code[c], o4[h][c]);
+                        for (int b = 0; b < 4; ++b) {
+                            o4[h][2 * b] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2v, cl[0][b]), w0, o4[h][2 * b], false);
+                            o4[h][2 * b] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2v, cl[1][b]), w1, o4[h][2 * b], false);
+                            o4[h][2 * b + 1] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2v, ch[0][b]), w0, o4[h][2 * b + 1], false);
+                            o4[h][2 * b + 1] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2v, ch[1][b]), w1, o4[h][2 * b + 1], false);
                         }
                     }
                     load_v(vl, it + 1);
@@ -959,6 +992,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(GS == 12
     // channel run summed (over the token quads), each head's weight sums over the lanes that
     // held its (token, head) sums.
     if constexpr (BITS != 2) {
+        // o = P.V * 2^24 / vs (odd channels 2^20 / vs: their codes sat 4 bits higher) + sum p*z
+        const float inv = vs != 0.0f ? 16777216.0f / vs : 0.0f;
         float v = ls4 + __shfl_xor(ls4, 1, 64);
         if constexpr (NP == 2) v += __shfl_xor(v, 2, 64);
         v = wave_sum_xor(v, 8, 32);
@@ -966,7 +1001,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(GS == 12
         for (int h = 0; h < NQ; ++h) {
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
-                float x = o4[h][c] + oz4[h];
+                float x = fmaf(o4[h][c], (c & 1) ? inv * 0.0625f : inv, oz4[h]);
                 x += xor16_f(x);
                 x += __shfl_xor(x, 32, 64);   // the four token quads (vg)
                 if (lane < 16) sh_o[h][wave][8 * vc + c] = x;
