@@ -12,10 +12,13 @@
 //    token row, low and high nibbles masked into bytes, which sets the channel order of the
 //    planes), A the digit planes (rows 4r..4r+3 head r's digits, other rows zero), so lane
 //    16r + n ends with head r's four digit sums of token n.  q.z is one wave sum per group;
-//  * values, per token: p*(z + c*s) = (p*s)*c + p*z on the vector units (one byte-to-float
-//    conversion and one fma per code; the token-major rows do not give the value matrix
-//    operand, which needs 8 tokens of one channel per lane), the p*z part summed per lane
-//    and added to its channels at the end.
+//  * values, per token: p*(z + c*s) = (p*s)*c + p*z on the vector units (the token-major
+//    rows do not give the value matrix operand, which needs 8 tokens of one channel per
+//    lane): one v_dot2_f32_f16 takes two tokens of one channel, their fp16 weights p*s*vs
+//    (vs a power of two shared by the wave, keeping them below 2^14) against their codes,
+//    moved by one byte permute into the low bits of each half, where they read as the fp16
+//    subnormals c*2^-24 (a high nibble as 16c*2^-24, scaled back at the end): no conversion.
+//    The p*z part is summed per lane and added to its channels at the end.
 //
 // Work split: grid (splits, kv heads x query chunks of NQ heads); a split owns whole key
 // groups, each of its 4 waves a contiguous run of them, 16 tokens per wave-iteration:
@@ -125,6 +128,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     };
 
     float m[NQ], lsum[NQ], o[NQ][8], oz[NQ];   // oz: sum of p*z of the lane's tokens and channel group
+    float vs = 0.0f;                             // the value weights' power of two
 #pragma unroll
     for (int r = 0; r < NQ; ++r) {
         m[r] = -INFINITY;
@@ -242,23 +246,48 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
                     pv[r][2] = x.z;
                     pv[r][3] = x.w;
                 }
+                float smax = 0.0f;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) smax = fmaxf(smax, h2f(cur.vp[u] & 0xffffu));
+                if (__builtin_amdgcn_ballot_w64(smax * vs > 16384.0f || (vs == 0.0f && smax > 0.0f))) {
+                    const float gm = wave_max_xor(smax, 1, 32);
+                    const float nvs = __builtin_ldexpf(1.0f, 14 - __builtin_amdgcn_frexp_expf(gm));
+                    if (vs != 0.0f && nvs < vs) {
+                        const float rs_ = nvs / vs;
+#pragma unroll
+                        for (int r = 0; r < NQ; ++r)
+#pragma unroll
+                            for (int c = 0; c < 8; ++c) o[r][c] *= rs_;
+                    }
+                    if (vs == 0.0f || nvs < vs) vs = nvs;
+                }
+                uint32_t cl[2][4], ch[2][4];   // [token pair (u = 0,1 / 2,3)][byte]: channels 8vc + 2b, 8vc + 2b + 1
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) {
+                        // byte b of the pair's first word in byte 0, of its second in byte 2
+                        const uint32_t x = __builtin_amdgcn_perm(cur.v[2 * j + 1], cur.v[2 * j], 0x0C000C00u | ((4u + b) << 16) | b);
+                        cl[j][b] = x & 0x000F000Fu;
+                        ch[j][b] = x & 0x00F000F0u;
+                    }
+                float sv[4], zv[4];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    const float s = h2f(cur.vp[u] & 0xffffu), z = h2f(cur.vp[u] >> 16);
-                    uint32_t lo = cur.v[u] & 0x0F0F0F0Fu, hi = (cur.v[u] >> 4) & 0x0F0F0F0Fu;
-                    asm volatile("" : "+v"(lo), "+v"(hi));
-                    float ps[NQ];
+                    sv[u] = h2f(cur.vp[u] & 0xffffu) * vs;
+                    zv[u] = h2f(cur.vp[u] >> 16);
+                }
 #pragma unroll
-                    for (int r = 0; r < NQ; ++r) {
-                        const float pt = pv[r][u];
-                        ps[r] = pt * s;
-                        oz[r] = fmaf(pt, z, oz[r]);
-                    }
+                for (int r = 0; r < NQ; ++r) {
+                    oz[r] = fmaf(pv[r][0], zv[0], fmaf(pv[r][1], zv[1], fmaf(pv[r][2], zv[2], fmaf(pv[r][3], zv[3], oz[r]))));
+                    const h2v w0 = {(_Float16)(pv[r][0] * sv[0]), (_Float16)(pv[r][1] * sv[1])};
+                    const h2v w1 = {(_Float16)(pv[r][2] * sv[2]), (_Float16)(pv[r][3] * sv[3])};
 #pragma unroll
-                    for (int c = 0; c < 8; ++c) {
-                        const float code = (float)((((c & 1) ? hi : lo) >> (8 * (c >> 1))) & 0xFFu);
-#pragma unroll
-                        for (int r = 0; r < NQ; ++r) o[r][c] = fmaf(ps[r], code, o[r][c]);
+                    for (int b = 0; b < 4; ++b) {
+                        o[r][2 * b] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2v, cl[0][b]), w0, o[r][2 * b], false);
+                        o[r][2 * b] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2v, cl[1][b]), w1, o[r][2 * b], false);
+                        o[r][2 * b + 1] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2v, ch[0][b]), w0, o[r][2 * b + 1], false);
+                        o[r][2 * b + 1] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2v, ch[1][b]), w1, o[r][2 * b + 1], false);
                     }
                 }
                 load_v(cur, it + 1);
@@ -269,13 +298,16 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
         tag = settle_tag(tag_v);
     }
 
-    // ---- the wave's state per query head: the four token groups' shares of o summed
-    // (lanes c, c+16, c+32, c+48), l summed over the wave (each token counted by its 4 lanes)
+    // ---- the wave's state per query head: o = P.V * 2^24 / vs (odd channels 2^20 / vs) plus
+    // the p*z shares, the four token groups' shares summed (lanes c, c+16, c+32, c+48), l summed
+    // over the wave (each token counted by its 4 lanes)
+    const float inv = vs != 0.0f ? 16777216.0f / vs : 0.0f;
 #pragma unroll
     for (int r = 0; r < NQ; ++r) {
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-            const float oc = o[r][c] + oz[r];   // the lane's p*z share belongs to each of its channels
+            // the lane's p*z share belongs to each of its channels
+            const float oc = fmaf(o[r][c], (c & 1) ? inv * 0.0625f : inv, oz[r]);
             float x = oc + xor16_f(oc);
             x += __shfl_xor(x, 32, 64);
             o[r][c] = x;
